@@ -1,0 +1,176 @@
+"""fp64 CPU oracle for the GQA/MQA KV-cache decode step.
+
+TEST INFRASTRUCTURE ONLY: the test suite, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` are the only callers. The product path
+(``gqa_kv_cache_decode_amd``) never imports this package, and this package
+never imports the product's code; the two share only the seeded input
+generator, which holds none of the method's arithmetic.
+
+The arithmetic lives in ``gqa_oracle.c`` (plain loops in double precision,
+compiled with ``gcc -O2 -fopenmp -ffp-contract=off``). This module is
+marshalling only: numpy arrays in, numpy arrays out.
+
+Pages the oracle follows (cited by title and section):
+
+* [MQA-review] velog review of "Fast Transformer Decoding: One Write-Head is
+  All You Need": §2.1 Dot-Product Attention (the k contraction, softmax and
+  v contraction), §2.4 Multi-head Attention (Incremental) (new K/V row
+  concatenated on the position axis, then attention over all rows), §3 Multi
+  Query Attention (K/V lose the head axis).
+* [GQA-lesson] ttlab "TF2 GQA" lesson: the g-knob table, the h mod g = 0 rule,
+  the cache element-count formula, the multiplication counts and the lab
+  description (contiguous query-head groups; K/V repeated per query head).
+* [LLM-inf-05] albangk "LLM inference 05" notes: the prefill/decode table, the
+  per-layer decode pseudocode and the bytes-per-token arithmetic.
+
+Parity status: every function here is pinned by ``tests/test_oracle_pins.py``
+and ``tests/test_oracle_golden.py`` (no function is "parity unpinned").
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "gqa_oracle.c")
+LIB_PATH = os.path.join(_HERE, "liboracle_gqa.so")
+
+F32 = 0
+BF16 = 1
+
+OK = 0
+ERR_ARG = -1
+ERR_GROUPS = -2
+ERR_UNSUPPORTED = -3
+ERR_CAPACITY = -4
+
+
+class OracleError(RuntimeError):
+    def __init__(self, code: int, what: str):
+        super().__init__(f"oracle {what} failed with code {code}")
+        self.code = code
+
+
+def build() -> str:
+    """Compile the C oracle in place (always recompiles)."""
+    cmd = [
+        "gcc", "-O2", "-fopenmp", "-ffp-contract=off", "-fPIC", "-shared",
+        "-std=c99", "-Wall", "-Wextra", "-o", LIB_PATH + ".tmp", _SRC, "-lm",
+    ]
+    subprocess.run(cmd, check=True)
+    os.replace(LIB_PATH + ".tmp", LIB_PATH)
+    return LIB_PATH
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        build()
+    lib = ctypes.CDLL(LIB_PATH)
+    vp = ctypes.c_void_p
+    i32 = ctypes.c_int
+    i64 = ctypes.c_int64
+    lib.oracle_kv_cache_elems.restype = i64
+    lib.oracle_kv_cache_elems.argtypes = [i64, i64, i64, i64]
+    lib.oracle_kv_bytes_per_token.restype = i64
+    lib.oracle_kv_bytes_per_token.argtypes = [i64, i64, i64, i64]
+    lib.oracle_kv_append.restype = i32
+    lib.oracle_kv_append.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32]
+    lib.oracle_decode_attention.restype = i32
+    lib.oracle_decode_attention.argtypes = [
+        vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
+        ctypes.c_float, i32, vp, i32,
+    ]
+    _lib = lib
+    return lib
+
+
+def _dtype_code(arr: np.ndarray) -> int:
+    if arr.dtype == np.float32:
+        return F32
+    if arr.dtype == np.uint16:
+        return BF16
+    raise TypeError(f"oracle takes float32 or bf16 bit patterns (uint16), got {arr.dtype}")
+
+
+def _ptr(arr: np.ndarray):
+    return arr.ctypes.data_as(ctypes.c_void_p)
+
+
+def kv_cache_elems(layers: int, kv_heads: int, length: int, head_dim: int) -> int:
+    """2 x layers x KV heads x length x head dim [GQA-lesson]."""
+    return int(_load().oracle_kv_cache_elems(layers, kv_heads, length, head_dim))
+
+
+def kv_bytes_per_token(layers: int, kv_heads: int, head_dim: int, elem_bytes: int) -> int:
+    """Bytes one token adds to a model's cache [LLM-inf-05, memory arithmetic]."""
+    return int(_load().oracle_kv_bytes_per_token(layers, kv_heads, head_dim, elem_bytes))
+
+
+def kv_append(k_cache, v_cache, k_new, v_new, lens) -> None:
+    """In place: write each sequence's new K/V row at position lens[b], then lens[b] += 1.
+
+    k_cache [b, g, cap, d_k], v_cache [b, g, cap, d_v], k_new [b, g, d_k],
+    v_new [b, g, d_v], lens int32 [b]; all C-contiguous numpy arrays of one
+    element type (float32, or uint16 bf16 bit patterns).
+    """
+    for a in (k_cache, v_cache, k_new, v_new, lens):
+        if not a.flags.c_contiguous:
+            raise ValueError("oracle arrays must be C-contiguous")
+    if lens.dtype != np.int32:
+        raise TypeError("lens must be int32")
+    b, g, cap, d_k = k_cache.shape
+    d_v = v_cache.shape[3]
+    dt = _dtype_code(k_cache)
+    rc = _load().oracle_kv_append(
+        _ptr(k_cache), _ptr(v_cache), _ptr(k_new), _ptr(v_new), _ptr(lens),
+        b, g, d_k, d_v, cap, dt)
+    if rc != OK:
+        raise OracleError(rc, "kv_append")
+
+
+def decode_attention(q, k_cache, v_cache, lens, scale: float, *, want_weights=False,
+                     threads: int = 0, count_muls=False):
+    """Attention of one query token per sequence against its cache, in fp64.
+
+    q [b, h, d_k]; caches [b, g, cap, d]; lens int32 [b] (attended lengths).
+    Returns out [b, h, d_v] float64, plus weights [b, h, cap] float64 and/or
+    the multiplication count when asked.
+    """
+    for a in (q, k_cache, v_cache, lens):
+        if not a.flags.c_contiguous:
+            raise ValueError("oracle arrays must be C-contiguous")
+    if lens.dtype != np.int32:
+        raise TypeError("lens must be int32")
+    b, h, d_k = q.shape
+    bk, g, cap, dk2 = k_cache.shape
+    d_v = v_cache.shape[3]
+    if bk != b or dk2 != d_k or v_cache.shape[:3] != (b, g, cap):
+        raise ValueError("shape mismatch between q and caches")
+    dt = _dtype_code(k_cache)
+    if _dtype_code(q) != dt or _dtype_code(v_cache) != dt:
+        raise TypeError("q, K and V must share an element type")
+    out = np.empty((b, h, d_v), dtype=np.float64)
+    weights = np.empty((b, h, cap), dtype=np.float64) if want_weights else None
+    muls = ctypes.c_int64(0)
+    rc = _load().oracle_decode_attention(
+        _ptr(out), _ptr(weights) if weights is not None else None,
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(lens),
+        b, h, g, d_k, d_v, cap, ctypes.c_float(scale), dt,
+        ctypes.byref(muls) if count_muls else None, threads)
+    if rc != OK:
+        raise OracleError(rc, "decode_attention")
+    res = [out]
+    if want_weights:
+        res.append(weights)
+    if count_muls:
+        res.append(int(muls.value))
+    return res[0] if len(res) == 1 else tuple(res)

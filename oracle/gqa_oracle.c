@@ -1,0 +1,223 @@
+/*
+ * Plain fp64 CPU oracle for one incremental decoding step of grouped-query
+ * attention against a per-sequence KV cache.
+ *
+ * TEST INFRASTRUCTURE ONLY. Only the test suite, the smoke check and the CPU
+ * baseline leg of the benchmark may load this library. The product path (the
+ * HIP library under gqa_kv_cache_decode_amd/csrc) shares no code, header,
+ * table or constant with this file.
+ *
+ * Sources (web pages; see the oracle package docstring for the full list):
+ *   [MQA-review]   "Fast Transformer Decoding: One Write-Head is All You Need"
+ *                  paper review (velog): §2.1 Dot-Product Attention,
+ *                  §2.4 Multi-head Attention (Incremental), §3 Multi Query
+ *                  Attention.
+ *   [GQA-lesson]   "TF2 GQA" lesson (ttlab): the g-knob table (g = h is MHA,
+ *                  1 < g < h is GQA, g = 1 is MQA), the h mod g = 0 rule, the
+ *                  cache element-count formula, the multiplication counts and
+ *                  the lab description (contiguous query-head groups, K/V
+ *                  repeated per query head).
+ *   [LLM-inf-05]   "LLM inference 05" notes (albangk): the prefill/decode
+ *                  table, the per-layer decode pseudocode (push K, push V,
+ *                  then attend) and the bytes-per-token arithmetic.
+ *
+ * What is computed is the plain definition, written out with no blocking,
+ * fusion or reordering:
+ *   for every sequence b and query head i (G = h/g query heads per KV head,
+ *   j = floor(i / G)):
+ *     s_t   = scale * sum_k q[b,i,k] * K[b,j,t,k]          t < L_b
+ *     w_t   = exp(s_t - max_u s_u) / sum_u exp(s_u - max_u s_u)
+ *     o[v]  = sum_t w_t * V[b,j,t,v]
+ * Subtracting the maximum logit leaves the softmax unchanged mathematically
+ * and keeps exp() finite; it is the one reading added to the pages' softmax.
+ *
+ * Element types: 0 = IEEE fp32, 1 = bf16 given as raw 16-bit patterns (the
+ * upper half of an fp32). Both are widened to double exactly.
+ *
+ * Build: gcc -O2 -fopenmp -ffp-contract=off -fPIC -shared (no fused
+ * multiply-add contraction, so every product and sum is one double rounding).
+ */
+#include <math.h>
+#include <omp.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORC_F32 0
+#define ORC_BF16 1
+
+#define ORC_OK 0
+#define ORC_ERR_ARG (-1)
+#define ORC_ERR_GROUPS (-2)
+#define ORC_ERR_UNSUPPORTED (-3)
+#define ORC_ERR_CAPACITY (-4)
+
+static size_t elem_size(int dtype) { return dtype == ORC_F32 ? 4u : 2u; }
+
+/* Exact widening of one stored element to double. */
+static double widen(const void* base, size_t idx, int dtype) {
+  if (dtype == ORC_F32) return (double)((const float*)base)[idx];
+  uint32_t bits = (uint32_t)((const uint16_t*)base)[idx] << 16;
+  float f;
+  memcpy(&f, &bits, sizeof f);
+  return (double)f;
+}
+
+/*
+ * Cache element count for one model: 2 (K and V) x layers x KV heads x
+ * length x head dimension [GQA-lesson, section on what shrinks and what
+ * does not]. The query-head count does not appear.
+ */
+int64_t oracle_kv_cache_elems(int64_t layers, int64_t kv_heads, int64_t length,
+                              int64_t head_dim) {
+  return 2 * layers * kv_heads * length * head_dim;
+}
+
+/*
+ * Bytes one token leaves in the cache: 2 x layers x KV heads x head dim x
+ * bytes per element [LLM-inf-05, memory arithmetic under "more depth"].
+ */
+int64_t oracle_kv_bytes_per_token(int64_t layers, int64_t kv_heads,
+                                  int64_t head_dim, int64_t elem_bytes) {
+  return oracle_kv_cache_elems(layers, kv_heads, 1, head_dim) * elem_bytes;
+}
+
+/*
+ * Append one token per sequence: the new key and value rows of every KV head
+ * are stored at position lens[b] and the length grows by one
+ * [MQA-review §2.4 and §3: the new row is concatenated on the position axis;
+ * LLM-inf-05 decode pseudocode: push K, push V, then attend].
+ *
+ * Caches are [b][g][cap][d_k] and [b][g][cap][d_v]; k_new is [b][g][d_k] and
+ * v_new is [b][g][d_v]; all in the same element type. The copy is of raw
+ * bits. Returns ORC_ERR_CAPACITY (and changes nothing) if any
+ * lens[b] is outside [0, cap).
+ */
+int oracle_kv_append(void* k_cache, void* v_cache, const void* k_new,
+                     const void* v_new, int32_t* lens, int b, int g, int d_k,
+                     int d_v, int cap, int dtype) {
+  if (!k_cache || !v_cache || !k_new || !v_new || !lens) return ORC_ERR_ARG;
+  if (b <= 0 || g <= 0 || d_k <= 0 || d_v <= 0 || cap <= 0) return ORC_ERR_ARG;
+  if (dtype != ORC_F32 && dtype != ORC_BF16) return ORC_ERR_UNSUPPORTED;
+  for (int s = 0; s < b; ++s)
+    if (lens[s] < 0 || lens[s] >= cap) return ORC_ERR_CAPACITY;
+  const size_t es = elem_size(dtype);
+  char* kc = (char*)k_cache;
+  char* vc = (char*)v_cache;
+  for (int s = 0; s < b; ++s) {
+    const size_t pos = (size_t)lens[s];
+    for (int j = 0; j < g; ++j) {
+      const size_t head = (size_t)s * g + j;
+      memcpy(kc + ((head * cap + pos) * d_k) * es,
+             (const char*)k_new + head * d_k * es, (size_t)d_k * es);
+      memcpy(vc + ((head * cap + pos) * d_v) * es,
+             (const char*)v_new + head * d_v * es, (size_t)d_v * es);
+    }
+    lens[s] = (int32_t)(pos + 1);
+  }
+  return ORC_OK;
+}
+
+/*
+ * One decoding step of attention for every (sequence, query head).
+ *
+ * q is [b][h][d_k]; caches are [b][g][cap][d]; lens[b] is the number of
+ * cached positions attended by sequence b (the token appended this step
+ * included, [LLM-inf-05 decode description: the new position mixes all
+ * earlier positions and itself]). out is [b][h][d_v] in double.
+ *
+ * Query head i reads KV head j = floor(i / (h/g)): query heads form contiguous
+ * groups of h/g, which is the same as repeating each KV head h/g times along
+ * the head axis [GQA-lesson, lab description; g-knob table]. h must be a
+ * multiple of g [GQA-lesson, divisibility rule]; otherwise ORC_ERR_GROUPS.
+ *
+ * Per row: logits (k contraction of [MQA-review §2.1]), softmax, and the
+ * weighted sum over positions (the v contraction of §2.1). A sequence with
+ * lens[b] == 0 attends nothing and gets an all-zero output.
+ *
+ * weights (optional, may be NULL) receives w_t as [b][h][cap] (entries
+ * t >= lens[b] are set to 0). mul_count (optional) receives the number of
+ * multiplications performed by the two contractions, counted as they happen
+ * (the scale multiply and the softmax are not counted, following the
+ * per-term multiplication counts of [GQA-lesson]).
+ *
+ * threads: OpenMP threads over the independent (b, i) rows (<= 0: default).
+ */
+int oracle_decode_attention(double* out, double* weights, const void* q,
+                            const void* k_cache, const void* v_cache,
+                            const int32_t* lens, int b, int h, int g, int d_k,
+                            int d_v, int cap, float scale, int dtype,
+                            int64_t* mul_count, int threads) {
+  if (!out || !q || !k_cache || !v_cache || !lens) return ORC_ERR_ARG;
+  if (b <= 0 || h <= 0 || g <= 0 || d_k <= 0 || d_v <= 0 || cap <= 0)
+    return ORC_ERR_ARG;
+  if (h % g != 0) return ORC_ERR_GROUPS;
+  if (dtype != ORC_F32 && dtype != ORC_BF16) return ORC_ERR_UNSUPPORTED;
+  for (int s = 0; s < b; ++s)
+    if (lens[s] < 0 || lens[s] > cap) return ORC_ERR_CAPACITY;
+
+  const int G = h / g;
+  const double dscale = (double)scale;
+  const long rows = (long)b * h;
+  int64_t muls = 0;
+  int failed = 0;
+  const int nthreads = threads > 0 ? threads : omp_get_max_threads();
+
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads) reduction(+ : muls) reduction(| : failed)
+  for (long r = 0; r < rows; ++r) {
+    const int s = (int)(r / h);
+    const int i = (int)(r % h);
+    const int j = i / G;
+    const int L = lens[s];
+    double* o = out + (size_t)r * d_v;
+    double* wrow = weights ? weights + (size_t)r * cap : NULL;
+    for (int v = 0; v < d_v; ++v) o[v] = 0.0;
+    if (wrow)
+      for (int t = 0; t < cap; ++t) wrow[t] = 0.0;
+    if (L == 0) continue;
+
+    double* logit = (double*)malloc(sizeof(double) * (size_t)L);
+    if (!logit) {
+      failed = 1;
+      continue;
+    }
+    const size_t qoff = (size_t)r * d_k;
+    const size_t kvhead = (size_t)s * g + j;
+
+    /* logits: contraction over the key dimension, in index order */
+    for (int t = 0; t < L; ++t) {
+      const size_t krow = (kvhead * cap + t) * d_k;
+      double acc = 0.0;
+      for (int k = 0; k < d_k; ++k) {
+        acc += widen(q, qoff + k, dtype) * widen(k_cache, krow + k, dtype);
+        muls += 1;
+      }
+      logit[t] = dscale * acc;
+    }
+
+    /* softmax over positions, max-subtracted */
+    double mx = logit[0];
+    for (int t = 1; t < L; ++t)
+      if (logit[t] > mx) mx = logit[t];
+    double z = 0.0;
+    for (int t = 0; t < L; ++t) {
+      logit[t] = exp(logit[t] - mx);
+      z += logit[t];
+    }
+    for (int t = 0; t < L; ++t) logit[t] = logit[t] / z;
+    if (wrow)
+      for (int t = 0; t < L; ++t) wrow[t] = logit[t];
+
+    /* weighted sum of value rows, in position order */
+    for (int t = 0; t < L; ++t) {
+      const size_t vrow = (kvhead * cap + t) * d_v;
+      for (int v = 0; v < d_v; ++v) {
+        o[v] += logit[t] * widen(v_cache, vrow + v, dtype);
+        muls += 1;
+      }
+    }
+    free(logit);
+  }
+  if (mul_count) *mul_count = muls;
+  return failed ? ORC_ERR_ARG : ORC_OK;
+}
