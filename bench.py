@@ -1,0 +1,254 @@
+"""Decode-step benchmark: KV-read GB/s, fraction of the HBM roofline, steps/s.
+
+One step is the whole hot path on one batch: append one token of K/V per
+sequence (gqa_kv_append), then attention of every query head over its cache
+(gqa_decode_attention). Inputs are seeded synthetic caches of the named
+workload (default: one Llama-3-70B-shaped GQA layer, b=16, h=64, g=8, d=128,
+bf16, lengths uniform on [1024, 8192]), resident in HBM before timing starts.
+
+So that every step reads its K/V from HBM rather than from the 256 MB
+last-level cache, the benchmark keeps several independent cache sets (each
+its own seeded draw) and cycles through them, one set per step; each set's
+lengths grow by one per step it takes, as in a real decode loop.
+
+value = algorithmic KV bytes of all timed steps / wall time of those steps,
+where the bytes of one step are sum_b g * L_b * (d_k + d_v) * elem_bytes at
+the attended lengths L_b. roofline.achieved uses the same bytes per decode
+launch over the decode kernel's own average duration (HIP events around each
+launch, on the launch stream).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+METRIC = "KV-read GB/s and % of HBM roofline; decode-attention steps/sec"
+PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "decode_traffic.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "gqa_kv_cache_decode_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(workload: str):
+    """HBM bytes per decode launch from committed counter runs, if they match this source."""
+    try:
+        with open(PROFILE_TRAFFIC) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    entry = rec.get(workload)
+    if not entry or entry.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return entry.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(wl, batch_host, budget_s: float):
+    """Time the fp64 oracle (as it stands) on one full step of one cache set."""
+    import oracle
+
+    threads = max(1, min(16, len(os.sched_getaffinity(0))))
+    kc = batch_host.k_cache.copy()
+    vc = batch_host.v_cache.copy()
+    lens = batch_host.lens.copy()
+    q = batch_host.q(0)
+    kn, vn = batch_host.new_kv(0)
+    oracle.kv_append(kc, vc, kn, vn, lens)
+    kv_bytes = int(lens.sum()) * wl.g * 2 * wl.d * wl.elem_bytes
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.decode_attention(q, kc, vc, lens, wl.scale, threads=threads)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or reps >= 1000:
+            break
+    return {"value": round(kv_bytes * reps / el / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"{reps} repetition(s) of one full decode step (b={wl.b}, all sequences, "
+                      f"sum L={int(lens.sum())}) of cache set 0, fp64 oracle with {threads} OpenMP threads",
+            "seconds": round(el, 3)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--sets", type=int, default=0, help="cache sets to cycle (0: enough for >= 1.5 GB)")
+    ap.add_argument("--path", type=int, default=0, help="0 auto, 1 vector, 2 matrix")
+    ap.add_argument("--chunk", type=int, default=0, help="positions per workgroup (0: automatic)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle time budget (0: skip)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run a 1 GiB device copy first (reference for HBM byte counters)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (every box here has one GPU; "
+              "the sharded design is described in DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from gqa_kv_cache_decode_amd import api, inputs
+    from gqa_kv_cache_decode_amd.workloads import HEADLINE, WORKLOADS, kv_bytes_attended
+
+    wl = WORKLOADS[args.workload or HEADLINE]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    total_steps = args.warmup + args.steps
+
+    # cache sets
+    set_bytes = wl.b * wl.g * wl.cap * wl.d * 2 * wl.elem_bytes
+    n_sets = args.sets or max(2, math.ceil(1.5e9 / set_bytes))
+    n_sets = min(n_sets, total_steps) if total_steps > 0 else 1
+    grow = math.ceil(total_steps / n_sets) + 1
+    log(f"workload {wl.name}: {n_sets} cache sets of {set_bytes / 1e6:.1f} MB")
+
+    def to_dev(a):
+        t = torch.from_numpy(a)
+        return (t.view(torch.bfloat16) if a.dtype == np.uint16 else t).to(dev)
+
+    sets = []
+    host0 = None
+    for r in range(n_sets):
+        batch = inputs.Batch(seed=wl.seed + 1000 * r, b=wl.b, h=wl.h, g=wl.g, d=wl.d,
+                             cap=wl.cap + grow, lens=wl.lens, dtype=wl.dtype, poison=False)
+        if r == 0:
+            host0 = batch
+        sets.append({
+            "kc": to_dev(batch.k_cache), "vc": to_dev(batch.v_cache),
+            "lens": torch.from_numpy(batch.lens.copy()).to(dev), "lens_h": batch.lens.copy(),
+            "cap": wl.cap + grow,
+        })
+        if r != 0:
+            del batch
+    log("caches resident")
+    cap = wl.cap + grow
+    max_len_bound = int(max(s["lens_h"].max() for s in sets)) + grow
+    ws = api.make_workspace(wl.b, wl.h, wl.g, wl.d, wl.d, max_len_bound, dt, dev)
+    out = torch.empty(wl.b, wl.h, wl.d, dtype=dt, device=dev)
+    qs = [to_dev(inputs.draw_q(wl.seed, s, wl.b, wl.h, wl.d, wl.dtype)) for s in range(min(total_steps, 64))]
+    news = []
+    for s in range(min(total_steps, 64)):
+        kn, vn = inputs.draw_new_kv(wl.seed, s, wl.b, wl.g, wl.d, wl.d, wl.dtype)
+        news.append((to_dev(kn), to_dev(vn)))
+
+    if args.calibrate_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    stream = torch.cuda.current_stream()
+
+    def step(i, ev_pair=None):
+        st = sets[i % n_sets]
+        kn, vn = news[i % len(news)]
+        max_len = int(st["lens_h"].max())
+        api.kv_append(st["kc"], st["vc"], kn, vn, st["lens"], max_len)
+        st["lens_h"] += 1
+        if ev_pair is not None:
+            ev_pair[0].record(stream)
+        api.decode_attention(out, qs[i % len(qs)], st["kc"], st["vc"], st["lens"], max_len + 1, wl.scale, ws,
+                             path=args.path, chunk_tokens=args.chunk)
+        if ev_pair is not None:
+            ev_pair[1].record(stream)
+        return kv_bytes_attended(wl.g, wl.d, wl.d, wl.elem_bytes, st["lens_h"])
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    log("warmup done")
+
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    total_bytes = 0
+    torch.cuda.synchronize()
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for k in range(args.steps):
+        total_bytes += step(args.warmup + k, evs[k])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    elapsed_ms = t_start.elapsed_time(t_end)
+    kern_ms = [a.elapsed_time(b) for a, b in evs]
+    kern_avg_ms = float(np.mean(kern_ms))
+    bytes_per_launch = total_bytes / args.steps
+    log(f"timed {args.steps} steps: {elapsed_ms:.3f} ms (host wall {wall * 1e3:.1f} ms); "
+        f"decode kernel avg {kern_avg_ms * 1e3:.2f} us, median {np.median(kern_ms) * 1e3:.2f} us")
+
+    value = total_bytes / (elapsed_ms / 1e3) / 1e9
+    achieved = bytes_per_launch / (kern_avg_ms / 1e3) / 1e9
+    plan_path, plan_chunk = api.plan(wl.b, wl.h, wl.g, wl.d, wl.d, cap, max_len_bound, dt, args.path, args.chunk)
+    traffic = traffic_from_profile(wl.name)
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        log("timing the CPU oracle ...")
+        cpu = cpu_baseline(wl, host0, args.cpu_seconds)
+
+    lens0 = host0.lens
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(elapsed_ms / args.steps, 5),
+        "steps_per_s": round(args.steps / (elapsed_ms / 1e3), 1),
+        "hbm_roofline_frac_of_step": round(value / HBM_PEAK_GBS, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": wl.name, "b": wl.b, "h": wl.h, "g": wl.g, "d_k": wl.d, "d_v": wl.d,
+            "lens": list(wl.lens) if isinstance(wl.lens, (list, tuple)) else wl.lens,
+            "lens_drawn_mean": float(lens0.mean()), "lens_drawn_min": int(lens0.min()),
+            "lens_drawn_max": int(lens0.max()), "cache_sets": n_sets, "seed": wl.seed,
+            "path": {1: "vector", 2: "matrix"}[plan_path], "chunk_tokens": plan_chunk,
+            "kv_bytes_per_step": int(bytes_per_launch),
+        },
+        "roofline": {
+            "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+            "kernel": "decode_matrix_kernel" if plan_path == 2 else "decode_vector_kernel",
+            "kernel_avg_us": round(kern_avg_ms * 1e3, 3),
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,114 @@
+"""Thin torch binding over the C ABI of include/gqa_decode.h.
+
+Argument marshalling only: tensors are checked for device, dtype, shape and
+contiguity, then their device pointers and sizes go to libgqa_decode.so on
+torch's current stream (or the stream given). Every step of the decode path
+runs in the library's HIP kernels.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from . import _lib
+from ._lib import PATH_AUTO, PATH_MATRIX, PATH_VECTOR  # noqa: F401  (re-exported)
+
+_DTYPES = {torch.float32: _lib.F32, torch.bfloat16: _lib.BF16}
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    try:
+        return _DTYPES[t.dtype]
+    except KeyError:
+        raise TypeError(f"unsupported element type {t.dtype}; use float32 or bfloat16") from None
+
+
+def _stream_handle(stream) -> ctypes.c_void_p:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check_gpu(*tensors: torch.Tensor) -> None:
+    dev = tensors[0].device
+    for t in tensors:
+        if t.device.type != "cuda" or t.device != dev:
+            raise ValueError("all tensors must live on the same GPU")
+        if not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous")
+
+
+def kv_append(k_cache: torch.Tensor, v_cache: torch.Tensor, k_new: torch.Tensor,
+              v_new: torch.Tensor, lens: torch.Tensor, max_len: int, stream=None) -> None:
+    """Store k_new [b,g,d_k] / v_new [b,g,d_v] at slot lens[s] of each sequence; lens += 1.
+
+    max_len: host-side upper bound of lens before the call.
+    """
+    _check_gpu(k_cache, v_cache, k_new, v_new, lens)
+    if lens.dtype != torch.int32:
+        raise TypeError("lens must be int32")
+    b, g, cap, d_k = k_cache.shape
+    d_v = v_cache.shape[3]
+    if tuple(v_cache.shape) != (b, g, cap, d_v) or tuple(k_new.shape) != (b, g, d_k) \
+            or tuple(v_new.shape) != (b, g, d_v) or tuple(lens.shape) != (b,):
+        raise ValueError("kv_append: inconsistent shapes")
+    dt = _dtype_code(k_cache)
+    if any(_dtype_code(t) != dt for t in (v_cache, k_new, v_new)):
+        raise TypeError("caches and new rows must share one element type")
+    lib = _lib.load()
+    rc = lib.gqa_kv_append(k_cache.data_ptr(), v_cache.data_ptr(), k_new.data_ptr(),
+                           v_new.data_ptr(), lens.data_ptr(), b, g, d_k, d_v, cap, int(max_len),
+                           dt, _stream_handle(stream))
+    _lib.check(rc, "gqa_kv_append")
+
+
+def workspace_size(b: int, h: int, g: int, d_k: int, d_v: int, max_len: int, dtype: torch.dtype) -> int:
+    n = _lib.load().gqa_decode_workspace_size(b, h, g, d_k, d_v, int(max_len), _DTYPES[dtype])
+    if n == 0:
+        raise ValueError("gqa_decode_workspace_size rejected the shape")
+    return int(n)
+
+
+def make_workspace(b: int, h: int, g: int, d_k: int, d_v: int, max_len: int, dtype: torch.dtype,
+                   device) -> torch.Tensor:
+    """A zero-filled workspace (the library keeps its counters zero between calls)."""
+    return torch.zeros(workspace_size(b, h, g, d_k, d_v, max_len, dtype), dtype=torch.uint8, device=device)
+
+
+def plan(b, h, g, d_k, d_v, cap, max_len, dtype: torch.dtype, path=PATH_AUTO, chunk_tokens=0):
+    """(path, chunk_tokens) the library would launch with; no GPU work."""
+    lib = _lib.load()
+    p, c = ctypes.c_int(0), ctypes.c_int(0)
+    rc = lib.gqa_decode_plan(b, h, g, d_k, d_v, cap, int(max_len), _DTYPES[dtype], path, chunk_tokens,
+                             ctypes.byref(p), ctypes.byref(c))
+    _lib.check(rc, "gqa_decode_plan")
+    return p.value, c.value
+
+
+def decode_attention(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                     lens: torch.Tensor, max_len: int, scale: float, workspace: torch.Tensor,
+                     path: int = PATH_AUTO, chunk_tokens: int = 0, stream=None) -> torch.Tensor:
+    """out[s,i] = softmax_t(scale * q[s,i] . K[s,j,t]) @ V[s,j,t], t < lens[s], j = i // (h/g).
+
+    q [b,h,d_k], caches [b,g,cap,d], lens int32 [b] (attended lengths), out [b,h,d_v].
+    """
+    _check_gpu(out, q, k_cache, v_cache, lens, workspace)
+    if lens.dtype != torch.int32:
+        raise TypeError("lens must be int32")
+    b, h, d_k = q.shape
+    bk, g, cap, dk2 = k_cache.shape
+    d_v = v_cache.shape[3]
+    if bk != b or dk2 != d_k or tuple(v_cache.shape) != (b, g, cap, d_v) \
+            or tuple(out.shape) != (b, h, d_v) or tuple(lens.shape) != (b,):
+        raise ValueError("decode_attention: inconsistent shapes")
+    dt = _dtype_code(q)
+    if any(_dtype_code(t) != dt for t in (k_cache, v_cache, out)):
+        raise TypeError("q, caches and out must share one element type")
+    lib = _lib.load()
+    rc = lib.gqa_decode_attention_ex(
+        out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), lens.data_ptr(),
+        b, h, g, d_k, d_v, cap, int(max_len), ctypes.c_float(scale), dt,
+        workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream_handle(stream),
+        path, chunk_tokens)
+    _lib.check(rc, "gqa_decode_attention")
+    return out

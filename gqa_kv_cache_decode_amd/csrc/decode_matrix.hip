@@ -1,0 +1,256 @@
+// Matrix-core (MFMA) split-K decode attention: bf16 K/V/q, d_k = d_v = 128,
+// fp32 accumulation, up to 64 query heads per KV head.
+//
+// Same result as the vector path (MQA review §2.1 per query head over the
+// cache of §2.4 / §3; contiguous head groups of the TF2 GQA lesson). Both
+// contractions of a G-head group against a 32-position tile are small dense
+// matrix products, so they run on v_mfma_f32_16x16x32_bf16 with the G query
+// heads padded to 16 (NB blocks of 16 heads):
+//
+//   scores  S^T[t][i] = sum_k K[t][k] * Q^T[k][i]   A = K tile, B = Q^T
+//   output  O^T[v][i] += sum_t V^T[v][t] * P^T[t][i] A = V^T tile, B = P^T
+//
+// Operand layout of the 16x16x32 MFMA (A: 16 rows x 32 k, B: 32 k x 16
+// columns, C: 16 x 16): lane l supplies row / column (l % 16) and the 8
+// k-slots of group (l / 16); lane l receives C rows 4*(l/16) .. +3 of column
+// l % 16. The contraction only needs A and B to agree on which k each
+// (group, slot) stands for, which is how the kernel picks K dims and V
+// positions freely:
+//
+// * K: lane (n = l%16, q = l/16) loads 16 bytes of row 16*sigma + n (sigma =
+//   sub-tile 0/1) at dims 32*ks + 8*q, ks = 0..3: exactly the A operand.
+// * The score MFMA leaves lane (n, q) with positions 16*sigma + 4q + 0..3 of
+//   head n: these 8 probabilities, packed to bf16, are the B operand of the
+//   value MFMA for k-group q, with k-slot r <-> position tau(q, r) =
+//   4q + r (r < 4) or 16 + 4q + (r - 4).
+// * V: lane (n, q) loads 16 bytes (dims 8n .. 8n+7) of the 8 rows tau(q, r);
+//   a quarter-wave reads whole 256-byte rows. An 8 x 8 transpose of 16-bit
+//   values inside the lane gives, for each e = 0..7, the 8 positions of dim
+//   8n + e: the A operand of value MFMA e, whose output row m is dim 8m + e.
+//   Lane (n, q) therefore accumulates dims 32q .. 32q + 31 of head n.
+//
+// Each wave walks its own 32-position tiles of the chunk with an online
+// softmax (base 2, running max per head shared by the 4 lanes of a head);
+// the four waves are merged through LDS and finish_chunk handles the split.
+#include "gqa_internal.hpp"
+
+namespace gqa {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int D = 128;
+constexpr int TILE = 32;
+constexpr int OPAD = 4;  // LDS row padding (floats) against bank conflicts
+
+__device__ __forceinline__ u32x4 load16(const uint16_t* ptr) {
+  return *reinterpret_cast<const u32x4*>(ptr);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// Value-MFMA A operand e from the 8 loaded V rows (vr[r] holds dims 8n..8n+7
+// of position tau(q, r)): dword k = (dim 8n+e of row 2k, of row 2k+1).
+template <int E>
+__device__ __forceinline__ bf16x8 v_transpose(const u32x4* vr) {
+  u32x4 a;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t x = vr[2 * k][E / 2];
+    const uint32_t y = vr[2 * k + 1][E / 2];
+    if constexpr ((E & 1) == 0) a[k] = (x & 0xffffu) | (y << 16);
+    else a[k] = (x >> 16) | (y & 0xffff0000u);
+  }
+  return as_bf16x8(a);
+}
+
+template <int NB>
+__global__ __launch_bounds__(kThreads) void decode_matrix_kernel(DecodeParams p) {
+  __shared__ float sm_m[kWaves][16];
+  __shared__ float sm_l[kWaves][16];
+  __shared__ float sm_o[kWaves][16][D + OPAD];
+  __shared__ float fin_m[NB * 16];
+  __shared__ float fin_l[NB * 16];
+  __shared__ float fin_o[NB * 16][D];
+  __shared__ int s_flag;
+
+  const int c = blockIdx.x;
+  const int j = blockIdx.y;
+  const int s = blockIdx.z;
+  const int G = p.G;
+  const int i0 = j * G;
+  const int L = attended_len(p, s);
+  if (L == 0) {
+    if (c == 0) write_zero_rows<uint16_t>(p, s, i0, G);
+    return;
+  }
+  const int n_valid = (L + p.chunk - 1) / p.chunk;
+  if (c >= n_valid) return;
+  const int t_begin = c * p.chunk;
+  const int t_end = min(L, t_begin + p.chunk);
+
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int n16 = lane & 15;
+  const int q4 = lane >> 4;
+
+  // Q^T operands: head nb*16 + n16, dims 32*ks + 8*q4 .. +7 (zero for padding heads).
+  bf16x8 qop[NB][4];
+  const uint16_t* qg = static_cast<const uint16_t*>(p.q) + (size_t(s) * p.h + i0) * D;
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const int head = nb * 16 + n16;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (head < G) v = load16(qg + size_t(head) * D + ks * 32 + q4 * 8);
+      qop[nb][ks] = as_bf16x8(v);
+    }
+  }
+
+  f32x4 oacc[NB][8];
+  float mrun[NB], lrun[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    mrun[nb] = kNegInf;
+    lrun[nb] = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) oacc[nb][e] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  }
+
+  const size_t kv_head = size_t(s) * p.g + j;
+  const uint16_t* kbase = static_cast<const uint16_t*>(p.k_cache) + kv_head * p.cap * D;
+  const uint16_t* vbase = static_cast<const uint16_t*>(p.v_cache) + kv_head * p.cap * D;
+  const float sl2 = p.scale_log2;
+
+  for (int t0 = t_begin + w * TILE; t0 < t_end; t0 += kWaves * TILE) {
+    const int nvalid = min(TILE, t_end - t0);
+    // ---- loads
+    u32x4 kr[2][4];
+#pragma unroll
+    for (int sg = 0; sg < 2; ++sg) {
+      const int row = 16 * sg + n16;
+      const uint16_t* kp = kbase + size_t(t0 + row) * D + q4 * 8;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        if (row < nvalid) kr[sg][ks] = load16(kp + ks * 32);
+        else kr[sg][ks] = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+    u32x4 vr[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const int row = (r < 4) ? (4 * q4 + r) : (16 + 4 * q4 + (r - 4));
+      if (row < nvalid) vr[r] = load16(vbase + size_t(t0 + row) * D + n16 * 8);
+      else vr[r] = u32x4{0u, 0u, 0u, 0u};
+    }
+    // ---- scores and online softmax, per 16-head block
+    bf16x8 pop[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      float sv[8];
+#pragma unroll
+      for (int sg = 0; sg < 2; ++sg) {
+        f32x4 sacc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+          sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kr[sg][ks]), qop[nb][ks], sacc, 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = 16 * sg + 4 * q4 + i;
+          sv[sg * 4 + i] = (row < nvalid) ? sacc[i] * sl2 : kNegInf;
+        }
+      }
+      float mx = sv[0];
+#pragma unroll
+      for (int k = 1; k < 8; ++k) mx = fmaxf(mx, sv[k]);
+      mx = fmaxf(mx, xor_shuffle(mx, 16));
+      mx = fmaxf(mx, xor_shuffle(mx, 32));
+      const float mn = fmaxf(mrun[nb], mx);
+      const float sub = (mn == kNegInf) ? 0.0f : mn;
+      const float alpha = fast_exp2(mrun[nb] - sub);
+      mrun[nb] = mn;
+      float psum = 0.0f;
+      bf16x8 pk;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const float pv = fast_exp2(sv[k] - sub);
+        const __bf16 pb = static_cast<__bf16>(pv);
+        pk[k] = pb;
+        psum += static_cast<float>(pb);  // the denominator sums the weights actually applied
+      }
+      pop[nb] = pk;
+      lrun[nb] = fmaf(lrun[nb], alpha, psum);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) oacc[nb][e] *= alpha;
+    }
+    // ---- weighted sum of V
+#define GQA_PV_STEP(E)                                                                   \
+    {                                                                                    \
+      const bf16x8 va = v_transpose<E>(vr);                                              \
+      _Pragma("unroll") for (int nb = 0; nb < NB; ++nb)                                  \
+        oacc[nb][E] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pop[nb], oacc[nb][E], 0, 0, 0); \
+    }
+    GQA_PV_STEP(0) GQA_PV_STEP(1) GQA_PV_STEP(2) GQA_PV_STEP(3)
+    GQA_PV_STEP(4) GQA_PV_STEP(5) GQA_PV_STEP(6) GQA_PV_STEP(7)
+#undef GQA_PV_STEP
+  }
+
+  // ---- merge the four waves through LDS, one 16-head block at a time
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    float lsum = lrun[nb];
+    lsum += xor_shuffle(lsum, 16);
+    lsum += xor_shuffle(lsum, 32);
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sm_o[w][n16][32 * q4 + 8 * i + e] = oacc[nb][e][i];
+    if (q4 == 0) {
+      sm_m[w][n16] = mrun[nb];
+      sm_l[w][n16] = lsum;
+    }
+    __syncthreads();
+    const int nh_blk = min(16, G - nb * 16);
+    for (int idx = threadIdx.x; idx < nh_blk * D; idx += kThreads) {
+      const int hh = idx / D, dd = idx - hh * D;
+      float M = sm_m[0][hh];
+#pragma unroll
+      for (int ww = 1; ww < kWaves; ++ww) M = fmaxf(M, sm_m[ww][hh]);
+      const float sub = (M == kNegInf) ? 0.0f : M;
+      float o = 0.0f, ls = 0.0f;
+#pragma unroll
+      for (int ww = 0; ww < kWaves; ++ww) {
+        const float wgt = fast_exp2(sm_m[ww][hh] - sub);
+        o = fmaf(wgt, sm_o[ww][hh][dd], o);
+        ls = fmaf(wgt, sm_l[ww][hh], ls);
+      }
+      fin_o[nb * 16 + hh][dd] = o;
+      if (dd == 0) {
+        fin_m[nb * 16 + hh] = M;
+        fin_l[nb * 16 + hh] = ls;
+      }
+    }
+    __syncthreads();
+  }
+  finish_chunk<uint16_t>(p, s, i0, G, c, n_valid, fin_m, fin_l, &fin_o[0][0], &s_flag);
+}
+
+}  // namespace
+
+hipError_t launch_decode_matrix(const DecodeParams& p, hipStream_t stream) {
+  const int n_chunks = (p.max_len + p.chunk - 1) / p.chunk;
+  const dim3 grid(n_chunks > 0 ? n_chunks : 1, p.g, p.b);
+  if (p.G <= 16) {
+    hipLaunchKernelGGL(decode_matrix_kernel<1>, grid, dim3(kThreads), 0, stream, p);
+  } else if (p.G <= 32) {
+    hipLaunchKernelGGL(decode_matrix_kernel<2>, grid, dim3(kThreads), 0, stream, p);
+  } else {
+    hipLaunchKernelGGL(decode_matrix_kernel<4>, grid, dim3(kThreads), 0, stream, p);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace gqa

@@ -1,0 +1,192 @@
+// C-ABI shim of libgqa_decode: argument checks, workspace sizing, launch
+// planning and dispatch. Every check runs on the host before anything is
+// enqueued, so each error path is reachable without a GPU.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <string>
+
+#include "../../include/gqa_decode.h"
+#include "gqa_internal.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int ok() {
+  g_last_error.clear();
+  return GQA_OK;
+}
+
+constexpr int kMaxBatch = 65535;
+constexpr int kMaxHeads = 4096;
+constexpr int kMaxLen = 1 << 28;
+constexpr float kLog2e = 1.4426950408889634f;
+// Workgroups the automatic chunk size aims for: eight per compute unit of an
+// MI355X (256 CUs), counted over the launch's upper bound of positions.
+constexpr long long kTargetWorkgroups = 8LL * 256;
+
+bool supported_head_dim(int d) { return d == 16 || d == 32 || d == 64 || d == 128 || d == 256; }
+
+struct Plan {
+  int path;
+  int chunk;
+  int heads_per_block;
+};
+
+// Shared shape checks of the decode entry points (pointers are checked by the
+// callers). Fills plan on success.
+int plan_decode(int b, int h, int g, int d_k, int d_v, int cap, int max_len, int dtype,
+                int path, int chunk_tokens, Plan* plan) {
+  if (b <= 0 || b > kMaxBatch) return fail(GQA_ERR_ARG, "b=%d must be in [1, %d]", b, kMaxBatch);
+  if (h <= 0 || h > kMaxHeads) return fail(GQA_ERR_ARG, "h=%d must be in [1, %d]", h, kMaxHeads);
+  if (g <= 0) return fail(GQA_ERR_ARG, "g=%d must be positive", g);
+  if (d_k <= 0 || d_v <= 0) return fail(GQA_ERR_ARG, "d_k=%d, d_v=%d must be positive", d_k, d_v);
+  if (cap <= 0) return fail(GQA_ERR_ARG, "cap=%d must be positive", cap);
+  if (max_len < 0) return fail(GQA_ERR_ARG, "max_len=%d must be >= 0", max_len);
+  if (h % g != 0)
+    return fail(GQA_ERR_GROUPS, "h=%d query heads cannot be split into g=%d equal groups", h, g);
+  if (dtype != GQA_DTYPE_F32 && dtype != GQA_DTYPE_BF16)
+    return fail(GQA_ERR_UNSUPPORTED, "dtype=%d is not GQA_DTYPE_F32 or GQA_DTYPE_BF16", dtype);
+  if (d_k != d_v || !supported_head_dim(d_k))
+    return fail(GQA_ERR_UNSUPPORTED, "head dims d_k=%d, d_v=%d: need d_k == d_v in {16,32,64,128,256}",
+                d_k, d_v);
+  if (max_len > cap) return fail(GQA_ERR_CAPACITY, "max_len=%d exceeds cap=%d", max_len, cap);
+  if (max_len > kMaxLen) return fail(GQA_ERR_UNSUPPORTED, "max_len=%d exceeds %d", max_len, kMaxLen);
+  if (path != GQA_PATH_AUTO && path != GQA_PATH_VECTOR && path != GQA_PATH_MATRIX)
+    return fail(GQA_ERR_UNSUPPORTED, "path=%d is not a GQA_PATH_* value", path);
+  if (chunk_tokens != 0 &&
+      (chunk_tokens < gqa::kMinChunk || chunk_tokens > gqa::kMaxChunk || chunk_tokens % gqa::kMinChunk))
+    return fail(GQA_ERR_UNSUPPORTED, "chunk_tokens=%d must be 0 or a multiple of %d in [%d, %d]",
+                chunk_tokens, gqa::kMinChunk, gqa::kMinChunk, gqa::kMaxChunk);
+
+  const int G = h / g;
+  const bool matrix_ok = dtype == GQA_DTYPE_BF16 && d_k == 128 && G <= 64;
+  if (path == GQA_PATH_MATRIX && !matrix_ok)
+    return fail(GQA_ERR_UNSUPPORTED, "matrix path needs bf16, d=128 and at most 64 heads per KV head");
+  int chosen = path;
+  if (chosen == GQA_PATH_AUTO) chosen = (matrix_ok && G >= 3) ? GQA_PATH_MATRIX : GQA_PATH_VECTOR;
+
+  const int hpb = chosen == GQA_PATH_MATRIX ? G : gqa::vector_heads_per_block(G);
+  const int nhb = (G + hpb - 1) / hpb;
+  int chunk = chunk_tokens;
+  if (chunk == 0) {
+    const long long units = (long long)b * g * nhb * (long long)(max_len > 0 ? max_len : 1);
+    long long want = (units + kTargetWorkgroups - 1) / kTargetWorkgroups;
+    want = (want + gqa::kMinChunk - 1) / gqa::kMinChunk * gqa::kMinChunk;
+    if (want < gqa::kMinChunk) want = gqa::kMinChunk;
+    if (want > 1024) want = 1024;
+    chunk = (int)want;
+  }
+  plan->path = chosen;
+  plan->chunk = chunk;
+  plan->heads_per_block = hpb;
+  return GQA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* gqa_last_error(void) { return g_last_error.c_str(); }
+
+int gqa_kv_append(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
+                  int32_t* lens, int b, int g, int d_k, int d_v, int cap, int max_len,
+                  int dtype, void* stream) {
+  if (!k_cache || !v_cache || !k_new || !v_new || !lens)
+    return fail(GQA_ERR_ARG, "gqa_kv_append: null pointer argument");
+  if (b <= 0 || b > kMaxBatch) return fail(GQA_ERR_ARG, "b=%d must be in [1, %d]", b, kMaxBatch);
+  if (g <= 0 || d_k <= 0 || d_v <= 0 || cap <= 0)
+    return fail(GQA_ERR_ARG, "g=%d, d_k=%d, d_v=%d, cap=%d must be positive", g, d_k, d_v, cap);
+  if (max_len < 0) return fail(GQA_ERR_ARG, "max_len=%d must be >= 0", max_len);
+  if (dtype != GQA_DTYPE_F32 && dtype != GQA_DTYPE_BF16)
+    return fail(GQA_ERR_UNSUPPORTED, "dtype=%d is not GQA_DTYPE_F32 or GQA_DTYPE_BF16", dtype);
+  if ((long long)max_len + 1 > cap)
+    return fail(GQA_ERR_CAPACITY, "appending to max_len=%d needs cap > %d, cap=%d", max_len, max_len, cap);
+  gqa::AppendParams p{k_cache, v_cache, k_new, v_new, lens, g, d_k, d_v, cap};
+  const hipError_t e = gqa::launch_append(p, b, dtype, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(GQA_ERR_HIP, "gqa_kv_append launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+size_t gqa_decode_workspace_size(int b, int h, int g, int d_k, int d_v, int max_len, int dtype) {
+  if (b <= 0 || b > kMaxBatch || h <= 0 || h > kMaxHeads || g <= 0 || h % g != 0 || d_k <= 0 ||
+      d_v <= 0 || max_len < 0 || max_len > kMaxLen || (dtype != GQA_DTYPE_F32 && dtype != GQA_DTYPE_BF16))
+    return 0;
+  return gqa::workspace_layout(b, h, d_v, max_len).total;
+}
+
+int gqa_decode_plan(int b, int h, int g, int d_k, int d_v, int cap, int max_len, int dtype,
+                    int path, int chunk_tokens, int* chosen_path, int* chosen_chunk_tokens) {
+  Plan plan;
+  const int rc = plan_decode(b, h, g, d_k, d_v, cap, max_len, dtype, path, chunk_tokens, &plan);
+  if (rc != GQA_OK) return rc;
+  if (chosen_path) *chosen_path = plan.path;
+  if (chosen_chunk_tokens) *chosen_chunk_tokens = plan.chunk;
+  return ok();
+}
+
+int gqa_decode_attention_ex(void* out, const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* lens, int b, int h, int g, int d_k, int d_v, int cap,
+                            int max_len, float scale, int dtype, void* workspace,
+                            size_t workspace_bytes, void* stream, int path, int chunk_tokens) {
+  if (!out || !q || !k_cache || !v_cache || !lens)
+    return fail(GQA_ERR_ARG, "gqa_decode_attention: null pointer argument");
+  Plan plan;
+  const int rc = plan_decode(b, h, g, d_k, d_v, cap, max_len, dtype, path, chunk_tokens, &plan);
+  if (rc != GQA_OK) return rc;
+  const gqa::WorkspaceLayout ws = gqa::workspace_layout(b, h, d_v, max_len);
+  if (!workspace) return fail(GQA_ERR_WORKSPACE, "workspace is null (%zu bytes needed)", ws.total);
+  if (workspace_bytes < ws.total)
+    return fail(GQA_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, ws.total);
+  if (reinterpret_cast<uintptr_t>(workspace) & 255)
+    return fail(GQA_ERR_ARG, "workspace must be 256-byte aligned");
+
+  gqa::DecodeParams p;
+  p.out = out;
+  p.q = q;
+  p.k_cache = k_cache;
+  p.v_cache = v_cache;
+  p.lens = lens;
+  char* wsb = static_cast<char*>(workspace);
+  p.ws_cnt = reinterpret_cast<int*>(wsb + ws.cnt_off);
+  p.ws_ml = reinterpret_cast<float*>(wsb + ws.ml_off);
+  p.ws_o = reinterpret_cast<float*>(wsb + ws.o_off);
+  p.b = b;
+  p.h = h;
+  p.g = g;
+  p.G = h / g;
+  p.d = d_k;
+  p.cap = cap;
+  p.max_len = max_len;
+  p.chunk = plan.chunk;
+  p.nch_stride = gqa::nch_stride_for(max_len);
+  p.scale_log2 = scale * kLog2e;
+
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  const hipError_t e = plan.path == GQA_PATH_MATRIX
+                           ? gqa::launch_decode_matrix(p, st)
+                           : gqa::launch_decode_vector(p, dtype, plan.heads_per_block, st);
+  if (e != hipSuccess) return fail(GQA_ERR_HIP, "gqa_decode_attention launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int gqa_decode_attention(void* out, const void* q, const void* k_cache, const void* v_cache,
+                         const int32_t* lens, int b, int h, int g, int d_k, int d_v, int cap,
+                         int max_len, float scale, int dtype, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  return gqa_decode_attention_ex(out, q, k_cache, v_cache, lens, b, h, g, d_k, d_v, cap, max_len,
+                                 scale, dtype, workspace, workspace_bytes, stream, GQA_PATH_AUTO, 0);
+}
+
+}  // extern "C"

@@ -1,0 +1,162 @@
+/*
+ * gqa_decode.h - C ABI of the MI355X (gfx950) incremental-decoding attention
+ * library for multi-head, grouped-query and multi-query attention.
+ *
+ * One decoding step of one attention layer, with the projections left to the
+ * caller, is:
+ *
+ *   gqa_kv_append(...)          store the new token's K and V rows in the cache
+ *   gqa_decode_attention(...)   let the new token's h query heads attend over
+ *                               every cached position, the new one included
+ *
+ * in that order on one stream. This is the per-layer decode loop of the
+ * "LLM inference 05" notes (albangk): push K, push V, then attend; and the
+ * incremental attention of the "Fast Transformer Decoding: One Write-Head is
+ * All You Need" review (velog), §2.4 Multi-head Attention (Incremental) and
+ * §3 Multi Query Attention, with the projections removed.
+ *
+ * Grouping (the "TF2 GQA" lesson, ttlab: the g-knob table and the lab): h
+ * query heads share g KV heads; g = h is MHA, g = 1 is MQA, and h must be a
+ * multiple of g. Query head i reads KV head floor(i / (h/g)), i.e. query heads
+ * form contiguous groups.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every tensor pointer is a DEVICE pointer on the current HIP device, owned
+ *   by the caller. The library never allocates, frees or keeps device memory
+ *   and keeps no state between calls apart from a per-device attribute cache
+ *   and the calling thread's last error message.
+ * - All tensors are dense and row-major (C-contiguous) with the shapes given
+ *   below; element type is one of GQA_DTYPE_*; q, caches, new rows and out
+ *   share it.
+ * - Caches: K is [b][g][cap][d_k], V is [b][g][cap][d_v]. Position t of
+ *   sequence s, KV head j starts at element ((s*g + j)*cap + t)*d.
+ * - lens is an int32 [b] device array: the number of valid cache positions
+ *   of each sequence.
+ * - max_len is the caller's host-side upper bound of lens (see each call).
+ *   It sizes the launch; positions at or beyond min(lens[s], max_len) are
+ *   never read.
+ * - stream is a hipStream_t passed as void* (NULL: the null stream). Calls
+ *   are asynchronous on it: a return of GQA_OK means "enqueued".
+ * - All argument checks run on the host before anything is enqueued, so an
+ *   error return leaves every buffer untouched and enqueues nothing.
+ *   gqa_last_error() then describes the failure.
+ */
+#ifndef GQA_DECODE_H
+#define GQA_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element types. bf16 is stored as the upper 16 bits of an IEEE fp32. */
+#define GQA_DTYPE_F32 0
+#define GQA_DTYPE_BF16 1
+
+/* Status codes. */
+#define GQA_OK 0
+#define GQA_ERR_ARG (-1)         /* null pointer, or a size <= 0 / too large     */
+#define GQA_ERR_GROUPS (-2)      /* h is not a multiple of g                     */
+#define GQA_ERR_UNSUPPORTED (-3) /* dtype, head dims or options not supported    */
+#define GQA_ERR_CAPACITY (-4)    /* max_len (plus the appended token) > cap      */
+#define GQA_ERR_WORKSPACE (-5)   /* workspace missing or smaller than required   */
+#define GQA_ERR_HIP (-6)         /* the HIP runtime refused a launch or a query  */
+
+/* Path selection for gqa_decode_attention_ex. */
+#define GQA_PATH_AUTO 0
+#define GQA_PATH_VECTOR 1 /* vector-ALU kernel: every supported shape and dtype   */
+#define GQA_PATH_MATRIX 2 /* MFMA kernel: bf16, d_k = d_v = 128, up to 64 heads/KV */
+
+/*
+ * Append one token per sequence ("LLM inference 05": push K, push V;
+ * MQA review §2.4 / §3: the new row is concatenated on the position axis).
+ *
+ * For every sequence s and KV head j < g, with p = lens[s]:
+ *   K[s][j][p][:] = k_new[s][j][:]   (d_k elements, copied bit for bit)
+ *   V[s][j][p][:] = v_new[s][j][:]   (d_v elements)
+ * then lens[s] = p + 1.
+ *
+ * k_new: [b][g][d_k], v_new: [b][g][d_v] (device, read only).
+ * k_cache, v_cache, lens: device, updated in place.
+ * max_len: host upper bound of lens[s] BEFORE the call; max_len + 1 <= cap is
+ *   checked (GQA_ERR_CAPACITY).
+ * Device-side precondition: 0 <= lens[s] <= max_len. A sequence whose lens[s]
+ *   is outside [0, cap) is left untouched (nothing written, lens unchanged).
+ * Errors: GQA_ERR_ARG (null pointer, b/g/d/cap <= 0, b > 65535),
+ *   GQA_ERR_UNSUPPORTED (dtype), GQA_ERR_CAPACITY, GQA_ERR_HIP.
+ */
+int gqa_kv_append(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
+                  int32_t* lens, int b, int g, int d_k, int d_v, int cap, int max_len,
+                  int dtype, void* stream);
+
+/*
+ * Bytes of device workspace gqa_decode_attention needs for this shape; the
+ * value covers every path and chunk size, so one buffer serves all calls with
+ * shapes no larger than these. Returns 0 for invalid arguments.
+ *
+ * The workspace holds split-softmax partials and one int32 counter per
+ * (sequence, query head). The counters must be ZERO before the first call
+ * that uses a buffer (e.g. allocate it zero-filled); every call leaves them
+ * zero again. Two calls that share a workspace must be ordered (same stream
+ * or synchronised); calls with distinct workspaces may run concurrently.
+ */
+size_t gqa_decode_workspace_size(int b, int h, int g, int d_k, int d_v, int max_len, int dtype);
+
+/*
+ * Attention of one query token per sequence over its cache (MQA review §2.1
+ * Dot-Product Attention applied per query head, §2.4 / §3 for the cache):
+ *
+ *   for s < b, i < h, j = floor(i / (h/g)), L = min(lens[s], max_len):
+ *     w_t = softmax_t( scale * sum_k q[s][i][k] * K[s][j][t][k] ),  t < L
+ *     out[s][i][v] = sum_t w_t * V[s][j][t][v]
+ *
+ * q: [b][h][d_k], out: [b][h][d_v], in the input element type (bf16 outputs
+ * are rounded to nearest even from fp32 accumulation). A sequence with L = 0
+ * gets an all-zero output row.
+ * lens: attended lengths (AFTER this step's append). max_len: host upper bound
+ *   of lens, 0 <= max_len <= cap (GQA_ERR_CAPACITY otherwise).
+ * scale: multiplies every logit (1/sqrt(d_k) for the usual scaled attention;
+ *   1 reproduces the pages' unscaled einsum).
+ * workspace / workspace_bytes: see gqa_decode_workspace_size.
+ * Supported: dtype F32 or BF16; d_k == d_v in {16, 32, 64, 128, 256};
+ *   b <= 65535; h <= 4096.
+ * Errors: GQA_ERR_ARG, GQA_ERR_GROUPS, GQA_ERR_UNSUPPORTED, GQA_ERR_CAPACITY,
+ *   GQA_ERR_WORKSPACE, GQA_ERR_HIP.
+ */
+int gqa_decode_attention(void* out, const void* q, const void* k_cache, const void* v_cache,
+                         const int32_t* lens, int b, int h, int g, int d_k, int d_v, int cap,
+                         int max_len, float scale, int dtype, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
+/*
+ * gqa_decode_attention with explicit launch choices, for tests and tuning.
+ * path: GQA_PATH_AUTO / GQA_PATH_VECTOR / GQA_PATH_MATRIX (MATRIX on an
+ *   unsupported shape gives GQA_ERR_UNSUPPORTED).
+ * chunk_tokens: positions per workgroup; 0 = automatic, otherwise a multiple
+ *   of 64 in [64, 65536] (GQA_ERR_UNSUPPORTED otherwise).
+ * Results equal gqa_decode_attention's up to floating-point summation order.
+ */
+int gqa_decode_attention_ex(void* out, const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* lens, int b, int h, int g, int d_k, int d_v, int cap,
+                            int max_len, float scale, int dtype, void* workspace,
+                            size_t workspace_bytes, void* stream, int path, int chunk_tokens);
+
+/*
+ * Describe the launch gqa_decode_attention_ex would make, without enqueueing
+ * anything: writes the chosen path (GQA_PATH_VECTOR or GQA_PATH_MATRIX) and
+ * chunk size. Same argument checks as the real call, minus pointers.
+ */
+int gqa_decode_plan(int b, int h, int g, int d_k, int d_v, int cap, int max_len, int dtype,
+                    int path, int chunk_tokens, int* chosen_path, int* chosen_chunk_tokens);
+
+/* Message for the calling thread's last non-OK return ("" if none). */
+const char* gqa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GQA_DECODE_H */

@@ -1,0 +1,128 @@
+"""CPU checks of the C-ABI library: it loads, exports what the header
+declares, and rejects bad arguments on the host before touching a GPU.
+
+No call here launches work: each one fails argument validation, which runs
+before any HIP call, or is a pure host query (workspace size, plan).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from gqa_kv_cache_decode_amd import _lib, build
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "gqa_decode.h")
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(build.LIB_PATH):
+        build.build()
+    return _lib.load()
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gqa_\w+)\s*\(", text)))
+
+
+def test_exports_every_declared_function(lib):
+    names = _declared()
+    assert names, "no declarations parsed"
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(_lib.SIGNATURES)
+
+
+def test_header_status_codes_match_binding():
+    text = open(HEADER).read()
+    codes = dict(re.findall(r"#define (GQA_\w+) \(?(-?\d+)\)?", text))
+    assert int(codes["GQA_OK"]) == _lib.OK
+    for code, name in _lib.ERROR_NAMES.items():
+        assert int(codes[name]) == code
+    assert int(codes["GQA_PATH_MATRIX"]) == _lib.PATH_MATRIX
+    assert int(codes["GQA_DTYPE_BF16"]) == _lib.BF16
+
+
+def _attn(lib, **kw):
+    a = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, lens=FAKE, b=2, h=8, g=2, dk=128, dv=128, cap=100,
+             max_len=50, scale=0.1, dtype=_lib.BF16, ws=FAKE, ws_bytes=1 << 30, stream=None, path=0, chunk=0)
+    a.update(kw)
+    return lib.gqa_decode_attention_ex(a["out"], a["q"], a["k"], a["v"], a["lens"], a["b"], a["h"], a["g"],
+                                       a["dk"], a["dv"], a["cap"], a["max_len"], a["scale"], a["dtype"],
+                                       a["ws"], a["ws_bytes"], a["stream"], a["path"], a["chunk"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(h=8, g=3), _lib.ERR_GROUPS),
+    (dict(h=28, g=8), _lib.ERR_GROUPS),
+    (dict(out=None), _lib.ERR_ARG),
+    (dict(lens=None), _lib.ERR_ARG),
+    (dict(b=0), _lib.ERR_ARG),
+    (dict(b=70000), _lib.ERR_ARG),
+    (dict(g=0), _lib.ERR_ARG),
+    (dict(max_len=-1), _lib.ERR_ARG),
+    (dict(dk=96, dv=96), _lib.ERR_UNSUPPORTED),
+    (dict(dk=128, dv=64), _lib.ERR_UNSUPPORTED),
+    (dict(dtype=7), _lib.ERR_UNSUPPORTED),
+    (dict(max_len=101), _lib.ERR_CAPACITY),
+    (dict(ws=None), _lib.ERR_WORKSPACE),
+    (dict(ws_bytes=16), _lib.ERR_WORKSPACE),
+    (dict(ws=ctypes.c_void_p(0x1010)), _lib.ERR_ARG),
+    (dict(chunk=100), _lib.ERR_UNSUPPORTED),
+    (dict(chunk=32), _lib.ERR_UNSUPPORTED),
+    (dict(path=9), _lib.ERR_UNSUPPORTED),
+    (dict(path=_lib.PATH_MATRIX, dtype=_lib.F32), _lib.ERR_UNSUPPORTED),
+    (dict(path=_lib.PATH_MATRIX, dk=64, dv=64), _lib.ERR_UNSUPPORTED),
+    (dict(path=_lib.PATH_MATRIX, h=130, g=2), _lib.ERR_UNSUPPORTED),
+])
+def test_decode_rejects(lib, kw, code):
+    assert _attn(lib, **kw) == code
+    assert lib.gqa_last_error().decode() != ""
+
+
+def test_append_rejects(lib):
+    def call(**kw):
+        a = dict(k=FAKE, v=FAKE, kn=FAKE, vn=FAKE, lens=FAKE, b=4, g=2, dk=16, dv=16, cap=10,
+                 max_len=9, dtype=_lib.F32)
+        a.update(kw)
+        return lib.gqa_kv_append(a["k"], a["v"], a["kn"], a["vn"], a["lens"], a["b"], a["g"], a["dk"],
+                                 a["dv"], a["cap"], a["max_len"], a["dtype"], None)
+    assert call(max_len=10) == _lib.ERR_CAPACITY
+    assert "cap" in lib.gqa_last_error().decode()
+    assert call(kn=None) == _lib.ERR_ARG
+    assert call(cap=0) == _lib.ERR_ARG
+    assert call(b=-1) == _lib.ERR_ARG
+    assert call(dtype=3) == _lib.ERR_UNSUPPORTED
+
+
+def test_workspace_size(lib):
+    ws = lib.gqa_decode_workspace_size
+    n = ws(16, 64, 8, 128, 128, 8256, _lib.BF16)
+    # counters + (m, l) + partial outputs for ceil(8256 / 64) chunk slots per row
+    rows, nch = 16 * 64, (8256 + 63) // 64
+    assert n >= rows * 4 + rows * nch * (2 + 128) * 4
+    assert n % 256 == 0
+    assert ws(16, 64, 7, 128, 128, 100, _lib.BF16) == 0  # h % g != 0
+    assert ws(16, 64, 8, 128, 128, -1, _lib.BF16) == 0
+    assert ws(1, 1, 1, 16, 16, 0, _lib.F32) > 0
+
+
+def test_plan_choices(lib):
+    def plan(b, h, g, d, cap, max_len, dtype, path=0, chunk=0):
+        p, c = ctypes.c_int(), ctypes.c_int()
+        rc = lib.gqa_decode_plan(b, h, g, d, d, cap, max_len, dtype, path, chunk, ctypes.byref(p), ctypes.byref(c))
+        assert rc == _lib.OK, lib.gqa_last_error()
+        return p.value, c.value
+    assert plan(16, 64, 8, 128, 8256, 8193, _lib.BF16)[0] == _lib.PATH_MATRIX
+    assert plan(8, 32, 1, 128, 4160, 4097, _lib.BF16)[0] == _lib.PATH_MATRIX
+    assert plan(4, 32, 32, 128, 32832, 32769, _lib.BF16)[0] == _lib.PATH_VECTOR  # one head per KV head
+    assert plan(2, 4, 2, 16, 128, 65, _lib.F32)[0] == _lib.PATH_VECTOR
+    for args in [(16, 64, 8, 128, 8256, 8193, _lib.BF16), (2, 4, 2, 16, 128, 65, _lib.F32),
+                 (64, 28, 4, 128, 2112, 2080, _lib.BF16)]:
+        _, c = plan(*args)
+        assert c % 64 == 0 and 64 <= c <= 1024
+    assert plan(16, 64, 8, 128, 8256, 8193, _lib.BF16, path=_lib.PATH_VECTOR, chunk=256) == (_lib.PATH_VECTOR, 256)
