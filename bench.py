@@ -99,7 +99,7 @@ def main():
     ap.add_argument("--workload", default=None)
     ap.add_argument("--sets", type=int, default=0, help="cache sets to cycle (0: enough for >= 1.5 GB)")
     ap.add_argument("--path", type=int, default=0, help="0 auto, 1 vector, 2 matrix")
-    ap.add_argument("--chunk", type=int, default=0, help="positions per workgroup (0: automatic)")
+    ap.add_argument("--workgroups", type=int, default=0, help="persistent grid size (0: automatic)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle time budget (0: skip)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run a 1 GiB device copy first (reference for HBM byte counters)")
@@ -176,7 +176,7 @@ def main():
         if ev_pair is not None:
             ev_pair[0].record(stream)
         api.decode_attention(out, qs[i % len(qs)], st["kc"], st["vc"], st["lens"], max_len + 1, wl.scale, ws,
-                             path=args.path, chunk_tokens=args.chunk)
+                             path=args.path, workgroups=args.workgroups)
         if ev_pair is not None:
             ev_pair[1].record(stream)
         return kv_bytes_attended(wl.g, wl.d, wl.d, wl.elem_bytes, st["lens_h"])
@@ -207,7 +207,7 @@ def main():
 
     value = total_bytes / (elapsed_ms / 1e3) / 1e9
     achieved = bytes_per_launch / (kern_avg_ms / 1e3) / 1e9
-    plan_path, plan_chunk = api.plan(wl.b, wl.h, wl.g, wl.d, wl.d, cap, max_len_bound, dt, args.path, args.chunk)
+    plan_path, plan_wgs = api.plan(wl.b, wl.h, wl.g, wl.d, wl.d, cap, max_len_bound, dt, args.path, args.workgroups)
     traffic = traffic_from_profile(wl.name)
 
     cpu = None
@@ -236,7 +236,7 @@ def main():
             "lens": list(wl.lens) if isinstance(wl.lens, (list, tuple)) else wl.lens,
             "lens_drawn_mean": float(lens0.mean()), "lens_drawn_min": int(lens0.min()),
             "lens_drawn_max": int(lens0.max()), "cache_sets": n_sets, "seed": wl.seed,
-            "path": {1: "vector", 2: "matrix"}[plan_path], "chunk_tokens": plan_chunk,
+            "path": {1: "vector", 2: "matrix"}[plan_path], "workgroups": plan_wgs,
             "kv_bytes_per_step": int(bytes_per_launch),
         },
         "roofline": {

@@ -75,11 +75,11 @@ def make_workspace(b: int, h: int, g: int, d_k: int, d_v: int, max_len: int, dty
     return torch.zeros(workspace_size(b, h, g, d_k, d_v, max_len, dtype), dtype=torch.uint8, device=device)
 
 
-def plan(b, h, g, d_k, d_v, cap, max_len, dtype: torch.dtype, path=PATH_AUTO, chunk_tokens=0):
-    """(path, chunk_tokens) the library would launch with; no GPU work."""
+def plan(b, h, g, d_k, d_v, cap, max_len, dtype: torch.dtype, path=PATH_AUTO, workgroups=0):
+    """(path, workgroups) the library would launch with on the current device; no GPU work."""
     lib = _lib.load()
     p, c = ctypes.c_int(0), ctypes.c_int(0)
-    rc = lib.gqa_decode_plan(b, h, g, d_k, d_v, cap, int(max_len), _DTYPES[dtype], path, chunk_tokens,
+    rc = lib.gqa_decode_plan(b, h, g, d_k, d_v, cap, int(max_len), _DTYPES[dtype], path, workgroups,
                              ctypes.byref(p), ctypes.byref(c))
     _lib.check(rc, "gqa_decode_plan")
     return p.value, c.value
@@ -87,7 +87,7 @@ def plan(b, h, g, d_k, d_v, cap, max_len, dtype: torch.dtype, path=PATH_AUTO, ch
 
 def decode_attention(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                      lens: torch.Tensor, max_len: int, scale: float, workspace: torch.Tensor,
-                     path: int = PATH_AUTO, chunk_tokens: int = 0, stream=None) -> torch.Tensor:
+                     path: int = PATH_AUTO, workgroups: int = 0, stream=None) -> torch.Tensor:
     """out[s,i] = softmax_t(scale * q[s,i] . K[s,j,t]) @ V[s,j,t], t < lens[s], j = i // (h/g).
 
     q [b,h,d_k], caches [b,g,cap,d], lens int32 [b] (attended lengths), out [b,h,d_v].
@@ -109,6 +109,6 @@ def decode_attention(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor, 
         out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), lens.data_ptr(),
         b, h, g, d_k, d_v, cap, int(max_len), ctypes.c_float(scale), dt,
         workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream_handle(stream),
-        path, chunk_tokens)
+        path, workgroups)
     _lib.check(rc, "gqa_decode_attention")
     return out

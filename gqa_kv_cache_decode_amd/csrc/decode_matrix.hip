@@ -1,5 +1,5 @@
-// Matrix-core (MFMA) split-K decode attention: bf16 K/V/q, d_k = d_v = 128,
-// fp32 accumulation, up to 64 query heads per KV head.
+// Matrix-core (MFMA) decode attention: bf16 K/V/q, d_k = d_v = 128, fp32
+// accumulation, up to 64 query heads per KV head.
 //
 // Same result as the vector path (MQA review §2.1 per query head over the
 // cache of §2.4 / §3; contiguous head groups of the TF2 GQA lesson). Both
@@ -17,9 +17,9 @@
 // (group, slot) stands for, which is how the kernel picks K dims and V
 // positions freely:
 //
-// * K: lane (n = l%16, q = l/16) loads 16 bytes of row 16*sigma + n (sigma =
+// * K: lane (n = l%16, q = l/16) loads 16 bytes of row 16*sg + n (sg =
 //   sub-tile 0/1) at dims 32*ks + 8*q, ks = 0..3: exactly the A operand.
-// * The score MFMA leaves lane (n, q) with positions 16*sigma + 4q + 0..3 of
+// * The score MFMA leaves lane (n, q) with positions 16*sg + 4q + 0..3 of
 //   head n: these 8 probabilities, packed to bf16, are the B operand of the
 //   value MFMA for k-group q, with k-slot r <-> position tau(q, r) =
 //   4q + r (r < 4) or 16 + 4q + (r - 4).
@@ -29,9 +29,12 @@
 //   8n + e: the A operand of value MFMA e, whose output row m is dim 8m + e.
 //   Lane (n, q) therefore accumulates dims 32q .. 32q + 31 of head n.
 //
-// Each wave walks its own 32-position tiles of the chunk with an online
-// softmax (base 2, running max per head shared by the 4 lanes of a head);
-// the four waves are merged through LDS and finish_chunk handles the split.
+// K and V are streamed once with nontemporal loads (they are not reused, and
+// keeping them out of the caches measurably raises HBM read bandwidth).
+// Workgroups follow the persistent schedule of gqa_internal.hpp; inside a
+// piece each wave walks every fourth tile with an online softmax (base 2,
+// running max per head shared by the 4 lanes of a head), and the waves are
+// merged through LDS before finish_piece.
 #include "gqa_internal.hpp"
 
 namespace gqa {
@@ -42,14 +45,17 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int D = 128;
-constexpr int TILE = 32;
 constexpr int OPAD = 4;  // LDS row padding (floats) against bank conflicts
 
 __device__ __forceinline__ u32x4 load16(const uint16_t* ptr) {
   return *reinterpret_cast<const u32x4*>(ptr);
 }
-
+__device__ __forceinline__ u32x4 stream16(const uint16_t* ptr) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(ptr));
+}
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+__device__ __forceinline__ int v_row(int q4, int r) { return (r < 4) ? (4 * q4 + r) : (16 + 4 * q4 + (r - 4)); }
 
 // Value-MFMA A operand e from the 8 loaded V rows (vr[r] holds dims 8n..8n+7
 // of position tau(q, r)): dword k = (dim 8n+e of row 2k, of row 2k+1).
@@ -67,182 +73,192 @@ __device__ __forceinline__ bf16x8 v_transpose(const u32x4* vr) {
 }
 
 template <int NB>
+struct WaveState {
+  f32x4 oacc[NB][8];
+  float mrun[NB], lrun[NB];
+};
+
+// One 32-position tile starting at kbase/vbase row t0 (FULL: all 32 rows
+// valid; otherwise only rows < nvalid are read).
+template <int NB, bool FULL>
+__device__ __forceinline__ void tile_step(WaveState<NB>& st, const bf16x8 (&qop)[NB][4], const uint16_t* kbase,
+                                          const uint16_t* vbase, int t0, int nvalid, float sl2, int n16,
+                                          int q4) {
+  u32x4 kr[2][4];
+#pragma unroll
+  for (int sg = 0; sg < 2; ++sg) {
+    const int row = 16 * sg + n16;
+    const uint16_t* kp = kbase + size_t(t0 + row) * D + q4 * 8;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      if (FULL || row < nvalid) kr[sg][ks] = stream16(kp + ks * 32);
+      else kr[sg][ks] = u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+  u32x4 vr[8];
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+    const int row = v_row(q4, r);
+    if (FULL || row < nvalid) vr[r] = stream16(vbase + size_t(t0 + row) * D + n16 * 8);
+    else vr[r] = u32x4{0u, 0u, 0u, 0u};
+  }
+  bf16x8 pop[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    float sv[8];
+#pragma unroll
+    for (int sg = 0; sg < 2; ++sg) {
+      f32x4 sacc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kr[sg][ks]), qop[nb][ks], sacc, 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = 16 * sg + 4 * q4 + i;
+        sv[sg * 4 + i] = (FULL || row < nvalid) ? sacc[i] * sl2 : kNegInf;
+      }
+    }
+    float mx = sv[0];
+#pragma unroll
+    for (int k = 1; k < 8; ++k) mx = fmaxf(mx, sv[k]);
+    mx = fmaxf(mx, xor_shuffle(mx, 16));
+    mx = fmaxf(mx, xor_shuffle(mx, 32));
+    const float mn = fmaxf(st.mrun[nb], mx);
+    const float sub = (mn == kNegInf) ? 0.0f : mn;
+    const float alpha = fast_exp2(st.mrun[nb] - sub);
+    st.mrun[nb] = mn;
+    float psum = 0.0f;
+    bf16x8 pk;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const __bf16 pb = static_cast<__bf16>(fast_exp2(sv[k] - sub));
+      pk[k] = pb;
+      psum += static_cast<float>(pb);  // the denominator sums the weights actually applied
+    }
+    pop[nb] = pk;
+    st.lrun[nb] = fmaf(st.lrun[nb], alpha, psum);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) st.oacc[nb][e] *= alpha;
+  }
+#define GQA_PV_STEP(E)                                                                           \
+  {                                                                                              \
+    const bf16x8 va = v_transpose<E>(vr);                                                        \
+    _Pragma("unroll") for (int nb = 0; nb < NB; ++nb) st.oacc[nb][E] =                           \
+        __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pop[nb], st.oacc[nb][E], 0, 0, 0);           \
+  }
+  GQA_PV_STEP(0) GQA_PV_STEP(1) GQA_PV_STEP(2) GQA_PV_STEP(3)
+  GQA_PV_STEP(4) GQA_PV_STEP(5) GQA_PV_STEP(6) GQA_PV_STEP(7)
+#undef GQA_PV_STEP
+}
+
+template <int NB>
 __global__ __launch_bounds__(kThreads) void decode_matrix_kernel(DecodeParams p) {
   __shared__ float sm_m[kWaves][16];
   __shared__ float sm_l[kWaves][16];
   __shared__ float sm_o[kWaves][16][D + OPAD];
   __shared__ float fin_m[NB * 16];
   __shared__ float fin_l[NB * 16];
-  __shared__ float fin_o[NB * 16][D];
+  __shared__ __attribute__((aligned(16))) float fin_o[NB * 16][D];
+  __shared__ float sm_merge[kMergeLds];
   __shared__ int s_flag;
 
-  const int c = blockIdx.x;
-  const int j = blockIdx.y;
-  const int s = blockIdx.z;
-  const int G = p.G;
-  const int i0 = j * G;
-  const int L = attended_len(p, s);
-  if (L == 0) {
-    if (c == 0) write_zero_rows<uint16_t>(p, s, i0, G);
-    return;
-  }
-  const int n_valid = (L + p.chunk - 1) / p.chunk;
-  if (c >= n_valid) return;
-  const int t_begin = c * p.chunk;
-  const int t_end = min(L, t_begin + p.chunk);
-
+  const int wg = blockIdx.x;
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   const int n16 = lane & 15;
   const int q4 = lane >> 4;
-
-  // Q^T operands: head nb*16 + n16, dims 32*ks + 8*q4 .. +7 (zero for padding heads).
-  bf16x8 qop[NB][4];
-  const uint16_t* qg = static_cast<const uint16_t*>(p.q) + (size_t(s) * p.h + i0) * D;
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    const int head = nb * 16 + n16;
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (head < G) v = load16(qg + size_t(head) * D + ks * 32 + q4 * 8);
-      qop[nb][ks] = as_bf16x8(v);
-    }
-  }
-
-  f32x4 oacc[NB][8];
-  float mrun[NB], lrun[NB];
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    mrun[nb] = kNegInf;
-    lrun[nb] = 0.0f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) oacc[nb][e] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  }
-
-  const size_t kv_head = size_t(s) * p.g + j;
-  const uint16_t* kbase = static_cast<const uint16_t*>(p.k_cache) + kv_head * p.cap * D;
-  const uint16_t* vbase = static_cast<const uint16_t*>(p.v_cache) + kv_head * p.cap * D;
+  const int G = p.G;
   const float sl2 = p.scale_log2;
 
-  for (int t0 = t_begin + w * TILE; t0 < t_end; t0 += kWaves * TILE) {
-    const int nvalid = min(TILE, t_end - t0);
-    // ---- loads
-    u32x4 kr[2][4];
-#pragma unroll
-    for (int sg = 0; sg < 2; ++sg) {
-      const int row = 16 * sg + n16;
-      const uint16_t* kp = kbase + size_t(t0 + row) * D + q4 * 8;
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        if (row < nvalid) kr[sg][ks] = load16(kp + ks * 32);
-        else kr[sg][ks] = u32x4{0u, 0u, 0u, 0u};
-      }
-    }
-    u32x4 vr[8];
-#pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      const int row = (r < 4) ? (4 * q4 + r) : (16 + 4 * q4 + (r - 4));
-      if (row < nvalid) vr[r] = load16(vbase + size_t(t0 + row) * D + n16 * 8);
-      else vr[r] = u32x4{0u, 0u, 0u, 0u};
-    }
-    // ---- scores and online softmax, per 16-head block
-    bf16x8 pop[NB];
+  zero_empty_sequences<uint16_t>(p, wg);
+
+  PieceWalker walker;
+  walker.init(p, wg);
+  Piece pc;
+  Pending pend;
+  pend.n = 0;
+  while (walker.next(pc)) {
+    const int s = pc.s, j = pc.grp;
+    const int i0 = j * G;
+    // Q^T operands: head nb*16 + n16, dims 32*ks + 8*q4 .. +7 (zero for padding heads).
+    bf16x8 qop[NB][4];
+    const uint16_t* qg = static_cast<const uint16_t*>(p.q) + (size_t(s) * p.h + i0) * D;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      float sv[8];
+      const int head = nb * 16 + n16;
 #pragma unroll
-      for (int sg = 0; sg < 2; ++sg) {
-        f32x4 sacc = {0.0f, 0.0f, 0.0f, 0.0f};
+      for (int ks = 0; ks < 4; ++ks) {
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (head < G) v = load16(qg + size_t(head) * D + ks * 32 + q4 * 8);
+        qop[nb][ks] = as_bf16x8(v);
+      }
+    }
+    WaveState<NB> st;
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-          sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kr[sg][ks]), qop[nb][ks], sacc, 0, 0, 0);
+    for (int nb = 0; nb < NB; ++nb) {
+      st.mrun[nb] = kNegInf;
+      st.lrun[nb] = 0.0f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int row = 16 * sg + 4 * q4 + i;
-          sv[sg * 4 + i] = (row < nvalid) ? sacc[i] * sl2 : kNegInf;
+      for (int e = 0; e < 8; ++e) st.oacc[nb][e] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+    const size_t kv_head = size_t(s) * p.g + j;
+    const uint16_t* kbase = static_cast<const uint16_t*>(p.k_cache) + kv_head * p.cap * D;
+    const uint16_t* vbase = static_cast<const uint16_t*>(p.v_cache) + kv_head * p.cap * D;
+    const int t_end = min(pc.L, pc.tile_end * kTile);
+    for (int tile = pc.tile_begin + w; tile < pc.tile_end; tile += kWaves) {
+      const int t0 = tile * kTile;
+      const int nvalid = t_end - t0;
+      if (nvalid >= kTile) tile_step<NB, true>(st, qop, kbase, vbase, t0, kTile, sl2, n16, q4);
+      else tile_step<NB, false>(st, qop, kbase, vbase, t0, nvalid, sl2, n16, q4);
+    }
+
+    // merge the four waves through LDS, one 16-head block at a time
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      float lsum = st.lrun[nb];
+      lsum += xor_shuffle(lsum, 16);
+      lsum += xor_shuffle(lsum, 32);
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sm_o[w][n16][32 * q4 + 8 * i + e] = st.oacc[nb][e][i];
+      if (q4 == 0) {
+        sm_m[w][n16] = st.mrun[nb];
+        sm_l[w][n16] = lsum;
+      }
+      __syncthreads();
+      const int nh_blk = min(16, G - nb * 16);
+      for (int idx = threadIdx.x; idx < nh_blk * D; idx += kThreads) {
+        const int hh = idx / D, dd = idx - hh * D;
+        float M = sm_m[0][hh];
+#pragma unroll
+        for (int ww = 1; ww < kWaves; ++ww) M = fmaxf(M, sm_m[ww][hh]);
+        const float sub = (M == kNegInf) ? 0.0f : M;
+        float o = 0.0f, ls = 0.0f;
+#pragma unroll
+        for (int ww = 0; ww < kWaves; ++ww) {
+          const float wgt = fast_exp2(sm_m[ww][hh] - sub);
+          o = fmaf(wgt, sm_o[ww][hh][dd], o);
+          ls = fmaf(wgt, sm_l[ww][hh], ls);
+        }
+        fin_o[nb * 16 + hh][dd] = o;
+        if (dd == 0) {
+          fin_m[nb * 16 + hh] = M;
+          fin_l[nb * 16 + hh] = ls;
         }
       }
-      float mx = sv[0];
-#pragma unroll
-      for (int k = 1; k < 8; ++k) mx = fmaxf(mx, sv[k]);
-      mx = fmaxf(mx, xor_shuffle(mx, 16));
-      mx = fmaxf(mx, xor_shuffle(mx, 32));
-      const float mn = fmaxf(mrun[nb], mx);
-      const float sub = (mn == kNegInf) ? 0.0f : mn;
-      const float alpha = fast_exp2(mrun[nb] - sub);
-      mrun[nb] = mn;
-      float psum = 0.0f;
-      bf16x8 pk;
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const float pv = fast_exp2(sv[k] - sub);
-        const __bf16 pb = static_cast<__bf16>(pv);
-        pk[k] = pb;
-        psum += static_cast<float>(pb);  // the denominator sums the weights actually applied
-      }
-      pop[nb] = pk;
-      lrun[nb] = fmaf(lrun[nb], alpha, psum);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) oacc[nb][e] *= alpha;
+      __syncthreads();
     }
-    // ---- weighted sum of V
-#define GQA_PV_STEP(E)                                                                   \
-    {                                                                                    \
-      const bf16x8 va = v_transpose<E>(vr);                                              \
-      _Pragma("unroll") for (int nb = 0; nb < NB; ++nb)                                  \
-        oacc[nb][E] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pop[nb], oacc[nb][E], 0, 0, 0); \
-    }
-    GQA_PV_STEP(0) GQA_PV_STEP(1) GQA_PV_STEP(2) GQA_PV_STEP(3)
-    GQA_PV_STEP(4) GQA_PV_STEP(5) GQA_PV_STEP(6) GQA_PV_STEP(7)
-#undef GQA_PV_STEP
+    publish_piece<uint16_t>(p, pc, wg, i0, G, fin_m, fin_l, &fin_o[0][0], pend);
+    settle_pending<uint16_t, NB * 2>(p, pend, sm_merge, &s_flag);
+    pend.n = 0;
   }
-
-  // ---- merge the four waves through LDS, one 16-head block at a time
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    float lsum = lrun[nb];
-    lsum += xor_shuffle(lsum, 16);
-    lsum += xor_shuffle(lsum, 32);
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) sm_o[w][n16][32 * q4 + 8 * i + e] = oacc[nb][e][i];
-    if (q4 == 0) {
-      sm_m[w][n16] = mrun[nb];
-      sm_l[w][n16] = lsum;
-    }
-    __syncthreads();
-    const int nh_blk = min(16, G - nb * 16);
-    for (int idx = threadIdx.x; idx < nh_blk * D; idx += kThreads) {
-      const int hh = idx / D, dd = idx - hh * D;
-      float M = sm_m[0][hh];
-#pragma unroll
-      for (int ww = 1; ww < kWaves; ++ww) M = fmaxf(M, sm_m[ww][hh]);
-      const float sub = (M == kNegInf) ? 0.0f : M;
-      float o = 0.0f, ls = 0.0f;
-#pragma unroll
-      for (int ww = 0; ww < kWaves; ++ww) {
-        const float wgt = fast_exp2(sm_m[ww][hh] - sub);
-        o = fmaf(wgt, sm_o[ww][hh][dd], o);
-        ls = fmaf(wgt, sm_l[ww][hh], ls);
-      }
-      fin_o[nb * 16 + hh][dd] = o;
-      if (dd == 0) {
-        fin_m[nb * 16 + hh] = M;
-        fin_l[nb * 16 + hh] = ls;
-      }
-    }
-    __syncthreads();
-  }
-  finish_chunk<uint16_t>(p, s, i0, G, c, n_valid, fin_m, fin_l, &fin_o[0][0], &s_flag);
 }
 
 }  // namespace
 
 hipError_t launch_decode_matrix(const DecodeParams& p, hipStream_t stream) {
-  const int n_chunks = (p.max_len + p.chunk - 1) / p.chunk;
-  const dim3 grid(n_chunks > 0 ? n_chunks : 1, p.g, p.b);
+  const dim3 grid(p.workgroups);
   if (p.G <= 16) {
     hipLaunchKernelGGL(decode_matrix_kernel<1>, grid, dim3(kThreads), 0, stream, p);
   } else if (p.G <= 32) {
@@ -251,6 +267,23 @@ hipError_t launch_decode_matrix(const DecodeParams& p, hipStream_t stream) {
     hipLaunchKernelGGL(decode_matrix_kernel<4>, grid, dim3(kThreads), 0, stream, p);
   }
   return hipGetLastError();
+}
+
+int matrix_workgroups_per_cu(int G) {
+  static int cached[3] = {0, 0, 0};
+  const int k = G <= 16 ? 0 : (G <= 32 ? 1 : 2);
+  if (cached[k] > 0) return cached[k];
+  int n = 0;
+  hipError_t e;
+  if (k == 0) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_matrix_kernel<1>, kThreads, 0);
+  else if (k == 1) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_matrix_kernel<2>, kThreads, 0);
+  else e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_matrix_kernel<4>, kThreads, 0);
+  if (e != hipSuccess || n <= 0) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  cached[k] = n;
+  return n;
 }
 
 }  // namespace gqa

@@ -1,27 +1,28 @@
-// Vector-ALU split-K decode attention (every supported dtype and head dim).
+// Vector-ALU decode attention (every supported dtype and head dim).
 //
 // Computes, per sequence s and query head i with KV head j = floor(i / G),
 //   out[s][i] = sum_t softmax_t(scale * q[s][i] . K[s][j][t]) V[s][j][t]
 // (MQA review §2.1 Dot-Product Attention applied per head, with the cache of
 // §2.4 / §3 and the contiguous head groups of the TF2 GQA lesson).
 //
-// Work decomposition: one workgroup per (position chunk, KV head, head block,
-// sequence). A head block is up to 8 query heads of one group, so each K/V
-// row fetched from HBM is used by all of them. A K/V row is split over
-// R = row_bytes / 16 consecutive lanes, each holding one 16-byte column, and
-// each wave load instruction covers 64 / R consecutive rows (1 KiB,
-// contiguous). Dot products are summed across the R lanes with DPP row
-// operations; every lane group keeps its own online-softmax state (running
-// max, sum, unnormalised output) in base 2, and the groups, then the four
-// waves (through LDS), are merged at the end. finish_chunk then writes the
-// output or the chunk's partial state and merges the chunks.
+// A workgroup handles up to HB query heads of one group (a head block), so
+// each K/V row fetched from HBM serves all of them. A K/V row is split over
+// R = row_bytes / 16 consecutive lanes, each holding one 16-byte column; one
+// wave load covers 64 / R consecutive rows (1 KiB, contiguous), and K/V are
+// streamed with nontemporal loads. Dot products are summed across the R
+// lanes with DPP row operations; every lane group keeps its own online-softmax
+// state (base-2 running max, sum, unnormalised output), and the groups, then
+// the four waves (through LDS), are merged at the end of each piece of the
+// persistent schedule (gqa_internal.hpp), which finish_piece completes.
 #include "gqa_internal.hpp"
 
 namespace gqa {
 namespace {
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
 template <typename T>
-__device__ __forceinline__ void widen16(const uint4& r, float* f) {
+__device__ __forceinline__ void widen16(const u32x4& r, float* f) {
   if constexpr (sizeof(T) == 4) {
     f[0] = __uint_as_float(r.x);
     f[1] = __uint_as_float(r.y);
@@ -35,87 +36,50 @@ __device__ __forceinline__ void widen16(const uint4& r, float* f) {
   }
 }
 
+template <typename T>
+__device__ __forceinline__ u32x4 stream16(const T* ptr) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(ptr));
+}
+
 template <typename T, int D, int HB>
-__global__ __launch_bounds__(kThreads) void decode_vector_kernel(DecodeParams p) {
-  constexpr int VEC = 16 / int(sizeof(T));  // elements per 16-byte column
-  constexpr int R = D / VEC;                // lanes per row
+struct Shape {
+  static constexpr int VEC = 16 / int(sizeof(T));  // elements per 16-byte column
+  static constexpr int R = D / VEC;                // lanes per row
   static_assert(R >= 1 && R <= 64 && (R & (R - 1)) == 0, "row must be 16..1024 bytes");
-  constexpr int RPW = 64 / R;               // rows per wave load
-  constexpr int U = (HB >= 8 && VEC == 8) ? 2 : 4;  // loads in flight per lane
-  constexpr int ROWS_IT = kWaves * RPW * U;
+  static constexpr int RPW = 64 / R;                // rows per wave load
+  static constexpr int NL = (kTile + RPW - 1) / RPW;  // loads per lane per tile
+  static constexpr int UMAX = (HB >= 8 && VEC == 8) ? 2 : (HB >= 4 ? 4 : 8);
+  static constexpr int U = NL < UMAX ? NL : UMAX;   // loads in flight per lane
+  static constexpr int NSUB = NL / U;
+  static_assert(NL % U == 0, "sub-batches must tile the 32-position tile");
+};
 
-  __shared__ float sm_m[kWaves][HB];
-  __shared__ float sm_l[kWaves][HB];
-  __shared__ float sm_o[kWaves][HB][D];
-  __shared__ float fin_m[HB];
-  __shared__ float fin_l[HB];
-  __shared__ float fin_o[HB][D];
-  __shared__ int s_flag;
-
-  const int c = blockIdx.x;
-  const int nhb = (p.G + HB - 1) / HB;
-  const int j = blockIdx.y / nhb;
-  const int hb = blockIdx.y - j * nhb;
-  const int s = blockIdx.z;
-  const int i0 = j * p.G + hb * HB;
-  const int nh = min(HB, p.G - hb * HB);
-  const int L = attended_len(p, s);
-  if (L == 0) {
-    if (c == 0) write_zero_rows<T>(p, s, i0, nh);
-    return;
-  }
-  const int n_valid = (L + p.chunk - 1) / p.chunk;
-  if (c >= n_valid) return;
-  const int t_begin = c * p.chunk;
-  const int t_end = min(L, t_begin + p.chunk);
-
-  const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
-  const int col = lane % R;
-  const int rg = lane / R;
-
-  // Query rows of the head block, widened and pre-multiplied by scale*log2(e).
-  float qf[HB][VEC];
-  const T* qrow = static_cast<const T*>(p.q) + (size_t(s) * p.h + i0) * D + col * VEC;
-#pragma unroll
-  for (int hh = 0; hh < HB; ++hh) {
-    if (hh < nh) {
-      const uint4 raw = *reinterpret_cast<const uint4*>(qrow + size_t(hh) * D);
-      widen16<T>(raw, qf[hh]);
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) qf[hh][e] *= p.scale_log2;
-    } else {
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) qf[hh][e] = 0.0f;
-    }
-  }
-
+template <typename T, int D, int HB>
+struct VState {
+  static constexpr int VEC = Shape<T, D, HB>::VEC;
   float m[HB], l[HB], acc[HB][VEC];
-#pragma unroll
-  for (int hh = 0; hh < HB; ++hh) {
-    m[hh] = kNegInf;
-    l[hh] = 0.0f;
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) acc[hh][e] = 0.0f;
-  }
+};
 
-  const size_t kv_head = size_t(s) * p.g + j;
-  const T* kbase = static_cast<const T*>(p.k_cache) + kv_head * p.cap * D + col * VEC;
-  const T* vbase = static_cast<const T*>(p.v_cache) + kv_head * p.cap * D + col * VEC;
-
-  for (int base = t_begin + w * RPW * U; base < t_end; base += ROWS_IT) {
-    uint4 kr[U], vr[U];
+// One 32-position tile starting at row t0 (FULL: all rows valid).
+template <typename T, int D, int HB, bool FULL>
+__device__ __forceinline__ void tile_step(VState<T, D, HB>& st, const float (&qf)[HB][Shape<T, D, HB>::VEC],
+                                          const T* kbase, const T* vbase, int t0, int nvalid, int rg) {
+  using S = Shape<T, D, HB>;
+  constexpr int VEC = S::VEC, U = S::U, RPW = S::RPW, R = S::R;
+#pragma unroll
+  for (int sb = 0; sb < S::NSUB; ++sb) {
+    u32x4 kr[U], vr[U];
     bool ok[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int t = base + u * RPW + rg;
-      ok[u] = t < t_end;
+      const int row = (sb * U + u) * RPW + rg;
+      ok[u] = FULL ? (row < kTile) : (row < nvalid);
       if (ok[u]) {
-        kr[u] = *reinterpret_cast<const uint4*>(kbase + size_t(t) * D);
-        vr[u] = *reinterpret_cast<const uint4*>(vbase + size_t(t) * D);
+        kr[u] = stream16(kbase + size_t(t0 + row) * D);
+        vr[u] = stream16(vbase + size_t(t0 + row) * D);
       } else {
-        kr[u] = make_uint4(0, 0, 0, 0);
-        vr[u] = make_uint4(0, 0, 0, 0);
+        kr[u] = u32x4{0u, 0u, 0u, 0u};
+        vr[u] = u32x4{0u, 0u, 0u, 0u};
       }
     }
     float sc[U][HB];
@@ -140,10 +104,10 @@ __global__ __launch_bounds__(kThreads) void decode_vector_kernel(DecodeParams p)
       float mx = sc[0][hh];
 #pragma unroll
       for (int u = 1; u < U; ++u) mx = fmaxf(mx, sc[u][hh]);
-      const float mn = fmaxf(m[hh], mx);
+      const float mn = fmaxf(st.m[hh], mx);
       const float sub = (mn == kNegInf) ? 0.0f : mn;
-      const float alpha = fast_exp2(m[hh] - sub);
-      m[hh] = mn;
+      const float alpha = fast_exp2(st.m[hh] - sub);
+      st.m[hh] = mn;
       float pu[U];
       float psum = 0.0f;
 #pragma unroll
@@ -151,103 +115,217 @@ __global__ __launch_bounds__(kThreads) void decode_vector_kernel(DecodeParams p)
         pu[u] = fast_exp2(sc[u][hh] - sub);
         psum += pu[u];
       }
-      l[hh] = fmaf(l[hh], alpha, psum);
+      st.l[hh] = fmaf(st.l[hh], alpha, psum);
 #pragma unroll
       for (int e = 0; e < VEC; ++e) {
-        float a = acc[hh][e] * alpha;
+        float a = st.acc[hh][e] * alpha;
 #pragma unroll
         for (int u = 0; u < U; ++u) a = fmaf(pu[u], vf[u][e], a);
-        acc[hh][e] = a;
+        st.acc[hh][e] = a;
       }
     }
   }
-
-  // Merge the lane groups of the wave (same column, different rows).
-#pragma unroll
-  for (int off = R; off < 64; off <<= 1) {
-#pragma unroll
-    for (int hh = 0; hh < HB; ++hh) {
-      const float mo = xor_shuffle(m[hh], off);
-      const float lo = xor_shuffle(l[hh], off);
-      float mn;
-      const MergeWeights wt = merge_weights(m[hh], mo, mn);
-      l[hh] = l[hh] * wt.a + lo * wt.b;
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) {
-        const float ao = xor_shuffle(acc[hh][e], off);
-        acc[hh][e] = acc[hh][e] * wt.a + ao * wt.b;
-      }
-      m[hh] = mn;
-    }
-  }
-  if (rg == 0) {
-#pragma unroll
-    for (int hh = 0; hh < HB; ++hh) {
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) sm_o[w][hh][col * VEC + e] = acc[hh][e];
-      if (col == 0) {
-        sm_m[w][hh] = m[hh];
-        sm_l[w][hh] = l[hh];
-      }
-    }
-  }
-  __syncthreads();
-  // Merge the four waves.
-  for (int idx = threadIdx.x; idx < HB * D; idx += kThreads) {
-    const int hh = idx / D, dd = idx - hh * D;
-    float M = sm_m[0][hh];
-#pragma unroll
-    for (int ww = 1; ww < kWaves; ++ww) M = fmaxf(M, sm_m[ww][hh]);
-    const float sub = (M == kNegInf) ? 0.0f : M;
-    float o = 0.0f, lsum = 0.0f;
-#pragma unroll
-    for (int ww = 0; ww < kWaves; ++ww) {
-      const float wgt = fast_exp2(sm_m[ww][hh] - sub);
-      o = fmaf(wgt, sm_o[ww][hh][dd], o);
-      lsum = fmaf(wgt, sm_l[ww][hh], lsum);
-    }
-    fin_o[hh][dd] = o;
-    if (dd == 0) {
-      fin_m[hh] = M;
-      fin_l[hh] = lsum;
-    }
-  }
-  __syncthreads();
-  finish_chunk<T>(p, s, i0, nh, c, n_valid, fin_m, fin_l, &fin_o[0][0], &s_flag);
 }
 
-template <typename T, int D>
-hipError_t launch_d(const DecodeParams& p, int hb, hipStream_t stream) {
-  const int n_chunks = (p.max_len + p.chunk - 1) / p.chunk;
-  const int nhb = (p.G + hb - 1) / hb;
-  const dim3 grid(n_chunks > 0 ? n_chunks : 1, p.g * nhb, p.b);
-  switch (hb) {
-    case 1: hipLaunchKernelGGL((decode_vector_kernel<T, D, 1>), grid, dim3(kThreads), 0, stream, p); break;
-    case 2: hipLaunchKernelGGL((decode_vector_kernel<T, D, 2>), grid, dim3(kThreads), 0, stream, p); break;
-    case 4: hipLaunchKernelGGL((decode_vector_kernel<T, D, 4>), grid, dim3(kThreads), 0, stream, p); break;
-    default: hipLaunchKernelGGL((decode_vector_kernel<T, D, 8>), grid, dim3(kThreads), 0, stream, p); break;
+template <typename T, int D, int HB>
+__global__ __launch_bounds__(kThreads) void decode_vector_kernel(DecodeParams p) {
+  using S = Shape<T, D, HB>;
+  constexpr int VEC = S::VEC, R = S::R;
+
+  __shared__ float sm_m[kWaves][HB];
+  __shared__ float sm_l[kWaves][HB];
+  __shared__ float sm_o[kWaves][HB][D];
+  __shared__ float fin_m[HB];
+  __shared__ float fin_l[HB];
+  __shared__ __attribute__((aligned(16))) float fin_o[HB][D];
+  __shared__ float sm_merge[kMergeLds];
+  __shared__ int s_flag;
+
+  const int wg = blockIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int col = lane % R;
+  const int rg = lane / R;
+
+  zero_empty_sequences<T>(p, wg);
+
+  PieceWalker walker;
+  walker.init(p, wg);
+  Piece pc;
+  Pending pend;
+  pend.n = 0;
+  while (walker.next(pc)) {
+    const int s = pc.s;
+    const int j = pc.grp / p.nhb;
+    const int hb = pc.grp - j * p.nhb;
+    const int i0 = j * p.G + hb * HB;
+    const int nh = min(HB, p.G - hb * HB);
+
+    // query rows of the head block, widened and pre-multiplied by scale*log2(e)
+    float qf[HB][VEC];
+    const T* qrow = static_cast<const T*>(p.q) + (size_t(s) * p.h + i0) * D + col * VEC;
+#pragma unroll
+    for (int hh = 0; hh < HB; ++hh) {
+      if (hh < nh) {
+        const u32x4 raw = *reinterpret_cast<const u32x4*>(qrow + size_t(hh) * D);
+        widen16<T>(raw, qf[hh]);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) qf[hh][e] *= p.scale_log2;
+      } else {
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) qf[hh][e] = 0.0f;
+      }
+    }
+    VState<T, D, HB> st;
+#pragma unroll
+    for (int hh = 0; hh < HB; ++hh) {
+      st.m[hh] = kNegInf;
+      st.l[hh] = 0.0f;
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) st.acc[hh][e] = 0.0f;
+    }
+    const size_t kv_head = size_t(s) * p.g + j;
+    const T* kbase = static_cast<const T*>(p.k_cache) + kv_head * p.cap * D + col * VEC;
+    const T* vbase = static_cast<const T*>(p.v_cache) + kv_head * p.cap * D + col * VEC;
+    const int t_end = min(pc.L, pc.tile_end * kTile);
+    for (int tile = pc.tile_begin + w; tile < pc.tile_end; tile += kWaves) {
+      const int t0 = tile * kTile;
+      const int nvalid = t_end - t0;
+      if (nvalid >= kTile) tile_step<T, D, HB, true>(st, qf, kbase, vbase, t0, kTile, rg);
+      else tile_step<T, D, HB, false>(st, qf, kbase, vbase, t0, nvalid, rg);
+    }
+
+    // merge the lane groups of the wave (same column, different rows)
+#pragma unroll
+    for (int off = R; off < 64; off <<= 1) {
+#pragma unroll
+      for (int hh = 0; hh < HB; ++hh) {
+        const float mo = xor_shuffle(st.m[hh], off);
+        const float lo = xor_shuffle(st.l[hh], off);
+        float mn;
+        const MergeWeights wt = merge_weights(st.m[hh], mo, mn);
+        st.l[hh] = st.l[hh] * wt.a + lo * wt.b;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          const float ao = xor_shuffle(st.acc[hh][e], off);
+          st.acc[hh][e] = st.acc[hh][e] * wt.a + ao * wt.b;
+        }
+        st.m[hh] = mn;
+      }
+    }
+    if (rg == 0) {
+#pragma unroll
+      for (int hh = 0; hh < HB; ++hh) {
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) sm_o[w][hh][col * VEC + e] = st.acc[hh][e];
+        if (col == 0) {
+          sm_m[w][hh] = st.m[hh];
+          sm_l[w][hh] = st.l[hh];
+        }
+      }
+    }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < HB * D; idx += kThreads) {
+      const int hh = idx / D, dd = idx - hh * D;
+      float M = sm_m[0][hh];
+#pragma unroll
+      for (int ww = 1; ww < kWaves; ++ww) M = fmaxf(M, sm_m[ww][hh]);
+      const float sub = (M == kNegInf) ? 0.0f : M;
+      float o = 0.0f, lsum = 0.0f;
+#pragma unroll
+      for (int ww = 0; ww < kWaves; ++ww) {
+        const float wgt = fast_exp2(sm_m[ww][hh] - sub);
+        o = fmaf(wgt, sm_o[ww][hh][dd], o);
+        lsum = fmaf(wgt, sm_l[ww][hh], lsum);
+      }
+      fin_o[hh][dd] = o;
+      if (dd == 0) {
+        fin_m[hh] = M;
+        fin_l[hh] = lsum;
+      }
+    }
+    __syncthreads();
+    publish_piece<T>(p, pc, wg, i0, nh, fin_m, fin_l, &fin_o[0][0], pend);
+    settle_pending<T, (HB * D / 4 + kThreads - 1) / kThreads>(p, pend, sm_merge, &s_flag);
+    pend.n = 0;
   }
+}
+
+template <typename T, int D, int HB>
+hipError_t launch_one(const DecodeParams& p, hipStream_t stream) {
+  hipLaunchKernelGGL((decode_vector_kernel<T, D, HB>), dim3(p.workgroups), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 
+template <typename T, int D>
+hipError_t launch_d(const DecodeParams& p, hipStream_t stream) {
+  switch (p.gblk) {
+    case 1: return launch_one<T, D, 1>(p, stream);
+    case 2: return launch_one<T, D, 2>(p, stream);
+    case 4: return launch_one<T, D, 4>(p, stream);
+    default: return launch_one<T, D, 8>(p, stream);
+  }
+}
+
 template <typename T>
-hipError_t launch_t(const DecodeParams& p, int hb, hipStream_t stream) {
+hipError_t launch_t(const DecodeParams& p, hipStream_t stream) {
   switch (p.d) {
-    case 16: return launch_d<T, 16>(p, hb, stream);
-    case 32: return launch_d<T, 32>(p, hb, stream);
-    case 64: return launch_d<T, 64>(p, hb, stream);
-    case 128: return launch_d<T, 128>(p, hb, stream);
-    case 256: return launch_d<T, 256>(p, hb, stream);
+    case 16: return launch_d<T, 16>(p, stream);
+    case 32: return launch_d<T, 32>(p, stream);
+    case 64: return launch_d<T, 64>(p, stream);
+    case 128: return launch_d<T, 128>(p, stream);
+    case 256: return launch_d<T, 256>(p, stream);
     default: return hipErrorInvalidValue;
+  }
+}
+
+
+template <typename T, int D>
+int occupancy_d(int hb) {
+  int n = 0;
+  hipError_t e;
+  switch (hb) {
+    case 1: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_vector_kernel<T, D, 1>, kThreads, 0); break;
+    case 2: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_vector_kernel<T, D, 2>, kThreads, 0); break;
+    case 4: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_vector_kernel<T, D, 4>, kThreads, 0); break;
+    default: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_vector_kernel<T, D, 8>, kThreads, 0); break;
+  }
+  if (e != hipSuccess || n <= 0) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  return n;
+}
+
+template <typename T>
+int occupancy_t(int d, int hb) {
+  switch (d) {
+    case 16: return occupancy_d<T, 16>(hb);
+    case 32: return occupancy_d<T, 32>(hb);
+    case 64: return occupancy_d<T, 64>(hb);
+    case 128: return occupancy_d<T, 128>(hb);
+    default: return occupancy_d<T, 256>(hb);
   }
 }
 
 }  // namespace
 
-hipError_t launch_decode_vector(const DecodeParams& p, int dtype, int heads_per_block,
-                                hipStream_t stream) {
-  if (dtype == 0) return launch_t<float>(p, heads_per_block, stream);
-  return launch_t<uint16_t>(p, heads_per_block, stream);
+int vector_workgroups_per_cu(int dtype, int d, int heads_per_block) {
+  static int cached[2][5][4] = {};
+  const int ti = dtype == 0 ? 0 : 1;
+  const int di = d == 16 ? 0 : d == 32 ? 1 : d == 64 ? 2 : d == 128 ? 3 : 4;
+  const int hi = heads_per_block == 1 ? 0 : heads_per_block == 2 ? 1 : heads_per_block == 4 ? 2 : 3;
+  int& c = cached[ti][di][hi];
+  if (c > 0) return c;
+  const int n = ti == 0 ? occupancy_t<float>(d, heads_per_block) : occupancy_t<uint16_t>(d, heads_per_block);
+  if (n > 0) c = n;
+  return n;
+}
+
+
+hipError_t launch_decode_vector(const DecodeParams& p, int dtype, hipStream_t stream) {
+  if (dtype == 0) return launch_t<float>(p, stream);
+  return launch_t<uint16_t>(p, stream);
 }
 
 }  // namespace gqa

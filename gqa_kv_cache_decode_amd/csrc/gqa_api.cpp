@@ -6,7 +6,7 @@
 
 #include <string>
 
-#include "../../include/gqa_decode.h"
+#include "gqa_decode.h"
 #include "gqa_internal.hpp"
 
 namespace {
@@ -32,22 +32,43 @@ constexpr int kMaxBatch = 65535;
 constexpr int kMaxHeads = 4096;
 constexpr int kMaxLen = 1 << 28;
 constexpr float kLog2e = 1.4426950408889634f;
-// Workgroups the automatic chunk size aims for: eight per compute unit of an
-// MI355X (256 CUs), counted over the launch's upper bound of positions.
-constexpr long long kTargetWorkgroups = 8LL * 256;
+constexpr int kDefaultCUs = 256;  // MI355X, used when no device can be queried
 
 bool supported_head_dim(int d) { return d == 16 || d == 32 || d == 64 || d == 128 || d == 256; }
 
+// Compute units of the current device (cached per device; kDefaultCUs if the
+// runtime cannot say).
+int device_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return kDefaultCUs;
+  if (cached[dev] > 0) return cached[dev];
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    n = kDefaultCUs;
+  cached[dev] = n;
+  return n;
+}
+
 struct Plan {
   int path;
-  int chunk;
-  int heads_per_block;
+  int gblk;
+  int nhb;
+  int workgroups;
 };
 
+// Largest head block any path may use for G heads per KV head (workspace sizing).
+int gblk_bound(int G) {
+  const int m = G < gqa::kMatrixMaxGroup ? G : gqa::kMatrixMaxGroup;
+  const int v = gqa::vector_heads_per_block(G);
+  return m > v ? m : v;
+}
+
 // Shared shape checks of the decode entry points (pointers are checked by the
-// callers). Fills plan on success.
-int plan_decode(int b, int h, int g, int d_k, int d_v, int cap, int max_len, int dtype,
-                int path, int chunk_tokens, Plan* plan) {
+// callers). Fills plan on success. workgroups: 0 = one per resident slot of
+// the device (compute units x workgroups that fit per unit, at most two).
+int plan_decode(int b, int h, int g, int d_k, int d_v, int cap, int max_len, int dtype, int path,
+                int workgroups, Plan* plan) {
   if (b <= 0 || b > kMaxBatch) return fail(GQA_ERR_ARG, "b=%d must be in [1, %d]", b, kMaxBatch);
   if (h <= 0 || h > kMaxHeads) return fail(GQA_ERR_ARG, "h=%d must be in [1, %d]", h, kMaxHeads);
   if (g <= 0) return fail(GQA_ERR_ARG, "g=%d must be positive", g);
@@ -65,32 +86,39 @@ int plan_decode(int b, int h, int g, int d_k, int d_v, int cap, int max_len, int
   if (max_len > kMaxLen) return fail(GQA_ERR_UNSUPPORTED, "max_len=%d exceeds %d", max_len, kMaxLen);
   if (path != GQA_PATH_AUTO && path != GQA_PATH_VECTOR && path != GQA_PATH_MATRIX)
     return fail(GQA_ERR_UNSUPPORTED, "path=%d is not a GQA_PATH_* value", path);
-  if (chunk_tokens != 0 &&
-      (chunk_tokens < gqa::kMinChunk || chunk_tokens > gqa::kMaxChunk || chunk_tokens % gqa::kMinChunk))
-    return fail(GQA_ERR_UNSUPPORTED, "chunk_tokens=%d must be 0 or a multiple of %d in [%d, %d]",
-                chunk_tokens, gqa::kMinChunk, gqa::kMinChunk, gqa::kMaxChunk);
+  if (workgroups < 0 || workgroups > gqa::kMaxWorkgroups)
+    return fail(GQA_ERR_UNSUPPORTED, "workgroups=%d must be in [0, %d]", workgroups, gqa::kMaxWorkgroups);
 
   const int G = h / g;
-  const bool matrix_ok = dtype == GQA_DTYPE_BF16 && d_k == 128 && G <= 64;
+  const bool matrix_ok = dtype == GQA_DTYPE_BF16 && d_k == 128 && G <= gqa::kMatrixMaxGroup;
   if (path == GQA_PATH_MATRIX && !matrix_ok)
     return fail(GQA_ERR_UNSUPPORTED, "matrix path needs bf16, d=128 and at most 64 heads per KV head");
   int chosen = path;
+  // Matrix cores pay once a K/V row serves three or more query heads; below
+  // that the vector path keeps up with HBM on its own.
   if (chosen == GQA_PATH_AUTO) chosen = (matrix_ok && G >= 3) ? GQA_PATH_MATRIX : GQA_PATH_VECTOR;
 
-  const int hpb = chosen == GQA_PATH_MATRIX ? G : gqa::vector_heads_per_block(G);
-  const int nhb = (G + hpb - 1) / hpb;
-  int chunk = chunk_tokens;
-  if (chunk == 0) {
-    const long long units = (long long)b * g * nhb * (long long)(max_len > 0 ? max_len : 1);
-    long long want = (units + kTargetWorkgroups - 1) / kTargetWorkgroups;
-    want = (want + gqa::kMinChunk - 1) / gqa::kMinChunk * gqa::kMinChunk;
-    if (want < gqa::kMinChunk) want = gqa::kMinChunk;
-    if (want > 1024) want = 1024;
-    chunk = (int)want;
-  }
   plan->path = chosen;
-  plan->chunk = chunk;
-  plan->heads_per_block = hpb;
+  if (chosen == GQA_PATH_MATRIX) {
+    plan->gblk = G;
+    plan->nhb = 1;
+  } else {
+    plan->gblk = gqa::vector_heads_per_block(G);
+    plan->nhb = (G + plan->gblk - 1) / plan->gblk;
+  }
+  if (workgroups == 0) {
+    // Up to two 4-wave workgroups per compute unit (8 waves keep enough loads
+    // in flight), never more than fit at once, so the persistent grid runs in
+    // a single round.
+    int fit = chosen == GQA_PATH_MATRIX ? gqa::matrix_workgroups_per_cu(G)
+                                        : gqa::vector_workgroups_per_cu(dtype, d_k, plan->gblk);
+    if (fit <= 0) fit = 2;  // no device to ask: assume the common case
+    const int per_cu = fit < 2 ? fit : 2;
+    long long n = (long long)device_cus() * per_cu;
+    if (n > gqa::kMaxWorkgroups) n = gqa::kMaxWorkgroups;
+    workgroups = int(n);
+  }
+  plan->workgroups = workgroups;
   return GQA_OK;
 }
 
@@ -123,29 +151,29 @@ size_t gqa_decode_workspace_size(int b, int h, int g, int d_k, int d_v, int max_
   if (b <= 0 || b > kMaxBatch || h <= 0 || h > kMaxHeads || g <= 0 || h % g != 0 || d_k <= 0 ||
       d_v <= 0 || max_len < 0 || max_len > kMaxLen || (dtype != GQA_DTYPE_F32 && dtype != GQA_DTYPE_BF16))
     return 0;
-  return gqa::workspace_layout(b, h, d_v, max_len).total;
+  return gqa::workspace_layout(b, h, gblk_bound(h / g), d_v).total;
 }
 
 int gqa_decode_plan(int b, int h, int g, int d_k, int d_v, int cap, int max_len, int dtype,
-                    int path, int chunk_tokens, int* chosen_path, int* chosen_chunk_tokens) {
+                    int path, int workgroups, int* chosen_path, int* chosen_workgroups) {
   Plan plan;
-  const int rc = plan_decode(b, h, g, d_k, d_v, cap, max_len, dtype, path, chunk_tokens, &plan);
+  const int rc = plan_decode(b, h, g, d_k, d_v, cap, max_len, dtype, path, workgroups, &plan);
   if (rc != GQA_OK) return rc;
   if (chosen_path) *chosen_path = plan.path;
-  if (chosen_chunk_tokens) *chosen_chunk_tokens = plan.chunk;
+  if (chosen_workgroups) *chosen_workgroups = plan.workgroups;
   return ok();
 }
 
 int gqa_decode_attention_ex(void* out, const void* q, const void* k_cache, const void* v_cache,
                             const int32_t* lens, int b, int h, int g, int d_k, int d_v, int cap,
                             int max_len, float scale, int dtype, void* workspace,
-                            size_t workspace_bytes, void* stream, int path, int chunk_tokens) {
+                            size_t workspace_bytes, void* stream, int path, int workgroups) {
   if (!out || !q || !k_cache || !v_cache || !lens)
     return fail(GQA_ERR_ARG, "gqa_decode_attention: null pointer argument");
   Plan plan;
-  const int rc = plan_decode(b, h, g, d_k, d_v, cap, max_len, dtype, path, chunk_tokens, &plan);
+  const int rc = plan_decode(b, h, g, d_k, d_v, cap, max_len, dtype, path, workgroups, &plan);
   if (rc != GQA_OK) return rc;
-  const gqa::WorkspaceLayout ws = gqa::workspace_layout(b, h, d_v, max_len);
+  const gqa::WorkspaceLayout ws = gqa::workspace_layout(b, h, gblk_bound(h / g), d_v);
   if (!workspace) return fail(GQA_ERR_WORKSPACE, "workspace is null (%zu bytes needed)", ws.total);
   if (workspace_bytes < ws.total)
     return fail(GQA_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, ws.total);
@@ -160,8 +188,7 @@ int gqa_decode_attention_ex(void* out, const void* q, const void* k_cache, const
   p.lens = lens;
   char* wsb = static_cast<char*>(workspace);
   p.ws_cnt = reinterpret_cast<int*>(wsb + ws.cnt_off);
-  p.ws_ml = reinterpret_cast<float*>(wsb + ws.ml_off);
-  p.ws_o = reinterpret_cast<float*>(wsb + ws.o_off);
+  p.ws_slots = reinterpret_cast<float*>(wsb + ws.slot_off);
   p.b = b;
   p.h = h;
   p.g = g;
@@ -169,14 +196,16 @@ int gqa_decode_attention_ex(void* out, const void* q, const void* k_cache, const
   p.d = d_k;
   p.cap = cap;
   p.max_len = max_len;
-  p.chunk = plan.chunk;
-  p.nch_stride = gqa::nch_stride_for(max_len);
+  p.gblk = plan.gblk;
+  p.nhb = plan.nhb;
+  p.ngroups = g * plan.nhb;
+  p.slot_floats = gqa::slot_floats_for(plan.gblk, d_v);
+  p.workgroups = plan.workgroups;
   p.scale_log2 = scale * kLog2e;
 
   const hipStream_t st = static_cast<hipStream_t>(stream);
-  const hipError_t e = plan.path == GQA_PATH_MATRIX
-                           ? gqa::launch_decode_matrix(p, st)
-                           : gqa::launch_decode_vector(p, dtype, plan.heads_per_block, st);
+  const hipError_t e = plan.path == GQA_PATH_MATRIX ? gqa::launch_decode_matrix(p, st)
+                                                    : gqa::launch_decode_vector(p, dtype, st);
   if (e != hipSuccess) return fail(GQA_ERR_HIP, "gqa_decode_attention launch: %s", hipGetErrorString(e));
   return ok();
 }

@@ -1,12 +1,38 @@
 // Internal declarations shared by the gfx950 kernels and the C-ABI shim.
 //
-// Workspace layout (one buffer, caller-owned, see gqa_decode_workspace_size):
-//   [counters]  int32  [b*h]                      zero between calls
-//   [ml]        float  [b*h][nch_stride][2]       (running max m, sum l) per chunk
-//   [o]         float  [b*h][nch_stride][d_v]     unnormalised partial output
-// Each region starts on a 256-byte boundary. nch_stride = ceil(max_len / 64),
-// the largest chunk count any chunk size (a multiple of 64) can produce.
-// The softmax state is kept in base-2 units: m is the max of scale*log2(e)*q.k.
+// Work schedule (both decode kernels)
+// -----------------------------------
+// The attention of one decode step is cut into units of TILE = 32 cached
+// positions of one "segment" (sequence s, KV-head group grp). Units are
+// ordered (s, grp, tile). With T units in all and P' = min(P, T) of the P
+// persistent workgroups taking part, workgroup p < P' takes the contiguous
+// range [floor(p*T/P'), floor((p+1)*T/P')) (never empty), so
+// every workgroup streams the same number of K/V bytes (within one tile) and
+// all finish together. T depends on the device-side lengths, so each wave
+// recomputes the schedule from lens at kernel start (a prefix sum over b).
+//
+// A workgroup's range is a run of "pieces": maximal runs of tiles inside one
+// segment. Only its first and its last piece can be part of a segment shared
+// with other workgroups; whole segments are finished directly. A shared piece
+// leaves its split-softmax state (m, l, o) in one of the workgroup's two
+// partial slots; the last workgroup of the segment to arrive (an atomic
+// ticket per segment) merges the slots and writes the output.
+//
+// Cross-workgroup visibility without cache-wide fences: on this multi-XCD
+// part a device-scope release fence writes back a whole L2, which costs more
+// than the attention itself. The partial states are therefore written with
+// agent-scope atomic stores (coherent at device scope), their completion is
+// awaited (s_waitcnt vmcnt(0)) before the ticket's agent-scope atomic add, and
+// the merging workgroup reads them with agent-scope atomic loads. Only these
+// atomic accesses touch the shared data, so no L2 writeback or invalidate is
+// needed.
+//
+// Workspace layout (caller-owned, see gqa_decode_workspace_size):
+//   [counters] int32 [b * h]                                  zero between calls
+//   [slots]    float [kMaxWorkgroups][2][slot_floats]         slot = o[gb][d], m[gb], l[gb]
+// slot_floats = gb*d + round_up(2*gb, 4), so every slot and its o block are
+// 16-byte aligned.
+// Each region starts on a 256-byte boundary.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -15,10 +41,12 @@
 
 namespace gqa {
 
-constexpr int kMinChunk = 64;     // chunk granularity (positions)
-constexpr int kMaxChunk = 65536;  // largest chunk the shim accepts
-constexpr int kThreads = 256;     // workgroup size of both decode kernels
+constexpr int kThreads = 256;  // workgroup size of both decode kernels
 constexpr int kWaves = kThreads / 64;
+constexpr int kTile = 32;             // positions per work unit
+constexpr int kMaxWorkgroups = 2048;  // persistent grid bound (workspace sizing)
+constexpr int kMatrixMaxGroup = 64;   // query heads per KV head on the matrix path
+constexpr int kVectorMaxBlock = 8;    // query heads per workgroup on the vector path
 
 struct AppendParams {
   void* k_cache;
@@ -36,42 +64,46 @@ struct DecodeParams {
   const void* v_cache;
   const int32_t* lens;
   int* ws_cnt;
-  float* ws_ml;
-  float* ws_o;
+  float* ws_slots;
   int b, h, g, G, d, cap, max_len;
-  int chunk;       // positions per workgroup
-  int nch_stride;  // chunk slots per (sequence, head) in the workspace
-  float scale_log2;  // scale * log2(e)
+  int gblk;         // query heads handled together (matrix: G; vector: head block)
+  int nhb;          // head blocks per KV head (matrix: 1)
+  int ngroups;      // segments per sequence: g * nhb
+  int slot_floats;  // gblk * d + round_up(2 * gblk, 4)
+  int workgroups;   // persistent grid size P
+  float scale_log2; // scale * log2(e)
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-inline int nch_stride_for(int max_len) {
-  const int n = (max_len + kMinChunk - 1) / kMinChunk;
-  return n > 0 ? n : 1;
-}
-
 struct WorkspaceLayout {
-  size_t cnt_off, ml_off, o_off, total;
+  size_t cnt_off, slot_off, total;
 };
 
-inline WorkspaceLayout workspace_layout(int b, int h, int d_v, int max_len) {
-  const size_t rows = size_t(b) * size_t(h);
-  const size_t nch = size_t(nch_stride_for(max_len));
+inline int slot_floats_for(int gblk, int d_v) { return gblk * d_v + ((2 * gblk + 3) & ~3); }
+
+// gblk_bound: the largest head block any path may use for this shape.
+inline WorkspaceLayout workspace_layout(int b, int h, int gblk_bound, int d_v) {
   WorkspaceLayout w;
   w.cnt_off = 0;
-  w.ml_off = align256(rows * sizeof(int));
-  w.o_off = w.ml_off + align256(rows * nch * 2 * sizeof(float));
-  w.total = w.o_off + align256(rows * nch * size_t(d_v) * sizeof(float));
+  w.slot_off = align256(size_t(b) * size_t(h) * sizeof(int));
+  w.total = w.slot_off + align256(size_t(kMaxWorkgroups) * 2 * size_t(slot_floats_for(gblk_bound, d_v)) * sizeof(float));
   return w;
 }
 
-// Launchers (defined next to their kernels). Return the hipError_t of the
-// launch.
+// LDS the split merge needs (floats): (m, l) of kMergePairs (slot, head)
+// pairs plus three per-head running values.
+constexpr int kMergePairs = 8 * kMatrixMaxGroup;  // a batch of 8 slots for up to 64 heads
+constexpr int kMergeLds = 2 * kMergePairs + 3 * kMatrixMaxGroup;
+
 hipError_t launch_append(const AppendParams& p, int b, int dtype, hipStream_t stream);
-hipError_t launch_decode_vector(const DecodeParams& p, int dtype, int heads_per_block,
-                                hipStream_t stream);
+hipError_t launch_decode_vector(const DecodeParams& p, int dtype, hipStream_t stream);
 hipError_t launch_decode_matrix(const DecodeParams& p, hipStream_t stream);
+
+// Workgroups of the decode kernel instance that fit on one compute unit at
+// once (runtime occupancy query, cached; 0 if the runtime cannot say).
+int matrix_workgroups_per_cu(int G);
+int vector_workgroups_per_cu(int dtype, int d, int heads_per_block);
 
 // Vector-path head block for G query heads per KV head: the smallest power of
 // two >= G, capped at 8 (larger groups use several head blocks).
@@ -79,7 +111,7 @@ inline int vector_heads_per_block(int G) {
   if (G <= 1) return 1;
   if (G <= 2) return 2;
   if (G <= 4) return 4;
-  return 8;
+  return kVectorMaxBlock;
 }
 
 }  // namespace gqa
@@ -105,20 +137,17 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 constexpr float kNegInf = -__builtin_huge_valf();
 
 // ---------------------------------------------------- cross-lane reductions
-// DPP controls (GFX9 encoding).
-constexpr int kDppQuadXor1 = 0xB1;       // quad_perm [1,0,3,2]
-constexpr int kDppQuadXor2 = 0x4E;       // quad_perm [2,3,0,1]
-constexpr int kDppRowHalfMirror = 0x141; // lane i <-> 7-i within 8
-constexpr int kDppRowMirror = 0x140;     // lane i <-> 15-i within 16
+constexpr int kDppQuadXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppRowHalfMirror = 0x141;  // lane i <-> 7-i within 8
+constexpr int kDppRowMirror = 0x140;      // lane i <-> 15-i within 16
 
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
 }
 
-__device__ __forceinline__ float xor_shuffle(float x, int mask) {
-  return __shfl_xor(x, mask, 64);
-}
+__device__ __forceinline__ float xor_shuffle(float x, int mask) { return __shfl_xor(x, mask, 64); }
 
 // Sum over each aligned group of R consecutive lanes (R a power of two <= 64);
 // every lane of the group receives the group sum.
@@ -133,11 +162,11 @@ __device__ __forceinline__ float group_sum(float x) {
   return x;
 }
 
-// Combine two split-softmax states (m in base-2 units); the result is written
-// to (m, l). Either state may be empty (m = -inf, l = 0, acc = 0).
 struct MergeWeights {
   float a, b;
 };
+// Weights that combine two split-softmax states with base-2 maxima m1, m2
+// (either may be an empty state, m = -inf); m_out receives the joint max.
 __device__ __forceinline__ MergeWeights merge_weights(float m1, float m2, float& m_out) {
   const float M = fmaxf(m1, m2);
   const float sub = (M == kNegInf) ? 0.0f : M;
@@ -145,84 +174,372 @@ __device__ __forceinline__ MergeWeights merge_weights(float m1, float m2, float&
   return {fast_exp2(m1 - sub), fast_exp2(m2 - sub)};
 }
 
-// ------------------------------------------------------- split finishing
-// Called by every thread of a workgroup once its combined state for query
-// heads [i0, i0 + nh) of sequence s over chunk c is in LDS:
-//   sm_m[nh], sm_l[nh]: base-2 running max and sum; sm_o[nh][d]: unnormalised
-//   output. n_valid is the number of chunks of this sequence that hold
-//   positions.
-// With one chunk the output is written directly. Otherwise the state goes to
-// the workspace, and the last workgroup of the (s, i0) group to finish
-// (an atomic ticket, released and acquired with device-scope fences) merges
-// every chunk's state and writes the output, then re-zeroes the ticket.
-template <typename TOut>
-__device__ void finish_chunk(const DecodeParams& p, int s, int i0, int nh, int c, int n_valid,
-                             const float* sm_m, const float* sm_l, const float* sm_o,
-                             int* sm_flag) {
-  const int tid = threadIdx.x;
-  const int d = p.d;
-  TOut* out = static_cast<TOut*>(p.out);
-  const size_t out_row0 = (size_t(s) * p.h + i0) * d;
-  if (n_valid == 1) {
-    for (int idx = tid; idx < nh * d; idx += kThreads) {
-      const float l = sm_l[idx / d];
-      const float v = l > 0.0f ? sm_o[idx] / l : 0.0f;
-      if constexpr (sizeof(TOut) == 2) out[out_row0 + idx] = f32_to_bf16(v);
-      else out[out_row0 + idx] = v;
-    }
-    return;
-  }
-  const size_t row0 = size_t(s) * p.h + i0;
-  const size_t stride = size_t(p.nch_stride);
-  for (int idx = tid; idx < nh * d; idx += kThreads) {
-    const int hh = idx / d, dd = idx - hh * d;
-    p.ws_o[((row0 + hh) * stride + c) * d + dd] = sm_o[idx];
-  }
-  for (int hh = tid; hh < nh; hh += kThreads) {
-    p.ws_ml[((row0 + hh) * stride + c) * 2 + 0] = sm_m[hh];
-    p.ws_ml[((row0 + hh) * stride + c) * 2 + 1] = sm_l[hh];
-  }
-  __threadfence();  // release this workgroup's partials device-wide
-  __syncthreads();
-  if (tid == 0) {
-    const int prev = atomicAdd(&p.ws_cnt[row0], 1);
-    *sm_flag = (prev == n_valid - 1);
-  }
-  __syncthreads();
-  if (!*sm_flag) return;
-  __threadfence();  // acquire the other workgroups' partials
-  for (int idx = tid; idx < nh * d; idx += kThreads) {
-    const int hh = idx / d, dd = idx - hh * d;
-    const size_t base = (row0 + hh) * stride;
-    float M = kNegInf;
-    for (int cc = 0; cc < n_valid; ++cc) M = fmaxf(M, p.ws_ml[(base + cc) * 2]);
-    const float sub = (M == kNegInf) ? 0.0f : M;
-    float num = 0.0f, den = 0.0f;
-    for (int cc = 0; cc < n_valid; ++cc) {
-      const float wgt = fast_exp2(p.ws_ml[(base + cc) * 2] - sub);
-      num += wgt * p.ws_o[(base + cc) * d + dd];
-      den += wgt * p.ws_ml[(base + cc) * 2 + 1];
-    }
-    const float v = den > 0.0f ? num / den : 0.0f;
-    if constexpr (sizeof(TOut) == 2) out[out_row0 + idx] = f32_to_bf16(v);
-    else out[out_row0 + idx] = v;
-  }
-  if (tid == 0) p.ws_cnt[row0] = 0;
-}
+// ------------------------------------------------------- device-coherent I/O
+// Buffer accesses with cache policy SC1 (device scope): stores write through
+// to the device-coherent level and loads do not hit stale per-XCD copies.
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+constexpr int kCpolDevice = 16;                   // SC1
+constexpr int kBufferWord3 = 0x00020000;          // raw (untyped) buffer resource
 
-// Zero output rows of a sequence that attends no positions.
-template <typename TOut>
-__device__ void write_zero_rows(const DecodeParams& p, int s, int i0, int nh) {
-  TOut* out = static_cast<TOut*>(p.out);
-  const size_t row0 = (size_t(s) * p.h + i0) * p.d;
-  for (int idx = threadIdx.x; idx < nh * p.d; idx += kThreads) out[row0 + idx] = TOut(0);
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t slots_rsrc(const DecodeParams& p) {
+  const int bytes = 2 * p.workgroups * p.slot_floats * int(sizeof(float));
+  return __builtin_amdgcn_make_buffer_rsrc(p.ws_slots, 0, bytes, kBufferWord3);
 }
+__device__ __forceinline__ void coherent_store4(__amdgpu_buffer_rsrc_t r, int byte_off, f32x4v v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4v, v), r, byte_off, 0, kCpolDevice);
+}
+__device__ __forceinline__ void coherent_store1(__amdgpu_buffer_rsrc_t r, int byte_off, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, byte_off, 0, kCpolDevice);
+}
+__device__ __forceinline__ f32x4v coherent_load4(__amdgpu_buffer_rsrc_t r, int byte_off) {
+  return __builtin_bit_cast(f32x4v, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, kCpolDevice));
+}
+__device__ __forceinline__ float coherent_load1(__amdgpu_buffer_rsrc_t r, int byte_off) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, kCpolDevice));
+}
+// Wait until this wave's earlier memory writes have completed.
+__device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // Effective attended length: lens clamped to [0, max_len].
 __device__ __forceinline__ int attended_len(const DecodeParams& p, int s) {
   int L = p.lens[s];
   L = L < 0 ? 0 : L;
   return L > p.max_len ? p.max_len : L;
+}
+
+__device__ __forceinline__ int tiles_of(int L) { return (L + kTile - 1) / kTile; }
+
+// Workgroup owning unit u when T units are split over P workgroups as
+// [floor(p*T/P), floor((p+1)*T/P)): the largest p with floor(p*T/P) <= u.
+__device__ __forceinline__ int owner_of(long long u, long long T, int P) {
+  return int(((u + 1) * P + T - 1) / T) - 1;
+}
+__device__ __forceinline__ long long range_begin(int p, long long T, int P) { return (long long)p * T / P; }
+
+// Wave-level inclusive prefix sum over 64 lanes.
+__device__ __forceinline__ long long wave_inclusive_scan(long long v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const long long o = __shfl_up(v, off, 64);
+    if (lane >= off) v += o;
+  }
+  return v;
+}
+
+// Attended lengths as seen by one wave. For b <= 64 every lane keeps the
+// length of sequence `lane` in a register after one load and lengths are
+// read with a shuffle; larger batches read lens through the cache.
+struct LensView {
+  const DecodeParams* p;
+  int reg;
+  bool in_regs;
+  __device__ void init(const DecodeParams& prm) {
+    p = &prm;
+    in_regs = prm.b <= 64;
+    const int lane = threadIdx.x & 63;
+    reg = (in_regs && lane < prm.b) ? attended_len(prm, lane) : 0;
+  }
+  // Length of sequence s (wave-uniform s, every lane active).
+  __device__ int len(int s) const { return in_regs ? __shfl(reg, s, 64) : attended_len(*p, s); }
+  // Length of sequence base + lane for the calling lane (0 beyond b).
+  __device__ int lane_len(int base) const {
+    const int s = base + (threadIdx.x & 63);
+    if (in_regs) return base == 0 ? reg : 0;
+    return s < p->b ? attended_len(*p, s) : 0;
+  }
+};
+
+// Where the schedule puts the first unit of workgroup `workgroup`: the
+// sequence s holding it (or b if the workgroup has no units), the unit index
+// of that sequence's first unit, the total unit count T, and the number of
+// workgroups that take part, P' = min(P, T), so that every taking part has a
+// non-empty range. Every lane of the calling wave gets the same answer.
+struct Located {
+  long long total;
+  long long seq_base;
+  int s;
+  int parts;
+};
+__device__ Located locate_units(const DecodeParams& p, const LensView& lv, int workgroup) {
+  long long carry = 0;
+  for (int base = 0; base < p.b; base += 64) {  // total units
+    const long long v = (long long)p.ngroups * tiles_of(lv.lane_len(base));
+    const long long incl = wave_inclusive_scan(v);
+    carry += __shfl(incl, 63, 64);
+  }
+  Located r;
+  r.total = carry;
+  r.parts = carry < p.workgroups ? int(carry) : p.workgroups;
+  r.s = p.b;
+  r.seq_base = carry;
+  if (workgroup >= r.parts) return r;
+  const long long u0 = range_begin(workgroup, carry, r.parts);
+  carry = 0;
+  for (int base = 0; base < p.b; base += 64) {
+    const int s = base + (threadIdx.x & 63);
+    const long long v = (long long)p.ngroups * tiles_of(lv.lane_len(base));
+    const long long incl = wave_inclusive_scan(v) + carry;
+    const long long excl = incl - v;
+    const unsigned long long hit = __ballot(s < p.b && v > 0 && excl <= u0 && u0 < incl);
+    if (hit) {
+      const int src = __ffsll((long long)hit) - 1;
+      r.s = base + src;
+      r.seq_base = __shfl(excl, src, 64);
+      return r;
+    }
+    carry = __shfl(incl, 63, 64);
+  }
+  return r;
+}
+
+// One piece of a workgroup's range: tiles [tile_begin, tile_end) of segment
+// (s, grp), i.e. positions [tile_begin*kTile, min(L, tile_end*kTile)).
+// p0 and p1 are the first and last workgroups whose ranges touch the segment.
+struct Piece {
+  int s, grp, L;
+  int tile_begin, tile_end, seg_tiles;
+  int p0, p1;
+};
+
+// Iterates the pieces of workgroup `wg`'s unit range.
+struct PieceWalker {
+  const DecodeParams* p;
+  LensView lv;
+  long long total, u, u_end, seq_base;
+  int s, parts;
+
+  __device__ void init(const DecodeParams& prm, int wg) {
+    p = &prm;
+    lv.init(prm);
+    const Located loc = locate_units(prm, lv, wg);
+    total = loc.total;
+    parts = loc.parts;
+    s = loc.s;
+    seq_base = loc.seq_base;
+    if (wg >= parts) {
+      u = u_end = 0;
+      return;
+    }
+    u = range_begin(wg, total, parts);
+    u_end = range_begin(wg + 1, total, parts);
+  }
+
+  __device__ bool next(Piece& pc) {
+    if (u >= u_end) return false;
+    int L = lv.len(s);
+    long long seq_units = (long long)p->ngroups * tiles_of(L);
+    while (u >= seq_base + seq_units && s + 1 < p->b) {  // skip to the sequence holding u
+      seq_base += seq_units;
+      ++s;
+      L = lv.len(s);
+      seq_units = (long long)p->ngroups * tiles_of(L);
+    }
+    const int nt = tiles_of(L);
+    const long long within = u - seq_base;
+    pc.s = s;
+    pc.L = L;
+    pc.grp = int(within / nt);
+    pc.seg_tiles = nt;
+    pc.tile_begin = int(within - (long long)pc.grp * nt);
+    const long long remain = u_end - u;
+    const long long seg_left = nt - pc.tile_begin;
+    pc.tile_end = pc.tile_begin + int(remain < seg_left ? remain : seg_left);
+    const long long seg_u0 = seq_base + (long long)pc.grp * nt;
+    pc.p0 = owner_of(seg_u0, total, parts);
+    pc.p1 = owner_of(seg_u0 + nt - 1, total, parts);
+    u += pc.tile_end - pc.tile_begin;
+    return true;
+  }
+};
+
+// ------------------------------------------------------- piece finishing
+template <typename TOut>
+__device__ __forceinline__ void store_out(TOut* out, size_t idx, float v) {
+  if constexpr (sizeof(TOut) == 2) out[idx] = f32_to_bf16(v);
+  else out[idx] = v;
+}
+
+// Shared pieces whose tickets are still to be taken (at most the first and
+// the last piece of a workgroup's range).
+struct Pending {
+  int n;
+  int s[2], grp[2], p0[2], p1[2], i0[2], nh[2];
+};
+
+// Called by every thread of the workgroup once the piece's combined state for
+// query heads [i0, i0 + nh) is in LDS: sm_m[nh], sm_l[nh] (base-2 max, sum)
+// and sm_o[nh][d] (unnormalised output, 16-byte aligned).
+//
+// A segment inside one workgroup is written out directly. Otherwise the piece
+// goes to a partial slot of this workgroup: slot 1 if this workgroup owns the
+// segment's first unit (the piece is the last of its range), slot 0 if not
+// (the piece is the first of its range), and is recorded in `pend` for
+// settle_pending. (Taking the ticket right away, as the kernels do, measured
+// faster than deferring every ticket to the end of the range: deferral puts
+// two ticket round trips and up to two merges in series at the very end.)
+template <typename TOut>
+__device__ void publish_piece(const DecodeParams& p, const Piece& pc, int wg, int i0, int nh,
+                              const float* sm_m, const float* sm_l, const float* sm_o, Pending& pend) {
+  const int tid = threadIdx.x;
+  const int d = p.d;
+  if (pc.p0 == pc.p1) {
+    TOut* out = static_cast<TOut*>(p.out);
+    const size_t out_row0 = (size_t(pc.s) * p.h + i0) * d;
+    for (int idx = tid; idx < nh * d; idx += kThreads) {
+      const float l = sm_l[idx / d];
+      store_out(out, out_row0 + idx, l > 0.0f ? sm_o[idx] / l : 0.0f);
+    }
+    return;
+  }
+  const __amdgpu_buffer_rsrc_t rs = slots_rsrc(p);
+  const int slot_bytes = p.slot_floats * int(sizeof(float));
+  const int ml_off = p.gblk * d * int(sizeof(float));  // m then l after the o block
+  const int mine = (wg * 2 + (wg == pc.p0 ? 1 : 0)) * slot_bytes;
+  const int n4 = nh * d / 4;
+  for (int c4 = tid; c4 < n4; c4 += kThreads)
+    coherent_store4(rs, mine + c4 * 16, *reinterpret_cast<const f32x4v*>(sm_o + 4 * c4));
+  for (int hh = tid; hh < nh; hh += kThreads) {
+    coherent_store1(rs, mine + ml_off + hh * 4, sm_m[hh]);
+    coherent_store1(rs, mine + ml_off + (p.gblk + hh) * 4, sm_l[hh]);
+  }
+  const int k = pend.n++;
+  pend.s[k] = pc.s;
+  pend.grp[k] = pc.grp;
+  pend.p0[k] = pc.p0;
+  pend.p1[k] = pc.p1;
+  pend.i0[k] = i0;
+  pend.nh[k] = nh;
+}
+
+// Merge of the n_slots partial states of one shared segment, by the
+// workgroup that took its last ticket: slot 1 of p0 and slot 0 of
+// p0+1 .. p1. Slots are read in batches of kMergeBatch; within a batch every
+// (m, l) load and every partial-output load of this thread is issued before
+// any is used, so a batch costs one memory round trip. Per-head running max,
+// rescale factor and denominator live in LDS.
+constexpr int kMergeBatch = 8;
+
+template <typename TOut, int MAXC>
+__device__ void merge_segment(const DecodeParams& p, int s, int p0, int n_slots, int i0, int nh,
+                              float* sm_merge) {
+  const int tid = threadIdx.x;
+  const int d = p.d;
+  const __amdgpu_buffer_rsrc_t rs = slots_rsrc(p);
+  const int slot_bytes = p.slot_floats * int(sizeof(float));
+  const int ml_off = p.gblk * d * int(sizeof(float));
+  const int n4 = nh * d / 4;
+  float* pm = sm_merge;                // [kMergeBatch][nh] m, then weights
+  float* pl = sm_merge + kMergePairs;  // [kMergeBatch][nh] l
+  float* run_m = sm_merge + 2 * kMergePairs;
+  float* run_den = run_m + kMatrixMaxGroup;
+  float* run_r = run_den + kMatrixMaxGroup;
+  f32x4v acc[MAXC];
+#pragma unroll
+  for (int c = 0; c < MAXC; ++c) acc[c] = f32x4v{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int hh = tid; hh < nh; hh += kThreads) {
+    run_m[hh] = kNegInf;
+    run_den[hh] = 0.0f;
+  }
+  for (int k0 = 0; k0 < n_slots; k0 += kMergeBatch) {
+    const int kn = min(kMergeBatch, n_slots - k0);
+    f32x4v o[kMergeBatch][MAXC];
+#pragma unroll
+    for (int k = 0; k < kMergeBatch; ++k) {
+      const int kk = k0 + k;
+      const int sb = ((p0 + kk) * 2 + (kk == 0 ? 1 : 0)) * slot_bytes;
+#pragma unroll
+      for (int c = 0; c < MAXC; ++c) {
+        const int c4 = tid + c * kThreads;
+        o[k][c] = (k < kn && c4 < n4) ? coherent_load4(rs, sb + c4 * 16) : f32x4v{0.0f, 0.0f, 0.0f, 0.0f};
+      }
+    }
+    for (int pair = tid; pair < kn * nh; pair += kThreads) {
+      const int k = pair / nh, hh = pair - k * nh;
+      const int kk = k0 + k;
+      const int sb = ((p0 + kk) * 2 + (kk == 0 ? 1 : 0)) * slot_bytes + ml_off;
+      pm[pair] = coherent_load1(rs, sb + hh * 4);
+      pl[pair] = coherent_load1(rs, sb + (p.gblk + hh) * 4);
+    }
+    __syncthreads();
+    for (int hh = tid; hh < nh; hh += kThreads) {
+      float M = run_m[hh];
+      for (int k = 0; k < kn; ++k) M = fmaxf(M, pm[k * nh + hh]);
+      const float sub = (M == kNegInf) ? 0.0f : M;
+      const float r = fast_exp2(run_m[hh] - sub);
+      float den = run_den[hh] * r;
+      for (int k = 0; k < kn; ++k) {
+        const float wgt = fast_exp2(pm[k * nh + hh] - sub);
+        den = fmaf(wgt, pl[k * nh + hh], den);
+        pm[k * nh + hh] = wgt;
+      }
+      run_m[hh] = M;
+      run_den[hh] = den;
+      run_r[hh] = r;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int c = 0; c < MAXC; ++c) {
+      const int c4 = tid + c * kThreads;
+      if (c4 < n4) {
+        const int hh = (4 * c4) / d;
+        f32x4v a = acc[c] * run_r[hh];
+#pragma unroll
+        for (int k = 0; k < kMergeBatch; ++k)
+          if (k < kn) a += pm[k * nh + hh] * o[k][c];
+        acc[c] = a;
+      }
+    }
+    __syncthreads();
+  }
+  TOut* out = static_cast<TOut*>(p.out);
+  const size_t out_row0 = (size_t(s) * p.h + i0) * d;
+#pragma unroll
+  for (int c = 0; c < MAXC; ++c) {
+    const int c4 = tid + c * kThreads;
+    if (c4 < n4) {
+      const int hh = (4 * c4) / d;
+      const float den = run_den[hh];
+      const float inv = den > 0.0f ? 1.0f / den : 0.0f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) store_out(out, out_row0 + 4 * c4 + e, acc[c][e] * inv);
+    }
+  }
+}
+
+// Take the tickets of the workgroup's pending pieces (after their partial
+// stores have completed) and merge every segment for which this workgroup
+// arrived last; the merger re-zeroes the segment's ticket.
+template <typename TOut, int MAXC>
+__device__ void settle_pending(const DecodeParams& p, const Pending& pend, float* sm_merge, int* sm_flag) {
+  if (pend.n == 0) return;
+  wait_stores();
+  __syncthreads();
+  for (int k = 0; k < pend.n; ++k) {
+    int* cnt = p.ws_cnt + size_t(pend.s[k]) * p.ngroups + pend.grp[k];
+    if (threadIdx.x == 0) *sm_flag = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    const int n_slots = pend.p1[k] - pend.p0[k] + 1;
+    const bool last = *sm_flag == n_slots - 1;
+    __syncthreads();
+    if (last) {
+      merge_segment<TOut, MAXC>(p, pend.s[k], pend.p0[k], n_slots, pend.i0[k], pend.nh[k], sm_merge);
+      if (threadIdx.x == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
+// Zero the output rows of sequences that attend nothing; sequence s is
+// handled by workgroup s mod P.
+template <typename TOut>
+__device__ void zero_empty_sequences(const DecodeParams& p, int wg) {
+  TOut* out = static_cast<TOut*>(p.out);
+  for (int s = wg; s < p.b; s += p.workgroups) {
+    if (attended_len(p, s) != 0) continue;
+    const size_t row0 = size_t(s) * p.h * p.d;
+    for (int idx = threadIdx.x; idx < p.h * p.d; idx += kThreads) out[row0 + idx] = TOut(0);
+  }
 }
 
 }  // namespace gqa

@@ -2,31 +2,20 @@
 // length by one ("LLM inference 05" notes: push K, push V before attending;
 // MQA review §2.4 / §3: the new row is concatenated on the position axis).
 //
-// One workgroup per sequence: it reads lens[s] once, copies the g new K rows
-// and g new V rows into slot lens[s] with 16-byte (or narrower) moves, and
-// only after a barrier writes lens[s] + 1, so every thread used the old
-// length. A length outside [0, cap) leaves the sequence untouched.
+// One workgroup per sequence reads lens[s] once. Its threads split the g new
+// K rows and g new V rows into UNIT-byte pieces, load every piece they own
+// before storing any (so the copy costs one memory round trip, not one per
+// row), and write them to slot lens[s]. Only after a barrier does one thread
+// write lens[s] + 1, so every thread used the old length. A length outside
+// [0, cap) leaves the sequence untouched.
 #include "gqa_internal.hpp"
 
 namespace gqa {
 namespace {
 
-// Copy n_bytes from src to dst with the widest unit that divides both the
-// size and the alignment (caches are contiguous rows, so rows of 16-byte
-// multiples move as uint4).
-__device__ __forceinline__ void copy_row_bytes(char* dst, const char* src, int n_bytes) {
-  if ((n_bytes & 15) == 0 && ((reinterpret_cast<uintptr_t>(dst) | reinterpret_cast<uintptr_t>(src)) & 15) == 0) {
-    for (int i = threadIdx.x; i < (n_bytes >> 4); i += blockDim.x)
-      reinterpret_cast<uint4*>(dst)[i] = reinterpret_cast<const uint4*>(src)[i];
-  } else if ((n_bytes & 3) == 0 && ((reinterpret_cast<uintptr_t>(dst) | reinterpret_cast<uintptr_t>(src)) & 3) == 0) {
-    for (int i = threadIdx.x; i < (n_bytes >> 2); i += blockDim.x)
-      reinterpret_cast<uint32_t*>(dst)[i] = reinterpret_cast<const uint32_t*>(src)[i];
-  } else {
-    for (int i = threadIdx.x; i < (n_bytes >> 1); i += blockDim.x)
-      reinterpret_cast<uint16_t*>(dst)[i] = reinterpret_cast<const uint16_t*>(src)[i];
-  }
-}
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
+template <typename UNIT, int PER_THREAD>
 __global__ __launch_bounds__(256) void kv_append_kernel(AppendParams p, int esize) {
   const int s = blockIdx.x;
   __shared__ int s_pos;
@@ -34,28 +23,62 @@ __global__ __launch_bounds__(256) void kv_append_kernel(AppendParams p, int esiz
   __syncthreads();
   const int pos = s_pos;
   if (pos < 0 || pos >= p.cap) return;  // precondition violated: change nothing
-  const int kb = p.d_k * esize, vb = p.d_v * esize;
-  for (int j = 0; j < p.g; ++j) {
-    const size_t head = size_t(s) * p.g + j;
-    char* kdst = static_cast<char*>(p.k_cache) + (head * p.cap + pos) * kb;
-    char* vdst = static_cast<char*>(p.v_cache) + (head * p.cap + pos) * vb;
-    copy_row_bytes(kdst, static_cast<const char*>(p.k_new) + head * kb, kb);
-    copy_row_bytes(vdst, static_cast<const char*>(p.v_new) + head * vb, vb);
+  const int ku = p.d_k * esize / int(sizeof(UNIT));  // units per K row
+  const int vu = p.d_v * esize / int(sizeof(UNIT));
+  const int total = p.g * (ku + vu);
+  const UNIT* kn = static_cast<const UNIT*>(p.k_new) + size_t(s) * p.g * ku;
+  const UNIT* vn = static_cast<const UNIT*>(p.v_new) + size_t(s) * p.g * vu;
+  UNIT* kc = static_cast<UNIT*>(p.k_cache);
+  UNIT* vc = static_cast<UNIT*>(p.v_cache);
+  for (int base = 0; base < total; base += PER_THREAD * blockDim.x) {
+    UNIT val[PER_THREAD] = {};
+    UNIT* dst[PER_THREAD];
+#pragma unroll
+    for (int r = 0; r < PER_THREAD; ++r) {
+      const int c = base + r * blockDim.x + threadIdx.x;
+      dst[r] = nullptr;
+      if (c < total) {
+        if (c < p.g * ku) {
+          const int j = c / ku, x = c - j * ku;
+          val[r] = kn[c];
+          dst[r] = kc + ((size_t(s) * p.g + j) * p.cap + pos) * ku + x;
+        } else {
+          const int cv = c - p.g * ku;
+          const int j = cv / vu, x = cv - j * vu;
+          val[r] = vn[cv];
+          dst[r] = vc + ((size_t(s) * p.g + j) * p.cap + pos) * vu + x;
+        }
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < PER_THREAD; ++r)
+      if (dst[r]) *dst[r] = val[r];
   }
   __syncthreads();
   if (threadIdx.x == 0) p.lens[s] = pos + 1;
 }
 
+bool aligned(const void* ptr, size_t a) { return (reinterpret_cast<uintptr_t>(ptr) % a) == 0; }
+
 }  // namespace
 
 hipError_t launch_append(const AppendParams& p, int b, int dtype, hipStream_t stream) {
   const int esize = dtype == 0 ? 4 : 2;
-  // one wave per 16-byte unit of the widest row, at least one wave, at most 256 threads
-  int units = ((p.d_k > p.d_v ? p.d_k : p.d_v) * esize + 15) / 16;
-  int threads = ((units + 63) / 64) * 64;
-  if (threads < 64) threads = 64;
-  if (threads > 256) threads = 256;
-  hipLaunchKernelGGL(kv_append_kernel, dim3(b), dim3(threads), 0, stream, p, esize);
+  const size_t kb = size_t(p.d_k) * esize, vb = size_t(p.d_v) * esize;
+  auto fits = [&](size_t a) {
+    return kb % a == 0 && vb % a == 0 && aligned(p.k_cache, a) && aligned(p.v_cache, a) &&
+           aligned(p.k_new, a) && aligned(p.v_new, a);
+  };
+  const size_t row_units16 = size_t(p.g) * (kb + vb) / 16;
+  int threads = int((row_units16 + 3) / 4);
+  threads = threads < 64 ? 64 : (threads > 256 ? 256 : ((threads + 63) / 64) * 64);
+  if (fits(16)) {
+    hipLaunchKernelGGL((kv_append_kernel<u32x4, 4>), dim3(b), dim3(threads), 0, stream, p, esize);
+  } else if (fits(4)) {
+    hipLaunchKernelGGL((kv_append_kernel<uint32_t, 4>), dim3(b), dim3(256), 0, stream, p, esize);
+  } else {
+    hipLaunchKernelGGL((kv_append_kernel<uint16_t, 4>), dim3(b), dim3(256), 0, stream, p, esize);
+  }
   return hipGetLastError();
 }
 

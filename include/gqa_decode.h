@@ -94,14 +94,16 @@ int gqa_kv_append(void* k_cache, void* v_cache, const void* k_new, const void* v
 
 /*
  * Bytes of device workspace gqa_decode_attention needs for this shape; the
- * value covers every path and chunk size, so one buffer serves all calls with
- * shapes no larger than these. Returns 0 for invalid arguments.
+ * value covers every path and launch size, so one buffer serves all calls
+ * with b, h/g and d_v no larger than these (it does not grow with max_len).
+ * Returns 0 for invalid arguments.
  *
- * The workspace holds split-softmax partials and one int32 counter per
- * (sequence, query head). The counters must be ZERO before the first call
- * that uses a buffer (e.g. allocate it zero-filled); every call leaves them
- * zero again. Two calls that share a workspace must be ordered (same stream
- * or synchronised); calls with distinct workspaces may run concurrently.
+ * The workspace holds int32 tickets (at most one per sequence and query
+ * head) and the split-softmax partial states of the persistent workgroups. The tickets
+ * must be ZERO before the first call that uses a buffer (e.g. allocate it
+ * zero-filled); every call leaves them zero again. Two calls that share a
+ * workspace must be ordered (same stream or synchronised); calls with
+ * distinct workspaces may run concurrently.
  */
 size_t gqa_decode_workspace_size(int b, int h, int g, int d_k, int d_v, int max_len, int dtype);
 
@@ -135,22 +137,24 @@ int gqa_decode_attention(void* out, const void* q, const void* k_cache, const vo
  * gqa_decode_attention with explicit launch choices, for tests and tuning.
  * path: GQA_PATH_AUTO / GQA_PATH_VECTOR / GQA_PATH_MATRIX (MATRIX on an
  *   unsupported shape gives GQA_ERR_UNSUPPORTED).
- * chunk_tokens: positions per workgroup; 0 = automatic, otherwise a multiple
- *   of 64 in [64, 65536] (GQA_ERR_UNSUPPORTED otherwise).
+ * workgroups: size of the persistent grid that splits the work evenly;
+ *   0 = automatic (compute units x resident workgroups per unit), otherwise
+ *   1 .. 2048 (GQA_ERR_UNSUPPORTED outside that range).
  * Results equal gqa_decode_attention's up to floating-point summation order.
  */
 int gqa_decode_attention_ex(void* out, const void* q, const void* k_cache, const void* v_cache,
                             const int32_t* lens, int b, int h, int g, int d_k, int d_v, int cap,
                             int max_len, float scale, int dtype, void* workspace,
-                            size_t workspace_bytes, void* stream, int path, int chunk_tokens);
+                            size_t workspace_bytes, void* stream, int path, int workgroups);
 
 /*
- * Describe the launch gqa_decode_attention_ex would make, without enqueueing
- * anything: writes the chosen path (GQA_PATH_VECTOR or GQA_PATH_MATRIX) and
- * chunk size. Same argument checks as the real call, minus pointers.
+ * Describe the launch gqa_decode_attention_ex would make on the current
+ * device, without enqueueing anything: writes the chosen path
+ * (GQA_PATH_VECTOR or GQA_PATH_MATRIX) and persistent grid size. Same
+ * argument checks as the real call, minus pointers.
  */
 int gqa_decode_plan(int b, int h, int g, int d_k, int d_v, int cap, int max_len, int dtype,
-                    int path, int chunk_tokens, int* chosen_path, int* chosen_chunk_tokens);
+                    int path, int workgroups, int* chosen_path, int* chosen_workgroups);
 
 /* Message for the calling thread's last non-OK return ("" if none). */
 const char* gqa_last_error(void);

@@ -49,11 +49,11 @@ def test_header_status_codes_match_binding():
 
 def _attn(lib, **kw):
     a = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, lens=FAKE, b=2, h=8, g=2, dk=128, dv=128, cap=100,
-             max_len=50, scale=0.1, dtype=_lib.BF16, ws=FAKE, ws_bytes=1 << 30, stream=None, path=0, chunk=0)
+             max_len=50, scale=0.1, dtype=_lib.BF16, ws=FAKE, ws_bytes=1 << 30, stream=None, path=0, wgs=0)
     a.update(kw)
     return lib.gqa_decode_attention_ex(a["out"], a["q"], a["k"], a["v"], a["lens"], a["b"], a["h"], a["g"],
                                        a["dk"], a["dv"], a["cap"], a["max_len"], a["scale"], a["dtype"],
-                                       a["ws"], a["ws_bytes"], a["stream"], a["path"], a["chunk"])
+                                       a["ws"], a["ws_bytes"], a["stream"], a["path"], a["wgs"])
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -72,8 +72,8 @@ def _attn(lib, **kw):
     (dict(ws=None), _lib.ERR_WORKSPACE),
     (dict(ws_bytes=16), _lib.ERR_WORKSPACE),
     (dict(ws=ctypes.c_void_p(0x1010)), _lib.ERR_ARG),
-    (dict(chunk=100), _lib.ERR_UNSUPPORTED),
-    (dict(chunk=32), _lib.ERR_UNSUPPORTED),
+    (dict(wgs=-1), _lib.ERR_UNSUPPORTED),
+    (dict(wgs=2049), _lib.ERR_UNSUPPORTED),
     (dict(path=9), _lib.ERR_UNSUPPORTED),
     (dict(path=_lib.PATH_MATRIX, dtype=_lib.F32), _lib.ERR_UNSUPPORTED),
     (dict(path=_lib.PATH_MATRIX, dk=64, dv=64), _lib.ERR_UNSUPPORTED),
@@ -102,19 +102,21 @@ def test_append_rejects(lib):
 def test_workspace_size(lib):
     ws = lib.gqa_decode_workspace_size
     n = ws(16, 64, 8, 128, 128, 8256, _lib.BF16)
-    # counters + (m, l) + partial outputs for ceil(8256 / 64) chunk slots per row
-    rows, nch = 16 * 64, (8256 + 63) // 64
-    assert n >= rows * 4 + rows * nch * (2 + 128) * 4
+    # tickets + two partial slots (m, l, o for a group of 8 heads) per persistent workgroup
+    assert n >= 16 * 64 * 4 + 2048 * 2 * 8 * (128 + 2) * 4
     assert n % 256 == 0
+    assert ws(16, 64, 8, 128, 128, 100, _lib.BF16) == n  # independent of the length
+    # groups smaller than the vector head block are sized for the block (G = 3 -> 4 heads)
+    assert ws(1, 12, 4, 128, 128, 10, _lib.BF16) >= 2048 * 2 * 4 * 130 * 4
     assert ws(16, 64, 7, 128, 128, 100, _lib.BF16) == 0  # h % g != 0
     assert ws(16, 64, 8, 128, 128, -1, _lib.BF16) == 0
     assert ws(1, 1, 1, 16, 16, 0, _lib.F32) > 0
 
 
 def test_plan_choices(lib):
-    def plan(b, h, g, d, cap, max_len, dtype, path=0, chunk=0):
+    def plan(b, h, g, d, cap, max_len, dtype, path=0, wgs=0):
         p, c = ctypes.c_int(), ctypes.c_int()
-        rc = lib.gqa_decode_plan(b, h, g, d, d, cap, max_len, dtype, path, chunk, ctypes.byref(p), ctypes.byref(c))
+        rc = lib.gqa_decode_plan(b, h, g, d, d, cap, max_len, dtype, path, wgs, ctypes.byref(p), ctypes.byref(c))
         assert rc == _lib.OK, lib.gqa_last_error()
         return p.value, c.value
     assert plan(16, 64, 8, 128, 8256, 8193, _lib.BF16)[0] == _lib.PATH_MATRIX
@@ -124,5 +126,5 @@ def test_plan_choices(lib):
     for args in [(16, 64, 8, 128, 8256, 8193, _lib.BF16), (2, 4, 2, 16, 128, 65, _lib.F32),
                  (64, 28, 4, 128, 2112, 2080, _lib.BF16)]:
         _, c = plan(*args)
-        assert c % 64 == 0 and 64 <= c <= 1024
-    assert plan(16, 64, 8, 128, 8256, 8193, _lib.BF16, path=_lib.PATH_VECTOR, chunk=256) == (_lib.PATH_VECTOR, 256)
+        assert 1 <= c <= 2048
+    assert plan(16, 64, 8, 128, 8256, 8193, _lib.BF16, path=_lib.PATH_VECTOR, wgs=77) == (_lib.PATH_VECTOR, 77)

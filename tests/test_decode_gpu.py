@@ -1,8 +1,8 @@
 """GPU decode parity against the fp64 oracle, through the C ABI.
 
 Covers every workload at full size (one decode step: append, then attend),
-both kernels (vector and matrix path) and several chunk sizes on the same
-inputs, the 32-step decode loop, and edge cases: empty and length-1
+both kernels (vector and matrix path) and several persistent grid sizes on
+the same inputs, the 32-step decode loop, and edge cases: empty and length-1
 sequences, ragged tails, group sizes that are not powers of two, the largest
 groups, every supported head dim, and lengths clamped by max_len. Caches are
 NaN-poisoned beyond each length, so any over-read fails the finiteness check.
@@ -40,12 +40,12 @@ class Problem:
     def query(self):
         return self.batch.q(self.step)
 
-    def gpu_attention(self, q_h, path=api.PATH_AUTO, chunk=0, max_len=None):
+    def gpu_attention(self, q_h, path=api.PATH_AUTO, wgs=0, max_len=None):
         max_len = int(self.lens_h.max()) if max_len is None else max_len
         out = torch.empty(self.b, self.h, self.d, dtype=torch_dtype(self.dtype), device="cuda")
         ws = api.make_workspace(self.b, self.h, self.g, self.d, self.d, max_len, torch_dtype(self.dtype), "cuda")
         api.decode_attention(out, to_dev(q_h), self.kc, self.vc, self.lens, max_len, self.scale, ws,
-                             path=path, chunk_tokens=chunk)
+                             path=path, workgroups=wgs)
         torch.cuda.synchronize()
         return out, ws
 
@@ -87,13 +87,13 @@ def llama(oracle_mod):
     return pb, q, pb.oracle_attention(q)
 
 
-@pytest.mark.parametrize("path,chunk", [(api.PATH_MATRIX, 64), (api.PATH_MATRIX, 128), (api.PATH_MATRIX, 1024),
-                                        (api.PATH_MATRIX, 8192), (api.PATH_VECTOR, 0), (api.PATH_VECTOR, 192),
-                                        (api.PATH_VECTOR, 4096)])
-def test_paths_and_chunks(gpu_lib, llama, path, chunk):
+@pytest.mark.parametrize("path,wgs", [(api.PATH_MATRIX, 1), (api.PATH_MATRIX, 7), (api.PATH_MATRIX, 128),
+                                      (api.PATH_MATRIX, 2048), (api.PATH_VECTOR, 0), (api.PATH_VECTOR, 5),
+                                      (api.PATH_VECTOR, 1000)])
+def test_paths_and_grid_sizes(gpu_lib, llama, path, wgs):
     pb, q, ref = llama
-    out, _ = pb.gpu_attention(q, path=path, chunk=chunk)
-    assert_parity(out, ref, pb.dtype, f"path={path} chunk={chunk}")
+    out, _ = pb.gpu_attention(q, path=path, wgs=wgs)
+    assert_parity(out, ref, pb.dtype, f"path={path} workgroups={wgs}")
 
 
 def test_deterministic(gpu_lib, llama):
@@ -155,9 +155,9 @@ def test_edge_shapes(gpu_lib, oracle_mod, b, h, g, d, cap, lens, dtype):
     if dtype == "bf16" and d == 128 and h // g <= 64:
         paths.append(api.PATH_MATRIX)
     for path in paths:
-        for chunk in (0, 64):
-            out, _ = pb.gpu_attention(q, path=path, chunk=chunk)
-            assert_parity(out, ref, dtype, f"path={path} chunk={chunk}")
+        for wgs in (0, 1, 3, 64):
+            out, _ = pb.gpu_attention(q, path=path, wgs=wgs)
+            assert_parity(out, ref, dtype, f"path={path} workgroups={wgs}")
             for s in range(b):
                 if pb.lens_h[s] == 0:
                     assert torch.count_nonzero(out[s].float()) == 0
@@ -202,7 +202,7 @@ def test_workspace_reuse_across_shapes(gpu_lib, oracle_mod):
         q = pb.query()
         out = torch.empty(pb.b, pb.h, pb.d, dtype=torch.bfloat16, device="cuda")
         api.decode_attention(out, to_dev(q), pb.kc, pb.vc, pb.lens, int(pb.lens_h.max()), pb.scale, ws,
-                             chunk_tokens=64)
+                             workgroups=64)
         torch.cuda.synchronize()
         assert_parity(out, pb.oracle_attention(q), "bf16")
     assert int(ws[: 4 * 16 * 4].view(torch.int32).abs().sum()) == 0
