@@ -7,9 +7,10 @@ workload (default: one Llama-3-70B-shaped GQA layer, b=16, h=64, g=8, d=128,
 bf16, lengths uniform on [1024, 8192]), resident in HBM before timing starts.
 
 So that every step reads its K/V from HBM rather than from the 256 MB
-last-level cache, the benchmark keeps several independent cache sets (each
-its own seeded draw) and cycles through them, one set per step; each set's
-lengths grow by one per step it takes, as in a real decode loop.
+last-level cache, the benchmark keeps several independent cache sets (same
+drawn lengths, contents from their own seeds) and cycles through them, one
+set per step; each set's lengths grow by one per step it takes, as in a real
+decode loop.
 
 value = algorithmic KV bytes of all timed steps / wall time of those steps,
 where the bytes of one step are sum_b g * L_b * (d_k + d_v) * elem_bytes at
@@ -22,7 +23,6 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import math
 import os
@@ -37,33 +37,21 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 METRIC = "KV-read GB/s and % of HBM roofline; decode-attention steps/sec"
-PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "decode_traffic.json")
+PROFILE_DIR = os.path.join(ROOT, "profiles")
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash() -> str:
-    h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "gqa_kv_cache_decode_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(name.encode() + b"\0" + f.read())
-    return h.hexdigest()[:16]
-
-
 def traffic_from_profile(workload: str):
-    """HBM bytes per decode launch from committed counter runs, if they match this source."""
-    try:
-        with open(PROFILE_TRAFFIC) as f:
-            rec = json.load(f)
-    except (OSError, ValueError):
+    """HBM bytes per decode launch from the committed counter summary, if it matches this source."""
+    from gqa_kv_cache_decode_amd import rocprof_summary
+
+    rec = rocprof_summary.read_traffic(os.path.join(PROFILE_DIR, f"decode_traffic_{workload}.txt"))
+    if not rec or rec.get("kernel_source_hash") != rocprof_summary.kernel_source_hash():
         return None
-    entry = rec.get(workload)
-    if not entry or entry.get("kernel_source_hash") != kernel_source_hash():
-        return None
-    return entry.get("hbm_bytes_per_launch")
+    return int(float(rec["hbm_bytes_per_launch"]))
 
 
 def cpu_baseline(wl, batch_host, budget_s: float):
@@ -135,8 +123,9 @@ def main():
     sets = []
     host0 = None
     for r in range(n_sets):
-        batch = inputs.Batch(seed=wl.seed + 1000 * r, b=wl.b, h=wl.h, g=wl.g, d=wl.d,
-                             cap=wl.cap + grow, lens=wl.lens, dtype=wl.dtype, poison=False)
+        # every set shares set 0's drawn lengths (identical bytes per step); contents differ
+        batch = inputs.Batch(seed=wl.seed + 1000 * r, b=wl.b, h=wl.h, g=wl.g, d=wl.d, cap=wl.cap + grow,
+                             lens=wl.lens if r == 0 else host0.lens.tolist(), dtype=wl.dtype, poison=False)
         if r == 0:
             host0 = batch
         sets.append({
