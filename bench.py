@@ -1,8 +1,9 @@
 """Decode-step benchmark: KV-read GB/s, fraction of the HBM roofline, steps/s.
 
 One step is the whole hot path on one batch: append one token of K/V per
-sequence (gqa_kv_append), then attention of every query head over its cache
-(gqa_decode_attention). Inputs are seeded synthetic caches of the named
+sequence, then attention of every query head over its cache, the new token
+included. By default the step is one gqa_decode_step launch (append and
+attention fused); --unfused runs gqa_kv_append then gqa_decode_attention. Inputs are seeded synthetic caches of the named
 workload (default: one Llama-3-70B-shaped GQA layer, b=16, h=64, g=8, d=128,
 bf16, lengths uniform on [1024, 8192]), resident in HBM before timing starts.
 
@@ -15,8 +16,10 @@ decode loop.
 value = algorithmic KV bytes of all timed steps / wall time of those steps,
 where the bytes of one step are sum_b g * L_b * (d_k + d_v) * elem_bytes at
 the attended lengths L_b. roofline.achieved uses the same bytes per decode
-launch over the decode kernel's own average duration (HIP events around each
-launch, on the launch stream).
+launch over the decode kernel's average launch duration, from HIP events on
+the launch stream: for the fused step (one launch per step) the timed
+region's time over the step count; with --unfused, a pair of events around
+each decode launch.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
@@ -89,6 +92,8 @@ def main():
     ap.add_argument("--path", type=int, default=0, help="0 auto, 1 vector, 2 matrix")
     ap.add_argument("--workgroups", type=int, default=0, help="persistent grid size (0: automatic)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle time budget (0: skip)")
+    ap.add_argument("--unfused", action="store_true",
+                    help="run the step as gqa_kv_append + gqa_decode_attention instead of gqa_decode_step")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run a 1 GiB device copy first (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -160,14 +165,19 @@ def main():
         st = sets[i % n_sets]
         kn, vn = news[i % len(news)]
         max_len = int(st["lens_h"].max())
-        api.kv_append(st["kc"], st["vc"], kn, vn, st["lens"], max_len)
-        st["lens_h"] += 1
+        if args.unfused:
+            api.kv_append(st["kc"], st["vc"], kn, vn, st["lens"], max_len)
         if ev_pair is not None:
             ev_pair[0].record(stream)
-        api.decode_attention(out, qs[i % len(qs)], st["kc"], st["vc"], st["lens"], max_len + 1, wl.scale, ws,
-                             path=args.path, workgroups=args.workgroups)
+        if args.unfused:
+            api.decode_attention(out, qs[i % len(qs)], st["kc"], st["vc"], st["lens"], max_len + 1, wl.scale, ws,
+                                 path=args.path, workgroups=args.workgroups)
+        else:
+            api.decode_step(out, qs[i % len(qs)], kn, vn, st["kc"], st["vc"], st["lens"], max_len, wl.scale, ws,
+                            path=args.path, workgroups=args.workgroups)
         if ev_pair is not None:
             ev_pair[1].record(stream)
+        st["lens_h"] += 1
         return kv_bytes_attended(wl.g, wl.d, wl.d, wl.elem_bytes, st["lens_h"])
 
     for i in range(args.warmup):
@@ -175,7 +185,12 @@ def main():
     torch.cuda.synchronize()
     log("warmup done")
 
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    # The fused step is one launch of the decode kernel, so the timed region is
+    # exactly `steps` back-to-back launches of it and its average launch
+    # duration is the region's time over `steps` (launch gaps included). The
+    # two-call form brackets each decode launch with its own pair of events.
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)] if args.unfused else [None] * args.steps
     total_bytes = 0
     torch.cuda.synchronize()
     t_start = torch.cuda.Event(enable_timing=True)
@@ -188,7 +203,10 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     elapsed_ms = t_start.elapsed_time(t_end)
-    kern_ms = [a.elapsed_time(b) for a, b in evs]
+    if args.unfused:
+        kern_ms = [a.elapsed_time(b) for a, b in evs]
+    else:
+        kern_ms = [elapsed_ms / args.steps]
     kern_avg_ms = float(np.mean(kern_ms))
     bytes_per_launch = total_bytes / args.steps
     log(f"timed {args.steps} steps: {elapsed_ms:.3f} ms (host wall {wall * 1e3:.1f} ms); "
@@ -226,12 +244,14 @@ def main():
             "lens_drawn_mean": float(lens0.mean()), "lens_drawn_min": int(lens0.min()),
             "lens_drawn_max": int(lens0.max()), "cache_sets": n_sets, "seed": wl.seed,
             "path": {1: "vector", 2: "matrix"}[plan_path], "workgroups": plan_wgs,
+            "step_api": "gqa_kv_append + gqa_decode_attention" if args.unfused else "gqa_decode_step",
             "kv_bytes_per_step": int(bytes_per_launch),
         },
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-            "kernel": "decode_matrix_kernel" if plan_path == 2 else "decode_vector_kernel",
+            "kernel": ("decode_matrix_kernel" if plan_path == 2 else "decode_vector_kernel")
+                      + ("" if args.unfused else " (fused step)"),
             "kernel_avg_us": round(kern_avg_ms * 1e3, 3),
         },
         "cpu_baseline": cpu,

@@ -39,6 +39,10 @@ SIGNATURES = {
                                     _i32, _f32, _i32, _vp, _sz, _vp]),
     "gqa_decode_attention_ex": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
                                        _i32, _f32, _i32, _vp, _sz, _vp, _i32, _i32]),
+    "gqa_decode_step": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                               _f32, _i32, _vp, _sz, _vp]),
+    "gqa_decode_step_ex": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                                  _f32, _i32, _vp, _sz, _vp, _i32, _i32]),
     "gqa_decode_plan": (_i32, [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _ip, _ip]),
     "gqa_last_error": (ctypes.c_char_p, []),
 }

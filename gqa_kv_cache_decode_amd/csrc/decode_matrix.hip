@@ -34,7 +34,11 @@
 // Workgroups follow the persistent schedule of gqa_internal.hpp; inside a
 // piece each wave walks every fourth tile with an online softmax (base 2,
 // running max per head shared by the 4 lanes of a head), and the waves are
-// merged through LDS before finish_piece.
+// merged through LDS before the piece is published.
+//
+// FUSED (the decode step): the tile holding the appended token takes that
+// row from k_new / v_new instead of the cache and writes it to its cache
+// slot; the last workgroup to finish stores the grown lengths.
 #include "gqa_internal.hpp"
 
 namespace gqa {
@@ -72,6 +76,18 @@ __device__ __forceinline__ bf16x8 v_transpose(const u32x4* vr) {
   return as_bf16x8(a);
 }
 
+// The appended token of a fused step: its rows in k_new / v_new and its cache
+// slot. `local` is its row within the current tile (outside [0, 32): none).
+struct NewRow {
+  int local;
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* kdst;
+  uint16_t* vdst;
+};
+
+__device__ __forceinline__ void store16(uint16_t* ptr, u32x4 v) { *reinterpret_cast<u32x4*>(ptr) = v; }
+
 template <int NB>
 struct WaveState {
   f32x4 oacc[NB][8];
@@ -79,11 +95,13 @@ struct WaveState {
 };
 
 // One 32-position tile starting at kbase/vbase row t0 (FULL: all 32 rows
-// valid; otherwise only rows < nvalid are read).
-template <int NB, bool FULL>
+// valid; otherwise only rows < nvalid are read). FUSED: the row nr.local is
+// the appended token, read from its new rows and stored into the cache by the
+// lanes that load it.
+template <int NB, bool FULL, bool FUSED>
 __device__ __forceinline__ void tile_step(WaveState<NB>& st, const bf16x8 (&qop)[NB][4], const uint16_t* kbase,
                                           const uint16_t* vbase, int t0, int nvalid, float sl2, int n16,
-                                          int q4) {
+                                          int q4, const NewRow& nr) {
   u32x4 kr[2][4];
 #pragma unroll
   for (int sg = 0; sg < 2; ++sg) {
@@ -91,16 +109,28 @@ __device__ __forceinline__ void tile_step(WaveState<NB>& st, const bf16x8 (&qop)
     const uint16_t* kp = kbase + size_t(t0 + row) * D + q4 * 8;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      if (FULL || row < nvalid) kr[sg][ks] = stream16(kp + ks * 32);
-      else kr[sg][ks] = u32x4{0u, 0u, 0u, 0u};
+      if (FUSED && row == nr.local) {
+        kr[sg][ks] = load16(nr.k + q4 * 8 + ks * 32);
+        store16(nr.kdst + q4 * 8 + ks * 32, kr[sg][ks]);
+      } else if (FULL || row < nvalid) {
+        kr[sg][ks] = stream16(kp + ks * 32);
+      } else {
+        kr[sg][ks] = u32x4{0u, 0u, 0u, 0u};
+      }
     }
   }
   u32x4 vr[8];
 #pragma unroll
   for (int r = 0; r < 8; ++r) {
     const int row = v_row(q4, r);
-    if (FULL || row < nvalid) vr[r] = stream16(vbase + size_t(t0 + row) * D + n16 * 8);
-    else vr[r] = u32x4{0u, 0u, 0u, 0u};
+    if (FUSED && row == nr.local) {
+      vr[r] = load16(nr.v + n16 * 8);
+      store16(nr.vdst + n16 * 8, vr[r]);
+    } else if (FULL || row < nvalid) {
+      vr[r] = stream16(vbase + size_t(t0 + row) * D + n16 * 8);
+    } else {
+      vr[r] = u32x4{0u, 0u, 0u, 0u};
+    }
   }
   bf16x8 pop[NB];
 #pragma unroll
@@ -151,7 +181,7 @@ __device__ __forceinline__ void tile_step(WaveState<NB>& st, const bf16x8 (&qop)
 #undef GQA_PV_STEP
 }
 
-template <int NB>
+template <int NB, bool FUSED>
 __global__ __launch_bounds__(kThreads) void decode_matrix_kernel(DecodeParams p) {
   __shared__ float sm_m[kWaves][16];
   __shared__ float sm_l[kWaves][16];
@@ -205,11 +235,24 @@ __global__ __launch_bounds__(kThreads) void decode_matrix_kernel(DecodeParams p)
     const uint16_t* kbase = static_cast<const uint16_t*>(p.k_cache) + kv_head * p.cap * D;
     const uint16_t* vbase = static_cast<const uint16_t*>(p.v_cache) + kv_head * p.cap * D;
     const int t_end = min(pc.L, pc.tile_end * kTile);
+    const int pos_new = FUSED ? pc.L - 1 : -1;  // the appended token (fused step)
     for (int tile = pc.tile_begin + w; tile < pc.tile_end; tile += kWaves) {
       const int t0 = tile * kTile;
       const int nvalid = t_end - t0;
-      if (nvalid >= kTile) tile_step<NB, true>(st, qop, kbase, vbase, t0, kTile, sl2, n16, q4);
-      else tile_step<NB, false>(st, qop, kbase, vbase, t0, nvalid, sl2, n16, q4);
+      if (FUSED && pos_new >= t0 && pos_new < t0 + kTile) {
+        // the segment's last tile: take the new row from k_new / v_new and store it
+        NewRow nr;
+        nr.local = pos_new - t0;
+        nr.k = static_cast<const uint16_t*>(p.k_new) + kv_head * D;
+        nr.v = static_cast<const uint16_t*>(p.v_new) + kv_head * D;
+        nr.kdst = static_cast<uint16_t*>(p.k_cache) + (kv_head * p.cap + pos_new) * D;
+        nr.vdst = static_cast<uint16_t*>(p.v_cache) + (kv_head * p.cap + pos_new) * D;
+        tile_step<NB, false, true>(st, qop, kbase, vbase, t0, nvalid, sl2, n16, q4, nr);
+      } else if (nvalid >= kTile) {
+        tile_step<NB, true, false>(st, qop, kbase, vbase, t0, kTile, sl2, n16, q4, NewRow{});
+      } else {
+        tile_step<NB, false, false>(st, qop, kbase, vbase, t0, nvalid, sl2, n16, q4, NewRow{});
+      }
     }
 
     // merge the four waves through LDS, one 16-head block at a time
@@ -253,36 +296,50 @@ __global__ __launch_bounds__(kThreads) void decode_matrix_kernel(DecodeParams p)
     settle_pending<uint16_t, NB * 2>(p, pend, sm_merge, &s_flag);
     pend.n = 0;
   }
+  if (FUSED) finish_step(p, &s_flag);
+}
+
+template <bool FUSED>
+void launch_nb(const DecodeParams& p, hipStream_t stream) {
+  const dim3 grid(p.workgroups);
+  if (p.G <= 16) {
+    hipLaunchKernelGGL((decode_matrix_kernel<1, FUSED>), grid, dim3(kThreads), 0, stream, p);
+  } else if (p.G <= 32) {
+    hipLaunchKernelGGL((decode_matrix_kernel<2, FUSED>), grid, dim3(kThreads), 0, stream, p);
+  } else {
+    hipLaunchKernelGGL((decode_matrix_kernel<4, FUSED>), grid, dim3(kThreads), 0, stream, p);
+  }
 }
 
 }  // namespace
 
 hipError_t launch_decode_matrix(const DecodeParams& p, hipStream_t stream) {
-  const dim3 grid(p.workgroups);
-  if (p.G <= 16) {
-    hipLaunchKernelGGL(decode_matrix_kernel<1>, grid, dim3(kThreads), 0, stream, p);
-  } else if (p.G <= 32) {
-    hipLaunchKernelGGL(decode_matrix_kernel<2>, grid, dim3(kThreads), 0, stream, p);
-  } else {
-    hipLaunchKernelGGL(decode_matrix_kernel<4>, grid, dim3(kThreads), 0, stream, p);
-  }
+  if (p.fused) launch_nb<true>(p, stream);
+  else launch_nb<false>(p, stream);
   return hipGetLastError();
 }
 
-int matrix_workgroups_per_cu(int G) {
-  static int cached[3] = {0, 0, 0};
+namespace {
+template <bool FUSED>
+hipError_t occupancy(int k, int* n) {
+  if (k == 0) return hipOccupancyMaxActiveBlocksPerMultiprocessor(n, decode_matrix_kernel<1, FUSED>, kThreads, 0);
+  if (k == 1) return hipOccupancyMaxActiveBlocksPerMultiprocessor(n, decode_matrix_kernel<2, FUSED>, kThreads, 0);
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(n, decode_matrix_kernel<4, FUSED>, kThreads, 0);
+}
+}  // namespace
+
+int matrix_workgroups_per_cu(int G, bool fused) {
+  static int cached[2][3] = {};
   const int k = G <= 16 ? 0 : (G <= 32 ? 1 : 2);
-  if (cached[k] > 0) return cached[k];
+  int& c = cached[fused ? 1 : 0][k];
+  if (c > 0) return c;
   int n = 0;
-  hipError_t e;
-  if (k == 0) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_matrix_kernel<1>, kThreads, 0);
-  else if (k == 1) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_matrix_kernel<2>, kThreads, 0);
-  else e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_matrix_kernel<4>, kThreads, 0);
+  const hipError_t e = fused ? occupancy<true>(k, &n) : occupancy<false>(k, &n);
   if (e != hipSuccess || n <= 0) {
     (void)hipGetLastError();
     return 0;
   }
-  cached[k] = n;
+  c = n;
   return n;
 }
 

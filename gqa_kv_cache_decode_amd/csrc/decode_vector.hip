@@ -60,10 +60,24 @@ struct VState {
   float m[HB], l[HB], acc[HB][VEC];
 };
 
-// One 32-position tile starting at row t0 (FULL: all rows valid).
-template <typename T, int D, int HB, bool FULL>
+// The appended token of a fused step: this lane's 16-byte column of its new
+// rows and of its cache slot; `local` is its row within the current tile.
+template <typename T>
+struct NewRow {
+  int local;
+  const T* k;
+  const T* v;
+  T* kdst;
+  T* vdst;
+};
+
+// One 32-position tile starting at row t0 (FULL: all rows valid). FUSED: the
+// row nr.local is the appended token, read from its new rows and stored into
+// the cache by the lanes that load it.
+template <typename T, int D, int HB, bool FULL, bool FUSED>
 __device__ __forceinline__ void tile_step(VState<T, D, HB>& st, const float (&qf)[HB][Shape<T, D, HB>::VEC],
-                                          const T* kbase, const T* vbase, int t0, int nvalid, int rg) {
+                                          const T* kbase, const T* vbase, int t0, int nvalid, int rg,
+                                          const NewRow<T>& nr) {
   using S = Shape<T, D, HB>;
   constexpr int VEC = S::VEC, U = S::U, RPW = S::RPW, R = S::R;
 #pragma unroll
@@ -74,7 +88,12 @@ __device__ __forceinline__ void tile_step(VState<T, D, HB>& st, const float (&qf
     for (int u = 0; u < U; ++u) {
       const int row = (sb * U + u) * RPW + rg;
       ok[u] = FULL ? (row < kTile) : (row < nvalid);
-      if (ok[u]) {
+      if (FUSED && row == nr.local) {
+        kr[u] = *reinterpret_cast<const u32x4*>(nr.k);
+        vr[u] = *reinterpret_cast<const u32x4*>(nr.v);
+        *reinterpret_cast<u32x4*>(nr.kdst) = kr[u];
+        *reinterpret_cast<u32x4*>(nr.vdst) = vr[u];
+      } else if (ok[u]) {
         kr[u] = stream16(kbase + size_t(t0 + row) * D);
         vr[u] = stream16(vbase + size_t(t0 + row) * D);
       } else {
@@ -127,7 +146,7 @@ __device__ __forceinline__ void tile_step(VState<T, D, HB>& st, const float (&qf
   }
 }
 
-template <typename T, int D, int HB>
+template <typename T, int D, int HB, bool FUSED>
 __global__ __launch_bounds__(kThreads) void decode_vector_kernel(DecodeParams p) {
   using S = Shape<T, D, HB>;
   constexpr int VEC = S::VEC, R = S::R;
@@ -188,11 +207,24 @@ __global__ __launch_bounds__(kThreads) void decode_vector_kernel(DecodeParams p)
     const T* kbase = static_cast<const T*>(p.k_cache) + kv_head * p.cap * D + col * VEC;
     const T* vbase = static_cast<const T*>(p.v_cache) + kv_head * p.cap * D + col * VEC;
     const int t_end = min(pc.L, pc.tile_end * kTile);
+    const int pos_new = FUSED ? pc.L - 1 : -1;  // the appended token (fused step)
     for (int tile = pc.tile_begin + w; tile < pc.tile_end; tile += kWaves) {
       const int t0 = tile * kTile;
       const int nvalid = t_end - t0;
-      if (nvalid >= kTile) tile_step<T, D, HB, true>(st, qf, kbase, vbase, t0, kTile, rg);
-      else tile_step<T, D, HB, false>(st, qf, kbase, vbase, t0, nvalid, rg);
+      if (FUSED && pos_new >= t0 && pos_new < t0 + kTile) {
+        // the segment's last tile: take the new row from k_new / v_new and store it
+        NewRow<T> nr;
+        nr.local = pos_new - t0;
+        nr.k = static_cast<const T*>(p.k_new) + kv_head * D + col * VEC;
+        nr.v = static_cast<const T*>(p.v_new) + kv_head * D + col * VEC;
+        nr.kdst = static_cast<T*>(p.k_cache) + (kv_head * p.cap + pos_new) * D + col * VEC;
+        nr.vdst = static_cast<T*>(p.v_cache) + (kv_head * p.cap + pos_new) * D + col * VEC;
+        tile_step<T, D, HB, false, true>(st, qf, kbase, vbase, t0, nvalid, rg, nr);
+      } else if (nvalid >= kTile) {
+        tile_step<T, D, HB, true, false>(st, qf, kbase, vbase, t0, kTile, rg, NewRow<T>{});
+      } else {
+        tile_step<T, D, HB, false, false>(st, qf, kbase, vbase, t0, nvalid, rg, NewRow<T>{});
+      }
     }
 
     // merge the lane groups of the wave (same column, different rows)
@@ -249,11 +281,15 @@ __global__ __launch_bounds__(kThreads) void decode_vector_kernel(DecodeParams p)
     settle_pending<T, (HB * D / 4 + kThreads - 1) / kThreads>(p, pend, sm_merge, &s_flag);
     pend.n = 0;
   }
+  if (FUSED) finish_step(p, &s_flag);
 }
 
 template <typename T, int D, int HB>
 hipError_t launch_one(const DecodeParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_vector_kernel<T, D, HB>), dim3(p.workgroups), dim3(kThreads), 0, stream, p);
+  if (p.fused)
+    hipLaunchKernelGGL((decode_vector_kernel<T, D, HB, true>), dim3(p.workgroups), dim3(kThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL((decode_vector_kernel<T, D, HB, false>), dim3(p.workgroups), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -280,15 +316,15 @@ hipError_t launch_t(const DecodeParams& p, hipStream_t stream) {
 }
 
 
-template <typename T, int D>
+template <typename T, int D, bool FUSED>
 int occupancy_d(int hb) {
   int n = 0;
   hipError_t e;
   switch (hb) {
-    case 1: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_vector_kernel<T, D, 1>, kThreads, 0); break;
-    case 2: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_vector_kernel<T, D, 2>, kThreads, 0); break;
-    case 4: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_vector_kernel<T, D, 4>, kThreads, 0); break;
-    default: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_vector_kernel<T, D, 8>, kThreads, 0); break;
+    case 1: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_vector_kernel<T, D, 1, FUSED>, kThreads, 0); break;
+    case 2: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_vector_kernel<T, D, 2, FUSED>, kThreads, 0); break;
+    case 4: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_vector_kernel<T, D, 4, FUSED>, kThreads, 0); break;
+    default: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_vector_kernel<T, D, 8, FUSED>, kThreads, 0); break;
   }
   if (e != hipSuccess || n <= 0) {
     (void)hipGetLastError();
@@ -297,27 +333,29 @@ int occupancy_d(int hb) {
   return n;
 }
 
-template <typename T>
+template <typename T, bool FUSED>
 int occupancy_t(int d, int hb) {
   switch (d) {
-    case 16: return occupancy_d<T, 16>(hb);
-    case 32: return occupancy_d<T, 32>(hb);
-    case 64: return occupancy_d<T, 64>(hb);
-    case 128: return occupancy_d<T, 128>(hb);
-    default: return occupancy_d<T, 256>(hb);
+    case 16: return occupancy_d<T, 16, FUSED>(hb);
+    case 32: return occupancy_d<T, 32, FUSED>(hb);
+    case 64: return occupancy_d<T, 64, FUSED>(hb);
+    case 128: return occupancy_d<T, 128, FUSED>(hb);
+    default: return occupancy_d<T, 256, FUSED>(hb);
   }
 }
 
 }  // namespace
 
-int vector_workgroups_per_cu(int dtype, int d, int heads_per_block) {
-  static int cached[2][5][4] = {};
+int vector_workgroups_per_cu(int dtype, int d, int heads_per_block, bool fused) {
+  static int cached[2][2][5][4] = {};
   const int ti = dtype == 0 ? 0 : 1;
   const int di = d == 16 ? 0 : d == 32 ? 1 : d == 64 ? 2 : d == 128 ? 3 : 4;
   const int hi = heads_per_block == 1 ? 0 : heads_per_block == 2 ? 1 : heads_per_block == 4 ? 2 : 3;
-  int& c = cached[ti][di][hi];
+  int& c = cached[fused ? 1 : 0][ti][di][hi];
   if (c > 0) return c;
-  const int n = ti == 0 ? occupancy_t<float>(d, heads_per_block) : occupancy_t<uint16_t>(d, heads_per_block);
+  int n;
+  if (fused) n = ti == 0 ? occupancy_t<float, true>(d, heads_per_block) : occupancy_t<uint16_t, true>(d, heads_per_block);
+  else n = ti == 0 ? occupancy_t<float, false>(d, heads_per_block) : occupancy_t<uint16_t, false>(d, heads_per_block);
   if (n > 0) c = n;
   return n;
 }

@@ -2,6 +2,7 @@
 // planning and dispatch. Every check runs on the host before anything is
 // enqueued, so each error path is reachable without a GPU.
 #include <stdarg.h>
+#include <stdint.h>
 #include <stdio.h>
 
 #include <string>
@@ -68,7 +69,7 @@ int gblk_bound(int G) {
 // callers). Fills plan on success. workgroups: 0 = one per resident slot of
 // the device (compute units x workgroups that fit per unit, at most two).
 int plan_decode(int b, int h, int g, int d_k, int d_v, int cap, int max_len, int dtype, int path,
-                int workgroups, Plan* plan) {
+                int workgroups, Plan* plan, bool fused = false) {
   if (b <= 0 || b > kMaxBatch) return fail(GQA_ERR_ARG, "b=%d must be in [1, %d]", b, kMaxBatch);
   if (h <= 0 || h > kMaxHeads) return fail(GQA_ERR_ARG, "h=%d must be in [1, %d]", h, kMaxHeads);
   if (g <= 0) return fail(GQA_ERR_ARG, "g=%d must be positive", g);
@@ -110,11 +111,22 @@ int plan_decode(int b, int h, int g, int d_k, int d_v, int cap, int max_len, int
     // Up to two 4-wave workgroups per compute unit (8 waves keep enough loads
     // in flight), never more than fit at once, so the persistent grid runs in
     // a single round.
-    int fit = chosen == GQA_PATH_MATRIX ? gqa::matrix_workgroups_per_cu(G)
-                                        : gqa::vector_workgroups_per_cu(dtype, d_k, plan->gblk);
+    int fit = chosen == GQA_PATH_MATRIX ? gqa::matrix_workgroups_per_cu(G, fused)
+                                        : gqa::vector_workgroups_per_cu(dtype, d_k, plan->gblk, fused);
     if (fit <= 0) fit = 2;  // no device to ask: assume the common case
     const int per_cu = fit < 2 ? fit : 2;
     long long n = (long long)device_cus() * per_cu;
+    // Each shared piece leaves gblk*(d_v+2) floats to merge; for large head
+    // groups keep at least G/2 tiles per workgroup (max 4 KiB of partial
+    // state per 16 KiB tile of K/V) so that single-workgroup merges stay
+    // small. The unit count is bounded on the host by max_len.
+    const int unit_len = gqa::kTile * gqa::kUnitTiles;
+    const long long units_bound = (long long)b * g * plan->nhb * ((max_len + unit_len - 1) / unit_len);
+    const int min_tiles = plan->gblk / 2;
+    const int min_units = min_tiles > gqa::kUnitTiles ? (min_tiles + gqa::kUnitTiles - 1) / gqa::kUnitTiles : 1;
+    const long long by_work = (units_bound + min_units - 1) / min_units;
+    if (n > by_work) n = by_work;
+    if (n < 1) n = 1;
     if (n > gqa::kMaxWorkgroups) n = gqa::kMaxWorkgroups;
     workgroups = int(n);
   }
@@ -164,21 +176,25 @@ int gqa_decode_plan(int b, int h, int g, int d_k, int d_v, int cap, int max_len,
   return ok();
 }
 
-int gqa_decode_attention_ex(void* out, const void* q, const void* k_cache, const void* v_cache,
-                            const int32_t* lens, int b, int h, int g, int d_k, int d_v, int cap,
-                            int max_len, float scale, int dtype, void* workspace,
-                            size_t workspace_bytes, void* stream, int path, int workgroups) {
-  if (!out || !q || !k_cache || !v_cache || !lens)
-    return fail(GQA_ERR_ARG, "gqa_decode_attention: null pointer argument");
+}  // extern "C"
+
+namespace {
+
+// Shared body of the attention and fused-step entry points. max_len_att is
+// the bound of the attended lengths (the appended token included).
+int decode_common(const char* fn, void* out, const void* q, void* k_cache, void* v_cache, int32_t* lens,
+                  const void* k_new, const void* v_new, int b, int h, int g, int d_k, int d_v, int cap,
+                  int max_len_att, float scale, int dtype, void* workspace, size_t workspace_bytes,
+                  void* stream, int path, int workgroups, int fused) {
   Plan plan;
-  const int rc = plan_decode(b, h, g, d_k, d_v, cap, max_len, dtype, path, workgroups, &plan);
+  const int rc = plan_decode(b, h, g, d_k, d_v, cap, max_len_att, dtype, path, workgroups, &plan, fused != 0);
   if (rc != GQA_OK) return rc;
   const gqa::WorkspaceLayout ws = gqa::workspace_layout(b, h, gblk_bound(h / g), d_v);
-  if (!workspace) return fail(GQA_ERR_WORKSPACE, "workspace is null (%zu bytes needed)", ws.total);
+  if (!workspace) return fail(GQA_ERR_WORKSPACE, "%s: workspace is null (%zu bytes needed)", fn, ws.total);
   if (workspace_bytes < ws.total)
-    return fail(GQA_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, ws.total);
+    return fail(GQA_ERR_WORKSPACE, "%s: workspace has %zu bytes, %zu needed", fn, workspace_bytes, ws.total);
   if (reinterpret_cast<uintptr_t>(workspace) & 255)
-    return fail(GQA_ERR_ARG, "workspace must be 256-byte aligned");
+    return fail(GQA_ERR_ARG, "%s: workspace must be 256-byte aligned", fn);
 
   gqa::DecodeParams p;
   p.out = out;
@@ -186,8 +202,11 @@ int gqa_decode_attention_ex(void* out, const void* q, const void* k_cache, const
   p.k_cache = k_cache;
   p.v_cache = v_cache;
   p.lens = lens;
+  p.k_new = k_new;
+  p.v_new = v_new;
   char* wsb = static_cast<char*>(workspace);
   p.ws_cnt = reinterpret_cast<int*>(wsb + ws.cnt_off);
+  p.ws_done = reinterpret_cast<int*>(wsb + ws.done_off);
   p.ws_slots = reinterpret_cast<float*>(wsb + ws.slot_off);
   p.b = b;
   p.h = h;
@@ -195,7 +214,8 @@ int gqa_decode_attention_ex(void* out, const void* q, const void* k_cache, const
   p.G = h / g;
   p.d = d_k;
   p.cap = cap;
-  p.max_len = max_len;
+  p.max_len = max_len_att;
+  p.fused = fused;
   p.gblk = plan.gblk;
   p.nhb = plan.nhb;
   p.ngroups = g * plan.nhb;
@@ -206,8 +226,45 @@ int gqa_decode_attention_ex(void* out, const void* q, const void* k_cache, const
   const hipStream_t st = static_cast<hipStream_t>(stream);
   const hipError_t e = plan.path == GQA_PATH_MATRIX ? gqa::launch_decode_matrix(p, st)
                                                     : gqa::launch_decode_vector(p, dtype, st);
-  if (e != hipSuccess) return fail(GQA_ERR_HIP, "gqa_decode_attention launch: %s", hipGetErrorString(e));
+  if (e != hipSuccess) return fail(GQA_ERR_HIP, "%s launch: %s", fn, hipGetErrorString(e));
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int gqa_decode_attention_ex(void* out, const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* lens, int b, int h, int g, int d_k, int d_v, int cap,
+                            int max_len, float scale, int dtype, void* workspace,
+                            size_t workspace_bytes, void* stream, int path, int workgroups) {
+  if (!out || !q || !k_cache || !v_cache || !lens)
+    return fail(GQA_ERR_ARG, "gqa_decode_attention: null pointer argument");
+  // The attention kernels only read the caches and lens when not fused.
+  return decode_common("gqa_decode_attention", out, q, const_cast<void*>(k_cache), const_cast<void*>(v_cache),
+                       const_cast<int32_t*>(lens), nullptr, nullptr, b, h, g, d_k, d_v, cap, max_len, scale,
+                       dtype, workspace, workspace_bytes, stream, path, workgroups, 0);
+}
+
+int gqa_decode_step_ex(void* out, const void* q, const void* k_new, const void* v_new, void* k_cache,
+                       void* v_cache, int32_t* lens, int b, int h, int g, int d_k, int d_v, int cap,
+                       int max_len, float scale, int dtype, void* workspace, size_t workspace_bytes,
+                       void* stream, int path, int workgroups) {
+  if (!out || !q || !k_new || !v_new || !k_cache || !v_cache || !lens)
+    return fail(GQA_ERR_ARG, "gqa_decode_step: null pointer argument");
+  if (max_len < 0) return fail(GQA_ERR_ARG, "max_len=%d must be >= 0", max_len);
+  if (cap > 0 && (long long)max_len + 1 > cap)
+    return fail(GQA_ERR_CAPACITY, "appending to max_len=%d needs cap > %d, cap=%d", max_len, max_len, cap);
+  if (max_len == INT32_MAX) return fail(GQA_ERR_CAPACITY, "max_len=%d too large", max_len);
+  return decode_common("gqa_decode_step", out, q, k_cache, v_cache, lens, k_new, v_new, b, h, g, d_k, d_v, cap,
+                       max_len + 1, scale, dtype, workspace, workspace_bytes, stream, path, workgroups, 1);
+}
+
+int gqa_decode_step(void* out, const void* q, const void* k_new, const void* v_new, void* k_cache,
+                    void* v_cache, int32_t* lens, int b, int h, int g, int d_k, int d_v, int cap, int max_len,
+                    float scale, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  return gqa_decode_step_ex(out, q, k_new, v_new, k_cache, v_cache, lens, b, h, g, d_k, d_v, cap, max_len, scale,
+                            dtype, workspace, workspace_bytes, stream, GQA_PATH_AUTO, 0);
 }
 
 int gqa_decode_attention(void* out, const void* q, const void* k_cache, const void* v_cache,

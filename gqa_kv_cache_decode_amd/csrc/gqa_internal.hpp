@@ -28,7 +28,7 @@
 // needed.
 //
 // Workspace layout (caller-owned, see gqa_decode_workspace_size):
-//   [counters] int32 [b * h]                                  zero between calls
+//   [counters] int32 [b * h], then int32 done                 zero between calls
 //   [slots]    float [kMaxWorkgroups][2][slot_floats]         slot = o[gb][d], m[gb], l[gb]
 // slot_floats = gb*d + round_up(2*gb, 4), so every slot and its o block are
 // 16-byte aligned.
@@ -43,7 +43,8 @@ namespace gqa {
 
 constexpr int kThreads = 256;  // workgroup size of both decode kernels
 constexpr int kWaves = kThreads / 64;
-constexpr int kTile = 32;             // positions per work unit
+constexpr int kTile = 32;             // positions per wave step
+constexpr int kUnitTiles = 4;         // tiles per schedule unit: one for each wave of a workgroup
 constexpr int kMaxWorkgroups = 2048;  // persistent grid bound (workspace sizing)
 constexpr int kMatrixMaxGroup = 64;   // query heads per KV head on the matrix path
 constexpr int kVectorMaxBlock = 8;    // query heads per workgroup on the vector path
@@ -60,12 +61,17 @@ struct AppendParams {
 struct DecodeParams {
   void* out;
   const void* q;
-  const void* k_cache;
-  const void* v_cache;
-  const int32_t* lens;
+  void* k_cache;      // written only by the fused step (the new row)
+  void* v_cache;
+  int32_t* lens;      // written only by the fused step (+1, by the last workgroup)
+  const void* k_new;  // fused step: the new token's rows [b][g][d]
+  const void* v_new;
   int* ws_cnt;
+  int* ws_done;       // fused step: workgroups finished (zero between calls)
   float* ws_slots;
-  int b, h, g, G, d, cap, max_len;
+  int b, h, g, G, d, cap;
+  int max_len;        // bound of the attended lengths (the appended token included)
+  int fused;          // 1: append the new token (position lens[s]) and attend over it
   int gblk;         // query heads handled together (matrix: G; vector: head block)
   int nhb;          // head blocks per KV head (matrix: 1)
   int ngroups;      // segments per sequence: g * nhb
@@ -77,7 +83,7 @@ struct DecodeParams {
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct WorkspaceLayout {
-  size_t cnt_off, slot_off, total;
+  size_t cnt_off, done_off, slot_off, total;
 };
 
 inline int slot_floats_for(int gblk, int d_v) { return gblk * d_v + ((2 * gblk + 3) & ~3); }
@@ -86,7 +92,8 @@ inline int slot_floats_for(int gblk, int d_v) { return gblk * d_v + ((2 * gblk +
 inline WorkspaceLayout workspace_layout(int b, int h, int gblk_bound, int d_v) {
   WorkspaceLayout w;
   w.cnt_off = 0;
-  w.slot_off = align256(size_t(b) * size_t(h) * sizeof(int));
+  w.done_off = size_t(b) * size_t(h) * sizeof(int);
+  w.slot_off = align256(w.done_off + sizeof(int));
   w.total = w.slot_off + align256(size_t(kMaxWorkgroups) * 2 * size_t(slot_floats_for(gblk_bound, d_v)) * sizeof(float));
   return w;
 }
@@ -102,8 +109,8 @@ hipError_t launch_decode_matrix(const DecodeParams& p, hipStream_t stream);
 
 // Workgroups of the decode kernel instance that fit on one compute unit at
 // once (runtime occupancy query, cached; 0 if the runtime cannot say).
-int matrix_workgroups_per_cu(int G);
-int vector_workgroups_per_cu(int dtype, int d, int heads_per_block);
+int matrix_workgroups_per_cu(int G, bool fused);
+int vector_workgroups_per_cu(int dtype, int d, int heads_per_block, bool fused);
 
 // Vector-path head block for G query heads per KV head: the smallest power of
 // two >= G, capped at 8 (larger groups use several head blocks).
@@ -201,14 +208,21 @@ __device__ __forceinline__ float coherent_load1(__amdgpu_buffer_rsrc_t r, int by
 // Wait until this wave's earlier memory writes have completed.
 __device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-// Effective attended length: lens clamped to [0, max_len].
+// Effective attended length: lens clamped to [0, max_len]; for the fused step
+// the stored length (before the append) is clamped to [0, max_len - 1] and
+// the appended token adds one.
 __device__ __forceinline__ int attended_len(const DecodeParams& p, int s) {
   int L = p.lens[s];
   L = L < 0 ? 0 : L;
-  return L > p.max_len ? p.max_len : L;
+  const int hi = p.max_len - p.fused;
+  return (L > hi ? hi : L) + p.fused;
 }
 
 __device__ __forceinline__ int tiles_of(int L) { return (L + kTile - 1) / kTile; }
+// Schedule units of a segment of length L. A unit is kUnitTiles tiles, so a
+// piece made of whole units gives every wave of its workgroup the same number
+// of tiles (only a segment's last unit can be short).
+__device__ __forceinline__ int units_of(int L) { return (L + kTile * kUnitTiles - 1) / (kTile * kUnitTiles); }
 
 // Workgroup owning unit u when T units are split over P workgroups as
 // [floor(p*T/P), floor((p+1)*T/P)): the largest p with floor(p*T/P) <= u.
@@ -265,7 +279,7 @@ struct Located {
 __device__ Located locate_units(const DecodeParams& p, const LensView& lv, int workgroup) {
   long long carry = 0;
   for (int base = 0; base < p.b; base += 64) {  // total units
-    const long long v = (long long)p.ngroups * tiles_of(lv.lane_len(base));
+    const long long v = (long long)p.ngroups * units_of(lv.lane_len(base));
     const long long incl = wave_inclusive_scan(v);
     carry += __shfl(incl, 63, 64);
   }
@@ -279,7 +293,7 @@ __device__ Located locate_units(const DecodeParams& p, const LensView& lv, int w
   carry = 0;
   for (int base = 0; base < p.b; base += 64) {
     const int s = base + (threadIdx.x & 63);
-    const long long v = (long long)p.ngroups * tiles_of(lv.lane_len(base));
+    const long long v = (long long)p.ngroups * units_of(lv.lane_len(base));
     const long long incl = wave_inclusive_scan(v) + carry;
     const long long excl = incl - v;
     const unsigned long long hit = __ballot(s < p.b && v > 0 && excl <= u0 && u0 < incl);
@@ -296,10 +310,11 @@ __device__ Located locate_units(const DecodeParams& p, const LensView& lv, int w
 
 // One piece of a workgroup's range: tiles [tile_begin, tile_end) of segment
 // (s, grp), i.e. positions [tile_begin*kTile, min(L, tile_end*kTile)).
-// p0 and p1 are the first and last workgroups whose ranges touch the segment.
+// tile_begin is a multiple of kUnitTiles. p0 and p1 are the first and last
+// workgroups whose ranges touch the segment.
 struct Piece {
   int s, grp, L;
-  int tile_begin, tile_end, seg_tiles;
+  int tile_begin, tile_end;
   int p0, p1;
 };
 
@@ -329,27 +344,29 @@ struct PieceWalker {
   __device__ bool next(Piece& pc) {
     if (u >= u_end) return false;
     int L = lv.len(s);
-    long long seq_units = (long long)p->ngroups * tiles_of(L);
+    long long seq_units = (long long)p->ngroups * units_of(L);
     while (u >= seq_base + seq_units && s + 1 < p->b) {  // skip to the sequence holding u
       seq_base += seq_units;
       ++s;
       L = lv.len(s);
-      seq_units = (long long)p->ngroups * tiles_of(L);
+      seq_units = (long long)p->ngroups * units_of(L);
     }
-    const int nt = tiles_of(L);
+    const int nu = units_of(L);
     const long long within = u - seq_base;
     pc.s = s;
     pc.L = L;
-    pc.grp = int(within / nt);
-    pc.seg_tiles = nt;
-    pc.tile_begin = int(within - (long long)pc.grp * nt);
+    pc.grp = int(within / nu);
+    const int ub = int(within - (long long)pc.grp * nu);
     const long long remain = u_end - u;
-    const long long seg_left = nt - pc.tile_begin;
-    pc.tile_end = pc.tile_begin + int(remain < seg_left ? remain : seg_left);
-    const long long seg_u0 = seq_base + (long long)pc.grp * nt;
+    const long long seg_left = nu - ub;
+    const int ue = ub + int(remain < seg_left ? remain : seg_left);
+    const int nt = tiles_of(L);
+    pc.tile_begin = ub * kUnitTiles;
+    pc.tile_end = ue * kUnitTiles < nt ? ue * kUnitTiles : nt;
+    const long long seg_u0 = seq_base + (long long)pc.grp * nu;
     pc.p0 = owner_of(seg_u0, total, parts);
-    pc.p1 = owner_of(seg_u0 + nt - 1, total, parts);
-    u += pc.tile_end - pc.tile_begin;
+    pc.p1 = owner_of(seg_u0 + nu - 1, total, parts);
+    u += ue - ub;
     return true;
   }
 };
@@ -528,6 +545,19 @@ __device__ void settle_pending(const DecodeParams& p, const Pending& pend, float
       if (threadIdx.x == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
+}
+
+// Fused step: every workgroup counts itself out; the last one, which runs
+// after every other workgroup has read lens for the last time, stores each
+// sequence's new length and re-zeroes the counter.
+__device__ void finish_step(const DecodeParams& p, int* sm_flag) {
+  __syncthreads();
+  if (threadIdx.x == 0)
+    *sm_flag = __hip_atomic_fetch_add(p.ws_done, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  if (*sm_flag != int(gridDim.x) - 1) return;
+  for (int s = threadIdx.x; s < p.b; s += kThreads) p.lens[s] = attended_len(p, s);
+  if (threadIdx.x == 0) __hip_atomic_store(p.ws_done, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Zero the output rows of sequences that attend nothing; sequence s is

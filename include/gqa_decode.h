@@ -9,7 +9,8 @@
  *   gqa_decode_attention(...)   let the new token's h query heads attend over
  *                               every cached position, the new one included
  *
- * in that order on one stream. This is the per-layer decode loop of the
+ * in that order on one stream, or both at once with gqa_decode_step (one
+ * launch). This is the per-layer decode loop of the
  * "LLM inference 05" notes (albangk): push K, push V, then attend; and the
  * incremental attention of the "Fast Transformer Decoding: One Write-Head is
  * All You Need" review (velog), §2.4 Multi-head Attention (Incremental) and
@@ -146,6 +147,34 @@ int gqa_decode_attention_ex(void* out, const void* q, const void* k_cache, const
                             const int32_t* lens, int b, int h, int g, int d_k, int d_v, int cap,
                             int max_len, float scale, int dtype, void* workspace,
                             size_t workspace_bytes, void* stream, int path, int workgroups);
+
+/*
+ * One whole decoding step in one launch: gqa_kv_append followed by
+ * gqa_decode_attention ("LLM inference 05": push K, push V, then attend;
+ * the new position attends to every earlier one and to itself).
+ *
+ * For every sequence s, with p = lens[s] (clamped to [0, max_len]):
+ *   K[s][j][p] = k_new[s][j], V[s][j][p] = v_new[s][j]   (bit for bit)
+ *   out[s][i]  = attention of q[s][i] over positions [0, p + 1)
+ *   lens[s]    = p + 1
+ * The appended row is taken straight from k_new / v_new for the attention
+ * and stored into the cache by the same kernel; lens is updated by the last
+ * workgroup to finish, after every workgroup has read it.
+ * max_len: host upper bound of lens BEFORE the call; max_len + 1 <= cap
+ *   (GQA_ERR_CAPACITY). Results equal the two-call sequence up to
+ *   floating-point summation order; caches and lens equal it bit for bit.
+ * Same shapes, workspace rules and errors as gqa_decode_attention (the
+ * workspace's counters include the step's finish counter).
+ */
+int gqa_decode_step(void* out, const void* q, const void* k_new, const void* v_new, void* k_cache,
+                    void* v_cache, int32_t* lens, int b, int h, int g, int d_k, int d_v, int cap, int max_len,
+                    float scale, int dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/* gqa_decode_step with the launch choices of gqa_decode_attention_ex. */
+int gqa_decode_step_ex(void* out, const void* q, const void* k_new, const void* v_new, void* k_cache,
+                       void* v_cache, int32_t* lens, int b, int h, int g, int d_k, int d_v, int cap,
+                       int max_len, float scale, int dtype, void* workspace, size_t workspace_bytes,
+                       void* stream, int path, int workgroups);
 
 /*
  * Describe the launch gqa_decode_attention_ex would make on the current

@@ -128,3 +128,20 @@ def test_plan_choices(lib):
         _, c = plan(*args)
         assert 1 <= c <= 2048
     assert plan(16, 64, 8, 128, 8256, 8193, _lib.BF16, path=_lib.PATH_VECTOR, wgs=77) == (_lib.PATH_VECTOR, 77)
+
+
+def test_step_rejects(lib):
+    def call(**kw):
+        a = dict(out=FAKE, q=FAKE, kn=FAKE, vn=FAKE, k=FAKE, v=FAKE, lens=FAKE, b=2, h=8, g=2, dk=128, dv=128,
+                 cap=100, max_len=50, dtype=_lib.BF16, ws=FAKE, ws_bytes=1 << 30)
+        a.update(kw)
+        return lib.gqa_decode_step(a["out"], a["q"], a["kn"], a["vn"], a["k"], a["v"], a["lens"], a["b"], a["h"],
+                                   a["g"], a["dk"], a["dv"], a["cap"], a["max_len"], 0.1, a["dtype"], a["ws"],
+                                   a["ws_bytes"], None)
+    assert call(max_len=100) == _lib.ERR_CAPACITY  # no room for the appended token
+    assert call(kn=None) == _lib.ERR_ARG
+    assert call(lens=None) == _lib.ERR_ARG
+    assert call(h=8, g=3) == _lib.ERR_GROUPS
+    assert call(dk=96, dv=96) == _lib.ERR_UNSUPPORTED
+    assert call(ws_bytes=8) == _lib.ERR_WORKSPACE
+    assert call(max_len=-2) == _lib.ERR_ARG
