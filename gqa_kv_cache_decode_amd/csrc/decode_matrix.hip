@@ -182,7 +182,7 @@ __device__ __forceinline__ void tile_step(WaveState<NB>& st, const bf16x8 (&qop)
 }
 
 template <int NB, bool FUSED>
-__global__ __launch_bounds__(kThreads) void decode_matrix_kernel(DecodeParams p) {
+__global__ __launch_bounds__(kThreads, NB == 1 ? 2 : 1) void decode_matrix_kernel(DecodeParams p) {
   __shared__ float sm_m[kWaves][16];
   __shared__ float sm_l[kWaves][16];
   __shared__ float sm_o[kWaves][16][D + OPAD];
@@ -191,6 +191,7 @@ __global__ __launch_bounds__(kThreads) void decode_matrix_kernel(DecodeParams p)
   __shared__ __attribute__((aligned(16))) float fin_o[NB * 16][D];
   __shared__ float sm_merge[kMergeLds];
   __shared__ int s_flag;
+  __shared__ SharedPiece s_deferred;
 
   const int wg = blockIdx.x;
   const int lane = threadIdx.x & 63;
@@ -205,8 +206,8 @@ __global__ __launch_bounds__(kThreads) void decode_matrix_kernel(DecodeParams p)
   PieceWalker walker;
   walker.init(p, wg);
   Piece pc;
-  Pending pend;
-  pend.n = 0;
+  DeferredPiece dfr;
+  dfr.init(&s_deferred);
   while (walker.next(pc)) {
     const int s = pc.s, j = pc.grp;
     const int i0 = j * G;
@@ -253,6 +254,7 @@ __global__ __launch_bounds__(kThreads) void decode_matrix_kernel(DecodeParams p)
       } else {
         tile_step<NB, false, false>(st, qop, kbase, vbase, t0, nvalid, sl2, n16, q4, NewRow{});
       }
+      dfr.take_if_due(p, w);
     }
 
     // merge the four waves through LDS, one 16-head block at a time
@@ -292,10 +294,10 @@ __global__ __launch_bounds__(kThreads) void decode_matrix_kernel(DecodeParams p)
       }
       __syncthreads();
     }
-    publish_piece<uint16_t>(p, pc, wg, i0, G, fin_m, fin_l, &fin_o[0][0], pend);
-    settle_pending<uint16_t, NB * 2>(p, pend, sm_merge, &s_flag);
-    pend.n = 0;
+    finish_piece<uint16_t, NB * 2>(p, pc, walker.more(), wg, i0, G, fin_m, fin_l, &fin_o[0][0], dfr, sm_merge,
+                                 &s_flag);
   }
+  dfr.resolve<uint16_t, NB * 2>(p, sm_merge, &s_flag);
   if (FUSED) finish_step(p, &s_flag);
 }
 

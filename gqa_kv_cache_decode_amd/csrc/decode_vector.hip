@@ -159,6 +159,7 @@ __global__ __launch_bounds__(kThreads) void decode_vector_kernel(DecodeParams p)
   __shared__ __attribute__((aligned(16))) float fin_o[HB][D];
   __shared__ float sm_merge[kMergeLds];
   __shared__ int s_flag;
+  __shared__ SharedPiece s_deferred;
 
   const int wg = blockIdx.x;
   const int lane = threadIdx.x & 63;
@@ -171,8 +172,8 @@ __global__ __launch_bounds__(kThreads) void decode_vector_kernel(DecodeParams p)
   PieceWalker walker;
   walker.init(p, wg);
   Piece pc;
-  Pending pend;
-  pend.n = 0;
+  DeferredPiece dfr;
+  dfr.init(&s_deferred);
   while (walker.next(pc)) {
     const int s = pc.s;
     const int j = pc.grp / p.nhb;
@@ -225,6 +226,7 @@ __global__ __launch_bounds__(kThreads) void decode_vector_kernel(DecodeParams p)
       } else {
         tile_step<T, D, HB, false, false>(st, qf, kbase, vbase, t0, nvalid, rg, NewRow<T>{});
       }
+      dfr.take_if_due(p, w);
     }
 
     // merge the lane groups of the wave (same column, different rows)
@@ -277,10 +279,10 @@ __global__ __launch_bounds__(kThreads) void decode_vector_kernel(DecodeParams p)
       }
     }
     __syncthreads();
-    publish_piece<T>(p, pc, wg, i0, nh, fin_m, fin_l, &fin_o[0][0], pend);
-    settle_pending<T, (HB * D / 4 + kThreads - 1) / kThreads>(p, pend, sm_merge, &s_flag);
-    pend.n = 0;
+    finish_piece<T, (HB * D / 4 + kThreads - 1) / kThreads>(p, pc, walker.more(), wg, i0, nh, fin_m, fin_l, &fin_o[0][0], dfr, sm_merge,
+                                 &s_flag);
   }
+  dfr.resolve<T, (HB * D / 4 + kThreads - 1) / kThreads>(p, sm_merge, &s_flag);
   if (FUSED) finish_step(p, &s_flag);
 }
 

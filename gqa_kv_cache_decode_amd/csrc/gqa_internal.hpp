@@ -341,6 +341,8 @@ struct PieceWalker {
     u_end = range_begin(wg + 1, total, parts);
   }
 
+  __device__ bool more() const { return u < u_end; }
+
   __device__ bool next(Piece& pc) {
     if (u >= u_end) return false;
     int L = lv.len(s);
@@ -378,56 +380,58 @@ __device__ __forceinline__ void store_out(TOut* out, size_t idx, float v) {
   else out[idx] = v;
 }
 
-// Shared pieces whose tickets are still to be taken (at most the first and
-// the last piece of a workgroup's range).
-struct Pending {
-  int n;
-  int s[2], grp[2], p0[2], p1[2], i0[2], nh[2];
+// A piece that shares its segment with other workgroups: the segment, its
+// first and last workgroups, and the query heads [i0, i0 + nh) it covers.
+struct SharedPiece {
+  int s, grp, p0, p1, i0, nh;
+  __device__ void set(const Piece& pc, int i0_, int nh_) {
+    s = pc.s;
+    grp = pc.grp;
+    p0 = pc.p0;
+    p1 = pc.p1;
+    i0 = i0_;
+    nh = nh_;
+  }
 };
 
-// Called by every thread of the workgroup once the piece's combined state for
-// query heads [i0, i0 + nh) is in LDS: sm_m[nh], sm_l[nh] (base-2 max, sum)
-// and sm_o[nh][d] (unnormalised output, 16-byte aligned).
-//
-// A segment inside one workgroup is written out directly. Otherwise the piece
-// goes to a partial slot of this workgroup: slot 1 if this workgroup owns the
-// segment's first unit (the piece is the last of its range), slot 0 if not
-// (the piece is the first of its range), and is recorded in `pend` for
-// settle_pending. (Taking the ticket right away, as the kernels do, measured
-// faster than deferring every ticket to the end of the range: deferral puts
-// two ticket round trips and up to two merges in series at the very end.)
+__device__ __forceinline__ int* ticket_of(const DecodeParams& p, const SharedPiece& sh) {
+  return p.ws_cnt + size_t(sh.s) * p.ngroups + sh.grp;
+}
+
+// The combined state of a piece for query heads [i0, i0 + nh) sits in LDS:
+// sm_m[nh], sm_l[nh] (base-2 max, sum) and sm_o[nh][d] (unnormalised output,
+// 16-byte aligned). A segment inside one workgroup is written out directly by
+// every thread.
 template <typename TOut>
-__device__ void publish_piece(const DecodeParams& p, const Piece& pc, int wg, int i0, int nh,
-                              const float* sm_m, const float* sm_l, const float* sm_o, Pending& pend) {
-  const int tid = threadIdx.x;
+__device__ void write_piece_out(const DecodeParams& p, int s, int i0, int nh, const float* sm_l,
+                                const float* sm_o) {
   const int d = p.d;
-  if (pc.p0 == pc.p1) {
-    TOut* out = static_cast<TOut*>(p.out);
-    const size_t out_row0 = (size_t(pc.s) * p.h + i0) * d;
-    for (int idx = tid; idx < nh * d; idx += kThreads) {
-      const float l = sm_l[idx / d];
-      store_out(out, out_row0 + idx, l > 0.0f ? sm_o[idx] / l : 0.0f);
-    }
-    return;
+  TOut* out = static_cast<TOut*>(p.out);
+  const size_t out_row0 = (size_t(s) * p.h + i0) * d;
+  for (int idx = threadIdx.x; idx < nh * d; idx += kThreads) {
+    const float l = sm_l[idx / d];
+    store_out(out, out_row0 + idx, l > 0.0f ? sm_o[idx] / l : 0.0f);
   }
+}
+
+// Store a shared piece's state into this workgroup's partial slot, with the
+// threads tid, tid + nthr, ...: slot 1 if this workgroup owns the segment's
+// first unit (the piece is the last of its range), slot 0 if not (the piece
+// is the first of its range). The stores bypass the non-coherent caches.
+__device__ void store_partial(const DecodeParams& p, const SharedPiece& sh, int wg, const float* sm_m,
+                              const float* sm_l, const float* sm_o, int tid, int nthr) {
+  const int d = p.d;
   const __amdgpu_buffer_rsrc_t rs = slots_rsrc(p);
   const int slot_bytes = p.slot_floats * int(sizeof(float));
   const int ml_off = p.gblk * d * int(sizeof(float));  // m then l after the o block
-  const int mine = (wg * 2 + (wg == pc.p0 ? 1 : 0)) * slot_bytes;
-  const int n4 = nh * d / 4;
-  for (int c4 = tid; c4 < n4; c4 += kThreads)
+  const int mine = (wg * 2 + (wg == sh.p0 ? 1 : 0)) * slot_bytes;
+  const int n4 = sh.nh * d / 4;
+  for (int c4 = tid; c4 < n4; c4 += nthr)
     coherent_store4(rs, mine + c4 * 16, *reinterpret_cast<const f32x4v*>(sm_o + 4 * c4));
-  for (int hh = tid; hh < nh; hh += kThreads) {
+  for (int hh = tid; hh < sh.nh; hh += nthr) {
     coherent_store1(rs, mine + ml_off + hh * 4, sm_m[hh]);
     coherent_store1(rs, mine + ml_off + (p.gblk + hh) * 4, sm_l[hh]);
   }
-  const int k = pend.n++;
-  pend.s[k] = pc.s;
-  pend.grp[k] = pc.grp;
-  pend.p0[k] = pc.p0;
-  pend.p1[k] = pc.p1;
-  pend.i0[k] = i0;
-  pend.nh[k] = nh;
 }
 
 // Merge of the n_slots partial states of one shared segment, by the
@@ -525,26 +529,98 @@ __device__ void merge_segment(const DecodeParams& p, int s, int p0, int n_slots,
   }
 }
 
-// Take the tickets of the workgroup's pending pieces (after their partial
-// stores have completed) and merge every segment for which this workgroup
-// arrived last; the merger re-zeroes the segment's ticket.
+// Take the ticket of a shared piece whose partial every thread has just
+// stored (after those stores have completed) and, if this workgroup arrived
+// last, merge the segment and re-zero its ticket.
 template <typename TOut, int MAXC>
-__device__ void settle_pending(const DecodeParams& p, const Pending& pend, float* sm_merge, int* sm_flag) {
-  if (pend.n == 0) return;
+__device__ void settle_shared(const DecodeParams& p, const SharedPiece& sh, float* sm_merge, int* sm_flag) {
   wait_stores();
   __syncthreads();
-  for (int k = 0; k < pend.n; ++k) {
-    int* cnt = p.ws_cnt + size_t(pend.s[k]) * p.ngroups + pend.grp[k];
-    if (threadIdx.x == 0) *sm_flag = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  int* cnt = ticket_of(p, sh);
+  if (threadIdx.x == 0) *sm_flag = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  const int n_slots = sh.p1 - sh.p0 + 1;
+  const bool last = *sm_flag == n_slots - 1;
+  __syncthreads();
+  if (last) {
+    merge_segment<TOut, MAXC>(p, sh.s, sh.p0, n_slots, sh.i0, sh.nh, sm_merge);
+    if (threadIdx.x == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// The first piece of a range that more pieces follow, when it is shared.
+// Settling it on the spot would stall the whole workgroup for a store
+// acknowledgement and a ticket round trip while the memory system is busiest
+// (measured at about 9 us). Instead wave 0 alone stores the partial (stored)
+// and the other waves go straight on to the next piece; wave 0 waits for its
+// stores and takes the ticket after its next tile (take), when they have
+// long completed; the ticket's value is looked at once the range is done
+// (resolve). The other workgroups of the segment hold it as their last or
+// only piece, so this workgroup is rarely the last to arrive.
+struct DeferredPiece {
+  SharedPiece* sh;  // in LDS
+  int state;        // 0 none, 1 partial stored, 2 ticket taken (wave 0's view)
+  int ticket;       // lane 0 of wave 0
+  __device__ void init(SharedPiece* lds) {
+    sh = lds;
+    state = 0;
+  }
+  // every thread; wave 0 stores
+  __device__ void stored(const DecodeParams& p, const SharedPiece& piece, int wg, const float* sm_m,
+                         const float* sm_l, const float* sm_o) {
+    state = 1;
+    if (threadIdx.x < 64) {
+      if (threadIdx.x == 0) *sh = piece;
+      store_partial(p, piece, wg, sm_m, sm_l, sm_o, threadIdx.x, 64);
+    }
+  }
+  // wave 0 only, once per deferred piece
+  __device__ void take(const DecodeParams& p) {
+    wait_stores();
+    if (threadIdx.x == 0)
+      ticket = __hip_atomic_fetch_add(ticket_of(p, *sh), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    state = 2;
+  }
+  __device__ __forceinline__ void take_if_due(const DecodeParams& p, int wave) {
+    if (wave == 0 && state == 1) take(p);
+  }
+  // every thread, after the range's last piece
+  template <typename TOut, int MAXC>
+  __device__ void resolve(const DecodeParams& p, float* sm_merge, int* sm_flag) {
+    if (state == 0) return;
+    if (threadIdx.x < 64 && state == 1) take(p);
     __syncthreads();
-    const int n_slots = pend.p1[k] - pend.p0[k] + 1;
+    if (threadIdx.x == 0) *sm_flag = ticket;
+    __syncthreads();
+    const SharedPiece d = *sh;
+    const int n_slots = d.p1 - d.p0 + 1;
     const bool last = *sm_flag == n_slots - 1;
     __syncthreads();
     if (last) {
-      merge_segment<TOut, MAXC>(p, pend.s[k], pend.p0[k], n_slots, pend.i0[k], pend.nh[k], sm_merge);
-      if (threadIdx.x == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      merge_segment<TOut, MAXC>(p, d.s, d.p0, n_slots, d.i0, d.nh, sm_merge);
+      if (threadIdx.x == 0) __hip_atomic_store(ticket_of(p, d), 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
+};
+
+// Every thread, once the piece's combined state is in LDS: write it out,
+// settle it, or defer it (see DeferredPiece).
+template <typename TOut, int MAXC>
+__device__ void finish_piece(const DecodeParams& p, const Piece& pc, bool more_follow, int wg, int i0, int nh,
+                             const float* sm_m, const float* sm_l, const float* sm_o, DeferredPiece& dfr,
+                             float* sm_merge, int* sm_flag) {
+  if (pc.p0 == pc.p1) {
+    write_piece_out<TOut>(p, pc.s, i0, nh, sm_l, sm_o);
+    return;
+  }
+  SharedPiece sh;
+  sh.set(pc, i0, nh);
+  if (more_follow) {  // the first piece of the range (slot 0)
+    dfr.stored(p, sh, wg, sm_m, sm_l, sm_o);
+    return;
+  }
+  store_partial(p, sh, wg, sm_m, sm_l, sm_o, threadIdx.x, kThreads);
+  settle_shared<TOut, MAXC>(p, sh, sm_merge, sm_flag);
 }
 
 // Fused step: every workgroup counts itself out; the last one, which runs
