@@ -191,7 +191,8 @@ int decode_common(const char* fn, void* out, const void* q, void* k_cache, void*
   if (rc != GQA_OK) return rc;
   const gqa::WorkspaceLayout ws = gqa::workspace_layout(b, h, gblk_bound(h / g), d_v);
   if (!workspace) return fail(GQA_ERR_WORKSPACE, "%s: workspace is null (%zu bytes needed)", fn, ws.total);
-  if (workspace_bytes < ws.total)
+  const size_t usable = workspace_bytes & ~size_t(255);
+  if (usable < ws.total)
     return fail(GQA_ERR_WORKSPACE, "%s: workspace has %zu bytes, %zu needed", fn, workspace_bytes, ws.total);
   if (reinterpret_cast<uintptr_t>(workspace) & 255)
     return fail(GQA_ERR_ARG, "%s: workspace must be 256-byte aligned", fn);
@@ -205,9 +206,10 @@ int decode_common(const char* fn, void* out, const void* q, void* k_cache, void*
   p.k_new = k_new;
   p.v_new = v_new;
   char* wsb = static_cast<char*>(workspace);
-  p.ws_cnt = reinterpret_cast<int*>(wsb + ws.cnt_off);
-  p.ws_done = reinterpret_cast<int*>(wsb + ws.done_off);
-  p.ws_slots = reinterpret_cast<float*>(wsb + ws.slot_off);
+  p.ws_slots = reinterpret_cast<float*>(wsb);
+  p.ws_done = reinterpret_cast<int*>(wsb + usable - 256);
+  p.ws_cnt = reinterpret_cast<int*>(wsb + usable - 256 - ws.cnt_bytes);
+  p.cnt_stride = int(gqa::counter_stride(b, h));
   p.b = b;
   p.h = h;
   p.g = g;

@@ -66,7 +66,7 @@ struct DecodeParams {
   int32_t* lens;      // written only by the fused step (+1, by the last workgroup)
   const void* k_new;  // fused step: the new token's rows [b][g][d]
   const void* v_new;
-  int* ws_cnt;
+  int* ws_cnt;        // tickets, cnt_stride ints apart
   int* ws_done;       // fused step: workgroups finished (zero between calls)
   float* ws_slots;
   int b, h, g, G, d, cap;
@@ -77,13 +77,27 @@ struct DecodeParams {
   int ngroups;      // segments per sequence: g * nhb
   int slot_floats;  // gblk * d + round_up(2 * gblk, 4)
   int workgroups;   // persistent grid size P
+  int cnt_stride;   // ints between consecutive tickets
   float scale_log2; // scale * log2(e)
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// Workspace layout, relative to the end of the caller's buffer so that a
+// buffer sized for one shape serves every smaller shape without the regions
+// of one call overlapping those of another: partial slots from the start,
+// then (at the end) the tickets and, in the last 256 bytes, the fused step's
+// counter. Tickets sit 128 bytes apart when b*h <= 8192, so that workgroups
+// taking tickets of different segments at the same moment do not contend for
+// one cache line; the ticket region never shrinks as b*h grows.
+inline size_t counter_stride(int b, int h) { return size_t(b) * size_t(h) <= 8192 ? 32 : 1; }
+inline size_t counter_ints(int b, int h) {
+  const size_t bh = size_t(b) * size_t(h);
+  return bh <= 8192 ? 32 * bh : (bh > 262144 ? bh : 262144);
+}
+
 struct WorkspaceLayout {
-  size_t cnt_off, done_off, slot_off, total;
+  size_t slot_bytes, cnt_bytes, total;
 };
 
 inline int slot_floats_for(int gblk, int d_v) { return gblk * d_v + ((2 * gblk + 3) & ~3); }
@@ -91,10 +105,9 @@ inline int slot_floats_for(int gblk, int d_v) { return gblk * d_v + ((2 * gblk +
 // gblk_bound: the largest head block any path may use for this shape.
 inline WorkspaceLayout workspace_layout(int b, int h, int gblk_bound, int d_v) {
   WorkspaceLayout w;
-  w.cnt_off = 0;
-  w.done_off = size_t(b) * size_t(h) * sizeof(int);
-  w.slot_off = align256(w.done_off + sizeof(int));
-  w.total = w.slot_off + align256(size_t(kMaxWorkgroups) * 2 * size_t(slot_floats_for(gblk_bound, d_v)) * sizeof(float));
+  w.slot_bytes = align256(size_t(kMaxWorkgroups) * 2 * size_t(slot_floats_for(gblk_bound, d_v)) * sizeof(float));
+  w.cnt_bytes = align256(counter_ints(b, h) * sizeof(int));
+  w.total = w.slot_bytes + w.cnt_bytes + 256;
   return w;
 }
 
@@ -395,7 +408,7 @@ struct SharedPiece {
 };
 
 __device__ __forceinline__ int* ticket_of(const DecodeParams& p, const SharedPiece& sh) {
-  return p.ws_cnt + size_t(sh.s) * p.ngroups + sh.grp;
+  return p.ws_cnt + (size_t(sh.s) * p.ngroups + sh.grp) * p.cnt_stride;
 }
 
 // The combined state of a piece for query heads [i0, i0 + nh) sits in LDS:

@@ -99,12 +99,16 @@ int gqa_kv_append(void* k_cache, void* v_cache, const void* k_new, const void* v
  * with b, h/g and d_v no larger than these (it does not grow with max_len).
  * Returns 0 for invalid arguments.
  *
- * The workspace holds int32 tickets (at most one per sequence and query
- * head) and the split-softmax partial states of the persistent workgroups. The tickets
- * must be ZERO before the first call that uses a buffer (e.g. allocate it
- * zero-filled); every call leaves them zero again. Two calls that share a
- * workspace must be ordered (same stream or synchronised); calls with
- * distinct workspaces may run concurrently.
+ * The workspace (256-byte aligned) holds the split-softmax partial states of
+ * the persistent workgroups from its start, and int32 counters at its end:
+ * the last 256 + 4*n bytes (of the buffer's size rounded down to 256), with
+ * n = 32*b*h if b*h <= 8192, else max(b*h, 262144). Those counter bytes must
+ * be ZERO before the first call that uses a buffer (e.g. allocate it
+ * zero-filled); every call leaves them zero again. Because the counters are
+ * placed from the end, a buffer sized for one shape serves any sequence of
+ * calls with b, h, h/g and d_v no larger. Two calls that share a workspace
+ * must be ordered (same stream or synchronised); calls with distinct
+ * workspaces may run concurrently.
  */
 size_t gqa_decode_workspace_size(int b, int h, int g, int d_k, int d_v, int max_len, int dtype);
 

@@ -63,3 +63,17 @@ def assert_parity(got_dev: torch.Tensor, ref: np.ndarray, dtype: str, what: str 
         assert rep["max_abs"] <= BF16_MAX_ABS, f"{what}: {rep}"
         assert rep["max_row_rel"] <= BF16_ROW_REL, f"{what}: {rep}"
     return rep
+
+
+def counter_bytes(ws, b, h):
+    """The workspace's counter region (its last 256 + 4n bytes, as the header states)."""
+    bh = b * h
+    n = 32 * bh if bh <= 8192 else max(bh, 262144)
+    usable = (ws.numel() * ws.element_size()) & ~255
+    cnt = ((4 * n + 255) // 256) * 256
+    return ws.view(torch.uint8)[usable - 256 - cnt: usable]
+
+
+def assert_counters_zero(ws, b, h):
+    region = counter_bytes(ws, b, h)
+    assert int(region.view(torch.int32).abs().sum()) == 0, "workspace counters not back to zero"

@@ -113,6 +113,24 @@ def test_workspace_size(lib):
     assert ws(1, 1, 1, 16, 16, 0, _lib.F32) > 0
 
 
+def test_workspace_size_monotone(lib):
+    # a buffer sized for one shape must serve every smaller shape: the size
+    # never decreases as b, h (at fixed h/g) or d_v grow, also across the
+    # b*h = 8192 boundary where the tickets stop being padded to 128 bytes
+    ws = lib.gqa_decode_workspace_size
+    shapes = [(b, G * g, g, d) for b in (1, 7, 64, 128, 129, 256, 1024) for g in (1, 2, 8)
+              for G in (1, 4, 8, 64) for d in (16, 128) if G * g <= 4096]
+    for (b, h, g, d) in shapes:
+        n = ws(b, h, g, d, d, 100, _lib.BF16)
+        assert n > 0 and n % 256 == 0
+        bh = b * h
+        tickets = 32 * bh if bh <= 8192 else max(bh, 262144)
+        assert n >= 4 * tickets + 256
+        for (b2, h2, g2, d2) in shapes:
+            if b2 <= b and h2 <= h and h2 // g2 <= h // g and d2 <= d:
+                assert ws(b2, h2, g2, d2, d2, 100, _lib.BF16) <= n, ((b, h, g, d), (b2, h2, g2, d2))
+
+
 def test_plan_choices(lib):
     def plan(b, h, g, d, cap, max_len, dtype, path=0, wgs=0):
         p, c = ctypes.c_int(), ctypes.c_int()

@@ -11,7 +11,7 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_util import assert_parity, to_dev, to_host_bits, torch_dtype
+from gpu_util import assert_counters_zero, assert_parity, to_dev, to_host_bits, torch_dtype
 from gqa_kv_cache_decode_amd import api, inputs
 from gqa_kv_cache_decode_amd.workloads import WORKLOADS
 
@@ -75,8 +75,7 @@ def test_workload_one_step(gpu_lib, oracle_mod, name):
     rep = assert_parity(out, ref, pb.dtype, name)
     print(f"  {name}: {rep}", flush=True)
     # the split counters are back to zero after the call
-    cnt = ws[: pb.b * pb.h * 4].view(torch.int32)
-    assert int(cnt.abs().sum()) == 0
+    assert_counters_zero(ws, pb.b, pb.h)
 
 
 @pytest.fixture(scope="module")
@@ -194,15 +193,33 @@ def test_unit_scale_and_large_logits(gpu_lib, oracle_mod):
 
 
 def test_workspace_reuse_across_shapes(gpu_lib, oracle_mod):
-    # one workspace sized for the largest call serves smaller ones in turn
+    # one workspace sized for the largest call serves smaller ones in any order
     big = Problem(oracle_mod, seed=93, b=4, h=16, g=2, d=128, cap=2000, lens=[2000, 1500, 900, 10], dtype="bf16")
     small = Problem(oracle_mod, seed=94, b=2, h=16, g=4, d=128, cap=500, lens=[500, 333], dtype="bf16")
     ws = api.make_workspace(4, 16, 2, 128, 128, 2000, torch.bfloat16, "cuda")
-    for pb in (big, small, big):
+    for pb in (small, big, small, big):
         q = pb.query()
         out = torch.empty(pb.b, pb.h, pb.d, dtype=torch.bfloat16, device="cuda")
         api.decode_attention(out, to_dev(q), pb.kc, pb.vc, pb.lens, int(pb.lens_h.max()), pb.scale, ws,
                              workgroups=64)
         torch.cuda.synchronize()
         assert_parity(out, pb.oracle_attention(q), "bf16")
-    assert int(ws[: 4 * 16 * 4].view(torch.int32).abs().sum()) == 0
+        assert_counters_zero(ws, pb.b, pb.h)
+    assert_counters_zero(ws, 4, 16)
+
+
+def test_workspace_reuse_across_ticket_padding(gpu_lib, oracle_mod):
+    # b*h above 8192 packs the tickets, at most 8192 pads them; one buffer serves both
+    big = Problem(oracle_mod, seed=95, b=160, h=64, g=8, d=128, cap=64,
+                  lens=[(7 * s) % 60 + 1 for s in range(160)], dtype="bf16")
+    small = Problem(oracle_mod, seed=96, b=100, h=64, g=8, d=128, cap=64,
+                    lens=[(11 * s) % 60 + 1 for s in range(100)], dtype="bf16")
+    ws = api.make_workspace(160, 64, 8, 128, 128, 64, torch.bfloat16, "cuda")
+    for pb in (small, big, small, big):
+        q = pb.query()
+        out = torch.empty(pb.b, pb.h, pb.d, dtype=torch.bfloat16, device="cuda")
+        api.decode_attention(out, to_dev(q), pb.kc, pb.vc, pb.lens, int(pb.lens_h.max()), pb.scale, ws,
+                             workgroups=1024)
+        torch.cuda.synchronize()
+        assert_parity(out, pb.oracle_attention(q), "bf16")
+        assert_counters_zero(ws, pb.b, pb.h)

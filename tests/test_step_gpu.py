@@ -10,7 +10,7 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_util import assert_parity, to_dev, to_host_bits, torch_dtype
+from gpu_util import assert_counters_zero, assert_parity, to_dev, to_host_bits, torch_dtype
 from gqa_kv_cache_decode_amd import api, inputs
 from gqa_kv_cache_decode_amd.workloads import WORKLOADS
 
@@ -50,8 +50,7 @@ class StepProblem:
         assert np.array_equal(self.lens.cpu().numpy(), self.lens_h)
         assert np.array_equal(to_host_bits(self.kc).view(np.uint8), self.batch.k_cache.view(np.uint8))
         assert np.array_equal(to_host_bits(self.vc).view(np.uint8), self.batch.v_cache.view(np.uint8))
-        n = self.b * self.h + 1  # tickets and the step's finish counter
-        assert int(self.ws[: 4 * n].view(torch.int32).abs().sum()) == 0
+        assert_counters_zero(self.ws, self.b, self.h)  # tickets and the step's finish counter
 
 
 def _workload(oracle_mod, name):
@@ -127,3 +126,16 @@ def test_step_equals_two_calls(gpu_lib, oracle_mod):
     assert torch.equal(a.kc.view(torch.int16), b.kc.view(torch.int16))
     assert torch.equal(a.vc.view(torch.int16), b.vc.view(torch.int16))
     assert (got_a.float() - out.float()).abs().max().item() <= 2e-2
+
+
+@pytest.mark.parametrize("b,path,dtype,d", [(64, api.PATH_MATRIX, "bf16", 128), (65, api.PATH_MATRIX, "bf16", 128),
+                                            (130, api.PATH_VECTOR, "f32", 32), (200, api.PATH_AUTO, "bf16", 64)])
+def test_step_batch_sizes_around_64(gpu_lib, oracle_mod, b, path, dtype, d):
+    # up to 64 sequences the kernels keep lens in registers and count the
+    # workgroups out early; beyond that they read lens while walking
+    lens = [(37 * s) % 150 for s in range(b)]
+    pb = StepProblem(oracle_mod, seed=305 + b, b=b, h=8, g=2, d=d, cap=160, lens=lens, dtype=dtype)
+    for step in range(3):
+        got, ref = pb.step(step, path=path)
+        assert_parity(got, ref, dtype, f"b={b} step={step}")
+        pb.check_state()
