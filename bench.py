@@ -214,7 +214,8 @@ def main():
 
     value = total_bytes / (elapsed_ms / 1e3) / 1e9
     achieved = bytes_per_launch / (kern_avg_ms / 1e3) / 1e9
-    plan_path, plan_wgs = api.plan(wl.b, wl.h, wl.g, wl.d, wl.d, cap, max_len_bound, dt, args.path, args.workgroups)
+    plan_path, plan_wgs, plan_merge = api.plan(wl.b, wl.h, wl.g, wl.d, wl.d, cap, max_len_bound, dt, args.path,
+                                               args.workgroups)
     traffic = traffic_from_profile(wl.name)
 
     cpu = None
@@ -244,6 +245,7 @@ def main():
             "lens_drawn_mean": float(lens0.mean()), "lens_drawn_min": int(lens0.min()),
             "lens_drawn_max": int(lens0.max()), "cache_sets": n_sets, "seed": wl.seed,
             "path": {1: "vector", 2: "matrix"}[plan_path], "workgroups": plan_wgs,
+            "split_merge": "second launch" if plan_merge == api.MERGE_KERNEL else "in the decode kernel",
             "step_api": "gqa_kv_append + gqa_decode_attention" if args.unfused else "gqa_decode_step",
             "kv_bytes_per_step": int(bytes_per_launch),
         },

@@ -23,6 +23,8 @@ ERR_HIP = -6
 PATH_AUTO = 0
 PATH_VECTOR = 1
 PATH_MATRIX = 2
+MERGE_INLINE = 0x10  # OR into path: split segments merged inside the decode launch
+MERGE_KERNEL = 0x20  # OR into path: split segments merged by a second launch
 
 ERROR_NAMES = {
     ERR_ARG: "GQA_ERR_ARG", ERR_GROUPS: "GQA_ERR_GROUPS", ERR_UNSUPPORTED: "GQA_ERR_UNSUPPORTED",

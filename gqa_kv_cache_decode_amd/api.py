@@ -12,7 +12,7 @@ import ctypes
 import torch
 
 from . import _lib
-from ._lib import PATH_AUTO, PATH_MATRIX, PATH_VECTOR  # noqa: F401  (re-exported)
+from ._lib import MERGE_INLINE, MERGE_KERNEL, PATH_AUTO, PATH_MATRIX, PATH_VECTOR  # noqa: F401  (re-exported)
 
 _DTYPES = {torch.float32: _lib.F32, torch.bfloat16: _lib.BF16}
 
@@ -76,13 +76,17 @@ def make_workspace(b: int, h: int, g: int, d_k: int, d_v: int, max_len: int, dty
 
 
 def plan(b, h, g, d_k, d_v, cap, max_len, dtype: torch.dtype, path=PATH_AUTO, workgroups=0):
-    """(path, workgroups) the library would launch with on the current device; no GPU work."""
+    """(path, workgroups, merge) the library would launch with on the current device; no GPU work.
+
+    path is PATH_VECTOR or PATH_MATRIX; merge is MERGE_INLINE or MERGE_KERNEL.
+    """
     lib = _lib.load()
     p, c = ctypes.c_int(0), ctypes.c_int(0)
     rc = lib.gqa_decode_plan(b, h, g, d_k, d_v, cap, int(max_len), _DTYPES[dtype], path, workgroups,
                              ctypes.byref(p), ctypes.byref(c))
     _lib.check(rc, "gqa_decode_plan")
-    return p.value, c.value
+    merge = p.value & (MERGE_INLINE | MERGE_KERNEL)
+    return p.value & ~(MERGE_INLINE | MERGE_KERNEL), c.value, merge
 
 
 def decode_attention(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
@@ -91,6 +95,7 @@ def decode_attention(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor, 
     """out[s,i] = softmax_t(scale * q[s,i] . K[s,j,t]) @ V[s,j,t], t < lens[s], j = i // (h/g).
 
     q [b,h,d_k], caches [b,g,cap,d], lens int32 [b] (attended lengths), out [b,h,d_v].
+    path: PATH_* optionally OR-ed with MERGE_INLINE / MERGE_KERNEL.
     """
     _check_gpu(out, q, k_cache, v_cache, lens, workspace)
     if lens.dtype != torch.int32:

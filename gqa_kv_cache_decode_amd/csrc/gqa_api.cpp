@@ -56,6 +56,7 @@ struct Plan {
   int gblk;
   int nhb;
   int workgroups;
+  bool merge_kernel;  // shared segments merged by a second launch
 };
 
 // Largest head block any path may use for G heads per KV head (workspace sizing).
@@ -85,8 +86,13 @@ int plan_decode(int b, int h, int g, int d_k, int d_v, int cap, int max_len, int
                 d_k, d_v);
   if (max_len > cap) return fail(GQA_ERR_CAPACITY, "max_len=%d exceeds cap=%d", max_len, cap);
   if (max_len > kMaxLen) return fail(GQA_ERR_UNSUPPORTED, "max_len=%d exceeds %d", max_len, kMaxLen);
-  if (path != GQA_PATH_AUTO && path != GQA_PATH_VECTOR && path != GQA_PATH_MATRIX)
-    return fail(GQA_ERR_UNSUPPORTED, "path=%d is not a GQA_PATH_* value", path);
+  const int merge_req = path & (GQA_MERGE_INLINE | GQA_MERGE_KERNEL);
+  const int path_req = path & ~(GQA_MERGE_INLINE | GQA_MERGE_KERNEL);
+  if ((path_req != GQA_PATH_AUTO && path_req != GQA_PATH_VECTOR && path_req != GQA_PATH_MATRIX) ||
+      merge_req == (GQA_MERGE_INLINE | GQA_MERGE_KERNEL))
+    return fail(GQA_ERR_UNSUPPORTED, "path=%d is not a GQA_PATH_* value, optionally with one GQA_MERGE_* flag",
+                path);
+  path = path_req;
   if (workgroups < 0 || workgroups > gqa::kMaxWorkgroups)
     return fail(GQA_ERR_UNSUPPORTED, "workgroups=%d must be in [0, %d]", workgroups, gqa::kMaxWorkgroups);
 
@@ -107,7 +113,11 @@ int plan_decode(int b, int h, int g, int d_k, int d_v, int cap, int max_len, int
     plan->gblk = gqa::vector_heads_per_block(G);
     plan->nhb = (G + plan->gblk - 1) / plan->gblk;
   }
-  if (workgroups == 0) {
+  const int unit_len = gqa::kTile * gqa::kUnitTiles;
+  const long long segments = (long long)b * g * plan->nhb;
+  const long long units_bound = segments * ((max_len + unit_len - 1) / unit_len);  // lengths <= max_len
+  const bool auto_grid = workgroups == 0;
+  if (auto_grid) {
     // Up to two 4-wave workgroups per compute unit (8 waves keep enough loads
     // in flight), never more than fit at once, so the persistent grid runs in
     // a single round.
@@ -116,19 +126,31 @@ int plan_decode(int b, int h, int g, int d_k, int d_v, int cap, int max_len, int
     if (fit <= 0) fit = 2;  // no device to ask: assume the common case
     const int per_cu = fit < 2 ? fit : 2;
     long long n = (long long)device_cus() * per_cu;
-    // Each shared piece leaves gblk*(d_v+2) floats to merge; for large head
-    // groups keep at least G/2 tiles per workgroup (max 4 KiB of partial
-    // state per 16 KiB tile of K/V) so that single-workgroup merges stay
-    // small. The unit count is bounded on the host by max_len.
-    const int unit_len = gqa::kTile * gqa::kUnitTiles;
-    const long long units_bound = (long long)b * g * plan->nhb * ((max_len + unit_len - 1) / unit_len);
-    const int min_tiles = plan->gblk / 2;
-    const int min_units = min_tiles > gqa::kUnitTiles ? (min_tiles + gqa::kUnitTiles - 1) / gqa::kUnitTiles : 1;
-    const long long by_work = (units_bound + min_units - 1) / min_units;
-    if (n > by_work) n = by_work;
+    if (n > units_bound) n = units_bound;
     if (n < 1) n = 1;
     if (n > gqa::kMaxWorkgroups) n = gqa::kMaxWorkgroups;
     workgroups = int(n);
+  }
+  // Merging a shared segment inside the decode kernel falls to the one
+  // workgroup that arrives last, which reads all the segment's partial states
+  // alone at the very end; past 64 KiB of them per segment a second launch
+  // that merges with one workgroup per (segment, head) is faster.
+  if (merge_req == GQA_MERGE_KERNEL) {
+    plan->merge_kernel = true;
+  } else if (merge_req == GQA_MERGE_INLINE) {
+    plan->merge_kernel = false;
+  } else {
+    const long long slots_per_segment = workgroups / (segments > 0 ? segments : 1) + 1;
+    plan->merge_kernel = slots_per_segment * plan->gblk * d_v * 4 > 64 * 1024;
+  }
+  if (auto_grid && !plan->merge_kernel) {
+    // Inline merges: for large head groups keep at least G/2 tiles per
+    // workgroup (at most 4 KiB of partial state per 16 KiB tile of K/V) so
+    // that the single-workgroup merges stay small.
+    const int min_tiles = plan->gblk / 2;
+    const int min_units = min_tiles > gqa::kUnitTiles ? (min_tiles + gqa::kUnitTiles - 1) / gqa::kUnitTiles : 1;
+    const long long by_work = (units_bound + min_units - 1) / min_units;
+    if (workgroups > by_work) workgroups = int(by_work > 0 ? by_work : 1);
   }
   plan->workgroups = workgroups;
   return GQA_OK;
@@ -171,7 +193,7 @@ int gqa_decode_plan(int b, int h, int g, int d_k, int d_v, int cap, int max_len,
   Plan plan;
   const int rc = plan_decode(b, h, g, d_k, d_v, cap, max_len, dtype, path, workgroups, &plan);
   if (rc != GQA_OK) return rc;
-  if (chosen_path) *chosen_path = plan.path;
+  if (chosen_path) *chosen_path = plan.path | (plan.merge_kernel ? GQA_MERGE_KERNEL : GQA_MERGE_INLINE);
   if (chosen_workgroups) *chosen_workgroups = plan.workgroups;
   return ok();
 }
@@ -206,10 +228,12 @@ int decode_common(const char* fn, void* out, const void* q, void* k_cache, void*
   p.k_new = k_new;
   p.v_new = v_new;
   char* wsb = static_cast<char*>(workspace);
-  p.ws_slots = reinterpret_cast<float*>(wsb);
+  p.seg_info = reinterpret_cast<int2*>(wsb);
+  p.ws_slots = reinterpret_cast<float*>(wsb + ws.info_bytes);
   p.ws_done = reinterpret_cast<int*>(wsb + usable - 256);
   p.ws_cnt = reinterpret_cast<int*>(wsb + usable - 256 - ws.cnt_bytes);
   p.cnt_stride = int(gqa::counter_stride(b, h));
+  p.merge_kernel = plan.merge_kernel ? 1 : 0;
   p.b = b;
   p.h = h;
   p.g = g;
@@ -226,9 +250,13 @@ int decode_common(const char* fn, void* out, const void* q, void* k_cache, void*
   p.scale_log2 = scale * kLog2e;
 
   const hipStream_t st = static_cast<hipStream_t>(stream);
-  const hipError_t e = plan.path == GQA_PATH_MATRIX ? gqa::launch_decode_matrix(p, st)
-                                                    : gqa::launch_decode_vector(p, dtype, st);
+  hipError_t e = plan.path == GQA_PATH_MATRIX ? gqa::launch_decode_matrix(p, st)
+                                              : gqa::launch_decode_vector(p, dtype, st);
   if (e != hipSuccess) return fail(GQA_ERR_HIP, "%s launch: %s", fn, hipGetErrorString(e));
+  if (plan.merge_kernel) {
+    e = gqa::launch_merge_partials(p, dtype, st);
+    if (e != hipSuccess) return fail(GQA_ERR_HIP, "%s merge launch: %s", fn, hipGetErrorString(e));
+  }
   return ok();
 }
 

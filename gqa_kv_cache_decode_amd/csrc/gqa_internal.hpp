@@ -2,37 +2,46 @@
 //
 // Work schedule (both decode kernels)
 // -----------------------------------
-// The attention of one decode step is cut into units of TILE = 32 cached
-// positions of one "segment" (sequence s, KV-head group grp). Units are
-// ordered (s, grp, tile). With T units in all and P' = min(P, T) of the P
+// The attention of one decode step is cut into units of four 32-position
+// tiles (one tile for each wave of a workgroup) of one "segment" (sequence
+// s, KV-head group grp); a segment's last unit may be short. Units are
+// ordered (s, grp, unit). With T units in all and P' = min(P, T) of the P
 // persistent workgroups taking part, workgroup p < P' takes the contiguous
-// range [floor(p*T/P'), floor((p+1)*T/P')) (never empty), so
-// every workgroup streams the same number of K/V bytes (within one tile) and
-// all finish together. T depends on the device-side lengths, so each wave
-// recomputes the schedule from lens at kernel start (a prefix sum over b).
+// range [floor(p*T/P'), floor((p+1)*T/P')) (never empty), so every workgroup
+// streams the same number of K/V bytes (within one unit) and all finish
+// together. T depends on the device-side lengths, so each wave recomputes the
+// schedule from lens at kernel start (a prefix sum over b).
 //
-// A workgroup's range is a run of "pieces": maximal runs of tiles inside one
+// A workgroup's range is a run of "pieces": maximal runs of units inside one
 // segment. Only its first and its last piece can be part of a segment shared
-// with other workgroups; whole segments are finished directly. A shared piece
-// leaves its split-softmax state (m, l, o) in one of the workgroup's two
-// partial slots; the last workgroup of the segment to arrive (an atomic
-// ticket per segment) merges the slots and writes the output.
+// with other workgroups; whole segments are written out directly. A shared
+// piece leaves its split-softmax state (m, l, o) in one of the workgroup's
+// two partial slots. Attention over a set of positions split into parts is
+// recovered exactly from the parts' states: with M = max_k m_k, the output is
+// sum_k 2^(m_k - M) o_k / sum_k 2^(m_k - M) l_k (the softmax of the MQA
+// review, §2.1, written over a union of position sets). Either the last
+// workgroup of the segment to arrive (an atomic ticket per segment) merges
+// the slots, or, for shapes whose segments are split over many workgroups, a
+// second launch (merge_partials_kernel) merges every shared segment with one
+// workgroup per (segment, query head).
 //
 // Cross-workgroup visibility without cache-wide fences: on this multi-XCD
 // part a device-scope release fence writes back a whole L2, which costs more
 // than the attention itself. The partial states are therefore written with
-// agent-scope atomic stores (coherent at device scope), their completion is
-// awaited (s_waitcnt vmcnt(0)) before the ticket's agent-scope atomic add, and
-// the merging workgroup reads them with agent-scope atomic loads. Only these
-// atomic accesses touch the shared data, so no L2 writeback or invalidate is
-// needed.
+// buffer stores that bypass the non-coherent caches (SC1), their completion
+// is awaited (s_waitcnt vmcnt(0)) before the ticket's agent-scope atomic add,
+// and the merging workgroup reads them with SC1 buffer loads. Only these
+// accesses touch the shared data, so no L2 writeback or invalidate is needed.
 //
-// Workspace layout (caller-owned, see gqa_decode_workspace_size):
-//   [counters] int32 [b * h], then int32 done                 zero between calls
-//   [slots]    float [kMaxWorkgroups][2][slot_floats]         slot = o[gb][d], m[gb], l[gb]
+// Workspace layout (caller-owned, see gqa_decode_workspace_size), from the
+// start of the buffer:
+//   [segment table] int2 [b * h]                              separate merge only
+//   [slots]  float [kMaxWorkgroups][2][slot_floats]           slot = o[gb][d], m[gb], l[gb]
+// and from its end (size rounded down to 256 bytes):
+//   [tickets] int32, cnt_stride apart                         zero between calls
+//   [done]   int32 in the last 256 bytes                      zero between calls
 // slot_floats = gb*d + round_up(2*gb, 4), so every slot and its o block are
-// 16-byte aligned.
-// Each region starts on a 256-byte boundary.
+// 16-byte aligned. Each region starts on a 256-byte boundary.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -78,6 +87,8 @@ struct DecodeParams {
   int slot_floats;  // gblk * d + round_up(2 * gblk, 4)
   int workgroups;   // persistent grid size P
   int cnt_stride;   // ints between consecutive tickets
+  int merge_kernel; // 1: shared segments are merged by merge_partials_kernel after this launch
+  int2* seg_info;   // merge_kernel: per segment (p0, p1) of its shared pieces, p1 = -1 if none
   float scale_log2; // scale * log2(e)
 };
 
@@ -97,17 +108,20 @@ inline size_t counter_ints(int b, int h) {
 }
 
 struct WorkspaceLayout {
-  size_t slot_bytes, cnt_bytes, total;
+  size_t info_bytes, slot_bytes, cnt_bytes, total;
 };
 
 inline int slot_floats_for(int gblk, int d_v) { return gblk * d_v + ((2 * gblk + 3) & ~3); }
 
-// gblk_bound: the largest head block any path may use for this shape.
+// gblk_bound: the largest head block any path may use for this shape. From
+// the start: the segment table of the separate merge (two ints per segment,
+// at most b*h segments), then the partial slots; tickets at the end.
 inline WorkspaceLayout workspace_layout(int b, int h, int gblk_bound, int d_v) {
   WorkspaceLayout w;
+  w.info_bytes = align256(size_t(b) * size_t(h) * 2 * sizeof(int));
   w.slot_bytes = align256(size_t(kMaxWorkgroups) * 2 * size_t(slot_floats_for(gblk_bound, d_v)) * sizeof(float));
   w.cnt_bytes = align256(counter_ints(b, h) * sizeof(int));
-  w.total = w.slot_bytes + w.cnt_bytes + 256;
+  w.total = w.info_bytes + w.slot_bytes + w.cnt_bytes + 256;
   return w;
 }
 
@@ -119,6 +133,7 @@ constexpr int kMergeLds = 2 * kMergePairs + 3 * kMatrixMaxGroup;
 hipError_t launch_append(const AppendParams& p, int b, int dtype, hipStream_t stream);
 hipError_t launch_decode_vector(const DecodeParams& p, int dtype, hipStream_t stream);
 hipError_t launch_decode_matrix(const DecodeParams& p, hipStream_t stream);
+hipError_t launch_merge_partials(const DecodeParams& p, int dtype, hipStream_t stream);
 
 // Workgroups of the decode kernel instance that fit on one compute unit at
 // once (runtime occupancy query, cached; 0 if the runtime cannot say).
@@ -622,12 +637,18 @@ template <typename TOut, int MAXC>
 __device__ void finish_piece(const DecodeParams& p, const Piece& pc, bool more_follow, int wg, int i0, int nh,
                              const float* sm_m, const float* sm_l, const float* sm_o, DeferredPiece& dfr,
                              float* sm_merge, int* sm_flag) {
+  if (p.merge_kernel && pc.tile_begin == 0 && threadIdx.x == 0)
+    p.seg_info[size_t(pc.s) * p.ngroups + pc.grp] = make_int2(pc.p0, pc.p0 == pc.p1 ? -1 : pc.p1);
   if (pc.p0 == pc.p1) {
     write_piece_out<TOut>(p, pc.s, i0, nh, sm_l, sm_o);
     return;
   }
   SharedPiece sh;
   sh.set(pc, i0, nh);
+  if (p.merge_kernel) {  // merged by the next launch: store and go on
+    store_partial(p, sh, wg, sm_m, sm_l, sm_o, threadIdx.x, kThreads);
+    return;
+  }
   if (more_follow) {  // the first piece of the range (slot 0)
     dfr.stored(p, sh, wg, sm_m, sm_l, sm_o);
     return;
@@ -656,6 +677,8 @@ __device__ void zero_empty_sequences(const DecodeParams& p, int wg) {
   TOut* out = static_cast<TOut*>(p.out);
   for (int s = wg; s < p.b; s += p.workgroups) {
     if (attended_len(p, s) != 0) continue;
+    if (p.merge_kernel)
+      for (int k = threadIdx.x; k < p.ngroups; k += kThreads) p.seg_info[size_t(s) * p.ngroups + k] = make_int2(0, -1);
     const size_t row0 = size_t(s) * p.h * p.d;
     for (int idx = threadIdx.x; idx < p.h * p.d; idx += kThreads) out[row0 + idx] = TOut(0);
   }

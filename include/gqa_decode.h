@@ -71,6 +71,10 @@ extern "C" {
 #define GQA_PATH_VECTOR 1 /* vector-ALU kernel: every supported shape and dtype   */
 #define GQA_PATH_MATRIX 2 /* MFMA kernel: bf16, d_k = d_v = 128, up to 64 heads/KV */
 
+/* How segments split over several workgroups are merged; OR one into path. */
+#define GQA_MERGE_INLINE 0x10 /* by the segment's last workgroup, inside the decode launch */
+#define GQA_MERGE_KERNEL 0x20 /* by a second launch, one workgroup per (segment, head)  */
+
 /*
  * Append one token per sequence ("LLM inference 05": push K, push V;
  * MQA review §2.4 / §3: the new row is concatenated on the position axis).
@@ -141,7 +145,11 @@ int gqa_decode_attention(void* out, const void* q, const void* k_cache, const vo
 /*
  * gqa_decode_attention with explicit launch choices, for tests and tuning.
  * path: GQA_PATH_AUTO / GQA_PATH_VECTOR / GQA_PATH_MATRIX (MATRIX on an
- *   unsupported shape gives GQA_ERR_UNSUPPORTED).
+ *   unsupported shape gives GQA_ERR_UNSUPPORTED), optionally OR-ed with
+ *   GQA_MERGE_INLINE or GQA_MERGE_KERNEL to fix how split segments are
+ *   merged (default: a second launch once a segment's partial states exceed
+ *   64 KiB, e.g. few long sequences with many heads per KV head). The second
+ *   launch goes to the same stream.
  * workgroups: size of the persistent grid that splits the work evenly;
  *   0 = automatic (compute units x resident workgroups per unit), otherwise
  *   1 .. 2048 (GQA_ERR_UNSUPPORTED outside that range).
@@ -183,8 +191,9 @@ int gqa_decode_step_ex(void* out, const void* q, const void* k_new, const void* 
 /*
  * Describe the launch gqa_decode_attention_ex would make on the current
  * device, without enqueueing anything: writes the chosen path
- * (GQA_PATH_VECTOR or GQA_PATH_MATRIX) and persistent grid size. Same
- * argument checks as the real call, minus pointers.
+ * (GQA_PATH_VECTOR or GQA_PATH_MATRIX, OR-ed with the GQA_MERGE_* flag in
+ * effect) and persistent grid size. Same argument checks as the real call,
+ * minus pointers.
  */
 int gqa_decode_plan(int b, int h, int g, int d_k, int d_v, int cap, int max_len, int dtype,
                     int path, int workgroups, int* chosen_path, int* chosen_workgroups);

@@ -137,15 +137,25 @@ def test_plan_choices(lib):
         rc = lib.gqa_decode_plan(b, h, g, d, d, cap, max_len, dtype, path, wgs, ctypes.byref(p), ctypes.byref(c))
         assert rc == _lib.OK, lib.gqa_last_error()
         return p.value, c.value
-    assert plan(16, 64, 8, 128, 8256, 8193, _lib.BF16)[0] == _lib.PATH_MATRIX
-    assert plan(8, 32, 1, 128, 4160, 4097, _lib.BF16)[0] == _lib.PATH_MATRIX
-    assert plan(4, 32, 32, 128, 32832, 32769, _lib.BF16)[0] == _lib.PATH_VECTOR  # one head per KV head
-    assert plan(2, 4, 2, 16, 128, 65, _lib.F32)[0] == _lib.PATH_VECTOR
+    M = _lib.MERGE_INLINE | _lib.MERGE_KERNEL
+    assert plan(16, 64, 8, 128, 8256, 8193, _lib.BF16)[0] == _lib.PATH_MATRIX | _lib.MERGE_INLINE
+    # few long segments with 32 heads per KV head: merged by a second launch
+    assert plan(8, 32, 1, 128, 4160, 4097, _lib.BF16)[0] == _lib.PATH_MATRIX | _lib.MERGE_KERNEL
+    assert plan(4, 32, 1, 128, 32832, 32769, _lib.BF16)[0] == _lib.PATH_MATRIX | _lib.MERGE_KERNEL
+    assert plan(4, 32, 32, 128, 32832, 32769, _lib.BF16)[0] & ~M == _lib.PATH_VECTOR  # one head per KV head
+    assert plan(2, 4, 2, 16, 128, 65, _lib.F32)[0] & ~M == _lib.PATH_VECTOR
     for args in [(16, 64, 8, 128, 8256, 8193, _lib.BF16), (2, 4, 2, 16, 128, 65, _lib.F32),
                  (64, 28, 4, 128, 2112, 2080, _lib.BF16)]:
         _, c = plan(*args)
         assert 1 <= c <= 2048
-    assert plan(16, 64, 8, 128, 8256, 8193, _lib.BF16, path=_lib.PATH_VECTOR, wgs=77) == (_lib.PATH_VECTOR, 77)
+    assert plan(16, 64, 8, 128, 8256, 8193, _lib.BF16, path=_lib.PATH_VECTOR, wgs=77)[1] == 77
+    # forced merge modes are kept; both flags at once are rejected
+    for flag in (_lib.MERGE_INLINE, _lib.MERGE_KERNEL):
+        assert plan(8, 32, 1, 128, 4160, 4097, _lib.BF16, path=_lib.PATH_MATRIX | flag)[0] == _lib.PATH_MATRIX | flag
+        assert plan(2, 4, 2, 16, 128, 65, _lib.F32, path=flag)[0] == _lib.PATH_VECTOR | flag
+    p, c = ctypes.c_int(), ctypes.c_int()
+    assert lib.gqa_decode_plan(8, 32, 1, 128, 128, 4160, 4097, _lib.BF16, M, 0, ctypes.byref(p),
+                               ctypes.byref(c)) == _lib.ERR_UNSUPPORTED
 
 
 def test_step_rejects(lib):

@@ -86,13 +86,24 @@ def llama(oracle_mod):
     return pb, q, pb.oracle_attention(q)
 
 
+@pytest.mark.parametrize("merge", [api.MERGE_INLINE, api.MERGE_KERNEL])
 @pytest.mark.parametrize("path,wgs", [(api.PATH_MATRIX, 1), (api.PATH_MATRIX, 7), (api.PATH_MATRIX, 128),
                                       (api.PATH_MATRIX, 2048), (api.PATH_VECTOR, 0), (api.PATH_VECTOR, 5),
                                       (api.PATH_VECTOR, 1000)])
-def test_paths_and_grid_sizes(gpu_lib, llama, path, wgs):
+def test_paths_and_grid_sizes(gpu_lib, llama, path, wgs, merge):
     pb, q, ref = llama
-    out, _ = pb.gpu_attention(q, path=path, wgs=wgs)
-    assert_parity(out, ref, pb.dtype, f"path={path} workgroups={wgs}")
+    out, ws = pb.gpu_attention(q, path=path | merge, wgs=wgs)
+    assert_parity(out, ref, pb.dtype, f"path={path} workgroups={wgs} merge={merge:#x}")
+    assert_counters_zero(ws, pb.b, pb.h)
+
+
+def test_merge_modes_agree_and_are_deterministic(gpu_lib, llama):
+    pb, q, _ = llama
+    a, _ = pb.gpu_attention(q, path=api.PATH_MATRIX | api.MERGE_KERNEL, wgs=2048)
+    b, _ = pb.gpu_attention(q, path=api.PATH_MATRIX | api.MERGE_KERNEL, wgs=2048)
+    c, _ = pb.gpu_attention(q, path=api.PATH_MATRIX | api.MERGE_INLINE, wgs=2048)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    assert (a.float() - c.float()).abs().max().item() <= 2e-2
 
 
 def test_deterministic(gpu_lib, llama):
@@ -153,13 +164,14 @@ def test_edge_shapes(gpu_lib, oracle_mod, b, h, g, d, cap, lens, dtype):
     paths = [api.PATH_AUTO, api.PATH_VECTOR]
     if dtype == "bf16" and d == 128 and h // g <= 64:
         paths.append(api.PATH_MATRIX)
-    for path in paths:
-        for wgs in (0, 1, 3, 64):
-            out, _ = pb.gpu_attention(q, path=path, wgs=wgs)
-            assert_parity(out, ref, dtype, f"path={path} workgroups={wgs}")
-            for s in range(b):
-                if pb.lens_h[s] == 0:
-                    assert torch.count_nonzero(out[s].float()) == 0
+    runs = [(path, wgs) for path in paths for wgs in (0, 1, 3, 64)]
+    runs += [(path | api.MERGE_KERNEL, wgs) for path in paths for wgs in (0, 3, 64)]
+    for path, wgs in runs:
+        out, _ = pb.gpu_attention(q, path=path, wgs=wgs)
+        assert_parity(out, ref, dtype, f"path={path:#x} workgroups={wgs}")
+        for s in range(b):
+            if pb.lens_h[s] == 0:
+                assert torch.count_nonzero(out[s].float()) == 0
 
 
 def test_max_len_clamps_lengths(gpu_lib, oracle_mod):

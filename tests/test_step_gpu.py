@@ -69,7 +69,11 @@ def test_step_workloads(gpu_lib, oracle_mod, name):
 
 
 @pytest.mark.parametrize("path,wgs", [(api.PATH_MATRIX, 0), (api.PATH_MATRIX, 1), (api.PATH_MATRIX, 37),
-                                      (api.PATH_MATRIX, 2048), (api.PATH_VECTOR, 0), (api.PATH_VECTOR, 3)])
+                                      (api.PATH_MATRIX, 2048), (api.PATH_VECTOR, 0), (api.PATH_VECTOR, 3),
+                                      (api.PATH_MATRIX | api.MERGE_KERNEL, 37),
+                                      (api.PATH_MATRIX | api.MERGE_KERNEL, 2048),
+                                      (api.PATH_VECTOR | api.MERGE_KERNEL, 3),
+                                      (api.PATH_MATRIX | api.MERGE_INLINE, 2048)])
 def test_step_paths_and_grids(gpu_lib, oracle_mod, path, wgs):
     pb = StepProblem(oracle_mod, seed=301, b=5, h=16, g=2, d=128, cap=700, lens=[0, 31, 32, 500, 698],
                      dtype="bf16")
