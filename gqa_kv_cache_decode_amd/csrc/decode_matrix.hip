@@ -32,7 +32,7 @@
 // K and V are streamed once with nontemporal loads (they are not reused, and
 // keeping them out of the caches measurably raises HBM read bandwidth).
 // Workgroups follow the persistent schedule of gqa_internal.hpp; inside a
-// piece each wave walks every fourth tile with an online softmax (base 2,
+// piece each wave walks every WAVES-th tile with an online softmax (base 2,
 // running max per head shared by the 4 lanes of a head), and the waves are
 // merged through LDS before the piece is published.
 //
@@ -50,6 +50,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int D = 128;
 constexpr int OPAD = 4;  // LDS row padding (floats) against bank conflicts
+constexpr int kMatrixWaves1 = 8;  // waves per workgroup of the one-head-block kernel
 
 __device__ __forceinline__ u32x4 load16(const uint16_t* ptr) {
   return *reinterpret_cast<const u32x4*>(ptr);
@@ -181,11 +182,18 @@ __device__ __forceinline__ void tile_step(WaveState<NB>& st, const bf16x8 (&qop)
 #undef GQA_PV_STEP
 }
 
-template <int NB, bool FUSED>
-__global__ __launch_bounds__(kThreads, NB == 1 ? 2 : 1) void decode_matrix_kernel(DecodeParams p) {
-  __shared__ float sm_m[kWaves][16];
-  __shared__ float sm_l[kWaves][16];
-  __shared__ float sm_o[kWaves][16][D + OPAD];
+// WAVES = 8 (one head block): one 512-thread workgroup per compute unit. Two
+// 4-wave workgroups per unit were measured slower: the one dispatched second
+// streams about a tenth slower than its partner (older waves win the issue
+// arbitration) and the unit's work ends with it, while the eight waves of one
+// workgroup share each piece and meet at its barriers. WAVES = 4: the larger
+// head blocks, whose register needs allow one 4-wave workgroup per unit.
+template <int NB, bool FUSED, int WAVES>
+__global__ __launch_bounds__(WAVES * 64, (NB == 1 && WAVES == 4) ? 2 : 1) void decode_matrix_kernel(DecodeParams p) {
+  constexpr int THREADS = WAVES * 64;
+  __shared__ float sm_m[WAVES][16];
+  __shared__ float sm_l[WAVES][16];
+  __shared__ float sm_o[WAVES][16][D + OPAD];
   __shared__ float fin_m[NB * 16];
   __shared__ float fin_l[NB * 16];
   __shared__ __attribute__((aligned(16))) float fin_o[NB * 16][D];
@@ -237,7 +245,7 @@ __global__ __launch_bounds__(kThreads, NB == 1 ? 2 : 1) void decode_matrix_kerne
     const uint16_t* vbase = static_cast<const uint16_t*>(p.v_cache) + kv_head * p.cap * D;
     const int t_end = min(pc.L, pc.tile_end * kTile);
     const int pos_new = FUSED ? pc.L - 1 : -1;  // the appended token (fused step)
-    for (int tile = pc.tile_begin + w; tile < pc.tile_end; tile += kWaves) {
+    for (int tile = pc.tile_begin + w; tile < pc.tile_end; tile += WAVES) {
       const int t0 = tile * kTile;
       const int nvalid = t_end - t0;
       if (FUSED && pos_new >= t0 && pos_new < t0 + kTile) {
@@ -257,7 +265,7 @@ __global__ __launch_bounds__(kThreads, NB == 1 ? 2 : 1) void decode_matrix_kerne
       dfr.take_if_due(p, w);
     }
 
-    // merge the four waves through LDS, one 16-head block at a time
+    // merge the waves through LDS, one 16-head block at a time
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       float lsum = st.lrun[nb];
@@ -273,15 +281,15 @@ __global__ __launch_bounds__(kThreads, NB == 1 ? 2 : 1) void decode_matrix_kerne
       }
       __syncthreads();
       const int nh_blk = min(16, G - nb * 16);
-      for (int idx = threadIdx.x; idx < nh_blk * D; idx += kThreads) {
+      for (int idx = threadIdx.x; idx < nh_blk * D; idx += THREADS) {
         const int hh = idx / D, dd = idx - hh * D;
         float M = sm_m[0][hh];
 #pragma unroll
-        for (int ww = 1; ww < kWaves; ++ww) M = fmaxf(M, sm_m[ww][hh]);
+        for (int ww = 1; ww < WAVES; ++ww) M = fmaxf(M, sm_m[ww][hh]);
         const float sub = (M == kNegInf) ? 0.0f : M;
         float o = 0.0f, ls = 0.0f;
 #pragma unroll
-        for (int ww = 0; ww < kWaves; ++ww) {
+        for (int ww = 0; ww < WAVES; ++ww) {
           const float wgt = fast_exp2(sm_m[ww][hh] - sub);
           o = fmaf(wgt, sm_o[ww][hh][dd], o);
           ls = fmaf(wgt, sm_l[ww][hh], ls);
@@ -294,10 +302,10 @@ __global__ __launch_bounds__(kThreads, NB == 1 ? 2 : 1) void decode_matrix_kerne
       }
       __syncthreads();
     }
-    finish_piece<uint16_t, NB * 2>(p, pc, walker.more(), wg, i0, G, fin_m, fin_l, &fin_o[0][0], dfr, sm_merge,
-                                 &s_flag);
+    finish_piece<uint16_t, NB * 8 / WAVES>(p, pc, walker.more(), wg, i0, G, fin_m, fin_l, &fin_o[0][0], dfr,
+                                           sm_merge, &s_flag);
   }
-  dfr.resolve<uint16_t, NB * 2>(p, sm_merge, &s_flag);
+  dfr.resolve<uint16_t, NB * 8 / WAVES>(p, sm_merge, &s_flag);
   if (FUSED) finish_step(p, &s_flag);
 }
 
@@ -305,11 +313,11 @@ template <bool FUSED>
 void launch_nb(const DecodeParams& p, hipStream_t stream) {
   const dim3 grid(p.workgroups);
   if (p.G <= 16) {
-    hipLaunchKernelGGL((decode_matrix_kernel<1, FUSED>), grid, dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((decode_matrix_kernel<1, FUSED, kMatrixWaves1>), grid, dim3(kMatrixWaves1 * 64), 0, stream, p);
   } else if (p.G <= 32) {
-    hipLaunchKernelGGL((decode_matrix_kernel<2, FUSED>), grid, dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((decode_matrix_kernel<2, FUSED, 4>), grid, dim3(256), 0, stream, p);
   } else {
-    hipLaunchKernelGGL((decode_matrix_kernel<4, FUSED>), grid, dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((decode_matrix_kernel<4, FUSED, 4>), grid, dim3(256), 0, stream, p);
   }
 }
 
@@ -324,11 +332,15 @@ hipError_t launch_decode_matrix(const DecodeParams& p, hipStream_t stream) {
 namespace {
 template <bool FUSED>
 hipError_t occupancy(int k, int* n) {
-  if (k == 0) return hipOccupancyMaxActiveBlocksPerMultiprocessor(n, decode_matrix_kernel<1, FUSED>, kThreads, 0);
-  if (k == 1) return hipOccupancyMaxActiveBlocksPerMultiprocessor(n, decode_matrix_kernel<2, FUSED>, kThreads, 0);
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(n, decode_matrix_kernel<4, FUSED>, kThreads, 0);
+  if (k == 0)
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(n, decode_matrix_kernel<1, FUSED, kMatrixWaves1>,
+                                                        kMatrixWaves1 * 64, 0);
+  if (k == 1) return hipOccupancyMaxActiveBlocksPerMultiprocessor(n, decode_matrix_kernel<2, FUSED, 4>, 256, 0);
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(n, decode_matrix_kernel<4, FUSED, 4>, 256, 0);
 }
 }  // namespace
+
+int matrix_waves(int G) { return G <= 16 ? kMatrixWaves1 : 4; }
 
 int matrix_workgroups_per_cu(int G, bool fused) {
   static int cached[2][3] = {};

@@ -113,18 +113,20 @@ int plan_decode(int b, int h, int g, int d_k, int d_v, int cap, int max_len, int
     plan->gblk = gqa::vector_heads_per_block(G);
     plan->nhb = (G + plan->gblk - 1) / plan->gblk;
   }
+  const int waves = chosen == GQA_PATH_MATRIX ? gqa::matrix_waves(G) : gqa::kWaves;
   const int unit_len = gqa::kTile * gqa::kUnitTiles;
   const long long segments = (long long)b * g * plan->nhb;
   const long long units_bound = segments * ((max_len + unit_len - 1) / unit_len);  // lengths <= max_len
   const bool auto_grid = workgroups == 0;
   if (auto_grid) {
-    // Up to two 4-wave workgroups per compute unit (8 waves keep enough loads
-    // in flight), never more than fit at once, so the persistent grid runs in
-    // a single round.
+    // Up to eight waves per compute unit (two 4-wave workgroups or one
+    // 8-wave one keep enough loads in flight), never more than fit at once, so
+    // the persistent grid runs in a single round.
     int fit = chosen == GQA_PATH_MATRIX ? gqa::matrix_workgroups_per_cu(G, fused)
                                         : gqa::vector_workgroups_per_cu(dtype, d_k, plan->gblk, fused);
     if (fit <= 0) fit = 2;  // no device to ask: assume the common case
-    const int per_cu = fit < 2 ? fit : 2;
+    const int per_cu_max = 8 / waves;
+    const int per_cu = fit < per_cu_max ? fit : per_cu_max;
     long long n = (long long)device_cus() * per_cu;
     if (n > units_bound) n = units_bound;
     if (n < 1) n = 1;

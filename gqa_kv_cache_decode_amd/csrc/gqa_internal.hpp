@@ -3,8 +3,8 @@
 // Work schedule (both decode kernels)
 // -----------------------------------
 // The attention of one decode step is cut into units of four 32-position
-// tiles (one tile for each wave of a workgroup) of one "segment" (sequence
-// s, KV-head group grp); a segment's last unit may be short. Units are
+// tiles of one "segment" (sequence s, KV-head group grp); a segment's last
+// unit may be short. Units are
 // ordered (s, grp, unit). With T units in all and P' = min(P, T) of the P
 // persistent workgroups taking part, workgroup p < P' takes the contiguous
 // range [floor(p*T/P'), floor((p+1)*T/P')) (never empty), so every workgroup
@@ -50,10 +50,10 @@
 
 namespace gqa {
 
-constexpr int kThreads = 256;  // workgroup size of both decode kernels
+constexpr int kThreads = 256;  // workgroup size of the vector decode and merge kernels
 constexpr int kWaves = kThreads / 64;
 constexpr int kTile = 32;             // positions per wave step
-constexpr int kUnitTiles = 4;         // tiles per schedule unit: one for each wave of a workgroup
+constexpr int kUnitTiles = 4;         // tiles per schedule unit
 constexpr int kMaxWorkgroups = 2048;  // persistent grid bound (workspace sizing)
 constexpr int kMatrixMaxGroup = 64;   // query heads per KV head on the matrix path
 constexpr int kVectorMaxBlock = 8;    // query heads per workgroup on the vector path
@@ -138,6 +138,8 @@ hipError_t launch_merge_partials(const DecodeParams& p, int dtype, hipStream_t s
 // Workgroups of the decode kernel instance that fit on one compute unit at
 // once (runtime occupancy query, cached; 0 if the runtime cannot say).
 int matrix_workgroups_per_cu(int G, bool fused);
+// Waves per workgroup of the matrix kernel instance for G heads per KV head.
+int matrix_waves(int G);
 int vector_workgroups_per_cu(int dtype, int d, int heads_per_block, bool fused);
 
 // Vector-path head block for G query heads per KV head: the smallest power of
@@ -247,9 +249,12 @@ __device__ __forceinline__ int attended_len(const DecodeParams& p, int s) {
 }
 
 __device__ __forceinline__ int tiles_of(int L) { return (L + kTile - 1) / kTile; }
-// Schedule units of a segment of length L. A unit is kUnitTiles tiles, so a
-// piece made of whole units gives every wave of its workgroup the same number
-// of tiles (only a segment's last unit can be short).
+// Schedule units of a segment of length L. A unit is kUnitTiles tiles, one
+// for each wave of a 4-wave workgroup, so that a piece made of whole units
+// gives each of those waves the same number of tiles (only a segment's last
+// unit can be short). The 8-wave matrix workgroups keep 4-tile units: 8-tile
+// units, which would balance their waves the same way, measured slower (the
+// coarser split of the work over workgroups costs more).
 __device__ __forceinline__ int units_of(int L) { return (L + kTile * kUnitTiles - 1) / (kTile * kUnitTiles); }
 
 // Workgroup owning unit u when T units are split over P workgroups as
@@ -338,7 +343,7 @@ __device__ Located locate_units(const DecodeParams& p, const LensView& lv, int w
 
 // One piece of a workgroup's range: tiles [tile_begin, tile_end) of segment
 // (s, grp), i.e. positions [tile_begin*kTile, min(L, tile_end*kTile)).
-// tile_begin is a multiple of kUnitTiles. p0 and p1 are the first and last
+// tile_begin is a multiple of the unit size. p0 and p1 are the first and last
 // workgroups whose ranges touch the segment.
 struct Piece {
   int s, grp, L;
@@ -436,7 +441,7 @@ __device__ void write_piece_out(const DecodeParams& p, int s, int i0, int nh, co
   const int d = p.d;
   TOut* out = static_cast<TOut*>(p.out);
   const size_t out_row0 = (size_t(s) * p.h + i0) * d;
-  for (int idx = threadIdx.x; idx < nh * d; idx += kThreads) {
+  for (int idx = threadIdx.x; idx < nh * d; idx += int(blockDim.x)) {
     const float l = sm_l[idx / d];
     store_out(out, out_row0 + idx, l > 0.0f ? sm_o[idx] / l : 0.0f);
   }
@@ -474,6 +479,7 @@ template <typename TOut, int MAXC>
 __device__ void merge_segment(const DecodeParams& p, int s, int p0, int n_slots, int i0, int nh,
                               float* sm_merge) {
   const int tid = threadIdx.x;
+  const int nthr = blockDim.x;
   const int d = p.d;
   const __amdgpu_buffer_rsrc_t rs = slots_rsrc(p);
   const int slot_bytes = p.slot_floats * int(sizeof(float));
@@ -487,7 +493,7 @@ __device__ void merge_segment(const DecodeParams& p, int s, int p0, int n_slots,
   f32x4v acc[MAXC];
 #pragma unroll
   for (int c = 0; c < MAXC; ++c) acc[c] = f32x4v{0.0f, 0.0f, 0.0f, 0.0f};
-  for (int hh = tid; hh < nh; hh += kThreads) {
+  for (int hh = tid; hh < nh; hh += nthr) {
     run_m[hh] = kNegInf;
     run_den[hh] = 0.0f;
   }
@@ -500,11 +506,11 @@ __device__ void merge_segment(const DecodeParams& p, int s, int p0, int n_slots,
       const int sb = ((p0 + kk) * 2 + (kk == 0 ? 1 : 0)) * slot_bytes;
 #pragma unroll
       for (int c = 0; c < MAXC; ++c) {
-        const int c4 = tid + c * kThreads;
+        const int c4 = tid + c * nthr;
         o[k][c] = (k < kn && c4 < n4) ? coherent_load4(rs, sb + c4 * 16) : f32x4v{0.0f, 0.0f, 0.0f, 0.0f};
       }
     }
-    for (int pair = tid; pair < kn * nh; pair += kThreads) {
+    for (int pair = tid; pair < kn * nh; pair += nthr) {
       const int k = pair / nh, hh = pair - k * nh;
       const int kk = k0 + k;
       const int sb = ((p0 + kk) * 2 + (kk == 0 ? 1 : 0)) * slot_bytes + ml_off;
@@ -512,7 +518,7 @@ __device__ void merge_segment(const DecodeParams& p, int s, int p0, int n_slots,
       pl[pair] = coherent_load1(rs, sb + (p.gblk + hh) * 4);
     }
     __syncthreads();
-    for (int hh = tid; hh < nh; hh += kThreads) {
+    for (int hh = tid; hh < nh; hh += nthr) {
       float M = run_m[hh];
       for (int k = 0; k < kn; ++k) M = fmaxf(M, pm[k * nh + hh]);
       const float sub = (M == kNegInf) ? 0.0f : M;
@@ -530,7 +536,7 @@ __device__ void merge_segment(const DecodeParams& p, int s, int p0, int n_slots,
     __syncthreads();
 #pragma unroll
     for (int c = 0; c < MAXC; ++c) {
-      const int c4 = tid + c * kThreads;
+      const int c4 = tid + c * nthr;
       if (c4 < n4) {
         const int hh = (4 * c4) / d;
         f32x4v a = acc[c] * run_r[hh];
@@ -546,7 +552,7 @@ __device__ void merge_segment(const DecodeParams& p, int s, int p0, int n_slots,
   const size_t out_row0 = (size_t(s) * p.h + i0) * d;
 #pragma unroll
   for (int c = 0; c < MAXC; ++c) {
-    const int c4 = tid + c * kThreads;
+    const int c4 = tid + c * nthr;
     if (c4 < n4) {
       const int hh = (4 * c4) / d;
       const float den = run_den[hh];
@@ -646,14 +652,14 @@ __device__ void finish_piece(const DecodeParams& p, const Piece& pc, bool more_f
   SharedPiece sh;
   sh.set(pc, i0, nh);
   if (p.merge_kernel) {  // merged by the next launch: store and go on
-    store_partial(p, sh, wg, sm_m, sm_l, sm_o, threadIdx.x, kThreads);
+    store_partial(p, sh, wg, sm_m, sm_l, sm_o, threadIdx.x, blockDim.x);
     return;
   }
   if (more_follow) {  // the first piece of the range (slot 0)
     dfr.stored(p, sh, wg, sm_m, sm_l, sm_o);
     return;
   }
-  store_partial(p, sh, wg, sm_m, sm_l, sm_o, threadIdx.x, kThreads);
+  store_partial(p, sh, wg, sm_m, sm_l, sm_o, threadIdx.x, blockDim.x);
   settle_shared<TOut, MAXC>(p, sh, sm_merge, sm_flag);
 }
 
@@ -666,7 +672,7 @@ __device__ void finish_step(const DecodeParams& p, int* sm_flag) {
     *sm_flag = __hip_atomic_fetch_add(p.ws_done, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
   if (*sm_flag != int(gridDim.x) - 1) return;
-  for (int s = threadIdx.x; s < p.b; s += kThreads) p.lens[s] = attended_len(p, s);
+  for (int s = threadIdx.x; s < p.b; s += int(blockDim.x)) p.lens[s] = attended_len(p, s);
   if (threadIdx.x == 0) __hip_atomic_store(p.ws_done, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
@@ -678,9 +684,9 @@ __device__ void zero_empty_sequences(const DecodeParams& p, int wg) {
   for (int s = wg; s < p.b; s += p.workgroups) {
     if (attended_len(p, s) != 0) continue;
     if (p.merge_kernel)
-      for (int k = threadIdx.x; k < p.ngroups; k += kThreads) p.seg_info[size_t(s) * p.ngroups + k] = make_int2(0, -1);
+      for (int k = threadIdx.x; k < p.ngroups; k += int(blockDim.x)) p.seg_info[size_t(s) * p.ngroups + k] = make_int2(0, -1);
     const size_t row0 = size_t(s) * p.h * p.d;
-    for (int idx = threadIdx.x; idx < p.h * p.d; idx += kThreads) out[row0 + idx] = TOut(0);
+    for (int idx = threadIdx.x; idx < p.h * p.d; idx += int(blockDim.x)) out[row0 + idx] = TOut(0);
   }
 }
 
