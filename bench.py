@@ -253,6 +253,7 @@ def main():
             "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
             "kernel": ("decode_matrix_kernel" if plan_path == 2 else "decode_vector_kernel")
+                      + (" + merge_partials_kernel" if plan_merge == api.MERGE_KERNEL else "")
                       + ("" if args.unfused else " (fused step)"),
             "kernel_avg_us": round(kern_avg_ms * 1e3, 3),
         },
