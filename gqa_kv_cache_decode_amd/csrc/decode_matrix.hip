@@ -211,7 +211,7 @@ __global__ __launch_bounds__(WAVES * 64, (NB == 1 && WAVES == 4) ? 2 : 1) void d
 
   zero_empty_sequences<uint16_t>(p, wg);
 
-  PieceWalker walker;
+  PieceWalker<WAVES == 8> walker;
   walker.init(p, wg);
   Piece pc;
   DeferredPiece dfr;

@@ -169,7 +169,7 @@ __global__ __launch_bounds__(kThreads) void decode_vector_kernel(DecodeParams p)
 
   zero_empty_sequences<T>(p, wg);
 
-  PieceWalker walker;
+  PieceWalker<false> walker;
   walker.init(p, wg);
   Piece pc;
   DeferredPiece dfr;

@@ -34,6 +34,7 @@ constexpr int kMaxHeads = 4096;
 constexpr int kMaxLen = 1 << 28;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kDefaultCUs = 256;  // MI355X, used when no device can be queried
+constexpr int kSegmentLead = 2;   // empty schedule units ahead of each segment
 
 bool supported_head_dim(int d) { return d == 16 || d == 32 || d == 64 || d == 128 || d == 256; }
 
@@ -116,7 +117,8 @@ int plan_decode(int b, int h, int g, int d_k, int d_v, int cap, int max_len, int
   const int waves = chosen == GQA_PATH_MATRIX ? gqa::matrix_waves(G) : gqa::kWaves;
   const int unit_len = gqa::kTile * gqa::kUnitTiles;
   const long long segments = (long long)b * g * plan->nhb;
-  const long long units_bound = segments * ((max_len + unit_len - 1) / unit_len);  // lengths <= max_len
+  // lengths <= max_len; kSegmentLead: empty units ahead of each segment (at most)
+  const long long units_bound = segments * ((max_len + unit_len - 1) / unit_len + kSegmentLead);
   const bool auto_grid = workgroups == 0;
   if (auto_grid) {
     // Up to eight waves per compute unit (two 4-wave workgroups or one
@@ -249,6 +251,10 @@ int decode_common(const char* fn, void* out, const void* q, void* k_cache, void*
   p.ngroups = g * plan.nhb;
   p.slot_floats = gqa::slot_floats_for(plan.gblk, d_v);
   p.workgroups = plan.workgroups;
+  // The lead units pay off where ranges are long and pieces few per
+  // workgroup (the one-head-block matrix kernel); elsewhere they were
+  // measured neutral or slower.
+  p.seg_lead = (plan.path == GQA_PATH_MATRIX && gqa::matrix_waves(p.G) == 8) ? kSegmentLead : 0;
   p.scale_log2 = scale * kLog2e;
 
   const hipStream_t st = static_cast<hipStream_t>(stream);

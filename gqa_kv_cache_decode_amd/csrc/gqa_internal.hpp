@@ -86,6 +86,7 @@ struct DecodeParams {
   int ngroups;      // segments per sequence: g * nhb
   int slot_floats;  // gblk * d + round_up(2 * gblk, 4)
   int workgroups;   // persistent grid size P
+  int seg_lead;     // empty schedule units ahead of each segment (piece start-up cost)
   int cnt_stride;   // ints between consecutive tickets
   int merge_kernel; // 1: shared segments are merged by merge_partials_kernel after this launch
   int2* seg_info;   // merge_kernel: per segment (p0, p1) of its shared pieces, p1 = -1 if none
@@ -257,6 +258,19 @@ __device__ __forceinline__ int tiles_of(int L) { return (L + kTile - 1) / kTile;
 // coarser split of the work over workgroups costs more).
 __device__ __forceinline__ int units_of(int L) { return (L + kTile * kUnitTiles - 1) / (kTile * kUnitTiles); }
 
+// Units a non-empty segment occupies in the schedule: its units_of(L) real
+// units preceded by p.seg_lead empty ones. The empty units carry no work;
+// they stand for the cost of starting a piece (query load, wave merge,
+// partial store and ticket), so that a workgroup whose range starts a new
+// segment gets correspondingly fewer real units.
+// LEAD = false: kernels launched with seg_lead = 0 compile the plain form.
+template <bool LEAD>
+__device__ __forceinline__ int sched_units_of(const DecodeParams& p, int L) {
+  const int nu = units_of(L);
+  if constexpr (!LEAD) return nu;
+  return nu > 0 ? nu + p.seg_lead : 0;
+}
+
 // Workgroup owning unit u when T units are split over P workgroups as
 // [floor(p*T/P), floor((p+1)*T/P)): the largest p with floor(p*T/P) <= u.
 __device__ __forceinline__ int owner_of(long long u, long long T, int P) {
@@ -309,10 +323,11 @@ struct Located {
   int s;
   int parts;
 };
+template <bool LEAD>
 __device__ Located locate_units(const DecodeParams& p, const LensView& lv, int workgroup) {
   long long carry = 0;
   for (int base = 0; base < p.b; base += 64) {  // total units
-    const long long v = (long long)p.ngroups * units_of(lv.lane_len(base));
+    const long long v = (long long)p.ngroups * sched_units_of<LEAD>(p, lv.lane_len(base));
     const long long incl = wave_inclusive_scan(v);
     carry += __shfl(incl, 63, 64);
   }
@@ -326,7 +341,7 @@ __device__ Located locate_units(const DecodeParams& p, const LensView& lv, int w
   carry = 0;
   for (int base = 0; base < p.b; base += 64) {
     const int s = base + (threadIdx.x & 63);
-    const long long v = (long long)p.ngroups * units_of(lv.lane_len(base));
+    const long long v = (long long)p.ngroups * sched_units_of<LEAD>(p, lv.lane_len(base));
     const long long incl = wave_inclusive_scan(v) + carry;
     const long long excl = incl - v;
     const unsigned long long hit = __ballot(s < p.b && v > 0 && excl <= u0 && u0 < incl);
@@ -351,7 +366,9 @@ struct Piece {
   int p0, p1;
 };
 
-// Iterates the pieces of workgroup `wg`'s unit range.
+// Iterates the pieces of workgroup `wg`'s unit range. LEAD: segments are
+// preceded by p.seg_lead empty units.
+template <bool LEAD>
 struct PieceWalker {
   const DecodeParams* p;
   LensView lv;
@@ -361,7 +378,7 @@ struct PieceWalker {
   __device__ void init(const DecodeParams& prm, int wg) {
     p = &prm;
     lv.init(prm);
-    const Located loc = locate_units(prm, lv, wg);
+    const Located loc = locate_units<LEAD>(prm, lv, wg);
     total = loc.total;
     parts = loc.parts;
     s = loc.s;
@@ -376,7 +393,8 @@ struct PieceWalker {
 
   __device__ bool more() const { return u < u_end; }
 
-  __device__ bool next(Piece& pc) {
+  // next() when segments have no leading empty units.
+  __device__ bool next_packed(Piece& pc) {
     if (u >= u_end) return false;
     int L = lv.len(s);
     long long seq_units = (long long)p->ngroups * units_of(L);
@@ -403,6 +421,44 @@ struct PieceWalker {
     pc.p1 = owner_of(seg_u0 + nu - 1, total, parts);
     u += ue - ub;
     return true;
+  }
+
+  __device__ bool next(Piece& pc) {
+    if constexpr (!LEAD) return next_packed(pc);
+    const int lead = p->seg_lead;
+    while (u < u_end) {
+      int L = lv.len(s);
+      long long seq_units = (long long)p->ngroups * sched_units_of<true>(*p, L);
+      while (u >= seq_base + seq_units && s + 1 < p->b) {  // skip to the sequence holding u
+        seq_base += seq_units;
+        ++s;
+        L = lv.len(s);
+        seq_units = (long long)p->ngroups * sched_units_of<true>(*p, L);
+      }
+      const int nu = units_of(L);
+      const int sl = nu + lead;
+      const long long within = u - seq_base;
+      const int grp = int(within / sl);
+      const int ub = int(within - (long long)grp * sl);
+      const long long remain = u_end - u;
+      const long long seg_left = sl - ub;
+      const int ue = ub + int(remain < seg_left ? remain : seg_left);
+      u += ue - ub;
+      const int rb = (ub > lead ? ub : lead) - lead;  // real units [rb, re) of the segment
+      const int re = ue - lead;
+      if (re <= rb) continue;  // only the segment's leading empty units
+      const int nt = tiles_of(L);
+      pc.s = s;
+      pc.L = L;
+      pc.grp = grp;
+      pc.tile_begin = rb * kUnitTiles;
+      pc.tile_end = re * kUnitTiles < nt ? re * kUnitTiles : nt;
+      const long long seg_u0 = seq_base + (long long)grp * sl + lead;  // first real unit
+      pc.p0 = owner_of(seg_u0, total, parts);
+      pc.p1 = owner_of(seg_u0 + nu - 1, total, parts);
+      return true;
+    }
+    return false;
   }
 };
 
