@@ -193,7 +193,7 @@ __global__ __launch_bounds__(WAVES * 64, (NB == 1 && WAVES == 4) ? 2 : 1) void d
   constexpr int THREADS = WAVES * 64;
   __shared__ float sm_m[WAVES][16];
   __shared__ float sm_l[WAVES][16];
-  __shared__ float sm_o[WAVES][16][D + OPAD];
+  __shared__ __attribute__((aligned(16))) float sm_o[WAVES][16][D + OPAD];
   __shared__ float fin_m[NB * 16];
   __shared__ float fin_l[NB * 16];
   __shared__ __attribute__((aligned(16))) float fin_o[NB * 16][D];
@@ -272,30 +272,43 @@ __global__ __launch_bounds__(WAVES * 64, (NB == 1 && WAVES == 4) ? 2 : 1) void d
       lsum += xor_shuffle(lsum, 16);
       lsum += xor_shuffle(lsum, 32);
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
+      for (int i = 0; i < 4; ++i) {  // dims 32*q4 + 8*i + e, e = 0..7
+        f32x4 lo, hi;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sm_o[w][n16][32 * q4 + 8 * i + e] = st.oacc[nb][e][i];
+        for (int e = 0; e < 4; ++e) {
+          lo[e] = st.oacc[nb][e][i];
+          hi[e] = st.oacc[nb][e + 4][i];
+        }
+        *reinterpret_cast<f32x4*>(&sm_o[w][n16][32 * q4 + 8 * i]) = lo;
+        *reinterpret_cast<f32x4*>(&sm_o[w][n16][32 * q4 + 8 * i + 4]) = hi;
+      }
       if (q4 == 0) {
         sm_m[w][n16] = st.mrun[nb];
         sm_l[w][n16] = lsum;
       }
       __syncthreads();
       const int nh_blk = min(16, G - nb * 16);
-      for (int idx = threadIdx.x; idx < nh_blk * D; idx += THREADS) {
-        const int hh = idx / D, dd = idx - hh * D;
+      // one 16-byte column of one head per thread: the head's weights are
+      // computed once for its four outputs
+      constexpr int C4 = D / 4;
+      for (int idx = threadIdx.x; idx < nh_blk * C4; idx += THREADS) {
+        const int hh = idx / C4, c4 = idx - hh * C4;
         float M = sm_m[0][hh];
 #pragma unroll
         for (int ww = 1; ww < WAVES; ++ww) M = fmaxf(M, sm_m[ww][hh]);
         const float sub = (M == kNegInf) ? 0.0f : M;
-        float o = 0.0f, ls = 0.0f;
+        f32x4 o = {0.0f, 0.0f, 0.0f, 0.0f};
+        float ls = 0.0f;
 #pragma unroll
         for (int ww = 0; ww < WAVES; ++ww) {
           const float wgt = fast_exp2(sm_m[ww][hh] - sub);
-          o = fmaf(wgt, sm_o[ww][hh][dd], o);
+          const f32x4 ov = *reinterpret_cast<const f32x4*>(&sm_o[ww][hh][4 * c4]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[e] = fmaf(wgt, ov[e], o[e]);
           ls = fmaf(wgt, sm_l[ww][hh], ls);
         }
-        fin_o[nb * 16 + hh][dd] = o;
-        if (dd == 0) {
+        *reinterpret_cast<f32x4*>(&fin_o[nb * 16 + hh][4 * c4]) = o;
+        if (c4 == 0) {
           fin_m[nb * 16 + hh] = M;
           fin_l[nb * 16 + hh] = ls;
         }
