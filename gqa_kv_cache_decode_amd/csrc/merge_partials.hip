@@ -9,9 +9,9 @@
 // unnormalised output), M = max_k m_k and
 //   out = sum_k 2^(m_k - M) o_k / sum_k 2^(m_k - M) l_k.
 //
-// Workgroup (segment, head): the 256 threads are split into 256 / (d/4)
+// Workgroup (segment, head): the 256 threads are split into K = 256 / (d/4)
 // groups; group r takes slots r, r + K, ... and thread c of a group one
-// 16-byte column of the head's output row; the groups are summed in LDS.
+// 16-byte column of the head's output row; the groups are combined in LDS.
 #include "gqa_internal.hpp"
 
 namespace gqa {
@@ -19,7 +19,7 @@ namespace {
 
 template <typename TOut>
 __global__ __launch_bounds__(kThreads) void merge_partials_kernel(DecodeParams p) {
-  __shared__ float sm_red[kThreads / 64];
+  __shared__ float sm_max[kThreads];
   __shared__ __attribute__((aligned(16))) float sm_acc[kThreads * 4];
   __shared__ float sm_den[kThreads];
 
@@ -48,61 +48,58 @@ __global__ __launch_bounds__(kThreads) void merge_partials_kernel(DecodeParams p
   const int o_off = (hh * d + 4 * c) * int(sizeof(float));
   auto slot_base = [&](int k) { return ((p0 + k) * 2 + (k == 0 ? 1 : 0)) * slot_bytes; };
 
-  // M = max over the slots of this head's running max
-  float mx = kNegInf;
-  for (int k = tid; k < n; k += kThreads) mx = fmaxf(mx, coherent_load1(rs, slot_base(k) + m_off));
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, xor_shuffle(mx, off));
-  if ((tid & 63) == 0) sm_red[tid >> 6] = mx;
-  __syncthreads();
-  float M = sm_red[0];
-#pragma unroll
-  for (int w = 1; w < kThreads / 64; ++w) M = fmaxf(M, sm_red[w]);
-  const float sub = (M == kNegInf) ? 0.0f : M;
-
+  // Each group keeps its own running max over the slots it reads, four slots
+  // in flight at a time, so the slots are read in one pass; the groups are
+  // combined by their maxima at the end.
   f32x4v acc = {0.0f, 0.0f, 0.0f, 0.0f};
   float den = 0.0f;
-  if (r < groups) {
-    int k = r;
-    for (; k + 3 * groups < n; k += 4 * groups) {  // four slots in flight
-      float mk[4], lk[4];
-      f32x4v ok[4];
+  float mrun = kNegInf;
+  auto absorb = [&](float mk, float lk, f32x4v ok) {
+    const float mn = fmaxf(mrun, mk);
+    const float sub = (mn == kNegInf) ? 0.0f : mn;
+    const float a = fast_exp2(mrun - sub), wgt = fast_exp2(mk - sub);
+    den = fmaf(wgt, lk, den * a);
+    acc = acc * a + wgt * ok;
+    mrun = mn;
+  };
+  int k = r;
+  for (; k + 3 * groups < n; k += 4 * groups) {
+    float mk[4], lk[4];
+    f32x4v ok[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int base = slot_base(k + u * groups);
-        mk[u] = coherent_load1(rs, base + m_off);
-        lk[u] = coherent_load1(rs, base + l_off);
-        ok[u] = coherent_load4(rs, base + o_off);
-      }
+    for (int u = 0; u < 4; ++u) {
+      const int base = slot_base(k + u * groups);
+      mk[u] = coherent_load1(rs, base + m_off);
+      lk[u] = coherent_load1(rs, base + l_off);
+      ok[u] = coherent_load4(rs, base + o_off);
+    }
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const float wgt = fast_exp2(mk[u] - sub);
-        den = fmaf(wgt, lk[u], den);
-        acc += wgt * ok[u];
-      }
-    }
-    for (; k < n; k += groups) {
-      const int base = slot_base(k);
-      const float wgt = fast_exp2(coherent_load1(rs, base + m_off) - sub);
-      den = fmaf(wgt, coherent_load1(rs, base + l_off), den);
-      acc += wgt * coherent_load4(rs, base + o_off);
-    }
+    for (int u = 0; u < 4; ++u) absorb(mk[u], lk[u], ok[u]);
+  }
+  for (; k < n; k += groups) {
+    const int base = slot_base(k);
+    absorb(coherent_load1(rs, base + m_off), coherent_load1(rs, base + l_off), coherent_load4(rs, base + o_off));
   }
   *reinterpret_cast<f32x4v*>(&sm_acc[4 * tid]) = acc;
   sm_den[tid] = den;
+  if (c == 0) sm_max[r] = mrun;
   __syncthreads();
   if (tid < d4) {
-    f32x4v a = *reinterpret_cast<const f32x4v*>(&sm_acc[4 * tid]);
-    float dsum = sm_den[tid];
-    for (int rr = 1; rr < groups; ++rr) {
-      a += *reinterpret_cast<const f32x4v*>(&sm_acc[4 * (rr * d4 + tid)]);
-      dsum += sm_den[rr * d4 + tid];
+    float M = sm_max[0];
+    for (int rr = 1; rr < groups; ++rr) M = fmaxf(M, sm_max[rr]);
+    const float sub = (M == kNegInf) ? 0.0f : M;
+    f32x4v o = {0.0f, 0.0f, 0.0f, 0.0f};
+    float dsum = 0.0f;
+    for (int rr = 0; rr < groups; ++rr) {
+      const float wgt = fast_exp2(sm_max[rr] - sub);
+      o += wgt * *reinterpret_cast<const f32x4v*>(&sm_acc[4 * (rr * d4 + tid)]);
+      dsum = fmaf(wgt, sm_den[rr * d4 + tid], dsum);
     }
     const float inv = dsum > 0.0f ? 1.0f / dsum : 0.0f;
     TOut* out = static_cast<TOut*>(p.out);
     const size_t o0 = (size_t(s) * p.h + size_t(j) * p.G + hb * gblk + hh) * d + 4 * tid;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) store_out(out, o0 + e, a[e] * inv);
+    for (int e = 0; e < 4; ++e) store_out(out, o0 + e, o[e] * inv);
   }
 }
 
