@@ -146,14 +146,24 @@ __device__ __forceinline__ void tile_step(VState<T, D, HB>& st, const float (&qf
   }
 }
 
+// Waves per workgroup: eight (one workgroup per compute unit) when a head
+// block's accumulators are small enough for two waves per SIMD, else four.
+template <typename T, int D, int HB>
+constexpr int vector_waves_of() {
+  return (HB <= 4 && HB * D * int(sizeof(T)) <= 512) ? 8 : 4;
+}
+
 template <typename T, int D, int HB, bool FUSED>
-__global__ __launch_bounds__(kThreads) void decode_vector_kernel(DecodeParams p) {
+__global__ __launch_bounds__((vector_waves_of<T, D, HB>() * 64)) void decode_vector_kernel(DecodeParams p) {
+  constexpr int WAVES = vector_waves_of<T, D, HB>();
+  constexpr int THREADS = WAVES * 64;
+  constexpr int MAXC = (HB * D / 4 + THREADS - 1) / THREADS;
   using S = Shape<T, D, HB>;
   constexpr int VEC = S::VEC, R = S::R;
 
-  __shared__ float sm_m[kWaves][HB];
-  __shared__ float sm_l[kWaves][HB];
-  __shared__ float sm_o[kWaves][HB][D];
+  __shared__ float sm_m[WAVES][HB];
+  __shared__ float sm_l[WAVES][HB];
+  __shared__ float sm_o[WAVES][HB][D];
   __shared__ float fin_m[HB];
   __shared__ float fin_l[HB];
   __shared__ __attribute__((aligned(16))) float fin_o[HB][D];
@@ -209,7 +219,7 @@ __global__ __launch_bounds__(kThreads) void decode_vector_kernel(DecodeParams p)
     const T* vbase = static_cast<const T*>(p.v_cache) + kv_head * p.cap * D + col * VEC;
     const int t_end = min(pc.L, pc.tile_end * kTile);
     const int pos_new = FUSED ? pc.L - 1 : -1;  // the appended token (fused step)
-    for (int tile = pc.tile_begin + w; tile < pc.tile_end; tile += kWaves) {
+    for (int tile = pc.tile_begin + w; tile < pc.tile_end; tile += WAVES) {
       const int t0 = tile * kTile;
       const int nvalid = t_end - t0;
       if (FUSED && pos_new >= t0 && pos_new < t0 + kTile) {
@@ -259,15 +269,15 @@ __global__ __launch_bounds__(kThreads) void decode_vector_kernel(DecodeParams p)
       }
     }
     __syncthreads();
-    for (int idx = threadIdx.x; idx < HB * D; idx += kThreads) {
+    for (int idx = threadIdx.x; idx < HB * D; idx += THREADS) {
       const int hh = idx / D, dd = idx - hh * D;
       float M = sm_m[0][hh];
 #pragma unroll
-      for (int ww = 1; ww < kWaves; ++ww) M = fmaxf(M, sm_m[ww][hh]);
+      for (int ww = 1; ww < WAVES; ++ww) M = fmaxf(M, sm_m[ww][hh]);
       const float sub = (M == kNegInf) ? 0.0f : M;
       float o = 0.0f, lsum = 0.0f;
 #pragma unroll
-      for (int ww = 0; ww < kWaves; ++ww) {
+      for (int ww = 0; ww < WAVES; ++ww) {
         const float wgt = fast_exp2(sm_m[ww][hh] - sub);
         o = fmaf(wgt, sm_o[ww][hh][dd], o);
         lsum = fmaf(wgt, sm_l[ww][hh], lsum);
@@ -279,19 +289,21 @@ __global__ __launch_bounds__(kThreads) void decode_vector_kernel(DecodeParams p)
       }
     }
     __syncthreads();
-    finish_piece<T, (HB * D / 4 + kThreads - 1) / kThreads>(p, pc, walker.more(), wg, i0, nh, fin_m, fin_l, &fin_o[0][0], dfr, sm_merge,
+    finish_piece<T, MAXC>(p, pc, walker.more(), wg, i0, nh, fin_m, fin_l, &fin_o[0][0], dfr, sm_merge,
                                  &s_flag);
   }
-  dfr.resolve<T, (HB * D / 4 + kThreads - 1) / kThreads>(p, sm_merge, &s_flag);
+  dfr.resolve<T, MAXC>(p, sm_merge, &s_flag);
   if (FUSED) finish_step(p, &s_flag);
 }
 
 template <typename T, int D, int HB>
 hipError_t launch_one(const DecodeParams& p, hipStream_t stream) {
   if (p.fused)
-    hipLaunchKernelGGL((decode_vector_kernel<T, D, HB, true>), dim3(p.workgroups), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((decode_vector_kernel<T, D, HB, true>), dim3(p.workgroups),
+                       dim3(vector_waves_of<T, D, HB>() * 64), 0, stream, p);
   else
-    hipLaunchKernelGGL((decode_vector_kernel<T, D, HB, false>), dim3(p.workgroups), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((decode_vector_kernel<T, D, HB, false>), dim3(p.workgroups),
+                       dim3(vector_waves_of<T, D, HB>() * 64), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -323,10 +335,10 @@ int occupancy_d(int hb) {
   int n = 0;
   hipError_t e;
   switch (hb) {
-    case 1: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_vector_kernel<T, D, 1, FUSED>, kThreads, 0); break;
-    case 2: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_vector_kernel<T, D, 2, FUSED>, kThreads, 0); break;
-    case 4: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_vector_kernel<T, D, 4, FUSED>, kThreads, 0); break;
-    default: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_vector_kernel<T, D, 8, FUSED>, kThreads, 0); break;
+    case 1: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_vector_kernel<T, D, 1, FUSED>, vector_waves_of<T, D, 1>() * 64, 0); break;
+    case 2: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_vector_kernel<T, D, 2, FUSED>, vector_waves_of<T, D, 2>() * 64, 0); break;
+    case 4: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_vector_kernel<T, D, 4, FUSED>, vector_waves_of<T, D, 4>() * 64, 0); break;
+    default: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_vector_kernel<T, D, 8, FUSED>, vector_waves_of<T, D, 8>() * 64, 0); break;
   }
   if (e != hipSuccess || n <= 0) {
     (void)hipGetLastError();
@@ -347,6 +359,11 @@ int occupancy_t(int d, int hb) {
 }
 
 }  // namespace
+
+int vector_waves(int dtype, int d, int heads_per_block) {
+  const int esize = dtype == 0 ? 4 : 2;
+  return (heads_per_block <= 4 && heads_per_block * d * esize <= 512) ? 8 : 4;
+}
 
 int vector_workgroups_per_cu(int dtype, int d, int heads_per_block, bool fused) {
   static int cached[2][2][5][4] = {};

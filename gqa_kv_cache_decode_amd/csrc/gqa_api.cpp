@@ -114,7 +114,7 @@ int plan_decode(int b, int h, int g, int d_k, int d_v, int cap, int max_len, int
     plan->gblk = gqa::vector_heads_per_block(G);
     plan->nhb = (G + plan->gblk - 1) / plan->gblk;
   }
-  const int waves = chosen == GQA_PATH_MATRIX ? gqa::matrix_waves(G) : gqa::kWaves;
+  const int waves = chosen == GQA_PATH_MATRIX ? gqa::matrix_waves(G) : gqa::vector_waves(dtype, d_k, plan->gblk);
   const int unit_len = gqa::kTile * gqa::kUnitTiles;
   const long long segments = (long long)b * g * plan->nhb;
   // lengths <= max_len; kSegmentLead: empty units ahead of each segment (at most)

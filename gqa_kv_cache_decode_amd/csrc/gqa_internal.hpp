@@ -142,6 +142,8 @@ int matrix_workgroups_per_cu(int G, bool fused);
 // Waves per workgroup of the matrix kernel instance for G heads per KV head.
 int matrix_waves(int G);
 int vector_workgroups_per_cu(int dtype, int d, int heads_per_block, bool fused);
+// Waves per workgroup of the vector kernel instance for this dtype, d and head block.
+int vector_waves(int dtype, int d, int heads_per_block);
 
 // Vector-path head block for G query heads per KV head: the smallest power of
 // two >= G, capped at 8 (larger groups use several head blocks).
