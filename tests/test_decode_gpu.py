@@ -235,3 +235,21 @@ def test_workspace_reuse_across_ticket_padding(gpu_lib, oracle_mod):
         torch.cuda.synchronize()
         assert_parity(out, pb.oracle_attention(q), "bf16")
         assert_counters_zero(ws, pb.b, pb.h)
+
+
+@pytest.mark.parametrize("b,h,g,d,cap,dtype", [
+    (65535, 2, 1, 16, 3, "f32"),      # the largest batch the ABI accepts
+    (2, 4096, 64, 128, 48, "bf16"),   # the most query heads, 64 per KV head (matrix, four blocks)
+    (2, 4096, 4096, 16, 12, "f32"),   # the most query heads, MHA
+])
+def test_maximum_sizes(gpu_lib, oracle_mod, b, h, g, d, cap, dtype):
+    rng = np.random.default_rng(b + h)
+    lens = rng.integers(0, cap, size=b).tolist()
+    pb = Problem(oracle_mod, seed=97, b=b, h=h, g=g, d=d, cap=cap, lens=lens, dtype=dtype)
+    print(f"maximum sizes: b={b} h={h} g={g} d={d} {dtype}", flush=True)
+    q = pb.query()
+    ref = pb.oracle_attention(q)
+    for merge in (api.MERGE_INLINE, api.MERGE_KERNEL):
+        out, ws = pb.gpu_attention(q, path=api.PATH_AUTO | merge)
+        assert_parity(out, ref, dtype, f"merge={merge:#x}")
+        assert_counters_zero(ws, b, h)

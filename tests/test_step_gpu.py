@@ -143,3 +143,14 @@ def test_step_batch_sizes_around_64(gpu_lib, oracle_mod, b, path, dtype, d):
         got, ref = pb.step(step, path=path)
         assert_parity(got, ref, dtype, f"b={b} step={step}")
         pb.check_state()
+
+
+def test_step_maximum_batch(gpu_lib, oracle_mod):
+    # the largest batch: the last workgroup writes all 65535 grown lengths
+    b = 65535
+    lens = np.random.default_rng(7).integers(0, 3, size=b).tolist()
+    pb = StepProblem(oracle_mod, seed=306, b=b, h=2, g=1, d=16, cap=5, lens=lens, dtype="f32")
+    for step in range(2):
+        got, ref = pb.step(step)
+        assert_parity(got, ref, "f32", f"step {step}")
+        pb.check_state()
