@@ -206,13 +206,14 @@ int gqa_decode_plan(int b, int h, int g, int d_k, int d_v, int cap, int max_len,
 
 namespace {
 
-// Shared body of the attention and fused-step entry points. max_len_att is
-// the bound of the attended lengths (the appended token included).
-int decode_common(const char* fn, void* out, const void* q, void* k_cache, void* v_cache, int32_t* lens,
-                  const void* k_new, const void* v_new, int b, int h, int g, int d_k, int d_v, int cap,
-                  int max_len_att, float scale, int dtype, void* workspace, size_t workspace_bytes,
-                  void* stream, int path, int workgroups, int fused) {
-  Plan plan;
+// Checks and launch parameters of the attention and fused-step entry points
+// (nothing is enqueued). max_len_att is the bound of the attended lengths
+// (the appended token included).
+int decode_prepare(const char* fn, void* out, const void* q, void* k_cache, void* v_cache, int32_t* lens,
+                   const void* k_new, const void* v_new, int b, int h, int g, int d_k, int d_v, int cap,
+                   int max_len_att, float scale, int dtype, void* workspace, size_t workspace_bytes, int path,
+                   int workgroups, int fused, gqa::DecodeParams* pp, Plan* planp) {
+  Plan& plan = *planp;
   const int rc = plan_decode(b, h, g, d_k, d_v, cap, max_len_att, dtype, path, workgroups, &plan, fused != 0);
   if (rc != GQA_OK) return rc;
   const gqa::WorkspaceLayout ws = gqa::workspace_layout(b, h, gblk_bound(h / g), d_v);
@@ -223,7 +224,7 @@ int decode_common(const char* fn, void* out, const void* q, void* k_cache, void*
   if (reinterpret_cast<uintptr_t>(workspace) & 255)
     return fail(GQA_ERR_ARG, "%s: workspace must be 256-byte aligned", fn);
 
-  gqa::DecodeParams p;
+  gqa::DecodeParams& p = *pp;
   p.out = out;
   p.q = q;
   p.k_cache = k_cache;
@@ -257,6 +258,10 @@ int decode_common(const char* fn, void* out, const void* q, void* k_cache, void*
   p.seg_lead = (plan.path == GQA_PATH_MATRIX && gqa::matrix_waves(p.G) == 8) ? kSegmentLead : 0;
   p.scale_log2 = scale * kLog2e;
 
+  return GQA_OK;
+}
+
+int decode_launch(const char* fn, const gqa::DecodeParams& p, const Plan& plan, int dtype, void* stream) {
   const hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e = plan.path == GQA_PATH_MATRIX ? gqa::launch_decode_matrix(p, st)
                                               : gqa::launch_decode_vector(p, dtype, st);
@@ -266,6 +271,41 @@ int decode_common(const char* fn, void* out, const void* q, void* k_cache, void*
     if (e != hipSuccess) return fail(GQA_ERR_HIP, "%s merge launch: %s", fn, hipGetErrorString(e));
   }
   return ok();
+}
+
+// Shared body of the attention and fused-step entry points. max_len_att is
+// the bound of the attended lengths (the appended token included).
+int decode_common(const char* fn, void* out, const void* q, void* k_cache, void* v_cache, int32_t* lens,
+                  const void* k_new, const void* v_new, int b, int h, int g, int d_k, int d_v, int cap,
+                  int max_len_att, float scale, int dtype, void* workspace, size_t workspace_bytes,
+                  void* stream, int path, int workgroups, int fused) {
+  gqa::DecodeParams p;
+  Plan plan;
+  const int rc = decode_prepare(fn, out, q, k_cache, v_cache, lens, k_new, v_new, b, h, g, d_k, d_v, cap,
+                                max_len_att, scale, dtype, workspace, workspace_bytes, path, workgroups, fused,
+                                &p, &plan);
+  if (rc != GQA_OK) return rc;
+  return decode_launch(fn, p, plan, dtype, stream);
+}
+
+bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15) == 0; }
+
+// Checks of one linear projection (rows x n_in times n_out x n_in, bf16).
+int linear_check(const char* fn, int rows, int n_in, int n_out, int dtype) {
+  if (dtype != GQA_DTYPE_BF16) return fail(GQA_ERR_UNSUPPORTED, "%s: projections need bf16 (dtype=%d)", fn, dtype);
+  if (rows <= 0 || rows > gqa::kLinearMaxRows)
+    return fail(GQA_ERR_UNSUPPORTED, "%s: rows=%d must be in [1, %d]", fn, rows, gqa::kLinearMaxRows);
+  if (n_in <= 0 || n_out <= 0) return fail(GQA_ERR_ARG, "%s: n_in=%d, n_out=%d must be positive", fn, n_in, n_out);
+  if (n_in % 8 != 0) return fail(GQA_ERR_UNSUPPORTED, "%s: n_in=%d must be a multiple of 8", fn, n_in);
+  return GQA_OK;
+}
+
+void linear_segment(gqa::LinearParams& lp, const void* w, void* y, int n_out) {
+  const int s = lp.nseg++;
+  lp.w[s] = static_cast<const uint16_t*>(w);
+  lp.y[s] = static_cast<uint16_t*>(y);
+  lp.n_out[s] = n_out;
+  lp.blocks[s] = (n_out + 15) / 16;
 }
 
 }  // namespace
@@ -303,6 +343,68 @@ int gqa_decode_step(void* out, const void* q, const void* k_new, const void* v_n
                     float scale, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
   return gqa_decode_step_ex(out, q, k_new, v_new, k_cache, v_cache, lens, b, h, g, d_k, d_v, cap, max_len, scale,
                             dtype, workspace, workspace_bytes, stream, GQA_PATH_AUTO, 0);
+}
+
+int gqa_linear(void* y, const void* x, const void* w, int rows, int n_in, int n_out, int dtype, void* stream) {
+  if (!y || !x || !w) return fail(GQA_ERR_ARG, "gqa_linear: null pointer argument");
+  const int rc = linear_check("gqa_linear", rows, n_in, n_out, dtype);
+  if (rc != GQA_OK) return rc;
+  if (!aligned16(x) || !aligned16(w)) return fail(GQA_ERR_ARG, "gqa_linear: x and w must be 16-byte aligned");
+  gqa::LinearParams lp{};
+  lp.x = static_cast<const uint16_t*>(x);
+  lp.rows = rows;
+  lp.n_in = n_in;
+  linear_segment(lp, w, y, n_out);
+  const hipError_t e = gqa::launch_linear(lp, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(GQA_ERR_HIP, "gqa_linear launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int gqa_decode_layer(void* y, const void* x, const void* w_q, const void* w_k, const void* w_v, const void* w_o,
+                     void* q, void* k_new, void* v_new, void* attn, void* k_cache, void* v_cache, int32_t* lens,
+                     int b, int h, int g, int d_model, int d_k, int d_v, int cap, int max_len, float scale,
+                     int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!y || !x || !w_q || !w_k || !w_v || !w_o || !q || !k_new || !v_new || !attn || !k_cache || !v_cache || !lens)
+    return fail(GQA_ERR_ARG, "gqa_decode_layer: null pointer argument");
+  if (d_model <= 0) return fail(GQA_ERR_ARG, "gqa_decode_layer: d_model=%d must be positive", d_model);
+  if (h <= 0 || g <= 0 || d_k <= 0 || d_v <= 0 || (long long)h * d_v > (1 << 30))
+    return fail(GQA_ERR_ARG, "gqa_decode_layer: h=%d, g=%d, d_k=%d, d_v=%d", h, g, d_k, d_v);
+  int rc = linear_check("gqa_decode_layer", b, d_model, 1, dtype);
+  if (rc != GQA_OK) return rc;
+  rc = linear_check("gqa_decode_layer", b, h * d_v, d_model, dtype);
+  if (rc != GQA_OK) return rc;
+  for (const void* ptr : {x, w_q, w_k, w_v, w_o, static_cast<const void*>(attn)})
+    if (!aligned16(ptr)) return fail(GQA_ERR_ARG, "gqa_decode_layer: x, weights and attn must be 16-byte aligned");
+  if (max_len < 0) return fail(GQA_ERR_ARG, "max_len=%d must be >= 0", max_len);
+  if (cap > 0 && (long long)max_len + 1 > cap)
+    return fail(GQA_ERR_CAPACITY, "appending to max_len=%d needs cap > %d, cap=%d", max_len, max_len, cap);
+  if (max_len == INT32_MAX) return fail(GQA_ERR_CAPACITY, "max_len=%d too large", max_len);
+  gqa::DecodeParams p;
+  Plan plan;
+  rc = decode_prepare("gqa_decode_layer", attn, q, k_cache, v_cache, lens, k_new, v_new, b, h, g, d_k, d_v, cap,
+                      max_len + 1, scale, dtype, workspace, workspace_bytes, GQA_PATH_AUTO, 0, 1, &p, &plan);
+  if (rc != GQA_OK) return rc;
+
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  gqa::LinearParams qkv{};
+  qkv.x = static_cast<const uint16_t*>(x);
+  qkv.rows = b;
+  qkv.n_in = d_model;
+  linear_segment(qkv, w_q, q, h * d_k);
+  linear_segment(qkv, w_k, k_new, g * d_k);
+  linear_segment(qkv, w_v, v_new, g * d_v);
+  hipError_t e = gqa::launch_linear(qkv, st);
+  if (e != hipSuccess) return fail(GQA_ERR_HIP, "gqa_decode_layer projection launch: %s", hipGetErrorString(e));
+  rc = decode_launch("gqa_decode_layer", p, plan, dtype, stream);
+  if (rc != GQA_OK) return rc;
+  gqa::LinearParams out{};
+  out.x = static_cast<const uint16_t*>(attn);
+  out.rows = b;
+  out.n_in = h * d_v;
+  linear_segment(out, w_o, y, d_model);
+  e = gqa::launch_linear(out, st);
+  if (e != hipSuccess) return fail(GQA_ERR_HIP, "gqa_decode_layer output projection launch: %s", hipGetErrorString(e));
+  return ok();
 }
 
 int gqa_decode_attention(void* out, const void* q, const void* k_cache, const void* v_cache,

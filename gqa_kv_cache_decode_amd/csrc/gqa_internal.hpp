@@ -95,6 +95,18 @@ struct DecodeParams {
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// y_s = x w_s^T for up to three weight matrices w_s [n_out_s][n_in] (bf16),
+// x [rows][n_in], y_s [rows][n_out_s]; blocks[s] = ceil(n_out_s / 16).
+constexpr int kLinearMaxRows = 64;
+struct LinearParams {
+  const uint16_t* x;
+  int rows, n_in, nseg;
+  const uint16_t* w[3];
+  uint16_t* y[3];
+  int n_out[3];
+  int blocks[3];
+};
+
 // Workspace layout, relative to the end of the caller's buffer so that a
 // buffer sized for one shape serves every smaller shape without the regions
 // of one call overlapping those of another: partial slots from the start,
@@ -135,6 +147,7 @@ hipError_t launch_append(const AppendParams& p, int b, int dtype, hipStream_t st
 hipError_t launch_decode_vector(const DecodeParams& p, int dtype, hipStream_t stream);
 hipError_t launch_decode_matrix(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_merge_partials(const DecodeParams& p, int dtype, hipStream_t stream);
+hipError_t launch_linear(const LinearParams& p, hipStream_t stream);
 
 // Workgroups of the decode kernel instance that fit on one compute unit at
 // once (runtime occupancy query, cached; 0 if the runtime cannot say).

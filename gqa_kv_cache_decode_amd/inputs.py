@@ -32,6 +32,8 @@ TAG_V = 3
 TAG_Q = 4
 TAG_KNEW = 5
 TAG_VNEW = 6
+TAG_X = 7        # the token vectors entering a layer
+TAG_WEIGHT = 8   # projection matrices (key: which matrix, then the row block)
 
 BF16_NAN = np.uint16(0x7FC0)
 
@@ -129,6 +131,31 @@ def draw_new_kv(seed: int, step: int, b: int, g: int, d_k: int, d_v: int, dtype:
     k = normals(seed, (TAG_KNEW, step), b * g * d_k, dtype).reshape(b, g, d_k)
     v = normals(seed, (TAG_VNEW, step), b * g * d_v, dtype).reshape(b, g, d_v)
     return k, v
+
+
+def draw_x(seed: int, step: int, b: int, d_model: int, dtype: str) -> np.ndarray:
+    """The token vectors entering a layer at one decode step, [b, d_model]."""
+    return normals(seed, (TAG_X, step), b * d_model, dtype).reshape(b, d_model)
+
+
+def draw_weight(seed: int, which: int, n_out: int, n_in: int, dtype: str) -> np.ndarray:
+    """A projection matrix [n_out, n_in] with entries N(0, 1/n_in) (rows drawn in parallel blocks).
+
+    which: 0 query, 1 key, 2 value, 3 output projection.
+    """
+    std = np.float32(1.0 / np.sqrt(n_in))
+    rows_per = max(1, (1 << 20) // n_in)
+    blocks = [(r0, min(n_out, r0 + rows_per)) for r0 in range(0, n_out, rows_per)]
+    out = np.empty((n_out, n_in), dtype=storage_dtype(dtype))
+
+    def fill(blk):
+        r0, r1 = blk
+        v = _rng(seed, TAG_WEIGHT, which, r0).standard_normal((r1 - r0) * n_in, dtype=np.float32) * std
+        out[r0:r1] = (v if dtype == "f32" else f32_to_bf16_bits(v)).reshape(r1 - r0, n_in)
+
+    with _cf.ThreadPoolExecutor(_workers()) as ex:
+        list(ex.map(fill, blocks))
+    return out
 
 
 class Batch:

@@ -189,6 +189,48 @@ int gqa_decode_step_ex(void* out, const void* q, const void* k_new, const void* 
                        void* stream, int path, int workgroups);
 
 /*
+ * A linear projection of the decode batch: y[r][o] = sum_k x[r][k] * w[o][k]
+ * for r < rows, o < n_out (the token's vector times a projection matrix, as
+ * in the MQA review, §2.4: q = x P_q, k = x P_k, v = x P_v, and the output
+ * y = o P_o). All three arrays are bf16 (GQA_DTYPE_BF16 only; anything else
+ * gives GQA_ERR_UNSUPPORTED), row-major and contiguous:
+ *   x [rows][n_in], w [n_out][n_in] (row o holds output feature o's weights,
+ *   PyTorch's Linear layout), y [rows][n_out].
+ * Accumulation in fp32, y rounded to bf16 (nearest even).
+ * rows in [1, 64] (a decode batch) and n_in a multiple of 8, else
+ * GQA_ERR_UNSUPPORTED; x and w 16-byte aligned, else GQA_ERR_ARG. y must not
+ * overlap x or w. Asynchronous on stream.
+ */
+int gqa_linear(void* y, const void* x, const void* w, int rows, int n_in, int n_out, int dtype, void* stream);
+
+/*
+ * One attention step of a decoder layer for the new token of each of b
+ * sequences (the MQA review, §2.4 incremental multi-head attention, with the
+ * K/V head axis of size g as in §3 for g = 1 and the TF2 GQA lesson for
+ * 1 < g < h):
+ *   q     = x W_q^T   -> [b][h][d_k]      (query projection)
+ *   k_new = x W_k^T   -> [b][g][d_k]      (key projection)
+ *   v_new = x W_v^T   -> [b][g][d_v]      (value projection)
+ *   gqa_decode_step(attn, q, k_new, v_new, caches, lens, ...)  -> attn [b][h][d_v]
+ *   y     = attn W_o^T -> [b][d_model]    (output projection)
+ * x [b][d_model]; W_q [h*d_k][d_model] (row i*d_k + c holds the pages'
+ * P_q[i][:][c]), W_k [g*d_k][d_model], W_v [g*d_v][d_model],
+ * W_o [d_model][h*d_v] (row m, column i*d_v + c holds P_o[i][m][c]).
+ * q, k_new, v_new and attn are caller-owned scratch of the sizes above; they
+ * hold the intermediate results when the call completes. The projections'
+ * outputs are stored in bf16 before the append and attention use them.
+ * bf16 only; b <= 64; d_model and h*d_v multiples of 8; caches, lens, cap,
+ * max_len, scale and workspace as in gqa_decode_step (lens grows by one).
+ * Every check runs before anything is enqueued; four launches on stream
+ * (one for the three input projections, the step, the output projection),
+ * five when the step merges split segments in a second launch.
+ */
+int gqa_decode_layer(void* y, const void* x, const void* w_q, const void* w_k, const void* w_v, const void* w_o,
+                     void* q, void* k_new, void* v_new, void* attn, void* k_cache, void* v_cache, int32_t* lens,
+                     int b, int h, int g, int d_model, int d_k, int d_v, int cap, int max_len, float scale,
+                     int dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Describe the launch gqa_decode_attention_ex would make on the current
  * device, without enqueueing anything: writes the chosen path
  * (GQA_PATH_VECTOR or GQA_PATH_MATRIX, OR-ed with the GQA_MERGE_* flag in

@@ -89,6 +89,10 @@ def _load():
         vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
         ctypes.c_float, i32, vp, i32,
     ]
+    lib.oracle_linear.restype = i32
+    lib.oracle_linear.argtypes = [vp, vp, vp, i32, i32, i32, i32]
+    lib.oracle_store.restype = None
+    lib.oracle_store.argtypes = [vp, vp, ctypes.c_size_t, i32]
     _lib = lib
     return lib
 
@@ -174,3 +178,49 @@ def decode_attention(q, k_cache, v_cache, lens, scale: float, *, want_weights=Fa
     if count_muls:
         res.append(int(muls.value))
     return res[0] if len(res) == 1 else tuple(res)
+
+
+def linear(x, w) -> np.ndarray:
+    """y[r][o] = sum_k x[r][k] * w[o][k] in fp64 [MQA-review §2.4 projections].
+
+    x [rows, n_in], w [n_out, n_in] (output-major), same element type.
+    """
+    x = np.ascontiguousarray(x)
+    w = np.ascontiguousarray(w)
+    dt = _dtype_code(x)
+    if _dtype_code(w) != dt or x.ndim != 2 or w.ndim != 2 or x.shape[1] != w.shape[1]:
+        raise OracleError(ERR_ARG, "linear shapes")
+    y = np.zeros((x.shape[0], w.shape[0]), dtype=np.float64)
+    rc = _load().oracle_linear(_ptr(y), _ptr(x), _ptr(w), x.shape[0], x.shape[1], w.shape[0], dt)
+    if rc != OK:
+        raise OracleError(rc, "linear")
+    return y
+
+
+def store(values, like_dtype) -> np.ndarray:
+    """Hold fp64 values in an element type (float32, or bf16 bit patterns as uint16), nearest even."""
+    values = np.ascontiguousarray(values, dtype=np.float64)
+    dt = F32 if np.dtype(like_dtype) == np.float32 else BF16
+    out = np.empty(values.shape, dtype=np.float32 if dt == F32 else np.uint16)
+    _load().oracle_store(_ptr(out), _ptr(values), values.size, dt)
+    return out
+
+
+def decode_layer(x, w_q, w_k, w_v, w_o, k_cache, v_cache, lens, scale: float, h: int):
+    """One decode step of a layer [MQA-review §2.4 incremental attention; §3 for g = 1].
+
+    q = x W_q^T, k_new = x W_k^T, v_new = x W_v^T (each held in the activation
+    type), append (k_cache, v_cache and lens updated in place), attention of q
+    over the grown caches (held in the activation type), then y = attn W_o^T.
+    Returns (y fp64 [b, d_model], dict of the intermediate arrays).
+    """
+    b = x.shape[0]
+    g, d_k, d_v = k_cache.shape[1], k_cache.shape[3], v_cache.shape[3]
+    q = store(linear(x, w_q), x.dtype).reshape(b, h, d_k)
+    k_new = store(linear(x, w_k), x.dtype).reshape(b, g, d_k)
+    v_new = store(linear(x, w_v), x.dtype).reshape(b, g, d_v)
+    kv_append(k_cache, v_cache, k_new, v_new, lens)
+    attn64 = decode_attention(q, k_cache, v_cache, lens, scale)
+    attn = store(attn64, x.dtype)
+    y = linear(attn.reshape(b, h * d_v), w_o)
+    return y, {"q": q, "k_new": k_new, "v_new": v_new, "attn": attn, "attn64": attn64}

@@ -221,3 +221,50 @@ int oracle_decode_attention(double* out, double* weights, const void* q,
   if (mul_count) *mul_count = muls;
   return failed ? ORC_ERR_ARG : ORC_OK;
 }
+
+/*
+ * A projection of the new token's vector by a weight matrix
+ * [MQA-review §2.4: q = x P_q, k = x P_k, v = x P_v for the incremental step,
+ * and y = o P_o after the attention; §3: P_k and P_v lose the head axis for
+ * MQA]. The matrix is given output-major: w[o][k] is the weight from input
+ * feature k to output feature o, so
+ *   y[r][o] = sum_k x[r][k] * w[o][k]      r < rows, o < n_out,
+ * with the sum over k in index order. x, w in the element type dtype; y in
+ * double.
+ */
+int oracle_linear(double* y, const void* x, const void* w, int rows, int n_in, int n_out, int dtype) {
+  if (!y || !x || !w || rows <= 0 || n_in <= 0 || n_out <= 0) return ORC_ERR_ARG;
+  if (dtype != ORC_F32 && dtype != ORC_BF16) return ORC_ERR_UNSUPPORTED;
+#pragma omp parallel for collapse(2) schedule(static)
+  for (int r = 0; r < rows; ++r) {
+    for (int o = 0; o < n_out; ++o) {
+      double acc = 0.0;
+      for (int k = 0; k < n_in; ++k)
+        acc += widen(x, (size_t)r * n_in + k, dtype) * widen(w, (size_t)o * n_in + k, dtype);
+      y[(size_t)r * n_out + o] = acc;
+    }
+  }
+  return ORC_OK;
+}
+
+/*
+ * Store doubles in an element type: fp32 by the C conversion (round to
+ * nearest even), bf16 as the upper 16 bits of that fp32 value rounded to
+ * nearest even (a NaN stays a NaN). Used where a value the step produces is
+ * held in the activation type before the next operation reads it.
+ */
+void oracle_store(void* dst, const double* src, size_t n, int dtype) {
+  for (size_t i = 0; i < n; ++i) {
+    const float f = (float)src[i];
+    if (dtype == ORC_F32) {
+      ((float*)dst)[i] = f;
+      continue;
+    }
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    uint16_t h;
+    if ((u & 0x7fffffffu) > 0x7f800000u) h = (uint16_t)((u >> 16) | 0x40u);
+    else h = (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+    ((uint16_t*)dst)[i] = h;
+  }
+}

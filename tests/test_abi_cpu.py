@@ -173,3 +173,37 @@ def test_step_rejects(lib):
     assert call(dk=96, dv=96) == _lib.ERR_UNSUPPORTED
     assert call(ws_bytes=8) == _lib.ERR_WORKSPACE
     assert call(max_len=-2) == _lib.ERR_ARG
+
+
+def test_linear_rejects(lib):
+    def call(**kw):
+        a = dict(y=FAKE, x=FAKE, w=FAKE, rows=16, n_in=64, n_out=32, dtype=_lib.BF16)
+        a.update(kw)
+        return lib.gqa_linear(a["y"], a["x"], a["w"], a["rows"], a["n_in"], a["n_out"], a["dtype"], None)
+    assert call(dtype=_lib.F32) == _lib.ERR_UNSUPPORTED
+    assert call(rows=65) == _lib.ERR_UNSUPPORTED
+    assert call(rows=0) == _lib.ERR_UNSUPPORTED
+    assert call(n_in=12) == _lib.ERR_UNSUPPORTED
+    assert call(n_out=0) == _lib.ERR_ARG
+    assert call(w=None) == _lib.ERR_ARG
+    assert call(x=ctypes.c_void_p(0x1008)) == _lib.ERR_ARG  # not 16-byte aligned
+    assert lib.gqa_last_error().decode() != ""
+
+
+def test_decode_layer_rejects(lib):
+    def call(**kw):
+        a = dict(b=16, h=64, g=8, d_model=8192, d=128, cap=100, max_len=50, dtype=_lib.BF16, ws=FAKE,
+                 ws_bytes=1 << 30, x=FAKE)
+        a.update(kw)
+        return lib.gqa_decode_layer(FAKE, a["x"], FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                    a["b"], a["h"], a["g"], a["d_model"], a["d"], a["d"], a["cap"], a["max_len"],
+                                    ctypes.c_float(0.1), a["dtype"], a["ws"], a["ws_bytes"], None)
+    assert call(dtype=_lib.F32) == _lib.ERR_UNSUPPORTED
+    assert call(b=65) == _lib.ERR_UNSUPPORTED
+    assert call(d_model=100) == _lib.ERR_UNSUPPORTED
+    assert call(d_model=0) == _lib.ERR_ARG
+    assert call(x=None) == _lib.ERR_ARG
+    assert call(max_len=100) == _lib.ERR_CAPACITY
+    assert call(h=60) == _lib.ERR_GROUPS
+    assert call(ws_bytes=64) == _lib.ERR_WORKSPACE
+    assert call(d=96) == _lib.ERR_UNSUPPORTED
