@@ -21,7 +21,16 @@ the launch stream: for the fused step (one launch per step) the timed
 region's time over the step count; with --unfused, a pair of events around
 each decode launch.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+With --layer the step is one gqa_decode_layer call instead: the query, key
+and value projections of the new token (one launch), the fused append +
+attention, and the output projection, with d_model = h * d_k and bf16
+weights in the packed layout. Each layer set holds its own cache and its own
+device copy of the four weight matrices, and consecutive steps go to
+consecutive sets, as a decode step walks the layers of a model. Its value is
+(weight bytes + KV bytes) per step over the step time, and its roofline is
+that of the whole layer (three launches).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--layer]
 """
 from __future__ import annotations
 
@@ -96,6 +105,8 @@ def main():
                     help="run the step as gqa_kv_append + gqa_decode_attention instead of gqa_decode_step")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run a 1 GiB device copy first (reference for HBM byte counters)")
+    ap.add_argument("--layer", action="store_true",
+                    help="time the whole decode layer (projections + step) instead of the step alone")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -113,6 +124,11 @@ def main():
     torch.cuda.set_device(dev)
     dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
     total_steps = args.warmup + args.steps
+    if args.layer:
+        if wl.dtype != "bf16" or args.unfused:
+            print("--layer runs bf16 workloads with the fused step only", file=sys.stderr)
+            sys.exit(2)
+        return bench_layer(args, wl, dev)
 
     # cache sets
     set_bytes = wl.b * wl.g * wl.cap * wl.d * 2 * wl.elem_bytes
@@ -258,6 +274,114 @@ def main():
             "kernel_avg_us": round(kern_avg_ms * 1e3, 3),
         },
         "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+def bench_layer(args, wl, dev):
+    """Whole-layer decode steps (gqa_decode_layer), cycling through layer sets."""
+    import torch
+
+    from gqa_kv_cache_decode_amd import api, inputs
+    from gqa_kv_cache_decode_amd.workloads import kv_bytes_attended
+
+    dt = torch.bfloat16
+    h, g, d = wl.h, wl.g, wl.d
+    d_model = h * d
+    total_steps = args.warmup + args.steps
+    w_shapes = [(h * d, d_model), (g * d, d_model), (g * d, d_model), (d_model, h * d)]
+    w_bytes = sum(2 * o * i for o, i in w_shapes)
+    cache_bytes = wl.b * g * wl.cap * d * 2 * wl.elem_bytes
+    n_sets = args.sets or max(2, math.ceil(1.5e9 / (w_bytes + cache_bytes)))
+    n_sets = min(n_sets, total_steps) if total_steps > 0 else 1
+    grow = math.ceil(total_steps / n_sets) + 1
+    cap = wl.cap + grow
+    log(f"layer {wl.name}, d_model={d_model}: {n_sets} layer sets of {(w_bytes + cache_bytes) / 1e6:.1f} MB")
+
+    def to_dev(a):
+        return torch.from_numpy(a).view(torch.bfloat16).to(dev)
+
+    # one draw of each matrix; every layer set packs its own device copy
+    w_host = [inputs.draw_weight(wl.seed, k, o, i, "bf16") for k, (o, i) in enumerate(w_shapes)]
+    sets, host0 = [], None
+    for r in range(n_sets):
+        batch = inputs.Batch(seed=wl.seed + 1000 * r, b=wl.b, h=h, g=g, d=d, cap=cap,
+                             lens=wl.lens if r == 0 else host0.lens.tolist(), dtype="bf16", poison=False)
+        if r == 0:
+            host0 = batch
+        ws_dev = []
+        for w in w_host:
+            t = to_dev(w)
+            ws_dev.append(api.PackedWeight(t))
+            del t
+        sets.append({"w": ws_dev, "kc": to_dev(batch.k_cache), "vc": to_dev(batch.v_cache),
+                     "lens": torch.from_numpy(batch.lens.copy()).to(dev), "lens_h": batch.lens.copy()})
+        if r != 0:
+            del batch
+    torch.cuda.synchronize()
+    log("layer sets resident")
+    max_len_bound = int(max(st["lens_h"].max() for st in sets)) + grow
+    ws = api.make_workspace(wl.b, h, g, d, d, max_len_bound, dt, dev)
+    scratch = api.LayerScratch(wl.b, h, g, d, d, dt, dev)
+    xs = [to_dev(inputs.draw_x(wl.seed, s, wl.b, d_model, "bf16")) for s in range(min(total_steps, 64))]
+    y = torch.empty(wl.b, d_model, dtype=dt, device=dev)
+    io_bytes = 2 * wl.b * (2 * d_model + 2 * h * d + 2 * g * d)  # x, y, q, attn, k_new, v_new
+
+    def step(i):
+        st = sets[i % n_sets]
+        api.decode_layer(y, xs[i % len(xs)], *st["w"], st["kc"], st["vc"], st["lens"], int(st["lens_h"].max()),
+                         wl.scale, ws, scratch)
+        st["lens_h"] += 1
+        return kv_bytes_attended(g, d, d, wl.elem_bytes, st["lens_h"])
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    log("warmup done")
+    stream = torch.cuda.current_stream()
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    kv_total = 0
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for k in range(args.steps):
+        kv_total += step(args.warmup + k)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    elapsed_ms = t_start.elapsed_time(t_end)
+    step_ms = elapsed_ms / args.steps
+    bytes_per_step = w_bytes + kv_total / args.steps + io_bytes
+    value = bytes_per_step / (step_ms / 1e3) / 1e9
+    log(f"timed {args.steps} layer steps: {elapsed_ms:.3f} ms, {step_ms * 1e3:.2f} us per step")
+    lens0 = host0.lens
+    rec = {
+        "metric": METRIC + " (whole decode layer: weight + KV bytes)",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 5),
+        "steps_per_s": round(args.steps / (elapsed_ms / 1e3), 1),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": wl.name + "_layer", "b": wl.b, "h": h, "g": g, "d_k": d, "d_v": d, "d_model": d_model,
+            "lens": list(wl.lens) if isinstance(wl.lens, (list, tuple)) else wl.lens,
+            "lens_drawn_mean": float(lens0.mean()), "layer_sets": n_sets, "seed": wl.seed,
+            "step_api": "gqa_decode_layer", "weight_bytes_per_step": w_bytes,
+            "kv_bytes_per_step": int(kv_total / args.steps), "io_bytes_per_step": io_bytes,
+        },
+        "roofline": {
+            "bound": "hbm", "achieved": round(value, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(value / HBM_PEAK_GBS, 4), "traffic": None,
+            "kernel": "gqa_decode_layer (linear_bf16_kernel, fused decode step, linear_bf16_kernel)",
+            "kernel_avg_us": round(step_ms * 1e3, 3),
+        },
+        "cpu_baseline": None,
     }
     print(json.dumps(rec), flush=True)
 

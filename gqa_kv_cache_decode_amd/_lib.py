@@ -46,6 +46,8 @@ SIGNATURES = {
     "gqa_decode_step_ex": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                                   _f32, _i32, _vp, _sz, _vp, _i32, _i32]),
     "gqa_decode_plan": (_i32, [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _ip, _ip]),
+    "gqa_packed_weight_bytes": (_sz, [_i32, _i32]),
+    "gqa_pack_weight": (_i32, [_vp, _vp, _i32, _i32, _i32, _vp]),
     "gqa_linear": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp]),
     "gqa_decode_layer": (_i32, [_vp] * 13 + [_i32] * 8 + [_f32, _i32, _vp, _sz, _vp]),
     "gqa_last_error": (ctypes.c_char_p, []),

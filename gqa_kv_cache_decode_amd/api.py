@@ -147,17 +147,31 @@ def decode_step(out: torch.Tensor, q: torch.Tensor, k_new: torch.Tensor, v_new: 
     return out
 
 
-def linear(y: torch.Tensor, x: torch.Tensor, w: torch.Tensor, stream=None) -> torch.Tensor:
-    """y[r] = w @ x[r] for a decode batch: x [rows, n_in], w [n_out, n_in], y [rows, n_out], bf16."""
-    _check_gpu(y, x, w)
+class PackedWeight:
+    """A [n_out, n_in] bf16 weight matrix in the library's packed layout (gqa_pack_weight)."""
+
+    def __init__(self, w: torch.Tensor, stream=None):
+        _check_gpu(w)
+        if w.dim() != 2 or w.dtype != torch.bfloat16:
+            raise ValueError("PackedWeight takes a 2-d bfloat16 matrix [n_out, n_in]")
+        self.n_out, self.n_in = w.shape
+        lib = _lib.load()
+        nbytes = int(lib.gqa_packed_weight_bytes(self.n_out, self.n_in))
+        self.data = torch.empty(nbytes, dtype=torch.uint8, device=w.device)
+        _lib.check(lib.gqa_pack_weight(self.data.data_ptr(), w.data_ptr(), self.n_out, self.n_in, _lib.BF16,
+                                       _stream_handle(stream)), "gqa_pack_weight")
+
+
+def linear(y: torch.Tensor, x: torch.Tensor, w: PackedWeight, stream=None) -> torch.Tensor:
+    """y[r] = W @ x[r] for a decode batch: x [rows, n_in], W [n_out, n_in] packed, y [rows, n_out], bf16."""
+    _check_gpu(y, x, w.data)
     rows, n_in = x.shape
-    n_out, n_in2 = w.shape
-    if n_in2 != n_in or tuple(y.shape) != (rows, n_out):
+    if w.n_in != n_in or tuple(y.shape) != (rows, w.n_out):
         raise ValueError("linear: inconsistent shapes")
     dt = _dtype_code(x)
-    if _dtype_code(w) != dt or _dtype_code(y) != dt:
-        raise TypeError("x, w and y must share one element type")
-    rc = _lib.load().gqa_linear(y.data_ptr(), x.data_ptr(), w.data_ptr(), rows, n_in, n_out, dt,
+    if _dtype_code(y) != dt:
+        raise TypeError("x and y must share one element type")
+    rc = _lib.load().gqa_linear(y.data_ptr(), x.data_ptr(), w.data.data_ptr(), rows, n_in, w.n_out, dt,
                                 _stream_handle(stream))
     _lib.check(rc, "gqa_linear")
     return y
@@ -173,34 +187,36 @@ class LayerScratch:
         self.attn = torch.empty(b, h, d_v, dtype=dtype, device=device)
 
 
-def decode_layer(y: torch.Tensor, x: torch.Tensor, w_q: torch.Tensor, w_k: torch.Tensor, w_v: torch.Tensor,
-                 w_o: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, lens: torch.Tensor, max_len: int,
+def decode_layer(y: torch.Tensor, x: torch.Tensor, w_q: PackedWeight, w_k: PackedWeight, w_v: PackedWeight,
+                 w_o: PackedWeight, k_cache: torch.Tensor, v_cache: torch.Tensor, lens: torch.Tensor, max_len: int,
                  scale: float, workspace: torch.Tensor, scratch: LayerScratch, stream=None) -> torch.Tensor:
     """Projections, append, attention and output projection of one decode step (gqa_decode_layer).
 
-    x, y [b, d_model]; w_q [h*d_k, d_model]; w_k [g*d_k, d_model]; w_v [g*d_v, d_model];
+    x, y [b, d_model]; packed w_q [h*d_k, d_model], w_k [g*d_k, d_model], w_v [g*d_v, d_model],
     w_o [d_model, h*d_v]; caches [b, g, cap, d]; lens int32 [b] (pre-append, grows by one).
     """
-    _check_gpu(y, x, w_q, w_k, w_v, w_o, k_cache, v_cache, lens, workspace, scratch.q, scratch.k_new,
-               scratch.v_new, scratch.attn)
+    _check_gpu(y, x, w_q.data, w_k.data, w_v.data, w_o.data, k_cache, v_cache, lens, workspace, scratch.q,
+               scratch.k_new, scratch.v_new, scratch.attn)
     if lens.dtype != torch.int32:
         raise TypeError("lens must be int32")
     b, d_model = x.shape
     bk, g, cap, d_k = k_cache.shape
     d_v = v_cache.shape[3]
     h = scratch.q.shape[1]
-    if bk != b or tuple(y.shape) != (b, d_model) or tuple(w_q.shape) != (h * d_k, d_model) \
-            or tuple(w_k.shape) != (g * d_k, d_model) or tuple(w_v.shape) != (g * d_v, d_model) \
-            or tuple(w_o.shape) != (d_model, h * d_v) or tuple(v_cache.shape) != (b, g, cap, d_v) \
+    shape = lambda w: (w.n_out, w.n_in)  # noqa: E731
+    if bk != b or tuple(y.shape) != (b, d_model) or shape(w_q) != (h * d_k, d_model) \
+            or shape(w_k) != (g * d_k, d_model) or shape(w_v) != (g * d_v, d_model) \
+            or shape(w_o) != (d_model, h * d_v) or tuple(v_cache.shape) != (b, g, cap, d_v) \
             or tuple(scratch.q.shape) != (b, h, d_k) or tuple(scratch.k_new.shape) != (b, g, d_k) \
             or tuple(scratch.v_new.shape) != (b, g, d_v) or tuple(scratch.attn.shape) != (b, h, d_v) \
             or tuple(lens.shape) != (b,):
         raise ValueError("decode_layer: inconsistent shapes")
     dt = _dtype_code(x)
-    if any(_dtype_code(t) != dt for t in (y, w_q, w_k, w_v, w_o, k_cache, v_cache, scratch.q)):
-        raise TypeError("activations, weights and caches must share one element type")
+    if any(_dtype_code(t) != dt for t in (y, k_cache, v_cache, scratch.q)):
+        raise TypeError("activations and caches must share one element type")
     rc = _lib.load().gqa_decode_layer(
-        y.data_ptr(), x.data_ptr(), w_q.data_ptr(), w_k.data_ptr(), w_v.data_ptr(), w_o.data_ptr(),
+        y.data_ptr(), x.data_ptr(), w_q.data.data_ptr(), w_k.data.data_ptr(), w_v.data.data_ptr(),
+        w_o.data.data_ptr(),
         scratch.q.data_ptr(), scratch.k_new.data_ptr(), scratch.v_new.data_ptr(), scratch.attn.data_ptr(),
         k_cache.data_ptr(), v_cache.data_ptr(), lens.data_ptr(), b, h, g, d_model, d_k, d_v, cap, int(max_len),
         ctypes.c_float(scale), dt, workspace.data_ptr(), workspace.numel() * workspace.element_size(),

@@ -345,6 +345,21 @@ int gqa_decode_step(void* out, const void* q, const void* k_new, const void* v_n
                             dtype, workspace, workspace_bytes, stream, GQA_PATH_AUTO, 0);
 }
 
+size_t gqa_packed_weight_bytes(int n_out, int n_in) {
+  if (n_out <= 0 || n_in <= 0) return 0;
+  return gqa::packed_weight_bytes(n_out, n_in);
+}
+
+int gqa_pack_weight(void* dst, const void* src, int n_out, int n_in, int dtype, void* stream) {
+  if (!dst || !src) return fail(GQA_ERR_ARG, "gqa_pack_weight: null pointer argument");
+  if (n_out <= 0 || n_in <= 0) return fail(GQA_ERR_ARG, "gqa_pack_weight: n_out=%d, n_in=%d", n_out, n_in);
+  if (dtype != GQA_DTYPE_BF16) return fail(GQA_ERR_UNSUPPORTED, "gqa_pack_weight: bf16 only (dtype=%d)", dtype);
+  if (!aligned16(dst)) return fail(GQA_ERR_ARG, "gqa_pack_weight: dst must be 16-byte aligned");
+  const hipError_t e = gqa::launch_pack_weight(dst, src, n_out, n_in, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(GQA_ERR_HIP, "gqa_pack_weight launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
 int gqa_linear(void* y, const void* x, const void* w, int rows, int n_in, int n_out, int dtype, void* stream) {
   if (!y || !x || !w) return fail(GQA_ERR_ARG, "gqa_linear: null pointer argument");
   const int rc = linear_check("gqa_linear", rows, n_in, n_out, dtype);

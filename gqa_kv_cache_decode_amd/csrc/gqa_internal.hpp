@@ -95,8 +95,9 @@ struct DecodeParams {
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-// y_s = x w_s^T for up to three weight matrices w_s [n_out_s][n_in] (bf16),
-// x [rows][n_in], y_s [rows][n_out_s]; blocks[s] = ceil(n_out_s / 16).
+// y_s = x w_s^T for up to three weight matrices w_s [n_out_s][n_in] (bf16,
+// packed by launch_pack_weight), x [rows][n_in], y_s [rows][n_out_s];
+// blocks[s] = ceil(n_out_s / 16).
 constexpr int kLinearMaxRows = 64;
 struct LinearParams {
   const uint16_t* x;
@@ -148,6 +149,8 @@ hipError_t launch_decode_vector(const DecodeParams& p, int dtype, hipStream_t st
 hipError_t launch_decode_matrix(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_merge_partials(const DecodeParams& p, int dtype, hipStream_t stream);
 hipError_t launch_linear(const LinearParams& p, hipStream_t stream);
+size_t packed_weight_bytes(int n_out, int n_in);
+hipError_t launch_pack_weight(void* dst, const void* src, int n_out, int n_in, hipStream_t stream);
 
 // Workgroups of the decode kernel instance that fit on one compute unit at
 // once (runtime occupancy query, cached; 0 if the runtime cannot say).

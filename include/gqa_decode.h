@@ -189,13 +189,25 @@ int gqa_decode_step_ex(void* out, const void* q, const void* k_new, const void* 
                        void* stream, int path, int workgroups);
 
 /*
+ * Projection weights are used in a packed layout: gqa_pack_weight reads a
+ * bf16 matrix w [n_out][n_in] (row o holds output feature o's weights,
+ * PyTorch's Linear layout) and writes gqa_packed_weight_bytes(n_out, n_in)
+ * bytes to dst (16-byte aligned, caller-owned, must not overlap src): the
+ * matrix cut into tiles of 16 rows x 32 columns, zero-padded at the edges,
+ * each tile in the order the matrix cores read it, the tiles of 16 rows
+ * consecutive. Pack once per weight matrix, reuse for every step.
+ * gqa_packed_weight_bytes returns 0 for non-positive sizes.
+ */
+size_t gqa_packed_weight_bytes(int n_out, int n_in);
+int gqa_pack_weight(void* dst, const void* src, int n_out, int n_in, int dtype, void* stream);
+
+/*
  * A linear projection of the decode batch: y[r][o] = sum_k x[r][k] * w[o][k]
  * for r < rows, o < n_out (the token's vector times a projection matrix, as
  * in the MQA review, §2.4: q = x P_q, k = x P_k, v = x P_v, and the output
- * y = o P_o). All three arrays are bf16 (GQA_DTYPE_BF16 only; anything else
- * gives GQA_ERR_UNSUPPORTED), row-major and contiguous:
- *   x [rows][n_in], w [n_out][n_in] (row o holds output feature o's weights,
- *   PyTorch's Linear layout), y [rows][n_out].
+ * y = o P_o). All arrays are bf16 (GQA_DTYPE_BF16 only; anything else gives
+ * GQA_ERR_UNSUPPORTED): x [rows][n_in] and y [rows][n_out] row-major and
+ * contiguous, w packed by gqa_pack_weight from its [n_out][n_in] form.
  * Accumulation in fp32, y rounded to bf16 (nearest even).
  * rows in [1, 64] (a decode batch) and n_in a multiple of 8, else
  * GQA_ERR_UNSUPPORTED; x and w 16-byte aligned, else GQA_ERR_ARG. y must not
@@ -213,9 +225,10 @@ int gqa_linear(void* y, const void* x, const void* w, int rows, int n_in, int n_
  *   v_new = x W_v^T   -> [b][g][d_v]      (value projection)
  *   gqa_decode_step(attn, q, k_new, v_new, caches, lens, ...)  -> attn [b][h][d_v]
  *   y     = attn W_o^T -> [b][d_model]    (output projection)
- * x [b][d_model]; W_q [h*d_k][d_model] (row i*d_k + c holds the pages'
- * P_q[i][:][c]), W_k [g*d_k][d_model], W_v [g*d_v][d_model],
- * W_o [d_model][h*d_v] (row m, column i*d_v + c holds P_o[i][m][c]).
+ * x [b][d_model]; the weights packed by gqa_pack_weight from
+ * W_q [h*d_k][d_model] (row i*d_k + c holds the pages' P_q[i][:][c]),
+ * W_k [g*d_k][d_model], W_v [g*d_v][d_model] and W_o [d_model][h*d_v]
+ * (row m, column i*d_v + c holds P_o[i][m][c]).
  * q, k_new, v_new and attn are caller-owned scratch of the sizes above; they
  * hold the intermediate results when the call completes. The projections'
  * outputs are stored in bf16 before the append and attention use them.

@@ -24,14 +24,28 @@ def test_linear_parity(gpu_lib, oracle_mod, rows, n_in, n_out):
     x = inputs.normals(11, (rows, n_in), rows * n_in, "bf16").reshape(rows, n_in)
     w = inputs.draw_weight(12 + n_out, 0, n_out, n_in, "bf16")
     y = torch.empty(rows, n_out, dtype=torch.bfloat16, device="cuda")
-    api.linear(y, to_dev(x), to_dev(w))
+    api.linear(y, to_dev(x), api.PackedWeight(to_dev(w)))
     torch.cuda.synchronize()
     assert_parity(y, oracle_mod.linear(x, w), "bf16", f"rows={rows} n_in={n_in} n_out={n_out}")
 
 
+@pytest.mark.parametrize("n_out,n_in", [(1, 8), (17, 40), (48, 1000), (64, 96)])
+def test_pack_weight_layout(gpu_lib, n_out, n_in):
+    # tile (block, s): lane l = 16q + n holds row 16*block + n, columns 32s + 8q .. +7; zero padding
+    w = inputs.draw_weight(15, 0, n_out, n_in, "bf16")
+    packed = api.PackedWeight(to_dev(w))
+    torch.cuda.synchronize()
+    got = packed.data.cpu().numpy().view(np.uint16)
+    nb, ns = (n_out + 15) // 16, (n_in + 31) // 32
+    padded = np.zeros((nb * 16, ns * 32), dtype=np.uint16)
+    padded[:n_out, :n_in] = w
+    want = padded.reshape(nb, 16, ns, 4, 8).transpose(0, 2, 3, 1, 4).reshape(-1)
+    assert got.size == want.size and np.array_equal(got, want)
+
+
 def test_linear_is_deterministic(gpu_lib):
     x = to_dev(inputs.normals(13, (1,), 16 * 4096, "bf16").reshape(16, 4096))
-    w = to_dev(inputs.draw_weight(14, 0, 4096, 4096, "bf16"))
+    w = api.PackedWeight(to_dev(inputs.draw_weight(14, 0, 4096, 4096, "bf16")))
     a = torch.empty(16, 4096, dtype=torch.bfloat16, device="cuda")
     b = torch.empty_like(a)
     api.linear(a, x, w)
@@ -49,7 +63,7 @@ class LayerProblem:
         self.w_k = inputs.draw_weight(seed, 1, g * d, d_model, "bf16")
         self.w_v = inputs.draw_weight(seed, 2, g * d, d_model, "bf16")
         self.w_o = inputs.draw_weight(seed, 3, d_model, h * d, "bf16")
-        self.dev_w = [to_dev(w) for w in (self.w_q, self.w_k, self.w_v, self.w_o)]
+        self.dev_w = [api.PackedWeight(to_dev(w)) for w in (self.w_q, self.w_k, self.w_v, self.w_o)]
         self.kc, self.vc = to_dev(self.batch.k_cache), to_dev(self.batch.v_cache)
         self.lens_h = self.batch.lens.copy()
         self.lens = torch.from_numpy(self.lens_h.copy()).cuda()
@@ -93,6 +107,17 @@ def _check_layer(pb, step):
 def test_decode_layer_small(gpu_lib, oracle_mod, h, g, d_model):
     pb = LayerProblem(oracle_mod, seed=401 + h + g, b=3, h=h, g=g, d=128, d_model=d_model, cap=80,
                       lens=[0, 5, 70])
+    for step in range(2):
+        _check_layer(pb, step)
+
+
+@pytest.mark.parametrize("b", [16, 20, 40])
+def test_decode_layer_odd_projection_blocks(gpu_lib, oracle_mod, b):
+    # d=16, g=3: the key and value projections have 3 blocks of 16 features each, so
+    # from 16 batch rows up (two blocks per workgroup) a workgroup holds a lone last
+    # block of each matrix and must not run into the next matrix of the launch
+    lens = [(7 * s) % 45 for s in range(b)]
+    pb = LayerProblem(oracle_mod, seed=450 + b, b=b, h=6, g=3, d=16, d_model=200, cap=48, lens=lens)
     for step in range(2):
         _check_layer(pb, step)
 
