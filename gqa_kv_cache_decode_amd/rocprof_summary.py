@@ -12,7 +12,7 @@ Two summaries:
   the kernel sources so that a later source change invalidates it.
 
 Usage:
-  python -m gqa_kv_cache_decode_amd.rocprof_summary stats CSV OUT --command CMD
+  python -m gqa_kv_cache_decode_amd.rocprof_summary stats CSV OUT --command CMD [--trace TRACE_CSV]
   python -m gqa_kv_cache_decode_amd.rocprof_summary traffic FETCH_CSV WRITE_CSV OUT \\
       --kernel decode_matrix_kernel --copy-bytes 1073741824 --algorithmic-bytes N --command CMD
 """
@@ -27,13 +27,18 @@ import statistics
 PKG = os.path.dirname(os.path.abspath(__file__))
 
 
+# The sources the decode kernels are built from; a change to any of them may
+# change the decode kernel's traffic. The projection and append-only sources
+# and the host-side entry points do not.
+DECODE_SOURCES = ("gqa_internal.hpp", "decode_matrix.hip", "decode_vector.hip", "merge_partials.hip")
+
+
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
     csrc = os.path.join(PKG, "csrc")
-    for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hip", ".cpp", ".hpp", ".h")):
-            with open(os.path.join(csrc, name), "rb") as f:
-                h.update(name.encode() + b"\0" + f.read())
+    for name in DECODE_SOURCES:
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
 
 
@@ -45,6 +50,20 @@ def stats_summary(csv_path: str, command: str) -> str:
     for r in rows:
         lines.append(f"{int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:10.3f} {float(r['MinNs']) / 1e3:10.3f} "
                      f"{float(r['MaxNs']) / 1e3:10.3f} {float(r['Percentage']):8.2f}  {r['Name'][:140]}")
+    return "\n".join(lines) + "\n"
+
+
+def by_grid_summary(trace_csv: str) -> str:
+    """Durations per (kernel, grid size) from ``<run>_kernel_trace.csv``: separates the
+    launches of one kernel with different shapes (the layer's two projections)."""
+    groups = {}
+    for r in csv.DictReader(open(trace_csv)):
+        key = (r["Kernel_Name"][:110], int(r["Grid_Size_X"]) // max(1, int(r["Workgroup_Size_X"])))
+        groups.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    lines = ["", "# per launch shape (kernel trace)",
+             f"{'calls':>6} {'avg_us':>10} {'min_us':>10} {'max_us':>10} {'wgs':>8}  kernel"]
+    for (name, wgs), d in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+        lines.append(f"{len(d):6d} {statistics.mean(d):10.3f} {min(d):10.3f} {max(d):10.3f} {wgs:8d}  {name}")
     return "\n".join(lines) + "\n"
 
 
@@ -116,6 +135,7 @@ def main():
     a.add_argument("csv")
     a.add_argument("out")
     a.add_argument("--command", required=True)
+    a.add_argument("--trace", default=None, help="kernel_trace.csv: add a breakdown per launch shape")
     b = sub.add_parser("traffic")
     b.add_argument("fetch_csv")
     b.add_argument("write_csv")
@@ -128,6 +148,8 @@ def main():
     args = ap.parse_args()
     if args.cmd == "stats":
         text = stats_summary(args.csv, args.command)
+        if args.trace:
+            text += by_grid_summary(args.trace)
     else:
         text = traffic_summary(args.fetch_csv, args.write_csv, args.kernel, args.copy_bytes,
                                args.algorithmic_bytes, args.command, args.workload)

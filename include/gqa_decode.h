@@ -234,9 +234,9 @@ int gqa_linear(void* y, const void* x, const void* w, int rows, int n_in, int n_
  * outputs are stored in bf16 before the append and attention use them.
  * bf16 only; b <= 64; d_model and h*d_v multiples of 8; caches, lens, cap,
  * max_len, scale and workspace as in gqa_decode_step (lens grows by one).
- * Every check runs before anything is enqueued; four launches on stream
+ * Every check runs before anything is enqueued; three launches on stream
  * (one for the three input projections, the step, the output projection),
- * five when the step merges split segments in a second launch.
+ * four when the step merges split segments in a second launch.
  */
 int gqa_decode_layer(void* y, const void* x, const void* w_q, const void* w_k, const void* w_v, const void* w_o,
                      void* q, void* k_new, void* v_new, void* attn, void* k_cache, void* v_cache, int32_t* lens,
