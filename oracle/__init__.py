@@ -23,8 +23,9 @@ Pages the oracle follows (cited by title and section):
 * [LLM-inf-05] albangk "LLM inference 05" notes: the prefill/decode table, the
   per-layer decode pseudocode and the bytes-per-token arithmetic.
 
-Parity status: every function here is pinned by ``tests/test_oracle_pins.py``
-and ``tests/test_oracle_golden.py`` (no function is "parity unpinned").
+Parity status: every function here is pinned by ``tests/test_oracle_pins.py``,
+``tests/test_oracle_golden.py``, ``tests/test_oracle_layer.py`` and
+``tests/test_oracle_fold.py`` (no function is "parity unpinned").
 """
 from __future__ import annotations
 
@@ -93,6 +94,10 @@ def _load():
     lib.oracle_linear.argtypes = [vp, vp, vp, i32, i32, i32, i32]
     lib.oracle_store.restype = None
     lib.oracle_store.argtypes = [vp, vp, ctypes.c_size_t, i32]
+    lib.oracle_fold_heads.restype = i32
+    lib.oracle_fold_heads.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32]
+    lib.oracle_round_bf16.restype = None
+    lib.oracle_round_bf16.argtypes = [vp, vp, ctypes.c_size_t]
     _lib = lib
     return lib
 
@@ -224,3 +229,39 @@ def decode_layer(x, w_q, w_k, w_v, w_o, k_cache, v_cache, lens, scale: float, h:
     attn = store(attn64, x.dtype)
     y = linear(attn.reshape(b, h * d_v), w_o)
     return y, {"q": q, "k_new": k_new, "v_new": v_new, "attn": attn, "attn64": attn64}
+
+
+def round_bf16(values) -> np.ndarray:
+    """fp64 values rounded once to bf16 (nearest even), as uint16 bit patterns."""
+    values = np.ascontiguousarray(values, dtype=np.float64)
+    out = np.empty(values.shape, dtype=np.uint16)
+    _load().oracle_round_bf16(_ptr(out), _ptr(values), values.size)
+    return out
+
+
+def fold_heads(src, g_dst: int, lens=None, *, out=None, max_rows=None) -> np.ndarray:
+    """Mean-fold of contiguous groups of KV heads [GQA-lesson, merging the groups].
+
+    src [b, g_src, cap, d] (float32 or bf16 bits); lens int32 [b] (rows per
+    sequence) or None (all max_rows rows, default cap). Returns dst [b, g_dst,
+    cap_dst, d]: ``out`` if given (rows at or beyond each length untouched),
+    else a new zero array of src's capacity.
+    """
+    src = np.ascontiguousarray(src)
+    b, g_src, cap_src, d = src.shape
+    dt = _dtype_code(src)
+    if out is None:
+        out = np.zeros((b, g_dst, cap_src, d), dtype=src.dtype)
+    if not out.flags.c_contiguous or out.dtype != src.dtype or out.shape[0] != b or out.shape[1] != g_dst \
+            or out.shape[3] != d:
+        raise OracleError(ERR_ARG, "fold_heads output")
+    if lens is not None:
+        lens = np.ascontiguousarray(lens, dtype=np.int32)
+        if lens.shape != (b,):
+            raise OracleError(ERR_ARG, "fold_heads lens")
+    rows = int(max_rows) if max_rows is not None else (int(lens.max()) if lens is not None else cap_src)
+    rc = _load().oracle_fold_heads(_ptr(out), _ptr(src), _ptr(lens) if lens is not None else None, b, g_src,
+                                   g_dst, cap_src, out.shape[2], d, rows, dt)
+    if rc != OK:
+        raise OracleError(rc, "fold_heads")
+    return out

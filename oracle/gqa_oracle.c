@@ -268,3 +268,79 @@ void oracle_store(void* dst, const double* src, size_t n, int dtype) {
     ((uint16_t*)dst)[i] = h;
   }
 }
+
+/*
+ * A double rounded once to bf16 (8 significant bits, fp32's exponent range,
+ * subnormals down to 2^-133), nearest even; returned as the bf16 bit pattern.
+ * The value is scaled by a power of two so that its last kept bit is the
+ * units place, rounded to an integer by nearbyint (the default rounding
+ * mode, nearest even), and scaled back; both scalings are exact.
+ */
+static uint16_t double_to_bf16(double x) {
+  if (isnan(x)) return (uint16_t)0x7fc0u;
+  const uint16_t sign = signbit(x) ? (uint16_t)0x8000u : (uint16_t)0u;
+  const double a = fabs(x);
+  if (a == 0.0) return sign;
+  if (isinf(a)) return (uint16_t)(sign | 0x7f80u);
+  int e;
+  frexp(a, &e); /* a in [2^(e-1), 2^e) */
+  int lsb = e - 8;
+  if (lsb < -133) lsb = -133;
+  const double v = ldexp(nearbyint(ldexp(a, -lsb)), lsb);
+  if (v >= 0x1p128) return (uint16_t)(sign | 0x7f80u);
+  const float f = (float)v; /* exact: at most 8 significant bits, in fp32's range */
+  uint32_t u;
+  memcpy(&u, &f, sizeof u);
+  return (uint16_t)(sign | (u >> 16));
+}
+
+/*
+ * Mean-fold of KV heads: turn a cache (or a key/value projection) with g_src
+ * KV heads into one with g_dst heads by averaging each contiguous group of
+ * F = g_src / g_dst heads [GQA-lesson, on merging the groups of a trained
+ * multi-head model: the KV heads of a group are averaged, and the lab folds
+ * the KV heads of contiguous groups by their mean]:
+ *   dst[b][j][t][c] = (sum_{f<F} src[b][j*F + f][t][c]) / F
+ * for t < rows_b and c < d, the sum in head order in double, the quotient
+ * rounded once to the element type (nearest even). rows_b = lens[b] when
+ * lens is given, else max_rows for every b. Rows of dst from rows_b on are
+ * not written. src is [b][g_src][cap_src][d], dst is [b][g_dst][cap_dst][d].
+ * A projection matrix [g*d_k][d_model] is the case b = 1, cap = d_k, d =
+ * d_model, lens = NULL, max_rows = d_k.
+ */
+int oracle_fold_heads(void* dst, const void* src, const int32_t* lens, int b, int g_src, int g_dst, int cap_src,
+                      int cap_dst, int d, int max_rows, int dtype) {
+  if (!dst || !src || b <= 0 || g_src <= 0 || g_dst <= 0 || cap_src <= 0 || cap_dst <= 0 || d <= 0 ||
+      max_rows < 0)
+    return ORC_ERR_ARG;
+  if (dtype != ORC_F32 && dtype != ORC_BF16) return ORC_ERR_UNSUPPORTED;
+  if (g_src % g_dst != 0) return ORC_ERR_GROUPS;
+  if (max_rows > cap_src || max_rows > cap_dst) return ORC_ERR_CAPACITY;
+  if (lens)
+    for (int s = 0; s < b; ++s)
+      if (lens[s] < 0 || lens[s] > max_rows) return ORC_ERR_CAPACITY;
+  const int F = g_src / g_dst;
+#pragma omp parallel for collapse(2) schedule(static)
+  for (int s = 0; s < b; ++s) {
+    for (int j = 0; j < g_dst; ++j) {
+      const int rows = lens ? lens[s] : max_rows;
+      for (int t = 0; t < rows; ++t) {
+        for (int c = 0; c < d; ++c) {
+          double sum = 0.0;
+          for (int f = 0; f < F; ++f)
+            sum += widen(src, (((size_t)s * g_src + (size_t)j * F + f) * cap_src + t) * d + c, dtype);
+          const double mean = sum / F;
+          const size_t o = (((size_t)s * g_dst + j) * cap_dst + t) * d + c;
+          if (dtype == ORC_F32) ((float*)dst)[o] = (float)mean;
+          else ((uint16_t*)dst)[o] = double_to_bf16(mean);
+        }
+      }
+    }
+  }
+  return ORC_OK;
+}
+
+/* double_to_bf16 over an array (for its own pins). */
+void oracle_round_bf16(uint16_t* dst, const double* src, size_t n) {
+  for (size_t i = 0; i < n; ++i) dst[i] = double_to_bf16(src[i]);
+}
