@@ -30,7 +30,14 @@ consecutive sets, as a decode step walks the layers of a model. Its value is
 (weight bytes + KV bytes) per step over the step time, and its roofline is
 that of the whole layer (three launches).
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--layer]
+With --fold the step is the mean-fold of a multi-head cache to fewer KV
+heads (gqa_fold_kv_heads on K, then on V; default: the long MHA workload,
+g = 32 -> 8): value = bytes read and written per step over the step time.
+The line also carries the lesson's comparison at the same cache and queries:
+the relative change of the attention output against MHA for each folded g,
+and the decode time over each folded cache.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--layer | --fold]
 """
 from __future__ import annotations
 
@@ -107,6 +114,8 @@ def main():
                     help="run a 1 GiB device copy first (reference for HBM byte counters)")
     ap.add_argument("--layer", action="store_true",
                     help="time the whole decode layer (projections + step) instead of the step alone")
+    ap.add_argument("--fold", type=int, default=0, metavar="G",
+                    help="time the mean-fold of the workload's cache to G KV heads instead of the step")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -129,6 +138,8 @@ def main():
             print("--layer runs bf16 workloads with the fused step only", file=sys.stderr)
             sys.exit(2)
         return bench_layer(args, wl, dev)
+    if args.fold:
+        return bench_fold(args, WORKLOADS[args.workload or "mha_long_bf16_g32"], dev)
 
     # cache sets
     set_bytes = wl.b * wl.g * wl.cap * wl.d * 2 * wl.elem_bytes
@@ -381,6 +392,104 @@ def bench_layer(args, wl, dev):
             "kernel": "gqa_decode_layer (linear_bf16_kernel, fused decode step, linear_bf16_kernel)",
             "kernel_avg_us": round(step_ms * 1e3, 3),
         },
+        "cpu_baseline": None,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+def bench_fold(args, wl, dev):
+    """Mean-fold of a multi-head cache to fewer KV heads, and the output change it brings."""
+    import torch
+
+    from gqa_kv_cache_decode_amd import api, inputs
+    from gqa_kv_cache_decode_amd.workloads import kv_bytes_attended
+
+    g_dst = args.fold
+    if wl.g % g_dst != 0:
+        print(f"--fold {g_dst}: {wl.name} has g={wl.g}, not a multiple", file=sys.stderr)
+        sys.exit(2)
+    dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    batch = inputs.Batch(seed=wl.seed, b=wl.b, h=wl.h, g=wl.g, d=wl.d, cap=wl.cap, lens=wl.lens, dtype=wl.dtype,
+                         poison=False)
+    L = batch.lens.copy()  # attended lengths: the drawn cache as it is
+
+    def to_dev(a):
+        t = torch.from_numpy(a)
+        return (t.view(torch.bfloat16) if a.dtype == np.uint16 else t).to(dev)
+
+    kc, vc = to_dev(batch.k_cache), to_dev(batch.v_cache)
+    lens = torch.from_numpy(L.astype(np.int32)).to(dev)
+    rows = int(L.max())
+    q = to_dev(batch.q(0))
+    del batch
+    kf = torch.empty(wl.b, g_dst, wl.cap, wl.d, dtype=dt, device=dev)
+    vf = torch.empty_like(kf)
+    stream = torch.cuda.current_stream()
+
+    def fold(k_dst, v_dst):
+        api.fold_kv_heads(k_dst, kc, lens, rows)
+        api.fold_kv_heads(v_dst, vc, lens, rows)
+
+    for _ in range(args.warmup):
+        fold(kf, vf)
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(args.steps):
+        fold(kf, vf)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    step_ms = t0.elapsed_time(t1) / args.steps
+    e = wl.elem_bytes
+    bytes_step = 2 * (wl.g + g_dst) * int(L.sum()) * wl.d * e  # K and V: g_src rows read, g_dst written
+    value = bytes_step / (step_ms / 1e3) / 1e9
+    log(f"fold {wl.g} -> {g_dst}: {step_ms * 1e3:.1f} us per step (two launches)")
+
+    # the lesson's comparison at the same cache and queries
+    def attend(k, v, g):
+        out = torch.empty(wl.b, wl.h, wl.d, dtype=dt, device=dev)
+        ws = api.make_workspace(wl.b, wl.h, g, wl.d, wl.d, rows, dt, dev)
+        api.decode_attention(out, q, k, v, lens, rows, wl.scale, ws)
+        torch.cuda.synchronize()
+        a, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(10):
+            api.decode_attention(out, q, k, v, lens, rows, wl.scale, ws)
+        b_.record(stream)
+        torch.cuda.synchronize()
+        return out.float(), a.elapsed_time(b_) / 10 * 1e3
+
+    ref, ref_us = attend(kc, vc, wl.g)
+    report = {str(wl.g): {"rel_l2_change": 0.0, "decode_us": round(ref_us, 2),
+                          "kv_bytes": kv_bytes_attended(wl.g, wl.d, wl.d, e, L)}}
+    for g in sorted({g_dst, 1} | {x for x in (8, 4) if wl.g % x == 0 and x < wl.g}, reverse=True):
+        k2 = torch.empty(wl.b, g, wl.cap, wl.d, dtype=dt, device=dev)
+        v2 = torch.empty_like(k2)
+        fold(k2, v2)
+        out, us = attend(k2, v2, g)
+        report[str(g)] = {"rel_l2_change": round(float((out - ref).norm() / ref.norm()), 4),
+                          "decode_us": round(us, 2), "kv_bytes": kv_bytes_attended(g, wl.d, wl.d, e, L)}
+        del k2, v2
+    rec = {
+        "metric": "KV-head mean-fold GB/s (bytes read + written); output change vs MHA at the same cache",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": {"workload": f"{wl.name}_fold_to_g{g_dst}", "b": wl.b, "h": wl.h, "g_src": wl.g, "g_dst": g_dst,
+                   "d": wl.d, "attended_len": int(L.max()), "step_api": "gqa_fold_kv_heads (K, then V)",
+                   "bytes_per_step": bytes_step},
+        "roofline": {"bound": "hbm", "achieved": round(value, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(value / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "fold_heads_kernel",
+                     "kernel_avg_us": round(step_ms * 1e3 / 2, 3)},
+        "fold_report": report,
         "cpu_baseline": None,
     }
     print(json.dumps(rec), flush=True)

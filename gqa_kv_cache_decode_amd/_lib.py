@@ -50,6 +50,7 @@ SIGNATURES = {
     "gqa_pack_weight": (_i32, [_vp, _vp, _i32, _i32, _i32, _vp]),
     "gqa_linear": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp]),
     "gqa_decode_layer": (_i32, [_vp] * 13 + [_i32] * 8 + [_f32, _i32, _vp, _sz, _vp]),
+    "gqa_fold_kv_heads": (_i32, [_vp, _vp, _vp] + [_i32] * 8 + [_vp]),
     "gqa_last_error": (ctypes.c_char_p, []),
 }
 

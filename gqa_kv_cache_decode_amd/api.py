@@ -223,3 +223,31 @@ def decode_layer(y: torch.Tensor, x: torch.Tensor, w_q: PackedWeight, w_k: Packe
         _stream_handle(stream))
     _lib.check(rc, "gqa_decode_layer")
     return y
+
+
+def fold_kv_heads(dst: torch.Tensor, src: torch.Tensor, lens: torch.Tensor | None = None,
+                  max_rows: int | None = None, stream=None) -> torch.Tensor:
+    """Mean-fold of contiguous KV-head groups (C entry point gqa_fold_kv_heads).
+
+    src [b, g_src, cap_src, d] -> dst [b, g_dst, cap_dst, d], same dtype; rows t < lens[s]
+    (or < max_rows, default the smaller capacity, when lens is None).
+    """
+    _check_gpu(dst, src)
+    if src.dim() != 4 or dst.dim() != 4 or src.shape[0] != dst.shape[0] or src.shape[3] != dst.shape[3]:
+        raise ValueError("fold_kv_heads: src [b, g_src, cap, d] and dst [b, g_dst, cap, d] expected")
+    b, g_src, cap_src, d = src.shape
+    g_dst, cap_dst = dst.shape[1], dst.shape[2]
+    dt = _dtype_code(src)
+    if _dtype_code(dst) != dt:
+        raise TypeError("src and dst must share one element type")
+    lens_ptr = None
+    if lens is not None:
+        _check_gpu(lens)
+        if lens.dtype != torch.int32 or tuple(lens.shape) != (b,):
+            raise ValueError("lens must be int32 [b]")
+        lens_ptr = lens.data_ptr()
+    rows = min(cap_src, cap_dst) if max_rows is None else int(max_rows)
+    rc = _lib.load().gqa_fold_kv_heads(dst.data_ptr(), src.data_ptr(), lens_ptr, b, g_src, g_dst, cap_src, cap_dst,
+                                       d, rows, dt, _stream_handle(stream))
+    _lib.check(rc, "gqa_fold_kv_heads")
+    return dst

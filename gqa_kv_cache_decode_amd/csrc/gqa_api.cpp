@@ -350,6 +350,38 @@ size_t gqa_packed_weight_bytes(int n_out, int n_in) {
   return gqa::packed_weight_bytes(n_out, n_in);
 }
 
+int gqa_fold_kv_heads(void* dst, const void* src, const int32_t* lens, int b, int g_src, int g_dst, int cap_src,
+                      int cap_dst, int d, int max_rows, int dtype, void* stream) {
+  if (!dst || !src) return fail(GQA_ERR_ARG, "gqa_fold_kv_heads: null pointer argument");
+  if (b <= 0 || b > kMaxBatch || g_src <= 0 || g_dst <= 0 || g_dst > 65535 || cap_src <= 0 || cap_dst <= 0 ||
+      d <= 0 || max_rows < 0)
+    return fail(GQA_ERR_ARG, "gqa_fold_kv_heads: b=%d, g_src=%d, g_dst=%d, cap_src=%d, cap_dst=%d, d=%d, max_rows=%d",
+                b, g_src, g_dst, cap_src, cap_dst, d, max_rows);
+  if (dtype != GQA_DTYPE_F32 && dtype != GQA_DTYPE_BF16)
+    return fail(GQA_ERR_UNSUPPORTED, "gqa_fold_kv_heads: dtype=%d", dtype);
+  if (g_src % g_dst != 0)
+    return fail(GQA_ERR_GROUPS, "gqa_fold_kv_heads: g_src=%d is not a multiple of g_dst=%d", g_src, g_dst);
+  if (d % 8 != 0) return fail(GQA_ERR_UNSUPPORTED, "gqa_fold_kv_heads: d=%d must be a multiple of 8", d);
+  if (max_rows > cap_src || max_rows > cap_dst)
+    return fail(GQA_ERR_CAPACITY, "gqa_fold_kv_heads: max_rows=%d exceeds cap_src=%d or cap_dst=%d", max_rows,
+                cap_src, cap_dst);
+  if ((long long)max_rows * d / 2048 >= (1LL << 31))
+    return fail(GQA_ERR_ARG, "gqa_fold_kv_heads: max_rows * d too large");
+  if (!aligned16(dst) || !aligned16(src)) return fail(GQA_ERR_ARG, "gqa_fold_kv_heads: dst and src must be 16-byte aligned");
+  const size_t es = dtype == GQA_DTYPE_F32 ? 4 : 2;
+  const size_t src_bytes = size_t(b) * g_src * size_t(cap_src) * d * es;
+  const size_t dst_bytes = size_t(b) * g_dst * size_t(cap_dst) * d * es;
+  const char* sp = static_cast<const char*>(src);
+  const char* dp = static_cast<const char*>(dst);
+  if (dp < sp + src_bytes && sp < dp + dst_bytes)
+    return fail(GQA_ERR_ARG, "gqa_fold_kv_heads: dst and src overlap");
+  if (max_rows == 0) return ok();
+  const gqa::FoldParams p{dst, src, lens, g_src, g_dst, cap_src, cap_dst, d, max_rows};
+  const hipError_t e = gqa::launch_fold(p, b, dtype, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(GQA_ERR_HIP, "gqa_fold_kv_heads launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
 int gqa_pack_weight(void* dst, const void* src, int n_out, int n_in, int dtype, void* stream) {
   if (!dst || !src) return fail(GQA_ERR_ARG, "gqa_pack_weight: null pointer argument");
   if (n_out <= 0 || n_in <= 0) return fail(GQA_ERR_ARG, "gqa_pack_weight: n_out=%d, n_in=%d", n_out, n_in);

@@ -108,6 +108,15 @@ struct LinearParams {
   int blocks[3];
 };
 
+// dst[s][j][t][:] = mean of src[s][j*F + f][t][:] over f < F, t < rows_s
+// (rows_s = min(lens[s], max_rows), or max_rows without lens); d % 8 == 0.
+struct FoldParams {
+  void* dst;
+  const void* src;
+  const int32_t* lens;
+  int g_src, g_dst, cap_src, cap_dst, d, max_rows;
+};
+
 // Workspace layout, relative to the end of the caller's buffer so that a
 // buffer sized for one shape serves every smaller shape without the regions
 // of one call overlapping those of another: partial slots from the start,
@@ -151,6 +160,7 @@ hipError_t launch_merge_partials(const DecodeParams& p, int dtype, hipStream_t s
 hipError_t launch_linear(const LinearParams& p, hipStream_t stream);
 size_t packed_weight_bytes(int n_out, int n_in);
 hipError_t launch_pack_weight(void* dst, const void* src, int n_out, int n_in, hipStream_t stream);
+hipError_t launch_fold(const FoldParams& p, int b, int dtype, hipStream_t stream);
 
 // Workgroups of the decode kernel instance that fit on one compute unit at
 // once (runtime occupancy query, cached; 0 if the runtime cannot say).

@@ -244,6 +244,30 @@ int gqa_decode_layer(void* y, const void* x, const void* w_q, const void* w_k, c
                      int dtype, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Mean-fold of KV heads ("TF2 GQA" lesson, on moving a trained multi-head
+ * model to grouped-query attention: each contiguous group of key/value heads
+ * is replaced by its average; the lesson's lab folds them that way and
+ * compares the outputs at the same weights). With F = g_src / g_dst:
+ *   dst[s][j][t][c] = (sum_{f<F} src[s][j*F + f][t][c]) / F
+ * for s < b, j < g_dst, t < rows_s, c < d, where rows_s = lens[s] (device
+ * int32, clamped to [0, max_rows]) or max_rows for every s when lens is
+ * NULL. The sum runs in head order in double precision and the mean is
+ * rounded once to the element type (nearest even; a NaN becomes bf16
+ * 0x7fc0), so the result is bitwise reproducible.
+ * src [b][g_src][cap_src][d] and dst [b][g_dst][cap_dst][d], contiguous,
+ * 16-byte aligned, caller-owned device memory that must not overlap; rows of
+ * dst at or beyond rows_s are not written. Fold the K and the V cache with
+ * one call each. A key or value projection W [g*d_k][d_model] folds as b = 1,
+ * cap = max_rows = d_k, d = d_model, lens = NULL.
+ * Errors: null pointers, sizes <= 0 (max_rows < 0), misalignment or overlap
+ * GQA_ERR_ARG; g_src % g_dst != 0 GQA_ERR_GROUPS; d % 8 != 0 or another
+ * dtype GQA_ERR_UNSUPPORTED; max_rows > cap_src or cap_dst GQA_ERR_CAPACITY.
+ * max_rows = 0 enqueues nothing. Asynchronous on stream.
+ */
+int gqa_fold_kv_heads(void* dst, const void* src, const int32_t* lens, int b, int g_src, int g_dst, int cap_src,
+                      int cap_dst, int d, int max_rows, int dtype, void* stream);
+
+/*
  * Describe the launch gqa_decode_attention_ex would make on the current
  * device, without enqueueing anything: writes the chosen path
  * (GQA_PATH_VECTOR or GQA_PATH_MATRIX, OR-ed with the GQA_MERGE_* flag in

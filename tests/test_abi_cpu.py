@@ -207,3 +207,26 @@ def test_decode_layer_rejects(lib):
     assert call(h=60) == _lib.ERR_GROUPS
     assert call(ws_bytes=64) == _lib.ERR_WORKSPACE
     assert call(d=96) == _lib.ERR_UNSUPPORTED
+
+
+def test_fold_rejects(lib):
+    FAKE2 = ctypes.c_void_p(1 << 40)  # far from FAKE: no overlap
+
+    def call(**kw):
+        a = dict(dst=FAKE2, src=FAKE, lens=None, b=2, g_src=8, g_dst=2, cap_src=64, cap_dst=64, d=128, rows=64,
+                 dtype=_lib.BF16)
+        a.update(kw)
+        return lib.gqa_fold_kv_heads(a["dst"], a["src"], a["lens"], a["b"], a["g_src"], a["g_dst"], a["cap_src"],
+                                     a["cap_dst"], a["d"], a["rows"], a["dtype"], None)
+    assert call(rows=0) == _lib.OK  # nothing to fold: nothing is enqueued
+    assert call(g_dst=3, rows=0) == _lib.ERR_GROUPS
+    assert call(d=12, rows=0) == _lib.ERR_UNSUPPORTED
+    assert call(dtype=7, rows=0) == _lib.ERR_UNSUPPORTED
+    assert call(rows=65) == _lib.ERR_CAPACITY
+    assert call(cap_dst=32) == _lib.ERR_CAPACITY
+    assert call(rows=-1) == _lib.ERR_ARG
+    assert call(src=None) == _lib.ERR_ARG
+    assert call(b=0) == _lib.ERR_ARG
+    assert call(dst=FAKE, rows=0) == _lib.ERR_ARG  # the same buffer: overlap
+    assert call(dst=ctypes.c_void_p((1 << 40) + 8), rows=0) == _lib.ERR_ARG  # not 16-byte aligned
+    assert lib.gqa_last_error().decode() != ""
