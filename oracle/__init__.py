@@ -25,7 +25,8 @@ Pages the oracle follows (cited by title and section):
 
 Parity status: every function here is pinned by ``tests/test_oracle_pins.py``,
 ``tests/test_oracle_golden.py``, ``tests/test_oracle_layer.py`` and
-``tests/test_oracle_fold.py`` (no function is "parity unpinned").
+``tests/test_oracle_fold.py`` and ``tests/test_oracle_paged.py`` (no function
+is "parity unpinned").
 """
 from __future__ import annotations
 
@@ -98,6 +99,10 @@ def _load():
     lib.oracle_fold_heads.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32]
     lib.oracle_round_bf16.restype = None
     lib.oracle_round_bf16.argtypes = [vp, vp, ctypes.c_size_t]
+    lib.oracle_gather_paged.restype = i32
+    lib.oracle_gather_paged.argtypes = [vp, vp, vp, vp] + [i32] * 8
+    lib.oracle_kv_append_paged.restype = i32
+    lib.oracle_kv_append_paged.argtypes = [vp] * 6 + [i32] * 8
     _lib = lib
     return lib
 
@@ -265,3 +270,50 @@ def fold_heads(src, g_dst: int, lens=None, *, out=None, max_rows=None) -> np.nda
     if rc != OK:
         raise OracleError(rc, "fold_heads")
     return out
+
+
+def gather_paged(pool, table, lens, block_size: int, cap: int) -> np.ndarray:
+    """The contiguous cache [b, g, cap, d] a paged pool stands for (rows t < lens[s]; zeros after).
+
+    pool [num_blocks, g, block_size, d]; table int32 [b, max_blocks]: row t of
+    head j of sequence s is pool[table[s, t // block_size], j, t % block_size].
+    """
+    pool = np.ascontiguousarray(pool)
+    table = np.ascontiguousarray(table, dtype=np.int32)
+    lens = np.ascontiguousarray(lens, dtype=np.int32)
+    num_blocks, g, bs, d = pool.shape
+    if bs != block_size or table.ndim != 2 or lens.shape != (table.shape[0],):
+        raise OracleError(ERR_ARG, "gather_paged shapes")
+    b, max_blocks = table.shape
+    out = np.zeros((b, g, cap, d), dtype=pool.dtype)
+    rc = _load().oracle_gather_paged(_ptr(out), _ptr(pool), _ptr(table), _ptr(lens), b, g, block_size, max_blocks,
+                                     num_blocks, cap, d, _dtype_code(pool))
+    if rc != OK:
+        raise OracleError(rc, "gather_paged")
+    return out
+
+
+def kv_append_paged(k_pool, v_pool, k_new, v_new, lens, table) -> None:
+    """In place: each sequence's new rows go to position lens[s] of its paged cache; lens += 1."""
+    for a in (k_pool, v_pool, k_new, v_new, lens, table):
+        if not a.flags.c_contiguous:
+            raise ValueError("oracle arrays must be C-contiguous")
+    if lens.dtype != np.int32 or table.dtype != np.int32:
+        raise TypeError("lens and table must be int32")
+    num_blocks, g, bs, d_k = k_pool.shape
+    d_v = v_pool.shape[3]
+    b, max_blocks = table.shape
+    rc = _load().oracle_kv_append_paged(_ptr(k_pool), _ptr(v_pool), _ptr(k_new), _ptr(v_new), _ptr(lens),
+                                        _ptr(table), b, g, d_k, d_v, bs, max_blocks, num_blocks,
+                                        _dtype_code(k_pool))
+    if rc != OK:
+        raise OracleError(rc, "kv_append_paged")
+
+
+def decode_attention_paged(q, k_pool, v_pool, lens, table, scale: float, **kw):
+    """Attention over paged caches: the attention of decode_attention over the caches they stand for."""
+    bs = k_pool.shape[2]
+    cap = table.shape[1] * bs
+    k = gather_paged(k_pool, table, lens, bs, cap)
+    v = gather_paged(v_pool, table, lens, bs, cap)
+    return decode_attention(q, k, v, np.ascontiguousarray(lens, dtype=np.int32), scale, **kw)

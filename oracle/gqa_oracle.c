@@ -344,3 +344,78 @@ int oracle_fold_heads(void* dst, const void* src, const int32_t* lens, int b, in
 void oracle_round_bf16(uint16_t* dst, const double* src, size_t n) {
   for (size_t i = 0; i < n; ++i) dst[i] = double_to_bf16(src[i]);
 }
+
+/*
+ * Paged caches. The pages name block-table caches (the "LLM inference 05"
+ * notes point to vLLM's paged cache) but give no layout; the plain reading
+ * taken here: a pool of blocks of B positions, pool[n][j][r][c] holding row r
+ * of KV head j in block n, and a table [b][max_blocks] naming, for sequence
+ * s, the block of positions n*B .. n*B + B - 1. A paged cache stands for the
+ * contiguous cache whose row t of head j is pool[table[s][t / B]][j][t % B];
+ * attention over it is the attention above over that cache.
+ */
+
+/*
+ * Gather the rows t < lens[s] of every sequence from a pool into a
+ * contiguous cache dst [b][g][cap][d] (rows from lens[s] on are not
+ * written). ORC_ERR_ARG if a table entry needed is outside [0, num_blocks),
+ * ORC_ERR_CAPACITY if a length exceeds cap or max_blocks * B.
+ */
+int oracle_gather_paged(void* dst, const void* pool, const int32_t* table, const int32_t* lens, int b, int g,
+                        int block_size, int max_blocks, int num_blocks, int cap, int d, int dtype) {
+  if (!dst || !pool || !table || !lens || b <= 0 || g <= 0 || block_size <= 0 || max_blocks <= 0 ||
+      num_blocks <= 0 || cap <= 0 || d <= 0)
+    return ORC_ERR_ARG;
+  if (dtype != ORC_F32 && dtype != ORC_BF16) return ORC_ERR_UNSUPPORTED;
+  const size_t es = elem_size(dtype);
+  for (int s = 0; s < b; ++s) {
+    const int L = lens[s];
+    if (L < 0 || L > cap || (int64_t)L > (int64_t)max_blocks * block_size) return ORC_ERR_CAPACITY;
+    for (int t = 0; t < L; ++t) {
+      const int blk = table[(size_t)s * max_blocks + t / block_size];
+      if (blk < 0 || blk >= num_blocks) return ORC_ERR_ARG;
+    }
+  }
+  for (int s = 0; s < b; ++s)
+    for (int j = 0; j < g; ++j)
+      for (int t = 0; t < lens[s]; ++t) {
+        const int blk = table[(size_t)s * max_blocks + t / block_size];
+        const size_t src_row = ((size_t)blk * g + j) * block_size + t % block_size;
+        const size_t dst_row = ((size_t)s * g + j) * cap + t;
+        memcpy((char*)dst + dst_row * d * es, (const char*)pool + src_row * d * es, d * es);
+      }
+  return ORC_OK;
+}
+
+/*
+ * Append to a paged cache: the new rows of sequence s go to position lens[s]
+ * (row lens[s] % B of block table[s][lens[s] / B]) and the length grows by
+ * one [MQA-review §2.4; LLM-inf-05 decode pseudocode]. ORC_ERR_CAPACITY (and
+ * nothing changed) if a length is outside [0, max_blocks * B), ORC_ERR_ARG if
+ * the block it needs is outside the pool.
+ */
+int oracle_kv_append_paged(void* k_pool, void* v_pool, const void* k_new, const void* v_new, int32_t* lens,
+                           const int32_t* table, int b, int g, int d_k, int d_v, int block_size, int max_blocks,
+                           int num_blocks, int dtype) {
+  if (!k_pool || !v_pool || !k_new || !v_new || !lens || !table || b <= 0 || g <= 0 || d_k <= 0 || d_v <= 0 ||
+      block_size <= 0 || max_blocks <= 0 || num_blocks <= 0)
+    return ORC_ERR_ARG;
+  if (dtype != ORC_F32 && dtype != ORC_BF16) return ORC_ERR_UNSUPPORTED;
+  const size_t es = elem_size(dtype);
+  for (int s = 0; s < b; ++s) {
+    if (lens[s] < 0 || (int64_t)lens[s] >= (int64_t)max_blocks * block_size) return ORC_ERR_CAPACITY;
+    const int blk = table[(size_t)s * max_blocks + lens[s] / block_size];
+    if (blk < 0 || blk >= num_blocks) return ORC_ERR_ARG;
+  }
+  for (int s = 0; s < b; ++s) {
+    const int p = lens[s];
+    const int blk = table[(size_t)s * max_blocks + p / block_size];
+    for (int j = 0; j < g; ++j) {
+      const size_t row = ((size_t)blk * g + j) * block_size + p % block_size;
+      memcpy((char*)k_pool + row * d_k * es, (const char*)k_new + ((size_t)s * g + j) * d_k * es, d_k * es);
+      memcpy((char*)v_pool + row * d_v * es, (const char*)v_new + ((size_t)s * g + j) * d_v * es, d_v * es);
+    }
+    lens[s] = p + 1;
+  }
+  return ORC_OK;
+}
