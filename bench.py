@@ -37,7 +37,10 @@ The line also carries the lesson's comparison at the same cache and queries:
 the relative change of the attention output against MHA for each folded g,
 and the decode time over each folded cache.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--layer | --fold]
+With --paged B the caches live in pools of B-position blocks behind shuffled
+block tables (gqa_decode_step_paged); bytes and timing as for the step.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--paged B] [--layer | --fold G]
 """
 from __future__ import annotations
 
@@ -114,6 +117,8 @@ def main():
                     help="run a 1 GiB device copy first (reference for HBM byte counters)")
     ap.add_argument("--layer", action="store_true",
                     help="time the whole decode layer (projections + step) instead of the step alone")
+    ap.add_argument("--paged", type=int, default=0, metavar="B",
+                    help="keep the caches in pools of B-position blocks behind shuffled block tables")
     ap.add_argument("--fold", type=int, default=0, metavar="G",
                     help="time the mean-fold of the workload's cache to G KV heads instead of the step")
     args = ap.parse_args()
@@ -152,6 +157,22 @@ def main():
         t = torch.from_numpy(a)
         return (t.view(torch.bfloat16) if a.dtype == np.uint16 else t).to(dev)
 
+    def to_pool(cache, bs, seed):
+        # every block of every sequence to a random place in one pool (block table [b, max_blocks])
+        b, g, cap, d = cache.shape
+        mb = (cap + bs - 1) // bs
+        gen = torch.Generator(device="cpu").manual_seed(seed)
+        perm = torch.randperm(b * mb, generator=gen).to(torch.int32)
+        pool = torch.empty(b * mb, g, bs, d, dtype=cache.dtype, device=dev)
+        padded = torch.zeros(b, g, mb * bs, d, dtype=cache.dtype, device=dev)
+        padded[:, :, :cap] = cache
+        pool[perm.long().to(dev)] = padded.view(b, g, mb, bs, d).permute(0, 2, 1, 3, 4).reshape(b * mb, g, bs, d)
+        del padded, cache
+        return pool, perm.view(b, mb).to(dev)
+
+    if args.paged and (args.unfused or args.paged < 32 or args.paged & (args.paged - 1)):
+        print("--paged B: B a power of two >= 32, fused step only", file=sys.stderr)
+        sys.exit(2)
     sets = []
     host0 = None
     for r in range(n_sets):
@@ -167,7 +188,11 @@ def main():
         })
         if r != 0:
             del batch
-    log("caches resident")
+        if args.paged:
+            st = sets[-1]
+            st["kc"], st["table"] = to_pool(st["kc"], args.paged, wl.seed + r)
+            st["vc"], _ = to_pool(st["vc"], args.paged, wl.seed + r)
+    log("caches resident" + (f" as pools of {args.paged}-position blocks" if args.paged else ""))
     cap = wl.cap + grow
     max_len_bound = int(max(s["lens_h"].max() for s in sets)) + grow
     ws = api.make_workspace(wl.b, wl.h, wl.g, wl.d, wl.d, max_len_bound, dt, dev)
@@ -199,6 +224,9 @@ def main():
         if args.unfused:
             api.decode_attention(out, qs[i % len(qs)], st["kc"], st["vc"], st["lens"], max_len + 1, wl.scale, ws,
                                  path=args.path, workgroups=args.workgroups)
+        elif args.paged:
+            api.decode_step_paged(out, qs[i % len(qs)], kn, vn, st["kc"], st["vc"], st["lens"], st["table"], max_len,
+                                  wl.scale, ws)
         else:
             api.decode_step(out, qs[i % len(qs)], kn, vn, st["kc"], st["vc"], st["lens"], max_len, wl.scale, ws,
                             path=args.path, workgroups=args.workgroups)
@@ -243,7 +271,7 @@ def main():
     achieved = bytes_per_launch / (kern_avg_ms / 1e3) / 1e9
     plan_path, plan_wgs, plan_merge = api.plan(wl.b, wl.h, wl.g, wl.d, wl.d, cap, max_len_bound, dt, args.path,
                                                args.workgroups)
-    traffic = traffic_from_profile(wl.name)
+    traffic = None if args.paged else traffic_from_profile(wl.name)
 
     cpu = None
     if args.cpu_seconds > 0:
@@ -267,13 +295,15 @@ def main():
         "dtype": wl.dtype,
         "data": "synthetic",
         "config": {
-            "workload": wl.name, "b": wl.b, "h": wl.h, "g": wl.g, "d_k": wl.d, "d_v": wl.d,
+            "workload": wl.name + (f"_paged_blocks{args.paged}" if args.paged else ""),
+            "b": wl.b, "h": wl.h, "g": wl.g, "d_k": wl.d, "d_v": wl.d,
             "lens": list(wl.lens) if isinstance(wl.lens, (list, tuple)) else wl.lens,
             "lens_drawn_mean": float(lens0.mean()), "lens_drawn_min": int(lens0.min()),
             "lens_drawn_max": int(lens0.max()), "cache_sets": n_sets, "seed": wl.seed,
             "path": {1: "vector", 2: "matrix"}[plan_path], "workgroups": plan_wgs,
             "split_merge": "second launch" if plan_merge == api.MERGE_KERNEL else "in the decode kernel",
-            "step_api": "gqa_kv_append + gqa_decode_attention" if args.unfused else "gqa_decode_step",
+            "step_api": ("gqa_kv_append + gqa_decode_attention" if args.unfused else
+                         f"gqa_decode_step_paged (blocks of {args.paged})" if args.paged else "gqa_decode_step"),
             "kv_bytes_per_step": int(bytes_per_launch),
         },
         "roofline": {
@@ -281,7 +311,7 @@ def main():
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
             "kernel": ("decode_matrix_kernel" if plan_path == 2 else "decode_vector_kernel")
                       + (" + merge_partials_kernel" if plan_merge == api.MERGE_KERNEL else "")
-                      + ("" if args.unfused else " (fused step)"),
+                      + ("" if args.unfused else " (fused step)") + (", paged" if args.paged else ""),
             "kernel_avg_us": round(kern_avg_ms * 1e3, 3),
         },
         "cpu_baseline": cpu,

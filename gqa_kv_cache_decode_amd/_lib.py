@@ -51,6 +51,9 @@ SIGNATURES = {
     "gqa_linear": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp]),
     "gqa_decode_layer": (_i32, [_vp] * 13 + [_i32] * 8 + [_f32, _i32, _vp, _sz, _vp]),
     "gqa_fold_kv_heads": (_i32, [_vp, _vp, _vp] + [_i32] * 8 + [_vp]),
+    "gqa_kv_append_paged": (_i32, [_vp] * 6 + [_i32] * 9 + [_vp]),
+    "gqa_decode_attention_paged": (_i32, [_vp] * 6 + [_i32] * 9 + [_f32, _i32, _vp, _sz, _vp]),
+    "gqa_decode_step_paged": (_i32, [_vp] * 8 + [_i32] * 9 + [_f32, _i32, _vp, _sz, _vp]),
     "gqa_last_error": (ctypes.c_char_p, []),
 }
 

@@ -251,3 +251,70 @@ def fold_kv_heads(dst: torch.Tensor, src: torch.Tensor, lens: torch.Tensor | Non
                                        d, rows, dt, _stream_handle(stream))
     _lib.check(rc, "gqa_fold_kv_heads")
     return dst
+
+
+def _paged_args(k_pool: torch.Tensor, v_pool: torch.Tensor, table: torch.Tensor, lens: torch.Tensor):
+    _check_gpu(k_pool, v_pool, table, lens)
+    if table.dtype != torch.int32 or lens.dtype != torch.int32 or table.dim() != 2:
+        raise TypeError("block table [b, max_blocks] and lens [b] must be int32")
+    num_blocks, g, bs, d_k = k_pool.shape
+    if tuple(v_pool.shape[:3]) != (num_blocks, g, bs):
+        raise ValueError("k_pool and v_pool must share [num_blocks, g, block_size]")
+    b, max_blocks = table.shape
+    if tuple(lens.shape) != (b,):
+        raise ValueError("lens must be [b]")
+    return b, g, d_k, v_pool.shape[3], bs, max_blocks, num_blocks
+
+
+def kv_append_paged(k_pool: torch.Tensor, v_pool: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                    lens: torch.Tensor, block_table: torch.Tensor, max_len: int, stream=None) -> None:
+    """Store k_new / v_new [b, g, d] at position lens[s] of each paged cache; lens += 1."""
+    b, g, d_k, d_v, bs, mb, nb = _paged_args(k_pool, v_pool, block_table, lens)
+    _check_gpu(k_pool, k_new, v_new)
+    if tuple(k_new.shape) != (b, g, d_k) or tuple(v_new.shape) != (b, g, d_v):
+        raise ValueError("kv_append_paged: k_new [b, g, d_k] and v_new [b, g, d_v] expected")
+    if any(_dtype_code(t) != _dtype_code(k_pool) for t in (v_pool, k_new, v_new)):
+        raise TypeError("pools and new rows must share one element type")
+    rc = _lib.load().gqa_kv_append_paged(k_pool.data_ptr(), v_pool.data_ptr(), k_new.data_ptr(), v_new.data_ptr(),
+                                         lens.data_ptr(), block_table.data_ptr(), b, g, d_k, d_v, bs, mb, nb,
+                                         int(max_len), _dtype_code(k_pool), _stream_handle(stream))
+    _lib.check(rc, "gqa_kv_append_paged")
+
+
+def decode_attention_paged(out: torch.Tensor, q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
+                           lens: torch.Tensor, block_table: torch.Tensor, max_len: int, scale: float,
+                           workspace: torch.Tensor, stream=None) -> torch.Tensor:
+    """Attention of q [b, h, d_k] over paged caches (pools [num_blocks, g, B, d], table [b, max_blocks])."""
+    b, g, d_k, d_v, bs, mb, nb = _paged_args(k_pool, v_pool, block_table, lens)
+    _check_gpu(k_pool, out, q, workspace)
+    h = q.shape[1]
+    if tuple(q.shape) != (b, h, d_k) or tuple(out.shape) != (b, h, d_v):
+        raise ValueError("decode_attention_paged: q [b, h, d_k] and out [b, h, d_v] expected")
+    if any(_dtype_code(t) != _dtype_code(q) for t in (k_pool, v_pool, out)):
+        raise TypeError("q, pools and out must share one element type")
+    rc = _lib.load().gqa_decode_attention_paged(
+        out.data_ptr(), q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), lens.data_ptr(), block_table.data_ptr(),
+        b, h, g, d_k, d_v, bs, mb, nb, int(max_len), float(scale), _dtype_code(q), workspace.data_ptr(),
+        workspace.numel() * workspace.element_size(), _stream_handle(stream))
+    _lib.check(rc, "gqa_decode_attention_paged")
+    return out
+
+
+def decode_step_paged(out: torch.Tensor, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                      k_pool: torch.Tensor, v_pool: torch.Tensor, lens: torch.Tensor, block_table: torch.Tensor,
+                      max_len: int, scale: float, workspace: torch.Tensor, stream=None) -> torch.Tensor:
+    """Append + attention in one launch on paged caches (max_len: bound of the pre-append lengths)."""
+    b, g, d_k, d_v, bs, mb, nb = _paged_args(k_pool, v_pool, block_table, lens)
+    _check_gpu(k_pool, out, q, k_new, v_new, workspace)
+    h = q.shape[1]
+    if tuple(q.shape) != (b, h, d_k) or tuple(out.shape) != (b, h, d_v) or tuple(k_new.shape) != (b, g, d_k) \
+            or tuple(v_new.shape) != (b, g, d_v):
+        raise ValueError("decode_step_paged: inconsistent shapes")
+    if any(_dtype_code(t) != _dtype_code(q) for t in (k_pool, v_pool, out, k_new, v_new)):
+        raise TypeError("q, rows, pools and out must share one element type")
+    rc = _lib.load().gqa_decode_step_paged(
+        out.data_ptr(), q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
+        lens.data_ptr(), block_table.data_ptr(), b, h, g, d_k, d_v, bs, mb, nb, int(max_len), float(scale),
+        _dtype_code(q), workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream_handle(stream))
+    _lib.check(rc, "gqa_decode_step_paged")
+    return out

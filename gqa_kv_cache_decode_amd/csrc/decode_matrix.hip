@@ -188,7 +188,9 @@ __device__ __forceinline__ void tile_step(WaveState<NB>& st, const bf16x8 (&qop)
 // arbitration) and the unit's work ends with it, while the eight waves of one
 // workgroup share each piece and meet at its barriers. WAVES = 4: the larger
 // head blocks, whose register needs allow one 4-wave workgroup per unit.
-template <int NB, bool FUSED, int WAVES>
+// PAGED: K/V live in block pools addressed through the block table (one
+// lookup per 32-position tile); otherwise in contiguous [b][g][cap][d] caches.
+template <int NB, bool FUSED, int WAVES, bool PAGED>
 __global__ __launch_bounds__(WAVES * 64, (NB == 1 && WAVES == 4) ? 2 : 1) void decode_matrix_kernel(DecodeParams p) {
   constexpr int THREADS = WAVES * 64;
   __shared__ float sm_m[WAVES][16];
@@ -248,19 +250,30 @@ __global__ __launch_bounds__(WAVES * 64, (NB == 1 && WAVES == 4) ? 2 : 1) void d
     for (int tile = pc.tile_begin + w; tile < pc.tile_end; tile += WAVES) {
       const int t0 = tile * kTile;
       const int nvalid = t_end - t0;
+      // rows of this tile: kb/vb + (tb + r) * D, r < 32
+      const uint16_t* kb = kbase;
+      const uint16_t* vb = vbase;
+      int tb = t0;
+      if constexpr (PAGED) {
+        const size_t row = kv_row<true, true>(p.pg, p.g, p.cap, s, j, t0);
+        kb = static_cast<const uint16_t*>(p.k_cache) + row * D;
+        vb = static_cast<const uint16_t*>(p.v_cache) + row * D;
+        tb = 0;
+      }
       if (FUSED && pos_new >= t0 && pos_new < t0 + kTile) {
         // the segment's last tile: take the new row from k_new / v_new and store it
         NewRow nr;
         nr.local = pos_new - t0;
         nr.k = static_cast<const uint16_t*>(p.k_new) + kv_head * D;
         nr.v = static_cast<const uint16_t*>(p.v_new) + kv_head * D;
-        nr.kdst = static_cast<uint16_t*>(p.k_cache) + (kv_head * p.cap + pos_new) * D;
-        nr.vdst = static_cast<uint16_t*>(p.v_cache) + (kv_head * p.cap + pos_new) * D;
-        tile_step<NB, false, true>(st, qop, kbase, vbase, t0, nvalid, sl2, n16, q4, nr);
+        const size_t new_row = kv_row<PAGED, true>(p.pg, p.g, p.cap, s, j, pos_new);
+        nr.kdst = static_cast<uint16_t*>(p.k_cache) + new_row * D;
+        nr.vdst = static_cast<uint16_t*>(p.v_cache) + new_row * D;
+        tile_step<NB, false, true>(st, qop, kb, vb, tb, nvalid, sl2, n16, q4, nr);
       } else if (nvalid >= kTile) {
-        tile_step<NB, true, false>(st, qop, kbase, vbase, t0, kTile, sl2, n16, q4, NewRow{});
+        tile_step<NB, true, false>(st, qop, kb, vb, tb, kTile, sl2, n16, q4, NewRow{});
       } else {
-        tile_step<NB, false, false>(st, qop, kbase, vbase, t0, nvalid, sl2, n16, q4, NewRow{});
+        tile_step<NB, false, false>(st, qop, kb, vb, tb, nvalid, sl2, n16, q4, NewRow{});
       }
       dfr.take_if_due(p, w);
     }
@@ -322,46 +335,50 @@ __global__ __launch_bounds__(WAVES * 64, (NB == 1 && WAVES == 4) ? 2 : 1) void d
   if (FUSED) finish_step(p, &s_flag);
 }
 
-template <bool FUSED>
+template <bool FUSED, bool PAGED>
 void launch_nb(const DecodeParams& p, hipStream_t stream) {
   const dim3 grid(p.workgroups);
   if (p.G <= 16) {
-    hipLaunchKernelGGL((decode_matrix_kernel<1, FUSED, kMatrixWaves1>), grid, dim3(kMatrixWaves1 * 64), 0, stream, p);
+    hipLaunchKernelGGL((decode_matrix_kernel<1, FUSED, kMatrixWaves1, PAGED>), grid, dim3(kMatrixWaves1 * 64), 0,
+                       stream, p);
   } else if (p.G <= 32) {
-    hipLaunchKernelGGL((decode_matrix_kernel<2, FUSED, 4>), grid, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((decode_matrix_kernel<2, FUSED, 4, PAGED>), grid, dim3(256), 0, stream, p);
   } else {
-    hipLaunchKernelGGL((decode_matrix_kernel<4, FUSED, 4>), grid, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((decode_matrix_kernel<4, FUSED, 4, PAGED>), grid, dim3(256), 0, stream, p);
   }
 }
 
 }  // namespace
 
 hipError_t launch_decode_matrix(const DecodeParams& p, hipStream_t stream) {
-  if (p.fused) launch_nb<true>(p, stream);
-  else launch_nb<false>(p, stream);
+  const bool paged = p.pg.table != nullptr;
+  if (p.fused) paged ? launch_nb<true, true>(p, stream) : launch_nb<true, false>(p, stream);
+  else paged ? launch_nb<false, true>(p, stream) : launch_nb<false, false>(p, stream);
   return hipGetLastError();
 }
 
 namespace {
-template <bool FUSED>
+template <bool FUSED, bool PAGED>
 hipError_t occupancy(int k, int* n) {
   if (k == 0)
-    return hipOccupancyMaxActiveBlocksPerMultiprocessor(n, decode_matrix_kernel<1, FUSED, kMatrixWaves1>,
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(n, decode_matrix_kernel<1, FUSED, kMatrixWaves1, PAGED>,
                                                         kMatrixWaves1 * 64, 0);
-  if (k == 1) return hipOccupancyMaxActiveBlocksPerMultiprocessor(n, decode_matrix_kernel<2, FUSED, 4>, 256, 0);
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(n, decode_matrix_kernel<4, FUSED, 4>, 256, 0);
+  if (k == 1)
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(n, decode_matrix_kernel<2, FUSED, 4, PAGED>, 256, 0);
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(n, decode_matrix_kernel<4, FUSED, 4, PAGED>, 256, 0);
 }
 }  // namespace
 
 int matrix_waves(int G) { return G <= 16 ? kMatrixWaves1 : 4; }
 
-int matrix_workgroups_per_cu(int G, bool fused) {
-  static int cached[2][3] = {};
+int matrix_workgroups_per_cu(int G, bool fused, bool paged) {
+  static int cached[2][2][3] = {};
   const int k = G <= 16 ? 0 : (G <= 32 ? 1 : 2);
-  int& c = cached[fused ? 1 : 0][k];
+  int& c = cached[paged ? 1 : 0][fused ? 1 : 0][k];
   if (c > 0) return c;
   int n = 0;
-  const hipError_t e = fused ? occupancy<true>(k, &n) : occupancy<false>(k, &n);
+  const hipError_t e = fused ? (paged ? occupancy<true, true>(k, &n) : occupancy<true, false>(k, &n))
+                             : (paged ? occupancy<false, true>(k, &n) : occupancy<false, false>(k, &n));
   if (e != hipSuccess || n <= 0) {
     (void)hipGetLastError();
     return 0;

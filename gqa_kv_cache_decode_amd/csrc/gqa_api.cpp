@@ -71,7 +71,7 @@ int gblk_bound(int G) {
 // callers). Fills plan on success. workgroups: 0 = one per resident slot of
 // the device (compute units x workgroups that fit per unit, at most two).
 int plan_decode(int b, int h, int g, int d_k, int d_v, int cap, int max_len, int dtype, int path,
-                int workgroups, Plan* plan, bool fused = false) {
+                int workgroups, Plan* plan, bool fused = false, bool paged = false) {
   if (b <= 0 || b > kMaxBatch) return fail(GQA_ERR_ARG, "b=%d must be in [1, %d]", b, kMaxBatch);
   if (h <= 0 || h > kMaxHeads) return fail(GQA_ERR_ARG, "h=%d must be in [1, %d]", h, kMaxHeads);
   if (g <= 0) return fail(GQA_ERR_ARG, "g=%d must be positive", g);
@@ -124,8 +124,8 @@ int plan_decode(int b, int h, int g, int d_k, int d_v, int cap, int max_len, int
     // Up to eight waves per compute unit (two 4-wave workgroups or one
     // 8-wave one keep enough loads in flight), never more than fit at once, so
     // the persistent grid runs in a single round.
-    int fit = chosen == GQA_PATH_MATRIX ? gqa::matrix_workgroups_per_cu(G, fused)
-                                        : gqa::vector_workgroups_per_cu(dtype, d_k, plan->gblk, fused);
+    int fit = chosen == GQA_PATH_MATRIX ? gqa::matrix_workgroups_per_cu(G, fused, paged)
+                                        : gqa::vector_workgroups_per_cu(dtype, d_k, plan->gblk, fused, paged);
     if (fit <= 0) fit = 2;  // no device to ask: assume the common case
     const int per_cu_max = 8 / waves;
     const int per_cu = fit < per_cu_max ? fit : per_cu_max;
@@ -179,7 +179,7 @@ int gqa_kv_append(void* k_cache, void* v_cache, const void* k_new, const void* v
     return fail(GQA_ERR_UNSUPPORTED, "dtype=%d is not GQA_DTYPE_F32 or GQA_DTYPE_BF16", dtype);
   if ((long long)max_len + 1 > cap)
     return fail(GQA_ERR_CAPACITY, "appending to max_len=%d needs cap > %d, cap=%d", max_len, max_len, cap);
-  gqa::AppendParams p{k_cache, v_cache, k_new, v_new, lens, g, d_k, d_v, cap};
+  gqa::AppendParams p{k_cache, v_cache, k_new, v_new, lens, g, d_k, d_v, cap, gqa::PagedLayout{nullptr, 0, 0, 0}};
   const hipError_t e = gqa::launch_append(p, b, dtype, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(GQA_ERR_HIP, "gqa_kv_append launch: %s", hipGetErrorString(e));
   return ok();
@@ -212,9 +212,11 @@ namespace {
 int decode_prepare(const char* fn, void* out, const void* q, void* k_cache, void* v_cache, int32_t* lens,
                    const void* k_new, const void* v_new, int b, int h, int g, int d_k, int d_v, int cap,
                    int max_len_att, float scale, int dtype, void* workspace, size_t workspace_bytes, int path,
-                   int workgroups, int fused, gqa::DecodeParams* pp, Plan* planp) {
+                   int workgroups, int fused, gqa::DecodeParams* pp, Plan* planp,
+                   const gqa::PagedLayout* paged = nullptr) {
   Plan& plan = *planp;
-  const int rc = plan_decode(b, h, g, d_k, d_v, cap, max_len_att, dtype, path, workgroups, &plan, fused != 0);
+  const int rc = plan_decode(b, h, g, d_k, d_v, cap, max_len_att, dtype, path, workgroups, &plan, fused != 0,
+                             paged != nullptr);
   if (rc != GQA_OK) return rc;
   const gqa::WorkspaceLayout ws = gqa::workspace_layout(b, h, gblk_bound(h / g), d_v);
   if (!workspace) return fail(GQA_ERR_WORKSPACE, "%s: workspace is null (%zu bytes needed)", fn, ws.total);
@@ -257,6 +259,7 @@ int decode_prepare(const char* fn, void* out, const void* q, void* k_cache, void
   // measured neutral or slower.
   p.seg_lead = (plan.path == GQA_PATH_MATRIX && gqa::matrix_waves(p.G) == 8) ? kSegmentLead : 0;
   p.scale_log2 = scale * kLog2e;
+  p.pg = paged ? *paged : gqa::PagedLayout{nullptr, 0, 0, 0};
 
   return GQA_OK;
 }
@@ -452,6 +455,98 @@ int gqa_decode_layer(void* y, const void* x, const void* w_q, const void* w_k, c
   e = gqa::launch_linear(out, st);
   if (e != hipSuccess) return fail(GQA_ERR_HIP, "gqa_decode_layer output projection launch: %s", hipGetErrorString(e));
   return ok();
+}
+
+}  // extern "C"
+
+namespace {
+
+// Checks of a paged layout; fills pg and the positions one sequence can hold.
+int paged_check(const char* fn, const int32_t* table, int b, int block_size, int max_blocks, int num_blocks,
+                gqa::PagedLayout* pg, int* cap) {
+  if (!table) return fail(GQA_ERR_ARG, "%s: block_table is null", fn);
+  if (max_blocks <= 0 || num_blocks <= 0)
+    return fail(GQA_ERR_ARG, "%s: max_blocks=%d, num_blocks=%d must be positive", fn, max_blocks, num_blocks);
+  if (block_size < gqa::kTile || block_size > (1 << 20) || (block_size & (block_size - 1)) != 0)
+    return fail(GQA_ERR_UNSUPPORTED, "%s: block_size=%d must be a power of two in [%d, 2^20]", fn, block_size,
+                gqa::kTile);
+  if (b > 0 && (long long)b * max_blocks >= (1LL << 31))
+    return fail(GQA_ERR_ARG, "%s: the block table (b=%d x max_blocks=%d) is too large", fn, b, max_blocks);
+  int lg = 0;
+  while ((1 << lg) < block_size) ++lg;
+  *pg = gqa::PagedLayout{table, max_blocks, lg, num_blocks};
+  const long long c = (long long)max_blocks * block_size;
+  *cap = c > INT32_MAX ? INT32_MAX : int(c);
+  return GQA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gqa_kv_append_paged(void* k_pool, void* v_pool, const void* k_new, const void* v_new, int32_t* lens,
+                        const int32_t* block_table, int b, int g, int d_k, int d_v, int block_size, int max_blocks,
+                        int num_blocks, int max_len, int dtype, void* stream) {
+  if (!k_pool || !v_pool || !k_new || !v_new || !lens)
+    return fail(GQA_ERR_ARG, "gqa_kv_append_paged: null pointer argument");
+  if (b <= 0 || b > kMaxBatch) return fail(GQA_ERR_ARG, "b=%d must be in [1, %d]", b, kMaxBatch);
+  if (g <= 0 || d_k <= 0 || d_v <= 0) return fail(GQA_ERR_ARG, "g=%d, d_k=%d, d_v=%d must be positive", g, d_k, d_v);
+  gqa::PagedLayout pg;
+  int cap = 0;
+  int rc = paged_check("gqa_kv_append_paged", block_table, b, block_size, max_blocks, num_blocks, &pg, &cap);
+  if (rc != GQA_OK) return rc;
+  if (max_len < 0) return fail(GQA_ERR_ARG, "max_len=%d must be >= 0", max_len);
+  if (dtype != GQA_DTYPE_F32 && dtype != GQA_DTYPE_BF16)
+    return fail(GQA_ERR_UNSUPPORTED, "dtype=%d is not GQA_DTYPE_F32 or GQA_DTYPE_BF16", dtype);
+  if ((long long)max_len + 1 > cap)
+    return fail(GQA_ERR_CAPACITY, "appending to max_len=%d needs max_blocks * block_size > %d, have %d", max_len,
+                max_len, cap);
+  gqa::AppendParams p{k_pool, v_pool, k_new, v_new, lens, g, d_k, d_v, cap, pg};
+  const hipError_t e = gqa::launch_append(p, b, dtype, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(GQA_ERR_HIP, "gqa_kv_append_paged launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int gqa_decode_attention_paged(void* out, const void* q, const void* k_pool, const void* v_pool,
+                               const int32_t* lens, const int32_t* block_table, int b, int h, int g, int d_k,
+                               int d_v, int block_size, int max_blocks, int num_blocks, int max_len, float scale,
+                               int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!out || !q || !k_pool || !v_pool || !lens)
+    return fail(GQA_ERR_ARG, "gqa_decode_attention_paged: null pointer argument");
+  gqa::PagedLayout pg;
+  int cap = 0;
+  int rc = paged_check("gqa_decode_attention_paged", block_table, b, block_size, max_blocks, num_blocks, &pg, &cap);
+  if (rc != GQA_OK) return rc;
+  gqa::DecodeParams p;
+  Plan plan;
+  rc = decode_prepare("gqa_decode_attention_paged", out, q, const_cast<void*>(k_pool), const_cast<void*>(v_pool),
+                      const_cast<int32_t*>(lens), nullptr, nullptr, b, h, g, d_k, d_v, cap, max_len, scale, dtype,
+                      workspace, workspace_bytes, GQA_PATH_AUTO, 0, 0, &p, &plan, &pg);
+  if (rc != GQA_OK) return rc;
+  return decode_launch("gqa_decode_attention_paged", p, plan, dtype, stream);
+}
+
+int gqa_decode_step_paged(void* out, const void* q, const void* k_new, const void* v_new, void* k_pool,
+                          void* v_pool, int32_t* lens, const int32_t* block_table, int b, int h, int g, int d_k,
+                          int d_v, int block_size, int max_blocks, int num_blocks, int max_len, float scale,
+                          int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!out || !q || !k_new || !v_new || !k_pool || !v_pool || !lens)
+    return fail(GQA_ERR_ARG, "gqa_decode_step_paged: null pointer argument");
+  gqa::PagedLayout pg;
+  int cap = 0;
+  int rc = paged_check("gqa_decode_step_paged", block_table, b, block_size, max_blocks, num_blocks, &pg, &cap);
+  if (rc != GQA_OK) return rc;
+  if (max_len < 0) return fail(GQA_ERR_ARG, "max_len=%d must be >= 0", max_len);
+  if ((long long)max_len + 1 > cap)
+    return fail(GQA_ERR_CAPACITY, "appending to max_len=%d needs max_blocks * block_size > %d, have %d", max_len,
+                max_len, cap);
+  if (max_len == INT32_MAX) return fail(GQA_ERR_CAPACITY, "max_len=%d too large", max_len);
+  gqa::DecodeParams p;
+  Plan plan;
+  rc = decode_prepare("gqa_decode_step_paged", out, q, k_pool, v_pool, lens, k_new, v_new, b, h, g, d_k, d_v, cap,
+                      max_len + 1, scale, dtype, workspace, workspace_bytes, GQA_PATH_AUTO, 0, 1, &p, &plan, &pg);
+  if (rc != GQA_OK) return rc;
+  return decode_launch("gqa_decode_step_paged", p, plan, dtype, stream);
 }
 
 int gqa_decode_attention(void* out, const void* q, const void* k_cache, const void* v_cache,

@@ -42,6 +42,13 @@
 //   [done]   int32 in the last 256 bytes                      zero between calls
 // slot_floats = gb*d + round_up(2*gb, 4), so every slot and its o block are
 // 16-byte aligned. Each region starts on a 256-byte boundary.
+//
+// Cache layouts. Contiguous: K [b][g][cap][d_k], V [b][g][cap][d_v]. Paged:
+// pools K [num_blocks][g][B][d_k], V [num_blocks][g][B][d_v] of blocks of B =
+// 2^bs_log2 >= 32 positions, and a block table int32 [b][table_stride]:
+// position t of sequence s lives in block table[s][t >> bs_log2] at row
+// t & (B - 1). A 32-position tile never straddles two blocks, so the kernels
+// look the block up once per tile; everything else is shared.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -58,6 +65,14 @@ constexpr int kMaxWorkgroups = 2048;  // persistent grid bound (workspace sizing
 constexpr int kMatrixMaxGroup = 64;   // query heads per KV head on the matrix path
 constexpr int kVectorMaxBlock = 8;    // query heads per workgroup on the vector path
 
+// Paged cache addressing (table == nullptr: contiguous [b][g][cap][d]).
+struct PagedLayout {
+  const int32_t* table;  // [b][table_stride] block ids
+  int table_stride;
+  int bs_log2;           // block of 2^bs_log2 positions
+  int num_blocks;        // ids are clamped to [0, num_blocks)
+};
+
 struct AppendParams {
   void* k_cache;
   void* v_cache;
@@ -65,6 +80,7 @@ struct AppendParams {
   const void* v_new;
   int32_t* lens;
   int g, d_k, d_v, cap;
+  PagedLayout pg;
 };
 
 struct DecodeParams {
@@ -91,6 +107,7 @@ struct DecodeParams {
   int merge_kernel; // 1: shared segments are merged by merge_partials_kernel after this launch
   int2* seg_info;   // merge_kernel: per segment (p0, p1) of its shared pieces, p1 = -1 if none
   float scale_log2; // scale * log2(e)
+  PagedLayout pg;   // paged caches (pg.table != nullptr); cap = table_stride << bs_log2
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -164,10 +181,13 @@ hipError_t launch_fold(const FoldParams& p, int b, int dtype, hipStream_t stream
 
 // Workgroups of the decode kernel instance that fit on one compute unit at
 // once (runtime occupancy query, cached; 0 if the runtime cannot say).
-int matrix_workgroups_per_cu(int G, bool fused);
+int matrix_workgroups_per_cu(int G, bool fused, bool paged);
 // Waves per workgroup of the matrix kernel instance for G heads per KV head.
 int matrix_waves(int G);
-int vector_workgroups_per_cu(int dtype, int d, int heads_per_block, bool fused);
+int vector_workgroups_per_cu(int dtype, int d, int heads_per_block, bool fused, bool paged);
+// The paged-cache instances of the vector kernel (their own translation unit).
+hipError_t launch_decode_vector_paged(const DecodeParams& p, int dtype, hipStream_t stream);
+int vector_occupancy_paged(int dtype, int d, int heads_per_block, bool fused);
 // Waves per workgroup of the vector kernel instance for this dtype, d and head block.
 int vector_waves(int dtype, int d, int heads_per_block);
 
@@ -184,6 +204,26 @@ inline int vector_heads_per_block(int G) {
 
 #if defined(__HIPCC__)
 namespace gqa {
+
+// ------------------------------------------------------------- addressing
+
+// Row index (multiply by the head dim for elements) of position t of KV head
+// j of sequence s: contiguous ((s*g + j)*cap + t), or, paged, row t mod B of
+// head j in the block the table names for t (clamped into the pool, so a bad
+// id reads or writes a wrong block of the pool, never outside it).
+// UNIFORM: s and t are the same in every lane of the wave (the table entry is
+// then read once, through the scalar unit).
+template <bool PAGED, bool UNIFORM>
+__device__ __forceinline__ size_t kv_row(const PagedLayout& pg, int g, int cap, int s, int j, int t) {
+  if constexpr (PAGED) {
+    int idx = s * pg.table_stride + (t >> pg.bs_log2);  // b * table_stride < 2^31 (host check)
+    if constexpr (UNIFORM) idx = __builtin_amdgcn_readfirstlane(idx);
+    const int blk = min(max(pg.table[idx], 0), pg.num_blocks - 1);
+    return ((size_t(blk) * g + j) << pg.bs_log2) + (t & ((1 << pg.bs_log2) - 1));
+  } else {
+    return (size_t(s) * g + j) * size_t(cap) + t;
+  }
+}
 
 // ---------------------------------------------------------------- numerics
 

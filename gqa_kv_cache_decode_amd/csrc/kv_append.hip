@@ -7,13 +7,18 @@
 // before storing any (so the copy costs one memory round trip, not one per
 // row), and write them to slot lens[s]. Only after a barrier does one thread
 // write lens[s] + 1, so every thread used the old length. A length outside
-// [0, cap) leaves the sequence untouched.
+// [0, cap) leaves the sequence untouched. With a paged cache (p.pg.table set)
+// the slot is row lens[s] mod B of the block the table names for lens[s].
 #include "gqa_internal.hpp"
 
 namespace gqa {
 namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ size_t slot_row(const AppendParams& p, int s, int j, int pos) {
+  return p.pg.table ? kv_row<true, false>(p.pg, p.g, p.cap, s, j, pos) : kv_row<false, false>(p.pg, p.g, p.cap, s, j, pos);
+}
 
 template <typename UNIT, int PER_THREAD>
 __global__ __launch_bounds__(256) void kv_append_kernel(AppendParams p, int esize) {
@@ -41,12 +46,12 @@ __global__ __launch_bounds__(256) void kv_append_kernel(AppendParams p, int esiz
         if (c < p.g * ku) {
           const int j = c / ku, x = c - j * ku;
           val[r] = kn[c];
-          dst[r] = kc + ((size_t(s) * p.g + j) * p.cap + pos) * ku + x;
+          dst[r] = kc + slot_row(p, s, j, pos) * ku + x;
         } else {
           const int cv = c - p.g * ku;
           const int j = cv / vu, x = cv - j * vu;
           val[r] = vn[cv];
-          dst[r] = vc + ((size_t(s) * p.g + j) * p.cap + pos) * vu + x;
+          dst[r] = vc + slot_row(p, s, j, pos) * vu + x;
         }
       }
     }

@@ -244,6 +244,44 @@ int gqa_decode_layer(void* y, const void* x, const void* w_q, const void* w_k, c
                      int dtype, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Paged caches. The "LLM inference 05" notes name block-table (vLLM-style)
+ * caches without fixing a layout; this library reads them as follows. K and
+ * V live in pools of blocks of block_size positions:
+ *   k_pool [num_blocks][g][block_size][d_k], v_pool [num_blocks][g][block_size][d_v]
+ * and block_table int32 [b][max_blocks] (row stride max_blocks) names, for
+ * sequence s, the pool block holding its positions n*block_size ..
+ * (n+1)*block_size - 1 in entry [s][n]. Position t of KV head j of sequence
+ * s is k_pool[block_table[s][t / block_size]][j][t % block_size]. A sequence
+ * holds at most max_blocks * block_size positions (its "cap").
+ * block_size is a power of two in [32, 2^20]: a 32-position tile of the
+ * decode kernels then never straddles two blocks. b * max_blocks < 2^31.
+ * Table entries the call needs (positions < the attended length, and the
+ * append position) must be valid ids; the kernels clamp any id into
+ * [0, num_blocks), so a bad id reads or writes the wrong block of the pool
+ * but never memory outside it. Entries past a sequence's last needed block
+ * are never read. All pointers are caller-owned device memory. Results are
+ * exactly those of the contiguous entry points on the cache the pool stands
+ * for (same kernels, same schedule, same arithmetic).
+ */
+
+/* gqa_kv_append on a paged cache: the new rows go to position lens[s]. */
+int gqa_kv_append_paged(void* k_pool, void* v_pool, const void* k_new, const void* v_new, int32_t* lens,
+                        const int32_t* block_table, int b, int g, int d_k, int d_v, int block_size, int max_blocks,
+                        int num_blocks, int max_len, int dtype, void* stream);
+
+/* gqa_decode_attention on paged caches (workspace as for the contiguous call). */
+int gqa_decode_attention_paged(void* out, const void* q, const void* k_pool, const void* v_pool,
+                               const int32_t* lens, const int32_t* block_table, int b, int h, int g, int d_k,
+                               int d_v, int block_size, int max_blocks, int num_blocks, int max_len, float scale,
+                               int dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/* gqa_decode_step (append + attention in one launch) on paged caches. */
+int gqa_decode_step_paged(void* out, const void* q, const void* k_new, const void* v_new, void* k_pool,
+                          void* v_pool, int32_t* lens, const int32_t* block_table, int b, int h, int g, int d_k,
+                          int d_v, int block_size, int max_blocks, int num_blocks, int max_len, float scale,
+                          int dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Mean-fold of KV heads ("TF2 GQA" lesson, on moving a trained multi-head
  * model to grouped-query attention: each contiguous group of key/value heads
  * is replaced by its average; the lesson's lab folds them that way and

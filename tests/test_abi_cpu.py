@@ -37,6 +37,27 @@ def test_exports_every_declared_function(lib):
     assert set(names) == set(_lib.SIGNATURES)
 
 
+def test_binding_signatures_match_the_header():
+    # the ctypes argument list of every function has the header's parameter count and kinds
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    kinds = {"ptr": ctypes.c_void_p, "int": ctypes.c_int, "float": ctypes.c_float, "size_t": ctypes.c_size_t}
+    for name, params in re.findall(r"\b(gqa_\w+)\s*\(([^)]*)\)\s*;", text):
+        params = [x.strip() for x in params.split(",") if x.strip() and x.strip() != "void"]
+        want = []
+        for prm in params:
+            if "*" in prm:
+                want.append(kinds["ptr"])
+            elif prm.startswith("size_t"):
+                want.append(kinds["size_t"])
+            elif prm.startswith("float"):
+                want.append(kinds["float"])
+            else:
+                want.append(kinds["int"])
+        got = [ctypes.c_void_p if (t is ctypes.c_void_p or issubclass(t, ctypes._Pointer)) else t
+               for t in _lib.SIGNATURES[name][1]]
+        assert got == want, name
+
+
 def test_header_status_codes_match_binding():
     text = open(HEADER).read()
     codes = dict(re.findall(r"#define (GQA_\w+) \(?(-?\d+)\)?", text))
@@ -229,4 +250,42 @@ def test_fold_rejects(lib):
     assert call(b=0) == _lib.ERR_ARG
     assert call(dst=FAKE, rows=0) == _lib.ERR_ARG  # the same buffer: overlap
     assert call(dst=ctypes.c_void_p((1 << 40) + 8), rows=0) == _lib.ERR_ARG  # not 16-byte aligned
+    assert lib.gqa_last_error().decode() != ""
+
+
+def test_paged_rejects(lib):
+    FAKE2 = ctypes.c_void_p(1 << 40)
+
+    def step(**kw):
+        a = dict(table=FAKE2, b=4, h=8, g=2, d=128, bs=64, mb=4, nb=16, max_len=100, dtype=_lib.BF16, ws_bytes=1 << 30)
+        a.update(kw)
+        return lib.gqa_decode_step_paged(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, a["table"], a["b"], a["h"], a["g"],
+                                         a["d"], a["d"], a["bs"], a["mb"], a["nb"], a["max_len"], ctypes.c_float(0.1),
+                                         a["dtype"], FAKE, a["ws_bytes"], None)
+
+    def attend(**kw):
+        a = dict(table=FAKE2, b=4, h=8, g=2, d=128, bs=64, mb=4, nb=16, max_len=100, ws_bytes=1 << 30)
+        a.update(kw)
+        return lib.gqa_decode_attention_paged(FAKE, FAKE, FAKE, FAKE, FAKE, a["table"], a["b"], a["h"], a["g"],
+                                              a["d"], a["d"], a["bs"], a["mb"], a["nb"], a["max_len"],
+                                              ctypes.c_float(0.1), _lib.BF16, FAKE, a["ws_bytes"], None)
+
+    def append(**kw):
+        a = dict(table=FAKE2, b=4, bs=64, mb=4, nb=16, max_len=100)
+        a.update(kw)
+        return lib.gqa_kv_append_paged(FAKE, FAKE, FAKE, FAKE, FAKE, a["table"], a["b"], 2, 128, 128, a["bs"],
+                                       a["mb"], a["nb"], a["max_len"], _lib.BF16, None)
+
+    for call in (step, attend, append):
+        assert call(table=None) == _lib.ERR_ARG
+        assert call(bs=16) == _lib.ERR_UNSUPPORTED    # below one 32-position tile
+        assert call(bs=96) == _lib.ERR_UNSUPPORTED    # not a power of two
+        assert call(mb=0) == _lib.ERR_ARG
+        assert call(nb=0) == _lib.ERR_ARG
+    assert step(max_len=256) == _lib.ERR_CAPACITY       # 4 blocks of 64: the append needs position 256
+    assert append(max_len=256) == _lib.ERR_CAPACITY
+    assert attend(max_len=257) == _lib.ERR_CAPACITY
+    assert step(h=6, g=4) == _lib.ERR_GROUPS
+    assert step(d=48) == _lib.ERR_UNSUPPORTED
+    assert step(ws_bytes=64) == _lib.ERR_WORKSPACE
     assert lib.gqa_last_error().decode() != ""
