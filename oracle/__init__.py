@@ -25,8 +25,8 @@ Pages the oracle follows (cited by title and section):
 
 Parity status: every function here is pinned by ``tests/test_oracle_pins.py``,
 ``tests/test_oracle_golden.py``, ``tests/test_oracle_layer.py`` and
-``tests/test_oracle_fold.py`` and ``tests/test_oracle_paged.py`` (no function
-is "parity unpinned").
+``tests/test_oracle_fold.py``, ``tests/test_oracle_paged.py`` and
+``tests/test_oracle_multi.py`` (no function is "parity unpinned").
 """
 from __future__ import annotations
 
@@ -103,6 +103,8 @@ def _load():
     lib.oracle_gather_paged.argtypes = [vp, vp, vp, vp] + [i32] * 8
     lib.oracle_kv_append_paged.restype = i32
     lib.oracle_kv_append_paged.argtypes = [vp] * 6 + [i32] * 8
+    lib.oracle_kv_append_multi.restype = i32
+    lib.oracle_kv_append_multi.argtypes = [vp] * 5 + [i32] * 7
     _lib = lib
     return lib
 
@@ -317,3 +319,45 @@ def decode_attention_paged(q, k_pool, v_pool, lens, table, scale: float, **kw):
     k = gather_paged(k_pool, table, lens, bs, cap)
     v = gather_paged(v_pool, table, lens, bs, cap)
     return decode_attention(q, k, v, np.ascontiguousarray(lens, dtype=np.int32), scale, **kw)
+
+
+def kv_append_multi(k_cache, v_cache, k_new, v_new, lens) -> None:
+    """In place: token r of sequence s goes to position lens[s] + r; lens += n.
+
+    k_new [b, n, g, d_k], v_new [b, n, g, d_v] [MQA-review §2.3 batched positions, §2.4].
+    """
+    for a in (k_cache, v_cache, k_new, v_new, lens):
+        if not a.flags.c_contiguous:
+            raise ValueError("oracle arrays must be C-contiguous")
+    if lens.dtype != np.int32:
+        raise TypeError("lens must be int32")
+    b, g, cap, d_k = k_cache.shape
+    d_v = v_cache.shape[3]
+    n = k_new.shape[1]
+    if k_new.shape != (b, n, g, d_k) or v_new.shape != (b, n, g, d_v):
+        raise OracleError(ERR_ARG, "kv_append_multi shapes")
+    rc = _load().oracle_kv_append_multi(_ptr(k_cache), _ptr(v_cache), _ptr(k_new), _ptr(v_new), _ptr(lens),
+                                        b, n, g, d_k, d_v, cap, _dtype_code(k_cache))
+    if rc != OK:
+        raise OracleError(rc, "kv_append_multi")
+
+
+def decode_attention_multi(q, k_cache, v_cache, lens, scale: float, threads: int = 0) -> np.ndarray:
+    """n query tokens per sequence over a cache that already holds them, with the causal mask.
+
+    q [b, n, h, d_k]; lens int32 [b] = attended length of the last token (the n new
+    tokens are the positions lens[s] - n .. lens[s] - 1). Token r attends positions
+    t < lens[s] - (n - 1 - r): everything before it and itself [MQA-review §2.3, the
+    batched form whose additive mask removes later positions; LLM-inf-05: under the
+    causal mask a position's K and V depend only on the positions up to it]. Each
+    token's row is the single-token attention over its own prefix. Returns [b, n, h, d_v].
+    """
+    b, n, h, d_k = q.shape
+    lens = np.ascontiguousarray(lens, dtype=np.int32)
+    if np.any(lens < n):
+        raise OracleError(ERR_ARG, "decode_attention_multi: every length must include the n new tokens")
+    out = np.empty((b, n, h, v_cache.shape[3]), dtype=np.float64)
+    for r in range(n):
+        prefix = (lens - (n - 1 - r)).astype(np.int32)
+        out[:, r] = decode_attention(np.ascontiguousarray(q[:, r]), k_cache, v_cache, prefix, scale, threads=threads)
+    return out

@@ -419,3 +419,35 @@ int oracle_kv_append_paged(void* k_pool, void* v_pool, const void* k_new, const 
   }
   return ORC_OK;
 }
+
+/*
+ * Append n new tokens per sequence: token r's key and value rows go to
+ * position lens[s] + r, then the length grows by n [MQA-review §2.3, the
+ * batched form that processes n positions of a sequence in one step; §2.4
+ * for the concatenation on the position axis]. k_new is [b][n][g][d_k],
+ * v_new [b][n][g][d_v]. ORC_ERR_CAPACITY (and nothing changed) if some
+ * lens[s] + n exceeds cap or a length is negative.
+ */
+int oracle_kv_append_multi(void* k_cache, void* v_cache, const void* k_new, const void* v_new, int32_t* lens, int b,
+                           int n, int g, int d_k, int d_v, int cap, int dtype) {
+  if (!k_cache || !v_cache || !k_new || !v_new || !lens || b <= 0 || n <= 0 || g <= 0 || d_k <= 0 || d_v <= 0 ||
+      cap <= 0)
+    return ORC_ERR_ARG;
+  if (dtype != ORC_F32 && dtype != ORC_BF16) return ORC_ERR_UNSUPPORTED;
+  for (int s = 0; s < b; ++s)
+    if (lens[s] < 0 || (int64_t)lens[s] + n > cap) return ORC_ERR_CAPACITY;
+  const size_t es = elem_size(dtype);
+  for (int s = 0; s < b; ++s) {
+    for (int r = 0; r < n; ++r) {
+      const int pos = lens[s] + r;
+      for (int j = 0; j < g; ++j) {
+        const size_t src = (((size_t)s * n + r) * g + j);
+        const size_t dst = ((size_t)s * g + j) * cap + pos;
+        memcpy((char*)k_cache + dst * d_k * es, (const char*)k_new + src * d_k * es, d_k * es);
+        memcpy((char*)v_cache + dst * d_v * es, (const char*)v_new + src * d_v * es, d_v * es);
+      }
+    }
+    lens[s] += n;
+  }
+  return ORC_OK;
+}
