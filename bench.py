@@ -40,7 +40,12 @@ and the decode time over each folded cache.
 With --paged B the caches live in pools of B-position blocks behind shuffled
 block tables (gqa_decode_step_paged); bytes and timing as for the step.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--paged B] [--layer | --fold G]
+With --tokens N (N > 1) each step appends N new tokens per sequence and runs
+their causal attention (gqa_decode_step_multi: two launches); bytes are
+those the last token attends, read once for all N tokens.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--paged B | --tokens N]
+                       [--layer | --fold G]
 """
 from __future__ import annotations
 
@@ -117,6 +122,8 @@ def main():
                     help="run a 1 GiB device copy first (reference for HBM byte counters)")
     ap.add_argument("--layer", action="store_true",
                     help="time the whole decode layer (projections + step) instead of the step alone")
+    ap.add_argument("--tokens", type=int, default=1, metavar="N",
+                    help="new tokens per sequence and step (N > 1: gqa_decode_step_multi, causal)")
     ap.add_argument("--paged", type=int, default=0, metavar="B",
                     help="keep the caches in pools of B-position blocks behind shuffled block tables")
     ap.add_argument("--fold", type=int, default=0, metavar="G",
@@ -150,7 +157,8 @@ def main():
     set_bytes = wl.b * wl.g * wl.cap * wl.d * 2 * wl.elem_bytes
     n_sets = args.sets or max(2, math.ceil(1.5e9 / set_bytes))
     n_sets = min(n_sets, total_steps) if total_steps > 0 else 1
-    grow = math.ceil(total_steps / n_sets) + 1
+    ntok = args.tokens
+    grow = math.ceil(total_steps / n_sets) * ntok + 1
     log(f"workload {wl.name}: {n_sets} cache sets of {set_bytes / 1e6:.1f} MB")
 
     def to_dev(a):
@@ -172,6 +180,9 @@ def main():
 
     if args.paged and (args.unfused or args.paged < 32 or args.paged & (args.paged - 1)):
         print("--paged B: B a power of two >= 32, fused step only", file=sys.stderr)
+        sys.exit(2)
+    if ntok < 1 or (ntok > 1 and (args.paged or args.unfused or wl.dtype != "bf16")):
+        print("--tokens N: N >= 1; N > 1 runs bf16 contiguous caches only", file=sys.stderr)
         sys.exit(2)
     sets = []
     host0 = None
@@ -202,6 +213,18 @@ def main():
     for s in range(min(total_steps, 64)):
         kn, vn = inputs.draw_new_kv(wl.seed, s, wl.b, wl.g, wl.d, wl.d, wl.dtype)
         news.append((to_dev(kn), to_dev(vn)))
+    if ntok > 1:
+        # token r of step s uses the one-token draws of index s * N + r, stacked token-major
+        ws = api.make_multi_workspace(wl.b, ntok, wl.h, wl.g, wl.d, wl.d, dt, dev)
+        out = torch.empty(wl.b, ntok, wl.h, wl.d, dtype=dt, device=dev)
+        nq = min(total_steps, 16)
+        qs = [torch.stack([to_dev(inputs.draw_q(wl.seed, s * ntok + r, wl.b, wl.h, wl.d, wl.dtype))
+                           for r in range(ntok)], dim=1).contiguous() for s in range(nq)]
+        news = []
+        for s in range(nq):
+            rows = [inputs.draw_new_kv(wl.seed, s * ntok + r, wl.b, wl.g, wl.d, wl.d, wl.dtype) for r in range(ntok)]
+            news.append((torch.stack([to_dev(k) for k, _ in rows], dim=1).contiguous(),
+                         torch.stack([to_dev(v) for _, v in rows], dim=1).contiguous()))
 
     if args.calibrate_copy:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
@@ -227,12 +250,14 @@ def main():
         elif args.paged:
             api.decode_step_paged(out, qs[i % len(qs)], kn, vn, st["kc"], st["vc"], st["lens"], st["table"], max_len,
                                   wl.scale, ws)
+        elif ntok > 1:
+            api.decode_step_multi(out, qs[i % len(qs)], kn, vn, st["kc"], st["vc"], st["lens"], max_len, wl.scale, ws)
         else:
             api.decode_step(out, qs[i % len(qs)], kn, vn, st["kc"], st["vc"], st["lens"], max_len, wl.scale, ws,
                             path=args.path, workgroups=args.workgroups)
         if ev_pair is not None:
             ev_pair[1].record(stream)
-        st["lens_h"] += 1
+        st["lens_h"] += ntok
         return kv_bytes_attended(wl.g, wl.d, wl.d, wl.elem_bytes, st["lens_h"])
 
     for i in range(args.warmup):
@@ -269,12 +294,13 @@ def main():
 
     value = total_bytes / (elapsed_ms / 1e3) / 1e9
     achieved = bytes_per_launch / (kern_avg_ms / 1e3) / 1e9
-    plan_path, plan_wgs, plan_merge = api.plan(wl.b, wl.h, wl.g, wl.d, wl.d, cap, max_len_bound, dt, args.path,
-                                               args.workgroups)
-    traffic = None if args.paged else traffic_from_profile(wl.name)
+    # a multi-token call is planned as a one-token call with N * h heads on the matrix path
+    plan_path, plan_wgs, plan_merge = api.plan(wl.b, wl.h * ntok, wl.g, wl.d, wl.d, cap, max_len_bound, dt,
+                                               api.PATH_MATRIX if ntok > 1 else args.path, args.workgroups)
+    traffic = None if (args.paged or ntok > 1) else traffic_from_profile(wl.name)
 
     cpu = None
-    if args.cpu_seconds > 0:
+    if args.cpu_seconds > 0 and ntok == 1:
         log("timing the CPU oracle ...")
         cpu = cpu_baseline(wl, host0, args.cpu_seconds)
 
@@ -295,7 +321,8 @@ def main():
         "dtype": wl.dtype,
         "data": "synthetic",
         "config": {
-            "workload": wl.name + (f"_paged_blocks{args.paged}" if args.paged else ""),
+            "workload": wl.name + (f"_paged_blocks{args.paged}" if args.paged else "")
+                        + (f"_{ntok}_tokens" if ntok > 1 else ""),
             "b": wl.b, "h": wl.h, "g": wl.g, "d_k": wl.d, "d_v": wl.d,
             "lens": list(wl.lens) if isinstance(wl.lens, (list, tuple)) else wl.lens,
             "lens_drawn_mean": float(lens0.mean()), "lens_drawn_min": int(lens0.min()),
@@ -303,7 +330,10 @@ def main():
             "path": {1: "vector", 2: "matrix"}[plan_path], "workgroups": plan_wgs,
             "split_merge": "second launch" if plan_merge == api.MERGE_KERNEL else "in the decode kernel",
             "step_api": ("gqa_kv_append + gqa_decode_attention" if args.unfused else
-                         f"gqa_decode_step_paged (blocks of {args.paged})" if args.paged else "gqa_decode_step"),
+                         f"gqa_decode_step_paged (blocks of {args.paged})" if args.paged else
+                         f"gqa_decode_step_multi ({ntok} tokens: append + causal attention)" if ntok > 1 else
+                         "gqa_decode_step"),
+            "new_tokens_per_step": ntok, "tokens_per_s": round(wl.b * ntok * args.steps / (elapsed_ms / 1e3), 1),
             "kv_bytes_per_step": int(bytes_per_launch),
         },
         "roofline": {
@@ -311,7 +341,8 @@ def main():
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
             "kernel": ("decode_matrix_kernel" if plan_path == 2 else "decode_vector_kernel")
                       + (" + merge_partials_kernel" if plan_merge == api.MERGE_KERNEL else "")
-                      + ("" if args.unfused else " (fused step)") + (", paged" if args.paged else ""),
+                      + ("" if args.unfused else " (fused step)" if ntok == 1 else
+                         f" (causal, {ntok} tokens) + kv_append_kernel") + (", paged" if args.paged else ""),
             "kernel_avg_us": round(kern_avg_ms * 1e3, 3),
         },
         "cpu_baseline": cpu,

@@ -54,6 +54,10 @@ SIGNATURES = {
     "gqa_kv_append_paged": (_i32, [_vp] * 6 + [_i32] * 9 + [_vp]),
     "gqa_decode_attention_paged": (_i32, [_vp] * 6 + [_i32] * 9 + [_f32, _i32, _vp, _sz, _vp]),
     "gqa_decode_step_paged": (_i32, [_vp] * 8 + [_i32] * 9 + [_f32, _i32, _vp, _sz, _vp]),
+    "gqa_decode_multi_workspace_size": (_sz, [_i32] * 7),
+    "gqa_kv_append_multi": (_i32, [_vp] * 5 + [_i32] * 8 + [_vp]),
+    "gqa_decode_attention_multi": (_i32, [_vp] * 5 + [_i32] * 8 + [_f32, _i32, _vp, _sz, _vp]),
+    "gqa_decode_step_multi": (_i32, [_vp] * 7 + [_i32] * 8 + [_f32, _i32, _vp, _sz, _vp]),
     "gqa_last_error": (ctypes.c_char_p, []),
 }
 

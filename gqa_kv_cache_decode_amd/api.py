@@ -318,3 +318,77 @@ def decode_step_paged(out: torch.Tensor, q: torch.Tensor, k_new: torch.Tensor, v
         _dtype_code(q), workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream_handle(stream))
     _lib.check(rc, "gqa_decode_step_paged")
     return out
+
+
+def make_multi_workspace(b: int, n: int, h: int, g: int, d_k: int, d_v: int, dtype: torch.dtype, device):
+    """Zeroed workspace for the multi-token calls (gqa_decode_multi_workspace_size bytes)."""
+    nbytes = int(_lib.load().gqa_decode_multi_workspace_size(b, n, h, g, d_k, d_v, _DTYPES[dtype]))
+    if nbytes == 0:
+        raise ValueError("unsupported shape for the multi-token workspace")
+    return torch.zeros(nbytes, dtype=torch.uint8, device=device)
+
+
+def _multi_shapes(q, k_cache, v_cache, lens):
+    _check_gpu(q, k_cache, v_cache, lens)
+    if lens.dtype != torch.int32:
+        raise TypeError("lens must be int32")
+    b, n, h, d_k = q.shape
+    bk, g, cap, dk2 = k_cache.shape
+    d_v = v_cache.shape[3]
+    if bk != b or dk2 != d_k or tuple(v_cache.shape) != (b, g, cap, d_v) or tuple(lens.shape) != (b,):
+        raise ValueError("multi-token call: inconsistent shapes")
+    return b, n, h, g, cap, d_k, d_v
+
+
+def kv_append_multi(k_cache, v_cache, k_new, v_new, lens, max_len: int, stream=None) -> None:
+    """Store token r's rows (k_new / v_new [b, n, g, d]) at position lens[s] + r; lens += n."""
+    _check_gpu(k_cache, v_cache, k_new, v_new, lens)
+    b, n, g, d_k = k_new.shape
+    if tuple(k_cache.shape[:2]) != (b, g) or tuple(v_new.shape[:3]) != (b, n, g) or lens.dtype != torch.int32 \
+            or tuple(lens.shape) != (b,) or k_cache.shape[3] != d_k or v_cache.shape[3] != v_new.shape[3] \
+            or tuple(v_cache.shape[:3]) != tuple(k_cache.shape[:3]):
+        raise ValueError("kv_append_multi: inconsistent shapes")
+    dt = _dtype_code(k_cache)
+    if any(_dtype_code(t) != dt for t in (v_cache, k_new, v_new)):
+        raise TypeError("caches and new rows must share one element type")
+    rc = _lib.load().gqa_kv_append_multi(k_cache.data_ptr(), v_cache.data_ptr(), k_new.data_ptr(), v_new.data_ptr(),
+                                         lens.data_ptr(), b, n, g, d_k, v_cache.shape[3], k_cache.shape[2],
+                                         int(max_len), dt, _stream_handle(stream))
+    _lib.check(rc, "gqa_kv_append_multi")
+
+
+def decode_attention_multi(out, q, k_cache, v_cache, lens, max_len: int, scale: float, workspace,
+                           stream=None) -> torch.Tensor:
+    """n query tokens per sequence (q, out [b, n, h, d]) over caches that already hold them, causal."""
+    b, n, h, g, cap, d_k, d_v = _multi_shapes(q, k_cache, v_cache, lens)
+    _check_gpu(out, workspace)
+    if tuple(out.shape) != (b, n, h, d_v):
+        raise ValueError("decode_attention_multi: out must be [b, n, h, d_v]")
+    dt = _dtype_code(q)
+    if any(_dtype_code(t) != dt for t in (k_cache, v_cache, out)):
+        raise TypeError("q, caches and out must share one element type")
+    rc = _lib.load().gqa_decode_attention_multi(
+        out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), lens.data_ptr(), b, n, h, g, d_k, d_v,
+        cap, int(max_len), float(scale), dt, workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+        _stream_handle(stream))
+    _lib.check(rc, "gqa_decode_attention_multi")
+    return out
+
+
+def decode_step_multi(out, q, k_new, v_new, k_cache, v_cache, lens, max_len: int, scale: float, workspace,
+                      stream=None) -> torch.Tensor:
+    """Append n tokens per sequence, then their causal attention (max_len: bound before the append)."""
+    b, n, h, g, cap, d_k, d_v = _multi_shapes(q, k_cache, v_cache, lens)
+    _check_gpu(out, k_new, v_new, workspace)
+    if tuple(out.shape) != (b, n, h, d_v) or tuple(k_new.shape) != (b, n, g, d_k) \
+            or tuple(v_new.shape) != (b, n, g, d_v):
+        raise ValueError("decode_step_multi: inconsistent shapes")
+    dt = _dtype_code(q)
+    if any(_dtype_code(t) != dt for t in (k_cache, v_cache, out, k_new, v_new)):
+        raise TypeError("q, rows, caches and out must share one element type")
+    rc = _lib.load().gqa_decode_step_multi(
+        out.data_ptr(), q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+        lens.data_ptr(), b, n, h, g, d_k, d_v, cap, int(max_len), float(scale), dt, workspace.data_ptr(),
+        workspace.numel() * workspace.element_size(), _stream_handle(stream))
+    _lib.check(rc, "gqa_decode_step_multi")
+    return out

@@ -98,11 +98,12 @@ struct WaveState {
 // One 32-position tile starting at kbase/vbase row t0 (FULL: all 32 rows
 // valid; otherwise only rows < nvalid are read). FUSED: the row nr.local is
 // the appended token, read from its new rows and stored into the cache by the
-// lanes that load it.
-template <int NB, bool FULL, bool FUSED>
+// lanes that load it. CAUSAL (multi-token decode): this lane's head column of
+// block nb only sees rows < lim[nb] (<= nvalid), its token's causal limit.
+template <int NB, bool FULL, bool FUSED, bool CAUSAL = false>
 __device__ __forceinline__ void tile_step(WaveState<NB>& st, const bf16x8 (&qop)[NB][4], const uint16_t* kbase,
                                           const uint16_t* vbase, int t0, int nvalid, float sl2, int n16,
-                                          int q4, const NewRow& nr) {
+                                          int q4, const NewRow& nr, const int* lim = nullptr) {
   u32x4 kr[2][4];
 #pragma unroll
   for (int sg = 0; sg < 2; ++sg) {
@@ -146,7 +147,8 @@ __device__ __forceinline__ void tile_step(WaveState<NB>& st, const bf16x8 (&qop)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int row = 16 * sg + 4 * q4 + i;
-        sv[sg * 4 + i] = (FULL || row < nvalid) ? sacc[i] * sl2 : kNegInf;
+        if constexpr (CAUSAL) sv[sg * 4 + i] = (FULL || row < lim[nb]) ? sacc[i] * sl2 : kNegInf;
+        else sv[sg * 4 + i] = (FULL || row < nvalid) ? sacc[i] * sl2 : kNegInf;
       }
     }
     float mx = sv[0];
@@ -190,7 +192,10 @@ __device__ __forceinline__ void tile_step(WaveState<NB>& st, const bf16x8 (&qop)
 // head blocks, whose register needs allow one 4-wave workgroup per unit.
 // PAGED: K/V live in block pools addressed through the block table (one
 // lookup per 32-position tile); otherwise in contiguous [b][g][cap][d] caches.
-template <int NB, bool FUSED, int WAVES, bool PAGED>
+// CAUSAL: multi-token decode; the group's heads are the GV = G * n_tok
+// virtual heads (token r, head i) of head_row, every K/V tile is read once
+// for all of them, and token r's heads see positions < L - (n_tok - 1 - r).
+template <int NB, bool FUSED, int WAVES, bool PAGED, bool CAUSAL>
 __global__ __launch_bounds__(WAVES * 64, (NB == 1 && WAVES == 4) ? 2 : 1) void decode_matrix_kernel(DecodeParams p) {
   constexpr int THREADS = WAVES * 64;
   __shared__ float sm_m[WAVES][16];
@@ -208,10 +213,10 @@ __global__ __launch_bounds__(WAVES * 64, (NB == 1 && WAVES == 4) ? 2 : 1) void d
   const int w = threadIdx.x >> 6;
   const int n16 = lane & 15;
   const int q4 = lane >> 4;
-  const int G = p.G;
+  const int G = CAUSAL ? p.G * p.n_tok : p.G;  // (virtual) heads per KV group
   const float sl2 = p.scale_log2;
 
-  zero_empty_sequences<uint16_t>(p, wg);
+  zero_empty_sequences<uint16_t, CAUSAL>(p, wg);
 
   PieceWalker<WAVES == 8> walker;
   walker.init(p, wg);
@@ -230,7 +235,13 @@ __global__ __launch_bounds__(WAVES * 64, (NB == 1 && WAVES == 4) ? 2 : 1) void d
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         u32x4 v = {0u, 0u, 0u, 0u};
-        if (head < G) v = load16(qg + size_t(head) * D + ks * 32 + q4 * 8);
+        if constexpr (CAUSAL) {
+          if (head < G)
+            v = load16(static_cast<const uint16_t*>(p.q) + head_row(p.n_tok, p.h, p.G, s, i0 + head) * D + ks * 32 +
+                       q4 * 8);
+        } else {
+          if (head < G) v = load16(qg + size_t(head) * D + ks * 32 + q4 * 8);
+        }
         qop[nb][ks] = as_bf16x8(v);
       }
     }
@@ -247,6 +258,15 @@ __global__ __launch_bounds__(WAVES * 64, (NB == 1 && WAVES == 4) ? 2 : 1) void d
     const uint16_t* vbase = static_cast<const uint16_t*>(p.v_cache) + kv_head * p.cap * D;
     const int t_end = min(pc.L, pc.tile_end * kTile);
     const int pos_new = FUSED ? pc.L - 1 : -1;  // the appended token (fused step)
+    // CAUSAL: how many of the last positions this lane's head column does not
+    // see (n_tok - 1 - its token); padding columns see what the last token sees
+    int hide[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int head = nb * 16 + n16;
+      hide[nb] = (CAUSAL && head < G) ? p.n_tok - 1 - head / p.G : 0;
+    }
+    const int hide_max = CAUSAL ? p.n_tok - 1 : 0;
     for (int tile = pc.tile_begin + w; tile < pc.tile_end; tile += WAVES) {
       const int t0 = tile * kTile;
       const int nvalid = t_end - t0;
@@ -270,8 +290,13 @@ __global__ __launch_bounds__(WAVES * 64, (NB == 1 && WAVES == 4) ? 2 : 1) void d
         nr.kdst = static_cast<uint16_t*>(p.k_cache) + new_row * D;
         nr.vdst = static_cast<uint16_t*>(p.v_cache) + new_row * D;
         tile_step<NB, false, true>(st, qop, kb, vb, tb, nvalid, sl2, n16, q4, nr);
-      } else if (nvalid >= kTile) {
+      } else if (nvalid >= kTile && (!CAUSAL || pc.L - t0 - hide_max >= kTile)) {
         tile_step<NB, true, false>(st, qop, kb, vb, tb, kTile, sl2, n16, q4, NewRow{});
+      } else if constexpr (CAUSAL) {
+        int lim[NB];
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) lim[nb] = min(nvalid, pc.L - t0 - hide[nb]);
+        tile_step<NB, false, false, true>(st, qop, kb, vb, tb, nvalid, sl2, n16, q4, NewRow{}, lim);
       } else {
         tile_step<NB, false, false>(st, qop, kb, vb, tb, nvalid, sl2, n16, q4, NewRow{});
       }
@@ -328,23 +353,24 @@ __global__ __launch_bounds__(WAVES * 64, (NB == 1 && WAVES == 4) ? 2 : 1) void d
       }
       __syncthreads();
     }
-    finish_piece<uint16_t, NB * 8 / WAVES>(p, pc, walker.more(), wg, i0, G, fin_m, fin_l, &fin_o[0][0], dfr,
+    finish_piece<uint16_t, NB * 8 / WAVES, CAUSAL>(p, pc, walker.more(), wg, i0, G, fin_m, fin_l, &fin_o[0][0], dfr,
                                            sm_merge, &s_flag);
   }
-  dfr.resolve<uint16_t, NB * 8 / WAVES>(p, sm_merge, &s_flag);
+  dfr.resolve<uint16_t, NB * 8 / WAVES, CAUSAL>(p, sm_merge, &s_flag);
   if (FUSED) finish_step(p, &s_flag);
 }
 
-template <bool FUSED, bool PAGED>
+template <bool FUSED, bool PAGED, bool CAUSAL>
 void launch_nb(const DecodeParams& p, hipStream_t stream) {
   const dim3 grid(p.workgroups);
-  if (p.G <= 16) {
-    hipLaunchKernelGGL((decode_matrix_kernel<1, FUSED, kMatrixWaves1, PAGED>), grid, dim3(kMatrixWaves1 * 64), 0,
-                       stream, p);
-  } else if (p.G <= 32) {
-    hipLaunchKernelGGL((decode_matrix_kernel<2, FUSED, 4, PAGED>), grid, dim3(256), 0, stream, p);
+  const int GV = p.G * p.n_tok;
+  if (GV <= 16) {
+    hipLaunchKernelGGL((decode_matrix_kernel<1, FUSED, kMatrixWaves1, PAGED, CAUSAL>), grid,
+                       dim3(kMatrixWaves1 * 64), 0, stream, p);
+  } else if (GV <= 32) {
+    hipLaunchKernelGGL((decode_matrix_kernel<2, FUSED, 4, PAGED, CAUSAL>), grid, dim3(256), 0, stream, p);
   } else {
-    hipLaunchKernelGGL((decode_matrix_kernel<4, FUSED, 4, PAGED>), grid, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((decode_matrix_kernel<4, FUSED, 4, PAGED, CAUSAL>), grid, dim3(256), 0, stream, p);
   }
 }
 
@@ -352,33 +378,42 @@ void launch_nb(const DecodeParams& p, hipStream_t stream) {
 
 hipError_t launch_decode_matrix(const DecodeParams& p, hipStream_t stream) {
   const bool paged = p.pg.table != nullptr;
-  if (p.fused) paged ? launch_nb<true, true>(p, stream) : launch_nb<true, false>(p, stream);
-  else paged ? launch_nb<false, true>(p, stream) : launch_nb<false, false>(p, stream);
+  if (p.n_tok > 1) launch_nb<false, false, true>(p, stream);  // multi-token: contiguous caches, no fused append
+  else if (p.fused) paged ? launch_nb<true, true, false>(p, stream) : launch_nb<true, false, false>(p, stream);
+  else paged ? launch_nb<false, true, false>(p, stream) : launch_nb<false, false, false>(p, stream);
   return hipGetLastError();
 }
 
 namespace {
-template <bool FUSED, bool PAGED>
+template <bool FUSED, bool PAGED, bool CAUSAL>
 hipError_t occupancy(int k, int* n) {
   if (k == 0)
-    return hipOccupancyMaxActiveBlocksPerMultiprocessor(n, decode_matrix_kernel<1, FUSED, kMatrixWaves1, PAGED>,
-                                                        kMatrixWaves1 * 64, 0);
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(
+        n, decode_matrix_kernel<1, FUSED, kMatrixWaves1, PAGED, CAUSAL>, kMatrixWaves1 * 64, 0);
   if (k == 1)
-    return hipOccupancyMaxActiveBlocksPerMultiprocessor(n, decode_matrix_kernel<2, FUSED, 4, PAGED>, 256, 0);
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(n, decode_matrix_kernel<4, FUSED, 4, PAGED>, 256, 0);
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(n, decode_matrix_kernel<2, FUSED, 4, PAGED, CAUSAL>, 256, 0);
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(n, decode_matrix_kernel<4, FUSED, 4, PAGED, CAUSAL>, 256, 0);
 }
 }  // namespace
 
 int matrix_waves(int G) { return G <= 16 ? kMatrixWaves1 : 4; }
 
-int matrix_workgroups_per_cu(int G, bool fused, bool paged) {
-  static int cached[2][2][3] = {};
+// kind: 0 one-token, 1 fused step, 2 paged, 3 paged fused step, 4 multi-token.
+int matrix_workgroups_per_cu(int G, bool fused, bool paged, bool causal) {
+  static int cached[5][3] = {};
   const int k = G <= 16 ? 0 : (G <= 32 ? 1 : 2);
-  int& c = cached[paged ? 1 : 0][fused ? 1 : 0][k];
+  const int kind = causal ? 4 : (paged ? 2 : 0) + (fused ? 1 : 0);
+  int& c = cached[kind][k];
   if (c > 0) return c;
   int n = 0;
-  const hipError_t e = fused ? (paged ? occupancy<true, true>(k, &n) : occupancy<true, false>(k, &n))
-                             : (paged ? occupancy<false, true>(k, &n) : occupancy<false, false>(k, &n));
+  hipError_t e;
+  switch (kind) {
+    case 0: e = occupancy<false, false, false>(k, &n); break;
+    case 1: e = occupancy<true, false, false>(k, &n); break;
+    case 2: e = occupancy<false, true, false>(k, &n); break;
+    case 3: e = occupancy<true, true, false>(k, &n); break;
+    default: e = occupancy<false, false, true>(k, &n); break;
+  }
   if (e != hipSuccess || n <= 0) {
     (void)hipGetLastError();
     return 0;

@@ -31,6 +31,7 @@ int ok() {
 
 constexpr int kMaxBatch = 65535;
 constexpr int kMaxHeads = 4096;
+constexpr int kMaxTokens = 64;  // new tokens per sequence of a multi-token call
 constexpr int kMaxLen = 1 << 28;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kDefaultCUs = 256;  // MI355X, used when no device can be queried
@@ -71,7 +72,7 @@ int gblk_bound(int G) {
 // callers). Fills plan on success. workgroups: 0 = one per resident slot of
 // the device (compute units x workgroups that fit per unit, at most two).
 int plan_decode(int b, int h, int g, int d_k, int d_v, int cap, int max_len, int dtype, int path,
-                int workgroups, Plan* plan, bool fused = false, bool paged = false) {
+                int workgroups, Plan* plan, bool fused = false, bool paged = false, bool causal = false) {
   if (b <= 0 || b > kMaxBatch) return fail(GQA_ERR_ARG, "b=%d must be in [1, %d]", b, kMaxBatch);
   if (h <= 0 || h > kMaxHeads) return fail(GQA_ERR_ARG, "h=%d must be in [1, %d]", h, kMaxHeads);
   if (g <= 0) return fail(GQA_ERR_ARG, "g=%d must be positive", g);
@@ -124,7 +125,7 @@ int plan_decode(int b, int h, int g, int d_k, int d_v, int cap, int max_len, int
     // Up to eight waves per compute unit (two 4-wave workgroups or one
     // 8-wave one keep enough loads in flight), never more than fit at once, so
     // the persistent grid runs in a single round.
-    int fit = chosen == GQA_PATH_MATRIX ? gqa::matrix_workgroups_per_cu(G, fused, paged)
+    int fit = chosen == GQA_PATH_MATRIX ? gqa::matrix_workgroups_per_cu(G, fused, paged, causal)
                                         : gqa::vector_workgroups_per_cu(dtype, d_k, plan->gblk, fused, paged);
     if (fit <= 0) fit = 2;  // no device to ask: assume the common case
     const int per_cu_max = 8 / waves;
@@ -179,7 +180,7 @@ int gqa_kv_append(void* k_cache, void* v_cache, const void* k_new, const void* v
     return fail(GQA_ERR_UNSUPPORTED, "dtype=%d is not GQA_DTYPE_F32 or GQA_DTYPE_BF16", dtype);
   if ((long long)max_len + 1 > cap)
     return fail(GQA_ERR_CAPACITY, "appending to max_len=%d needs cap > %d, cap=%d", max_len, max_len, cap);
-  gqa::AppendParams p{k_cache, v_cache, k_new, v_new, lens, g, d_k, d_v, cap, gqa::PagedLayout{nullptr, 0, 0, 0}};
+  gqa::AppendParams p{k_cache, v_cache, k_new, v_new, lens, g, d_k, d_v, cap, gqa::PagedLayout{nullptr, 0, 0, 0}, 1};
   const hipError_t e = gqa::launch_append(p, b, dtype, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(GQA_ERR_HIP, "gqa_kv_append launch: %s", hipGetErrorString(e));
   return ok();
@@ -213,10 +214,10 @@ int decode_prepare(const char* fn, void* out, const void* q, void* k_cache, void
                    const void* k_new, const void* v_new, int b, int h, int g, int d_k, int d_v, int cap,
                    int max_len_att, float scale, int dtype, void* workspace, size_t workspace_bytes, int path,
                    int workgroups, int fused, gqa::DecodeParams* pp, Plan* planp,
-                   const gqa::PagedLayout* paged = nullptr) {
+                   const gqa::PagedLayout* paged = nullptr, bool causal = false) {
   Plan& plan = *planp;
   const int rc = plan_decode(b, h, g, d_k, d_v, cap, max_len_att, dtype, path, workgroups, &plan, fused != 0,
-                             paged != nullptr);
+                             paged != nullptr, causal);
   if (rc != GQA_OK) return rc;
   const gqa::WorkspaceLayout ws = gqa::workspace_layout(b, h, gblk_bound(h / g), d_v);
   if (!workspace) return fail(GQA_ERR_WORKSPACE, "%s: workspace is null (%zu bytes needed)", fn, ws.total);
@@ -260,6 +261,7 @@ int decode_prepare(const char* fn, void* out, const void* q, void* k_cache, void
   p.seg_lead = (plan.path == GQA_PATH_MATRIX && gqa::matrix_waves(p.G) == 8) ? kSegmentLead : 0;
   p.scale_log2 = scale * kLog2e;
   p.pg = paged ? *paged : gqa::PagedLayout{nullptr, 0, 0, 0};
+  p.n_tok = 1;
 
   return GQA_OK;
 }
@@ -480,6 +482,31 @@ int paged_check(const char* fn, const int32_t* table, int b, int block_size, int
   return GQA_OK;
 }
 
+// Checks and launch parameters of a multi-token attention (nothing enqueued).
+// The n tokens of a KV group are its n * G virtual heads: planned and laid
+// out as a one-token call with n * h heads, then addressed through head_row.
+int multi_prepare(const char* fn, void* out, const void* q, const void* k_cache, const void* v_cache,
+                  const int32_t* lens, int b, int n, int h, int g, int d_k, int d_v, int cap, int max_len, float scale,
+                  int dtype, void* workspace, size_t workspace_bytes, gqa::DecodeParams* p, Plan* plan) {
+  if (!out || !q || !k_cache || !v_cache || !lens) return fail(GQA_ERR_ARG, "%s: null pointer argument", fn);
+  if (n <= 0 || n > kMaxTokens) return fail(GQA_ERR_ARG, "%s: n=%d must be in [1, %d]", fn, n, kMaxTokens);
+  if (h <= 0 || g <= 0 || (long long)n * h > kMaxHeads)
+    return fail(GQA_ERR_ARG, "%s: h=%d, g=%d, n=%d (n * h at most %d)", fn, h, g, n, kMaxHeads);
+  if (h % g != 0) return fail(GQA_ERR_GROUPS, "h=%d query heads cannot be split into g=%d equal groups", h, g);
+  if (dtype != GQA_DTYPE_BF16 || d_k != 128 || d_v != 128 || n * (h / g) > gqa::kMatrixMaxGroup)
+    return fail(GQA_ERR_UNSUPPORTED, "%s: needs bf16, d_k = d_v = 128 and n * h / g <= %d (n=%d, h/g=%d)", fn,
+                gqa::kMatrixMaxGroup, n, h / g);
+  const int rc = decode_prepare(fn, out, q, const_cast<void*>(k_cache), const_cast<void*>(v_cache),
+                                const_cast<int32_t*>(lens), nullptr, nullptr, b, n * h, g, d_k, d_v, cap, max_len,
+                                scale, dtype, workspace, workspace_bytes, GQA_PATH_MATRIX, 0, 0, p, plan, nullptr,
+                                n > 1);
+  if (rc != GQA_OK) return rc;
+  p->h = h;
+  p->G = h / g;
+  p->n_tok = n;
+  return GQA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -501,7 +528,7 @@ int gqa_kv_append_paged(void* k_pool, void* v_pool, const void* k_new, const voi
   if ((long long)max_len + 1 > cap)
     return fail(GQA_ERR_CAPACITY, "appending to max_len=%d needs max_blocks * block_size > %d, have %d", max_len,
                 max_len, cap);
-  gqa::AppendParams p{k_pool, v_pool, k_new, v_new, lens, g, d_k, d_v, cap, pg};
+  gqa::AppendParams p{k_pool, v_pool, k_new, v_new, lens, g, d_k, d_v, cap, pg, 1};
   const hipError_t e = gqa::launch_append(p, b, dtype, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(GQA_ERR_HIP, "gqa_kv_append_paged launch: %s", hipGetErrorString(e));
   return ok();
@@ -547,6 +574,62 @@ int gqa_decode_step_paged(void* out, const void* q, const void* k_new, const voi
                       max_len + 1, scale, dtype, workspace, workspace_bytes, GQA_PATH_AUTO, 0, 1, &p, &plan, &pg);
   if (rc != GQA_OK) return rc;
   return decode_launch("gqa_decode_step_paged", p, plan, dtype, stream);
+}
+
+size_t gqa_decode_multi_workspace_size(int b, int n, int h, int g, int d_k, int d_v, int dtype) {
+  if (n <= 0 || n > kMaxTokens || h <= 0 || (long long)n * h > kMaxHeads) return 0;
+  return gqa_decode_workspace_size(b, n * h, g, d_k, d_v, 0, dtype);
+}
+
+int gqa_kv_append_multi(void* k_cache, void* v_cache, const void* k_new, const void* v_new, int32_t* lens, int b,
+                        int n, int g, int d_k, int d_v, int cap, int max_len, int dtype, void* stream) {
+  if (!k_cache || !v_cache || !k_new || !v_new || !lens)
+    return fail(GQA_ERR_ARG, "gqa_kv_append_multi: null pointer argument");
+  if (b <= 0 || b > kMaxBatch) return fail(GQA_ERR_ARG, "b=%d must be in [1, %d]", b, kMaxBatch);
+  if (n <= 0 || n > kMaxTokens) return fail(GQA_ERR_ARG, "n=%d must be in [1, %d]", n, kMaxTokens);
+  if (g <= 0 || d_k <= 0 || d_v <= 0 || cap <= 0)
+    return fail(GQA_ERR_ARG, "g=%d, d_k=%d, d_v=%d, cap=%d must be positive", g, d_k, d_v, cap);
+  if (max_len < 0) return fail(GQA_ERR_ARG, "max_len=%d must be >= 0", max_len);
+  if (dtype != GQA_DTYPE_F32 && dtype != GQA_DTYPE_BF16)
+    return fail(GQA_ERR_UNSUPPORTED, "dtype=%d is not GQA_DTYPE_F32 or GQA_DTYPE_BF16", dtype);
+  if ((long long)max_len + n > cap)
+    return fail(GQA_ERR_CAPACITY, "appending %d tokens to max_len=%d needs cap >= %lld, cap=%d", n, max_len,
+                (long long)max_len + n, cap);
+  gqa::AppendParams p{k_cache, v_cache, k_new, v_new, lens, g, d_k, d_v, cap, gqa::PagedLayout{nullptr, 0, 0, 0}, n};
+  const hipError_t e = gqa::launch_append(p, b, dtype, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(GQA_ERR_HIP, "gqa_kv_append_multi launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int gqa_decode_attention_multi(void* out, const void* q, const void* k_cache, const void* v_cache,
+                               const int32_t* lens, int b, int n, int h, int g, int d_k, int d_v, int cap,
+                               int max_len, float scale, int dtype, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  const char* fn = "gqa_decode_attention_multi";
+  gqa::DecodeParams p;
+  Plan plan;
+  const int rc = multi_prepare(fn, out, q, k_cache, v_cache, lens, b, n, h, g, d_k, d_v, cap, max_len, scale, dtype,
+                               workspace, workspace_bytes, &p, &plan);
+  if (rc != GQA_OK) return rc;
+  return decode_launch(fn, p, plan, dtype, stream);
+}
+
+int gqa_decode_step_multi(void* out, const void* q, const void* k_new, const void* v_new, void* k_cache,
+                          void* v_cache, int32_t* lens, int b, int n, int h, int g, int d_k, int d_v, int cap,
+                          int max_len, float scale, int dtype, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  const char* fn = "gqa_decode_step_multi";
+  if (!k_new || !v_new) return fail(GQA_ERR_ARG, "%s: null pointer argument", fn);
+  if (max_len < 0 || max_len > INT32_MAX - kMaxTokens) return fail(GQA_ERR_ARG, "%s: max_len=%d out of range", fn, max_len);
+  // every check of both launches runs before the first is enqueued
+  gqa::DecodeParams p;
+  Plan plan;
+  int rc = multi_prepare(fn, out, q, k_cache, v_cache, lens, b, n, h, g, d_k, d_v, cap, max_len + n, scale, dtype,
+                         workspace, workspace_bytes, &p, &plan);
+  if (rc != GQA_OK) return rc;
+  rc = gqa_kv_append_multi(k_cache, v_cache, k_new, v_new, lens, b, n, g, d_k, d_v, cap, max_len, dtype, stream);
+  if (rc != GQA_OK) return rc;
+  return decode_launch(fn, p, plan, dtype, stream);
 }
 
 int gqa_decode_attention(void* out, const void* q, const void* k_cache, const void* v_cache,

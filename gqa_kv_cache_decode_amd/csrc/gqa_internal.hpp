@@ -81,6 +81,7 @@ struct AppendParams {
   int32_t* lens;
   int g, d_k, d_v, cap;
   PagedLayout pg;
+  int n_tok;  // new tokens per sequence (k_new [b][n_tok][g][d_k])
 };
 
 struct DecodeParams {
@@ -108,6 +109,7 @@ struct DecodeParams {
   int2* seg_info;   // merge_kernel: per segment (p0, p1) of its shared pieces, p1 = -1 if none
   float scale_log2; // scale * log2(e)
   PagedLayout pg;   // paged caches (pg.table != nullptr); cap = table_stride << bs_log2
+  int n_tok;        // query tokens per sequence (1: one-token decode; see head_row)
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -181,7 +183,7 @@ hipError_t launch_fold(const FoldParams& p, int b, int dtype, hipStream_t stream
 
 // Workgroups of the decode kernel instance that fit on one compute unit at
 // once (runtime occupancy query, cached; 0 if the runtime cannot say).
-int matrix_workgroups_per_cu(int G, bool fused, bool paged);
+int matrix_workgroups_per_cu(int G, bool fused, bool paged, bool causal = false);
 // Waves per workgroup of the matrix kernel instance for G heads per KV head.
 int matrix_waves(int G);
 int vector_workgroups_per_cu(int dtype, int d, int heads_per_block, bool fused, bool paged);
@@ -223,6 +225,19 @@ __device__ __forceinline__ size_t kv_row(const PagedLayout& pg, int g, int cap, 
   } else {
     return (size_t(s) * g + j) * size_t(cap) + t;
   }
+}
+
+// Multi-token decode: each KV group j serves GV = G * n_tok "virtual heads"
+// v = r * G + i (token r, query head j*G + i), numbered V = j * GV + v over
+// the sequence; q and out are [b][n_tok][h][d], so virtual head V of
+// sequence s lives in row (s * n_tok + r) * h + j * G + i. With n_tok = 1
+// that is row s * h + V. The one-token kernels instantiate the finishing
+// code below with MULTI = false, where the row is s * h + V outright.
+__device__ __forceinline__ size_t head_row(int n_tok, int h, int G, int s, int V) {
+  if (n_tok == 1) return size_t(s) * h + V;
+  const int GV = G * n_tok;
+  const int j = V / GV, v = V - j * GV, r = v / G;
+  return (size_t(s) * n_tok + r) * h + size_t(j) * G + (v - r * G);
 }
 
 // ---------------------------------------------------------------- numerics
@@ -559,15 +574,29 @@ __device__ __forceinline__ int* ticket_of(const DecodeParams& p, const SharedPie
 // sm_m[nh], sm_l[nh] (base-2 max, sum) and sm_o[nh][d] (unnormalised output,
 // 16-byte aligned). A segment inside one workgroup is written out directly by
 // every thread.
-template <typename TOut>
+template <bool MULTI>
+__device__ __forceinline__ size_t out_row(const DecodeParams& p, int s, int V) {
+  if constexpr (MULTI) return head_row(p.n_tok, p.h, p.G, s, V);
+  else return size_t(s) * p.h + V;
+}
+
+template <typename TOut, bool MULTI>
 __device__ void write_piece_out(const DecodeParams& p, int s, int i0, int nh, const float* sm_l,
                                 const float* sm_o) {
   const int d = p.d;
   TOut* out = static_cast<TOut*>(p.out);
-  const size_t out_row0 = (size_t(s) * p.h + i0) * d;
-  for (int idx = threadIdx.x; idx < nh * d; idx += int(blockDim.x)) {
-    const float l = sm_l[idx / d];
-    store_out(out, out_row0 + idx, l > 0.0f ? sm_o[idx] / l : 0.0f);
+  if constexpr (MULTI) {
+    for (int idx = threadIdx.x; idx < nh * d; idx += int(blockDim.x)) {
+      const int hh = idx / d;
+      const float l = sm_l[hh];
+      store_out(out, out_row<true>(p, s, i0 + hh) * d + (idx - hh * d), l > 0.0f ? sm_o[idx] / l : 0.0f);
+    }
+  } else {
+    const size_t out_row0 = (size_t(s) * p.h + i0) * d;
+    for (int idx = threadIdx.x; idx < nh * d; idx += int(blockDim.x)) {
+      const float l = sm_l[idx / d];
+      store_out(out, out_row0 + idx, l > 0.0f ? sm_o[idx] / l : 0.0f);
+    }
   }
 }
 
@@ -599,7 +628,7 @@ __device__ void store_partial(const DecodeParams& p, const SharedPiece& sh, int 
 // rescale factor and denominator live in LDS.
 constexpr int kMergeBatch = 8;
 
-template <typename TOut, int MAXC>
+template <typename TOut, int MAXC, bool MULTI>
 __device__ void merge_segment(const DecodeParams& p, int s, int p0, int n_slots, int i0, int nh,
                               float* sm_merge) {
   const int tid = threadIdx.x;
@@ -673,7 +702,6 @@ __device__ void merge_segment(const DecodeParams& p, int s, int p0, int n_slots,
     __syncthreads();
   }
   TOut* out = static_cast<TOut*>(p.out);
-  const size_t out_row0 = (size_t(s) * p.h + i0) * d;
 #pragma unroll
   for (int c = 0; c < MAXC; ++c) {
     const int c4 = tid + c * nthr;
@@ -681,8 +709,10 @@ __device__ void merge_segment(const DecodeParams& p, int s, int p0, int n_slots,
       const int hh = (4 * c4) / d;
       const float den = run_den[hh];
       const float inv = den > 0.0f ? 1.0f / den : 0.0f;
+      const size_t o0 = MULTI ? out_row<true>(p, s, i0 + hh) * d + (4 * c4 - hh * d)
+                              : (size_t(s) * p.h + i0) * d + 4 * c4;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) store_out(out, out_row0 + 4 * c4 + e, acc[c][e] * inv);
+      for (int e = 0; e < 4; ++e) store_out(out, o0 + e, acc[c][e] * inv);
     }
   }
 }
@@ -690,7 +720,7 @@ __device__ void merge_segment(const DecodeParams& p, int s, int p0, int n_slots,
 // Take the ticket of a shared piece whose partial every thread has just
 // stored (after those stores have completed) and, if this workgroup arrived
 // last, merge the segment and re-zero its ticket.
-template <typename TOut, int MAXC>
+template <typename TOut, int MAXC, bool MULTI>
 __device__ void settle_shared(const DecodeParams& p, const SharedPiece& sh, float* sm_merge, int* sm_flag) {
   wait_stores();
   __syncthreads();
@@ -701,7 +731,7 @@ __device__ void settle_shared(const DecodeParams& p, const SharedPiece& sh, floa
   const bool last = *sm_flag == n_slots - 1;
   __syncthreads();
   if (last) {
-    merge_segment<TOut, MAXC>(p, sh.s, sh.p0, n_slots, sh.i0, sh.nh, sm_merge);
+    merge_segment<TOut, MAXC, MULTI>(p, sh.s, sh.p0, n_slots, sh.i0, sh.nh, sm_merge);
     if (threadIdx.x == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
@@ -743,7 +773,7 @@ struct DeferredPiece {
     if (wave == 0 && state == 1) take(p);
   }
   // every thread, after the range's last piece
-  template <typename TOut, int MAXC>
+  template <typename TOut, int MAXC, bool MULTI = false>
   __device__ void resolve(const DecodeParams& p, float* sm_merge, int* sm_flag) {
     if (state == 0) return;
     if (threadIdx.x < 64 && state == 1) take(p);
@@ -755,7 +785,7 @@ struct DeferredPiece {
     const bool last = *sm_flag == n_slots - 1;
     __syncthreads();
     if (last) {
-      merge_segment<TOut, MAXC>(p, d.s, d.p0, n_slots, d.i0, d.nh, sm_merge);
+      merge_segment<TOut, MAXC, MULTI>(p, d.s, d.p0, n_slots, d.i0, d.nh, sm_merge);
       if (threadIdx.x == 0) __hip_atomic_store(ticket_of(p, d), 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
@@ -763,14 +793,14 @@ struct DeferredPiece {
 
 // Every thread, once the piece's combined state is in LDS: write it out,
 // settle it, or defer it (see DeferredPiece).
-template <typename TOut, int MAXC>
+template <typename TOut, int MAXC, bool MULTI = false>
 __device__ void finish_piece(const DecodeParams& p, const Piece& pc, bool more_follow, int wg, int i0, int nh,
                              const float* sm_m, const float* sm_l, const float* sm_o, DeferredPiece& dfr,
                              float* sm_merge, int* sm_flag) {
   if (p.merge_kernel && pc.tile_begin == 0 && threadIdx.x == 0)
     p.seg_info[size_t(pc.s) * p.ngroups + pc.grp] = make_int2(pc.p0, pc.p0 == pc.p1 ? -1 : pc.p1);
   if (pc.p0 == pc.p1) {
-    write_piece_out<TOut>(p, pc.s, i0, nh, sm_l, sm_o);
+    write_piece_out<TOut, MULTI>(p, pc.s, i0, nh, sm_l, sm_o);
     return;
   }
   SharedPiece sh;
@@ -784,7 +814,7 @@ __device__ void finish_piece(const DecodeParams& p, const Piece& pc, bool more_f
     return;
   }
   store_partial(p, sh, wg, sm_m, sm_l, sm_o, threadIdx.x, blockDim.x);
-  settle_shared<TOut, MAXC>(p, sh, sm_merge, sm_flag);
+  settle_shared<TOut, MAXC, MULTI>(p, sh, sm_merge, sm_flag);
 }
 
 // Fused step: every workgroup counts itself out; the last one, which runs
@@ -802,15 +832,16 @@ __device__ void finish_step(const DecodeParams& p, int* sm_flag) {
 
 // Zero the output rows of sequences that attend nothing; sequence s is
 // handled by workgroup s mod P.
-template <typename TOut>
+template <typename TOut, bool MULTI = false>
 __device__ void zero_empty_sequences(const DecodeParams& p, int wg) {
   TOut* out = static_cast<TOut*>(p.out);
   for (int s = wg; s < p.b; s += p.workgroups) {
     if (attended_len(p, s) != 0) continue;
     if (p.merge_kernel)
       for (int k = threadIdx.x; k < p.ngroups; k += int(blockDim.x)) p.seg_info[size_t(s) * p.ngroups + k] = make_int2(0, -1);
-    const size_t row0 = size_t(s) * p.h * p.d;
-    for (int idx = threadIdx.x; idx < p.h * p.d; idx += int(blockDim.x)) out[row0 + idx] = TOut(0);
+    const int n_tok = MULTI ? p.n_tok : 1;
+    const size_t row0 = size_t(s) * n_tok * p.h * p.d;  // the rows of all its tokens
+    for (int idx = threadIdx.x; idx < n_tok * p.h * p.d; idx += int(blockDim.x)) out[row0 + idx] = TOut(0);
   }
 }
 

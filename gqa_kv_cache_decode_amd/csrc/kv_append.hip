@@ -9,6 +9,9 @@
 // write lens[s] + 1, so every thread used the old length. A length outside
 // [0, cap) leaves the sequence untouched. With a paged cache (p.pg.table set)
 // the slot is row lens[s] mod B of the block the table names for lens[s].
+// With n_tok > 1 tokens per sequence (k_new [b][n_tok][g][d]), token r goes
+// to position lens[s] + r and the length grows by n_tok (all of them must
+// fit below cap, else the sequence is left untouched).
 #include "gqa_internal.hpp"
 
 namespace gqa {
@@ -27,12 +30,13 @@ __global__ __launch_bounds__(256) void kv_append_kernel(AppendParams p, int esiz
   if (threadIdx.x == 0) s_pos = p.lens[s];
   __syncthreads();
   const int pos = s_pos;
-  if (pos < 0 || pos >= p.cap) return;  // precondition violated: change nothing
+  if (pos < 0 || pos > p.cap - p.n_tok) return;  // precondition violated: change nothing
   const int ku = p.d_k * esize / int(sizeof(UNIT));  // units per K row
   const int vu = p.d_v * esize / int(sizeof(UNIT));
-  const int total = p.g * (ku + vu);
-  const UNIT* kn = static_cast<const UNIT*>(p.k_new) + size_t(s) * p.g * ku;
-  const UNIT* vn = static_cast<const UNIT*>(p.v_new) + size_t(s) * p.g * vu;
+  const int kall = p.n_tok * p.g * ku;  // K units of all the sequence's new tokens
+  const int total = kall + p.n_tok * p.g * vu;
+  const UNIT* kn = static_cast<const UNIT*>(p.k_new) + size_t(s) * kall;
+  const UNIT* vn = static_cast<const UNIT*>(p.v_new) + size_t(s) * p.n_tok * p.g * vu;
   UNIT* kc = static_cast<UNIT*>(p.k_cache);
   UNIT* vc = static_cast<UNIT*>(p.v_cache);
   for (int base = 0; base < total; base += PER_THREAD * blockDim.x) {
@@ -43,15 +47,17 @@ __global__ __launch_bounds__(256) void kv_append_kernel(AppendParams p, int esiz
       const int c = base + r * blockDim.x + threadIdx.x;
       dst[r] = nullptr;
       if (c < total) {
-        if (c < p.g * ku) {
-          const int j = c / ku, x = c - j * ku;
+        if (c < kall) {
+          const int row = c / ku, x = c - row * ku;  // row = token * g + head
+          const int tok = row / p.g, j = row - tok * p.g;
           val[r] = kn[c];
-          dst[r] = kc + slot_row(p, s, j, pos) * ku + x;
+          dst[r] = kc + slot_row(p, s, j, pos + tok) * ku + x;
         } else {
-          const int cv = c - p.g * ku;
-          const int j = cv / vu, x = cv - j * vu;
+          const int cv = c - kall;
+          const int row = cv / vu, x = cv - row * vu;
+          const int tok = row / p.g, j = row - tok * p.g;
           val[r] = vn[cv];
-          dst[r] = vc + slot_row(p, s, j, pos) * vu + x;
+          dst[r] = vc + slot_row(p, s, j, pos + tok) * vu + x;
         }
       }
     }
@@ -60,7 +66,7 @@ __global__ __launch_bounds__(256) void kv_append_kernel(AppendParams p, int esiz
       if (dst[r]) *dst[r] = val[r];
   }
   __syncthreads();
-  if (threadIdx.x == 0) p.lens[s] = pos + 1;
+  if (threadIdx.x == 0) p.lens[s] = pos + p.n_tok;
 }
 
 bool aligned(const void* ptr, size_t a) { return (reinterpret_cast<uintptr_t>(ptr) % a) == 0; }
@@ -74,7 +80,7 @@ hipError_t launch_append(const AppendParams& p, int b, int dtype, hipStream_t st
     return kb % a == 0 && vb % a == 0 && aligned(p.k_cache, a) && aligned(p.v_cache, a) &&
            aligned(p.k_new, a) && aligned(p.v_new, a);
   };
-  const size_t row_units16 = size_t(p.g) * (kb + vb) / 16;
+  const size_t row_units16 = size_t(p.n_tok) * p.g * (kb + vb) / 16;
   int threads = int((row_units16 + 3) / 4);
   threads = threads < 64 ? 64 : (threads > 256 ? 256 : ((threads + 63) / 64) * 64);
   if (fits(16)) {

@@ -30,7 +30,7 @@ __global__ __launch_bounds__(kThreads) void merge_partials_kernel(DecodeParams p
   const int grp = seg - s * p.ngroups;
   const int j = grp / p.nhb;
   const int hb = grp - j * p.nhb;
-  const int nh = min(gblk, p.G - hb * gblk);
+  const int nh = min(gblk, p.G * p.n_tok - hb * gblk);  // virtual heads of a multi-token call
   if (hh >= nh) return;
   const int2 info = p.seg_info[seg];
   if (info.y < 0) return;  // written out by the decode kernel (or empty)
@@ -97,7 +97,7 @@ __global__ __launch_bounds__(kThreads) void merge_partials_kernel(DecodeParams p
     }
     const float inv = dsum > 0.0f ? 1.0f / dsum : 0.0f;
     TOut* out = static_cast<TOut*>(p.out);
-    const size_t o0 = (size_t(s) * p.h + size_t(j) * p.G + hb * gblk + hh) * d + 4 * tid;
+    const size_t o0 = head_row(p.n_tok, p.h, p.G, s, j * p.G * p.n_tok + hb * gblk + hh) * d + 4 * tid;
 #pragma unroll
     for (int e = 0; e < 4; ++e) store_out(out, o0 + e, o[e] * inv);
   }

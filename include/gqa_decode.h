@@ -244,6 +244,43 @@ int gqa_decode_layer(void* y, const void* x, const void* w_q, const void* w_k, c
                      int dtype, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Multi-token decode: n new tokens per sequence in one step (speculative or
+ * chunked decoding), the batched form of the MQA review (§2.3: n query
+ * positions of each sequence at once, with an additive mask) with the causal
+ * mask: the new tokens sit at positions L .. L + n - 1 after the cache's L
+ * rows, and token r attends every cached position and the new tokens up to
+ * and including itself (the "LLM inference 05" notes: under the causal mask
+ * a position's K and V depend only on the positions up to it).
+ *   q, out      [b][n][h][d]   (token-major; out same dtype as q)
+ *   k_new, v_new [b][n][g][d]
+ * gqa_kv_append_multi writes token r of sequence s at position lens[s] + r
+ * and adds n to lens[s] (max_len + n <= cap, else GQA_ERR_CAPACITY; a device
+ * length with lens[s] + n > cap leaves that sequence untouched).
+ * gqa_decode_attention_multi: lens[s] is the attended length of the LAST
+ * new token (the cache already holds the n new rows); token r attends
+ * positions t < lens[s] - (n - 1 - r). max_len bounds lens on the host.
+ * gqa_decode_step_multi = append, then attention (two launches; every check
+ * runs before the first); max_len bounds the lengths before the append.
+ * All n tokens of a KV group share each K/V tile: the n * h/g query rows of a
+ * group run together on the matrix cores, so the bytes read do not grow
+ * with n. Attention needs bf16, d_k = d_v = 128 and n * h/g <= 64, else
+ * GQA_ERR_UNSUPPORTED; 1 <= n <= 64 (GQA_ERR_ARG). The workspace is
+ * gqa_decode_multi_workspace_size bytes (that of a one-token call with n * h
+ * query heads), same rules as gqa_decode_attention.
+ */
+size_t gqa_decode_multi_workspace_size(int b, int n, int h, int g, int d_k, int d_v, int dtype);
+int gqa_kv_append_multi(void* k_cache, void* v_cache, const void* k_new, const void* v_new, int32_t* lens, int b,
+                        int n, int g, int d_k, int d_v, int cap, int max_len, int dtype, void* stream);
+int gqa_decode_attention_multi(void* out, const void* q, const void* k_cache, const void* v_cache,
+                               const int32_t* lens, int b, int n, int h, int g, int d_k, int d_v, int cap,
+                               int max_len, float scale, int dtype, void* workspace, size_t workspace_bytes,
+                               void* stream);
+int gqa_decode_step_multi(void* out, const void* q, const void* k_new, const void* v_new, void* k_cache,
+                          void* v_cache, int32_t* lens, int b, int n, int h, int g, int d_k, int d_v, int cap,
+                          int max_len, float scale, int dtype, void* workspace, size_t workspace_bytes,
+                          void* stream);
+
+/*
  * Paged caches. The "LLM inference 05" notes name block-table (vLLM-style)
  * caches without fixing a layout; this library reads them as follows. K and
  * V live in pools of blocks of block_size positions:

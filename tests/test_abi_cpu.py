@@ -289,3 +289,35 @@ def test_paged_rejects(lib):
     assert step(d=48) == _lib.ERR_UNSUPPORTED
     assert step(ws_bytes=64) == _lib.ERR_WORKSPACE
     assert lib.gqa_last_error().decode() != ""
+
+
+def test_multi_rejects_on_the_host(lib):
+    def attend(**kw):
+        a = dict(b=4, n=2, h=64, g=8, d=128, cap=100, max_len=60, dtype=_lib.BF16, ws_bytes=1 << 30)
+        a.update(kw)
+        return lib.gqa_decode_attention_multi(FAKE, FAKE, FAKE, FAKE, FAKE, a["b"], a["n"], a["h"], a["g"], a["d"],
+                                              a["d"], a["cap"], a["max_len"], ctypes.c_float(0.1), a["dtype"], FAKE,
+                                              a["ws_bytes"], None)
+
+    def step(**kw):
+        a = dict(b=4, n=2, h=64, g=8, d=128, cap=100, max_len=60, dtype=_lib.BF16, ws_bytes=1 << 30)
+        a.update(kw)
+        return lib.gqa_decode_step_multi(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, a["b"], a["n"], a["h"], a["g"],
+                                         a["d"], a["d"], a["cap"], a["max_len"], ctypes.c_float(0.1), a["dtype"], FAKE,
+                                         a["ws_bytes"], None)
+    for call in (attend, step):
+        assert call(n=0) == _lib.ERR_ARG
+        assert call(n=65) == _lib.ERR_ARG
+        assert call(n=9) == _lib.ERR_UNSUPPORTED       # 9 x 8 virtual heads > 64
+        assert call(dtype=_lib.F32) == _lib.ERR_UNSUPPORTED
+        assert call(d=64) == _lib.ERR_UNSUPPORTED
+        assert call(h=60) == _lib.ERR_GROUPS
+        assert call(ws_bytes=64) == _lib.ERR_WORKSPACE
+    assert attend(max_len=101) == _lib.ERR_CAPACITY
+    assert step(max_len=99) == _lib.ERR_CAPACITY       # 99 + 2 > 100
+    assert lib.gqa_kv_append_multi(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 3, 8, 128, 128, 100, 98, _lib.BF16,
+                                   None) == _lib.ERR_CAPACITY
+    # the multi-token workspace is that of a one-token call with n * h heads
+    assert lib.gqa_decode_multi_workspace_size(4, 2, 64, 8, 128, 128, _lib.BF16) == \
+        lib.gqa_decode_workspace_size(4, 128, 8, 128, 128, 0, _lib.BF16)
+    assert lib.gqa_decode_multi_workspace_size(4, 0, 64, 8, 128, 128, _lib.BF16) == 0

@@ -1,0 +1,140 @@
+"""GPU parity of multi-token decode (gqa_kv_append_multi, gqa_decode_attention_multi,
+gqa_decode_step_multi) against the fp64 oracle.
+
+n new tokens per sequence sit at positions L .. L + n - 1; token r attends the
+cache and the new tokens up to itself. The kernel runs the n * h/g query rows
+of a KV group together on the matrix cores, one K/V read for all of them.
+Checked: outputs to the decode parity bar (every token, every head) at group
+sizes that take one, two and four 16-row MFMA blocks, lengths whose new
+tokens straddle a tile boundary or fill an empty cache, and the split merge
+done by a second launch; the appended rows bit for bit; n = 1 equal bit for
+bit to the one-token call; a multi-step loop; the Llama-3-70B shape.
+"""
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import assert_parity, to_dev, to_host_bits
+from gqa_kv_cache_decode_amd import api, inputs
+from gqa_kv_cache_decode_amd.workloads import WORKLOADS
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    # b, h, g, n, pre-append lengths
+    (3, 64, 8, 2, [0, 30, 300]),        # 16 virtual heads: one MFMA block, 8 waves
+    (3, 64, 8, 4, [1, 29, 511]),        # 32: two blocks
+    (2, 64, 8, 8, [5, 700]),            # 64: four blocks
+    (4, 28, 4, 3, [0, 62, 63, 200]),    # 21: G = 7
+    (2, 32, 1, 2, [900, 3000]),         # MQA, 64 virtual heads, split merge by a second launch
+    (3, 8, 8, 4, [3, 33, 97]),          # MHA-shaped (G = 1), 4 virtual heads
+    (2, 16, 4, 1, [40, 1000]),          # n = 1
+]
+
+
+def _draw(rng, shape):
+    return inputs.f32_to_bf16_bits(rng.standard_normal(shape).astype(np.float32))
+
+
+class MultiProblem:
+    def __init__(self, b, h, g, n, lens, seed, steps=1):
+        self.b, self.h, self.g, self.n, self.d = b, h, g, n, 128
+        cap = max(lens) + n * steps + 8
+        self.batch = inputs.Batch(seed=seed, b=b, h=h, g=g, d=128, cap=cap, lens=lens, dtype="bf16", poison=True)
+        self.cap = cap
+        self.rng = np.random.default_rng(seed)
+        self.scale = float(np.float32(1.0 / np.sqrt(128)))
+        self.kc, self.vc = to_dev(self.batch.k_cache), to_dev(self.batch.v_cache)
+        self.lens = torch.from_numpy(self.batch.lens.copy()).cuda()
+        self.kc_h, self.vc_h, self.lens_h = self.batch.k_cache.copy(), self.batch.v_cache.copy(), self.batch.lens.copy()
+        self.ws = api.make_multi_workspace(b, n, h, g, 128, 128, torch.bfloat16, "cuda")
+
+    def draw_step(self):
+        return (_draw(self.rng, (self.b, self.n, self.h, 128)), _draw(self.rng, (self.b, self.n, self.g, 128)),
+                _draw(self.rng, (self.b, self.n, self.g, 128)))
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: f"h{c[1]}g{c[2]}n{c[3]}")
+def test_multi_append_then_attention(gpu_lib, oracle_mod, case):
+    b, h, g, n, lens = case
+    pb = MultiProblem(b, h, g, n, lens, seed=1200 + h + g + n)
+    q, kn, vn = pb.draw_step()
+    api.kv_append_multi(pb.kc, pb.vc, to_dev(kn), to_dev(vn), pb.lens, int(max(lens)))
+    out = torch.empty(b, n, h, 128, dtype=torch.bfloat16, device="cuda")
+    api.decode_attention_multi(out, to_dev(q), pb.kc, pb.vc, pb.lens, int(max(lens)) + n, pb.scale, pb.ws)
+    torch.cuda.synchronize()
+    oracle_mod.kv_append_multi(pb.kc_h, pb.vc_h, kn, vn, pb.lens_h)
+    assert np.array_equal(pb.lens.cpu().numpy(), pb.lens_h)
+    assert np.array_equal(to_host_bits(pb.kc), pb.kc_h) and np.array_equal(to_host_bits(pb.vc), pb.vc_h)
+    want = oracle_mod.decode_attention_multi(q, pb.kc_h, pb.vc_h, pb.lens_h, pb.scale)
+    assert_parity(out, want, "bf16", f"multi-token {case}")
+
+
+@pytest.mark.parametrize("case", CASES[:5], ids=lambda c: f"h{c[1]}g{c[2]}n{c[3]}")
+def test_multi_step_loop(gpu_lib, oracle_mod, case):
+    b, h, g, n, lens = case
+    steps = 3
+    pb = MultiProblem(b, h, g, n, lens, seed=1300 + h + g + n, steps=steps)
+    for step in range(steps):
+        q, kn, vn = pb.draw_step()
+        max_len = int(pb.lens_h.max())
+        out = torch.empty(b, n, h, 128, dtype=torch.bfloat16, device="cuda")
+        api.decode_step_multi(out, to_dev(q), to_dev(kn), to_dev(vn), pb.kc, pb.vc, pb.lens, max_len, pb.scale, pb.ws)
+        torch.cuda.synchronize()
+        oracle_mod.kv_append_multi(pb.kc_h, pb.vc_h, kn, vn, pb.lens_h)
+        want = oracle_mod.decode_attention_multi(q, pb.kc_h, pb.vc_h, pb.lens_h, pb.scale)
+        assert_parity(out, want, "bf16", f"multi step {step} {case}")
+        assert np.array_equal(pb.lens.cpu().numpy(), pb.lens_h)
+        assert np.array_equal(to_host_bits(pb.kc), pb.kc_h)
+
+
+def test_one_token_multi_equals_the_one_token_call(gpu_lib):
+    b, h, g = 3, 64, 8
+    pb = MultiProblem(b, h, g, 1, [100, 2000, 4097], seed=1400)
+    q, _, _ = pb.draw_step()
+    max_len = int(pb.lens_h.max())
+    out = torch.empty(b, 1, h, 128, dtype=torch.bfloat16, device="cuda")
+    api.decode_attention_multi(out, to_dev(q), pb.kc, pb.vc, pb.lens, max_len, pb.scale, pb.ws)
+    ref = torch.empty(b, h, 128, dtype=torch.bfloat16, device="cuda")
+    ws = api.make_workspace(b, h, g, 128, 128, max_len, torch.bfloat16, "cuda")
+    api.decode_attention(ref, to_dev(np.ascontiguousarray(q[:, 0])), pb.kc, pb.vc, pb.lens, max_len, pb.scale, ws,
+                         path=api.PATH_MATRIX)
+    torch.cuda.synchronize()
+    assert torch.equal(out[:, 0].view(torch.int16), ref.view(torch.int16))
+
+
+def test_multi_rejects(gpu_lib):
+    pb = MultiProblem(2, 64, 8, 2, [10, 20], seed=1500)
+    q = torch.zeros(2, 2, 64, 128, dtype=torch.bfloat16, device="cuda")
+    out = torch.empty_like(q)
+    with pytest.raises(RuntimeError, match="n \\* h / g"):   # 9 tokens x 8 heads > 64
+        api.decode_attention_multi(torch.empty(2, 9, 64, 128, dtype=torch.bfloat16, device="cuda"),
+                                   torch.zeros(2, 9, 64, 128, dtype=torch.bfloat16, device="cuda"), pb.kc, pb.vc,
+                                   pb.lens, 20, pb.scale, api.make_multi_workspace(2, 9, 64, 8, 128, 128,
+                                                                                   torch.bfloat16, "cuda"))
+    with pytest.raises(RuntimeError, match="CAPACITY"):
+        api.decode_step_multi(out, q, torch.zeros(2, 2, 8, 128, dtype=torch.bfloat16, device="cuda"),
+                              torch.zeros(2, 2, 8, 128, dtype=torch.bfloat16, device="cuda"), pb.kc, pb.vc, pb.lens,
+                              pb.cap - 1, pb.scale, pb.ws)
+    assert np.array_equal(pb.lens.cpu().numpy(), pb.lens_h)  # nothing was enqueued
+
+
+def test_multi_llama3_70b_shape(gpu_lib, oracle_mod):
+    # the Llama-3-70B-shaped batch with 4 speculative tokens per sequence (32 virtual heads per group)
+    wl = WORKLOADS["llama3_70b_gqa_bf16"]
+    n = 4
+    print(f"multi-token step: Llama-3-70B shape, n={n}", flush=True)
+    batch = inputs.Batch(seed=wl.seed, b=wl.b, h=wl.h, g=wl.g, d=wl.d, cap=wl.cap, lens=wl.lens, dtype="bf16",
+                         poison=True)
+    rng = np.random.default_rng(7)
+    q, kn, vn = (_draw(rng, (wl.b, n, x, 128)) for x in (wl.h, wl.g, wl.g))
+    kc, vc = to_dev(batch.k_cache), to_dev(batch.v_cache)
+    lens = torch.from_numpy(batch.lens.copy()).cuda()
+    ws = api.make_multi_workspace(wl.b, n, wl.h, wl.g, 128, 128, torch.bfloat16, "cuda")
+    out = torch.empty(wl.b, n, wl.h, 128, dtype=torch.bfloat16, device="cuda")
+    api.decode_step_multi(out, to_dev(q), to_dev(kn), to_dev(vn), kc, vc, lens, int(batch.lens.max()), wl.scale, ws)
+    torch.cuda.synchronize()
+    kc_h, vc_h, lens_h = batch.k_cache, batch.v_cache, batch.lens.copy()
+    oracle_mod.kv_append_multi(kc_h, vc_h, kn, vn, lens_h)
+    want = oracle_mod.decode_attention_multi(q, kc_h, vc_h, lens_h, wl.scale, threads=16)
+    assert_parity(out, want, "bf16", "multi-token Llama-3-70B shape")
