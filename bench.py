@@ -44,8 +44,12 @@ With --tokens N (N > 1) each step appends N new tokens per sequence and runs
 their causal attention (gqa_decode_step_multi: two launches); bytes are
 those the last token attends, read once for all N tokens.
 
+With --graph the timed steps are captured in one HIP graph and replayed, which
+removes the host's per-call cost (it matters for the small, launch-bound
+workloads).
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--paged B | --tokens N]
-                       [--layer | --fold G]
+                       [--graph] [--layer | --fold G]
 """
 from __future__ import annotations
 
@@ -122,6 +126,8 @@ def main():
                     help="run a 1 GiB device copy first (reference for HBM byte counters)")
     ap.add_argument("--layer", action="store_true",
                     help="time the whole decode layer (projections + step) instead of the step alone")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture the timed steps in one HIP graph and time its replay (no host launch cost)")
     ap.add_argument("--tokens", type=int, default=1, metavar="N",
                     help="new tokens per sequence and step (N > 1: gqa_decode_step_multi, causal)")
     ap.add_argument("--paged", type=int, default=0, metavar="B",
@@ -180,6 +186,9 @@ def main():
 
     if args.paged and (args.unfused or args.paged < 32 or args.paged & (args.paged - 1)):
         print("--paged B: B a power of two >= 32, fused step only", file=sys.stderr)
+        sys.exit(2)
+    if args.graph and args.unfused:
+        print("--graph times the fused step only", file=sys.stderr)
         sys.exit(2)
     if ntok < 1 or (ntok > 1 and (args.paged or args.unfused or wl.dtype != "bf16")):
         print("--tokens N: N >= 1; N > 1 runs bf16 contiguous caches only", file=sys.stderr)
@@ -275,10 +284,24 @@ def main():
     torch.cuda.synchronize()
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
+    if args.graph:
+        # The library only enqueues kernels on the given stream, so the whole
+        # timed loop is captured once (host mirrors of the lengths advance as
+        # the launches are recorded; the device state is untouched until the
+        # replay) and replayed once inside the timed region.
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for k in range(args.steps):
+                total_bytes += step(args.warmup + k, None)
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream()
     wall0 = time.perf_counter()
     t_start.record(stream)
-    for k in range(args.steps):
-        total_bytes += step(args.warmup + k, evs[k])
+    if args.graph:
+        graph.replay()
+    else:
+        for k in range(args.steps):
+            total_bytes += step(args.warmup + k, evs[k])
     t_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
@@ -334,6 +357,7 @@ def main():
                          f"gqa_decode_step_multi ({ntok} tokens: append + causal attention)" if ntok > 1 else
                          "gqa_decode_step"),
             "new_tokens_per_step": ntok, "tokens_per_s": round(wl.b * ntok * args.steps / (elapsed_ms / 1e3), 1),
+            "launch": "one HIP graph of all timed steps" if args.graph else "eager, one call per step",
             "kv_bytes_per_step": int(bytes_per_launch),
         },
         "roofline": {
