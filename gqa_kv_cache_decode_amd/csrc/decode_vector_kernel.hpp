@@ -12,7 +12,7 @@
 // streamed with nontemporal loads. Dot products are summed across the R
 // lanes with DPP row operations; every lane group keeps its own online-softmax
 // state (base-2 running max, sum, unnormalised output), and the groups, then
-// the four waves (through LDS), are merged at the end of each piece of the
+// the waves (four or eight, through LDS), are merged at the end of each piece of the
 // persistent schedule (gqa_internal.hpp), which finish_piece completes.
 //
 // The kernel template lives in this header so that its contiguous-cache

@@ -57,8 +57,7 @@
 
 namespace gqa {
 
-constexpr int kThreads = 256;  // workgroup size of the vector decode and merge kernels
-constexpr int kWaves = kThreads / 64;
+constexpr int kThreads = 256;  // workgroup size of the merge kernel (and of the 4-wave decode instances)
 constexpr int kTile = 32;             // positions per wave step
 constexpr int kUnitTiles = 4;         // tiles per schedule unit
 constexpr int kMaxWorkgroups = 2048;  // persistent grid bound (workspace sizing)

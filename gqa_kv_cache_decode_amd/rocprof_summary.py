@@ -22,6 +22,7 @@ import argparse
 import csv
 import hashlib
 import os
+import re
 import statistics
 
 PKG = os.path.dirname(os.path.abspath(__file__))
@@ -34,12 +35,19 @@ DECODE_SOURCES = ("gqa_internal.hpp", "decode_matrix.hip", "decode_vector_kernel
                   "decode_vector_paged.hip", "merge_partials.hip")
 
 
+def _code_only(text: str) -> str:
+    """Source text without comments and blank space, so that a comment edit keeps the stamp."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
     csrc = os.path.join(PKG, "csrc")
     for name in DECODE_SOURCES:
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(name.encode() + b"\0" + f.read())
+        with open(os.path.join(csrc, name), encoding="utf-8") as f:
+            h.update(name.encode() + b"\0" + _code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 
