@@ -137,8 +137,9 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (every box here has one GPU; "
-              "the sharded design is described in DESIGN.md)", file=sys.stderr)
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported. Across GPUs the step would be "
+              "sharded by sequence (or by KV head) with no exchange, so its per-GPU work is the one-GPU "
+              "step on that GPU's share.", file=sys.stderr)
         sys.exit(2)
 
     import torch
