@@ -10,7 +10,12 @@
  *                               every cached position, the new one included
  *
  * in that order on one stream, or both at once with gqa_decode_step (one
- * launch). This is the per-layer decode loop of the
+ * launch). Around that core the library also offers: the same three calls on
+ * paged caches (*_paged), n new tokens per sequence with a causal mask
+ * (*_multi), the layer's projections and the whole layer step
+ * (gqa_pack_weight, gqa_linear, gqa_decode_layer), and the mean-fold of KV
+ * heads that turns an MHA cache into a GQA one (gqa_fold_kv_heads).
+ * The step is the per-layer decode loop of the
  * "LLM inference 05" notes (albangk): push K, push V, then attend; and the
  * incremental attention of the "Fast Transformer Decoding: One Write-Head is
  * All You Need" review (velog), §2.4 Multi-head Attention (Incremental) and
