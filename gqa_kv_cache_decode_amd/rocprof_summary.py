@@ -70,9 +70,12 @@ def by_grid_summary(trace_csv: str) -> str:
         key = (r["Kernel_Name"][:110], int(r["Grid_Size_X"]) // max(1, int(r["Workgroup_Size_X"])))
         groups.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
     lines = ["", "# per launch shape (kernel trace)",
-             f"{'calls':>6} {'avg_us':>10} {'min_us':>10} {'max_us':>10} {'wgs':>8}  kernel"]
+             f"{'calls':>6} {'avg_us':>9} {'p10_us':>9} {'p50_us':>9} {'p90_us':>9} {'min_us':>9} {'max_us':>9} "
+             f"{'wgs':>7}  kernel"]
     for (name, wgs), d in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
-        lines.append(f"{len(d):6d} {statistics.mean(d):10.3f} {min(d):10.3f} {max(d):10.3f} {wgs:8d}  {name}")
+        q = statistics.quantiles(d, n=10) if len(d) > 1 else [d[0]] * 9
+        lines.append(f"{len(d):6d} {statistics.mean(d):9.3f} {q[0]:9.3f} {q[4]:9.3f} {q[8]:9.3f} {min(d):9.3f} "
+                     f"{max(d):9.3f} {wgs:7d}  {name}")
     return "\n".join(lines) + "\n"
 
 
