@@ -16,8 +16,10 @@
 // persistent schedule (gqa_internal.hpp), which finish_piece completes.
 //
 // The kernel template lives in this header so that its contiguous-cache
-// instances (decode_vector.hip) and paged-cache instances
-// (decode_vector_paged.hip) compile as two translation units in parallel.
+// instances (decode_vector.hip), paged-cache instances
+// (decode_vector_paged.hip) and multi-token instances
+// (decode_vector_multi.hip) compile as translation units of their own, in
+// parallel.
 #pragma once
 
 #include "gqa_internal.hpp"
@@ -79,11 +81,12 @@ struct NewRow {
 
 // One 32-position tile starting at row t0 (FULL: all rows valid). FUSED: the
 // row nr.local is the appended token, read from its new rows and stored into
-// the cache by the lanes that load it.
-template <typename T, int D, int HB, bool FULL, bool FUSED>
+// the cache by the lanes that load it. CAUSAL (multi-token decode): head hh
+// of the block only sees rows < lim[hh] (<= nvalid), its token's limit.
+template <typename T, int D, int HB, bool FULL, bool FUSED, bool CAUSAL = false>
 __device__ __forceinline__ void tile_step(VState<T, D, HB>& st, const float (&qf)[HB][Shape<T, D, HB>::VEC],
                                           const T* kbase, const T* vbase, int t0, int nvalid, int rg,
-                                          const NewRow<T>& nr) {
+                                          const NewRow<T>& nr, const int* lim = nullptr) {
   using S = Shape<T, D, HB>;
   constexpr int VEC = S::VEC, U = S::U, RPW = S::RPW, R = S::R;
 #pragma unroll
@@ -118,7 +121,8 @@ __device__ __forceinline__ void tile_step(VState<T, D, HB>& st, const float (&qf
 #pragma unroll
         for (int e = 0; e < VEC; ++e) part = fmaf(qf[hh][e], kf[e], part);
         part = group_sum<R>(part);
-        sc[u][hh] = ok[u] ? part : kNegInf;
+        if constexpr (CAUSAL) sc[u][hh] = (ok[u] && (sb * U + u) * RPW + rg < lim[hh]) ? part : kNegInf;
+        else sc[u][hh] = ok[u] ? part : kNegInf;
       }
     }
     float vf[U][VEC];
@@ -161,7 +165,10 @@ constexpr int vector_waves_of() {
 
 // PAGED: K/V live in block pools addressed through the block table (one
 // lookup per 32-position tile); otherwise in contiguous [b][g][cap][d] caches.
-template <typename T, int D, int HB, bool FUSED, bool PAGED>
+// CAUSAL: multi-token decode; each KV group has GV = G * n_tok virtual heads
+// (token r, head i; see head_row), taken HB at a time, and token r's heads
+// see positions < L - (n_tok - 1 - r).
+template <typename T, int D, int HB, bool FUSED, bool PAGED, bool CAUSAL = false>
 __global__ __launch_bounds__((vector_waves_of<T, D, HB>() * 64)) void decode_vector_kernel(DecodeParams p) {
   constexpr int WAVES = vector_waves_of<T, D, HB>();
   constexpr int THREADS = WAVES * 64;
@@ -185,7 +192,8 @@ __global__ __launch_bounds__((vector_waves_of<T, D, HB>() * 64)) void decode_vec
   const int col = lane % R;
   const int rg = lane / R;
 
-  zero_empty_sequences<T>(p, wg);
+  zero_empty_sequences<T, CAUSAL>(p, wg);
+  const int GV = CAUSAL ? p.G * p.n_tok : p.G;  // (virtual) heads per KV group
 
   PieceWalker<false> walker;
   walker.init(p, wg);
@@ -196,8 +204,8 @@ __global__ __launch_bounds__((vector_waves_of<T, D, HB>() * 64)) void decode_vec
     const int s = pc.s;
     const int j = pc.grp / p.nhb;
     const int hb = pc.grp - j * p.nhb;
-    const int i0 = j * p.G + hb * HB;
-    const int nh = min(HB, p.G - hb * HB);
+    const int i0 = j * GV + hb * HB;
+    const int nh = min(HB, GV - hb * HB);
 
     // query rows of the head block, widened and pre-multiplied by scale*log2(e)
     float qf[HB][VEC];
@@ -205,7 +213,9 @@ __global__ __launch_bounds__((vector_waves_of<T, D, HB>() * 64)) void decode_vec
 #pragma unroll
     for (int hh = 0; hh < HB; ++hh) {
       if (hh < nh) {
-        const u32x4 raw = *reinterpret_cast<const u32x4*>(qrow + size_t(hh) * D);
+        const T* qp = CAUSAL ? static_cast<const T*>(p.q) + head_row(p.n_tok, p.h, p.G, s, i0 + hh) * D + col * VEC
+                             : qrow + size_t(hh) * D;
+        const u32x4 raw = *reinterpret_cast<const u32x4*>(qp);
         widen16<T>(raw, qf[hh]);
 #pragma unroll
         for (int e = 0; e < VEC; ++e) qf[hh][e] *= p.scale_log2;
@@ -227,6 +237,11 @@ __global__ __launch_bounds__((vector_waves_of<T, D, HB>() * 64)) void decode_vec
     const T* vbase = static_cast<const T*>(p.v_cache) + kv_head * p.cap * D + col * VEC;
     const int t_end = min(pc.L, pc.tile_end * kTile);
     const int pos_new = FUSED ? pc.L - 1 : -1;  // the appended token (fused step)
+    // CAUSAL: how many of the last positions head hh does not see
+    int hide[HB];
+#pragma unroll
+    for (int hh = 0; hh < HB; ++hh) hide[hh] = (CAUSAL && hh < nh) ? p.n_tok - 1 - (hb * HB + hh) / p.G : 0;
+    const int hide_max = CAUSAL ? p.n_tok - 1 : 0;
     for (int tile = pc.tile_begin + w; tile < pc.tile_end; tile += WAVES) {
       const int t0 = tile * kTile;
       const int nvalid = t_end - t0;
@@ -250,8 +265,13 @@ __global__ __launch_bounds__((vector_waves_of<T, D, HB>() * 64)) void decode_vec
         nr.kdst = static_cast<T*>(p.k_cache) + new_row * D + col * VEC;
         nr.vdst = static_cast<T*>(p.v_cache) + new_row * D + col * VEC;
         tile_step<T, D, HB, false, true>(st, qf, kb, vb, tb, nvalid, rg, nr);
-      } else if (nvalid >= kTile) {
+      } else if (nvalid >= kTile && (!CAUSAL || pc.L - t0 - hide_max >= kTile)) {
         tile_step<T, D, HB, true, false>(st, qf, kb, vb, tb, kTile, rg, NewRow<T>{});
+      } else if constexpr (CAUSAL) {
+        int lim[HB];
+#pragma unroll
+        for (int hh = 0; hh < HB; ++hh) lim[hh] = min(nvalid, pc.L - t0 - hide[hh]);
+        tile_step<T, D, HB, false, false, true>(st, qf, kb, vb, tb, nvalid, rg, NewRow<T>{}, lim);
       } else {
         tile_step<T, D, HB, false, false>(st, qf, kb, vb, tb, nvalid, rg, NewRow<T>{});
       }
@@ -308,61 +328,63 @@ __global__ __launch_bounds__((vector_waves_of<T, D, HB>() * 64)) void decode_vec
       }
     }
     __syncthreads();
-    finish_piece<T, MAXC>(p, pc, walker.more(), wg, i0, nh, fin_m, fin_l, &fin_o[0][0], dfr, sm_merge,
+    finish_piece<T, MAXC, CAUSAL>(p, pc, walker.more(), wg, i0, nh, fin_m, fin_l, &fin_o[0][0], dfr, sm_merge,
                                  &s_flag);
   }
-  dfr.resolve<T, MAXC>(p, sm_merge, &s_flag);
+  dfr.resolve<T, MAXC, CAUSAL>(p, sm_merge, &s_flag);
   if (FUSED) finish_step(p, &s_flag);
 }
 
-template <typename T, int D, int HB, bool PAGED>
+// CAUSAL instances exist without FUSED (the multi-token append is its own launch).
+template <typename T, int D, int HB, bool PAGED, bool CAUSAL>
 hipError_t launch_one(const DecodeParams& p, hipStream_t stream) {
-  if (p.fused)
-    hipLaunchKernelGGL((decode_vector_kernel<T, D, HB, true, PAGED>), dim3(p.workgroups),
-                       dim3(vector_waves_of<T, D, HB>() * 64), 0, stream, p);
+  const dim3 grid(p.workgroups), block(vector_waves_of<T, D, HB>() * 64);
+  if constexpr (CAUSAL)
+    hipLaunchKernelGGL((decode_vector_kernel<T, D, HB, false, PAGED, true>), grid, block, 0, stream, p);
+  else if (p.fused)
+    hipLaunchKernelGGL((decode_vector_kernel<T, D, HB, true, PAGED>), grid, block, 0, stream, p);
   else
-    hipLaunchKernelGGL((decode_vector_kernel<T, D, HB, false, PAGED>), dim3(p.workgroups),
-                       dim3(vector_waves_of<T, D, HB>() * 64), 0, stream, p);
+    hipLaunchKernelGGL((decode_vector_kernel<T, D, HB, false, PAGED>), grid, block, 0, stream, p);
   return hipGetLastError();
 }
 
-template <typename T, int D, bool PAGED>
+template <typename T, int D, bool PAGED, bool CAUSAL>
 hipError_t launch_d(const DecodeParams& p, hipStream_t stream) {
   switch (p.gblk) {
-    case 1: return launch_one<T, D, 1, PAGED>(p, stream);
-    case 2: return launch_one<T, D, 2, PAGED>(p, stream);
-    case 4: return launch_one<T, D, 4, PAGED>(p, stream);
-    default: return launch_one<T, D, 8, PAGED>(p, stream);
+    case 1: return launch_one<T, D, 1, PAGED, CAUSAL>(p, stream);
+    case 2: return launch_one<T, D, 2, PAGED, CAUSAL>(p, stream);
+    case 4: return launch_one<T, D, 4, PAGED, CAUSAL>(p, stream);
+    default: return launch_one<T, D, 8, PAGED, CAUSAL>(p, stream);
   }
 }
 
-template <typename T, bool PAGED>
+template <typename T, bool PAGED, bool CAUSAL>
 hipError_t launch_t(const DecodeParams& p, hipStream_t stream) {
   switch (p.d) {
-    case 16: return launch_d<T, 16, PAGED>(p, stream);
-    case 32: return launch_d<T, 32, PAGED>(p, stream);
-    case 64: return launch_d<T, 64, PAGED>(p, stream);
-    case 128: return launch_d<T, 128, PAGED>(p, stream);
-    case 256: return launch_d<T, 256, PAGED>(p, stream);
+    case 16: return launch_d<T, 16, PAGED, CAUSAL>(p, stream);
+    case 32: return launch_d<T, 32, PAGED, CAUSAL>(p, stream);
+    case 64: return launch_d<T, 64, PAGED, CAUSAL>(p, stream);
+    case 128: return launch_d<T, 128, PAGED, CAUSAL>(p, stream);
+    case 256: return launch_d<T, 256, PAGED, CAUSAL>(p, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
-template <bool PAGED>
+template <bool PAGED, bool CAUSAL = false>
 hipError_t launch_vector(const DecodeParams& p, int dtype, hipStream_t stream) {
-  return dtype == 0 ? launch_t<float, PAGED>(p, stream) : launch_t<uint16_t, PAGED>(p, stream);
+  return dtype == 0 ? launch_t<float, PAGED, CAUSAL>(p, stream) : launch_t<uint16_t, PAGED, CAUSAL>(p, stream);
 }
 
 
-template <typename T, int D, bool FUSED, bool PAGED>
+template <typename T, int D, bool FUSED, bool PAGED, bool CAUSAL>
 int occupancy_d(int hb) {
   int n = 0;
   hipError_t e;
   switch (hb) {
-    case 1: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_vector_kernel<T, D, 1, FUSED, PAGED>, vector_waves_of<T, D, 1>() * 64, 0); break;
-    case 2: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_vector_kernel<T, D, 2, FUSED, PAGED>, vector_waves_of<T, D, 2>() * 64, 0); break;
-    case 4: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_vector_kernel<T, D, 4, FUSED, PAGED>, vector_waves_of<T, D, 4>() * 64, 0); break;
-    default: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_vector_kernel<T, D, 8, FUSED, PAGED>, vector_waves_of<T, D, 8>() * 64, 0); break;
+    case 1: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_vector_kernel<T, D, 1, FUSED, PAGED, CAUSAL>, vector_waves_of<T, D, 1>() * 64, 0); break;
+    case 2: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_vector_kernel<T, D, 2, FUSED, PAGED, CAUSAL>, vector_waves_of<T, D, 2>() * 64, 0); break;
+    case 4: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_vector_kernel<T, D, 4, FUSED, PAGED, CAUSAL>, vector_waves_of<T, D, 4>() * 64, 0); break;
+    default: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_vector_kernel<T, D, 8, FUSED, PAGED, CAUSAL>, vector_waves_of<T, D, 8>() * 64, 0); break;
   }
   if (e != hipSuccess || n <= 0) {
     (void)hipGetLastError();
@@ -371,22 +393,27 @@ int occupancy_d(int hb) {
   return n;
 }
 
-template <typename T, bool FUSED, bool PAGED>
+template <typename T, bool FUSED, bool PAGED, bool CAUSAL>
 int occupancy_t(int d, int hb) {
   switch (d) {
-    case 16: return occupancy_d<T, 16, FUSED, PAGED>(hb);
-    case 32: return occupancy_d<T, 32, FUSED, PAGED>(hb);
-    case 64: return occupancy_d<T, 64, FUSED, PAGED>(hb);
-    case 128: return occupancy_d<T, 128, FUSED, PAGED>(hb);
-    default: return occupancy_d<T, 256, FUSED, PAGED>(hb);
+    case 16: return occupancy_d<T, 16, FUSED, PAGED, CAUSAL>(hb);
+    case 32: return occupancy_d<T, 32, FUSED, PAGED, CAUSAL>(hb);
+    case 64: return occupancy_d<T, 64, FUSED, PAGED, CAUSAL>(hb);
+    case 128: return occupancy_d<T, 128, FUSED, PAGED, CAUSAL>(hb);
+    default: return occupancy_d<T, 256, FUSED, PAGED, CAUSAL>(hb);
   }
 }
 
 // Workgroups of one instance that fit on a compute unit (0 if unknown).
-template <bool PAGED>
+template <bool PAGED, bool CAUSAL = false>
 int vector_occupancy(int dtype, int d, int hb, bool fused) {
-  if (fused) return dtype == 0 ? occupancy_t<float, true, PAGED>(d, hb) : occupancy_t<uint16_t, true, PAGED>(d, hb);
-  return dtype == 0 ? occupancy_t<float, false, PAGED>(d, hb) : occupancy_t<uint16_t, false, PAGED>(d, hb);
+  if constexpr (CAUSAL) {
+    return dtype == 0 ? occupancy_t<float, false, PAGED, true>(d, hb) : occupancy_t<uint16_t, false, PAGED, true>(d, hb);
+  } else {
+    if (fused)
+      return dtype == 0 ? occupancy_t<float, true, PAGED, false>(d, hb) : occupancy_t<uint16_t, true, PAGED, false>(d, hb);
+    return dtype == 0 ? occupancy_t<float, false, PAGED, false>(d, hb) : occupancy_t<uint16_t, false, PAGED, false>(d, hb);
+  }
 }
 
 

@@ -126,7 +126,7 @@ int plan_decode(int b, int h, int g, int d_k, int d_v, int cap, int max_len, int
     // 8-wave one keep enough loads in flight), never more than fit at once, so
     // the persistent grid runs in a single round.
     int fit = chosen == GQA_PATH_MATRIX ? gqa::matrix_workgroups_per_cu(G, fused, paged, causal)
-                                        : gqa::vector_workgroups_per_cu(dtype, d_k, plan->gblk, fused, paged);
+                                        : gqa::vector_workgroups_per_cu(dtype, d_k, plan->gblk, fused, paged, causal);
     if (fit <= 0) fit = 2;  // no device to ask: assume the common case
     const int per_cu_max = 8 / waves;
     const int per_cu = fit < per_cu_max ? fit : per_cu_max;
@@ -493,12 +493,11 @@ int multi_prepare(const char* fn, void* out, const void* q, const void* k_cache,
   if (h <= 0 || g <= 0 || (long long)n * h > kMaxHeads)
     return fail(GQA_ERR_ARG, "%s: h=%d, g=%d, n=%d (n * h at most %d)", fn, h, g, n, kMaxHeads);
   if (h % g != 0) return fail(GQA_ERR_GROUPS, "h=%d query heads cannot be split into g=%d equal groups", h, g);
-  if (dtype != GQA_DTYPE_BF16 || d_k != 128 || d_v != 128 || n * (h / g) > gqa::kMatrixMaxGroup)
-    return fail(GQA_ERR_UNSUPPORTED, "%s: needs bf16, d_k = d_v = 128 and n * h / g <= %d (n=%d, h/g=%d)", fn,
-                gqa::kMatrixMaxGroup, n, h / g);
+  // planned like a one-token call with n * h heads: the matrix path when it
+  // applies (bf16, d = 128, n * h/g in [3, 64]), else the vector path
   const int rc = decode_prepare(fn, out, q, const_cast<void*>(k_cache), const_cast<void*>(v_cache),
                                 const_cast<int32_t*>(lens), nullptr, nullptr, b, n * h, g, d_k, d_v, cap, max_len,
-                                scale, dtype, workspace, workspace_bytes, GQA_PATH_MATRIX, 0, 0, p, plan, nullptr,
+                                scale, dtype, workspace, workspace_bytes, GQA_PATH_AUTO, 0, 0, p, plan, nullptr,
                                 n > 1);
   if (rc != GQA_OK) return rc;
   p->h = h;

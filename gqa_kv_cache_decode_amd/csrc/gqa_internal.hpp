@@ -185,10 +185,12 @@ hipError_t launch_fold(const FoldParams& p, int b, int dtype, hipStream_t stream
 int matrix_workgroups_per_cu(int G, bool fused, bool paged, bool causal = false);
 // Waves per workgroup of the matrix kernel instance for G heads per KV head.
 int matrix_waves(int G);
-int vector_workgroups_per_cu(int dtype, int d, int heads_per_block, bool fused, bool paged);
-// The paged-cache instances of the vector kernel (their own translation unit).
+int vector_workgroups_per_cu(int dtype, int d, int heads_per_block, bool fused, bool paged, bool causal = false);
+// The paged-cache and multi-token instances of the vector kernel (translation units of their own).
 hipError_t launch_decode_vector_paged(const DecodeParams& p, int dtype, hipStream_t stream);
 int vector_occupancy_paged(int dtype, int d, int heads_per_block, bool fused);
+hipError_t launch_decode_vector_multi(const DecodeParams& p, int dtype, hipStream_t stream);
+int vector_occupancy_multi(int dtype, int d, int heads_per_block);
 // Waves per workgroup of the vector kernel instance for this dtype, d and head block.
 int vector_waves(int dtype, int d, int heads_per_block);
 

@@ -267,11 +267,12 @@ int gqa_decode_layer(void* y, const void* x, const void* w_q, const void* w_k, c
  * gqa_decode_step_multi = append, then attention (two launches; every check
  * runs before the first); max_len bounds the lengths before the append.
  * All n tokens of a KV group share each K/V tile: the n * h/g query rows of a
- * group run together on the matrix cores, so the bytes read do not grow
- * with n. Attention needs bf16, d_k = d_v = 128 and n * h/g <= 64, else
- * GQA_ERR_UNSUPPORTED; 1 <= n <= 64 (GQA_ERR_ARG). The workspace is
- * gqa_decode_multi_workspace_size bytes (that of a one-token call with n * h
- * query heads), same rules as gqa_decode_attention.
+ * group run together (on the matrix cores for bf16, d = 128 and
+ * n * h/g <= 64; otherwise on the vector path, a head block at a time), so
+ * the bytes read do not grow with n. Element types and head dims as for
+ * gqa_decode_attention; 1 <= n <= 64 and n * h <= 4096 (GQA_ERR_ARG). The
+ * workspace is gqa_decode_multi_workspace_size bytes (that of a one-token
+ * call with n * h query heads), same rules as gqa_decode_attention.
  */
 size_t gqa_decode_multi_workspace_size(int b, int n, int h, int g, int d_k, int d_v, int dtype);
 int gqa_kv_append_multi(void* k_cache, void* v_cache, const void* k_new, const void* v_new, int32_t* lens, int b,

@@ -308,9 +308,9 @@ def test_multi_rejects_on_the_host(lib):
     for call in (attend, step):
         assert call(n=0) == _lib.ERR_ARG
         assert call(n=65) == _lib.ERR_ARG
-        assert call(n=9) == _lib.ERR_UNSUPPORTED       # 9 x 8 virtual heads > 64
-        assert call(dtype=_lib.F32) == _lib.ERR_UNSUPPORTED
-        assert call(d=64) == _lib.ERR_UNSUPPORTED
+        assert call(n=64, h=128, g=8) == _lib.ERR_ARG  # 64 x 128 query rows > 4096
+        assert call(dtype=7) == _lib.ERR_UNSUPPORTED
+        assert call(d=48) == _lib.ERR_UNSUPPORTED
         assert call(h=60) == _lib.ERR_GROUPS
         assert call(ws_bytes=64) == _lib.ERR_WORKSPACE
     assert attend(max_len=101) == _lib.ERR_CAPACITY

@@ -2,13 +2,15 @@
 gqa_decode_step_multi) against the fp64 oracle.
 
 n new tokens per sequence sit at positions L .. L + n - 1; token r attends the
-cache and the new tokens up to itself. The kernel runs the n * h/g query rows
-of a KV group together on the matrix cores, one K/V read for all of them.
-Checked: outputs to the decode parity bar (every token, every head) at group
-sizes that take one, two and four 16-row MFMA blocks, lengths whose new
-tokens straddle a tile boundary or fill an empty cache, and the split merge
-done by a second launch; the appended rows bit for bit; n = 1 equal bit for
-bit to the one-token call; a multi-step loop; the Llama-3-70B shape.
+cache and the new tokens up to itself. The kernels run the n * h/g query rows
+of a KV group together (on the matrix cores, or a head block at a time on the
+vector path), one K/V read for all of them. Checked: outputs to the decode
+parity bar (every token, every head) at group sizes that take one, two and
+four 16-row MFMA blocks, the vector path (fp32, other head dims, fewer than
+three or more than 64 virtual heads), lengths whose new tokens straddle a
+tile boundary or fill an empty cache, and the split merge done by a second
+launch; the appended rows bit for bit; n = 1 equal bit for bit to the
+one-token call; a multi-step loop; the Llama-3-70B shape.
 """
 import numpy as np
 import pytest
@@ -21,7 +23,7 @@ from gqa_kv_cache_decode_amd.workloads import WORKLOADS
 pytestmark = pytest.mark.gpu
 
 CASES = [
-    # b, h, g, n, pre-append lengths
+    # b, h, g, n, pre-append lengths[, dtype, d]
     (3, 64, 8, 2, [0, 30, 300]),        # 16 virtual heads: one MFMA block, 8 waves
     (3, 64, 8, 4, [1, 29, 511]),        # 32: two blocks
     (2, 64, 8, 8, [5, 700]),            # 64: four blocks
@@ -29,63 +31,87 @@ CASES = [
     (2, 32, 1, 2, [900, 3000]),         # MQA, 64 virtual heads, split merge by a second launch
     (3, 8, 8, 4, [3, 33, 97]),          # MHA-shaped (G = 1), 4 virtual heads
     (2, 16, 4, 1, [40, 1000]),          # n = 1
+    (3, 8, 8, 2, [3, 33, 97]),          # 2 virtual heads: the vector path
+    (2, 72, 8, 8, [64, 300]),           # 72 virtual heads (> 64): the vector path, head blocks of 8
+    (3, 8, 4, 3, [0, 31, 100], "f32", 16),    # fp32 (vector path), the tiny shape's head dim
+    (2, 16, 4, 4, [10, 200], "bf16", 64),     # bf16, d = 64 (vector path)
+    (2, 12, 3, 2, [70, 33], "f32", 256),      # fp32, d = 256
 ]
 
 
-def _draw(rng, shape):
-    return inputs.f32_to_bf16_bits(rng.standard_normal(shape).astype(np.float32))
+def _unpack(case):
+    b, h, g, n, lens = case[:5]
+    dtype = case[5] if len(case) > 5 else "bf16"
+    d = case[6] if len(case) > 6 else 128
+    return b, h, g, n, lens, dtype, d
+
+
+def _draw(rng, shape, dtype="bf16"):
+    x = rng.standard_normal(shape).astype(np.float32)
+    return inputs.f32_to_bf16_bits(x) if dtype == "bf16" else x
 
 
 class MultiProblem:
-    def __init__(self, b, h, g, n, lens, seed, steps=1):
-        self.b, self.h, self.g, self.n, self.d = b, h, g, n, 128
+    def __init__(self, b, h, g, n, lens, seed, steps=1, dtype="bf16", d=128):
+        self.b, self.h, self.g, self.n, self.d, self.dtype = b, h, g, n, d, dtype
+        self.tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
         cap = max(lens) + n * steps + 8
-        self.batch = inputs.Batch(seed=seed, b=b, h=h, g=g, d=128, cap=cap, lens=lens, dtype="bf16", poison=True)
+        self.batch = inputs.Batch(seed=seed, b=b, h=h, g=g, d=d, cap=cap, lens=lens, dtype=dtype, poison=True)
         self.cap = cap
         self.rng = np.random.default_rng(seed)
-        self.scale = float(np.float32(1.0 / np.sqrt(128)))
+        self.scale = float(np.float32(1.0 / np.sqrt(d)))
         self.kc, self.vc = to_dev(self.batch.k_cache), to_dev(self.batch.v_cache)
         self.lens = torch.from_numpy(self.batch.lens.copy()).cuda()
         self.kc_h, self.vc_h, self.lens_h = self.batch.k_cache.copy(), self.batch.v_cache.copy(), self.batch.lens.copy()
-        self.ws = api.make_multi_workspace(b, n, h, g, 128, 128, torch.bfloat16, "cuda")
+        self.ws = api.make_multi_workspace(b, n, h, g, d, d, self.tdt, "cuda")
 
     def draw_step(self):
-        return (_draw(self.rng, (self.b, self.n, self.h, 128)), _draw(self.rng, (self.b, self.n, self.g, 128)),
-                _draw(self.rng, (self.b, self.n, self.g, 128)))
+        return (_draw(self.rng, (self.b, self.n, self.h, self.d), self.dtype),
+                _draw(self.rng, (self.b, self.n, self.g, self.d), self.dtype),
+                _draw(self.rng, (self.b, self.n, self.g, self.d), self.dtype))
 
 
-@pytest.mark.parametrize("case", CASES, ids=lambda c: f"h{c[1]}g{c[2]}n{c[3]}")
+def _id(c):
+    b, h, g, n, lens, dtype, d = _unpack(c)
+    return f"h{h}g{g}n{n}" + ("" if (dtype, d) == ("bf16", 128) else f"-{dtype}-d{d}")
+
+
+def _same_bits(a, b):
+    return np.array_equal(np.ascontiguousarray(a).view(np.uint8), np.ascontiguousarray(b).view(np.uint8))
+
+
+@pytest.mark.parametrize("case", CASES, ids=_id)
 def test_multi_append_then_attention(gpu_lib, oracle_mod, case):
-    b, h, g, n, lens = case
-    pb = MultiProblem(b, h, g, n, lens, seed=1200 + h + g + n)
+    b, h, g, n, lens, dtype, d = _unpack(case)
+    pb = MultiProblem(b, h, g, n, lens, seed=1200 + h + g + n + d, dtype=dtype, d=d)
     q, kn, vn = pb.draw_step()
     api.kv_append_multi(pb.kc, pb.vc, to_dev(kn), to_dev(vn), pb.lens, int(max(lens)))
-    out = torch.empty(b, n, h, 128, dtype=torch.bfloat16, device="cuda")
+    out = torch.empty(b, n, h, d, dtype=pb.tdt, device="cuda")
     api.decode_attention_multi(out, to_dev(q), pb.kc, pb.vc, pb.lens, int(max(lens)) + n, pb.scale, pb.ws)
     torch.cuda.synchronize()
     oracle_mod.kv_append_multi(pb.kc_h, pb.vc_h, kn, vn, pb.lens_h)
     assert np.array_equal(pb.lens.cpu().numpy(), pb.lens_h)
-    assert np.array_equal(to_host_bits(pb.kc), pb.kc_h) and np.array_equal(to_host_bits(pb.vc), pb.vc_h)
+    assert _same_bits(to_host_bits(pb.kc), pb.kc_h) and _same_bits(to_host_bits(pb.vc), pb.vc_h)
     want = oracle_mod.decode_attention_multi(q, pb.kc_h, pb.vc_h, pb.lens_h, pb.scale)
-    assert_parity(out, want, "bf16", f"multi-token {case}")
+    assert_parity(out, want, dtype, f"multi-token {case}")
 
 
-@pytest.mark.parametrize("case", CASES[:5], ids=lambda c: f"h{c[1]}g{c[2]}n{c[3]}")
+@pytest.mark.parametrize("case", CASES[:5] + CASES[7:], ids=_id)
 def test_multi_step_loop(gpu_lib, oracle_mod, case):
-    b, h, g, n, lens = case
+    b, h, g, n, lens, dtype, d = _unpack(case)
     steps = 3
-    pb = MultiProblem(b, h, g, n, lens, seed=1300 + h + g + n, steps=steps)
+    pb = MultiProblem(b, h, g, n, lens, seed=1300 + h + g + n + d, steps=steps, dtype=dtype, d=d)
     for step in range(steps):
         q, kn, vn = pb.draw_step()
         max_len = int(pb.lens_h.max())
-        out = torch.empty(b, n, h, 128, dtype=torch.bfloat16, device="cuda")
+        out = torch.empty(b, n, h, d, dtype=pb.tdt, device="cuda")
         api.decode_step_multi(out, to_dev(q), to_dev(kn), to_dev(vn), pb.kc, pb.vc, pb.lens, max_len, pb.scale, pb.ws)
         torch.cuda.synchronize()
         oracle_mod.kv_append_multi(pb.kc_h, pb.vc_h, kn, vn, pb.lens_h)
         want = oracle_mod.decode_attention_multi(q, pb.kc_h, pb.vc_h, pb.lens_h, pb.scale)
-        assert_parity(out, want, "bf16", f"multi step {step} {case}")
+        assert_parity(out, want, dtype, f"multi step {step} {case}")
         assert np.array_equal(pb.lens.cpu().numpy(), pb.lens_h)
-        assert np.array_equal(to_host_bits(pb.kc), pb.kc_h)
+        assert _same_bits(to_host_bits(pb.kc), pb.kc_h)
 
 
 def test_one_token_multi_equals_the_one_token_call(gpu_lib):
@@ -107,11 +133,9 @@ def test_multi_rejects(gpu_lib):
     pb = MultiProblem(2, 64, 8, 2, [10, 20], seed=1500)
     q = torch.zeros(2, 2, 64, 128, dtype=torch.bfloat16, device="cuda")
     out = torch.empty_like(q)
-    with pytest.raises(RuntimeError, match="n \\* h / g"):   # 9 tokens x 8 heads > 64
-        api.decode_attention_multi(torch.empty(2, 9, 64, 128, dtype=torch.bfloat16, device="cuda"),
-                                   torch.zeros(2, 9, 64, 128, dtype=torch.bfloat16, device="cuda"), pb.kc, pb.vc,
-                                   pb.lens, 20, pb.scale, api.make_multi_workspace(2, 9, 64, 8, 128, 128,
-                                                                                   torch.bfloat16, "cuda"))
+    with pytest.raises(RuntimeError, match="WORKSPACE"):   # a one-token workspace is too small for 2 tokens
+        api.decode_attention_multi(out, q, pb.kc, pb.vc, pb.lens, 22, pb.scale,
+                                   api.make_workspace(2, 64, 8, 128, 128, 22, torch.bfloat16, "cuda"))
     with pytest.raises(RuntimeError, match="CAPACITY"):
         api.decode_step_multi(out, q, torch.zeros(2, 2, 8, 128, dtype=torch.bfloat16, device="cuda"),
                               torch.zeros(2, 2, 8, 128, dtype=torch.bfloat16, device="cuda"), pb.kc, pb.vc, pb.lens,
