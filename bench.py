@@ -41,14 +41,15 @@ With --paged B the caches live in pools of B-position blocks behind shuffled
 block tables (gqa_decode_step_paged); bytes and timing as for the step.
 
 With --tokens N (N > 1) each step appends N new tokens per sequence and runs
-their causal attention (gqa_decode_step_multi: two launches); bytes are
-those the last token attends, read once for all N tokens.
+their causal attention (gqa_decode_step_multi: two launches; with --paged B
+too, gqa_decode_step_multi_paged); bytes are those the last token attends,
+read once for all N tokens.
 
 With --graph the timed steps are captured in one HIP graph and replayed, which
 removes the host's per-call cost (it matters for the small, launch-bound
 workloads).
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--paged B | --tokens N]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--paged B] [--tokens N]
                        [--graph] [--layer | --fold G]
 """
 from __future__ import annotations
@@ -129,7 +130,7 @@ def main():
     ap.add_argument("--graph", action="store_true",
                     help="capture the timed steps in one HIP graph and time its replay (no host launch cost)")
     ap.add_argument("--tokens", type=int, default=1, metavar="N",
-                    help="new tokens per sequence and step (N > 1: gqa_decode_step_multi, causal)")
+                    help="new tokens per sequence and step (N > 1: gqa_decode_step_multi[_paged], causal)")
     ap.add_argument("--paged", type=int, default=0, metavar="B",
                     help="keep the caches in pools of B-position blocks behind shuffled block tables")
     ap.add_argument("--fold", type=int, default=0, metavar="G",
@@ -191,8 +192,9 @@ def main():
     if args.graph and args.unfused:
         print("--graph times the fused step only", file=sys.stderr)
         sys.exit(2)
-    if ntok < 1 or (ntok > 1 and (args.paged or args.unfused or wl.dtype != "bf16")):
-        print("--tokens N: N >= 1; N > 1 runs bf16 contiguous caches only", file=sys.stderr)
+    if ntok < 1 or (ntok > 1 and args.unfused):
+        print("--tokens N: N >= 1; N > 1 times the multi-token step (append + attention), not --unfused",
+              file=sys.stderr)
         sys.exit(2)
     sets = []
     host0 = None
@@ -257,6 +259,9 @@ def main():
         if args.unfused:
             api.decode_attention(out, qs[i % len(qs)], st["kc"], st["vc"], st["lens"], max_len + 1, wl.scale, ws,
                                  path=args.path, workgroups=args.workgroups)
+        elif args.paged and ntok > 1:
+            api.decode_step_multi_paged(out, qs[i % len(qs)], kn, vn, st["kc"], st["vc"], st["lens"], st["table"],
+                                        max_len, wl.scale, ws)
         elif args.paged:
             api.decode_step_paged(out, qs[i % len(qs)], kn, vn, st["kc"], st["vc"], st["lens"], st["table"], max_len,
                                   wl.scale, ws)
@@ -318,9 +323,9 @@ def main():
 
     value = total_bytes / (elapsed_ms / 1e3) / 1e9
     achieved = bytes_per_launch / (kern_avg_ms / 1e3) / 1e9
-    # a multi-token call is planned as a one-token call with N * h heads on the matrix path
+    # a multi-token call is planned as a one-token call with N * h heads
     plan_path, plan_wgs, plan_merge = api.plan(wl.b, wl.h * ntok, wl.g, wl.d, wl.d, cap, max_len_bound, dt,
-                                               api.PATH_MATRIX if ntok > 1 else args.path, args.workgroups)
+                                               api.PATH_AUTO if ntok > 1 else args.path, args.workgroups)
     traffic = None if (args.paged or ntok > 1) else traffic_from_profile(wl.name)
 
     cpu = None
@@ -354,6 +359,8 @@ def main():
             "path": {1: "vector", 2: "matrix"}[plan_path], "workgroups": plan_wgs,
             "split_merge": "second launch" if plan_merge == api.MERGE_KERNEL else "in the decode kernel",
             "step_api": ("gqa_kv_append + gqa_decode_attention" if args.unfused else
+                         f"gqa_decode_step_multi_paged ({ntok} tokens, blocks of {args.paged})"
+                         if args.paged and ntok > 1 else
                          f"gqa_decode_step_paged (blocks of {args.paged})" if args.paged else
                          f"gqa_decode_step_multi ({ntok} tokens: append + causal attention)" if ntok > 1 else
                          "gqa_decode_step"),

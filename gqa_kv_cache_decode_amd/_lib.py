@@ -58,6 +58,9 @@ SIGNATURES = {
     "gqa_kv_append_multi": (_i32, [_vp] * 5 + [_i32] * 8 + [_vp]),
     "gqa_decode_attention_multi": (_i32, [_vp] * 5 + [_i32] * 8 + [_f32, _i32, _vp, _sz, _vp]),
     "gqa_decode_step_multi": (_i32, [_vp] * 7 + [_i32] * 8 + [_f32, _i32, _vp, _sz, _vp]),
+    "gqa_kv_append_multi_paged": (_i32, [_vp] * 6 + [_i32] * 10 + [_vp]),
+    "gqa_decode_attention_multi_paged": (_i32, [_vp] * 6 + [_i32] * 10 + [_f32, _i32, _vp, _sz, _vp]),
+    "gqa_decode_step_multi_paged": (_i32, [_vp] * 8 + [_i32] * 10 + [_f32, _i32, _vp, _sz, _vp]),
     "gqa_last_error": (ctypes.c_char_p, []),
 }
 

@@ -392,3 +392,64 @@ def decode_step_multi(out, q, k_new, v_new, k_cache, v_cache, lens, max_len: int
         workspace.numel() * workspace.element_size(), _stream_handle(stream))
     _lib.check(rc, "gqa_decode_step_multi")
     return out
+
+
+def kv_append_multi_paged(k_pool, v_pool, k_new, v_new, lens, block_table, max_len: int, stream=None) -> None:
+    """Store token r's rows (k_new / v_new [b, n, g, d]) at position lens[s] + r of each paged cache; lens += n."""
+    b, g, d_k, d_v, bs, mb, nb = _paged_args(k_pool, v_pool, block_table, lens)
+    _check_gpu(k_new, v_new)
+    n = k_new.shape[1] if k_new.dim() == 4 else 0
+    if tuple(k_new.shape) != (b, n, g, d_k) or tuple(v_new.shape) != (b, n, g, d_v):
+        raise ValueError("kv_append_multi_paged: k_new [b, n, g, d_k] and v_new [b, n, g, d_v] expected")
+    dt = _dtype_code(k_pool)
+    if any(_dtype_code(t) != dt for t in (v_pool, k_new, v_new)):
+        raise TypeError("pools and new rows must share one element type")
+    rc = _lib.load().gqa_kv_append_multi_paged(
+        k_pool.data_ptr(), v_pool.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), lens.data_ptr(),
+        block_table.data_ptr(), b, n, g, d_k, d_v, bs, mb, nb, int(max_len), dt, _stream_handle(stream))
+    _lib.check(rc, "gqa_kv_append_multi_paged")
+
+
+def _multi_paged_shapes(out, q, k_pool, v_pool, lens, block_table):
+    b, g, d_k, d_v, bs, mb, nb = _paged_args(k_pool, v_pool, block_table, lens)
+    _check_gpu(out, q)
+    if q.dim() != 4:
+        raise ValueError("q must be [b, n, h, d_k]")
+    n, h = q.shape[1], q.shape[2]
+    if tuple(q.shape) != (b, n, h, d_k) or tuple(out.shape) != (b, n, h, d_v):
+        raise ValueError("multi-token paged call: q [b, n, h, d_k] and out [b, n, h, d_v] expected")
+    return b, n, h, g, d_k, d_v, bs, mb, nb
+
+
+def decode_attention_multi_paged(out, q, k_pool, v_pool, lens, block_table, max_len: int, scale: float, workspace,
+                                 stream=None) -> torch.Tensor:
+    """n query tokens per sequence (q, out [b, n, h, d]) over paged caches that already hold them, causal."""
+    b, n, h, g, d_k, d_v, bs, mb, nb = _multi_paged_shapes(out, q, k_pool, v_pool, lens, block_table)
+    _check_gpu(workspace)
+    dt = _dtype_code(q)
+    if any(_dtype_code(t) != dt for t in (k_pool, v_pool, out)):
+        raise TypeError("q, pools and out must share one element type")
+    rc = _lib.load().gqa_decode_attention_multi_paged(
+        out.data_ptr(), q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), lens.data_ptr(), block_table.data_ptr(),
+        b, n, h, g, d_k, d_v, bs, mb, nb, int(max_len), float(scale), dt, workspace.data_ptr(),
+        workspace.numel() * workspace.element_size(), _stream_handle(stream))
+    _lib.check(rc, "gqa_decode_attention_multi_paged")
+    return out
+
+
+def decode_step_multi_paged(out, q, k_new, v_new, k_pool, v_pool, lens, block_table, max_len: int, scale: float,
+                            workspace, stream=None) -> torch.Tensor:
+    """Append n tokens per sequence to paged caches, then their causal attention (max_len: bound before)."""
+    b, n, h, g, d_k, d_v, bs, mb, nb = _multi_paged_shapes(out, q, k_pool, v_pool, lens, block_table)
+    _check_gpu(k_new, v_new, workspace)
+    if tuple(k_new.shape) != (b, n, g, d_k) or tuple(v_new.shape) != (b, n, g, d_v):
+        raise ValueError("decode_step_multi_paged: k_new [b, n, g, d_k] and v_new [b, n, g, d_v] expected")
+    dt = _dtype_code(q)
+    if any(_dtype_code(t) != dt for t in (k_pool, v_pool, out, k_new, v_new)):
+        raise TypeError("q, rows, pools and out must share one element type")
+    rc = _lib.load().gqa_decode_step_multi_paged(
+        out.data_ptr(), q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
+        lens.data_ptr(), block_table.data_ptr(), b, n, h, g, d_k, d_v, bs, mb, nb, int(max_len), float(scale), dt,
+        workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream_handle(stream))
+    _lib.check(rc, "gqa_decode_step_multi_paged")
+    return out

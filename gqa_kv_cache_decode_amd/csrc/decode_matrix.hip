@@ -378,7 +378,7 @@ void launch_nb(const DecodeParams& p, hipStream_t stream) {
 
 hipError_t launch_decode_matrix(const DecodeParams& p, hipStream_t stream) {
   const bool paged = p.pg.table != nullptr;
-  if (p.n_tok > 1) launch_nb<false, false, true>(p, stream);  // multi-token: contiguous caches, no fused append
+  if (p.n_tok > 1) paged ? launch_nb<false, true, true>(p, stream) : launch_nb<false, false, true>(p, stream);
   else if (p.fused) paged ? launch_nb<true, true, false>(p, stream) : launch_nb<true, false, false>(p, stream);
   else paged ? launch_nb<false, true, false>(p, stream) : launch_nb<false, false, false>(p, stream);
   return hipGetLastError();
@@ -398,11 +398,12 @@ hipError_t occupancy(int k, int* n) {
 
 int matrix_waves(int G) { return G <= 16 ? kMatrixWaves1 : 4; }
 
-// kind: 0 one-token, 1 fused step, 2 paged, 3 paged fused step, 4 multi-token.
+// kind: 0 one-token, 1 fused step, 2 paged, 3 paged fused step, 4 multi-token,
+// 5 paged multi-token (the multi-token append is its own launch: never fused).
 int matrix_workgroups_per_cu(int G, bool fused, bool paged, bool causal) {
-  static int cached[5][3] = {};
+  static int cached[6][3] = {};
   const int k = G <= 16 ? 0 : (G <= 32 ? 1 : 2);
-  const int kind = causal ? 4 : (paged ? 2 : 0) + (fused ? 1 : 0);
+  const int kind = causal ? (paged ? 5 : 4) : (paged ? 2 : 0) + (fused ? 1 : 0);
   int& c = cached[kind][k];
   if (c > 0) return c;
   int n = 0;
@@ -412,7 +413,8 @@ int matrix_workgroups_per_cu(int G, bool fused, bool paged, bool causal) {
     case 1: e = occupancy<true, false, false>(k, &n); break;
     case 2: e = occupancy<false, true, false>(k, &n); break;
     case 3: e = occupancy<true, true, false>(k, &n); break;
-    default: e = occupancy<false, false, true>(k, &n); break;
+    case 4: e = occupancy<false, false, true>(k, &n); break;
+    default: e = occupancy<false, true, true>(k, &n); break;
   }
   if (e != hipSuccess || n <= 0) {
     (void)hipGetLastError();

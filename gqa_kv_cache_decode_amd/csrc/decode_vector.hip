@@ -1,7 +1,8 @@
 // Vector-ALU decode attention: the contiguous-cache instances of the kernel
 // in decode_vector_kernel.hpp, and the launch and occupancy entry points of
 // every variant (the paged instances are in decode_vector_paged.hip, the
-// multi-token ones in decode_vector_multi.hip).
+// multi-token ones in decode_vector_multi.hip and, over paged caches,
+// decode_vector_multi_paged.hip).
 #include "decode_vector_kernel.hpp"
 
 namespace gqa {
@@ -12,15 +13,16 @@ int vector_waves(int dtype, int d, int heads_per_block) {
 }
 
 int vector_workgroups_per_cu(int dtype, int d, int heads_per_block, bool fused, bool paged, bool causal) {
-  // kind: 0 one-token, 1 fused step, 2 paged, 3 paged fused step, 4 multi-token
-  static int cached[5][2][5][4] = {};
+  // kind: 0 one-token, 1 fused step, 2 paged, 3 paged fused step, 4 multi-token, 5 paged multi-token
+  static int cached[6][2][5][4] = {};
   const int ti = dtype == 0 ? 0 : 1;
   const int di = d == 16 ? 0 : d == 32 ? 1 : d == 64 ? 2 : d == 128 ? 3 : 4;
   const int hi = heads_per_block == 1 ? 0 : heads_per_block == 2 ? 1 : heads_per_block == 4 ? 2 : 3;
-  const int kind = causal ? 4 : (paged ? 2 : 0) + (fused ? 1 : 0);
+  const int kind = causal ? (paged ? 5 : 4) : (paged ? 2 : 0) + (fused ? 1 : 0);
   int& c = cached[kind][ti][di][hi];
   if (c > 0) return c;
-  const int n = causal ? vector_occupancy_multi(dtype, d, heads_per_block)
+  const int n = causal ? (paged ? vector_occupancy_multi_paged(dtype, d, heads_per_block)
+                                 : vector_occupancy_multi(dtype, d, heads_per_block))
                        : paged ? vector_occupancy_paged(dtype, d, heads_per_block, fused)
                                : vector_occupancy<false>(dtype, d, heads_per_block, fused);
   if (n > 0) c = n;
@@ -28,7 +30,8 @@ int vector_workgroups_per_cu(int dtype, int d, int heads_per_block, bool fused, 
 }
 
 hipError_t launch_decode_vector(const DecodeParams& p, int dtype, hipStream_t stream) {
-  if (p.n_tok > 1) return launch_decode_vector_multi(p, dtype, stream);
+  if (p.n_tok > 1)
+    return p.pg.table ? launch_decode_vector_multi_paged(p, dtype, stream) : launch_decode_vector_multi(p, dtype, stream);
   if (p.pg.table) return launch_decode_vector_paged(p, dtype, stream);
   return launch_vector<false>(p, dtype, stream);
 }

@@ -487,7 +487,8 @@ int paged_check(const char* fn, const int32_t* table, int b, int block_size, int
 // out as a one-token call with n * h heads, then addressed through head_row.
 int multi_prepare(const char* fn, void* out, const void* q, const void* k_cache, const void* v_cache,
                   const int32_t* lens, int b, int n, int h, int g, int d_k, int d_v, int cap, int max_len, float scale,
-                  int dtype, void* workspace, size_t workspace_bytes, gqa::DecodeParams* p, Plan* plan) {
+                  int dtype, void* workspace, size_t workspace_bytes, gqa::DecodeParams* p, Plan* plan,
+                  const gqa::PagedLayout* pg = nullptr) {
   if (!out || !q || !k_cache || !v_cache || !lens) return fail(GQA_ERR_ARG, "%s: null pointer argument", fn);
   if (n <= 0 || n > kMaxTokens) return fail(GQA_ERR_ARG, "%s: n=%d must be in [1, %d]", fn, n, kMaxTokens);
   if (h <= 0 || g <= 0 || (long long)n * h > kMaxHeads)
@@ -497,13 +498,35 @@ int multi_prepare(const char* fn, void* out, const void* q, const void* k_cache,
   // applies (bf16, d = 128, n * h/g in [3, 64]), else the vector path
   const int rc = decode_prepare(fn, out, q, const_cast<void*>(k_cache), const_cast<void*>(v_cache),
                                 const_cast<int32_t*>(lens), nullptr, nullptr, b, n * h, g, d_k, d_v, cap, max_len,
-                                scale, dtype, workspace, workspace_bytes, GQA_PATH_AUTO, 0, 0, p, plan, nullptr,
+                                scale, dtype, workspace, workspace_bytes, GQA_PATH_AUTO, 0, 0, p, plan, pg,
                                 n > 1);
   if (rc != GQA_OK) return rc;
   p->h = h;
   p->G = h / g;
   p->n_tok = n;
   return GQA_OK;
+}
+
+// Checks and launch of a multi-token append; cap is the positions a
+// sequence can hold (max_blocks * block_size when pg is set).
+int append_multi(const char* fn, void* k_cache, void* v_cache, const void* k_new, const void* v_new, int32_t* lens,
+                 int b, int n, int g, int d_k, int d_v, int cap, int max_len, int dtype, void* stream,
+                 const gqa::PagedLayout& pg) {
+  if (!k_cache || !v_cache || !k_new || !v_new || !lens) return fail(GQA_ERR_ARG, "%s: null pointer argument", fn);
+  if (b <= 0 || b > kMaxBatch) return fail(GQA_ERR_ARG, "b=%d must be in [1, %d]", b, kMaxBatch);
+  if (n <= 0 || n > kMaxTokens) return fail(GQA_ERR_ARG, "n=%d must be in [1, %d]", n, kMaxTokens);
+  if (g <= 0 || d_k <= 0 || d_v <= 0 || cap <= 0)
+    return fail(GQA_ERR_ARG, "g=%d, d_k=%d, d_v=%d, cap=%d must be positive", g, d_k, d_v, cap);
+  if (max_len < 0) return fail(GQA_ERR_ARG, "max_len=%d must be >= 0", max_len);
+  if (dtype != GQA_DTYPE_F32 && dtype != GQA_DTYPE_BF16)
+    return fail(GQA_ERR_UNSUPPORTED, "dtype=%d is not GQA_DTYPE_F32 or GQA_DTYPE_BF16", dtype);
+  if ((long long)max_len + n > cap)
+    return fail(GQA_ERR_CAPACITY, "%s: appending %d tokens to max_len=%d needs room for %lld positions, have %d", fn,
+                n, max_len, (long long)max_len + n, cap);
+  gqa::AppendParams p{k_cache, v_cache, k_new, v_new, lens, g, d_k, d_v, cap, pg, n};
+  const hipError_t e = gqa::launch_append(p, b, dtype, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(GQA_ERR_HIP, "%s launch: %s", fn, hipGetErrorString(e));
+  return ok();
 }
 
 }  // namespace
@@ -582,22 +605,8 @@ size_t gqa_decode_multi_workspace_size(int b, int n, int h, int g, int d_k, int 
 
 int gqa_kv_append_multi(void* k_cache, void* v_cache, const void* k_new, const void* v_new, int32_t* lens, int b,
                         int n, int g, int d_k, int d_v, int cap, int max_len, int dtype, void* stream) {
-  if (!k_cache || !v_cache || !k_new || !v_new || !lens)
-    return fail(GQA_ERR_ARG, "gqa_kv_append_multi: null pointer argument");
-  if (b <= 0 || b > kMaxBatch) return fail(GQA_ERR_ARG, "b=%d must be in [1, %d]", b, kMaxBatch);
-  if (n <= 0 || n > kMaxTokens) return fail(GQA_ERR_ARG, "n=%d must be in [1, %d]", n, kMaxTokens);
-  if (g <= 0 || d_k <= 0 || d_v <= 0 || cap <= 0)
-    return fail(GQA_ERR_ARG, "g=%d, d_k=%d, d_v=%d, cap=%d must be positive", g, d_k, d_v, cap);
-  if (max_len < 0) return fail(GQA_ERR_ARG, "max_len=%d must be >= 0", max_len);
-  if (dtype != GQA_DTYPE_F32 && dtype != GQA_DTYPE_BF16)
-    return fail(GQA_ERR_UNSUPPORTED, "dtype=%d is not GQA_DTYPE_F32 or GQA_DTYPE_BF16", dtype);
-  if ((long long)max_len + n > cap)
-    return fail(GQA_ERR_CAPACITY, "appending %d tokens to max_len=%d needs cap >= %lld, cap=%d", n, max_len,
-                (long long)max_len + n, cap);
-  gqa::AppendParams p{k_cache, v_cache, k_new, v_new, lens, g, d_k, d_v, cap, gqa::PagedLayout{nullptr, 0, 0, 0}, n};
-  const hipError_t e = gqa::launch_append(p, b, dtype, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return fail(GQA_ERR_HIP, "gqa_kv_append_multi launch: %s", hipGetErrorString(e));
-  return ok();
+  return append_multi("gqa_kv_append_multi", k_cache, v_cache, k_new, v_new, lens, b, n, g, d_k, d_v, cap, max_len,
+                      dtype, stream, gqa::PagedLayout{nullptr, 0, 0, 0});
 }
 
 int gqa_decode_attention_multi(void* out, const void* q, const void* k_cache, const void* v_cache,
@@ -627,6 +636,56 @@ int gqa_decode_step_multi(void* out, const void* q, const void* k_new, const voi
                          workspace, workspace_bytes, &p, &plan);
   if (rc != GQA_OK) return rc;
   rc = gqa_kv_append_multi(k_cache, v_cache, k_new, v_new, lens, b, n, g, d_k, d_v, cap, max_len, dtype, stream);
+  if (rc != GQA_OK) return rc;
+  return decode_launch(fn, p, plan, dtype, stream);
+}
+
+int gqa_kv_append_multi_paged(void* k_pool, void* v_pool, const void* k_new, const void* v_new, int32_t* lens,
+                              const int32_t* block_table, int b, int n, int g, int d_k, int d_v, int block_size,
+                              int max_blocks, int num_blocks, int max_len, int dtype, void* stream) {
+  const char* fn = "gqa_kv_append_multi_paged";
+  gqa::PagedLayout pg;
+  int cap = 0;
+  const int rc = paged_check(fn, block_table, b, block_size, max_blocks, num_blocks, &pg, &cap);
+  if (rc != GQA_OK) return rc;
+  return append_multi(fn, k_pool, v_pool, k_new, v_new, lens, b, n, g, d_k, d_v, cap, max_len, dtype, stream, pg);
+}
+
+int gqa_decode_attention_multi_paged(void* out, const void* q, const void* k_pool, const void* v_pool,
+                                     const int32_t* lens, const int32_t* block_table, int b, int n, int h, int g,
+                                     int d_k, int d_v, int block_size, int max_blocks, int num_blocks, int max_len,
+                                     float scale, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "gqa_decode_attention_multi_paged";
+  gqa::PagedLayout pg;
+  int cap = 0;
+  int rc = paged_check(fn, block_table, b, block_size, max_blocks, num_blocks, &pg, &cap);
+  if (rc != GQA_OK) return rc;
+  gqa::DecodeParams p;
+  Plan plan;
+  rc = multi_prepare(fn, out, q, k_pool, v_pool, lens, b, n, h, g, d_k, d_v, cap, max_len, scale, dtype, workspace,
+                     workspace_bytes, &p, &plan, &pg);
+  if (rc != GQA_OK) return rc;
+  return decode_launch(fn, p, plan, dtype, stream);
+}
+
+int gqa_decode_step_multi_paged(void* out, const void* q, const void* k_new, const void* v_new, void* k_pool,
+                                void* v_pool, int32_t* lens, const int32_t* block_table, int b, int n, int h, int g,
+                                int d_k, int d_v, int block_size, int max_blocks, int num_blocks, int max_len,
+                                float scale, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "gqa_decode_step_multi_paged";
+  if (!k_new || !v_new) return fail(GQA_ERR_ARG, "%s: null pointer argument", fn);
+  if (max_len < 0 || max_len > INT32_MAX - kMaxTokens) return fail(GQA_ERR_ARG, "%s: max_len=%d out of range", fn, max_len);
+  gqa::PagedLayout pg;
+  int cap = 0;
+  int rc = paged_check(fn, block_table, b, block_size, max_blocks, num_blocks, &pg, &cap);
+  if (rc != GQA_OK) return rc;
+  // every check of both launches runs before the first is enqueued
+  gqa::DecodeParams p;
+  Plan plan;
+  rc = multi_prepare(fn, out, q, k_pool, v_pool, lens, b, n, h, g, d_k, d_v, cap, max_len + n, scale, dtype,
+                     workspace, workspace_bytes, &p, &plan, &pg);
+  if (rc != GQA_OK) return rc;
+  rc = append_multi(fn, k_pool, v_pool, k_new, v_new, lens, b, n, g, d_k, d_v, cap, max_len, dtype, stream, pg);
   if (rc != GQA_OK) return rc;
   return decode_launch(fn, p, plan, dtype, stream);
 }

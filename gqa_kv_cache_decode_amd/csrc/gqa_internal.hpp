@@ -191,6 +191,8 @@ hipError_t launch_decode_vector_paged(const DecodeParams& p, int dtype, hipStrea
 int vector_occupancy_paged(int dtype, int d, int heads_per_block, bool fused);
 hipError_t launch_decode_vector_multi(const DecodeParams& p, int dtype, hipStream_t stream);
 int vector_occupancy_multi(int dtype, int d, int heads_per_block);
+hipError_t launch_decode_vector_multi_paged(const DecodeParams& p, int dtype, hipStream_t stream);
+int vector_occupancy_multi_paged(int dtype, int d, int heads_per_block);
 // Waves per workgroup of the vector kernel instance for this dtype, d and head block.
 int vector_waves(int dtype, int d, int heads_per_block);
 

@@ -12,9 +12,10 @@
  * in that order on one stream, or both at once with gqa_decode_step (one
  * launch). Around that core the library also offers: the same three calls on
  * paged caches (*_paged), n new tokens per sequence with a causal mask
- * (*_multi), the layer's projections and the whole layer step
- * (gqa_pack_weight, gqa_linear, gqa_decode_layer), and the mean-fold of KV
- * heads that turns an MHA cache into a GQA one (gqa_fold_kv_heads).
+ * (*_multi, and *_multi_paged over paged caches), the layer's projections
+ * and the whole layer step (gqa_pack_weight, gqa_linear, gqa_decode_layer),
+ * and the mean-fold of KV heads that turns an MHA cache into a GQA one
+ * (gqa_fold_kv_heads).
  * The step is the per-layer decode loop of the
  * "LLM inference 05" notes (albangk): push K, push V, then attend; and the
  * incremental attention of the "Fast Transformer Decoding: One Write-Head is
@@ -323,6 +324,30 @@ int gqa_decode_step_paged(void* out, const void* q, const void* k_new, const voi
                           void* v_pool, int32_t* lens, const int32_t* block_table, int b, int h, int g, int d_k,
                           int d_v, int block_size, int max_blocks, int num_blocks, int max_len, float scale,
                           int dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Multi-token decode over paged caches: the *_multi calls above with the
+ * caches replaced by block pools and a block table, laid out as for the paged
+ * calls (pools [num_blocks][g][block_size][d], table int32 [b][max_blocks],
+ * ids clamped into the pool). A sequence holds max_blocks * block_size
+ * positions; an append of n tokens needs max_len + n of them (else
+ * GQA_ERR_CAPACITY, nothing enqueued) and may cross into a new block, whose
+ * table entry must then be valid. q, out, k_new, v_new, n, the causal limits,
+ * the workspace (gqa_decode_multi_workspace_size) and the error rules are
+ * those of the contiguous *_multi calls, and so are the results, bit for bit,
+ * on the cache the pool stands for.
+ */
+int gqa_kv_append_multi_paged(void* k_pool, void* v_pool, const void* k_new, const void* v_new, int32_t* lens,
+                              const int32_t* block_table, int b, int n, int g, int d_k, int d_v, int block_size,
+                              int max_blocks, int num_blocks, int max_len, int dtype, void* stream);
+int gqa_decode_attention_multi_paged(void* out, const void* q, const void* k_pool, const void* v_pool,
+                                     const int32_t* lens, const int32_t* block_table, int b, int n, int h, int g,
+                                     int d_k, int d_v, int block_size, int max_blocks, int num_blocks, int max_len,
+                                     float scale, int dtype, void* workspace, size_t workspace_bytes, void* stream);
+int gqa_decode_step_multi_paged(void* out, const void* q, const void* k_new, const void* v_new, void* k_pool,
+                                void* v_pool, int32_t* lens, const int32_t* block_table, int b, int n, int h, int g,
+                                int d_k, int d_v, int block_size, int max_blocks, int num_blocks, int max_len,
+                                float scale, int dtype, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Mean-fold of KV heads ("TF2 GQA" lesson, on moving a trained multi-head

@@ -361,3 +361,35 @@ def decode_attention_multi(q, k_cache, v_cache, lens, scale: float, threads: int
         prefix = (lens - (n - 1 - r)).astype(np.int32)
         out[:, r] = decode_attention(np.ascontiguousarray(q[:, r]), k_cache, v_cache, prefix, scale, threads=threads)
     return out
+
+
+def kv_append_multi_paged(k_pool, v_pool, k_new, v_new, lens, table) -> None:
+    """In place: token r of sequence s goes to position lens[s] + r of its paged cache; lens += n.
+
+    The multi-token append (n single appends in a row [MQA-review §2.3, §2.4])
+    on the block-table layout of kv_append_paged. All or nothing: if any
+    sequence lacks room for its n tokens or a table entry they need is not a
+    pool block, nothing changes (OracleError).
+    """
+    b, n, g, d_k = k_new.shape
+    num_blocks, _, bs, _ = k_pool.shape
+    max_blocks = table.shape[1]
+    for s in range(b):
+        L = int(lens[s])
+        if L < 0 or L + n > max_blocks * bs:
+            raise OracleError(ERR_CAPACITY, "kv_append_multi_paged")
+        for t in range(L, L + n):
+            if not 0 <= int(table[s, t // bs]) < num_blocks:
+                raise OracleError(ERR_ARG, "kv_append_multi_paged: table entry")
+    for r in range(n):
+        kv_append_paged(k_pool, v_pool, np.ascontiguousarray(k_new[:, r]), np.ascontiguousarray(v_new[:, r]), lens,
+                        table)
+
+
+def decode_attention_multi_paged(q, k_pool, v_pool, lens, table, scale: float, threads: int = 0) -> np.ndarray:
+    """Multi-token causal attention over paged caches: decode_attention_multi over the caches they stand for."""
+    bs = k_pool.shape[2]
+    cap = table.shape[1] * bs
+    k = gather_paged(k_pool, table, lens, bs, cap)
+    v = gather_paged(v_pool, table, lens, bs, cap)
+    return decode_attention_multi(q, k, v, np.ascontiguousarray(lens, dtype=np.int32), scale, threads=threads)

@@ -321,3 +321,43 @@ def test_multi_rejects_on_the_host(lib):
     assert lib.gqa_decode_multi_workspace_size(4, 2, 64, 8, 128, 128, _lib.BF16) == \
         lib.gqa_decode_workspace_size(4, 128, 8, 128, 128, 0, _lib.BF16)
     assert lib.gqa_decode_multi_workspace_size(4, 0, 64, 8, 128, 128, _lib.BF16) == 0
+
+
+def test_multi_paged_rejects_on_the_host(lib):
+    FAKE2 = ctypes.c_void_p(1 << 40)
+    base = dict(table=FAKE2, b=4, n=2, h=64, g=8, d=128, bs=64, mb=4, nb=16, max_len=100, dtype=_lib.BF16,
+                ws_bytes=1 << 30)
+
+    def attend(**kw):
+        a = dict(base, **kw)
+        return lib.gqa_decode_attention_multi_paged(FAKE, FAKE, FAKE, FAKE, FAKE, a["table"], a["b"], a["n"], a["h"],
+                                                    a["g"], a["d"], a["d"], a["bs"], a["mb"], a["nb"], a["max_len"],
+                                                    ctypes.c_float(0.1), a["dtype"], FAKE, a["ws_bytes"], None)
+
+    def step(**kw):
+        a = dict(base, **kw)
+        return lib.gqa_decode_step_multi_paged(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, a["table"], a["b"], a["n"],
+                                               a["h"], a["g"], a["d"], a["d"], a["bs"], a["mb"], a["nb"], a["max_len"],
+                                               ctypes.c_float(0.1), a["dtype"], FAKE, a["ws_bytes"], None)
+
+    def append(**kw):
+        a = dict(base, **kw)
+        return lib.gqa_kv_append_multi_paged(FAKE, FAKE, FAKE, FAKE, FAKE, a["table"], a["b"], a["n"], a["g"], a["d"],
+                                             a["d"], a["bs"], a["mb"], a["nb"], a["max_len"], a["dtype"], None)
+
+    for call in (attend, step, append):
+        assert call(table=None) == _lib.ERR_ARG
+        assert call(bs=16) == _lib.ERR_UNSUPPORTED      # below one 32-position tile
+        assert call(bs=96) == _lib.ERR_UNSUPPORTED      # not a power of two
+        assert call(mb=0) == _lib.ERR_ARG
+        assert call(n=0) == _lib.ERR_ARG
+        assert call(n=65) == _lib.ERR_ARG
+        assert call(dtype=7) == _lib.ERR_UNSUPPORTED
+    for call in (attend, step):
+        assert call(n=64, h=128) == _lib.ERR_ARG         # 64 x 128 query rows > 4096
+        assert call(h=60) == _lib.ERR_GROUPS
+        assert call(d=48) == _lib.ERR_UNSUPPORTED
+        assert call(ws_bytes=64) == _lib.ERR_WORKSPACE
+    assert attend(max_len=257) == _lib.ERR_CAPACITY      # 4 blocks of 64 positions
+    assert step(max_len=255) == _lib.ERR_CAPACITY        # 255 + 2 > 256
+    assert append(max_len=255) == _lib.ERR_CAPACITY
