@@ -218,7 +218,7 @@ __global__ __launch_bounds__(WAVES * 64, (NB == 1 && WAVES == 4) ? 2 : 1) void d
 
   zero_empty_sequences<uint16_t, CAUSAL>(p, wg);
 
-  PieceWalker<WAVES == 8> walker;
+  PieceWalker<true> walker;
   walker.init(p, wg);
   Piece pc;
   DeferredPiece dfr;

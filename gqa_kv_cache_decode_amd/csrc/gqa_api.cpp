@@ -35,7 +35,12 @@ constexpr int kMaxTokens = 64;  // new tokens per sequence of a multi-token call
 constexpr int kMaxLen = 1 << 28;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kDefaultCUs = 256;  // MI355X, used when no device can be queried
-constexpr int kSegmentLead = 2;   // empty schedule units ahead of each segment
+// Empty schedule units ahead of each segment (lead units; see plan_decode).
+constexpr int kSegmentLead8 = 2;       // eight-wave matrix kernel (up to 16 heads per KV head)
+constexpr int kSegmentLead32 = 3;      // four-wave kernel, 17-32 heads
+constexpr int kSegmentLead64 = 5;      // four-wave kernel, 33-64 heads
+constexpr int kMaxSegmentLead = 5;
+constexpr int kLeadMinUnits = 8;       // four-wave kernels: lead units only from this many units per workgroup
 
 bool supported_head_dim(int d) { return d == 16 || d == 32 || d == 64 || d == 128 || d == 256; }
 
@@ -59,6 +64,7 @@ struct Plan {
   int nhb;
   int workgroups;
   bool merge_kernel;  // shared segments merged by a second launch
+  int seg_lead;       // empty schedule units ahead of each segment
 };
 
 // Largest head block any path may use for G heads per KV head (workspace sizing).
@@ -118,8 +124,9 @@ int plan_decode(int b, int h, int g, int d_k, int d_v, int cap, int max_len, int
   const int waves = chosen == GQA_PATH_MATRIX ? gqa::matrix_waves(G) : gqa::vector_waves(dtype, d_k, plan->gblk);
   const int unit_len = gqa::kTile * gqa::kUnitTiles;
   const long long segments = (long long)b * g * plan->nhb;
-  // lengths <= max_len; kSegmentLead: empty units ahead of each segment (at most)
-  const long long units_bound = segments * ((max_len + unit_len - 1) / unit_len + kSegmentLead);
+  // lengths <= max_len; kMaxSegmentLead: empty units ahead of each segment (at most)
+  const long long units_plain = segments * ((max_len + unit_len - 1) / unit_len);
+  const long long units_bound = units_plain + segments * kMaxSegmentLead;
   const bool auto_grid = workgroups == 0;
   if (auto_grid) {
     // Up to eight waves per compute unit (two 4-wave workgroups or one
@@ -158,6 +165,21 @@ int plan_decode(int b, int h, int g, int d_k, int d_v, int cap, int max_len, int
     if (workgroups > by_work) workgroups = int(by_work > 0 ? by_work : 1);
   }
   plan->workgroups = workgroups;
+  // Lead units: empty units ahead of each segment in the schedule, so that a
+  // range starting just before a segment skips them instead of opening a
+  // piece of a unit or two there (each piece costs a query load, a merge of
+  // the waves and a publish). On the matrix path, where ranges are long
+  // against that cost, they pay off; measured best: 2 for the eight-wave
+  // kernel, 3 and 5 for the four-wave 32- and 64-head ones, whose pieces
+  // cost more to merge and publish (4 and 8 new tokens per sequence on the
+  // Llama-3-70B shape: -7 % and -14 %). Where a workgroup's range is a few
+  // units (MQA, one long sequence per KV head) they only add imbalance, and
+  // the vector path was measured neutral or slower.
+  plan->seg_lead = 0;
+  if (chosen == GQA_PATH_MATRIX) {
+    if (waves == 8) plan->seg_lead = kSegmentLead8;
+    else if (units_plain >= (long long)kLeadMinUnits * workgroups) plan->seg_lead = G <= 32 ? kSegmentLead32 : kSegmentLead64;
+  }
   return GQA_OK;
 }
 
@@ -255,10 +277,7 @@ int decode_prepare(const char* fn, void* out, const void* q, void* k_cache, void
   p.ngroups = g * plan.nhb;
   p.slot_floats = gqa::slot_floats_for(plan.gblk, d_v);
   p.workgroups = plan.workgroups;
-  // The lead units pay off where ranges are long and pieces few per
-  // workgroup (the one-head-block matrix kernel); elsewhere they were
-  // measured neutral or slower.
-  p.seg_lead = (plan.path == GQA_PATH_MATRIX && gqa::matrix_waves(p.G) == 8) ? kSegmentLead : 0;
+  p.seg_lead = plan.seg_lead;
   p.scale_log2 = scale * kLog2e;
   p.pg = paged ? *paged : gqa::PagedLayout{nullptr, 0, 0, 0};
   p.n_tok = 1;
