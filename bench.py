@@ -49,8 +49,12 @@ With --graph the timed steps are captured in one HIP graph and replayed, which
 removes the host's per-call cost (it matters for the small, launch-bound
 workloads).
 
+With --flushed R, R more steps are timed one at a time after the timed region,
+each after a 1 GiB fill that evicts every cache level: the line gains their
+p10 / p50 / p90 latency ("flushed"). --cpu-threads T sets the oracle's threads.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--paged B] [--tokens N]
-                       [--graph] [--layer | --fold G]
+                       [--graph] [--layer | --fold G] [--flushed R] [--cpu-threads T]
 """
 from __future__ import annotations
 
@@ -86,11 +90,11 @@ def traffic_from_profile(workload: str):
     return int(float(rec["hbm_bytes_per_launch"]))
 
 
-def cpu_baseline(wl, batch_host, budget_s: float):
-    """Time the fp64 oracle (as it stands) on one full step of one cache set."""
+def cpu_baseline(wl, batch_host, budget_s: float, threads: int = 0):
+    """Time the fp64 oracle (as it stands) on one full step of one cache set (threads 0: up to 16 cores)."""
     import oracle
 
-    threads = max(1, min(16, len(os.sched_getaffinity(0))))
+    threads = threads or max(1, min(16, len(os.sched_getaffinity(0))))
     kc = batch_host.k_cache.copy()
     vc = batch_host.v_cache.copy()
     lens = batch_host.lens.copy()
@@ -121,6 +125,10 @@ def main():
     ap.add_argument("--path", type=int, default=0, help="0 auto, 1 vector, 2 matrix")
     ap.add_argument("--workgroups", type=int, default=0, help="persistent grid size (0: automatic)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle time budget (0: skip)")
+    ap.add_argument("--cpu-threads", type=int, default=0, help="oracle threads (0: the cores, at most 16)")
+    ap.add_argument("--flushed", type=int, default=0, metavar="R",
+                    help="after the timed steps, time R more steps one at a time, each after a 1 GiB fill "
+                         "(outside the events) that evicts the caches; adds p10/p50/p90 to the line")
     ap.add_argument("--unfused", action="store_true",
                     help="run the step as gqa_kv_append + gqa_decode_attention instead of gqa_decode_step")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -152,7 +160,7 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
-    total_steps = args.warmup + args.steps
+    total_steps = args.warmup + args.steps + args.flushed
     if args.layer:
         if wl.dtype != "bf16" or args.unfused:
             print("--layer runs bf16 workloads with the fused step only", file=sys.stderr)
@@ -323,6 +331,24 @@ def main():
 
     value = total_bytes / (elapsed_ms / 1e3) / 1e9
     achieved = bytes_per_launch / (kern_avg_ms / 1e3) / 1e9
+    flushed = None
+    if args.flushed > 0 and not args.graph:
+        # one step at a time, each after a 1 GiB fill outside its events (every
+        # cache level evicted): the latency of a cold step, not a throughput
+        fill = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        lat = []
+        for k in range(args.flushed):
+            fill.fill_(k & 255)
+            ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            step(args.warmup + args.steps + k, ev)
+            ev[1].synchronize()
+            lat.append(ev[0].elapsed_time(ev[1]) * 1e3)
+        del fill
+        flushed = {"reps": args.flushed, "p10_us": round(float(np.percentile(lat, 10)), 2),
+                   "p50_us": round(float(np.median(lat)), 2), "p90_us": round(float(np.percentile(lat, 90)), 2),
+                   "what": "per-step events around the " + ("decode launch" if args.unfused else "step's launches")
+                           + ", each step after a 1 GiB fill"}
+        log(f"flushed steps: p10 / p50 / p90 {flushed['p10_us']} / {flushed['p50_us']} / {flushed['p90_us']} us")
     # a multi-token call is planned as a one-token call with N * h heads
     plan_path, plan_wgs, plan_merge = api.plan(wl.b, wl.h * ntok, wl.g, wl.d, wl.d, cap, max_len_bound, dt,
                                                api.PATH_AUTO if ntok > 1 else args.path, args.workgroups)
@@ -331,7 +357,7 @@ def main():
     cpu = None
     if args.cpu_seconds > 0 and ntok == 1:
         log("timing the CPU oracle ...")
-        cpu = cpu_baseline(wl, host0, args.cpu_seconds)
+        cpu = cpu_baseline(wl, host0, args.cpu_seconds, args.cpu_threads)
 
     lens0 = host0.lens
     rec = {
@@ -379,6 +405,8 @@ def main():
         },
         "cpu_baseline": cpu,
     }
+    if flushed is not None:
+        rec["flushed"] = flushed
     print(json.dumps(rec), flush=True)
 
 
