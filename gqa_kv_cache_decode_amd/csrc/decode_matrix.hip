@@ -39,6 +39,8 @@
 // FUSED (the decode step): the tile holding the appended token takes that
 // row from k_new / v_new instead of the cache and writes it to its cache
 // slot; the last workgroup to finish stores the grown lengths.
+#include <atomic>
+
 #include "gqa_internal.hpp"
 
 namespace gqa {
@@ -400,12 +402,15 @@ int matrix_waves(int G) { return G <= 16 ? kMatrixWaves1 : 4; }
 
 // kind: 0 one-token, 1 fused step, 2 paged, 3 paged fused step, 4 multi-token,
 // 5 paged multi-token (the multi-token append is its own launch: never fused).
+// The answer depends only on the kernel and the architecture, so it is kept
+// once per process (relaxed atomics: concurrent first calls store the same value).
 int matrix_workgroups_per_cu(int G, bool fused, bool paged, bool causal) {
-  static int cached[6][3] = {};
+  static std::atomic<int> cached[6][3] = {};
   const int k = G <= 16 ? 0 : (G <= 32 ? 1 : 2);
   const int kind = causal ? (paged ? 5 : 4) : (paged ? 2 : 0) + (fused ? 1 : 0);
-  int& c = cached[kind][k];
-  if (c > 0) return c;
+  std::atomic<int>& c = cached[kind][k];
+  const int known = c.load(std::memory_order_relaxed);
+  if (known > 0) return known;
   int n = 0;
   hipError_t e;
   switch (kind) {
@@ -420,7 +425,7 @@ int matrix_workgroups_per_cu(int G, bool fused, bool paged, bool causal) {
     (void)hipGetLastError();
     return 0;
   }
-  c = n;
+  c.store(n, std::memory_order_relaxed);
   return n;
 }
 

@@ -5,6 +5,7 @@
 #include <stdint.h>
 #include <stdio.h>
 
+#include <atomic>
 #include <string>
 
 #include "gqa_decode.h"
@@ -44,17 +45,19 @@ constexpr int kLeadMinUnits = 8;       // four-wave kernels: lead units only fro
 
 bool supported_head_dim(int d) { return d == 16 || d == 32 || d == 64 || d == 128 || d == 256; }
 
-// Compute units of the current device (cached per device; kDefaultCUs if the
-// runtime cannot say).
+// Compute units of the current device (cached per device, relaxed atomics:
+// concurrent first calls store the same value; kDefaultCUs if the runtime
+// cannot say).
 int device_cus() {
-  static int cached[64] = {0};
+  static std::atomic<int> cached[64] = {};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return kDefaultCUs;
-  if (cached[dev] > 0) return cached[dev];
+  const int known = cached[dev].load(std::memory_order_relaxed);
+  if (known > 0) return known;
   int n = 0;
   if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
     n = kDefaultCUs;
-  cached[dev] = n;
+  cached[dev].store(n, std::memory_order_relaxed);
   return n;
 }
 
