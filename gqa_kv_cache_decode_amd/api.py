@@ -36,6 +36,10 @@ def _check_gpu(*tensors: torch.Tensor) -> None:
             raise ValueError("all tensors must live on the same GPU")
         if not t.is_contiguous():
             raise ValueError("all tensors must be contiguous")
+    # the library launches on the current device (and its current stream)
+    if dev.index is not None and dev.index != torch.cuda.current_device():
+        raise ValueError(f"tensors live on {dev}, the current device is cuda:{torch.cuda.current_device()} "
+                         "(use torch.cuda.device or torch.cuda.set_device)")
 
 
 def kv_append(k_cache: torch.Tensor, v_cache: torch.Tensor, k_new: torch.Tensor,
