@@ -38,6 +38,8 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kDefaultCUs = 256;  // MI355X, used when no device can be queried
 // Empty schedule units ahead of each segment (lead units; see plan_decode).
 constexpr int kSegmentLead8 = 2;       // eight-wave matrix kernel (up to 16 heads per KV head)
+constexpr int kSegmentLead8Short = 3;  // ... when no segment is longer than kShortSegmentUnits
+constexpr int kShortSegmentUnits = 24;
 constexpr int kSegmentLead32 = 3;      // four-wave kernel, 17-32 heads
 constexpr int kSegmentLead64 = 5;      // four-wave kernel, 33-64 heads
 constexpr int kMaxSegmentLead = 5;
@@ -173,15 +175,21 @@ int plan_decode(int b, int h, int g, int d_k, int d_v, int cap, int max_len, int
   // piece of a unit or two there (each piece costs a query load, a merge of
   // the waves and a publish). On the matrix path, where ranges are long
   // against that cost, they pay off; measured best: 2 for the eight-wave
-  // kernel, 3 and 5 for the four-wave 32- and 64-head ones, whose pieces
-  // cost more to merge and publish (4 and 8 new tokens per sequence on the
+  // kernel (3 where segments are short, at most 24 units: the Qwen2.5-7B
+  // shape at 2049 positions, -1.4 %; the Llama-3-70B shape, up to 64 units,
+  // is 1.2 % slower with 3), 3 and 5 for the four-wave 32- and 64-head ones,
+  // whose pieces cost more to merge and publish (4 and 8 new tokens per sequence on the
   // Llama-3-70B shape: -7 % and -14 %). Where a workgroup's range is a few
   // units (MQA, one long sequence per KV head) they only add imbalance, and
   // the vector path was measured neutral or slower.
   plan->seg_lead = 0;
   if (chosen == GQA_PATH_MATRIX) {
-    if (waves == 8) plan->seg_lead = kSegmentLead8;
-    else if (units_plain >= (long long)kLeadMinUnits * workgroups) plan->seg_lead = G <= 32 ? kSegmentLead32 : kSegmentLead64;
+    if (waves == 8) {
+      const long long seg_units = (max_len + unit_len - 1) / unit_len;  // the longest segment
+      plan->seg_lead = seg_units <= kShortSegmentUnits ? kSegmentLead8Short : kSegmentLead8;
+    } else if (units_plain >= (long long)kLeadMinUnits * workgroups) {
+      plan->seg_lead = G <= 32 ? kSegmentLead32 : kSegmentLead64;
+    }
   }
   return GQA_OK;
 }
