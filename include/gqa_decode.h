@@ -31,8 +31,10 @@
  * ---------------------------------------
  * - Every tensor pointer is a DEVICE pointer on the current HIP device, owned
  *   by the caller. The library never allocates, frees or keeps device memory
- *   and keeps no state between calls apart from a per-device attribute cache
- *   and the calling thread's last error message.
+ *   and keeps no state between calls apart from host-side caches of device
+ *   attributes and kernel occupancy (safe to fill from several threads) and
+ *   the calling thread's last error message. The workspace of the attention
+ *   calls is the caller's too; a call leaves its counters at zero.
  * - All tensors are dense and row-major (C-contiguous) with the shapes given
  *   below; element type is one of GQA_DTYPE_*; q, caches, new rows and out
  *   share it.
