@@ -469,12 +469,15 @@ struct PieceWalker {
     parts = loc.parts;
     s = loc.s;
     seq_base = loc.seq_base;
-    if (wg >= parts) {
-      u = u_end = 0;
-      return;
-    }
-    u = range_begin(wg, total, parts);
-    u_end = range_begin(wg + 1, total, parts);
+    // A workgroup past the last taking part gets the empty range [0, 0).
+    // Written as selects, not an early return: with two paths that each store
+    // u and u_end, the compiler merges the stores through a pointer that picks
+    // the field, which keeps both fields in scratch memory for the kernel's
+    // whole life (a reload and a wait at every piece).
+    const bool takes_part = wg < parts;
+    const int parts_nz = parts > 0 ? parts : 1;
+    u = takes_part ? range_begin(wg, total, parts_nz) : 0;
+    u_end = takes_part ? range_begin(wg + 1, total, parts_nz) : 0;
   }
 
   __device__ bool more() const { return u < u_end; }
