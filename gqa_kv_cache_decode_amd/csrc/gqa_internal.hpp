@@ -705,6 +705,13 @@ __device__ void merge_segment(const DecodeParams& p, int s, int p0, int n_slots,
         acc[c] = a;
       }
     }
+    // Every load of the batch has been used by now. The loads are issued and
+    // used under the same condition, which the compiler's wait placement does
+    // not pair up: without this compiler-visible wait it carries them as
+    // outstanding past the merge and waits for all memory operations at the
+    // top of the piece loop, i.e. for the stores of the previous piece, at
+    // the start of every piece. (vmcnt(0); the other counters unconstrained.)
+    __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
   }
   TOut* out = static_cast<TOut*>(p.out);
