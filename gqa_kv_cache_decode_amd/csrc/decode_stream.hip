@@ -1,0 +1,702 @@
+// Matrix-core decode attention for up to 16 query heads per KV head (one
+// 16-column MFMA block), bf16 K/V/q, d_k = d_v = 128, one query token per
+// sequence, at most 64 sequences: the Llama-3-70B- and Qwen2.5-7B-shaped GQA
+// steps. Same result as the other decode kernels (MQA review §2.1 per query
+// head over the cache of §2.4 / §3; contiguous head groups of the TF2 GQA
+// lesson); the per-tile arithmetic is the one of decode_matrix.hip (scores
+// K·Q^T and output P·V on v_mfma_f32_16x16x32_bf16, base-2 softmax).
+//
+// What differs is how a workgroup walks its work, shaped by the measured
+// timeline of the earlier schedule (per-workgroup clock stamps on the
+// Llama-3-70B shape): the bulk of the stream ran at the memory system's
+// rate, and the time was lost at the start (lengths, then query rows, then
+// the first tile) and at the end, where the waves of one workgroup finished
+// their statically dealt tiles up to ~13 µs apart (the compute unit serves
+// its waves unevenly) and a barrier-bound merge and publish followed.
+//
+// * The static split of the (sequence, KV head) segments over the persistent
+//   workgroups is balanced to one 32-position tile (16 KiB), not four.
+// * Inside a workgroup, seven streaming waves take the range's tiles one at a
+//   time from an LDS counter, so a wave that is served faster takes more
+//   tiles and all finish together. Each tile's split-softmax state (max m,
+//   sum of weights l, unnormalised output o) is computed from scratch, so it
+//   does not depend on which wave computed it.
+// * The eighth wave folds the tile states in tile order out of an LDS ring
+//   (m = max, o and l rescaled by 2^(m_k - m)), which fixes the arithmetic:
+//   results are bit for bit the same whichever wave took which tile. It also
+//   writes, publishes or merges each finished piece, so the streaming waves
+//   never stop for that.
+// * A tile's K/V loads are issued before the query rows it needs.
+// * Fused step: the grown lengths can be written as soon as every workgroup
+//   has read the old ones, which all do at their start. The folding wave of
+//   each workgroup counts it out right after that read on one of 16
+//   counters, and the last of each group on one more, so no more than 16
+//   atomics meet on one address and none waits at the end of the launch.
+//
+// Split segments (a segment whose tiles fall in the ranges of several
+// workgroups, its "parts") are merged by the part that finishes last, with
+// its own state still in registers. A part counts itself in on the
+// segment's ticket (agent-scope atomic) as soon as it has folded its last
+// tile; a part that does not get the last ticket stores its state in its
+// partial slot (SC1 stores, which bypass the non-coherent caches), waits for
+// them, and raises the slot's ready flag. The last part waits for the other
+// parts' flags (each of those has already counted in, so it is running and
+// only has its stores left; the wait is bounded all the same), reads their
+// states (SC1 loads), merges them in part order and writes the output rows,
+// then re-zeroes the ticket and the flags. A few tiles before its end a
+// part looks at the ticket: if every other part has counted in by then it
+// is the last without counting. Heavily split segments are instead left to
+// a second launch (merge_partials_kernel).
+#include <atomic>
+
+#include "gqa_internal.hpp"
+
+namespace gqa {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kD = 128;
+constexpr int kWaves = 8;
+constexpr int kBlockThreads = kWaves * 64;
+constexpr int kHeads = 16;          // one MFMA column block
+constexpr int kRow = kD + 4;        // LDS row stride (floats), padded against bank conflicts
+constexpr int kRing = 16;           // tile states in the LDS ring
+constexpr int kFolder = kWaves - 1; // the folding wave; waves 0 .. kWaves - 2 stream
+constexpr int kPeekTiles = 3;       // tiles before a piece's end at which its ticket is looked at
+constexpr int kFlagSpins = 1 << 22; // bound of the wait for another part's ready flag
+// Parts of a segment whose states the merge holds in registers at once, by
+// columns per lane.
+template <int NCH>
+constexpr int fast_slots() { return NCH == 8 ? 2 : (NCH == 4 ? 5 : 9); }
+constexpr int kCountGroups = 16;    // first-level counters of the fused step's length update
+constexpr int kCountStride = 32;    // ints between counters (128 bytes)
+
+__device__ __forceinline__ u32x4 ld16(const uint16_t* ptr) { return *reinterpret_cast<const u32x4*>(ptr); }
+__device__ __forceinline__ u32x4 nt16(const uint16_t* ptr) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(ptr));
+}
+__device__ __forceinline__ void st16(uint16_t* ptr, u32x4 v) { *reinterpret_cast<u32x4*>(ptr) = v; }
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// V rows this lane loads for k-slot r of the value MFMA (see decode_matrix.hip).
+__device__ __forceinline__ int v_row(int q4, int r) { return (r < 4) ? (4 * q4 + r) : (16 + 4 * q4 + (r - 4)); }
+
+template <int E>
+__device__ __forceinline__ bf16x8 v_transpose(const u32x4* vr) {
+  u32x4 a;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t x = vr[2 * k][E / 2];
+    const uint32_t y = vr[2 * k + 1][E / 2];
+    if constexpr ((E & 1) == 0) a[k] = (x & 0xffffu) | (y << 16);
+    else a[k] = (x >> 16) | (y & 0xffff0000u);
+  }
+  return as_bf16x8(a);
+}
+
+// One 32-position tile in registers: K rows as the score MFMA's A operand
+// (k[sg * 4 + ks]: row 16 sg + n16, dims 32 ks + 8 q4 .. +7), V rows
+// tau(q4, r) (dims 8 n16 .. +7).
+struct Tile {
+  u32x4 k[8];
+  u32x4 v[8];
+};
+
+// Issue the loads of a tile whose rows start at kb / vb (FULL: all 32 rows
+// valid, else rows < nvalid; the others read as zero).
+template <bool FULL>
+__device__ __forceinline__ void load_tile(Tile& t, const uint16_t* kb, const uint16_t* vb, int nvalid, int n16,
+                                          int q4) {
+#pragma unroll
+  for (int sg = 0; sg < 2; ++sg) {
+    const int row = 16 * sg + n16;
+    const uint16_t* kp = kb + size_t(row) * kD + q4 * 8;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      t.k[sg * 4 + ks] = (FULL || row < nvalid) ? nt16(kp + ks * 32) : u32x4{0u, 0u, 0u, 0u};
+  }
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+    const int row = v_row(q4, r);
+    t.v[r] = (FULL || row < nvalid) ? nt16(vb + size_t(row) * kD + n16 * 8) : u32x4{0u, 0u, 0u, 0u};
+  }
+}
+
+// The split-softmax state of one tile, from scratch: per head m = the
+// tile's largest scaled logit (base 2), l = sum of its weights 2^(s - m)
+// (rounded to bf16, as applied), o = their weighted sum of V rows. Lane
+// (n16, q4) holds head n16: o[e][i] = dim 32 q4 + 8 i + e; m and l are the
+// same in the head's four lanes. Rows >= nvalid are masked unless FULL.
+template <bool FULL>
+__device__ __forceinline__ void tile_state(f32x4 (&o)[8], float& m, float& l, const bf16x8 (&qop)[4],
+                                           const Tile& t, int nvalid, float sl2, int q4) {
+  float sv[8];
+#pragma unroll
+  for (int sg = 0; sg < 2; ++sg) {
+    f32x4 sacc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(t.k[sg * 4 + ks]), qop[ks], sacc, 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 16 * sg + 4 * q4 + i;
+      sv[sg * 4 + i] = (FULL || row < nvalid) ? sacc[i] * sl2 : kNegInf;
+    }
+  }
+  float mx = sv[0];
+#pragma unroll
+  for (int k = 1; k < 8; ++k) mx = fmaxf(mx, sv[k]);
+  mx = fmaxf(mx, xor_shuffle(mx, 16));
+  mx = fmaxf(mx, xor_shuffle(mx, 32));
+  const float sub = (mx == kNegInf) ? 0.0f : mx;
+  float psum = 0.0f;
+  bf16x8 pk;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const __bf16 pb = static_cast<__bf16>(fast_exp2(sv[k] - sub));
+    pk[k] = pb;
+    psum += static_cast<float>(pb);  // the denominator sums the weights actually applied
+  }
+  psum += xor_shuffle(psum, 16);
+  psum += xor_shuffle(psum, 32);
+  m = mx;
+  l = psum;
+#define GQA_PV(E)                                                                                       \
+  o[E] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v_transpose<E>(t.v), pk, f32x4{0.0f, 0.0f, 0.0f, 0.0f}, \
+                                                 0, 0, 0);
+  GQA_PV(0) GQA_PV(1) GQA_PV(2) GQA_PV(3) GQA_PV(4) GQA_PV(5) GQA_PV(6) GQA_PV(7)
+#undef GQA_PV
+}
+
+// The schedule in tiles. Segments (s, j) are ordered by s, then j; segment
+// (s, j) is preceded by `lead` empty tiles (the cost of opening a piece, so
+// that a range starting just before a segment skips them). With T tiles in
+// all (empty ones included) and P' = min(P, T) workgroups taking part,
+// workgroup p takes [floor(p T / P'), floor((p + 1) T / P')).
+struct Range {
+  long long total, u, u_end, seq_base;
+  int s, parts;
+};
+
+// Wave-uniform values computed through lane shuffles, made visibly uniform
+// (scalar registers) for the compiler.
+__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ long long uni(long long x) {
+  const unsigned lo = __builtin_amdgcn_readfirstlane(unsigned(x & 0xffffffffll));
+  const unsigned hi = __builtin_amdgcn_readfirstlane(unsigned((unsigned long long)x >> 32));
+  return (long long)(((unsigned long long)hi << 32) | lo);
+}
+
+__device__ __forceinline__ long long seg_tiles(int L, int lead) {
+  const int nt = tiles_of(L);
+  return nt > 0 ? nt + lead : 0;
+}
+
+// Every lane of the wave: the workgroup's range from the lengths (lane s
+// holds L_s; b <= 64).
+__device__ Range locate(const DecodeParams& p, int Lreg, int wg) {
+  const int lane = threadIdx.x & 63;
+  const long long v = lane < p.b ? (long long)p.g * seg_tiles(Lreg, p.seg_lead) : 0;
+  const long long incl = wave_inclusive_scan(v);
+  Range r;
+  r.total = uni(__shfl(incl, 63, 64));
+  r.parts = r.total < p.workgroups ? int(r.total) : p.workgroups;
+  const bool takes_part = wg < r.parts;
+  const int parts_nz = r.parts > 0 ? r.parts : 1;
+  r.u = takes_part ? range_begin(wg, r.total, parts_nz) : 0;
+  r.u_end = takes_part ? range_begin(wg + 1, r.total, parts_nz) : 0;
+  const long long excl = incl - v;
+  const unsigned long long hit = __ballot(lane < p.b && v > 0 && excl <= r.u && r.u < incl);
+  const int src = hit ? __ffsll((long long)hit) - 1 : 0;
+  r.s = uni(hit ? src : p.b);
+  r.seq_base = uni(hit ? __shfl(excl, src, 64) : r.total);
+  r.u = uni(r.u);
+  r.u_end = uni(r.u_end);
+  return r;
+}
+
+struct StreamPiece {
+  int s, grp, L;
+  int tb, te;  // real tiles [tb, te) of the segment
+  int p0, p1;  // first and last workgroups whose ranges hold real tiles of the segment
+};
+
+// Next piece of the range (lengths from the lane registers via shuffles).
+__device__ bool next_piece(const DecodeParams& p, Range& r, int Lreg, StreamPiece& pc) {
+  const int lead = p.seg_lead;
+  while (r.u < r.u_end) {
+    int L = uni(__shfl(Lreg, r.s, 64));
+    long long seq = (long long)p.g * seg_tiles(L, lead);
+    while (r.u >= r.seq_base + seq && r.s + 1 < p.b) {
+      r.seq_base += seq;
+      ++r.s;
+      L = uni(__shfl(Lreg, r.s, 64));
+      seq = (long long)p.g * seg_tiles(L, lead);
+    }
+    const int nt = tiles_of(L);
+    const int sl = nt + lead;
+    const long long within = r.u - r.seq_base;
+    const int grp = int(within / sl);
+    const int ub = int(within - (long long)grp * sl);
+    const long long remain = r.u_end - r.u;
+    const long long seg_left = sl - ub;
+    const int ue = ub + int(remain < seg_left ? remain : seg_left);
+    r.u += ue - ub;
+    const int rb = (ub > lead ? ub : lead) - lead;
+    const int re = ue - lead;
+    if (re <= rb) continue;  // only the segment's empty lead tiles
+    pc.s = r.s;
+    pc.grp = grp;
+    pc.L = L;
+    pc.tb = rb;
+    pc.te = re;
+    const long long seg_u0 = r.seq_base + (long long)grp * sl + lead;
+    pc.p0 = owner_of(seg_u0, r.total, r.parts);
+    pc.p1 = owner_of(seg_u0 + nt - 1, r.total, r.parts);
+    return true;
+  }
+  return false;
+}
+
+// Byte offset of partial slot `slot` of workgroup `wg`.
+__device__ __forceinline__ int slot_offset(const DecodeParams& p, int wg, int slot) {
+  return (wg * 2 + slot) * p.slot_floats * int(sizeof(float));
+}
+
+// One step of the in-order merge of a segment's partial states: fold the
+// state (m, l, o) of the next part into the running (run, den, acc). Every
+// merge of a split segment in this kernel goes through this exact sequence,
+// so its result does not depend on which workgroup or path performed it.
+struct MergeWeights2 {
+  float r, w, run;
+};
+__device__ __forceinline__ MergeWeights2 merge_weights2(float run, float m) {
+  const float M = fmaxf(run, m);
+  const float sub = (M == kNegInf) ? 0.0f : M;
+  return {fast_exp2(run - sub), fast_exp2(m - sub), M};
+}
+__device__ __forceinline__ f32x4 merge_o(f32x4 acc, const MergeWeights2& mw, f32x4 o) {
+  f32x4 out;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) out[e] = __builtin_fmaf(mw.w, o[e], acc[e] * mw.r);
+  return out;
+}
+__device__ __forceinline__ float merge_l(float den, const MergeWeights2& mw, float l) {
+  return __builtin_fmaf(mw.w, l, den * mw.r);
+}
+__device__ __forceinline__ uint2 to_bf16x4(f32x4 v) {
+  uint2 pk;
+  pk.x = uint32_t(f32_to_bf16(v[0])) | (uint32_t(f32_to_bf16(v[1])) << 16);
+  pk.y = uint32_t(f32_to_bf16(v[2])) | (uint32_t(f32_to_bf16(v[3])) << 16);
+  return pk;
+}
+
+// Fused step: counting the workgroups out after their read of the lengths.
+// Workgroup wg counts on first-level counter wg mod 16; the last of each
+// group counts on the top counter; the last of those writes the lengths and
+// re-zeroes all counters. The folding wave drives it between tiles: the
+// atomics are issued early and their results looked at only later.
+struct LenCount {
+  int state;  // 0 first-level count issued, 1 top count issued, 2 done
+  int val;
+  __device__ void start(const DecodeParams& p, int wg) {
+    // called after the workgroup barrier that follows the read of lens (its
+    // values are in LDS by then); keep the compiler from moving the count up
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    int v = 0;
+    if ((threadIdx.x & 63) == 0)
+      v = __hip_atomic_fetch_add(p.ws_done + kCountStride * (1 + wg % kCountGroups), 1, __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
+    val = v;  // only lane 0's value is meaningful; read through readfirstlane
+    state = 0;
+  }
+  __device__ void step(const DecodeParams& p, const int* s_lens) {
+    if (state == 2) return;
+    const int wg = blockIdx.x;
+    const int P = int(gridDim.x);
+    const int v = __builtin_amdgcn_readfirstlane(val);
+    if (state == 0) {
+      const int grp = wg % kCountGroups;
+      const int members = (P - grp + kCountGroups - 1) / kCountGroups;
+      if (v != members - 1) {
+        state = 2;
+        return;
+      }
+      int t = 0;
+      if ((threadIdx.x & 63) == 0) t = __hip_atomic_fetch_add(p.ws_done, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      val = t;
+      state = 1;
+      return;
+    }
+    // state 1: the top count's result
+    const int groups = P < kCountGroups ? P : kCountGroups;
+    if (v == groups - 1) {
+      const int lane = threadIdx.x & 63;
+      if (lane < p.b) p.lens[lane] = s_lens[lane];  // attended length = grown length
+      if (lane < groups) __hip_atomic_store(p.ws_done + kCountStride * (1 + lane), 0, __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_AGENT);
+      if (lane == 0) __hip_atomic_store(p.ws_done, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    state = 2;
+  }
+};
+
+// Ready flag of partial slot `slot` of workgroup `wg` (zero between calls).
+__device__ __forceinline__ int* slot_flag(const DecodeParams& p, int wg, int slot) {
+  return p.ws_done + kFlagsOffset / sizeof(int) + wg * 2 + slot;
+}
+
+// The merging wave waits until every other part of segment p0 .. p0 +
+// n_slots - 1 has raised its ready flag (each has already taken its ticket,
+// so it is running and only has its stores left). The wait is bounded.
+__device__ void wait_parts(const DecodeParams& p, int p0, int n_slots, int own) {
+  const int lane = threadIdx.x & 63;
+  for (int q0 = 0; q0 < n_slots; q0 += 64) {
+    const int q = q0 + lane;
+    const bool need = q < n_slots && q != own;
+    int* f = need ? slot_flag(p, p0 + q, q == 0 ? 1 : 0) : nullptr;
+    for (int it = 0; it < kFlagSpins; ++it) {
+      const bool ready = !need || __hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0;
+      if (__ballot(!ready) == 0) break;
+      __builtin_amdgcn_s_sleep(2);
+    }
+  }
+}
+
+// Merge of the parts of segment (s, j) in part order (slot 1 of p0, then
+// slot 0 of p0 + 1 .. p0 + n_slots - 1), with part `own` taken from this
+// wave's registers, up to B parts' loads in flight at a time; then the
+// output rows. Lane layout as in fold_range.
+template <int NCH>
+__device__ void merge_parts(const DecodeParams& p, int s, int j, int p0, int n_slots, int own,
+                            const f32x4 (&own_o)[NCH], float own_m, float own_l) {
+  constexpr int HP = (kD / 4) / NCH;
+  constexpr int B = fast_slots<NCH>();
+  const int lane = threadIdx.x & 63;
+  const int G = p.G;
+  const int hh = lane / HP;
+  const int sub = lane - hh * HP;
+  if (hh >= G) return;
+  const __amdgpu_buffer_rsrc_t rs = slots_rsrc(p);
+  const int ml_off = G * kD * int(sizeof(float));
+  float run = kNegInf, den = 0.0f;
+  f32x4 res[NCH];
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) res[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int k0 = 0; k0 < n_slots; k0 += B) {
+    f32x4 o[B][NCH];
+    float m[B], l[B];
+#pragma unroll
+    for (int q = 0; q < B; ++q) {
+      const int k = k0 + q;
+      if (k < n_slots && k != own) {
+        const int sb = slot_offset(p, p0 + k, k == 0 ? 1 : 0);
+#pragma unroll
+        for (int i = 0; i < NCH; ++i) o[q][i] = coherent_load4(rs, sb + (hh * kD + 4 * (sub + HP * i)) * 4);
+        m[q] = coherent_load1(rs, sb + ml_off + hh * 4);
+        l[q] = coherent_load1(rs, sb + ml_off + (G + hh) * 4);
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < B; ++q) {
+      const int k = k0 + q;
+      if (k < n_slots) {
+        const bool mine = k == own;
+        const MergeWeights2 mw = merge_weights2(run, mine ? own_m : m[q]);
+#pragma unroll
+        for (int i = 0; i < NCH; ++i) res[i] = merge_o(res[i], mw, mine ? own_o[i] : o[q][i]);
+        den = merge_l(den, mw, mine ? own_l : l[q]);
+        run = mw.run;
+      }
+    }
+  }
+  const float inv = den > 0.0f ? 1.0f / den : 0.0f;
+  uint16_t* out = static_cast<uint16_t*>(p.out) + (size_t(s) * p.h + size_t(j) * G + hh) * kD;
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) *reinterpret_cast<uint2*>(out + 4 * (sub + HP * i)) = to_bf16x4(res[i] * inv);
+}
+
+// The folding wave: fold the tile states of the workgroup's range in tile
+// order and finish every piece (write it out or publish it), count the
+// workgroup out for the fused step's lengths, settle tickets. Lane layout:
+// HP = 32 / NCH lanes per head (NCH = 2, 4, 8 for up to 4, 8, 16 heads);
+// lane l holds head l / HP and its four-dim columns c = (l mod HP) + HP i,
+// i < NCH, so each lane weighs a single head per tile.
+template <int NCH, bool FUSED>
+__device__ void fold_range(const DecodeParams& p, const Range& range, int Lreg, float (*s_o)[kHeads * kRow],
+                           float (*s_m)[kHeads], float (*s_l)[kHeads], int* s_ready, int* s_folded,
+                           const int* s_lens) {
+  constexpr int HP = (kD / 4) / NCH;
+  const int wg = blockIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int G = p.G;
+  const int hh = lane / HP;
+  const int sub = lane - hh * HP;
+  const bool active = hh < G;
+  LenCount cnt;
+  cnt.state = 2;
+  if (FUSED) cnt.start(p, wg);
+  Range it = range;
+  StreamPiece pc;
+  int k = 0;  // next range tile to fold
+  while (next_piece(p, it, Lreg, pc)) {
+    const int n = pc.te - pc.tb;
+    const int s = pc.s, j = pc.grp;
+    const bool shared = pc.p0 != pc.p1;
+    const bool inline_merge = shared && !p.merge_kernel;
+    const int n_slots = pc.p1 - pc.p0 + 1;
+    const int own = wg - pc.p0;  // this workgroup's part of the segment
+    int* ticket = p.ws_cnt + (size_t(s) * p.ngroups + j) * p.cnt_stride;
+    // a few tiles before the end, look at the ticket: if every other part
+    // has counted in by then, this one merges without counting
+    const int peek_at = n > kPeekTiles ? n - kPeekTiles : 0;
+    int peek = -1;
+    f32x4 acc[NCH];
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) acc[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    float am = kNegInf, al = 0.0f;
+    for (int e = 0; e < n; ++e, ++k) {
+      if (inline_merge && e == peek_at && lane == 0)
+        peek = __hip_atomic_load(ticket, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const int slot = k & (kRing - 1);
+      while (__hip_atomic_load(&s_ready[slot], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) != k)
+        __builtin_amdgcn_s_sleep(1);
+      if (active) {
+        const float* row = &s_o[slot][hh * kRow + 4 * sub];
+        f32x4 ot[NCH];
+#pragma unroll
+        for (int i = 0; i < NCH; ++i) ot[i] = *reinterpret_cast<const f32x4*>(row + 4 * HP * i);
+        const float mt = s_m[slot][hh];
+        const float lt = s_l[slot][hh];
+        const float M = fmaxf(am, mt);
+        const float sb = (M == kNegInf) ? 0.0f : M;
+        const float a = fast_exp2(am - sb), bt = fast_exp2(mt - sb);
+#pragma unroll
+        for (int i = 0; i < NCH; ++i) acc[i] = acc[i] * a + ot[i] * bt;
+        al = al * a + lt * bt;
+        am = M;
+      }
+      // every lane's reads of the slot are done before it is handed back
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+      __builtin_amdgcn_wave_barrier();
+      if (lane == 0) __hip_atomic_store(s_folded, k + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+      if (FUSED) cnt.step(p, s_lens);
+    }
+    // the piece is complete
+    if (!shared) {
+      if (active) {
+        uint16_t* out = static_cast<uint16_t*>(p.out) + (size_t(s) * p.h + size_t(j) * G + hh) * kD;
+        const float inv = al > 0.0f ? 1.0f / al : 0.0f;
+#pragma unroll
+        for (int i = 0; i < NCH; ++i) *reinterpret_cast<uint2*>(out + 4 * (sub + HP * i)) = to_bf16x4(acc[i] * inv);
+      }
+      if (p.merge_kernel && pc.tb == 0 && lane == 0) p.seg_info[size_t(s) * p.ngroups + j] = make_int2(pc.p0, -1);
+      continue;
+    }
+    int t = n_slots - 1;  // every other part counted in at the peek
+    if (!inline_merge || __builtin_amdgcn_readfirstlane(peek) != n_slots - 1) {
+      t = 0;
+      if (inline_merge && lane == 0) t = __hip_atomic_fetch_add(ticket, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      t = __builtin_amdgcn_readfirstlane(t);
+    }
+    if (inline_merge && t == n_slots - 1) {
+      // the last part: merge once the others' states are in their slots, and
+      // leave the ticket and their flags at zero
+      wait_parts(p, pc.p0, n_slots, own);
+      merge_parts<NCH>(p, s, j, pc.p0, n_slots, own, acc, am, al);
+      if (lane < n_slots && lane != own)
+        __hip_atomic_store(slot_flag(p, pc.p0 + lane, lane == 0 ? 1 : 0), 0, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+      if (lane == 0) __hip_atomic_store(ticket, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      continue;
+    }
+    // publish this part's state, then (inline merge) its ready flag
+    const __amdgpu_buffer_rsrc_t rs = slots_rsrc(p);
+    const int ml_off = G * kD * int(sizeof(float));
+    const int my_slot = wg == pc.p0 ? 1 : 0;
+    const int slot_off = slot_offset(p, wg, my_slot);
+    if (active) {
+#pragma unroll
+      for (int i = 0; i < NCH; ++i)
+        coherent_store4(rs, slot_off + (hh * kD + 4 * (sub + HP * i)) * int(sizeof(float)), acc[i]);
+      if (sub == 0) {
+        coherent_store1(rs, slot_off + ml_off + hh * 4, am);
+        coherent_store1(rs, slot_off + ml_off + (G + hh) * 4, al);
+      }
+    }
+    if (p.merge_kernel) {
+      if (pc.tb == 0 && lane == 0) p.seg_info[size_t(s) * p.ngroups + j] = make_int2(pc.p0, pc.p1);
+    } else {
+      wait_stores();
+      if (lane == 0) __hip_atomic_store(slot_flag(p, wg, my_slot), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  if (FUSED) {
+    while (cnt.state != 2) cnt.step(p, s_lens);
+  }
+}
+
+template <bool FUSED, bool PAGED>
+__global__ __launch_bounds__(kBlockThreads, 1) void decode_stream_kernel(DecodeParams p) {
+  __shared__ __attribute__((aligned(16))) float s_o[kRing][kHeads * kRow];
+  __shared__ float s_m[kRing][kHeads];
+  __shared__ float s_l[kRing][kHeads];
+  __shared__ int s_ready[kRing];  // range tile index whose state a ring slot holds (-1: none yet)
+  __shared__ int s_lens[64];
+  __shared__ int s_next;          // next range tile to hand out
+  __shared__ int s_folded;        // range tiles folded so far
+
+  const int wg = blockIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int n16 = lane & 15;
+  const int q4 = lane >> 4;
+  const int G = p.G;
+  const float sl2 = p.scale_log2;
+
+  if (w == 0) s_lens[lane] = lane < p.b ? attended_len(p, lane) : 0;
+  if (threadIdx.x < kRing) s_ready[threadIdx.x] = -1;
+  if (threadIdx.x == 0) {
+    s_next = 0;
+    s_folded = 0;
+  }
+  if (!FUSED) zero_empty_sequences<uint16_t, false>(p, wg);
+  __syncthreads();
+
+  const int Lreg = s_lens[lane];
+  const Range range = locate(p, Lreg, wg);
+
+  if (w != kFolder) {
+    // ---- streaming wave: take tiles, leave their states in the ring
+    Range it = range;
+    StreamPiece pc;
+    bool have = next_piece(p, it, Lreg, pc);
+    long long kb = 0;             // range tiles before piece pc
+    int q_seg = -1;               // segment whose query rows are in qop
+    bf16x8 qop[4];
+    while (have) {
+      int k = 0;
+      if (lane == 0) k = __hip_atomic_fetch_add(&s_next, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      k = __builtin_amdgcn_readfirstlane(k);
+      while (have && k >= kb + (pc.te - pc.tb)) {
+        kb += pc.te - pc.tb;
+        have = next_piece(p, it, Lreg, pc);
+      }
+      if (!have) break;
+      const int s = pc.s, j = pc.grp;
+      const size_t kv_head = size_t(s) * p.g + j;
+      const int tile = pc.tb + int(k - kb);
+      const int t0 = tile * kTile;
+      const int nvalid = pc.L - t0;
+      if (FUSED && nvalid <= kTile) {
+        // the segment's last tile holds the appended token: store its rows
+        // into their cache slot, wait for the stores, then read the tile
+        const size_t new_row = kv_row<PAGED, true>(p.pg, p.g, p.cap, s, j, pc.L - 1);
+        if (lane < 32) {
+          const bool is_k = lane < 16;
+          const uint16_t* src = static_cast<const uint16_t*>(is_k ? p.k_new : p.v_new) + kv_head * kD;
+          uint16_t* dst = static_cast<uint16_t*>(is_k ? p.k_cache : p.v_cache) + new_row * kD;
+          st16(dst + 8 * (lane & 15), ld16(src + 8 * (lane & 15)));
+        }
+        wait_stores();
+      }
+      const uint16_t* kbp;
+      const uint16_t* vbp;
+      if constexpr (PAGED) {
+        const size_t row = kv_row<true, true>(p.pg, p.g, p.cap, s, j, t0);
+        kbp = static_cast<const uint16_t*>(p.k_cache) + row * kD;
+        vbp = static_cast<const uint16_t*>(p.v_cache) + row * kD;
+      } else {
+        kbp = static_cast<const uint16_t*>(p.k_cache) + (kv_head * p.cap + t0) * kD;
+        vbp = static_cast<const uint16_t*>(p.v_cache) + (kv_head * p.cap + t0) * kD;
+      }
+      Tile t;
+      if (nvalid >= kTile) load_tile<true>(t, kbp, vbp, kTile, n16, q4);
+      else load_tile<false>(t, kbp, vbp, nvalid, n16, q4);
+      const int seg = s * p.g + j;
+      if (seg != q_seg) {
+        // the group's query rows, after the tile's loads are on their way
+        const uint16_t* qg = static_cast<const uint16_t*>(p.q) + (size_t(s) * p.h + size_t(j) * G) * kD;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          u32x4 v = {0u, 0u, 0u, 0u};
+          if (n16 < G) v = ld16(qg + size_t(n16) * kD + ks * 32 + q4 * 8);
+          qop[ks] = as_bf16x8(v);
+        }
+        q_seg = seg;
+      }
+      f32x4 o[8];
+      float m, l;
+      if (nvalid >= kTile) tile_state<true>(o, m, l, qop, t, kTile, sl2, q4);
+      else tile_state<false>(o, m, l, qop, t, nvalid, sl2, q4);
+      // slot k mod kRing is free once tile k - kRing has been folded
+      const int slot = k & (kRing - 1);
+      while (__hip_atomic_load(&s_folded, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) <= k - kRing)
+        __builtin_amdgcn_s_sleep(1);
+      if (n16 < G) {
+        float* row = &s_o[slot][n16 * kRow + 32 * q4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          *reinterpret_cast<f32x4*>(row + 8 * i) = f32x4{o[0][i], o[1][i], o[2][i], o[3][i]};
+          *reinterpret_cast<f32x4*>(row + 8 * i + 4) = f32x4{o[4][i], o[5][i], o[6][i], o[7][i]};
+        }
+        if (q4 == 0) {
+          s_m[slot][n16] = m;
+          s_l[slot][n16] = l;
+        }
+      }
+      // every lane's writes are done before the slot is marked
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+      __builtin_amdgcn_wave_barrier();
+      if (lane == 0) __hip_atomic_store(&s_ready[slot], k, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+    return;
+  }
+
+  // ---- folding wave (one instance per head-block width)
+  if (G <= 4) fold_range<2, FUSED>(p, range, Lreg, s_o, s_m, s_l, s_ready, &s_folded, s_lens);
+  else if (G <= 8) fold_range<4, FUSED>(p, range, Lreg, s_o, s_m, s_l, s_ready, &s_folded, s_lens);
+  else fold_range<8, FUSED>(p, range, Lreg, s_o, s_m, s_l, s_ready, &s_folded, s_lens);
+}
+
+template <bool FUSED, bool PAGED>
+void launch(const DecodeParams& p, hipStream_t stream) {
+  hipLaunchKernelGGL((decode_stream_kernel<FUSED, PAGED>), dim3(p.workgroups), dim3(kBlockThreads), 0, stream, p);
+}
+
+}  // namespace
+
+hipError_t launch_decode_stream(const DecodeParams& p, hipStream_t stream) {
+  const bool paged = p.pg.table != nullptr;
+  if (p.fused) paged ? launch<true, true>(p, stream) : launch<true, false>(p, stream);
+  else paged ? launch<false, true>(p, stream) : launch<false, false>(p, stream);
+  return hipGetLastError();
+}
+
+// Workgroups of the instance that fit on one compute unit (cached per
+// process; the answer depends only on the kernel and the architecture).
+int stream_workgroups_per_cu(bool fused, bool paged) {
+  static std::atomic<int> cached[4] = {};
+  const int k = (fused ? 1 : 0) + (paged ? 2 : 0);
+  const int known = cached[k].load(std::memory_order_relaxed);
+  if (known > 0) return known;
+  int n = 0;
+  hipError_t e;
+  switch (k) {
+    case 0: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_stream_kernel<false, false>, kBlockThreads, 0); break;
+    case 1: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_stream_kernel<true, false>, kBlockThreads, 0); break;
+    case 2: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_stream_kernel<false, true>, kBlockThreads, 0); break;
+    default: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_stream_kernel<true, true>, kBlockThreads, 0); break;
+  }
+  if (e != hipSuccess || n <= 0) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  cached[k].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+}  // namespace gqa

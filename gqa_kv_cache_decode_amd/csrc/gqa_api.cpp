@@ -44,6 +44,7 @@ constexpr int kSegmentLead32 = 3;      // four-wave kernel, 17-32 heads
 constexpr int kSegmentLead64 = 5;      // four-wave kernel, 33-64 heads
 constexpr int kMaxSegmentLead = 5;
 constexpr int kLeadMinUnits = 8;       // four-wave kernels: lead units only from this many units per workgroup
+constexpr int kStreamLeadTiles = 8;    // one-block stream kernel: empty tiles ahead of each segment
 
 bool supported_head_dim(int d) { return d == 16 || d == 32 || d == 64 || d == 128 || d == 256; }
 
@@ -69,7 +70,8 @@ struct Plan {
   int nhb;
   int workgroups;
   bool merge_kernel;  // shared segments merged by a second launch
-  int seg_lead;       // empty schedule units ahead of each segment
+  int seg_lead;       // empty schedule units ahead of each segment (tiles for the stream kernel)
+  bool stream;        // the one-block stream kernel (decode_stream.hip)
 };
 
 // Largest head block any path may use for G heads per KV head (workspace sizing).
@@ -126,19 +128,23 @@ int plan_decode(int b, int h, int g, int d_k, int d_v, int cap, int max_len, int
     plan->gblk = gqa::vector_heads_per_block(G);
     plan->nhb = (G + plan->gblk - 1) / plan->gblk;
   }
+  // One query token, at most 16 heads per KV head and 64 sequences: the
+  // stream kernel (tile-granular schedule, waves finishing pieces on their own).
+  plan->stream = chosen == GQA_PATH_MATRIX && !causal && G <= gqa::kStreamMaxGroup && b <= gqa::kStreamMaxBatch;
   const int waves = chosen == GQA_PATH_MATRIX ? gqa::matrix_waves(G) : gqa::vector_waves(dtype, d_k, plan->gblk);
-  const int unit_len = gqa::kTile * gqa::kUnitTiles;
+  const int unit_len = plan->stream ? gqa::kTile : gqa::kTile * gqa::kUnitTiles;
   const long long segments = (long long)b * g * plan->nhb;
   // lengths <= max_len; kMaxSegmentLead: empty units ahead of each segment (at most)
   const long long units_plain = segments * ((max_len + unit_len - 1) / unit_len);
-  const long long units_bound = units_plain + segments * kMaxSegmentLead;
+  const long long units_bound = units_plain + segments * (plan->stream ? kStreamLeadTiles : kMaxSegmentLead);
   const bool auto_grid = workgroups == 0;
   if (auto_grid) {
     // Up to eight waves per compute unit (two 4-wave workgroups or one
     // 8-wave one keep enough loads in flight), never more than fit at once, so
     // the persistent grid runs in a single round.
-    int fit = chosen == GQA_PATH_MATRIX ? gqa::matrix_workgroups_per_cu(G, fused, paged, causal)
-                                        : gqa::vector_workgroups_per_cu(dtype, d_k, plan->gblk, fused, paged, causal);
+    int fit = plan->stream ? gqa::stream_workgroups_per_cu(fused, paged)
+              : chosen == GQA_PATH_MATRIX ? gqa::matrix_workgroups_per_cu(G, fused, paged, causal)
+                                          : gqa::vector_workgroups_per_cu(dtype, d_k, plan->gblk, fused, paged, causal);
     if (fit <= 0) fit = 2;  // no device to ask: assume the common case
     const int per_cu_max = 8 / waves;
     const int per_cu = fit < per_cu_max ? fit : per_cu_max;
@@ -165,7 +171,8 @@ int plan_decode(int b, int h, int g, int d_k, int d_v, int cap, int max_len, int
     // workgroup (at most 4 KiB of partial state per 16 KiB tile of K/V) so
     // that the single-workgroup merges stay small.
     const int min_tiles = plan->gblk / 2;
-    const int min_units = min_tiles > gqa::kUnitTiles ? (min_tiles + gqa::kUnitTiles - 1) / gqa::kUnitTiles : 1;
+    const int min_units = plan->stream ? (min_tiles > 1 ? min_tiles : 1)
+                          : min_tiles > gqa::kUnitTiles ? (min_tiles + gqa::kUnitTiles - 1) / gqa::kUnitTiles : 1;
     const long long by_work = (units_bound + min_units - 1) / min_units;
     if (workgroups > by_work) workgroups = int(by_work > 0 ? by_work : 1);
   }
@@ -183,7 +190,9 @@ int plan_decode(int b, int h, int g, int d_k, int d_v, int cap, int max_len, int
   // units (MQA, one long sequence per KV head) they only add imbalance, and
   // the vector path was measured neutral or slower.
   plan->seg_lead = 0;
-  if (chosen == GQA_PATH_MATRIX) {
+  if (plan->stream) {
+    plan->seg_lead = kStreamLeadTiles;
+  } else if (chosen == GQA_PATH_MATRIX) {
     if (waves == 8) {
       const long long seg_units = (max_len + unit_len - 1) / unit_len;  // the longest segment
       plan->seg_lead = seg_units <= kShortSegmentUnits ? kSegmentLead8Short : kSegmentLead8;
@@ -271,8 +280,8 @@ int decode_prepare(const char* fn, void* out, const void* q, void* k_cache, void
   char* wsb = static_cast<char*>(workspace);
   p.seg_info = reinterpret_cast<int2*>(wsb);
   p.ws_slots = reinterpret_cast<float*>(wsb + ws.info_bytes);
-  p.ws_done = reinterpret_cast<int*>(wsb + usable - 256);
-  p.ws_cnt = reinterpret_cast<int*>(wsb + usable - 256 - ws.cnt_bytes);
+  p.ws_done = reinterpret_cast<int*>(wsb + usable - gqa::kDoneBytes);
+  p.ws_cnt = reinterpret_cast<int*>(wsb + usable - gqa::kDoneBytes - ws.cnt_bytes);
   p.cnt_stride = int(gqa::counter_stride(b, h));
   p.merge_kernel = plan.merge_kernel ? 1 : 0;
   p.b = b;
@@ -298,8 +307,9 @@ int decode_prepare(const char* fn, void* out, const void* q, void* k_cache, void
 
 int decode_launch(const char* fn, const gqa::DecodeParams& p, const Plan& plan, int dtype, void* stream) {
   const hipStream_t st = static_cast<hipStream_t>(stream);
-  hipError_t e = plan.path == GQA_PATH_MATRIX ? gqa::launch_decode_matrix(p, st)
-                                              : gqa::launch_decode_vector(p, dtype, st);
+  hipError_t e = plan.stream ? gqa::launch_decode_stream(p, st)
+                 : plan.path == GQA_PATH_MATRIX ? gqa::launch_decode_matrix(p, st)
+                                                : gqa::launch_decode_vector(p, dtype, st);
   if (e != hipSuccess) return fail(GQA_ERR_HIP, "%s launch: %s", fn, hipGetErrorString(e));
   if (plan.merge_kernel) {
     e = gqa::launch_merge_partials(p, dtype, st);

@@ -39,7 +39,7 @@
 //   [slots]  float [kMaxWorkgroups][2][slot_floats]           slot = o[gb][d], m[gb], l[gb]
 // and from its end (size rounded down to 256 bytes):
 //   [tickets] int32, cnt_stride apart                         zero between calls
-//   [done]   int32 in the last 256 bytes                      zero between calls
+//   [done]   int32 counters and slot flags, last kDoneBytes   zero between calls
 // slot_floats = gb*d + round_up(2*gb, 4), so every slot and its o block are
 // 16-byte aligned. Each region starts on a 256-byte boundary.
 //
@@ -113,6 +113,12 @@ struct DecodeParams {
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// The very end of the workspace: the fused step's completion counters (one
+// top counter and 16 first-level ones, 128 bytes apart) in the first 4 KiB,
+// then one ready flag per partial slot (kMaxWorkgroups x 2 int32).
+constexpr size_t kFlagsOffset = 4096;
+constexpr size_t kDoneBytes = kFlagsOffset + size_t(kMaxWorkgroups) * 2 * sizeof(int);
+
 // y_s = x w_s^T for up to three weight matrices w_s [n_out_s][n_in] (bf16,
 // packed by launch_pack_weight), x [rows][n_in], y_s [rows][n_out_s];
 // blocks[s] = ceil(n_out_s / 16).
@@ -138,8 +144,8 @@ struct FoldParams {
 // Workspace layout, relative to the end of the caller's buffer so that a
 // buffer sized for one shape serves every smaller shape without the regions
 // of one call overlapping those of another: partial slots from the start,
-// then (at the end) the tickets and, in the last 256 bytes, the fused step's
-// counter. Tickets sit 128 bytes apart when b*h <= 8192, so that workgroups
+// then (at the end) the tickets and, in the last kDoneBytes bytes, the fused
+// step's counters. Tickets sit 128 bytes apart when b*h <= 8192, so that workgroups
 // taking tickets of different segments at the same moment do not contend for
 // one cache line; the ticket region never shrinks as b*h grows.
 inline size_t counter_stride(int b, int h) { return size_t(b) * size_t(h) <= 8192 ? 32 : 1; }
@@ -162,7 +168,7 @@ inline WorkspaceLayout workspace_layout(int b, int h, int gblk_bound, int d_v) {
   w.info_bytes = align256(size_t(b) * size_t(h) * 2 * sizeof(int));
   w.slot_bytes = align256(size_t(kMaxWorkgroups) * 2 * size_t(slot_floats_for(gblk_bound, d_v)) * sizeof(float));
   w.cnt_bytes = align256(counter_ints(b, h) * sizeof(int));
-  w.total = w.info_bytes + w.slot_bytes + w.cnt_bytes + 256;
+  w.total = w.info_bytes + w.slot_bytes + w.cnt_bytes + kDoneBytes;
   return w;
 }
 
@@ -174,6 +180,12 @@ constexpr int kMergeLds = 2 * kMergePairs + 3 * kMatrixMaxGroup;
 hipError_t launch_append(const AppendParams& p, int b, int dtype, hipStream_t stream);
 hipError_t launch_decode_vector(const DecodeParams& p, int dtype, hipStream_t stream);
 hipError_t launch_decode_matrix(const DecodeParams& p, hipStream_t stream);
+// One-token matrix decode for up to 16 heads per KV head and up to 64
+// sequences (decode_stream.hip); seg_lead counts empty tiles there.
+constexpr int kStreamMaxGroup = 16;
+constexpr int kStreamMaxBatch = 64;
+hipError_t launch_decode_stream(const DecodeParams& p, hipStream_t stream);
+int stream_workgroups_per_cu(bool fused, bool paged);
 hipError_t launch_merge_partials(const DecodeParams& p, int dtype, hipStream_t stream);
 hipError_t launch_linear(const LinearParams& p, hipStream_t stream);
 size_t packed_weight_bytes(int n_out, int n_in);

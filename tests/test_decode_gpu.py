@@ -125,16 +125,19 @@ def test_decode_loop_32_steps(gpu_lib, oracle_mod):
     wl = WORKLOADS["qwen25_7b_gqa_bf16"]
     print("decode loop: qwen25_7b_gqa_bf16, 32 steps", flush=True)
     pb = _workload_problem(oracle_mod, wl.name)
-    rows = np.arange(0, wl.b, 8)  # sampled sequences checked against the oracle at every step
     for step in range(wl.steps):
+        # every sequence and head against the oracle at every step, and the
+        # appended caches and lengths bit for bit
         pb.step = step
         pb.append()
+        assert np.array_equal(pb.lens.cpu().numpy(), pb.lens_h), f"step {step}"
+        assert np.array_equal(to_host_bits(pb.kc).view(np.uint8), pb.batch.k_cache.view(np.uint8)), f"step {step}"
+        assert np.array_equal(to_host_bits(pb.vc).view(np.uint8), pb.batch.v_cache.view(np.uint8)), f"step {step}"
         q = pb.query()
         out, _ = pb.gpu_attention(q)
-        ref = pb.oracle_attention(q, rows)
-        assert_parity(out[torch.from_numpy(rows).cuda()], ref, pb.dtype, f"step {step}")
+        ref = pb.oracle_attention(q)
+        assert_parity(out, ref, pb.dtype, f"step {step}")
     assert int(pb.lens_h.min()) == int(pb.lens_h.max()) == 2080
-    assert np.array_equal(pb.lens.cpu().numpy(), pb.lens_h)
 
 
 EDGE = [
