@@ -151,6 +151,33 @@ def decode_step(out: torch.Tensor, q: torch.Tensor, k_new: torch.Tensor, v_new: 
     return out
 
 
+def decode_step_static(out: torch.Tensor, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                       k_cache: torch.Tensor, v_cache: torch.Tensor, lens: torch.Tensor, max_len: int, scale: float,
+                       stream=None) -> torch.Tensor:
+    """decode_step with the library's own per-GPU scratch array as workspace (allocates nothing).
+
+    Calls that overlap on one GPU race on that array; serialise them.
+    """
+    _check_gpu(out, q, k_new, v_new, k_cache, v_cache, lens)
+    if lens.dtype != torch.int32:
+        raise TypeError("lens must be int32")
+    b, h, d_k = q.shape
+    bk, g, cap, dk2 = k_cache.shape
+    d_v = v_cache.shape[3]
+    if bk != b or dk2 != d_k or tuple(v_cache.shape) != (b, g, cap, d_v) or tuple(out.shape) != (b, h, d_v) \
+            or tuple(lens.shape) != (b,) or tuple(k_new.shape) != (b, g, d_k) or tuple(v_new.shape) != (b, g, d_v):
+        raise ValueError("decode_step_static: inconsistent shapes")
+    dt = _dtype_code(q)
+    if any(_dtype_code(t) != dt for t in (k_cache, v_cache, out, k_new, v_new)):
+        raise TypeError("q, rows, caches and out must share one element type")
+    lib = _lib.load()
+    rc = lib.gqa_decode_step_static(
+        out.data_ptr(), q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+        lens.data_ptr(), b, h, g, d_k, d_v, cap, int(max_len), ctypes.c_float(scale), dt, _stream_handle(stream))
+    _lib.check(rc, "gqa_decode_step_static")
+    return out
+
+
 class PackedWeight:
     """A [n_out, n_in] bf16 weight matrix in the library's packed layout (gqa_pack_weight)."""
 

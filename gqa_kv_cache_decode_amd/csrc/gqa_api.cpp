@@ -256,12 +256,15 @@ int decode_prepare(const char* fn, void* out, const void* q, void* k_cache, void
                    const void* k_new, const void* v_new, int b, int h, int g, int d_k, int d_v, int cap,
                    int max_len_att, float scale, int dtype, void* workspace, size_t workspace_bytes, int path,
                    int workgroups, int fused, gqa::DecodeParams* pp, Plan* planp,
-                   const gqa::PagedLayout* paged = nullptr, bool causal = false) {
+                   const gqa::PagedLayout* paged = nullptr, bool causal = false, bool slots_by_grid = false) {
   Plan& plan = *planp;
   const int rc = plan_decode(b, h, g, d_k, d_v, cap, max_len_att, dtype, path, workgroups, &plan, fused != 0,
                              paged != nullptr, causal);
   if (rc != GQA_OK) return rc;
-  const gqa::WorkspaceLayout ws = gqa::workspace_layout(b, h, gblk_bound(h / g), d_v);
+  // Partial slots for every possible grid (the caller's workspace serves any
+  // call of this shape), or only for the planned grid (the static scratch).
+  const gqa::WorkspaceLayout ws = gqa::workspace_layout(b, h, gblk_bound(h / g), d_v,
+                                                        slots_by_grid ? plan.workgroups : gqa::kMaxWorkgroups);
   if (!workspace) return fail(GQA_ERR_WORKSPACE, "%s: workspace is null (%zu bytes needed)", fn, ws.total);
   const size_t usable = workspace_bytes & ~size_t(255);
   if (usable < ws.total)
@@ -736,6 +739,83 @@ int gqa_decode_attention(void* out, const void* q, const void* k_cache, const vo
                          size_t workspace_bytes, void* stream) {
   return gqa_decode_attention_ex(out, q, k_cache, v_cache, lens, b, h, g, d_k, d_v, cap, max_len,
                                  scale, dtype, workspace, workspace_bytes, stream, GQA_PATH_AUTO, 0);
+}
+
+}  // extern "C"
+
+// ----------------------------------------------------------- static scratch
+//
+// For callers that cannot allocate device memory (code under HIP graph
+// capture, tight serving loops, harnesses that forbid allocation): the fused
+// step with its workspace in this file-scope device array instead of a
+// caller buffer. Each GPU the library runs on holds its own copy (for the
+// life of the process) at its own address, which is fetched once per device
+// with hipGetSymbolAddress; host code uses that address, never the array's
+// name (which on the host is only a stand-in). The counters the kernels need
+// at zero are zero when the module is loaded and every call leaves them zero
+// again; the partial states need no clearing. All calls on one GPU share
+// the array, so calls that overlap on one GPU (different streams without
+// synchronisation) race.
+static constexpr size_t kStaticScratchBytes = size_t(8) << 20;  // 8 MiB
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+
+// Device address of this device's scratch array (nullptr and an error
+// message on failure). Concurrent first calls store the same address.
+void* static_scratch(const char* fn) {
+  static std::atomic<void*> addr[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    fail(GQA_ERR_HIP, "%s: no usable current device (%s)", fn, hipGetErrorString(e));
+    return nullptr;
+  }
+  void* known = addr[dev].load(std::memory_order_relaxed);
+  if (known) return known;
+  void* ptr = nullptr;
+  e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+  if (e != hipSuccess || !ptr) {
+    fail(GQA_ERR_HIP, "%s: hipGetSymbolAddress of the static scratch: %s", fn, hipGetErrorString(e));
+    return nullptr;
+  }
+  addr[dev].store(ptr, std::memory_order_relaxed);
+  return ptr;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gqa_decode_step_static(void* out, const void* q, const void* k_new, const void* v_new, void* k_cache,
+                           void* v_cache, int32_t* lens, int b, int h, int g, int d_k, int d_v, int cap, int max_len,
+                           float scale, int dtype, void* stream) {
+  const char* fn = "gqa_decode_step_static";
+  if (!out || !q || !k_new || !v_new || !k_cache || !v_cache || !lens)
+    return fail(GQA_ERR_ARG, "%s: null pointer argument", fn);
+  if (max_len < 0) return fail(GQA_ERR_ARG, "max_len=%d must be >= 0", max_len);
+  if (cap > 0 && (long long)max_len + 1 > cap)
+    return fail(GQA_ERR_CAPACITY, "appending to max_len=%d needs cap > %d, cap=%d", max_len, max_len, cap);
+  if (max_len == INT32_MAX) return fail(GQA_ERR_CAPACITY, "max_len=%d too large", max_len);
+  // every shape check first (no device is needed for them), then the scratch
+  // of the current device; the layout reserves partial slots for the planned
+  // grid only, and a shape that needs more than the array holds is rejected
+  Plan plan;
+  int rc = plan_decode(b, h, g, d_k, d_v, cap, max_len + 1, dtype, GQA_PATH_AUTO, 0, &plan, true);
+  if (rc != GQA_OK) return rc;
+  const size_t need = gqa::workspace_layout(b, h, gblk_bound(h / g), d_v, plan.workgroups).total;
+  if (need > kStaticScratchBytes)
+    return fail(GQA_ERR_WORKSPACE, "%s: this shape needs %zu bytes of workspace, the static scratch holds %zu", fn,
+                need, kStaticScratchBytes);
+  void* ws = static_scratch(fn);
+  if (!ws) return GQA_ERR_HIP;
+  gqa::DecodeParams p;
+  rc = decode_prepare(fn, out, q, k_cache, v_cache, lens, k_new, v_new, b, h, g, d_k, d_v, cap, max_len + 1, scale,
+                      dtype, ws, kStaticScratchBytes, GQA_PATH_AUTO, 0, 1, &p, &plan, nullptr, false, true);
+  if (rc != GQA_OK) return rc;
+  return decode_launch(fn, p, plan, dtype, stream);
 }
 
 }  // extern "C"

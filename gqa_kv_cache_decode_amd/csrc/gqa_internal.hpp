@@ -160,13 +160,15 @@ struct WorkspaceLayout {
 
 inline int slot_floats_for(int gblk, int d_v) { return gblk * d_v + ((2 * gblk + 3) & ~3); }
 
-// gblk_bound: the largest head block any path may use for this shape. From
-// the start: the segment table of the separate merge (two ints per segment,
-// at most b*h segments), then the partial slots; tickets at the end.
-inline WorkspaceLayout workspace_layout(int b, int h, int gblk_bound, int d_v) {
+// gblk_bound: the largest head block any path may use for this shape;
+// slot_wgs: the workgroups whose two partial slots are reserved (every
+// possible grid: kMaxWorkgroups; a known grid: its size). From the start:
+// the segment table of the separate merge (two ints per segment, at most
+// b*h segments), then the partial slots; tickets at the end.
+inline WorkspaceLayout workspace_layout(int b, int h, int gblk_bound, int d_v, int slot_wgs = kMaxWorkgroups) {
   WorkspaceLayout w;
   w.info_bytes = align256(size_t(b) * size_t(h) * 2 * sizeof(int));
-  w.slot_bytes = align256(size_t(kMaxWorkgroups) * 2 * size_t(slot_floats_for(gblk_bound, d_v)) * sizeof(float));
+  w.slot_bytes = align256(size_t(slot_wgs) * 2 * size_t(slot_floats_for(gblk_bound, d_v)) * sizeof(float));
   w.cnt_bytes = align256(counter_ints(b, h) * sizeof(int));
   w.total = w.info_bytes + w.slot_bytes + w.cnt_bytes + kDoneBytes;
   return w;

@@ -385,6 +385,23 @@ int gqa_fold_kv_heads(void* dst, const void* src, const int32_t* lens, int b, in
 int gqa_decode_plan(int b, int h, int g, int d_k, int d_v, int cap, int max_len, int dtype,
                     int path, int workgroups, int* chosen_path, int* chosen_workgroups);
 
+/*
+ * gqa_decode_step without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation. The workspace is an 8 MiB array inside
+ * the library, one per GPU, kept for the life of the process; the call
+ * allocates nothing. Same arguments, results (bit for bit), ordering and
+ * errors as gqa_decode_step, plus GQA_ERR_WORKSPACE when the shape needs
+ * more than the 8 MiB (partial slots are reserved only for the planned grid:
+ * the Llama-3-70B-shaped step, b = 16, h = 64, g = 8, d = 128, needs about
+ * 2.3 MB) and GQA_ERR_HIP if the array's device address cannot be obtained.
+ * All calls on one GPU share the array: calls that overlap on one GPU
+ * (different streams, not synchronised) race and must be serialised.
+ */
+int gqa_decode_step_static(void* out, const void* q, const void* k_new, const void* v_new, void* k_cache,
+                           void* v_cache, int32_t* lens, int b, int h, int g, int d_k, int d_v, int cap, int max_len,
+                           float scale, int dtype, void* stream);
+
 /* Message for the calling thread's last non-OK return ("" if none). */
 const char* gqa_last_error(void);
 

@@ -361,3 +361,24 @@ def test_multi_paged_rejects_on_the_host(lib):
     assert attend(max_len=257) == _lib.ERR_CAPACITY      # 4 blocks of 64 positions
     assert step(max_len=255) == _lib.ERR_CAPACITY        # 255 + 2 > 256
     assert append(max_len=255) == _lib.ERR_CAPACITY
+
+
+def test_static_scratch_step_rejects_on_the_host(lib):
+    # the allocation-free step checks everything a workspace call checks, and
+    # refuses shapes whose workspace would not fit its 8 MiB array, before any
+    # device work (no GPU is needed to reach these codes)
+    def step(**kw):
+        a = dict(out=FAKE, q=FAKE, kn=FAKE, vn=FAKE, kc=FAKE, vc=FAKE, lens=FAKE, b=16, h=64, g=8, d=128, cap=8300,
+                 max_len=8192, scale=0.088, dtype=_lib.BF16)
+        a.update(kw)
+        return lib.gqa_decode_step_static(a["out"], a["q"], a["kn"], a["vn"], a["kc"], a["vc"], a["lens"], a["b"],
+                                          a["h"], a["g"], a["d"], a["d"], a["cap"], a["max_len"], a["scale"],
+                                          a["dtype"], None)
+    assert step(q=None) == _lib.ERR_ARG
+    assert step(h=60, g=8) == _lib.ERR_GROUPS
+    assert step(max_len=8300) == _lib.ERR_CAPACITY
+    assert step(d=96) == _lib.ERR_UNSUPPORTED
+    # 64 sequences x 4096 heads, 64 heads per KV head: slots, segment table
+    # and tickets far beyond 8 MiB
+    assert step(b=64, h=4096, g=64, cap=4, max_len=1) == _lib.ERR_WORKSPACE
+    assert "static scratch" in lib.gqa_last_error().decode()
