@@ -24,9 +24,10 @@ Pages the oracle follows (cited by title and section):
   per-layer decode pseudocode and the bytes-per-token arithmetic.
 
 Parity status: every function here is pinned by ``tests/test_oracle_pins.py``,
-``tests/test_oracle_golden.py``, ``tests/test_oracle_layer.py`` and
-``tests/test_oracle_fold.py``, ``tests/test_oracle_paged.py`` and
-``tests/test_oracle_multi.py`` (no function is "parity unpinned").
+``tests/test_oracle_golden.py``, ``tests/test_oracle_layer.py``,
+``tests/test_oracle_fold.py``, ``tests/test_oracle_paged.py``,
+``tests/test_oracle_multi.py``, ``tests/test_oracle_multi_paged.py`` and
+``tests/test_oracle_merge.py`` (no function is "parity unpinned").
 """
 from __future__ import annotations
 
@@ -91,6 +92,9 @@ def _load():
         vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
         ctypes.c_float, i32, vp, i32,
     ]
+    lib.oracle_decode_attention_chunked.restype = i32
+    lib.oracle_decode_attention_chunked.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
+                                                    ctypes.c_float, i32, i32]
     lib.oracle_linear.restype = i32
     lib.oracle_linear.argtypes = [vp, vp, vp, i32, i32, i32, i32]
     lib.oracle_store.restype = None
@@ -190,6 +194,31 @@ def decode_attention(q, k_cache, v_cache, lens, scale: float, *, want_weights=Fa
     if count_muls:
         res.append(int(muls.value))
     return res[0] if len(res) == 1 else tuple(res)
+
+
+def decode_attention_chunked(q, k_cache, v_cache, lens, bounds, scale: float, threads: int = 0) -> np.ndarray:
+    """decode_attention computed chunk by chunk and merged [MQA-review §2.1 softmax over a union of chunks].
+
+    bounds int32 [b, n_chunks + 1]: chunk c of sequence s is positions
+    bounds[s, c] .. bounds[s, c + 1] - 1 (0 first, lens[s] last, non-decreasing).
+    """
+    for a in (q, k_cache, v_cache, lens):
+        if not a.flags.c_contiguous:
+            raise ValueError("oracle arrays must be C-contiguous")
+    bounds = np.ascontiguousarray(bounds, dtype=np.int32)
+    b, h, d_k = q.shape
+    _, g, cap, _ = k_cache.shape
+    d_v = v_cache.shape[3]
+    if bounds.ndim != 2 or bounds.shape[0] != b:
+        raise OracleError(ERR_ARG, "decode_attention_chunked bounds")
+    dt = _dtype_code(k_cache)
+    out = np.empty((b, h, d_v), dtype=np.float64)
+    rc = _load().oracle_decode_attention_chunked(
+        _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(np.ascontiguousarray(lens, dtype=np.int32)),
+        _ptr(bounds), bounds.shape[1] - 1, b, h, g, d_k, d_v, cap, ctypes.c_float(scale), dt, threads)
+    if rc != OK:
+        raise OracleError(rc, "decode_attention_chunked")
+    return out
 
 
 def linear(x, w) -> np.ndarray:

@@ -223,6 +223,115 @@ int oracle_decode_attention(double* out, double* weights, const void* q,
 }
 
 /*
+ * The same attention computed over a split of every sequence's positions
+ * into consecutive chunks: each chunk's state is computed on its own (m =
+ * its largest logit, l = sum over its positions of exp(s_t - m), o[v] = sum
+ * of exp(s_t - m) V[t][v]) and the states are combined with M = max_c m_c:
+ *   out[v] = sum_c exp(m_c - M) o_c[v] / sum_c exp(m_c - M) l_c.
+ * This is the softmax of [MQA-review §2.1] written over a union of position
+ * sets (a chunk with no positions is skipped); it equals the direct form in
+ * exact arithmetic and is the split-and-merge a split-K schedule performs.
+ * bounds is [b][n_chunks + 1]: chunk c of sequence s covers positions
+ * [bounds[s][c], bounds[s][c + 1]), with bounds[s][0] = 0, non-decreasing,
+ * and bounds[s][n_chunks] = lens[s] (ORC_ERR_ARG otherwise). Logits and
+ * sums run in index order within a chunk, chunks in order.
+ */
+int oracle_decode_attention_chunked(double* out, const void* q, const void* k_cache, const void* v_cache,
+                                    const int32_t* lens, const int32_t* bounds, int n_chunks, int b, int h,
+                                    int g, int d_k, int d_v, int cap, float scale, int dtype, int threads) {
+  if (!out || !q || !k_cache || !v_cache || !lens || !bounds || n_chunks <= 0) return ORC_ERR_ARG;
+  if (b <= 0 || h <= 0 || g <= 0 || d_k <= 0 || d_v <= 0 || cap <= 0) return ORC_ERR_ARG;
+  if (h % g != 0) return ORC_ERR_GROUPS;
+  if (dtype != ORC_F32 && dtype != ORC_BF16) return ORC_ERR_UNSUPPORTED;
+  for (int s = 0; s < b; ++s) {
+    if (lens[s] < 0 || lens[s] > cap) return ORC_ERR_CAPACITY;
+    const int32_t* bs = bounds + (size_t)s * (n_chunks + 1);
+    if (bs[0] != 0 || bs[n_chunks] != lens[s]) return ORC_ERR_ARG;
+    for (int c = 0; c < n_chunks; ++c)
+      if (bs[c + 1] < bs[c]) return ORC_ERR_ARG;
+  }
+  const int G = h / g;
+  const double dscale = (double)scale;
+  const long rows = (long)b * h;
+  int failed = 0;
+  const int nthreads = threads > 0 ? threads : omp_get_max_threads();
+
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads) reduction(| : failed)
+  for (long r = 0; r < rows; ++r) {
+    const int s = (int)(r / h);
+    const int i = (int)(r % h);
+    const int j = i / G;
+    const int32_t* bs = bounds + (size_t)s * (n_chunks + 1);
+    double* o = out + (size_t)r * d_v;
+    for (int v = 0; v < d_v; ++v) o[v] = 0.0;
+    if (lens[s] == 0) continue;
+    double* cm = (double*)malloc(sizeof(double) * (size_t)n_chunks);
+    double* cl = (double*)malloc(sizeof(double) * (size_t)n_chunks);
+    double* co = (double*)malloc(sizeof(double) * (size_t)n_chunks * d_v);
+    if (!cm || !cl || !co) {
+      free(cm);
+      free(cl);
+      free(co);
+      failed = 1;
+      continue;
+    }
+    const size_t qoff = (size_t)r * d_k;
+    const size_t kvhead = (size_t)s * g + j;
+    /* each chunk on its own */
+    for (int c = 0; c < n_chunks; ++c) {
+      double* oc = co + (size_t)c * d_v;
+      for (int v = 0; v < d_v; ++v) oc[v] = 0.0;
+      cl[c] = 0.0;
+      cm[c] = 0.0;
+      const int t0 = bs[c], t1 = bs[c + 1];
+      if (t1 == t0) continue;
+      double* logit = (double*)malloc(sizeof(double) * (size_t)(t1 - t0));
+      if (!logit) {
+        failed = 1;
+        continue;
+      }
+      for (int t = t0; t < t1; ++t) {
+        const size_t krow = (kvhead * cap + t) * d_k;
+        double acc = 0.0;
+        for (int k = 0; k < d_k; ++k) acc += widen(q, qoff + k, dtype) * widen(k_cache, krow + k, dtype);
+        logit[t - t0] = dscale * acc;
+      }
+      double mx = logit[0];
+      for (int t = 1; t < t1 - t0; ++t)
+        if (logit[t] > mx) mx = logit[t];
+      cm[c] = mx;
+      for (int t = t0; t < t1; ++t) {
+        const double e = exp(logit[t - t0] - mx);
+        cl[c] += e;
+        const size_t vrow = (kvhead * cap + t) * d_v;
+        for (int v = 0; v < d_v; ++v) oc[v] += e * widen(v_cache, vrow + v, dtype);
+      }
+      free(logit);
+    }
+    /* combine the chunks' states */
+    double M = 0.0;
+    int any = 0;
+    for (int c = 0; c < n_chunks; ++c)
+      if (bs[c + 1] > bs[c] && (!any || cm[c] > M)) {
+        M = cm[c];
+        any = 1;
+      }
+    double den = 0.0;
+    for (int c = 0; c < n_chunks; ++c) {
+      if (bs[c + 1] == bs[c]) continue;
+      const double wgt = exp(cm[c] - M);
+      den += wgt * cl[c];
+      for (int v = 0; v < d_v; ++v) o[v] += wgt * co[(size_t)c * d_v + v];
+    }
+    for (int v = 0; v < d_v; ++v) o[v] /= den;
+    free(cm);
+    free(cl);
+    free(co);
+  }
+  return failed ? ORC_ERR_ARG : ORC_OK;
+}
+
+/*
  * A projection of the new token's vector by a weight matrix
  * [MQA-review §2.4: q = x P_q, k = x P_k, v = x P_v for the incremental step,
  * and y = o P_o after the attention; §3: P_k and P_v lose the head axis for
@@ -248,28 +357,6 @@ int oracle_linear(double* y, const void* x, const void* w, int rows, int n_in, i
 }
 
 /*
- * Store doubles in an element type: fp32 by the C conversion (round to
- * nearest even), bf16 as the upper 16 bits of that fp32 value rounded to
- * nearest even (a NaN stays a NaN). Used where a value the step produces is
- * held in the activation type before the next operation reads it.
- */
-void oracle_store(void* dst, const double* src, size_t n, int dtype) {
-  for (size_t i = 0; i < n; ++i) {
-    const float f = (float)src[i];
-    if (dtype == ORC_F32) {
-      ((float*)dst)[i] = f;
-      continue;
-    }
-    uint32_t u;
-    memcpy(&u, &f, sizeof u);
-    uint16_t h;
-    if ((u & 0x7fffffffu) > 0x7f800000u) h = (uint16_t)((u >> 16) | 0x40u);
-    else h = (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
-    ((uint16_t*)dst)[i] = h;
-  }
-}
-
-/*
  * A double rounded once to bf16 (8 significant bits, fp32's exponent range,
  * subnormals down to 2^-133), nearest even; returned as the bf16 bit pattern.
  * The value is scaled by a power of two so that its last kept bit is the
@@ -292,6 +379,19 @@ static uint16_t double_to_bf16(double x) {
   uint32_t u;
   memcpy(&u, &f, sizeof u);
   return (uint16_t)(sign | (u >> 16));
+}
+
+/*
+ * Store doubles in an element type, each rounded once to the nearest value of
+ * that type (ties to even; a NaN stays a NaN): fp32 by the C conversion,
+ * bf16 by double_to_bf16. Used where a value the step produces is held in
+ * the activation type before the next operation reads it.
+ */
+void oracle_store(void* dst, const double* src, size_t n, int dtype) {
+  for (size_t i = 0; i < n; ++i) {
+    if (dtype == ORC_F32) ((float*)dst)[i] = (float)src[i];
+    else ((uint16_t*)dst)[i] = double_to_bf16(src[i]);
+  }
 }
 
 /*

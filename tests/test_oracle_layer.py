@@ -17,6 +17,7 @@ import pytest
 import torch
 
 import oracle
+from exact_round import round_bf16_exact
 from gqa_kv_cache_decode_amd import inputs
 
 
@@ -84,28 +85,39 @@ def test_linear_closed_forms():
     assert np.array_equal(oracle.linear(np.ascontiguousarray(x[2:3]), w)[0], y[2])
 
 
-def test_store_rounds_like_torch_bfloat16():
+def test_store_rounds_once_to_nearest():
+    # the activation hold is one rounding of the fp64 value to the nearest
+    # bf16 (ties to even), checked against exact rational rounding on values
+    # with more significant bits than fp32 holds
     rng = np.random.default_rng(5)
+    mant = 1.0 + rng.integers(0, 2 ** 40, 1500) * 2.0 ** -40
     vals = np.concatenate([
-        rng.standard_normal(2000) * 10.0 ** rng.integers(-30, 30, 2000),
-        [0.0, -0.0, 1.0, -2.0, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, np.inf, -np.inf, 3.4e38, 1e-40],
+        rng.standard_normal(1500) * 10.0 ** rng.integers(-30, 30, 1500),
+        mant * np.where(rng.random(1500) < 0.5, -1.0, 1.0) * 2.0 ** rng.integers(-120, 120, 1500),
+        [0.0, -0.0, 1.0, -2.0, 1e-40, -3e-39],
     ])
     got = oracle.store(vals, np.uint16)
-    want = torch.from_numpy(vals.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    want = np.array([round_bf16_exact(v) for v in vals], dtype=np.uint16)
+    # a negative value that rounds to zero keeps its sign
     assert np.array_equal(got, want)
-    # ties go to the even neighbour
-    assert got[-6] == 0x3F80 and got[-5] == 0x3F82
+    # just above a tie that fp32 cannot hold: rounding through fp32 first would
+    # land on the tie and go to even (0x3F80); one rounding goes up
+    assert oracle.store(np.array([1 + 2.0 ** -8 + 2.0 ** -30]), np.uint16)[0] == 0x3F81
+    assert oracle.store(np.array([1 + 2.0 ** -8]), np.uint16)[0] == 0x3F80      # exact tie: to even
+    assert oracle.store(np.array([1 + 3 * 2.0 ** -8]), np.uint16)[0] == 0x3F82  # exact tie: to even
+    assert oracle.store(np.array([np.inf, -np.inf, 3.4e38]), np.uint16).tolist() == [0x7F80, 0xFF80, 0x7F80]
     nan = oracle.store(np.array([np.nan]), np.uint16)[0]
     assert (nan & 0x7F80) == 0x7F80 and (nan & 0x7F) != 0
+    # fp32: numpy's conversion of a double is one correctly rounded step
     f32 = oracle.store(vals, np.float32)
     assert np.array_equal(f32, vals.astype(np.float32))
 
 
 def _layer_by_einsum(x, P_q, P_k, P_v, P_o, k_cache, v_cache, lens, scale):
-    """The layer step restated from the pages' einsum forms, in float64 with torch's bf16 holds."""
+    """The layer step restated from the pages' einsum forms, in float64, each hold one exact rounding to bf16."""
     def hold(a):
-        return _f64(torch.from_numpy(np.asarray(a, dtype=np.float32)).to(torch.bfloat16)
-                    .view(torch.int16).numpy().view(np.uint16))
+        a = np.asarray(a, dtype=np.float64)
+        return _f64(np.array([round_bf16_exact(v) for v in a.ravel()], dtype=np.uint16).reshape(a.shape))
     x = _f64(x)
     q = hold(np.einsum("bm,imc->bic", x, _f64(P_q)))
     k = hold(np.einsum("bm,jmc->bjc", x, _f64(P_k)))
