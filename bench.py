@@ -49,12 +49,22 @@ With --graph the timed steps are captured in one HIP graph and replayed, which
 removes the host's per-call cost (it matters for the small, launch-bound
 workloads).
 
+After the timed region the same number of steps runs again with an event
+between consecutive steps: their p10 / p50 / p90 go into the line
+("per_step_us"). roofline.traffic is the HBM traffic over algorithmic bytes
+measured by the committed counter summary (both on one set of lengths, and
+only while the decode sources match its stamp) times this line's bytes.
+
+With --gscale the line is the long-context comparison across KV-head counts
+(g = 32 / 8 / 1 on one seed): bytes and time per step, and the time ratio.
+
 With --flushed R, R more steps are timed one at a time after the timed region,
 each after a 1 GiB fill that evicts every cache level: the line gains their
-p10 / p50 / p90 latency ("flushed"). --cpu-threads T sets the oracle's threads.
+p10 / p50 / p90 latency ("flushed"). The CPU baseline times the fp64 oracle on
+every host core the process may use and on one core (--cpu-threads T: T threads).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--paged B] [--tokens N]
-                       [--graph] [--layer | --fold G] [--flushed R] [--cpu-threads T]
+                       [--graph] [--layer | --fold G | --gscale] [--flushed R] [--cpu-threads T]
 """
 from __future__ import annotations
 
@@ -81,20 +91,30 @@ def log(*a):
 
 
 def traffic_from_profile(workload: str):
-    """HBM bytes per decode launch from the committed counter summary, if it matches this source."""
+    """HBM traffic over algorithmic bytes of the decode launch, from the committed counter summary.
+
+    The ratio (both measured in one counter run, on one set of lengths) if the
+    summary's source stamp matches the current decode sources, else None.
+    """
     from gqa_kv_cache_decode_amd import rocprof_summary
 
-    rec = rocprof_summary.read_traffic(os.path.join(PROFILE_DIR, f"decode_traffic_{workload}.txt"))
+    path = os.path.join(PROFILE_DIR, f"decode_traffic_{workload}.txt")
+    rec = rocprof_summary.read_traffic(path)
     if not rec or rec.get("kernel_source_hash") != rocprof_summary.kernel_source_hash():
         return None
-    return int(float(rec["hbm_bytes_per_launch"]))
+    return float(rec["hbm_bytes_per_launch"]) / float(rec["algorithmic_bytes_per_launch"]), os.path.relpath(path, ROOT)
 
 
 def cpu_baseline(wl, batch_host, budget_s: float, threads: int = 0):
-    """Time the fp64 oracle (as it stands) on one full step of one cache set (threads 0: up to 16 cores)."""
+    """Time the fp64 oracle (as it stands) on full decode steps of one cache set.
+
+    Half the budget with every host core this process may run on (or the
+    given thread count), half on one core; the same algorithmic bytes as the
+    GPU line.
+    """
     import oracle
 
-    threads = threads or max(1, min(16, len(os.sched_getaffinity(0))))
+    threads = threads or len(os.sched_getaffinity(0))
     kc = batch_host.k_cache.copy()
     vc = batch_host.v_cache.copy()
     lens = batch_host.lens.copy()
@@ -102,17 +122,25 @@ def cpu_baseline(wl, batch_host, budget_s: float, threads: int = 0):
     kn, vn = batch_host.new_kv(0)
     oracle.kv_append(kc, vc, kn, vn, lens)
     kv_bytes = int(lens.sum()) * wl.g * 2 * wl.d * wl.elem_bytes
-    reps, t0 = 0, time.perf_counter()
-    while True:
-        oracle.decode_attention(q, kc, vc, lens, wl.scale, threads=threads)
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s or reps >= 1000:
-            break
+
+    def timed(nthreads, seconds):
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            oracle.decode_attention(q, kc, vc, lens, wl.scale, threads=nthreads)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= seconds or reps >= 1000:
+                return reps, el
+
+    reps, el = timed(threads, budget_s / 2)
+    reps1, el1 = timed(1, budget_s / 2)
     return {"value": round(kv_bytes * reps / el / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
             "sample": f"{reps} repetition(s) of one full decode step (b={wl.b}, all sequences, "
-                      f"sum L={int(lens.sum())}) of cache set 0, fp64 oracle with {threads} OpenMP threads",
-            "seconds": round(el, 3)}
+                      f"sum L={int(lens.sum())}) of cache set 0, fp64 oracle on {threads} OpenMP threads "
+                      f"(all host cores available to the process); then {reps1} on one thread",
+            "seconds": round(el, 3),
+            "one_core": {"value": round(kv_bytes * reps1 / el1 / 1e9, 4), "unit": "GB/s", "cores": 1,
+                         "seconds": round(el1, 3)}}
 
 
 def main():
@@ -124,8 +152,12 @@ def main():
     ap.add_argument("--sets", type=int, default=0, help="cache sets to cycle (0: enough for >= 1.5 GB)")
     ap.add_argument("--path", type=int, default=0, help="0 auto, 1 vector, 2 matrix")
     ap.add_argument("--workgroups", type=int, default=0, help="persistent grid size (0: automatic)")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle time budget (0: skip)")
-    ap.add_argument("--cpu-threads", type=int, default=0, help="oracle threads (0: the cores, at most 16)")
+    ap.add_argument("--cpu-seconds", type=float, default=16.0,
+                    help="oracle time budget, half on all cores, half on one (0: skip)")
+    ap.add_argument("--cpu-threads", type=int, default=0, help="oracle threads (0: every core the process may use)")
+    ap.add_argument("--gscale", action="store_true",
+                    help="the long-context MHA comparison: g = 32, 8, 1 KV heads on the same seed (h = 32, "
+                         "b = 4, L = 32769), bytes and time per step and the time ratio")
     ap.add_argument("--flushed", type=int, default=0, metavar="R",
                     help="after the timed steps, time R more steps one at a time, each after a 1 GiB fill "
                          "(outside the events) that evicts the caches; adds p10/p50/p90 to the line")
@@ -160,7 +192,7 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
-    total_steps = args.warmup + args.steps + args.flushed
+    total_steps = args.warmup + 2 * args.steps + args.flushed
     if args.layer:
         if wl.dtype != "bf16" or args.unfused:
             print("--layer runs bf16 workloads with the fused step only", file=sys.stderr)
@@ -168,6 +200,8 @@ def main():
         return bench_layer(args, wl, dev)
     if args.fold:
         return bench_fold(args, WORKLOADS[args.workload or "mha_long_bf16_g32"], dev)
+    if args.gscale:
+        return bench_gscale(args, dev)
 
     # cache sets
     set_bytes = wl.b * wl.g * wl.cap * wl.d * 2 * wl.elem_bytes
@@ -331,6 +365,22 @@ def main():
 
     value = total_bytes / (elapsed_ms / 1e3) / 1e9
     achieved = bytes_per_launch / (kern_avg_ms / 1e3) / 1e9
+    # The same number of steps again, with an event between consecutive steps
+    # (outside the timed region above): the spread of single steps.
+    per_step = None
+    if not args.graph and args.steps >= 5:
+        marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+        torch.cuda.synchronize()
+        marks[0].record(stream)
+        for k in range(args.steps):
+            step(args.warmup + args.steps + k, None)
+            marks[k + 1].record(stream)
+        torch.cuda.synchronize()
+        d = np.array([marks[k].elapsed_time(marks[k + 1]) * 1e3 for k in range(args.steps)])
+        per_step = {"p10_us": round(float(np.percentile(d, 10)), 2), "p50_us": round(float(np.median(d)), 2),
+                    "p90_us": round(float(np.percentile(d, 90)), 2), "steps": args.steps,
+                    "what": "a second pass of as many steps, one event between consecutive steps"}
+        log(f"per step: p10 / p50 / p90 {per_step['p10_us']} / {per_step['p50_us']} / {per_step['p90_us']} us")
     flushed = None
     if args.flushed > 0 and not args.graph:
         # one step at a time, each after a 1 GiB fill outside its events (every
@@ -340,7 +390,7 @@ def main():
         for k in range(args.flushed):
             fill.fill_(k & 255)
             ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-            step(args.warmup + args.steps + k, ev)
+            step(args.warmup + 2 * args.steps + k, ev)
             ev[1].synchronize()
             lat.append(ev[0].elapsed_time(ev[1]) * 1e3)
         del fill
@@ -350,9 +400,11 @@ def main():
                            + ", each step after a 1 GiB fill"}
         log(f"flushed steps: p10 / p50 / p90 {flushed['p10_us']} / {flushed['p50_us']} / {flushed['p90_us']} us")
     # a multi-token call is planned as a one-token call with N * h heads
-    plan_path, plan_wgs, plan_merge = api.plan(wl.b, wl.h * ntok, wl.g, wl.d, wl.d, cap, max_len_bound, dt,
-                                               api.PATH_AUTO if ntok > 1 else args.path, args.workgroups)
-    traffic = None if (args.paged or ntok > 1) else traffic_from_profile(wl.name)
+    plan_path, plan_wgs, plan_merge, plan_stream = api.plan(wl.b, wl.h * ntok, wl.g, wl.d, wl.d, cap, max_len_bound,
+                                                            dt, api.PATH_AUTO if ntok > 1 else args.path,
+                                                            args.workgroups, stream_flag=True)
+    plan_stream = plan_stream and ntok == 1
+    traffic = None if (args.paged or ntok > 1 or args.unfused) else traffic_from_profile(wl.name)
 
     cpu = None
     if args.cpu_seconds > 0 and ntok == 1:
@@ -396,8 +448,12 @@ def main():
         },
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-            "kernel": ("decode_matrix_kernel" if plan_path == 2 else "decode_vector_kernel")
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None if traffic is None else int(round(traffic[0] * bytes_per_launch)),
+            "traffic_ratio": None if traffic is None else round(traffic[0], 4),
+            "traffic_source": None if traffic is None else traffic[1],
+            "kernel": ("decode_stream_kernel" if plan_stream else
+                       "decode_matrix_kernel" if plan_path == 2 else "decode_vector_kernel")
                       + (" + merge_partials_kernel" if plan_merge == api.MERGE_KERNEL else "")
                       + ("" if args.unfused else " (fused step)" if ntok == 1 else
                          f" (causal, {ntok} tokens) + kv_append_kernel") + (", paged" if args.paged else ""),
@@ -405,6 +461,8 @@ def main():
         },
         "cpu_baseline": cpu,
     }
+    if per_step is not None:
+        rec["per_step_us"] = per_step
     if flushed is not None:
         rec["flushed"] = flushed
     print(json.dumps(rec), flush=True)
@@ -514,6 +572,84 @@ def bench_layer(args, wl, dev):
             "kernel_avg_us": round(step_ms * 1e3, 3),
         },
         "cpu_baseline": None,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+def bench_gscale(args, dev):
+    """The long-context comparison across KV-head counts: g = 32 (MHA), 8 and 1 (MQA) on one seed.
+
+    h = 32 query heads, b = 4, 32,768 cached positions plus the appended one,
+    bf16. Each g runs the fused step on two cache sets in rotation (each set
+    larger than the last-level cache): bytes read per step scale with g (the
+    TF2 GQA lesson's cache-size rule), and the time ratio g = 32 : g = 1 is
+    reported beside the review's "about 12x faster decoding" for MQA, which
+    is a whole-decoder figure on unstated hardware (context, not a target).
+    """
+    import torch
+
+    from gqa_kv_cache_decode_amd import api, inputs
+    from gqa_kv_cache_decode_amd.workloads import WORKLOADS, kv_bytes_attended
+
+    steps, warmup = max(args.steps, 5), args.warmup
+    res = {}
+    for g in (32, 8, 1):
+        wl = WORKLOADS[f"mha_long_bf16_g{g}"]
+        grow = warmup + steps + 2
+        cap = wl.cap + grow
+        sets = []
+        for r in range(2):
+            bt = inputs.Batch(seed=wl.seed + 1000 * r, b=wl.b, h=wl.h, g=wl.g, d=wl.d, cap=cap, lens=wl.lens,
+                              dtype=wl.dtype, poison=False)
+            to = lambda a: torch.from_numpy(a).view(torch.bfloat16).to(dev)
+            sets.append({"kc": to(bt.k_cache), "vc": to(bt.v_cache), "lens": torch.from_numpy(bt.lens.copy()).to(dev),
+                         "lens_h": bt.lens.copy()})
+            del bt
+        q = torch.from_numpy(inputs.draw_q(wl.seed, 0, wl.b, wl.h, wl.d, wl.dtype)).view(torch.bfloat16).to(dev)
+        kn, vn = [torch.from_numpy(a).view(torch.bfloat16).to(dev)
+                  for a in inputs.draw_new_kv(wl.seed, 0, wl.b, wl.g, wl.d, wl.d, wl.dtype)]
+        out = torch.empty(wl.b, wl.h, wl.d, dtype=torch.bfloat16, device=dev)
+        ws = api.make_workspace(wl.b, wl.h, wl.g, wl.d, wl.d, cap, torch.bfloat16, dev)
+        stream = torch.cuda.current_stream()
+
+        def step(i):
+            st = sets[i % 2]
+            api.decode_step(out, q, kn, vn, st["kc"], st["vc"], st["lens"], int(st["lens_h"].max()), wl.scale, ws)
+            st["lens_h"] += 1
+            return kv_bytes_attended(wl.g, wl.d, wl.d, wl.elem_bytes, st["lens_h"])
+
+        for i in range(warmup):
+            step(i)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        total = 0
+        e0.record(stream)
+        for k in range(steps):
+            total += step(warmup + k)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / steps
+        plan_path, wgs, merge = api.plan(wl.b, wl.h, wl.g, wl.d, wl.d, cap, int(sets[0]["lens_h"].max()),
+                                         torch.bfloat16)
+        res[g] = {"kv_bytes_per_step": int(total / steps), "us_per_step": round(us, 2),
+                  "tb_per_s": round(total / steps / (us * 1e-6) / 1e12, 3),
+                  "path": {1: "vector", 2: "matrix"}[plan_path], "workgroups": wgs,
+                  "split_merge": "second launch" if merge == api.MERGE_KERNEL else "in the decode kernel"}
+        log(f"g={g}: {us:.1f} us per step, {res[g]['tb_per_s']} TB/s")
+        del sets, ws
+        torch.cuda.empty_cache()
+    ratio = res[32]["us_per_step"] / res[1]["us_per_step"]
+    rec = {
+        "metric": "decode-step time across KV-head counts at the same shape (g = 32 / 8 / 1)",
+        "value": round(ratio, 2), "unit": "x (time g=32 / time g=1)", "n_gpus": 1, "steps": steps,
+        "warmup": warmup, "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "mha_long_bf16_g32_g8_g1", "b": 4, "h": 32, "d_k": 128, "d_v": 128,
+                   "attended_len": 32769, "seed": 1005, "step_api": "gqa_decode_step"},
+        "per_g": {str(g): r for g, r in res.items()},
+        "bytes_ratio_g32_over_g1": round(res[32]["kv_bytes_per_step"] / res[1]["kv_bytes_per_step"], 2),
+        "pages_claim": "about 12x faster decoding with multi-query attention than multi-head (Fast Transformer "
+                       "Decoding review, 4.2 Speed): a whole decoder on hardware the pages do not state; context only",
     }
     print(json.dumps(rec), flush=True)
 

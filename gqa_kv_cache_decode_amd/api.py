@@ -79,10 +79,12 @@ def make_workspace(b: int, h: int, g: int, d_k: int, d_v: int, max_len: int, dty
     return torch.zeros(workspace_size(b, h, g, d_k, d_v, max_len, dtype), dtype=torch.uint8, device=device)
 
 
-def plan(b, h, g, d_k, d_v, cap, max_len, dtype: torch.dtype, path=PATH_AUTO, workgroups=0):
+def plan(b, h, g, d_k, d_v, cap, max_len, dtype: torch.dtype, path=PATH_AUTO, workgroups=0, stream_flag=False):
     """(path, workgroups, merge) the library would launch with on the current device; no GPU work.
 
-    path is PATH_VECTOR or PATH_MATRIX; merge is MERGE_INLINE or MERGE_KERNEL.
+    path is PATH_VECTOR or PATH_MATRIX; merge is MERGE_INLINE or MERGE_KERNEL. With
+    stream_flag, a fourth value says whether the matrix path runs its one-block
+    streaming kernel.
     """
     lib = _lib.load()
     p, c = ctypes.c_int(0), ctypes.c_int(0)
@@ -90,7 +92,10 @@ def plan(b, h, g, d_k, d_v, cap, max_len, dtype: torch.dtype, path=PATH_AUTO, wo
                              ctypes.byref(p), ctypes.byref(c))
     _lib.check(rc, "gqa_decode_plan")
     merge = p.value & (MERGE_INLINE | MERGE_KERNEL)
-    return p.value & ~(MERGE_INLINE | MERGE_KERNEL), c.value, merge
+    chosen = p.value & ~(MERGE_INLINE | MERGE_KERNEL | _lib.PLAN_STREAM)
+    if stream_flag:
+        return chosen, c.value, merge, bool(p.value & _lib.PLAN_STREAM)
+    return chosen, c.value, merge
 
 
 def decode_attention(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,

@@ -171,15 +171,12 @@ __device__ __forceinline__ void tile_state(f32x4 (&o)[8], float& m, float& l, co
 #undef GQA_PV
 }
 
-// The schedule in tiles. Segments (s, j) are ordered by s, then j; segment
-// (s, j) is preceded by `lead` empty tiles (the cost of opening a piece, so
-// that a range starting just before a segment skips them). With T tiles in
-// all (empty ones included) and P' = min(P, T) workgroups taking part,
-// workgroup p takes [floor(p T / P'), floor((p + 1) T / P')).
-struct Range {
-  long long total, u, u_end, seq_base;
-  int s, parts;
-};
+// The schedule (schedule.hpp) in single tiles: segments (s, j) ordered by s,
+// then j, segment (s, j) preceded by `lead` empty tiles (the cost of
+// opening a piece, so that a range starting just before a segment skips
+// them), workgroup p < P' taking tiles [floor(p T / P'), floor((p + 1) T / P')).
+using Range = sched::Cursor;
+using StreamPiece = sched::Piece;
 
 // Wave-uniform values computed through lane shuffles, made visibly uniform
 // (scalar registers) for the compiler.
@@ -190,75 +187,30 @@ __device__ __forceinline__ long long uni(long long x) {
   return (long long)(((unsigned long long)hi << 32) | lo);
 }
 
-__device__ __forceinline__ long long seg_tiles(int L, int lead) {
-  const int nt = tiles_of(L);
-  return nt > 0 ? nt + lead : 0;
-}
-
 // Every lane of the wave: the workgroup's range from the lengths (lane s
-// holds L_s; b <= 64).
+// holds L_s; b <= 64); the sums of sched::locate_serial as a wave scan.
 __device__ Range locate(const DecodeParams& p, int Lreg, int wg) {
   const int lane = threadIdx.x & 63;
-  const long long v = lane < p.b ? (long long)p.g * seg_tiles(Lreg, p.seg_lead) : 0;
+  const long long v = lane < p.b ? (long long)p.g * sched::seg_units<1>(Lreg, p.seg_lead) : 0;
   const long long incl = wave_inclusive_scan(v);
   Range r;
   r.total = uni(__shfl(incl, 63, 64));
   r.parts = r.total < p.workgroups ? int(r.total) : p.workgroups;
   const bool takes_part = wg < r.parts;
   const int parts_nz = r.parts > 0 ? r.parts : 1;
-  r.u = takes_part ? range_begin(wg, r.total, parts_nz) : 0;
-  r.u_end = takes_part ? range_begin(wg + 1, r.total, parts_nz) : 0;
+  r.u = uni(takes_part ? sched::range_begin(wg, r.total, parts_nz) : 0);
+  r.u_end = uni(takes_part ? sched::range_begin(wg + 1, r.total, parts_nz) : 0);
   const long long excl = incl - v;
   const unsigned long long hit = __ballot(lane < p.b && v > 0 && excl <= r.u && r.u < incl);
   const int src = hit ? __ffsll((long long)hit) - 1 : 0;
   r.s = uni(hit ? src : p.b);
   r.seq_base = uni(hit ? __shfl(excl, src, 64) : r.total);
-  r.u = uni(r.u);
-  r.u_end = uni(r.u_end);
   return r;
 }
 
-struct StreamPiece {
-  int s, grp, L;
-  int tb, te;  // real tiles [tb, te) of the segment
-  int p0, p1;  // first and last workgroups whose ranges hold real tiles of the segment
-};
-
 // Next piece of the range (lengths from the lane registers via shuffles).
-__device__ bool next_piece(const DecodeParams& p, Range& r, int Lreg, StreamPiece& pc) {
-  const int lead = p.seg_lead;
-  while (r.u < r.u_end) {
-    int L = uni(__shfl(Lreg, r.s, 64));
-    long long seq = (long long)p.g * seg_tiles(L, lead);
-    while (r.u >= r.seq_base + seq && r.s + 1 < p.b) {
-      r.seq_base += seq;
-      ++r.s;
-      L = uni(__shfl(Lreg, r.s, 64));
-      seq = (long long)p.g * seg_tiles(L, lead);
-    }
-    const int nt = tiles_of(L);
-    const int sl = nt + lead;
-    const long long within = r.u - r.seq_base;
-    const int grp = int(within / sl);
-    const int ub = int(within - (long long)grp * sl);
-    const long long remain = r.u_end - r.u;
-    const long long seg_left = sl - ub;
-    const int ue = ub + int(remain < seg_left ? remain : seg_left);
-    r.u += ue - ub;
-    const int rb = (ub > lead ? ub : lead) - lead;
-    const int re = ue - lead;
-    if (re <= rb) continue;  // only the segment's empty lead tiles
-    pc.s = r.s;
-    pc.grp = grp;
-    pc.L = L;
-    pc.tb = rb;
-    pc.te = re;
-    const long long seg_u0 = r.seq_base + (long long)grp * sl + lead;
-    pc.p0 = owner_of(seg_u0, r.total, r.parts);
-    pc.p1 = owner_of(seg_u0 + nt - 1, r.total, r.parts);
-    return true;
-  }
-  return false;
+__device__ __forceinline__ bool next_piece(const DecodeParams& p, Range& r, int Lreg, StreamPiece& pc) {
+  return sched::next_piece<1>([Lreg](int s) { return uni(__shfl(Lreg, s, 64)); }, p.b, p.g, p.seg_lead, r, pc);
 }
 
 // Byte offset of partial slot `slot` of workgroup `wg`.
@@ -443,7 +395,7 @@ __device__ void fold_range(const DecodeParams& p, const Range& range, int Lreg, 
   StreamPiece pc;
   int k = 0;  // next range tile to fold
   while (next_piece(p, it, Lreg, pc)) {
-    const int n = pc.te - pc.tb;
+    const int n = pc.tile_end - pc.tile_begin;
     const int s = pc.s, j = pc.grp;
     const bool shared = pc.p0 != pc.p1;
     const bool inline_merge = shared && !p.merge_kernel;
@@ -493,7 +445,7 @@ __device__ void fold_range(const DecodeParams& p, const Range& range, int Lreg, 
 #pragma unroll
         for (int i = 0; i < NCH; ++i) *reinterpret_cast<uint2*>(out + 4 * (sub + HP * i)) = to_bf16x4(acc[i] * inv);
       }
-      if (p.merge_kernel && pc.tb == 0 && lane == 0) p.seg_info[size_t(s) * p.ngroups + j] = make_int2(pc.p0, -1);
+      if (p.merge_kernel && pc.tile_begin == 0 && lane == 0) p.seg_info[size_t(s) * p.ngroups + j] = make_int2(pc.p0, -1);
       continue;
     }
     int t = n_slots - 1;  // every other part counted in at the peek
@@ -528,7 +480,7 @@ __device__ void fold_range(const DecodeParams& p, const Range& range, int Lreg, 
       }
     }
     if (p.merge_kernel) {
-      if (pc.tb == 0 && lane == 0) p.seg_info[size_t(s) * p.ngroups + j] = make_int2(pc.p0, pc.p1);
+      if (pc.tile_begin == 0 && lane == 0) p.seg_info[size_t(s) * p.ngroups + j] = make_int2(pc.p0, pc.p1);
     } else {
       wait_stores();
       if (lane == 0) __hip_atomic_store(slot_flag(p, wg, my_slot), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -581,14 +533,14 @@ __global__ __launch_bounds__(kBlockThreads, 1) void decode_stream_kernel(DecodeP
       int k = 0;
       if (lane == 0) k = __hip_atomic_fetch_add(&s_next, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
       k = __builtin_amdgcn_readfirstlane(k);
-      while (have && k >= kb + (pc.te - pc.tb)) {
-        kb += pc.te - pc.tb;
+      while (have && k >= kb + (pc.tile_end - pc.tile_begin)) {
+        kb += pc.tile_end - pc.tile_begin;
         have = next_piece(p, it, Lreg, pc);
       }
       if (!have) break;
       const int s = pc.s, j = pc.grp;
       const size_t kv_head = size_t(s) * p.g + j;
-      const int tile = pc.tb + int(k - kb);
+      const int tile = pc.tile_begin + int(k - kb);
       const int t0 = tile * kTile;
       const int nvalid = pc.L - t0;
       if (FUSED && nvalid <= kTile) {

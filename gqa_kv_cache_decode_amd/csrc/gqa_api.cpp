@@ -240,7 +240,9 @@ int gqa_decode_plan(int b, int h, int g, int d_k, int d_v, int cap, int max_len,
   Plan plan;
   const int rc = plan_decode(b, h, g, d_k, d_v, cap, max_len, dtype, path, workgroups, &plan);
   if (rc != GQA_OK) return rc;
-  if (chosen_path) *chosen_path = plan.path | (plan.merge_kernel ? GQA_MERGE_KERNEL : GQA_MERGE_INLINE);
+  if (chosen_path)
+    *chosen_path = plan.path | (plan.merge_kernel ? GQA_MERGE_KERNEL : GQA_MERGE_INLINE) |
+                   (plan.stream ? GQA_PLAN_STREAM : 0);
   if (chosen_workgroups) *chosen_workgroups = plan.workgroups;
   return ok();
 }

@@ -55,6 +55,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "schedule.hpp"
+
 namespace gqa {
 
 constexpr int kThreads = 256;  // workgroup size of the merge kernel (and of the 4-wave decode instances)
@@ -349,14 +351,15 @@ __device__ __forceinline__ int attended_len(const DecodeParams& p, int s) {
   return (L > hi ? hi : L) + p.fused;
 }
 
-__device__ __forceinline__ int tiles_of(int L) { return (L + kTile - 1) / kTile; }
-// Schedule units of a segment of length L. A unit is kUnitTiles tiles, one
-// for each wave of a 4-wave workgroup, so that a piece made of whole units
-// gives each of those waves the same number of tiles (only a segment's last
-// unit can be short). The 8-wave matrix workgroups keep 4-tile units: 8-tile
-// units, which would balance their waves the same way, measured slower (the
-// coarser split of the work over workgroups costs more).
-__device__ __forceinline__ int units_of(int L) { return (L + kTile * kUnitTiles - 1) / (kTile * kUnitTiles); }
+__device__ __forceinline__ int tiles_of(int L) { return sched::tiles_of(L); }
+// Schedule units of a segment of length L (schedule.hpp). A unit is
+// kUnitTiles tiles, one for each wave of a 4-wave workgroup, so that a piece
+// made of whole units gives each of those waves the same number of tiles
+// (only a segment's last unit can be short). The 8-wave matrix workgroups
+// keep 4-tile units: 8-tile units, which would balance their waves the same
+// way, measured slower (the coarser split of the work over workgroups costs
+// more).
+__device__ __forceinline__ int units_of(int L) { return sched::units_of<kUnitTiles>(L); }
 
 // Units a non-empty segment occupies in the schedule: its units_of(L) real
 // units preceded by p.seg_lead empty ones. The empty units carry no work;
@@ -366,17 +369,11 @@ __device__ __forceinline__ int units_of(int L) { return (L + kTile * kUnitTiles 
 // LEAD = false: kernels launched with seg_lead = 0 compile the plain form.
 template <bool LEAD>
 __device__ __forceinline__ int sched_units_of(const DecodeParams& p, int L) {
-  const int nu = units_of(L);
-  if constexpr (!LEAD) return nu;
-  return nu > 0 ? nu + p.seg_lead : 0;
+  return int(sched::seg_units<kUnitTiles>(L, LEAD ? p.seg_lead : 0));
 }
 
-// Workgroup owning unit u when T units are split over P workgroups as
-// [floor(p*T/P), floor((p+1)*T/P)): the largest p with floor(p*T/P) <= u.
-__device__ __forceinline__ int owner_of(long long u, long long T, int P) {
-  return int(((u + 1) * P + T - 1) / T) - 1;
-}
-__device__ __forceinline__ long long range_begin(int p, long long T, int P) { return (long long)p * T / P; }
+using sched::owner_of;
+using sched::range_begin;
 
 // Wave-level inclusive prefix sum over 64 lanes.
 __device__ __forceinline__ long long wave_inclusive_scan(long long v) {
@@ -460,108 +457,41 @@ __device__ Located locate_units(const DecodeParams& p, const LensView& lv, int w
 // (s, grp), i.e. positions [tile_begin*kTile, min(L, tile_end*kTile)).
 // tile_begin is a multiple of the unit size. p0 and p1 are the first and last
 // workgroups whose ranges touch the segment.
-struct Piece {
-  int s, grp, L;
-  int tile_begin, tile_end;
-  int p0, p1;
-};
+using Piece = sched::Piece;
 
-// Iterates the pieces of workgroup `wg`'s unit range. LEAD: segments are
-// preceded by p.seg_lead empty units.
+// Iterates the pieces of workgroup `wg`'s unit range (schedule.hpp). LEAD:
+// segments are preceded by p.seg_lead empty units.
 template <bool LEAD>
 struct PieceWalker {
   const DecodeParams* p;
   LensView lv;
-  long long total, u, u_end, seq_base;
-  int s, parts;
+  sched::Cursor c;
 
   __device__ void init(const DecodeParams& prm, int wg) {
     p = &prm;
     lv.init(prm);
     const Located loc = locate_units<LEAD>(prm, lv, wg);
-    total = loc.total;
-    parts = loc.parts;
-    s = loc.s;
-    seq_base = loc.seq_base;
+    c.total = loc.total;
+    c.parts = loc.parts;
+    c.s = loc.s;
+    c.seq_base = loc.seq_base;
     // A workgroup past the last taking part gets the empty range [0, 0).
     // Written as selects, not an early return: with two paths that each store
     // u and u_end, the compiler merges the stores through a pointer that picks
     // the field, which keeps both fields in scratch memory for the kernel's
     // whole life (a reload and a wait at every piece).
-    const bool takes_part = wg < parts;
-    const int parts_nz = parts > 0 ? parts : 1;
-    u = takes_part ? range_begin(wg, total, parts_nz) : 0;
-    u_end = takes_part ? range_begin(wg + 1, total, parts_nz) : 0;
+    const bool takes_part = wg < c.parts;
+    const int parts_nz = c.parts > 0 ? c.parts : 1;
+    c.u = takes_part ? range_begin(wg, c.total, parts_nz) : 0;
+    c.u_end = takes_part ? range_begin(wg + 1, c.total, parts_nz) : 0;
   }
 
-  __device__ bool more() const { return u < u_end; }
-
-  // next() when segments have no leading empty units.
-  __device__ bool next_packed(Piece& pc) {
-    if (u >= u_end) return false;
-    int L = lv.len(s);
-    long long seq_units = (long long)p->ngroups * units_of(L);
-    while (u >= seq_base + seq_units && s + 1 < p->b) {  // skip to the sequence holding u
-      seq_base += seq_units;
-      ++s;
-      L = lv.len(s);
-      seq_units = (long long)p->ngroups * units_of(L);
-    }
-    const int nu = units_of(L);
-    const long long within = u - seq_base;
-    pc.s = s;
-    pc.L = L;
-    pc.grp = int(within / nu);
-    const int ub = int(within - (long long)pc.grp * nu);
-    const long long remain = u_end - u;
-    const long long seg_left = nu - ub;
-    const int ue = ub + int(remain < seg_left ? remain : seg_left);
-    const int nt = tiles_of(L);
-    pc.tile_begin = ub * kUnitTiles;
-    pc.tile_end = ue * kUnitTiles < nt ? ue * kUnitTiles : nt;
-    const long long seg_u0 = seq_base + (long long)pc.grp * nu;
-    pc.p0 = owner_of(seg_u0, total, parts);
-    pc.p1 = owner_of(seg_u0 + nu - 1, total, parts);
-    u += ue - ub;
-    return true;
-  }
+  __device__ bool more() const { return c.u < c.u_end; }
 
   __device__ bool next(Piece& pc) {
-    if constexpr (!LEAD) return next_packed(pc);
-    const int lead = p->seg_lead;
-    while (u < u_end) {
-      int L = lv.len(s);
-      long long seq_units = (long long)p->ngroups * sched_units_of<true>(*p, L);
-      while (u >= seq_base + seq_units && s + 1 < p->b) {  // skip to the sequence holding u
-        seq_base += seq_units;
-        ++s;
-        L = lv.len(s);
-        seq_units = (long long)p->ngroups * sched_units_of<true>(*p, L);
-      }
-      const int nu = units_of(L);
-      const int sl = nu + lead;
-      const long long within = u - seq_base;
-      const int grp = int(within / sl);
-      const int ub = int(within - (long long)grp * sl);
-      const long long remain = u_end - u;
-      const long long seg_left = sl - ub;
-      const int ue = ub + int(remain < seg_left ? remain : seg_left);
-      u += ue - ub;
-      const int rb = (ub > lead ? ub : lead) - lead;  // real units [rb, re) of the segment
-      const int re = ue - lead;
-      if (re <= rb) continue;  // only the segment's leading empty units
-      const int nt = tiles_of(L);
-      pc.s = s;
-      pc.L = L;
-      pc.grp = grp;
-      pc.tile_begin = rb * kUnitTiles;
-      pc.tile_end = re * kUnitTiles < nt ? re * kUnitTiles : nt;
-      const long long seg_u0 = seq_base + (long long)grp * sl + lead;  // first real unit
-      pc.p0 = owner_of(seg_u0, total, parts);
-      pc.p1 = owner_of(seg_u0 + nu - 1, total, parts);
-      return true;
-    }
-    return false;
+    const LensView& lens = lv;
+    return sched::next_piece<kUnitTiles>([&lens](int s) { return lens.len(s); }, p->b, p->ngroups,
+                                         LEAD ? p->seg_lead : 0, c, pc);
   }
 };
 

@@ -31,9 +31,9 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 # The sources the decode kernels are built from; a change to any of them may
 # change the decode kernel's traffic. The projection and append-only sources
 # and the host-side entry points do not.
-DECODE_SOURCES = ("gqa_internal.hpp", "decode_matrix.hip", "decode_vector_kernel.hpp", "decode_vector.hip",
-                  "decode_vector_paged.hip", "decode_vector_multi.hip", "decode_vector_multi_paged.hip",
-                  "merge_partials.hip")
+DECODE_SOURCES = ("gqa_internal.hpp", "schedule.hpp", "decode_stream.hip", "decode_matrix.hip",
+                  "decode_vector_kernel.hpp", "decode_vector.hip", "decode_vector_paged.hip",
+                  "decode_vector_multi.hip", "decode_vector_multi_paged.hip", "merge_partials.hip")
 
 
 def _code_only(text: str) -> str:

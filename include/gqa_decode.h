@@ -82,6 +82,9 @@ extern "C" {
 /* How segments split over several workgroups are merged; OR one into path. */
 #define GQA_MERGE_INLINE 0x10 /* by the segment's last workgroup, inside the decode launch */
 #define GQA_MERGE_KERNEL 0x20 /* by a second launch, one workgroup per (segment, head)  */
+/* Reported by gqa_decode_plan only: the matrix path runs its one-block
+   streaming kernel (one query token, up to 16 heads per KV head, b <= 64). */
+#define GQA_PLAN_STREAM 0x40
 
 /*
  * Append one token per sequence ("LLM inference 05": push K, push V;
@@ -379,7 +382,8 @@ int gqa_fold_kv_heads(void* dst, const void* src, const int32_t* lens, int b, in
  * Describe the launch gqa_decode_attention_ex would make on the current
  * device, without enqueueing anything: writes the chosen path
  * (GQA_PATH_VECTOR or GQA_PATH_MATRIX, OR-ed with the GQA_MERGE_* flag in
- * effect) and persistent grid size. Same argument checks as the real call,
+ * effect and with GQA_PLAN_STREAM when the matrix path runs its one-block
+ * streaming kernel) and persistent grid size. Same argument checks as the real call,
  * minus pointers.
  */
 int gqa_decode_plan(int b, int h, int g, int d_k, int d_v, int cap, int max_len, int dtype,

@@ -159,7 +159,13 @@ def test_plan_choices(lib):
         assert rc == _lib.OK, lib.gqa_last_error()
         return p.value, c.value
     M = _lib.MERGE_INLINE | _lib.MERGE_KERNEL
-    assert plan(16, 64, 8, 128, 8256, 8193, _lib.BF16)[0] == _lib.PATH_MATRIX | _lib.MERGE_INLINE
+    # the Llama-3-70B shape: the matrix path's one-block streaming kernel, merges inside the launch
+    assert plan(16, 64, 8, 128, 8256, 8193, _lib.BF16)[0] == _lib.PATH_MATRIX | _lib.MERGE_INLINE | _lib.PLAN_STREAM
+    assert plan(64, 28, 4, 128, 2112, 2080, _lib.BF16)[0] & _lib.PLAN_STREAM  # the Qwen2.5-7B shape too
+    # past 16 heads per KV head or 64 sequences: the unit kernels
+    assert not plan(65, 64, 8, 128, 2112, 2080, _lib.BF16)[0] & _lib.PLAN_STREAM
+    assert not plan(16, 64, 2, 128, 2112, 2080, _lib.BF16)[0] & _lib.PLAN_STREAM
+    M = M | _lib.PLAN_STREAM
     # few long segments with 32 heads per KV head: merged by a second launch
     assert plan(8, 32, 1, 128, 4160, 4097, _lib.BF16)[0] == _lib.PATH_MATRIX | _lib.MERGE_KERNEL
     assert plan(4, 32, 1, 128, 32832, 32769, _lib.BF16)[0] == _lib.PATH_MATRIX | _lib.MERGE_KERNEL
