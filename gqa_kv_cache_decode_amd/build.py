@@ -2,7 +2,11 @@
 
 Every HIP source under csrc/ is compiled to an object in parallel, then the
 objects are linked into ``gqa_kv_cache_decode_amd/libgqa_decode.so``. All
-device code is built with packed-FP32 instruction selection disabled.
+device code is built with packed-FP32 instruction selection disabled, and
+with the AMDGPU atomic optimizer off: every atomic in these kernels is
+issued by a single lane, so the optimizer's wave-wide rewrite gains nothing,
+and its form waits for the atomic's result right where it is issued, which
+would stall a wave that counts in early on purpose.
 """
 from __future__ import annotations
 
@@ -22,6 +26,7 @@ ARCH = "gfx950"
 COMMON_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
     "-I", os.path.join(ROOT, "include"),
 ]
 

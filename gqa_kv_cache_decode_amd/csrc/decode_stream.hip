@@ -34,19 +34,19 @@
 //   atomics meet on one address and none waits at the end of the launch.
 //
 // Split segments (a segment whose tiles fall in the ranges of several
-// workgroups, its "parts") are merged by the part that finishes last, with
+// workgroups, its "parts") are merged by the part that counts in last, with
 // its own state still in registers. A part counts itself in on the
-// segment's ticket (agent-scope atomic) as soon as it has folded its last
-// tile; a part that does not get the last ticket stores its state in its
-// partial slot (SC1 stores, which bypass the non-coherent caches), waits for
-// them, and raises the slot's ready flag. The last part waits for the other
-// parts' flags (each of those has already counted in, so it is running and
-// only has its stores left; the wait is bounded all the same), reads their
-// states (SC1 loads), merges them in part order and writes the output rows,
-// then re-zeroes the ticket and the flags. A few tiles before its end a
-// part looks at the ticket: if every other part has counted in by then it
-// is the last without counting. Heavily split segments are instead left to
-// a second launch (merge_partials_kernel).
+// segment's ticket (agent-scope atomic) a few tiles before it has folded its
+// last one, so the round trip is hidden; a part that does not get the last
+// ticket, once its last tile is folded, stores its state in its partial slot
+// (SC1 stores, which bypass the non-coherent caches), waits for them, and
+// raises the slot's ready flag. The last part, once its own tiles are
+// folded, waits for the other parts' flags (each of those has counted in,
+// so it is running and has only its own tiles and stores left; none waits
+// for the merger, so the wait ends, and it is bounded all the same), reads
+// their states (SC1 loads), merges them in part order and writes the output
+// rows, then re-zeroes the ticket and the flags. Heavily split segments are
+// instead left to a second launch (merge_partials_kernel).
 #include <atomic>
 
 #include "gqa_internal.hpp"
@@ -65,12 +65,15 @@ constexpr int kHeads = 16;          // one MFMA column block
 constexpr int kRow = kD + 4;        // LDS row stride (floats), padded against bank conflicts
 constexpr int kRing = 16;           // tile states in the LDS ring
 constexpr int kFolder = kWaves - 1; // the folding wave; waves 0 .. kWaves - 2 stream
-constexpr int kPeekTiles = 3;       // tiles before a piece's end at which its ticket is looked at
+constexpr int kCountTiles = 3;      // tiles before a piece's end at which it counts in on its ticket
 constexpr int kFlagSpins = 1 << 22; // bound of the wait for another part's ready flag
 // Parts of a segment whose states the merge holds in registers at once, by
 // columns per lane.
 template <int NCH>
 constexpr int fast_slots() { return NCH == 8 ? 2 : (NCH == 4 ? 5 : 9); }
+// Ring slots the folding wave reads in one round, by columns per lane.
+template <int NCH>
+constexpr int fold_batch() { return NCH == 8 ? 2 : 4; }
 constexpr int kCountGroups = 16;    // first-level counters of the fused step's length update
 constexpr int kCountStride = 32;    // ints between counters (128 bytes)
 
@@ -382,6 +385,7 @@ __device__ void fold_range(const DecodeParams& p, const Range& range, int Lreg, 
                            float (*s_m)[kHeads], float (*s_l)[kHeads], int* s_ready, int* s_folded,
                            const int* s_lens) {
   constexpr int HP = (kD / 4) / NCH;
+  constexpr int R = fold_batch<NCH>();
   const int wg = blockIdx.x;
   const int lane = threadIdx.x & 63;
   const int G = p.G;
@@ -402,39 +406,66 @@ __device__ void fold_range(const DecodeParams& p, const Range& range, int Lreg, 
     const int n_slots = pc.p1 - pc.p0 + 1;
     const int own = wg - pc.p0;  // this workgroup's part of the segment
     int* ticket = p.ws_cnt + (size_t(s) * p.ngroups + j) * p.cnt_stride;
-    // a few tiles before the end, look at the ticket: if every other part
-    // has counted in by then, this one merges without counting
-    const int peek_at = n > kPeekTiles ? n - kPeekTiles : 0;
-    int peek = -1;
+    // a few tiles before the end, count in on the segment's ticket: the part
+    // that counts in last merges, the others publish at their end
+    const int count_at = n > kCountTiles ? n - kCountTiles : 0;
+    int t = 0;
     f32x4 acc[NCH];
 #pragma unroll
     for (int i = 0; i < NCH; ++i) acc[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     float am = kNegInf, al = 0.0f;
-    for (int e = 0; e < n; ++e, ++k) {
-      if (inline_merge && e == peek_at && lane == 0)
-        peek = __hip_atomic_load(ticket, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int e = 0; e < n;) {
       const int slot = k & (kRing - 1);
       while (__hip_atomic_load(&s_ready[slot], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) != k)
         __builtin_amdgcn_s_sleep(1);
+      // tile k is in; so may be the next few: take the run of them that is
+      // ready (up to R, inside the piece) with one round of LDS reads, then
+      // fold them one by one in tile order (the same arithmetic as one at a
+      // time, so the result does not depend on how they were batched)
+      int rd[R];
+#pragma unroll
+      for (int i = 1; i < R; ++i)
+        rd[i] = __hip_atomic_load(&s_ready[(k + i) & (kRing - 1)], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP);
+      int r = 1;
+#pragma unroll
+      for (int i = 1; i < R; ++i)
+        if (r == i && e + i < n && rd[i] == k + i) r = i + 1;
+      r = __builtin_amdgcn_readfirstlane(r);
+      if (inline_merge && lane == 0 && count_at >= e && count_at < e + r)
+        t = __hip_atomic_fetch_add(ticket, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if (active) {
-        const float* row = &s_o[slot][hh * kRow + 4 * sub];
-        f32x4 ot[NCH];
+        f32x4 ot[R][NCH];
+        float mt[R], lt[R];
 #pragma unroll
-        for (int i = 0; i < NCH; ++i) ot[i] = *reinterpret_cast<const f32x4*>(row + 4 * HP * i);
-        const float mt = s_m[slot][hh];
-        const float lt = s_l[slot][hh];
-        const float M = fmaxf(am, mt);
-        const float sb = (M == kNegInf) ? 0.0f : M;
-        const float a = fast_exp2(am - sb), bt = fast_exp2(mt - sb);
+        for (int i = 0; i < R; ++i) {
+          if (i < r) {
+            const int sl = (k + i) & (kRing - 1);
+            const float* row = &s_o[sl][hh * kRow + 4 * sub];
 #pragma unroll
-        for (int i = 0; i < NCH; ++i) acc[i] = acc[i] * a + ot[i] * bt;
-        al = al * a + lt * bt;
-        am = M;
+            for (int c = 0; c < NCH; ++c) ot[i][c] = *reinterpret_cast<const f32x4*>(row + 4 * HP * c);
+            mt[i] = s_m[sl][hh];
+            lt[i] = s_l[sl][hh];
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < R; ++i) {
+          if (i < r) {
+            const float M = fmaxf(am, mt[i]);
+            const float sb = (M == kNegInf) ? 0.0f : M;
+            const float a = fast_exp2(am - sb), bt = fast_exp2(mt[i] - sb);
+#pragma unroll
+            for (int c = 0; c < NCH; ++c) acc[c] = acc[c] * a + ot[i][c] * bt;
+            al = al * a + lt[i] * bt;
+            am = M;
+          }
+        }
       }
-      // every lane's reads of the slot are done before it is handed back
+      // every lane's reads of the slots are done before they are handed back
       __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
       __builtin_amdgcn_wave_barrier();
-      if (lane == 0) __hip_atomic_store(s_folded, k + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+      e += r;
+      k += r;
+      if (lane == 0) __hip_atomic_store(s_folded, k, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
       if (FUSED) cnt.step(p, s_lens);
     }
     // the piece is complete
@@ -448,12 +479,7 @@ __device__ void fold_range(const DecodeParams& p, const Range& range, int Lreg, 
       if (p.merge_kernel && pc.tile_begin == 0 && lane == 0) p.seg_info[size_t(s) * p.ngroups + j] = make_int2(pc.p0, -1);
       continue;
     }
-    int t = n_slots - 1;  // every other part counted in at the peek
-    if (!inline_merge || __builtin_amdgcn_readfirstlane(peek) != n_slots - 1) {
-      t = 0;
-      if (inline_merge && lane == 0) t = __hip_atomic_fetch_add(ticket, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      t = __builtin_amdgcn_readfirstlane(t);
-    }
+    t = __builtin_amdgcn_readfirstlane(t);
     if (inline_merge && t == n_slots - 1) {
       // the last part: merge once the others' states are in their slots, and
       // leave the ticket and their flags at zero
