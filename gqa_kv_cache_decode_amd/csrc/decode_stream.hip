@@ -1,7 +1,7 @@
-// Matrix-core decode attention for up to 16 query heads per KV head (one
-// 16-column MFMA block), bf16 K/V/q, d_k = d_v = 128, one query token per
-// sequence, at most 64 sequences: the Llama-3-70B- and Qwen2.5-7B-shaped GQA
-// steps. Same result as the other decode kernels (MQA review §2.1 per query
+// Matrix-core decode attention for up to 32 query heads per KV head (one or
+// two 16-column MFMA blocks), bf16 K/V/q, d_k = d_v = 128, one query token
+// per sequence, at most 64 sequences: the Llama-3-70B- and Qwen2.5-7B-shaped
+// GQA steps and the 32-head MQA ones. Same result as the other decode kernels (MQA review §2.1 per query
 // head over the cache of §2.4 / §3; contiguous head groups of the TF2 GQA
 // lesson); the per-tile arithmetic is the one of decode_matrix.hip (scores
 // K·Q^T and output P·V on v_mfma_f32_16x16x32_bf16, base-2 softmax).
@@ -61,26 +61,26 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kD = 128;
 constexpr int kWaves = 8;
 constexpr int kBlockThreads = kWaves * 64;
-constexpr int kHeads = 16;          // one MFMA column block
+constexpr int kBlockHeads = 16;     // query heads of one MFMA column block
 constexpr int kRow = kD + 4;        // LDS row stride (floats), padded against bank conflicts
-constexpr int kRing = 16;           // tile states in the LDS ring
+// Tile states in the LDS ring with NB column blocks of heads (NB = 1: up to
+// 16 heads per KV head, NB = 2: up to 32); either way about 135 KB of LDS.
+template <int NB>
+constexpr int ring_slots() { return NB == 1 ? 16 : 8; }
 constexpr int kFolder = kWaves - 1; // the folding wave; waves 0 .. kWaves - 2 stream
 constexpr int kCountTiles = 3;      // tiles before a piece's end at which it counts in on its ticket
 constexpr int kFlagSpins = 1 << 22; // bound of the wait for another part's ready flag
 // Parts of a segment whose states the merge holds in registers at once, by
 // columns per lane.
 template <int NCH>
-constexpr int fast_slots() { return NCH == 8 ? 2 : (NCH == 4 ? 5 : 9); }
+constexpr int fast_slots() { return NCH == 16 ? 1 : (NCH == 8 ? 2 : (NCH == 4 ? 5 : 9)); }
 // Ring slots the folding wave reads in one round, by columns per lane.
 template <int NCH>
-constexpr int fold_batch() { return NCH == 8 ? 2 : 4; }
+constexpr int fold_batch() { return NCH == 16 ? 1 : (NCH == 8 ? 2 : 4); }
 constexpr int kCountGroups = 16;    // first-level counters of the fused step's length update
 constexpr int kCountStride = 32;    // ints between counters (128 bytes)
 
 __device__ __forceinline__ u32x4 ld16(const uint16_t* ptr) { return *reinterpret_cast<const u32x4*>(ptr); }
-__device__ __forceinline__ u32x4 nt16(const uint16_t* ptr) {
-  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(ptr));
-}
 __device__ __forceinline__ void st16(uint16_t* ptr, u32x4 v) { *reinterpret_cast<u32x4*>(ptr) = v; }
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
@@ -108,68 +108,96 @@ struct Tile {
   u32x4 v[8];
 };
 
-// Issue the loads of a tile whose rows start at kb / vb (FULL: all 32 rows
-// valid, else rows < nvalid; the others read as zero).
-template <bool FULL>
+// Issue the loads of a tile whose rows start at kb / vb, rows < nvalid
+// valid. Each half tile (16 rows) of K and of V is read through a buffer
+// resource that covers exactly its valid rows: the hardware's range check
+// (on the per-lane offset plus the instruction's constant offset, which
+// stay below 4 KiB here) returns zero for the rows past them, with no
+// per-row test, and nothing past the tile's valid rows is touched. Every
+// address is one per-lane 32-bit offset plus a constant. Loads are
+// non-temporal: each K/V byte is used once.
+constexpr int kCpolStream = 2;  // NT
+constexpr int kRowBytes = kD * int(sizeof(uint16_t));
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t half_rsrc(const uint16_t* base, int half, int nvalid) {
+  const int rows = nvalid - 16 * half;
+  const int bytes = rows <= 0 ? 0 : (rows >= 16 ? 16 : rows) * kRowBytes;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base) + size_t(16 * half) * kD, 0, bytes,
+                                           kBufferWord3);
+}
+__device__ __forceinline__ u32x4 tile_ld(__amdgpu_buffer_rsrc_t r, int voff, int off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff + off, 0, kCpolStream));
+}
 __device__ __forceinline__ void load_tile(Tile& t, const uint16_t* kb, const uint16_t* vb, int nvalid, int n16,
                                           int q4) {
+  // K row 16 sg + n16 (row n16 of half sg), dims 32 ks + 8 q4 .. +7
+  const int ko = n16 * kRowBytes + q4 * 16;
 #pragma unroll
   for (int sg = 0; sg < 2; ++sg) {
-    const int row = 16 * sg + n16;
-    const uint16_t* kp = kb + size_t(row) * kD + q4 * 8;
+    const __amdgpu_buffer_rsrc_t rk = half_rsrc(kb, sg, nvalid);
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-      t.k[sg * 4 + ks] = (FULL || row < nvalid) ? nt16(kp + ks * 32) : u32x4{0u, 0u, 0u, 0u};
+    for (int ks = 0; ks < 4; ++ks) t.k[sg * 4 + ks] = tile_ld(rk, ko, ks * 64);
   }
+  // V row v_row(q4, r) = 4 q4 + r (r < 4) or 16 + 4 q4 + r - 4, dims 8 n16 .. +7
+  const int vo = 4 * q4 * kRowBytes + n16 * 16;
 #pragma unroll
-  for (int r = 0; r < 8; ++r) {
-    const int row = v_row(q4, r);
-    t.v[r] = (FULL || row < nvalid) ? nt16(vb + size_t(row) * kD + n16 * 8) : u32x4{0u, 0u, 0u, 0u};
+  for (int hf = 0; hf < 2; ++hf) {
+    const __amdgpu_buffer_rsrc_t rv = half_rsrc(vb, hf, nvalid);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) t.v[4 * hf + r] = tile_ld(rv, vo, r * kRowBytes);
   }
 }
 
-// The split-softmax state of one tile, from scratch: per head m = the
-// tile's largest scaled logit (base 2), l = sum of its weights 2^(s - m)
-// (rounded to bf16, as applied), o = their weighted sum of V rows. Lane
-// (n16, q4) holds head n16: o[e][i] = dim 32 q4 + 8 i + e; m and l are the
-// same in the head's four lanes. Rows >= nvalid are masked unless FULL.
-template <bool FULL>
-__device__ __forceinline__ void tile_state(f32x4 (&o)[8], float& m, float& l, const bf16x8 (&qop)[4],
-                                           const Tile& t, int nvalid, float sl2, int q4) {
-  float sv[8];
+// The split-softmax state of one tile, from scratch, for NB column blocks of
+// 16 heads: per head m = the tile's largest scaled logit (base 2), l = sum
+// of its weights 2^(s - m) (rounded to bf16, as applied), o = their
+// weighted sum of V rows. Lane (n16, q4) holds head 16 b + n16 of block b:
+// o[b][e][i] = dim 32 q4 + 8 i + e; m and l are the same in the head's four
+// lanes. Rows >= nvalid are masked unless FULL. The K rows and the
+// transposed V operands are shared by the blocks.
+template <bool FULL, int NB>
+__device__ __forceinline__ void tile_state(f32x4 (&o)[NB][8], float (&m)[NB], float (&l)[NB],
+                                           const bf16x8 (&qop)[NB][4], const Tile& t, int nvalid, float sl2,
+                                           int q4) {
+  bf16x8 pk[NB];
 #pragma unroll
-  for (int sg = 0; sg < 2; ++sg) {
-    f32x4 sacc = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int b = 0; b < NB; ++b) {
+    float sv[8];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(t.k[sg * 4 + ks]), qop[ks], sacc, 0, 0, 0);
+    for (int sg = 0; sg < 2; ++sg) {
+      f32x4 sacc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = 16 * sg + 4 * q4 + i;
-      sv[sg * 4 + i] = (FULL || row < nvalid) ? sacc[i] * sl2 : kNegInf;
+      for (int ks = 0; ks < 4; ++ks)
+        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(t.k[sg * 4 + ks]), qop[b][ks], sacc, 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = 16 * sg + 4 * q4 + i;
+        sv[sg * 4 + i] = (FULL || row < nvalid) ? sacc[i] * sl2 : kNegInf;
+      }
     }
-  }
-  float mx = sv[0];
+    float mx = sv[0];
 #pragma unroll
-  for (int k = 1; k < 8; ++k) mx = fmaxf(mx, sv[k]);
-  mx = fmaxf(mx, xor_shuffle(mx, 16));
-  mx = fmaxf(mx, xor_shuffle(mx, 32));
-  const float sub = (mx == kNegInf) ? 0.0f : mx;
-  float psum = 0.0f;
-  bf16x8 pk;
+    for (int k = 1; k < 8; ++k) mx = fmaxf(mx, sv[k]);
+    mx = fmaxf(mx, xor_shuffle(mx, 16));
+    mx = fmaxf(mx, xor_shuffle(mx, 32));
+    const float sub = (mx == kNegInf) ? 0.0f : mx;
+    float psum = 0.0f;
 #pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    const __bf16 pb = static_cast<__bf16>(fast_exp2(sv[k] - sub));
-    pk[k] = pb;
-    psum += static_cast<float>(pb);  // the denominator sums the weights actually applied
+    for (int k = 0; k < 8; ++k) {
+      const __bf16 pb = static_cast<__bf16>(fast_exp2(sv[k] - sub));
+      pk[b][k] = pb;
+      psum += static_cast<float>(pb);  // the denominator sums the weights actually applied
+    }
+    psum += xor_shuffle(psum, 16);
+    psum += xor_shuffle(psum, 32);
+    m[b] = mx;
+    l[b] = psum;
   }
-  psum += xor_shuffle(psum, 16);
-  psum += xor_shuffle(psum, 32);
-  m = mx;
-  l = psum;
 #define GQA_PV(E)                                                                                       \
-  o[E] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v_transpose<E>(t.v), pk, f32x4{0.0f, 0.0f, 0.0f, 0.0f}, \
-                                                 0, 0, 0);
+  {                                                                                                     \
+    const bf16x8 vt = v_transpose<E>(t.v);                                                              \
+    _Pragma("unroll") for (int b = 0; b < NB; ++b) o[b][E] =                                            \
+        __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt, pk[b], f32x4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);     \
+  }
   GQA_PV(0) GQA_PV(1) GQA_PV(2) GQA_PV(3) GQA_PV(4) GQA_PV(5) GQA_PV(6) GQA_PV(7)
 #undef GQA_PV
 }
@@ -377,15 +405,17 @@ __device__ void merge_parts(const DecodeParams& p, int s, int j, int p0, int n_s
 // The folding wave: fold the tile states of the workgroup's range in tile
 // order and finish every piece (write it out or publish it), count the
 // workgroup out for the fused step's lengths, settle tickets. Lane layout:
-// HP = 32 / NCH lanes per head (NCH = 2, 4, 8 for up to 4, 8, 16 heads);
-// lane l holds head l / HP and its four-dim columns c = (l mod HP) + HP i,
-// i < NCH, so each lane weighs a single head per tile.
-template <int NCH, bool FUSED>
-__device__ void fold_range(const DecodeParams& p, const Range& range, int Lreg, float (*s_o)[kHeads * kRow],
-                           float (*s_m)[kHeads], float (*s_l)[kHeads], int* s_ready, int* s_folded,
-                           const int* s_lens) {
+// HP = 32 / NCH lanes per head (NCH = 2, 4, 8, 16 for up to 4, 8, 16, 32
+// heads); lane l holds head l / HP and its four-dim columns
+// c = (l mod HP) + HP i, i < NCH, so each lane weighs a single head per tile.
+// The ring has ring_slots<NB>() slots of 16 NB heads.
+template <int NCH, bool FUSED, int NB>
+__device__ void fold_range(const DecodeParams& p, const Range& range, int Lreg,
+                           float (*s_o)[kBlockHeads * NB * kRow], float (*s_m)[kBlockHeads * NB],
+                           float (*s_l)[kBlockHeads * NB], int* s_ready, int* s_folded, const int* s_lens) {
   constexpr int HP = (kD / 4) / NCH;
   constexpr int R = fold_batch<NCH>();
+  constexpr int kRing = ring_slots<NB>();
   const int wg = blockIdx.x;
   const int lane = threadIdx.x & 63;
   const int G = p.G;
@@ -450,13 +480,12 @@ __device__ void fold_range(const DecodeParams& p, const Range& range, int Lreg, 
 #pragma unroll
         for (int i = 0; i < R; ++i) {
           if (i < r) {
-            const float M = fmaxf(am, mt[i]);
-            const float sb = (M == kNegInf) ? 0.0f : M;
-            const float a = fast_exp2(am - sb), bt = fast_exp2(mt[i] - sb);
+            // the same step as every merge of split states (2^(m_k - m) rescale)
+            const MergeWeights2 mw = merge_weights2(am, mt[i]);
 #pragma unroll
-            for (int c = 0; c < NCH; ++c) acc[c] = acc[c] * a + ot[i][c] * bt;
-            al = al * a + lt[i] * bt;
-            am = M;
+            for (int c = 0; c < NCH; ++c) acc[c] = merge_o(acc[c], mw, ot[i][c]);
+            al = merge_l(al, mw, lt[i]);
+            am = mw.run;
           }
         }
       }
@@ -517,8 +546,10 @@ __device__ void fold_range(const DecodeParams& p, const Range& range, int Lreg, 
   }
 }
 
-template <bool FUSED, bool PAGED>
+template <bool FUSED, bool PAGED, int NB>
 __global__ __launch_bounds__(kBlockThreads, 1) void decode_stream_kernel(DecodeParams p) {
+  constexpr int kRing = ring_slots<NB>();
+  constexpr int kHeads = kBlockHeads * NB;
   __shared__ __attribute__((aligned(16))) float s_o[kRing][kHeads * kRow];
   __shared__ float s_m[kRing][kHeads];
   __shared__ float s_l[kRing][kHeads];
@@ -554,7 +585,7 @@ __global__ __launch_bounds__(kBlockThreads, 1) void decode_stream_kernel(DecodeP
     bool have = next_piece(p, it, Lreg, pc);
     long long kb = 0;             // range tiles before piece pc
     int q_seg = -1;               // segment whose query rows are in qop
-    bf16x8 qop[4];
+    bf16x8 qop[NB][4];
     while (have) {
       int k = 0;
       if (lane == 0) k = __hip_atomic_fetch_add(&s_next, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
@@ -573,12 +604,14 @@ __global__ __launch_bounds__(kBlockThreads, 1) void decode_stream_kernel(DecodeP
         // the segment's last tile holds the appended token: store its rows
         // into their cache slot, wait for the stores, then read the tile
         const size_t new_row = kv_row<PAGED, true>(p.pg, p.g, p.cap, s, j, pc.L - 1);
-        if (lane < 32) {
-          const bool is_k = lane < 16;
-          const uint16_t* src = static_cast<const uint16_t*>(is_k ? p.k_new : p.v_new) + kv_head * kD;
-          uint16_t* dst = static_cast<uint16_t*>(is_k ? p.k_cache : p.v_cache) + new_row * kD;
-          st16(dst + 8 * (lane & 15), ld16(src + 8 * (lane & 15)));
-        }
+        // lanes 0-15 copy the K row, lanes 16-31 the V row (uniform bases,
+        // per-lane 16-byte offsets)
+        if (lane < 16)
+          st16(static_cast<uint16_t*>(p.k_cache) + new_row * kD + 8 * lane,
+               ld16(static_cast<const uint16_t*>(p.k_new) + kv_head * kD + 8 * lane));
+        else if (lane < 32)
+          st16(static_cast<uint16_t*>(p.v_cache) + new_row * kD + 8 * (lane - 16),
+               ld16(static_cast<const uint16_t*>(p.v_new) + kv_head * kD + 8 * (lane - 16)));
         wait_stores();
       }
       const uint16_t* kbp;
@@ -592,38 +625,44 @@ __global__ __launch_bounds__(kBlockThreads, 1) void decode_stream_kernel(DecodeP
         vbp = static_cast<const uint16_t*>(p.v_cache) + (kv_head * p.cap + t0) * kD;
       }
       Tile t;
-      if (nvalid >= kTile) load_tile<true>(t, kbp, vbp, kTile, n16, q4);
-      else load_tile<false>(t, kbp, vbp, nvalid, n16, q4);
+      load_tile(t, kbp, vbp, nvalid < kTile ? nvalid : kTile, n16, q4);
       const int seg = s * p.g + j;
       if (seg != q_seg) {
         // the group's query rows, after the tile's loads are on their way
         const uint16_t* qg = static_cast<const uint16_t*>(p.q) + (size_t(s) * p.h + size_t(j) * G) * kD;
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          u32x4 v = {0u, 0u, 0u, 0u};
-          if (n16 < G) v = ld16(qg + size_t(n16) * kD + ks * 32 + q4 * 8);
-          qop[ks] = as_bf16x8(v);
-        }
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks) {
+            const int head = kBlockHeads * b + n16;
+            u32x4 v = {0u, 0u, 0u, 0u};
+            if (head < G) v = ld16(qg + size_t(head) * kD + ks * 32 + q4 * 8);
+            qop[b][ks] = as_bf16x8(v);
+          }
         q_seg = seg;
       }
-      f32x4 o[8];
-      float m, l;
-      if (nvalid >= kTile) tile_state<true>(o, m, l, qop, t, kTile, sl2, q4);
-      else tile_state<false>(o, m, l, qop, t, nvalid, sl2, q4);
+      f32x4 o[NB][8];
+      float m[NB], l[NB];
+      if (nvalid >= kTile) tile_state<true, NB>(o, m, l, qop, t, kTile, sl2, q4);
+      else tile_state<false, NB>(o, m, l, qop, t, nvalid, sl2, q4);
       // slot k mod kRing is free once tile k - kRing has been folded
       const int slot = k & (kRing - 1);
       while (__hip_atomic_load(&s_folded, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) <= k - kRing)
         __builtin_amdgcn_s_sleep(1);
-      if (n16 < G) {
-        float* row = &s_o[slot][n16 * kRow + 32 * q4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          *reinterpret_cast<f32x4*>(row + 8 * i) = f32x4{o[0][i], o[1][i], o[2][i], o[3][i]};
-          *reinterpret_cast<f32x4*>(row + 8 * i + 4) = f32x4{o[4][i], o[5][i], o[6][i], o[7][i]};
-        }
-        if (q4 == 0) {
-          s_m[slot][n16] = m;
-          s_l[slot][n16] = l;
+      for (int b = 0; b < NB; ++b) {
+        const int head = kBlockHeads * b + n16;
+        if (head < G) {
+          float* row = &s_o[slot][head * kRow + 32 * q4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            *reinterpret_cast<f32x4*>(row + 8 * i) = f32x4{o[b][0][i], o[b][1][i], o[b][2][i], o[b][3][i]};
+            *reinterpret_cast<f32x4*>(row + 8 * i + 4) = f32x4{o[b][4][i], o[b][5][i], o[b][6][i], o[b][7][i]};
+          }
+          if (q4 == 0) {
+            s_m[slot][head] = m[b];
+            s_l[slot][head] = l[b];
+          }
         }
       }
       // every lane's writes are done before the slot is marked
@@ -635,14 +674,23 @@ __global__ __launch_bounds__(kBlockThreads, 1) void decode_stream_kernel(DecodeP
   }
 
   // ---- folding wave (one instance per head-block width)
-  if (G <= 4) fold_range<2, FUSED>(p, range, Lreg, s_o, s_m, s_l, s_ready, &s_folded, s_lens);
-  else if (G <= 8) fold_range<4, FUSED>(p, range, Lreg, s_o, s_m, s_l, s_ready, &s_folded, s_lens);
-  else fold_range<8, FUSED>(p, range, Lreg, s_o, s_m, s_l, s_ready, &s_folded, s_lens);
+  if constexpr (NB == 1) {
+    if (G <= 4) fold_range<2, FUSED, NB>(p, range, Lreg, s_o, s_m, s_l, s_ready, &s_folded, s_lens);
+    else if (G <= 8) fold_range<4, FUSED, NB>(p, range, Lreg, s_o, s_m, s_l, s_ready, &s_folded, s_lens);
+    else fold_range<8, FUSED, NB>(p, range, Lreg, s_o, s_m, s_l, s_ready, &s_folded, s_lens);
+  } else {
+    fold_range<16, FUSED, NB>(p, range, Lreg, s_o, s_m, s_l, s_ready, &s_folded, s_lens);
+  }
 }
 
 template <bool FUSED, bool PAGED>
 void launch(const DecodeParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_stream_kernel<FUSED, PAGED>), dim3(p.workgroups), dim3(kBlockThreads), 0, stream, p);
+  if (p.G <= kBlockHeads)
+    hipLaunchKernelGGL((decode_stream_kernel<FUSED, PAGED, 1>), dim3(p.workgroups), dim3(kBlockThreads), 0, stream,
+                       p);
+  else
+    hipLaunchKernelGGL((decode_stream_kernel<FUSED, PAGED, 2>), dim3(p.workgroups), dim3(kBlockThreads), 0, stream,
+                       p);
 }
 
 }  // namespace
@@ -656,18 +704,23 @@ hipError_t launch_decode_stream(const DecodeParams& p, hipStream_t stream) {
 
 // Workgroups of the instance that fit on one compute unit (cached per
 // process; the answer depends only on the kernel and the architecture).
-int stream_workgroups_per_cu(bool fused, bool paged) {
-  static std::atomic<int> cached[4] = {};
-  const int k = (fused ? 1 : 0) + (paged ? 2 : 0);
+int stream_workgroups_per_cu(bool fused, bool paged, int G) {
+  static std::atomic<int> cached[8] = {};
+  const bool wide = G > kBlockHeads;
+  const int k = (fused ? 1 : 0) + (paged ? 2 : 0) + (wide ? 4 : 0);
   const int known = cached[k].load(std::memory_order_relaxed);
   if (known > 0) return known;
   int n = 0;
   hipError_t e;
   switch (k) {
-    case 0: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_stream_kernel<false, false>, kBlockThreads, 0); break;
-    case 1: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_stream_kernel<true, false>, kBlockThreads, 0); break;
-    case 2: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_stream_kernel<false, true>, kBlockThreads, 0); break;
-    default: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_stream_kernel<true, true>, kBlockThreads, 0); break;
+    case 0: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_stream_kernel<false, false, 1>, kBlockThreads, 0); break;
+    case 1: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_stream_kernel<true, false, 1>, kBlockThreads, 0); break;
+    case 2: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_stream_kernel<false, true, 1>, kBlockThreads, 0); break;
+    case 3: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_stream_kernel<true, true, 1>, kBlockThreads, 0); break;
+    case 4: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_stream_kernel<false, false, 2>, kBlockThreads, 0); break;
+    case 5: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_stream_kernel<true, false, 2>, kBlockThreads, 0); break;
+    case 6: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_stream_kernel<false, true, 2>, kBlockThreads, 0); break;
+    default: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_stream_kernel<true, true, 2>, kBlockThreads, 0); break;
   }
   if (e != hipSuccess || n <= 0) {
     (void)hipGetLastError();

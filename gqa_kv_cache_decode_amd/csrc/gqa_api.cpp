@@ -128,7 +128,7 @@ int plan_decode(int b, int h, int g, int d_k, int d_v, int cap, int max_len, int
     plan->gblk = gqa::vector_heads_per_block(G);
     plan->nhb = (G + plan->gblk - 1) / plan->gblk;
   }
-  // One query token, at most 16 heads per KV head and 64 sequences: the
+  // One query token, at most 32 heads per KV head and 64 sequences: the
   // stream kernel (tile-granular schedule, waves finishing pieces on their own).
   plan->stream = chosen == GQA_PATH_MATRIX && !causal && G <= gqa::kStreamMaxGroup && b <= gqa::kStreamMaxBatch;
   const int waves = chosen == GQA_PATH_MATRIX ? gqa::matrix_waves(G) : gqa::vector_waves(dtype, d_k, plan->gblk);
@@ -142,7 +142,7 @@ int plan_decode(int b, int h, int g, int d_k, int d_v, int cap, int max_len, int
     // Up to eight waves per compute unit (two 4-wave workgroups or one
     // 8-wave one keep enough loads in flight), never more than fit at once, so
     // the persistent grid runs in a single round.
-    int fit = plan->stream ? gqa::stream_workgroups_per_cu(fused, paged)
+    int fit = plan->stream ? gqa::stream_workgroups_per_cu(fused, paged, G)
               : chosen == GQA_PATH_MATRIX ? gqa::matrix_workgroups_per_cu(G, fused, paged, causal)
                                           : gqa::vector_workgroups_per_cu(dtype, d_k, plan->gblk, fused, paged, causal);
     if (fit <= 0) fit = 2;  // no device to ask: assume the common case

@@ -184,12 +184,12 @@ constexpr int kMergeLds = 2 * kMergePairs + 3 * kMatrixMaxGroup;
 hipError_t launch_append(const AppendParams& p, int b, int dtype, hipStream_t stream);
 hipError_t launch_decode_vector(const DecodeParams& p, int dtype, hipStream_t stream);
 hipError_t launch_decode_matrix(const DecodeParams& p, hipStream_t stream);
-// One-token matrix decode for up to 16 heads per KV head and up to 64
+// One-token matrix decode for up to 32 heads per KV head and up to 64
 // sequences (decode_stream.hip); seg_lead counts empty tiles there.
-constexpr int kStreamMaxGroup = 16;
+constexpr int kStreamMaxGroup = 32;
 constexpr int kStreamMaxBatch = 64;
 hipError_t launch_decode_stream(const DecodeParams& p, hipStream_t stream);
-int stream_workgroups_per_cu(bool fused, bool paged);
+int stream_workgroups_per_cu(bool fused, bool paged, int G);
 hipError_t launch_merge_partials(const DecodeParams& p, int dtype, hipStream_t stream);
 hipError_t launch_linear(const LinearParams& p, hipStream_t stream);
 size_t packed_weight_bytes(int n_out, int n_in);

@@ -162,13 +162,17 @@ def test_plan_choices(lib):
     # the Llama-3-70B shape: the matrix path's one-block streaming kernel, merges inside the launch
     assert plan(16, 64, 8, 128, 8256, 8193, _lib.BF16)[0] == _lib.PATH_MATRIX | _lib.MERGE_INLINE | _lib.PLAN_STREAM
     assert plan(64, 28, 4, 128, 2112, 2080, _lib.BF16)[0] & _lib.PLAN_STREAM  # the Qwen2.5-7B shape too
-    # past 16 heads per KV head or 64 sequences: the unit kernels
+    # up to 32 heads per KV head (two column blocks) as well
+    assert plan(16, 64, 2, 128, 2112, 2080, _lib.BF16)[0] & _lib.PLAN_STREAM
+    assert plan(16, 24, 1, 128, 2112, 2080, _lib.BF16)[0] & _lib.PLAN_STREAM
+    # past 32 heads per KV head or 64 sequences: the unit kernels
     assert not plan(65, 64, 8, 128, 2112, 2080, _lib.BF16)[0] & _lib.PLAN_STREAM
-    assert not plan(16, 64, 2, 128, 2112, 2080, _lib.BF16)[0] & _lib.PLAN_STREAM
+    assert not plan(16, 64, 1, 128, 2112, 2080, _lib.BF16)[0] & _lib.PLAN_STREAM
     M = M | _lib.PLAN_STREAM
     # few long segments with 32 heads per KV head: merged by a second launch
-    assert plan(8, 32, 1, 128, 4160, 4097, _lib.BF16)[0] == _lib.PATH_MATRIX | _lib.MERGE_KERNEL
-    assert plan(4, 32, 1, 128, 32832, 32769, _lib.BF16)[0] == _lib.PATH_MATRIX | _lib.MERGE_KERNEL
+    S = _lib.PATH_MATRIX | _lib.MERGE_KERNEL | _lib.PLAN_STREAM
+    assert plan(8, 32, 1, 128, 4160, 4097, _lib.BF16)[0] == S
+    assert plan(4, 32, 1, 128, 32832, 32769, _lib.BF16)[0] == S
     assert plan(4, 32, 32, 128, 32832, 32769, _lib.BF16)[0] & ~M == _lib.PATH_VECTOR  # one head per KV head
     assert plan(2, 4, 2, 16, 128, 65, _lib.F32)[0] & ~M == _lib.PATH_VECTOR
     for args in [(16, 64, 8, 128, 8256, 8193, _lib.BF16), (2, 4, 2, 16, 128, 65, _lib.F32),
@@ -178,7 +182,8 @@ def test_plan_choices(lib):
     assert plan(16, 64, 8, 128, 8256, 8193, _lib.BF16, path=_lib.PATH_VECTOR, wgs=77)[1] == 77
     # forced merge modes are kept; both flags at once are rejected
     for flag in (_lib.MERGE_INLINE, _lib.MERGE_KERNEL):
-        assert plan(8, 32, 1, 128, 4160, 4097, _lib.BF16, path=_lib.PATH_MATRIX | flag)[0] == _lib.PATH_MATRIX | flag
+        assert plan(8, 32, 1, 128, 4160, 4097, _lib.BF16, path=_lib.PATH_MATRIX | flag)[0] & ~_lib.PLAN_STREAM == \
+            _lib.PATH_MATRIX | flag
         assert plan(2, 4, 2, 16, 128, 65, _lib.F32, path=flag)[0] == _lib.PATH_VECTOR | flag
     p, c = ctypes.c_int(), ctypes.c_int()
     assert lib.gqa_decode_plan(8, 32, 1, 128, 128, 4160, 4097, _lib.BF16, M, 0, ctypes.byref(p),

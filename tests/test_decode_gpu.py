@@ -147,6 +147,8 @@ EDGE = [
     (2, 12, 4, 128, 100, [97, 3], "bf16"),           # G = 3
     (2, 64, 1, 128, 200, [200, 131], "bf16"),        # G = 64 (four 16-head blocks)
     (2, 34, 2, 128, 90, [90, 45], "bf16"),           # G = 17 (second head block partly used)
+    (3, 32, 1, 128, 300, [300, 33, 0], "bf16"),      # G = 32, MQA: two full head blocks
+    (2, 64, 2, 128, 129, [129, 96], "bf16"),         # G = 32 with two KV heads
     (2, 6, 6, 128, 70, [70, 5], "bf16"),             # MHA, vector path
     (3, 10, 2, 16, 80, [80, 1, 33], "bf16"),
     (3, 10, 5, 32, 80, [79, 2, 40], "bf16"),

@@ -83,6 +83,20 @@ def test_step_paths_and_grids(gpu_lib, oracle_mod, path, wgs):
         pb.check_state()
 
 
+@pytest.mark.parametrize("h,g,lens,wgs", [(32, 1, [0, 31, 32, 95], 0), (32, 1, [0, 31, 32, 95], 5),
+                                          (40, 2, [70, 1, 64, 33], 0), (64, 2, [96, 97], 3)])
+def test_step_wide_head_groups(gpu_lib, oracle_mod, h, g, lens, wgs):
+    # 17 to 32 query heads per KV head (two MFMA column blocks), ragged tails
+    # around the 32-position tiles, poisoned slots past every length
+    print(f"wide head groups: h={h} g={g} lens={lens} workgroups={wgs}", flush=True)
+    pb = StepProblem(oracle_mod, seed=320 + h + wgs, b=len(lens), h=h, g=g, d=128, cap=104, lens=lens, dtype="bf16")
+    for step in range(4):
+        merge = api.MERGE_KERNEL if step == 3 else api.MERGE_INLINE
+        got, ref = pb.step(step, path=api.PATH_MATRIX | merge, wgs=wgs)
+        assert_parity(got, ref, "bf16", f"step {step} merge={merge:#x}")
+        pb.check_state()
+
+
 @pytest.mark.parametrize("dtype,d,h,g", [("f32", 16, 4, 2), ("f32", 128, 8, 8), ("bf16", 64, 12, 3),
                                          ("bf16", 256, 4, 1), ("f32", 256, 6, 2)])
 def test_step_vector_shapes(gpu_lib, oracle_mod, dtype, d, h, g):
