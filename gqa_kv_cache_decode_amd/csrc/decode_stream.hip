@@ -67,25 +67,21 @@ constexpr int kRow = kD + 4;        // LDS row stride (floats), padded against b
 // 16 heads per KV head, NB = 2: up to 32); either way about 135 KB of LDS.
 template <int NB>
 constexpr int ring_slots() { return NB == 1 ? 16 : 8; }
-constexpr int kFolder = kWaves - 1; // the folding wave; waves 0 .. kWaves - 2 stream
 constexpr int kCountTiles = 3;      // tiles before a piece's end at which it counts in on its ticket
 constexpr int kFlagSpins = 1 << 22; // bound of the wait for another part's ready flag
 // Parts of a segment whose states the merge holds in registers at once, by
 // columns per lane.
 template <int NCH>
-constexpr int fast_slots() { return NCH == 16 ? 1 : (NCH == 8 ? 2 : (NCH == 4 ? 5 : 9)); }
+constexpr int fast_slots() { return NCH == 8 ? 2 : (NCH == 4 ? 5 : 9); }
 // Ring slots the folding wave reads in one round, by columns per lane.
 template <int NCH>
-constexpr int fold_batch() { return NCH == 16 ? 1 : (NCH == 8 ? 2 : 4); }
+constexpr int fold_batch() { return NCH == 8 ? 2 : 4; }
 constexpr int kCountGroups = 16;    // first-level counters of the fused step's length update
 constexpr int kCountStride = 32;    // ints between counters (128 bytes)
 
 __device__ __forceinline__ u32x4 ld16(const uint16_t* ptr) { return *reinterpret_cast<const u32x4*>(ptr); }
 __device__ __forceinline__ void st16(uint16_t* ptr, u32x4 v) { *reinterpret_cast<u32x4*>(ptr) = v; }
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
-
-// V rows this lane loads for k-slot r of the value MFMA (see decode_matrix.hip).
-__device__ __forceinline__ int v_row(int q4, int r) { return (r < 4) ? (4 * q4 + r) : (16 + 4 * q4 + (r - 4)); }
 
 template <int E>
 __device__ __forceinline__ bf16x8 v_transpose(const u32x4* vr) {
@@ -102,7 +98,9 @@ __device__ __forceinline__ bf16x8 v_transpose(const u32x4* vr) {
 
 // One 32-position tile in registers: K rows as the score MFMA's A operand
 // (k[sg * 4 + ks]: row 16 sg + n16, dims 32 ks + 8 q4 .. +7), V rows
-// tau(q4, r) (dims 8 n16 .. +7).
+// v[r] = row 4 q4 + r (r < 4) or 16 + 4 q4 + r - 4 (dims 8 n16 .. +7): the
+// positions this lane's k-slots of the value MFMA weigh (as in
+// decode_matrix.hip).
 struct Tile {
   u32x4 k[8];
   u32x4 v[8];
@@ -137,7 +135,7 @@ __device__ __forceinline__ void load_tile(Tile& t, const uint16_t* kb, const uin
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) t.k[sg * 4 + ks] = tile_ld(rk, ko, ks * 64);
   }
-  // V row v_row(q4, r) = 4 q4 + r (r < 4) or 16 + 4 q4 + r - 4, dims 8 n16 .. +7
+  // V row 4 q4 + r (r < 4) or 16 + 4 q4 + r - 4, dims 8 n16 .. +7
   const int vo = 4 * q4 * kRowBytes + n16 * 16;
 #pragma unroll
   for (int hf = 0; hf < 2; ++hf) {
@@ -327,20 +325,22 @@ struct LenCount {
   }
 };
 
-// Ready flag of partial slot `slot` of workgroup `wg` (zero between calls).
-__device__ __forceinline__ int* slot_flag(const DecodeParams& p, int wg, int slot) {
-  return p.ws_done + kFlagsOffset / sizeof(int) + wg * 2 + slot;
+// Ready flag of head block `half` of partial slot `slot` of workgroup `wg`
+// (zero between calls).
+__device__ __forceinline__ int* slot_flag(const DecodeParams& p, int wg, int slot, int half) {
+  return p.ws_done + kFlagsOffset / sizeof(int) + (wg * 2 + slot) * 2 + half;
 }
 
-// The merging wave waits until every other part of segment p0 .. p0 +
-// n_slots - 1 has raised its ready flag (each has already taken its ticket,
-// so it is running and only has its stores left). The wait is bounded.
-__device__ void wait_parts(const DecodeParams& p, int p0, int n_slots, int own) {
+// The merging wave of head block `half` waits until every other part of
+// segment p0 .. p0 + n_slots - 1 has raised that block's ready flag (each
+// part has already taken its ticket, so it is running and has only its own
+// tiles and stores left). The wait is bounded.
+__device__ void wait_parts(const DecodeParams& p, int p0, int n_slots, int own, int half) {
   const int lane = threadIdx.x & 63;
   for (int q0 = 0; q0 < n_slots; q0 += 64) {
     const int q = q0 + lane;
     const bool need = q < n_slots && q != own;
-    int* f = need ? slot_flag(p, p0 + q, q == 0 ? 1 : 0) : nullptr;
+    int* f = need ? slot_flag(p, p0 + q, q == 0 ? 1 : 0, half) : nullptr;
     for (int it = 0; it < kFlagSpins; ++it) {
       const bool ready = !need || __hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0;
       if (__ballot(!ready) == 0) break;
@@ -352,16 +352,16 @@ __device__ void wait_parts(const DecodeParams& p, int p0, int n_slots, int own) 
 // Merge of the parts of segment (s, j) in part order (slot 1 of p0, then
 // slot 0 of p0 + 1 .. p0 + n_slots - 1), with part `own` taken from this
 // wave's registers, up to B parts' loads in flight at a time; then the
-// output rows. Lane layout as in fold_range.
+// output rows. Lane layout as in fold_range, heads from h0.
 template <int NCH>
-__device__ void merge_parts(const DecodeParams& p, int s, int j, int p0, int n_slots, int own,
+__device__ void merge_parts(const DecodeParams& p, int s, int j, int p0, int n_slots, int own, int h0,
                             const f32x4 (&own_o)[NCH], float own_m, float own_l) {
   constexpr int HP = (kD / 4) / NCH;
   constexpr int B = fast_slots<NCH>();
   const int lane = threadIdx.x & 63;
   const int G = p.G;
-  const int hh = lane / HP;
-  const int sub = lane - hh * HP;
+  const int hh = h0 + lane / HP;
+  const int sub = lane % HP;
   if (hh >= G) return;
   const __amdgpu_buffer_rsrc_t rs = slots_rsrc(p);
   const int ml_off = G * kD * int(sizeof(float));
@@ -402,33 +402,43 @@ __device__ void merge_parts(const DecodeParams& p, int s, int j, int p0, int n_s
   for (int i = 0; i < NCH; ++i) *reinterpret_cast<uint2*>(out + 4 * (sub + HP * i)) = to_bf16x4(res[i] * inv);
 }
 
-// The folding wave: fold the tile states of the workgroup's range in tile
-// order and finish every piece (write it out or publish it), count the
-// workgroup out for the fused step's lengths, settle tickets. Lane layout:
-// HP = 32 / NCH lanes per head (NCH = 2, 4, 8, 16 for up to 4, 8, 16, 32
-// heads); lane l holds head l / HP and its four-dim columns
-// c = (l mod HP) + HP i, i < NCH, so each lane weighs a single head per tile.
-// The ring has ring_slots<NB>() slots of 16 NB heads.
+// A folding wave: fold the tile states of the workgroup's range in tile
+// order for the heads of its block and finish every piece for them (write
+// them out, publish them or merge them). With NB = 2 there is one folding
+// wave per block of 16 heads, each working alone on its heads with its own
+// ready flags; block 0's wave also counts the workgroup out for the fused
+// step's lengths and takes the piece tickets, and hands each ticket's result
+// to block 1's wave through LDS (s_tk: value and piece number, 16 pieces
+// deep; block 1 is never more than a ring's worth of tiles, hence of pieces,
+// behind block 0). Lane layout: HP = 32 / NCH lanes per head (NCH = 2, 4,
+// 8 for up to 4, 8, 16 heads per block); lane l holds head 16 hb + l / HP
+// and its four-dim columns c = (l mod HP) + HP i, i < NCH, so each lane
+// weighs a single head per tile. The ring has ring_slots<NB>() slots of
+// 16 NB heads; s_folded[hb] counts the tiles block hb has folded.
 template <int NCH, bool FUSED, int NB>
-__device__ void fold_range(const DecodeParams& p, const Range& range, int Lreg,
+__device__ void fold_range(const DecodeParams& p, const Range& range, int Lreg, int hb,
                            float (*s_o)[kBlockHeads * NB * kRow], float (*s_m)[kBlockHeads * NB],
-                           float (*s_l)[kBlockHeads * NB], int* s_ready, int* s_folded, const int* s_lens) {
+                           float (*s_l)[kBlockHeads * NB], int* s_ready, int* s_folded, int (*s_tk)[16],
+                           const int* s_lens) {
   constexpr int HP = (kD / 4) / NCH;
   constexpr int R = fold_batch<NCH>();
   constexpr int kRing = ring_slots<NB>();
   const int wg = blockIdx.x;
   const int lane = threadIdx.x & 63;
   const int G = p.G;
-  const int hh = lane / HP;
-  const int sub = lane - hh * HP;
+  const int h0 = kBlockHeads * hb;
+  const int hh = h0 + lane / HP;
+  const int sub = lane % HP;
   const bool active = hh < G;
+  const bool lead = hb == 0;  // counts, takes tickets
   LenCount cnt;
   cnt.state = 2;
-  if (FUSED) cnt.start(p, wg);
+  if (FUSED && lead) cnt.start(p, wg);
   Range it = range;
   StreamPiece pc;
-  int k = 0;  // next range tile to fold
-  while (next_piece(p, it, Lreg, pc)) {
+  int k = 0;    // next range tile to fold
+  int ord = 0;  // pieces finished so far
+  for (; next_piece(p, it, Lreg, pc); ++ord) {
     const int n = pc.tile_end - pc.tile_begin;
     const int s = pc.s, j = pc.grp;
     const bool shared = pc.p0 != pc.p1;
@@ -461,7 +471,7 @@ __device__ void fold_range(const DecodeParams& p, const Range& range, int Lreg,
       for (int i = 1; i < R; ++i)
         if (r == i && e + i < n && rd[i] == k + i) r = i + 1;
       r = __builtin_amdgcn_readfirstlane(r);
-      if (inline_merge && lane == 0 && count_at >= e && count_at < e + r)
+      if (lead && inline_merge && lane == 0 && count_at >= e && count_at < e + r)
         t = __hip_atomic_fetch_add(ticket, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if (active) {
         f32x4 ot[R][NCH];
@@ -494,8 +504,8 @@ __device__ void fold_range(const DecodeParams& p, const Range& range, int Lreg,
       __builtin_amdgcn_wave_barrier();
       e += r;
       k += r;
-      if (lane == 0) __hip_atomic_store(s_folded, k, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
-      if (FUSED) cnt.step(p, s_lens);
+      if (lane == 0) __hip_atomic_store(&s_folded[hb], k, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+      if (FUSED && lead) cnt.step(p, s_lens);
     }
     // the piece is complete
     if (!shared) {
@@ -505,19 +515,32 @@ __device__ void fold_range(const DecodeParams& p, const Range& range, int Lreg,
 #pragma unroll
         for (int i = 0; i < NCH; ++i) *reinterpret_cast<uint2*>(out + 4 * (sub + HP * i)) = to_bf16x4(acc[i] * inv);
       }
-      if (p.merge_kernel && pc.tile_begin == 0 && lane == 0) p.seg_info[size_t(s) * p.ngroups + j] = make_int2(pc.p0, -1);
+      if (lead && p.merge_kernel && pc.tile_begin == 0 && lane == 0)
+        p.seg_info[size_t(s) * p.ngroups + j] = make_int2(pc.p0, -1);
       continue;
     }
-    t = __builtin_amdgcn_readfirstlane(t);
+    if (inline_merge) {
+      if (lead) {
+        t = __builtin_amdgcn_readfirstlane(t);
+        if (NB > 1 && lane == 0) {
+          s_tk[0][ord & 15] = t;
+          __hip_atomic_store(&s_tk[1][ord & 15], ord + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+        }
+      } else {
+        while (__hip_atomic_load(&s_tk[1][ord & 15], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) != ord + 1)
+          __builtin_amdgcn_s_sleep(1);
+        t = __builtin_amdgcn_readfirstlane(s_tk[0][ord & 15]);
+      }
+    }
     if (inline_merge && t == n_slots - 1) {
       // the last part: merge once the others' states are in their slots, and
       // leave the ticket and their flags at zero
-      wait_parts(p, pc.p0, n_slots, own);
-      merge_parts<NCH>(p, s, j, pc.p0, n_slots, own, acc, am, al);
+      wait_parts(p, pc.p0, n_slots, own, hb);
+      merge_parts<NCH>(p, s, j, pc.p0, n_slots, own, h0, acc, am, al);
       if (lane < n_slots && lane != own)
-        __hip_atomic_store(slot_flag(p, pc.p0 + lane, lane == 0 ? 1 : 0), 0, __ATOMIC_RELAXED,
+        __hip_atomic_store(slot_flag(p, pc.p0 + lane, lane == 0 ? 1 : 0, hb), 0, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
-      if (lane == 0) __hip_atomic_store(ticket, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (lead && lane == 0) __hip_atomic_store(ticket, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       continue;
     }
     // publish this part's state, then (inline merge) its ready flag
@@ -535,13 +558,14 @@ __device__ void fold_range(const DecodeParams& p, const Range& range, int Lreg,
       }
     }
     if (p.merge_kernel) {
-      if (pc.tile_begin == 0 && lane == 0) p.seg_info[size_t(s) * p.ngroups + j] = make_int2(pc.p0, pc.p1);
+      if (lead && pc.tile_begin == 0 && lane == 0) p.seg_info[size_t(s) * p.ngroups + j] = make_int2(pc.p0, pc.p1);
     } else {
       wait_stores();
-      if (lane == 0) __hip_atomic_store(slot_flag(p, wg, my_slot), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (lane == 0)
+        __hip_atomic_store(slot_flag(p, wg, my_slot, hb), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
-  if (FUSED) {
+  if (FUSED && lead) {
     while (cnt.state != 2) cnt.step(p, s_lens);
   }
 }
@@ -556,7 +580,9 @@ __global__ __launch_bounds__(kBlockThreads, 1) void decode_stream_kernel(DecodeP
   __shared__ int s_ready[kRing];  // range tile index whose state a ring slot holds (-1: none yet)
   __shared__ int s_lens[64];
   __shared__ int s_next;          // next range tile to hand out
-  __shared__ int s_folded;        // range tiles folded so far
+  __shared__ int s_folded[NB];    // range tiles folded so far, per head block
+  __shared__ int s_tk[2][16];     // ticket results handed from block 0's folding wave to block 1's
+  constexpr int kStreamers = kWaves - NB;  // waves 0 .. kStreamers - 1 stream, one folding wave per head block
 
   const int wg = blockIdx.x;
   const int lane = threadIdx.x & 63;
@@ -568,17 +594,16 @@ __global__ __launch_bounds__(kBlockThreads, 1) void decode_stream_kernel(DecodeP
 
   if (w == 0) s_lens[lane] = lane < p.b ? attended_len(p, lane) : 0;
   if (threadIdx.x < kRing) s_ready[threadIdx.x] = -1;
-  if (threadIdx.x == 0) {
-    s_next = 0;
-    s_folded = 0;
-  }
+  if (threadIdx.x < NB) s_folded[threadIdx.x] = 0;
+  if (threadIdx.x < 16) s_tk[1][threadIdx.x] = 0;
+  if (threadIdx.x == 0) s_next = 0;
   if (!FUSED) zero_empty_sequences<uint16_t, false>(p, wg);
   __syncthreads();
 
   const int Lreg = s_lens[lane];
   const Range range = locate(p, Lreg, wg);
 
-  if (w != kFolder) {
+  if (w < kStreamers) {
     // ---- streaming wave: take tiles, leave their states in the ring
     Range it = range;
     StreamPiece pc;
@@ -647,8 +672,16 @@ __global__ __launch_bounds__(kBlockThreads, 1) void decode_stream_kernel(DecodeP
       else tile_state<false, NB>(o, m, l, qop, t, nvalid, sl2, q4);
       // slot k mod kRing is free once tile k - kRing has been folded
       const int slot = k & (kRing - 1);
-      while (__hip_atomic_load(&s_folded, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) <= k - kRing)
+      // (by every head block's folding wave)
+      while (true) {
+        int folded = __hip_atomic_load(&s_folded[0], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP);
+        if constexpr (NB > 1) {
+          const int f1 = __hip_atomic_load(&s_folded[1], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP);
+          folded = f1 < folded ? f1 : folded;
+        }
+        if (folded > k - kRing) break;
         __builtin_amdgcn_s_sleep(1);
+      }
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
         const int head = kBlockHeads * b + n16;
@@ -673,13 +706,13 @@ __global__ __launch_bounds__(kBlockThreads, 1) void decode_stream_kernel(DecodeP
     return;
   }
 
-  // ---- folding wave (one instance per head-block width)
+  // ---- folding waves (one per block of 16 heads; lane layout by the heads in use)
   if constexpr (NB == 1) {
-    if (G <= 4) fold_range<2, FUSED, NB>(p, range, Lreg, s_o, s_m, s_l, s_ready, &s_folded, s_lens);
-    else if (G <= 8) fold_range<4, FUSED, NB>(p, range, Lreg, s_o, s_m, s_l, s_ready, &s_folded, s_lens);
-    else fold_range<8, FUSED, NB>(p, range, Lreg, s_o, s_m, s_l, s_ready, &s_folded, s_lens);
+    if (G <= 4) fold_range<2, FUSED, NB>(p, range, Lreg, 0, s_o, s_m, s_l, s_ready, s_folded, s_tk, s_lens);
+    else if (G <= 8) fold_range<4, FUSED, NB>(p, range, Lreg, 0, s_o, s_m, s_l, s_ready, s_folded, s_tk, s_lens);
+    else fold_range<8, FUSED, NB>(p, range, Lreg, 0, s_o, s_m, s_l, s_ready, s_folded, s_tk, s_lens);
   } else {
-    fold_range<16, FUSED, NB>(p, range, Lreg, s_o, s_m, s_l, s_ready, &s_folded, s_lens);
+    fold_range<8, FUSED, NB>(p, range, Lreg, w - kStreamers, s_o, s_m, s_l, s_ready, s_folded, s_tk, s_lens);
   }
 }
 

@@ -117,9 +117,10 @@ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 // The very end of the workspace: the fused step's completion counters (one
 // top counter and 16 first-level ones, 128 bytes apart) in the first 4 KiB,
-// then one ready flag per partial slot (kMaxWorkgroups x 2 int32).
+// then one ready flag per partial slot and head block of 16 heads
+// (kMaxWorkgroups x 2 slots x 2 blocks, int32).
 constexpr size_t kFlagsOffset = 4096;
-constexpr size_t kDoneBytes = kFlagsOffset + size_t(kMaxWorkgroups) * 2 * sizeof(int);
+constexpr size_t kDoneBytes = kFlagsOffset + size_t(kMaxWorkgroups) * 2 * 2 * sizeof(int);
 
 // y_s = x w_s^T for up to three weight matrices w_s [n_out_s][n_in] (bf16,
 // packed by launch_pack_weight), x [rows][n_in], y_s [rows][n_out_s];

@@ -115,9 +115,10 @@ int gqa_kv_append(void* k_cache, void* v_cache, const void* k_new, const void* v
  * Returns 0 for invalid arguments.
  *
  * The workspace (256-byte aligned) holds the split-softmax partial states of
- * the persistent workgroups from its start, and int32 counters at its end:
- * the last 256 + 4*n bytes (of the buffer's size rounded down to 256), with
- * n = 32*b*h if b*h <= 8192, else max(b*h, 262144). Those counter bytes must
+ * the persistent workgroups from its start, and int32 counters and flags at
+ * its end: the last 36864 + c bytes (of the buffer's size rounded down to
+ * 256), where c = 4*n rounded up to a multiple of 256, with n = 32*b*h if
+ * b*h <= 8192, else max(b*h, 262144). Those counter bytes must
  * be ZERO before the first call that uses a buffer (e.g. allocate it
  * zero-filled); every call leaves them zero again. Because the counters are
  * placed from the end, a buffer sized for one shape serves any sequence of

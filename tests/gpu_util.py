@@ -66,12 +66,12 @@ def assert_parity(got_dev: torch.Tensor, ref: np.ndarray, dtype: str, what: str 
 
 
 def counter_bytes(ws, b, h):
-    """The workspace's counter region (its last 4096 + 4n bytes, as the header states)."""
+    """The workspace's counter region (its last 36864 + c bytes, as the header states)."""
     bh = b * h
     n = 32 * bh if bh <= 8192 else max(bh, 262144)
     usable = (ws.numel() * ws.element_size()) & ~255
     cnt = ((4 * n + 255) // 256) * 256
-    return ws.view(torch.uint8)[usable - 4096 - cnt: usable]
+    return ws.view(torch.uint8)[usable - 36864 - cnt: usable]
 
 
 def assert_counters_zero(ws, b, h):
