@@ -60,6 +60,10 @@ struct Shape {
   static constexpr int U = NL < UMAX ? NL : UMAX;   // loads in flight per lane
   static constexpr int NSUB = NL / U;
   static_assert(NL % U == 0, "sub-batches must tile the 32-position tile");
+  // Sub-batches unrolled in a tile: all of them, except with 256-dim rows
+  // (one row per wave load, 32 sub-batches of loads), where unrolling lets
+  // the compiler hoist later sub-batches' loads and run out of registers.
+  static constexpr int SB_UNROLL = D >= 256 ? 1 : NSUB;
 };
 
 template <typename T, int D, int HB>
@@ -89,7 +93,7 @@ __device__ __forceinline__ void tile_step(VState<T, D, HB>& st, const float (&qf
                                           const NewRow<T>& nr, const int* lim = nullptr) {
   using S = Shape<T, D, HB>;
   constexpr int VEC = S::VEC, U = S::U, RPW = S::RPW, R = S::R;
-#pragma unroll
+#pragma unroll S::SB_UNROLL
   for (int sb = 0; sb < S::NSUB; ++sb) {
     u32x4 kr[U], vr[U];
     bool ok[U];
