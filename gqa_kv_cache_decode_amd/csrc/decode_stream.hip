@@ -1,10 +1,14 @@
 // Matrix-core decode attention for up to 32 query heads per KV head (one or
-// two 16-column MFMA blocks), bf16 K/V/q, d_k = d_v = 128, one query token
-// per sequence, at most 64 sequences: the Llama-3-70B- and Qwen2.5-7B-shaped
-// GQA steps and the 32-head MQA ones. Same result as the other decode kernels (MQA review §2.1 per query
-// head over the cache of §2.4 / §3; contiguous head groups of the TF2 GQA
-// lesson); the per-tile arithmetic is the one of decode_matrix.hip (scores
-// K·Q^T and output P·V on v_mfma_f32_16x16x32_bf16, base-2 softmax).
+// two 16-column MFMA blocks), bf16 K/V/q, d_k = d_v = 128, at most 64
+// sequences: the Llama-3-70B- and Qwen2.5-7B-shaped GQA steps and the
+// 32-head MQA ones with one query token per sequence, and causal calls with
+// n query tokens per sequence whose n * G "virtual heads" fit in 32 (each
+// token's heads see the cache and the new positions up to its own; MQA
+// review §2.3, batched form with its mask). Same result as the other decode
+// kernels (MQA review §2.1 per query head over the cache of §2.4 / §3;
+// contiguous head groups of the TF2 GQA lesson); the per-tile arithmetic is
+// the one of decode_matrix.hip (scores K·Q^T and output P·V on
+// v_mfma_f32_16x16x32_bf16, base-2 softmax).
 //
 // What differs is how a workgroup walks its work, shaped by the measured
 // timeline of the earlier schedule (per-workgroup clock stamps on the
@@ -150,12 +154,14 @@ __device__ __forceinline__ void load_tile(Tile& t, const uint16_t* kb, const uin
 // of its weights 2^(s - m) (rounded to bf16, as applied), o = their
 // weighted sum of V rows. Lane (n16, q4) holds head 16 b + n16 of block b:
 // o[b][e][i] = dim 32 q4 + 8 i + e; m and l are the same in the head's four
-// lanes. Rows >= nvalid are masked unless FULL. The K rows and the
-// transposed V operands are shared by the blocks.
+// lanes. Unless FULL, the rows of block b at or past lim[b] are masked
+// (lim[b] <= the tile's valid rows; below them only for a causal
+// multi-token call). The K rows and the transposed V operands are shared by
+// the blocks.
 template <bool FULL, int NB>
 __device__ __forceinline__ void tile_state(f32x4 (&o)[NB][8], float (&m)[NB], float (&l)[NB],
-                                           const bf16x8 (&qop)[NB][4], const Tile& t, int nvalid, float sl2,
-                                           int q4) {
+                                           const bf16x8 (&qop)[NB][4], const Tile& t, const int (&lim)[NB],
+                                           float sl2, int q4) {
   bf16x8 pk[NB];
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
@@ -169,7 +175,7 @@ __device__ __forceinline__ void tile_state(f32x4 (&o)[NB][8], float (&m)[NB], fl
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int row = 16 * sg + 4 * q4 + i;
-        sv[sg * 4 + i] = (FULL || row < nvalid) ? sacc[i] * sl2 : kNegInf;
+        sv[sg * 4 + i] = (FULL || row < lim[b]) ? sacc[i] * sl2 : kNegInf;
       }
     }
     float mx = sv[0];
@@ -240,6 +246,16 @@ __device__ Range locate(const DecodeParams& p, int Lreg, int wg) {
 // Next piece of the range (lengths from the lane registers via shuffles).
 __device__ __forceinline__ bool next_piece(const DecodeParams& p, Range& r, int Lreg, StreamPiece& pc) {
   return sched::next_piece<1>([Lreg](int s) { return uni(__shfl(Lreg, s, 64)); }, p.b, p.g, p.seg_lead, r, pc);
+}
+
+// Row in q and out of (virtual) head hh of KV group j of sequence s, GV
+// heads per group: s * h + j * GV + hh for one query token per sequence;
+// for a causal multi-token call virtual head hh is token hh / G's head
+// j * G + hh mod G (head_row).
+template <bool CAUSAL>
+__device__ __forceinline__ size_t vrow(const DecodeParams& p, int s, int j, int GV, int hh) {
+  if constexpr (CAUSAL) return head_row(p.n_tok, p.h, p.G, s, j * GV + hh);
+  else return size_t(s) * p.h + size_t(j) * GV + hh;
 }
 
 // Byte offset of partial slot `slot` of workgroup `wg`.
@@ -353,13 +369,13 @@ __device__ void wait_parts(const DecodeParams& p, int p0, int n_slots, int own, 
 // slot 0 of p0 + 1 .. p0 + n_slots - 1), with part `own` taken from this
 // wave's registers, up to B parts' loads in flight at a time; then the
 // output rows. Lane layout as in fold_range, heads from h0.
-template <int NCH>
+template <int NCH, bool CAUSAL>
 __device__ void merge_parts(const DecodeParams& p, int s, int j, int p0, int n_slots, int own, int h0,
                             const f32x4 (&own_o)[NCH], float own_m, float own_l) {
   constexpr int HP = (kD / 4) / NCH;
   constexpr int B = fast_slots<NCH>();
   const int lane = threadIdx.x & 63;
-  const int G = p.G;
+  const int G = p.gblk;
   const int hh = h0 + lane / HP;
   const int sub = lane % HP;
   if (hh >= G) return;
@@ -397,7 +413,7 @@ __device__ void merge_parts(const DecodeParams& p, int s, int j, int p0, int n_s
     }
   }
   const float inv = den > 0.0f ? 1.0f / den : 0.0f;
-  uint16_t* out = static_cast<uint16_t*>(p.out) + (size_t(s) * p.h + size_t(j) * G + hh) * kD;
+  uint16_t* out = static_cast<uint16_t*>(p.out) + vrow<CAUSAL>(p, s, j, G, hh) * kD;
 #pragma unroll
   for (int i = 0; i < NCH; ++i) *reinterpret_cast<uint2*>(out + 4 * (sub + HP * i)) = to_bf16x4(res[i] * inv);
 }
@@ -415,7 +431,7 @@ __device__ void merge_parts(const DecodeParams& p, int s, int j, int p0, int n_s
 // and its four-dim columns c = (l mod HP) + HP i, i < NCH, so each lane
 // weighs a single head per tile. The ring has ring_slots<NB>() slots of
 // 16 NB heads; s_folded[hb] counts the tiles block hb has folded.
-template <int NCH, bool FUSED, int NB>
+template <int NCH, bool FUSED, int NB, bool CAUSAL>
 __device__ void fold_range(const DecodeParams& p, const Range& range, int Lreg, int hb,
                            float (*s_o)[kBlockHeads * NB * kRow], float (*s_m)[kBlockHeads * NB],
                            float (*s_l)[kBlockHeads * NB], int* s_ready, int* s_folded, int (*s_tk)[16],
@@ -425,7 +441,7 @@ __device__ void fold_range(const DecodeParams& p, const Range& range, int Lreg, 
   constexpr int kRing = ring_slots<NB>();
   const int wg = blockIdx.x;
   const int lane = threadIdx.x & 63;
-  const int G = p.G;
+  const int G = p.gblk;  // (virtual) heads per KV group
   const int h0 = kBlockHeads * hb;
   const int hh = h0 + lane / HP;
   const int sub = lane % HP;
@@ -510,7 +526,7 @@ __device__ void fold_range(const DecodeParams& p, const Range& range, int Lreg, 
     // the piece is complete
     if (!shared) {
       if (active) {
-        uint16_t* out = static_cast<uint16_t*>(p.out) + (size_t(s) * p.h + size_t(j) * G + hh) * kD;
+        uint16_t* out = static_cast<uint16_t*>(p.out) + vrow<CAUSAL>(p, s, j, G, hh) * kD;
         const float inv = al > 0.0f ? 1.0f / al : 0.0f;
 #pragma unroll
         for (int i = 0; i < NCH; ++i) *reinterpret_cast<uint2*>(out + 4 * (sub + HP * i)) = to_bf16x4(acc[i] * inv);
@@ -536,7 +552,7 @@ __device__ void fold_range(const DecodeParams& p, const Range& range, int Lreg, 
       // the last part: merge once the others' states are in their slots, and
       // leave the ticket and their flags at zero
       wait_parts(p, pc.p0, n_slots, own, hb);
-      merge_parts<NCH>(p, s, j, pc.p0, n_slots, own, h0, acc, am, al);
+      merge_parts<NCH, CAUSAL>(p, s, j, pc.p0, n_slots, own, h0, acc, am, al);
       if (lane < n_slots && lane != own)
         __hip_atomic_store(slot_flag(p, pc.p0 + lane, lane == 0 ? 1 : 0, hb), 0, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
@@ -570,7 +586,7 @@ __device__ void fold_range(const DecodeParams& p, const Range& range, int Lreg, 
   }
 }
 
-template <bool FUSED, bool PAGED, int NB>
+template <bool FUSED, bool PAGED, int NB, bool CAUSAL>
 __global__ __launch_bounds__(kBlockThreads, 1) void decode_stream_kernel(DecodeParams p) {
   constexpr int kRing = ring_slots<NB>();
   constexpr int kHeads = kBlockHeads * NB;
@@ -589,7 +605,7 @@ __global__ __launch_bounds__(kBlockThreads, 1) void decode_stream_kernel(DecodeP
   const int w = threadIdx.x >> 6;
   const int n16 = lane & 15;
   const int q4 = lane >> 4;
-  const int G = p.G;
+  const int G = p.gblk;  // (virtual) heads per KV group
   const float sl2 = p.scale_log2;
 
   if (w == 0) s_lens[lane] = lane < p.b ? attended_len(p, lane) : 0;
@@ -597,7 +613,7 @@ __global__ __launch_bounds__(kBlockThreads, 1) void decode_stream_kernel(DecodeP
   if (threadIdx.x < NB) s_folded[threadIdx.x] = 0;
   if (threadIdx.x < 16) s_tk[1][threadIdx.x] = 0;
   if (threadIdx.x == 0) s_next = 0;
-  if (!FUSED) zero_empty_sequences<uint16_t, false>(p, wg);
+  if (!FUSED) zero_empty_sequences<uint16_t, CAUSAL>(p, wg);
   __syncthreads();
 
   const int Lreg = s_lens[lane];
@@ -654,22 +670,40 @@ __global__ __launch_bounds__(kBlockThreads, 1) void decode_stream_kernel(DecodeP
       const int seg = s * p.g + j;
       if (seg != q_seg) {
         // the group's query rows, after the tile's loads are on their way
-        const uint16_t* qg = static_cast<const uint16_t*>(p.q) + (size_t(s) * p.h + size_t(j) * G) * kD;
 #pragma unroll
-        for (int b = 0; b < NB; ++b)
+        for (int b = 0; b < NB; ++b) {
+          const int head = kBlockHeads * b + n16;
+          const uint16_t* qrow = static_cast<const uint16_t*>(p.q) + vrow<CAUSAL>(p, s, j, G, head) * kD;
 #pragma unroll
           for (int ks = 0; ks < 4; ++ks) {
-            const int head = kBlockHeads * b + n16;
             u32x4 v = {0u, 0u, 0u, 0u};
-            if (head < G) v = ld16(qg + size_t(head) * kD + ks * 32 + q4 * 8);
+            if (head < G) v = ld16(qrow + ks * 32 + q4 * 8);
             qop[b][ks] = as_bf16x8(v);
           }
+        }
         q_seg = seg;
       }
+      // rows each head block sees: the tile's valid rows, and for a causal
+      // multi-token call only those before its token's position (virtual
+      // head v is token v / G_real, which sees n_tok - 1 - v / G_real fewer
+      // of the last positions; padding heads as many as the last token)
+      int lim[NB];
+      bool full = nvalid >= kTile;
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        lim[b] = nvalid < kTile ? nvalid : kTile;
+        if constexpr (CAUSAL) {
+          const int head = kBlockHeads * b + n16;
+          const int hide = head < G ? p.n_tok - 1 - head / p.G : 0;
+          const int seen = pc.L - t0 - hide;
+          lim[b] = seen < lim[b] ? seen : lim[b];
+        }
+      }
+      if constexpr (CAUSAL) full = full && pc.L - t0 - (p.n_tok - 1) >= kTile;
       f32x4 o[NB][8];
       float m[NB], l[NB];
-      if (nvalid >= kTile) tile_state<true, NB>(o, m, l, qop, t, kTile, sl2, q4);
-      else tile_state<false, NB>(o, m, l, qop, t, nvalid, sl2, q4);
+      if (full) tile_state<true, NB>(o, m, l, qop, t, lim, sl2, q4);
+      else tile_state<false, NB>(o, m, l, qop, t, lim, sl2, q4);
       // slot k mod kRing is free once tile k - kRing has been folded
       const int slot = k & (kRing - 1);
       // (by every head block's folding wave)
@@ -708,30 +742,32 @@ __global__ __launch_bounds__(kBlockThreads, 1) void decode_stream_kernel(DecodeP
 
   // ---- folding waves (one per block of 16 heads; lane layout by the heads in use)
   if constexpr (NB == 1) {
-    if (G <= 4) fold_range<2, FUSED, NB>(p, range, Lreg, 0, s_o, s_m, s_l, s_ready, s_folded, s_tk, s_lens);
-    else if (G <= 8) fold_range<4, FUSED, NB>(p, range, Lreg, 0, s_o, s_m, s_l, s_ready, s_folded, s_tk, s_lens);
-    else fold_range<8, FUSED, NB>(p, range, Lreg, 0, s_o, s_m, s_l, s_ready, s_folded, s_tk, s_lens);
+    if (G <= 4) fold_range<2, FUSED, NB, CAUSAL>(p, range, Lreg, 0, s_o, s_m, s_l, s_ready, s_folded, s_tk, s_lens);
+    else if (G <= 8) fold_range<4, FUSED, NB, CAUSAL>(p, range, Lreg, 0, s_o, s_m, s_l, s_ready, s_folded, s_tk, s_lens);
+    else fold_range<8, FUSED, NB, CAUSAL>(p, range, Lreg, 0, s_o, s_m, s_l, s_ready, s_folded, s_tk, s_lens);
   } else {
-    fold_range<8, FUSED, NB>(p, range, Lreg, w - kStreamers, s_o, s_m, s_l, s_ready, s_folded, s_tk, s_lens);
+    fold_range<8, FUSED, NB, CAUSAL>(p, range, Lreg, w - kStreamers, s_o, s_m, s_l, s_ready, s_folded, s_tk,
+                                     s_lens);
   }
 }
 
-template <bool FUSED, bool PAGED>
+template <bool FUSED, bool PAGED, bool CAUSAL>
 void launch(const DecodeParams& p, hipStream_t stream) {
-  if (p.G <= kBlockHeads)
-    hipLaunchKernelGGL((decode_stream_kernel<FUSED, PAGED, 1>), dim3(p.workgroups), dim3(kBlockThreads), 0, stream,
-                       p);
+  if (p.gblk <= kBlockHeads)
+    hipLaunchKernelGGL((decode_stream_kernel<FUSED, PAGED, 1, CAUSAL>), dim3(p.workgroups), dim3(kBlockThreads), 0,
+                       stream, p);
   else
-    hipLaunchKernelGGL((decode_stream_kernel<FUSED, PAGED, 2>), dim3(p.workgroups), dim3(kBlockThreads), 0, stream,
-                       p);
+    hipLaunchKernelGGL((decode_stream_kernel<FUSED, PAGED, 2, CAUSAL>), dim3(p.workgroups), dim3(kBlockThreads), 0,
+                       stream, p);
 }
 
 }  // namespace
 
 hipError_t launch_decode_stream(const DecodeParams& p, hipStream_t stream) {
   const bool paged = p.pg.table != nullptr;
-  if (p.fused) paged ? launch<true, true>(p, stream) : launch<true, false>(p, stream);
-  else paged ? launch<false, true>(p, stream) : launch<false, false>(p, stream);
+  if (p.n_tok > 1) paged ? launch<false, true, true>(p, stream) : launch<false, false, true>(p, stream);
+  else if (p.fused) paged ? launch<true, true, false>(p, stream) : launch<true, false, false>(p, stream);
+  else paged ? launch<false, true, false>(p, stream) : launch<false, false, false>(p, stream);
   return hipGetLastError();
 }
 
@@ -746,14 +782,14 @@ int stream_workgroups_per_cu(bool fused, bool paged, int G) {
   int n = 0;
   hipError_t e;
   switch (k) {
-    case 0: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_stream_kernel<false, false, 1>, kBlockThreads, 0); break;
-    case 1: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_stream_kernel<true, false, 1>, kBlockThreads, 0); break;
-    case 2: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_stream_kernel<false, true, 1>, kBlockThreads, 0); break;
-    case 3: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_stream_kernel<true, true, 1>, kBlockThreads, 0); break;
-    case 4: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_stream_kernel<false, false, 2>, kBlockThreads, 0); break;
-    case 5: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_stream_kernel<true, false, 2>, kBlockThreads, 0); break;
-    case 6: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_stream_kernel<false, true, 2>, kBlockThreads, 0); break;
-    default: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_stream_kernel<true, true, 2>, kBlockThreads, 0); break;
+    case 0: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_stream_kernel<false, false, 1, false>, kBlockThreads, 0); break;
+    case 1: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_stream_kernel<true, false, 1, false>, kBlockThreads, 0); break;
+    case 2: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_stream_kernel<false, true, 1, false>, kBlockThreads, 0); break;
+    case 3: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_stream_kernel<true, true, 1, false>, kBlockThreads, 0); break;
+    case 4: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_stream_kernel<false, false, 2, false>, kBlockThreads, 0); break;
+    case 5: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_stream_kernel<true, false, 2, false>, kBlockThreads, 0); break;
+    case 6: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_stream_kernel<false, true, 2, false>, kBlockThreads, 0); break;
+    default: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_stream_kernel<true, true, 2, false>, kBlockThreads, 0); break;
   }
   if (e != hipSuccess || n <= 0) {
     (void)hipGetLastError();

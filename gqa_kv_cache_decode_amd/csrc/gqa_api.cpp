@@ -128,9 +128,9 @@ int plan_decode(int b, int h, int g, int d_k, int d_v, int cap, int max_len, int
     plan->gblk = gqa::vector_heads_per_block(G);
     plan->nhb = (G + plan->gblk - 1) / plan->gblk;
   }
-  // One query token, at most 32 heads per KV head and 64 sequences: the
-  // stream kernel (tile-granular schedule, waves finishing pieces on their own).
-  plan->stream = chosen == GQA_PATH_MATRIX && !causal && G <= gqa::kStreamMaxGroup && b <= gqa::kStreamMaxBatch;
+  // At most 32 (virtual) heads per KV head and 64 sequences: the stream
+  // kernel (tile-granular schedule, waves finishing pieces on their own).
+  plan->stream = chosen == GQA_PATH_MATRIX && G <= gqa::kStreamMaxGroup && b <= gqa::kStreamMaxBatch;
   const int waves = plan->stream ? 8
                     : chosen == GQA_PATH_MATRIX ? gqa::matrix_waves(G) : gqa::vector_waves(dtype, d_k, plan->gblk);
   const int unit_len = plan->stream ? gqa::kTile : gqa::kTile * gqa::kUnitTiles;

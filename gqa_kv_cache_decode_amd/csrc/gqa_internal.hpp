@@ -185,8 +185,9 @@ constexpr int kMergeLds = 2 * kMergePairs + 3 * kMatrixMaxGroup;
 hipError_t launch_append(const AppendParams& p, int b, int dtype, hipStream_t stream);
 hipError_t launch_decode_vector(const DecodeParams& p, int dtype, hipStream_t stream);
 hipError_t launch_decode_matrix(const DecodeParams& p, hipStream_t stream);
-// One-token matrix decode for up to 32 heads per KV head and up to 64
-// sequences (decode_stream.hip); seg_lead counts empty tiles there.
+// Matrix decode for up to 32 (virtual) heads per KV head and up to 64
+// sequences (decode_stream.hip), one query token per sequence or a causal
+// multi-token call; seg_lead counts empty tiles there.
 constexpr int kStreamMaxGroup = 32;
 constexpr int kStreamMaxBatch = 64;
 hipError_t launch_decode_stream(const DecodeParams& p, hipStream_t stream);
