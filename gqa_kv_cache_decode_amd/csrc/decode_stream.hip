@@ -641,18 +641,36 @@ __global__ __launch_bounds__(kBlockThreads, 1) void decode_stream_kernel(DecodeP
       const int tile = pc.tile_begin + int(k - kb);
       const int t0 = tile * kTile;
       const int nvalid = pc.L - t0;
-      if (FUSED && nvalid <= kTile) {
-        // the segment's last tile holds the appended token: store its rows
-        // into their cache slot, wait for the stores, then read the tile
-        const size_t new_row = kv_row<PAGED, true>(p.pg, p.g, p.cap, s, j, pc.L - 1);
-        // lanes 0-15 copy the K row, lanes 16-31 the V row (uniform bases,
-        // per-lane 16-byte offsets)
-        if (lane < 16)
-          st16(static_cast<uint16_t*>(p.k_cache) + new_row * kD + 8 * lane,
-               ld16(static_cast<const uint16_t*>(p.k_new) + kv_head * kD + 8 * lane));
-        else if (lane < 32)
-          st16(static_cast<uint16_t*>(p.v_cache) + new_row * kD + 8 * (lane - 16),
-               ld16(static_cast<const uint16_t*>(p.v_new) + kv_head * kD + 8 * (lane - 16)));
+      // fused step: the appended tokens are the segment's last p.fused
+      // positions; a tile holding any of them stores their rows (token r of
+      // sequence s from k_new / v_new [b][n][g][d]) into their cache slots,
+      // waits for the stores, then reads the tile. Lanes l and l + 32 take
+      // two consecutive positions, lanes 0-15 of each half the K row and
+      // lanes 16-31 the V row; up to eight rows' loads are issued before the
+      // first store, so that the rows cost one round trip, not one each.
+      const int first_new = pc.L - p.fused;
+      if (FUSED && t0 + kTile > first_new) {
+        const int n_new = p.fused;
+        const int pos0 = t0 > first_new ? t0 : first_new;
+        const int pos_end = pc.L < t0 + kTile ? pc.L : t0 + kTile;
+        const bool is_v = (lane & 16) != 0;
+        const int col = 8 * (lane & 15);
+        const uint16_t* src_base = static_cast<const uint16_t*>(is_v ? p.v_new : p.k_new);
+        uint16_t* dst_base = static_cast<uint16_t*>(is_v ? p.v_cache : p.k_cache);
+        for (int base = pos0; base < pos_end; base += 8) {
+          u32x4 row[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int pos = base + 2 * i + (lane >> 5);
+            if (pos < pos_end)
+              row[i] = ld16(src_base + ((size_t(s) * n_new + (pos - first_new)) * p.g + j) * kD + col);
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int pos = base + 2 * i + (lane >> 5);
+            if (pos < pos_end) st16(dst_base + kv_row<PAGED, true>(p.pg, p.g, p.cap, s, j, pos) * kD + col, row[i]);
+          }
+        }
         wait_stores();
       }
       const uint16_t* kbp;
@@ -765,9 +783,13 @@ void launch(const DecodeParams& p, hipStream_t stream) {
 
 hipError_t launch_decode_stream(const DecodeParams& p, hipStream_t stream) {
   const bool paged = p.pg.table != nullptr;
-  if (p.n_tok > 1) paged ? launch<false, true, true>(p, stream) : launch<false, false, true>(p, stream);
-  else if (p.fused) paged ? launch<true, true, false>(p, stream) : launch<true, false, false>(p, stream);
-  else paged ? launch<false, true, false>(p, stream) : launch<false, false, false>(p, stream);
+  if (p.n_tok > 1) {
+    if (p.fused) paged ? launch<true, true, true>(p, stream) : launch<true, false, true>(p, stream);
+    else paged ? launch<false, true, true>(p, stream) : launch<false, false, true>(p, stream);
+  } else {
+    if (p.fused) paged ? launch<true, true, false>(p, stream) : launch<true, false, false>(p, stream);
+    else paged ? launch<false, true, false>(p, stream) : launch<false, false, false>(p, stream);
+  }
   return hipGetLastError();
 }
 

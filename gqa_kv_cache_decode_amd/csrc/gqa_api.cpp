@@ -531,10 +531,13 @@ int paged_check(const char* fn, const int32_t* table, int b, int block_size, int
 // Checks and launch parameters of a multi-token attention (nothing enqueued).
 // The n tokens of a KV group are its n * G virtual heads: planned and laid
 // out as a one-token call with n * h heads, then addressed through head_row.
+// fused: the step's n appended rows are stored by the attention launch
+// itself (k_new, v_new; the stream kernel only).
 int multi_prepare(const char* fn, void* out, const void* q, const void* k_cache, const void* v_cache,
                   const int32_t* lens, int b, int n, int h, int g, int d_k, int d_v, int cap, int max_len, float scale,
                   int dtype, void* workspace, size_t workspace_bytes, gqa::DecodeParams* p, Plan* plan,
-                  const gqa::PagedLayout* pg = nullptr) {
+                  const gqa::PagedLayout* pg = nullptr, const void* k_new = nullptr, const void* v_new = nullptr,
+                  bool fused = false) {
   if (!out || !q || !k_cache || !v_cache || !lens) return fail(GQA_ERR_ARG, "%s: null pointer argument", fn);
   if (n <= 0 || n > kMaxTokens) return fail(GQA_ERR_ARG, "%s: n=%d must be in [1, %d]", fn, n, kMaxTokens);
   if (h <= 0 || g <= 0 || (long long)n * h > kMaxHeads)
@@ -543,8 +546,8 @@ int multi_prepare(const char* fn, void* out, const void* q, const void* k_cache,
   // planned like a one-token call with n * h heads: the matrix path when it
   // applies (bf16, d = 128, n * h/g in [3, 64]), else the vector path
   const int rc = decode_prepare(fn, out, q, const_cast<void*>(k_cache), const_cast<void*>(v_cache),
-                                const_cast<int32_t*>(lens), nullptr, nullptr, b, n * h, g, d_k, d_v, cap, max_len,
-                                scale, dtype, workspace, workspace_bytes, GQA_PATH_AUTO, 0, 0, p, plan, pg,
+                                const_cast<int32_t*>(lens), k_new, v_new, b, n * h, g, d_k, d_v, cap, max_len,
+                                scale, dtype, workspace, workspace_bytes, GQA_PATH_AUTO, 0, fused ? n : 0, p, plan, pg,
                                 n > 1);
   if (rc != GQA_OK) return rc;
   p->h = h;
@@ -681,6 +684,12 @@ int gqa_decode_step_multi(void* out, const void* q, const void* k_new, const voi
   int rc = multi_prepare(fn, out, q, k_cache, v_cache, lens, b, n, h, g, d_k, d_v, cap, max_len + n, scale, dtype,
                          workspace, workspace_bytes, &p, &plan);
   if (rc != GQA_OK) return rc;
+  if (plan.stream) {  // one launch: the tiles holding the new positions store the new rows first
+    rc = multi_prepare(fn, out, q, k_cache, v_cache, lens, b, n, h, g, d_k, d_v, cap, max_len + n, scale, dtype,
+                       workspace, workspace_bytes, &p, &plan, nullptr, k_new, v_new, true);
+    if (rc != GQA_OK) return rc;
+    return decode_launch(fn, p, plan, dtype, stream);
+  }
   rc = gqa_kv_append_multi(k_cache, v_cache, k_new, v_new, lens, b, n, g, d_k, d_v, cap, max_len, dtype, stream);
   if (rc != GQA_OK) return rc;
   return decode_launch(fn, p, plan, dtype, stream);
@@ -731,6 +740,12 @@ int gqa_decode_step_multi_paged(void* out, const void* q, const void* k_new, con
   rc = multi_prepare(fn, out, q, k_pool, v_pool, lens, b, n, h, g, d_k, d_v, cap, max_len + n, scale, dtype,
                      workspace, workspace_bytes, &p, &plan, &pg);
   if (rc != GQA_OK) return rc;
+  if (plan.stream) {  // one launch, as in gqa_decode_step_multi
+    rc = multi_prepare(fn, out, q, k_pool, v_pool, lens, b, n, h, g, d_k, d_v, cap, max_len + n, scale, dtype,
+                       workspace, workspace_bytes, &p, &plan, &pg, k_new, v_new, true);
+    if (rc != GQA_OK) return rc;
+    return decode_launch(fn, p, plan, dtype, stream);
+  }
   rc = append_multi(fn, k_pool, v_pool, k_new, v_new, lens, b, n, g, d_k, d_v, cap, max_len, dtype, stream, pg);
   if (rc != GQA_OK) return rc;
   return decode_launch(fn, p, plan, dtype, stream);
