@@ -20,22 +20,25 @@
 //
 // * The static split of the (sequence, KV head) segments over the persistent
 //   workgroups is balanced to one 32-position tile (16 KiB), not four.
-// * Inside a workgroup, seven streaming waves take the range's tiles one at a
-//   time from an LDS counter, so a wave that is served faster takes more
-//   tiles and all finish together. Each tile's split-softmax state (max m,
-//   sum of weights l, unnormalised output o) is computed from scratch, so it
-//   does not depend on which wave computed it.
-// * The eighth wave folds the tile states in tile order out of an LDS ring
-//   (m = max, o and l rescaled by 2^(m_k - m)), which fixes the arithmetic:
-//   results are bit for bit the same whichever wave took which tile. It also
-//   writes, publishes or merges each finished piece, so the streaming waves
-//   never stop for that.
+// * Inside a workgroup, the streaming waves (seven; six with two head
+//   blocks) take the range's tiles one at a time from an LDS counter, so a
+//   wave that is served faster takes more tiles and all finish together.
+//   Each tile's split-softmax state (max m, sum of weights l, unnormalised
+//   output o) is computed from scratch, so it does not depend on which wave
+//   computed it.
+// * A folding wave per block of 16 heads folds the tile states in tile order
+//   out of an LDS ring (m = max, o and l rescaled by 2^(m_k - m)), which
+//   fixes the arithmetic: results are bit for bit the same whichever wave
+//   took which tile. It also writes, publishes or merges each finished
+//   piece, so the streaming waves never stop for that.
 // * A tile's K/V loads are issued before the query rows it needs.
-// * Fused step: the grown lengths can be written as soon as every workgroup
-//   has read the old ones, which all do at their start. The folding wave of
-//   each workgroup counts it out right after that read on one of 16
-//   counters, and the last of each group on one more, so no more than 16
-//   atomics meet on one address and none waits at the end of the launch.
+// * Fused step: a tile holding appended positions first stores their rows
+//   into the cache. The grown lengths can be written as soon as every
+//   workgroup has read the old ones, which all do at their start. The
+//   folding wave of each workgroup counts it out right after that read on
+//   one of 16 counters, and the last of each group on one more, so no more
+//   than 16 atomics meet on one address and none waits at the end of the
+//   launch.
 //
 // Split segments (a segment whose tiles fall in the ranges of several
 // workgroups, its "parts") are merged by the part that counts in last, with
