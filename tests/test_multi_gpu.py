@@ -129,6 +129,29 @@ def test_one_token_multi_equals_the_one_token_call(gpu_lib):
     assert torch.equal(out[:, 0].view(torch.int16), ref.view(torch.int16))
 
 
+@pytest.mark.parametrize("b,h,g,n,lens", [(3, 64, 8, 4, [1, 29, 511]), (4, 28, 4, 3, [0, 62, 63, 200]),
+                                           (3, 64, 8, 2, [0, 31, 300])])
+def test_multi_step_equals_append_then_attention(gpu_lib, b, h, g, n, lens):
+    # the one-launch step (new rows stored by the tiles that hold them) and the
+    # two calls give the same bits: the same tile states folded in the same order
+    print(f"multi-token step against the two calls: h={h} g={g} n={n} lens={lens}", flush=True)
+    one = MultiProblem(b, h, g, n, lens, seed=1450 + n)
+    two = MultiProblem(b, h, g, n, lens, seed=1450 + n)
+    q, kn, vn = one.draw_step()
+    max_len = int(one.lens_h.max())
+    out1 = torch.empty(b, n, h, 128, dtype=torch.bfloat16, device="cuda")
+    out2 = torch.empty_like(out1)
+    api.decode_step_multi(out1, to_dev(q), to_dev(kn), to_dev(vn), one.kc, one.vc, one.lens, max_len, one.scale,
+                          one.ws)
+    api.kv_append_multi(two.kc, two.vc, to_dev(kn), to_dev(vn), two.lens, max_len)
+    api.decode_attention_multi(out2, to_dev(q), two.kc, two.vc, two.lens, max_len + n, two.scale, two.ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out1.view(torch.int16), out2.view(torch.int16))
+    assert torch.equal(one.lens, two.lens)
+    assert torch.equal(one.kc.view(torch.int16), two.kc.view(torch.int16))
+    assert torch.equal(one.vc.view(torch.int16), two.vc.view(torch.int16))
+
+
 def test_multi_rejects(gpu_lib):
     pb = MultiProblem(2, 64, 8, 2, [10, 20], seed=1500)
     q = torch.zeros(2, 2, 64, 128, dtype=torch.bfloat16, device="cuda")
