@@ -1,8 +1,8 @@
-// Matrix-core decode attention for up to 32 query heads per KV head (one or
-// two 16-column MFMA blocks), bf16 K/V/q, d_k = d_v = 128, at most 64
+// Matrix-core decode attention for up to 64 query heads per KV head (one,
+// two or four 16-column MFMA blocks), bf16 K/V/q, d_k = d_v = 128, at most 64
 // sequences: the Llama-3-70B- and Qwen2.5-7B-shaped GQA steps and the
 // 32-head MQA ones with one query token per sequence, and causal calls with
-// n query tokens per sequence whose n * G "virtual heads" fit in 32 (each
+// n query tokens per sequence whose n * G "virtual heads" fit in 64 (each
 // token's heads see the cache and the new positions up to its own; MQA
 // review §2.3, batched form with its mask). Same result as the other decode
 // kernels (MQA review §2.1 per query head over the cache of §2.4 / §3;
@@ -20,8 +20,8 @@
 //
 // * The static split of the (sequence, KV head) segments over the persistent
 //   workgroups is balanced to one 32-position tile (16 KiB), not four.
-// * Inside a workgroup, the streaming waves (seven; six with two head
-//   blocks) take the range's tiles one at a time from an LDS counter, so a
+// * Inside a workgroup, the streaming waves (seven; six or four with two or
+//   four head blocks) take the range's tiles one at a time from an LDS counter, so a
 //   wave that is served faster takes more tiles and all finish together.
 //   Each tile's split-softmax state (max m, sum of weights l, unnormalised
 //   output o) is computed from scratch, so it does not depend on which wave
@@ -70,19 +70,23 @@ constexpr int kWaves = 8;
 constexpr int kBlockThreads = kWaves * 64;
 constexpr int kBlockHeads = 16;     // query heads of one MFMA column block
 constexpr int kRow = kD + 4;        // LDS row stride (floats), padded against bank conflicts
-// Tile states in the LDS ring with NB column blocks of heads (NB = 1: up to
-// 16 heads per KV head, NB = 2: up to 32); either way about 135 KB of LDS.
+// Tile states in the LDS ring with NB column blocks of heads (NB = 1, 2, 4:
+// up to 16, 32, 64 heads per KV head); each way about 135 KB of LDS.
 template <int NB>
-constexpr int ring_slots() { return NB == 1 ? 16 : 8; }
+constexpr int ring_slots() { return NB == 1 ? 16 : (NB == 2 ? 8 : 4); }
+// Folding waves by head blocks: one per block of 16 heads for up to 32
+// heads, one per 32 heads for 64 (so that six waves stream, not four).
+template <int NB>
+constexpr int folders() { return NB == 4 ? 2 : NB; }
 constexpr int kCountTiles = 3;      // tiles before a piece's end at which it counts in on its ticket
 constexpr int kFlagSpins = 1 << 22; // bound of the wait for another part's ready flag
 // Parts of a segment whose states the merge holds in registers at once, by
 // columns per lane.
 template <int NCH>
-constexpr int fast_slots() { return NCH == 8 ? 2 : (NCH == 4 ? 5 : 9); }
+constexpr int fast_slots() { return NCH == 16 ? 1 : (NCH == 8 ? 2 : (NCH == 4 ? 5 : 9)); }
 // Ring slots the folding wave reads in one round, by columns per lane.
 template <int NCH>
-constexpr int fold_batch() { return NCH == 8 ? 2 : 4; }
+constexpr int fold_batch() { return NCH == 16 ? 1 : (NCH == 8 ? 2 : 4); }
 constexpr int kCountGroups = 16;    // first-level counters of the fused step's length update
 constexpr int kCountStride = 32;    // ints between counters (128 bytes)
 
@@ -163,8 +167,8 @@ __device__ __forceinline__ void load_tile(Tile& t, const uint16_t* kb, const uin
 // the blocks.
 template <bool FULL, int NB>
 __device__ __forceinline__ void tile_state(f32x4 (&o)[NB][8], float (&m)[NB], float (&l)[NB],
-                                           const bf16x8 (&qop)[NB][4], const Tile& t, const int (&lim)[NB],
-                                           float sl2, int q4) {
+                                           const bf16x8 (*qop)[4], const Tile& t, const int* lim, float sl2,
+                                           int q4) {
   bf16x8 pk[NB];
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
@@ -344,14 +348,14 @@ struct LenCount {
   }
 };
 
-// Ready flag of head block `half` of partial slot `slot` of workgroup `wg`
+// Ready flag of folding wave `half`'s heads in partial slot `slot` of workgroup `wg`
 // (zero between calls).
 __device__ __forceinline__ int* slot_flag(const DecodeParams& p, int wg, int slot, int half) {
-  return p.ws_done + kFlagsOffset / sizeof(int) + (wg * 2 + slot) * 2 + half;
+  return p.ws_done + kFlagsOffset / sizeof(int) + (wg * 2 + slot) * kFlagBlocks + half;
 }
 
-// The merging wave of head block `half` waits until every other part of
-// segment p0 .. p0 + n_slots - 1 has raised that block's ready flag (each
+// The merging folding wave `half` waits until every other part of segment
+// p0 .. p0 + n_slots - 1 has raised that wave's ready flag (each
 // part has already taken its ticket, so it is running and has only its own
 // tiles and stores left). The wait is bounded.
 __device__ void wait_parts(const DecodeParams& p, int p0, int n_slots, int own, int half) {
@@ -422,18 +426,19 @@ __device__ void merge_parts(const DecodeParams& p, int s, int j, int p0, int n_s
 }
 
 // A folding wave: fold the tile states of the workgroup's range in tile
-// order for the heads of its block and finish every piece for them (write
-// them out, publish them or merge them). With NB = 2 there is one folding
-// wave per block of 16 heads, each working alone on its heads with its own
-// ready flags; block 0's wave also counts the workgroup out for the fused
-// step's lengths and takes the piece tickets, and hands each ticket's result
-// to block 1's wave through LDS (s_tk: value and piece number, 16 pieces
-// deep; block 1 is never more than a ring's worth of tiles, hence of pieces,
-// behind block 0). Lane layout: HP = 32 / NCH lanes per head (NCH = 2, 4,
-// 8 for up to 4, 8, 16 heads per block); lane l holds head 16 hb + l / HP
-// and its four-dim columns c = (l mod HP) + HP i, i < NCH, so each lane
-// weighs a single head per tile. The ring has ring_slots<NB>() slots of
-// 16 NB heads; s_folded[hb] counts the tiles block hb has folded.
+// order for its heads and finish every piece for them (write them out,
+// publish them or merge them). With NB = 2 there is one folding wave per
+// block of 16 heads, with NB = 4 one per 32 heads, each working alone on
+// its heads with its own ready flags; wave 0 of them also counts the
+// workgroup out for the fused step's lengths and takes the piece tickets,
+// and hands each ticket's result to the other through LDS (s_tk: value and
+// piece number, 16 pieces deep; no folding wave is more than a ring's worth
+// of tiles, hence of pieces, behind wave 0). Lane layout: HP = 32 / NCH
+// lanes per head (NCH = 2, 4, 8, 16 for up to 4, 8, 16, 32 heads per
+// wave); lane l of folding wave hb holds head (64 / HP) hb + l / HP and its
+// four-dim columns c = (l mod HP) + HP i, i < NCH, so each lane weighs a
+// single head per tile. The ring has ring_slots<NB>() slots of 16 NB heads;
+// s_folded[hb] counts the tiles folding wave hb has folded.
 template <int NCH, bool FUSED, int NB, bool CAUSAL>
 __device__ void fold_range(const DecodeParams& p, const Range& range, int Lreg, int hb,
                            float (*s_o)[kBlockHeads * NB * kRow], float (*s_m)[kBlockHeads * NB],
@@ -445,7 +450,7 @@ __device__ void fold_range(const DecodeParams& p, const Range& range, int Lreg, 
   const int wg = blockIdx.x;
   const int lane = threadIdx.x & 63;
   const int G = p.gblk;  // (virtual) heads per KV group
-  const int h0 = kBlockHeads * hb;
+  const int h0 = (64 / HP) * hb;  // heads per folding wave: 64 / HP
   const int hh = h0 + lane / HP;
   const int sub = lane % HP;
   const bool active = hh < G;
@@ -599,9 +604,9 @@ __global__ __launch_bounds__(kBlockThreads, 1) void decode_stream_kernel(DecodeP
   __shared__ int s_ready[kRing];  // range tile index whose state a ring slot holds (-1: none yet)
   __shared__ int s_lens[64];
   __shared__ int s_next;          // next range tile to hand out
-  __shared__ int s_folded[NB];    // range tiles folded so far, per head block
-  __shared__ int s_tk[2][16];     // ticket results handed from block 0's folding wave to block 1's
-  constexpr int kStreamers = kWaves - NB;  // waves 0 .. kStreamers - 1 stream, one folding wave per head block
+  __shared__ int s_folded[folders<NB>()];  // range tiles folded so far, per folding wave
+  __shared__ int s_tk[2][16];     // ticket results handed from block 0's folding wave to the others
+  constexpr int kStreamers = kWaves - folders<NB>();  // waves 0 .. kStreamers - 1 stream, the others fold
 
   const int wg = blockIdx.x;
   const int lane = threadIdx.x & 63;
@@ -613,7 +618,7 @@ __global__ __launch_bounds__(kBlockThreads, 1) void decode_stream_kernel(DecodeP
 
   if (w == 0) s_lens[lane] = lane < p.b ? attended_len(p, lane) : 0;
   if (threadIdx.x < kRing) s_ready[threadIdx.x] = -1;
-  if (threadIdx.x < NB) s_folded[threadIdx.x] = 0;
+  if (threadIdx.x < folders<NB>()) s_folded[threadIdx.x] = 0;
   if (threadIdx.x < 16) s_tk[1][threadIdx.x] = 0;
   if (threadIdx.x == 0) s_next = 0;
   if (!FUSED) zero_empty_sequences<uint16_t, CAUSAL>(p, wg);
@@ -649,8 +654,9 @@ __global__ __launch_bounds__(kBlockThreads, 1) void decode_stream_kernel(DecodeP
       // sequence s from k_new / v_new [b][n][g][d]) into their cache slots,
       // waits for the stores, then reads the tile. Lanes l and l + 32 take
       // two consecutive positions, lanes 0-15 of each half the K row and
-      // lanes 16-31 the V row; up to eight rows' loads are issued before the
-      // first store, so that the rows cost one round trip, not one each.
+      // lanes 16-31 the V row; up to eight rows' loads (four with four head
+      // blocks, for registers) are issued before the first store, so that the
+      // rows cost one round trip, not one each.
       const int first_new = pc.L - p.fused;
       if (FUSED && t0 + kTile > first_new) {
         const int n_new = p.fused;
@@ -660,16 +666,17 @@ __global__ __launch_bounds__(kBlockThreads, 1) void decode_stream_kernel(DecodeP
         const int col = 8 * (lane & 15);
         const uint16_t* src_base = static_cast<const uint16_t*>(is_v ? p.v_new : p.k_new);
         uint16_t* dst_base = static_cast<uint16_t*>(is_v ? p.v_cache : p.k_cache);
-        for (int base = pos0; base < pos_end; base += 8) {
-          u32x4 row[4];
+        constexpr int kRowBatch = 4;
+        for (int base = pos0; base < pos_end; base += 2 * kRowBatch) {
+          u32x4 row[kRowBatch];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
+          for (int i = 0; i < kRowBatch; ++i) {
             const int pos = base + 2 * i + (lane >> 5);
             if (pos < pos_end)
               row[i] = ld16(src_base + ((size_t(s) * n_new + (pos - first_new)) * p.g + j) * kD + col);
           }
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
+          for (int i = 0; i < kRowBatch; ++i) {
             const int pos = base + 2 * i + (lane >> 5);
             if (pos < pos_end) st16(dst_base + kv_row<PAGED, true>(p.pg, p.g, p.cap, s, j, pos) * kD + col, row[i]);
           }
@@ -721,35 +728,45 @@ __global__ __launch_bounds__(kBlockThreads, 1) void decode_stream_kernel(DecodeP
         }
       }
       if constexpr (CAUSAL) full = full && pc.L - t0 - (p.n_tok - 1) >= kTile;
-      f32x4 o[NB][8];
-      float m[NB], l[NB];
-      if (full) tile_state<true, NB>(o, m, l, qop, t, lim, sl2, q4);
-      else tile_state<false, NB>(o, m, l, qop, t, lim, sl2, q4);
-      // slot k mod kRing is free once tile k - kRing has been folded
+      // the state is computed and deposited in one pass for one or two head
+      // blocks, in one pass per block for four (registers); the first pass
+      // is computed before the wait for the slot, so that the wait overlaps it
+      constexpr int BP = NB == 4 ? 1 : NB;
       const int slot = k & (kRing - 1);
-      // (by every head block's folding wave)
-      while (true) {
-        int folded = __hip_atomic_load(&s_folded[0], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP);
-        if constexpr (NB > 1) {
-          const int f1 = __hip_atomic_load(&s_folded[1], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP);
-          folded = f1 < folded ? f1 : folded;
-        }
-        if (folded > k - kRing) break;
-        __builtin_amdgcn_s_sleep(1);
-      }
 #pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        const int head = kBlockHeads * b + n16;
-        if (head < G) {
-          float* row = &s_o[slot][head * kRow + 32 * q4];
+      for (int bp = 0; bp < NB; bp += BP) {
+        f32x4 o[BP][8];
+        float m[BP], l[BP];
+        if (full) tile_state<true, BP>(o, m, l, &qop[bp], t, &lim[bp], sl2, q4);
+        else tile_state<false, BP>(o, m, l, &qop[bp], t, &lim[bp], sl2, q4);
+        if (bp == 0) {
+          // slot k mod kRing is free once tile k - kRing has been folded (by
+          // every head block's folding wave)
+          while (true) {
+            int folded = __hip_atomic_load(&s_folded[0], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            *reinterpret_cast<f32x4*>(row + 8 * i) = f32x4{o[b][0][i], o[b][1][i], o[b][2][i], o[b][3][i]};
-            *reinterpret_cast<f32x4*>(row + 8 * i + 4) = f32x4{o[b][4][i], o[b][5][i], o[b][6][i], o[b][7][i]};
+            for (int f = 1; f < folders<NB>(); ++f) {
+              const int ff = __hip_atomic_load(&s_folded[f], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP);
+              folded = ff < folded ? ff : folded;
+            }
+            if (folded > k - kRing) break;
+            __builtin_amdgcn_s_sleep(1);
           }
-          if (q4 == 0) {
-            s_m[slot][head] = m[b];
-            s_l[slot][head] = l[b];
+        }
+#pragma unroll
+        for (int b = 0; b < BP; ++b) {
+          const int head = kBlockHeads * (bp + b) + n16;
+          if (head < G) {
+            float* row = &s_o[slot][head * kRow + 32 * q4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              *reinterpret_cast<f32x4*>(row + 8 * i) = f32x4{o[b][0][i], o[b][1][i], o[b][2][i], o[b][3][i]};
+              *reinterpret_cast<f32x4*>(row + 8 * i + 4) = f32x4{o[b][4][i], o[b][5][i], o[b][6][i], o[b][7][i]};
+            }
+            if (q4 == 0) {
+              s_m[slot][head] = m[b];
+              s_l[slot][head] = l[b];
+            }
           }
         }
       }
@@ -767,8 +784,9 @@ __global__ __launch_bounds__(kBlockThreads, 1) void decode_stream_kernel(DecodeP
     else if (G <= 8) fold_range<4, FUSED, NB, CAUSAL>(p, range, Lreg, 0, s_o, s_m, s_l, s_ready, s_folded, s_tk, s_lens);
     else fold_range<8, FUSED, NB, CAUSAL>(p, range, Lreg, 0, s_o, s_m, s_l, s_ready, s_folded, s_tk, s_lens);
   } else {
-    fold_range<8, FUSED, NB, CAUSAL>(p, range, Lreg, w - kStreamers, s_o, s_m, s_l, s_ready, s_folded, s_tk,
-                                     s_lens);
+    // 16 heads per folding wave (NCH = 8) with two blocks, 32 (NCH = 16) with four
+    fold_range<NB == 4 ? 16 : 8, FUSED, NB, CAUSAL>(p, range, Lreg, w - kStreamers, s_o, s_m, s_l, s_ready,
+                                                    s_folded, s_tk, s_lens);
   }
 }
 
@@ -777,8 +795,11 @@ void launch(const DecodeParams& p, hipStream_t stream) {
   if (p.gblk <= kBlockHeads)
     hipLaunchKernelGGL((decode_stream_kernel<FUSED, PAGED, 1, CAUSAL>), dim3(p.workgroups), dim3(kBlockThreads), 0,
                        stream, p);
-  else
+  else if (p.gblk <= 2 * kBlockHeads)
     hipLaunchKernelGGL((decode_stream_kernel<FUSED, PAGED, 2, CAUSAL>), dim3(p.workgroups), dim3(kBlockThreads), 0,
+                       stream, p);
+  else
+    hipLaunchKernelGGL((decode_stream_kernel<FUSED, PAGED, 4, CAUSAL>), dim3(p.workgroups), dim3(kBlockThreads), 0,
                        stream, p);
 }
 
@@ -799,9 +820,9 @@ hipError_t launch_decode_stream(const DecodeParams& p, hipStream_t stream) {
 // Workgroups of the instance that fit on one compute unit (cached per
 // process; the answer depends only on the kernel and the architecture).
 int stream_workgroups_per_cu(bool fused, bool paged, int G) {
-  static std::atomic<int> cached[8] = {};
-  const bool wide = G > kBlockHeads;
-  const int k = (fused ? 1 : 0) + (paged ? 2 : 0) + (wide ? 4 : 0);
+  static std::atomic<int> cached[12] = {};
+  const int nb = G <= kBlockHeads ? 0 : (G <= 2 * kBlockHeads ? 1 : 2);
+  const int k = (fused ? 1 : 0) + (paged ? 2 : 0) + 4 * nb;
   const int known = cached[k].load(std::memory_order_relaxed);
   if (known > 0) return known;
   int n = 0;
@@ -814,7 +835,11 @@ int stream_workgroups_per_cu(bool fused, bool paged, int G) {
     case 4: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_stream_kernel<false, false, 2, false>, kBlockThreads, 0); break;
     case 5: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_stream_kernel<true, false, 2, false>, kBlockThreads, 0); break;
     case 6: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_stream_kernel<false, true, 2, false>, kBlockThreads, 0); break;
-    default: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_stream_kernel<true, true, 2, false>, kBlockThreads, 0); break;
+    case 7: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_stream_kernel<true, true, 2, false>, kBlockThreads, 0); break;
+    case 8: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_stream_kernel<false, false, 4, false>, kBlockThreads, 0); break;
+    case 9: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_stream_kernel<true, false, 4, false>, kBlockThreads, 0); break;
+    case 10: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_stream_kernel<false, true, 4, false>, kBlockThreads, 0); break;
+    default: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_stream_kernel<true, true, 4, false>, kBlockThreads, 0); break;
   }
   if (e != hipSuccess || n <= 0) {
     (void)hipGetLastError();

@@ -128,7 +128,7 @@ int plan_decode(int b, int h, int g, int d_k, int d_v, int cap, int max_len, int
     plan->gblk = gqa::vector_heads_per_block(G);
     plan->nhb = (G + plan->gblk - 1) / plan->gblk;
   }
-  // At most 32 (virtual) heads per KV head and 64 sequences: the stream
+  // At most 64 (virtual) heads per KV head and 64 sequences: the stream
   // kernel (tile-granular schedule, waves finishing pieces on their own).
   plan->stream = chosen == GQA_PATH_MATRIX && G <= gqa::kStreamMaxGroup && b <= gqa::kStreamMaxBatch;
   const int waves = plan->stream ? 8
@@ -158,14 +158,22 @@ int plan_decode(int b, int h, int g, int d_k, int d_v, int cap, int max_len, int
   // Merging a shared segment inside the decode kernel falls to the one
   // workgroup that arrives last, which reads all the segment's partial states
   // alone at the very end; past 64 KiB of them per segment a second launch
-  // that merges with one workgroup per (segment, head) is faster.
+  // that merges with one workgroup per (segment, head) is faster. With 33-64
+  // heads the stream kernel merges with two waves of 32 heads each; there
+  // the limit is 48 KiB per wave, i.e. three parts (measured inline against
+  // the second launch: three parts, the eight-token Llama-3-70B step 93 us
+  // against 101, b = 64, h = 128, g = 2 at 2,048 positions 47 against 56;
+  // four parts, b = 40, h = 64, g = 2, two tokens, 45.5 against 44; five
+  // parts, b = 64, h = 64, g = 1, 45 against 36.5).
   if (merge_req == GQA_MERGE_KERNEL) {
     plan->merge_kernel = true;
   } else if (merge_req == GQA_MERGE_INLINE) {
     plan->merge_kernel = false;
   } else {
     const long long slots_per_segment = workgroups / (segments > 0 ? segments : 1) + 1;
-    plan->merge_kernel = slots_per_segment * plan->gblk * d_v * 4 > 64 * 1024;
+    const long long per_head = slots_per_segment * d_v * 4;  // partial-state bytes per head
+    plan->merge_kernel = plan->stream && plan->gblk > 32 ? per_head * 32 > 48 * 1024
+                                                        : per_head * plan->gblk > 64 * 1024;
   }
   if (auto_grid && !plan->merge_kernel) {
     // Inline merges: for large head groups keep at least G/2 tiles per

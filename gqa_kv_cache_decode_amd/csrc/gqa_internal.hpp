@@ -117,10 +117,11 @@ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 // The very end of the workspace: the fused step's completion counters (one
 // top counter and 16 first-level ones, 128 bytes apart) in the first 4 KiB,
-// then one ready flag per partial slot and head block of 16 heads
-// (kMaxWorkgroups x 2 slots x 2 blocks, int32).
+// then one ready flag per partial slot and folding wave of the stream kernel
+// (kMaxWorkgroups x 2 slots x kFlagBlocks waves, int32).
 constexpr size_t kFlagsOffset = 4096;
-constexpr size_t kDoneBytes = kFlagsOffset + size_t(kMaxWorkgroups) * 2 * 2 * sizeof(int);
+constexpr int kFlagBlocks = 2;
+constexpr size_t kDoneBytes = kFlagsOffset + size_t(kMaxWorkgroups) * 2 * kFlagBlocks * sizeof(int);
 
 // y_s = x w_s^T for up to three weight matrices w_s [n_out_s][n_in] (bf16,
 // packed by launch_pack_weight), x [rows][n_in], y_s [rows][n_out_s];
@@ -185,10 +186,10 @@ constexpr int kMergeLds = 2 * kMergePairs + 3 * kMatrixMaxGroup;
 hipError_t launch_append(const AppendParams& p, int b, int dtype, hipStream_t stream);
 hipError_t launch_decode_vector(const DecodeParams& p, int dtype, hipStream_t stream);
 hipError_t launch_decode_matrix(const DecodeParams& p, hipStream_t stream);
-// Matrix decode for up to 32 (virtual) heads per KV head and up to 64
+// Matrix decode for up to 64 (virtual) heads per KV head and up to 64
 // sequences (decode_stream.hip), one query token per sequence or a causal
 // multi-token call; seg_lead counts empty tiles there.
-constexpr int kStreamMaxGroup = 32;
+constexpr int kStreamMaxGroup = 64;
 constexpr int kStreamMaxBatch = 64;
 hipError_t launch_decode_stream(const DecodeParams& p, hipStream_t stream);
 int stream_workgroups_per_cu(bool fused, bool paged, int G);

@@ -273,7 +273,7 @@ int gqa_decode_layer(void* y, const void* x, const void* w_q, const void* w_k, c
  * positions t < lens[s] - (n - 1 - r). max_len bounds lens on the host.
  * gqa_decode_step_multi = append, then attention, with the same result as
  * the two calls: one launch where the tiles holding the new positions store
- * the new rows before reading them (bf16, d = 128, n * h/g <= 32, b <= 64),
+ * the new rows before reading them (bf16, d = 128, n * h/g <= 64, b <= 64),
  * else two launches; every check runs before anything is enqueued; max_len
  * bounds the lengths before the append.
  * All n tokens of a KV group share each K/V tile: the n * h/g query rows of a

@@ -162,12 +162,17 @@ def test_plan_choices(lib):
     # the Llama-3-70B shape: the matrix path's one-block streaming kernel, merges inside the launch
     assert plan(16, 64, 8, 128, 8256, 8193, _lib.BF16)[0] == _lib.PATH_MATRIX | _lib.MERGE_INLINE | _lib.PLAN_STREAM
     assert plan(64, 28, 4, 128, 2112, 2080, _lib.BF16)[0] & _lib.PLAN_STREAM  # the Qwen2.5-7B shape too
-    # up to 32 heads per KV head (two column blocks) as well
+    # up to 64 heads per KV head (two or four column blocks) as well
     assert plan(16, 64, 2, 128, 2112, 2080, _lib.BF16)[0] & _lib.PLAN_STREAM
     assert plan(16, 24, 1, 128, 2112, 2080, _lib.BF16)[0] & _lib.PLAN_STREAM
-    # past 32 heads per KV head or 64 sequences: the unit kernels
+    assert plan(16, 64, 1, 128, 2112, 2080, _lib.BF16)[0] & _lib.PLAN_STREAM
+    # 64 heads per KV head: merged inline up to three parts per segment (two waves of 32 heads), else
+    # by a second launch
+    assert plan(64, 128, 2, 128, 2112, 2048, _lib.BF16)[0] == _lib.PATH_MATRIX | _lib.MERGE_INLINE | _lib.PLAN_STREAM
+    assert plan(64, 64, 1, 128, 2112, 2048, _lib.BF16)[0] == _lib.PATH_MATRIX | _lib.MERGE_KERNEL | _lib.PLAN_STREAM
+    # past 64 sequences: the unit kernels
     assert not plan(65, 64, 8, 128, 2112, 2080, _lib.BF16)[0] & _lib.PLAN_STREAM
-    assert not plan(16, 64, 1, 128, 2112, 2080, _lib.BF16)[0] & _lib.PLAN_STREAM
+    assert not plan(65, 64, 1, 128, 2112, 2080, _lib.BF16)[0] & _lib.PLAN_STREAM
     M = M | _lib.PLAN_STREAM
     # few long segments with 32 heads per KV head: merged by a second launch
     S = _lib.PATH_MATRIX | _lib.MERGE_KERNEL | _lib.PLAN_STREAM

@@ -146,6 +146,7 @@ EDGE = [
     (4, 7, 1, 128, 130, [33, 64, 65, 129], "bf16"),  # G = 7 on the matrix path, tails around 32/64
     (2, 12, 4, 128, 100, [97, 3], "bf16"),           # G = 3
     (2, 64, 1, 128, 200, [200, 131], "bf16"),        # G = 64 (four 16-head blocks)
+    (2, 40, 1, 128, 150, [150, 37], "bf16"),         # G = 40 (third block partly used, fourth empty)
     (2, 34, 2, 128, 90, [90, 45], "bf16"),           # G = 17 (second head block partly used)
     (3, 32, 1, 128, 300, [300, 33, 0], "bf16"),      # G = 32, MQA: two full head blocks
     (2, 64, 2, 128, 129, [129, 96], "bf16"),         # G = 32 with two KV heads

@@ -83,7 +83,7 @@ def test_matrix_kernel_instances_use_no_scratch_up_to_32_heads(remarks):
 def test_stream_kernel_instances_use_no_scratch(remarks):
     res = remarks["decode_stream.hip"]
     inst = {k: v for k, v in res.items() if "decode_stream_kernel" in k}
-    assert len(inst) == 12, sorted(inst)  # (fused or not / causal) x paged x one or two head blocks
+    assert len(inst) == 24, sorted(inst)  # fused x paged x causal x one, two or four head blocks
     _check_common(inst)
     for name, r in inst.items():
         assert r["scratch"] == 0, f"{name}: {r['scratch']} bytes of scratch per lane"

@@ -130,7 +130,8 @@ def test_one_token_multi_equals_the_one_token_call(gpu_lib):
 
 
 @pytest.mark.parametrize("b,h,g,n,lens", [(3, 64, 8, 4, [1, 29, 511]), (4, 28, 4, 3, [0, 62, 63, 200]),
-                                           (3, 64, 8, 2, [0, 31, 300])])
+                                           (3, 64, 8, 2, [0, 31, 300]), (2, 64, 8, 8, [5, 700]),
+                                           (2, 24, 4, 8, [3, 260])])
 def test_multi_step_equals_append_then_attention(gpu_lib, b, h, g, n, lens):
     # the one-launch step (new rows stored by the tiles that hold them) and the
     # two calls give the same bits: the same tile states folded in the same order
@@ -166,10 +167,11 @@ def test_multi_rejects(gpu_lib):
     assert np.array_equal(pb.lens.cpu().numpy(), pb.lens_h)  # nothing was enqueued
 
 
-def test_multi_llama3_70b_shape(gpu_lib, oracle_mod):
-    # the Llama-3-70B-shaped batch with 4 speculative tokens per sequence (32 virtual heads per group)
+@pytest.mark.parametrize("n", [4, 8])
+def test_multi_llama3_70b_shape(gpu_lib, oracle_mod, n):
+    # the Llama-3-70B-shaped batch with 4 or 8 speculative tokens per sequence (32 or 64 virtual heads
+    # per group; with 8, two folding waves of 32 heads merge the split segments inside the launch)
     wl = WORKLOADS["llama3_70b_gqa_bf16"]
-    n = 4
     print(f"multi-token step: Llama-3-70B shape, n={n}", flush=True)
     batch = inputs.Batch(seed=wl.seed, b=wl.b, h=wl.h, g=wl.g, d=wl.d, cap=wl.cap, lens=wl.lens, dtype="bf16",
                          poison=True)
