@@ -63,6 +63,8 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kD = 128;
@@ -156,6 +158,25 @@ __device__ __forceinline__ void load_tile(Tile& t, const uint16_t* kb, const uin
   }
 }
 
+// op over the four 16-lane rows of the wave (lanes n, n + 16, n + 32,
+// n + 48), the same value in all four: rows 0 and 1 and rows 2 and 3 are
+// combined through the row-pair swap, then the two halves through the
+// half swap (each a register exchange between lanes, no LDS round trip), as
+// op(op(r0, r1), op(r2, r3)) for the symmetric ops used here.
+template <typename Op>
+__device__ __forceinline__ float across_rows(float x, Op op) {
+  // (the pair's elements are copied to scalars before the bit casts: a cast
+  // of a vector element in place reads element 0)
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);  // {r0 r0 r2 r2}, {r1 r1 r3 r3}
+  const unsigned a0 = a[0], a1 = a[1];
+  const float y = op(__builtin_bit_cast(float, a0), __builtin_bit_cast(float, a1));
+  const unsigned v = __builtin_bit_cast(unsigned, y);
+  const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);  // {lo lo}, {hi hi}
+  const unsigned b0 = b[0], b1 = b[1];
+  return op(__builtin_bit_cast(float, b0), __builtin_bit_cast(float, b1));
+}
+
 // The split-softmax state of one tile, from scratch, for NB column blocks of
 // 16 heads: per head m = the tile's largest scaled logit (base 2), l = sum
 // of its weights 2^(s - m) (rounded to bf16, as applied), o = their
@@ -172,7 +193,7 @@ __device__ __forceinline__ void tile_state(f32x4 (&o)[NB][8], float (&m)[NB], fl
   bf16x8 pk[NB];
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
-    float sv[8];
+    float sv[8];  // scores, unscaled when FULL, else scaled and masked
 #pragma unroll
     for (int sg = 0; sg < 2; ++sg) {
       f32x4 sacc = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -182,24 +203,47 @@ __device__ __forceinline__ void tile_state(f32x4 (&o)[NB][8], float (&m)[NB], fl
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int row = 16 * sg + 4 * q4 + i;
-        sv[sg * 4 + i] = (FULL || row < lim[b]) ? sacc[i] * sl2 : kNegInf;
+        if constexpr (FULL) sv[sg * 4 + i] = sacc[i];
+        else sv[sg * 4 + i] = row < lim[b] ? sacc[i] * sl2 : kNegInf;
       }
     }
+    // m: the largest scaled score. In a full tile it is found on the
+    // unscaled scores (the largest for a positive scale, the smallest for a
+    // negative one) and scaled once: a correctly rounded product keeps the
+    // order, so this is the same value as the largest rounded product.
     float mx = sv[0];
+    if (FULL && sl2 < 0.0f) {
 #pragma unroll
-    for (int k = 1; k < 8; ++k) mx = fmaxf(mx, sv[k]);
-    mx = fmaxf(mx, xor_shuffle(mx, 16));
-    mx = fmaxf(mx, xor_shuffle(mx, 32));
+      for (int k = 1; k < 8; ++k) mx = fminf(mx, sv[k]);
+      mx = across_rows(mx, [](float x, float y) { return fminf(x, y); });
+    } else {
+#pragma unroll
+      for (int k = 1; k < 8; ++k) mx = fmaxf(mx, sv[k]);
+      mx = across_rows(mx, [](float x, float y) { return fmaxf(x, y); });
+    }
+    if constexpr (FULL) mx *= sl2;
     const float sub = (mx == kNegInf) ? 0.0f : mx;
+    // weights 2^(s - m), rounded to bf16 in pairs (the value MFMA's operand);
+    // the denominator sums the weights as rounded, in position order
     float psum = 0.0f;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const __bf16 pb = static_cast<__bf16>(fast_exp2(sv[k] - sub));
-      pk[b][k] = pb;
-      psum += static_cast<float>(pb);  // the denominator sums the weights actually applied
+    for (int k = 0; k < 8; k += 2) {
+      float e0, e1;
+      if constexpr (FULL) {
+        e0 = fast_exp2(fmaf(sv[k], sl2, -sub));
+        e1 = fast_exp2(fmaf(sv[k + 1], sl2, -sub));
+      } else {
+        e0 = fast_exp2(sv[k] - sub);
+        e1 = fast_exp2(sv[k + 1] - sub);
+      }
+      const bf16x2 pr = __builtin_convertvector((f32x2){e0, e1}, bf16x2);
+      pk[b][k] = pr[0];
+      pk[b][k + 1] = pr[1];
+      const uint32_t w = __builtin_bit_cast(uint32_t, pr);
+      psum += __builtin_bit_cast(float, w << 16);
+      psum += __builtin_bit_cast(float, w & 0xffff0000u);
     }
-    psum += xor_shuffle(psum, 16);
-    psum += xor_shuffle(psum, 32);
+    psum = across_rows(psum, [](float x, float y) { return x + y; });
     m[b] = mx;
     l[b] = psum;
   }
