@@ -37,6 +37,7 @@ CASES = [
     ("bf16", 4, 64, 8, 128, [0, 31, 32, 300], 32),        # matrix, G = 8
     ("bf16", 3, 28, 4, 128, [1, 200, 511], 64),           # matrix, G = 7
     ("bf16", 2, 32, 1, 128, [700, 1500], 256),            # matrix, G = 32, merged by a second launch
+    ("bf16", 2, 64, 1, 128, [300, 77], 64),               # matrix, G = 64: four head blocks
     ("bf16", 3, 8, 4, 128, [5, 64, 190], 32),             # vector, G = 2
     ("bf16", 2, 16, 16, 64, [33, 129], 128),              # vector, MHA
     ("f32", 2, 4, 2, 16, [37, 64], 32),                   # vector, fp32
