@@ -44,7 +44,7 @@ constexpr int kSegmentLead32 = 3;      // four-wave kernel, 17-32 heads
 constexpr int kSegmentLead64 = 5;      // four-wave kernel, 33-64 heads
 constexpr int kMaxSegmentLead = 5;
 constexpr int kLeadMinUnits = 8;       // four-wave kernels: lead units only from this many units per workgroup
-constexpr int kStreamLeadTiles = 4;    // one-block stream kernel: empty tiles ahead of each segment
+constexpr int kStreamLeadTiles = 6;    // one-block stream kernel: empty tiles ahead of each segment
 
 bool supported_head_dim(int d) { return d == 16 || d == 32 || d == 64 || d == 128 || d == 256; }
 

@@ -144,7 +144,7 @@ def test_failing_64_head_shape_of_the_unit_kernel(sched):
             assert len(rows) >= 2
 
 
-@pytest.mark.parametrize("ut,lead", [(1, 0), (1, 4), (1, 8), (4, 0), (4, 2), (4, 5)])
+@pytest.mark.parametrize("ut,lead", [(1, 0), (1, 4), (1, 6), (1, 8), (4, 0), (4, 2), (4, 5)])
 def test_workload_shapes(sched, ut, lead):
     rng = np.random.default_rng(1003)
     llama = rng.integers(1024, 8193, 16) + 1
