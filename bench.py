@@ -290,10 +290,26 @@ def main():
 
     stream = torch.cuda.current_stream()
 
+    # Every set starts from set 0's lengths and grows by ntok per step it
+    # takes, so a step's host-side bound and byte count follow from how many
+    # steps its set has taken (tables, so the timed loop issues launches and
+    # little else: steps of ~20 us are otherwise bound by the host).
+    lens0 = sets[0]["lens_h"].copy()
+    max0 = int(lens0.max())
+    taken = [0] * n_sets
+    bytes_after = []  # bytes_after[c]: attended bytes of a set's step number c (0-based)
+
+    def step_bytes(c):
+        while len(bytes_after) <= c:
+            bytes_after.append(kv_bytes_attended(wl.g, wl.d, wl.d, wl.elem_bytes, lens0 + ntok * (len(bytes_after) + 1)))
+        return bytes_after[c]
+
     def step(i, ev_pair=None):
-        st = sets[i % n_sets]
+        si = i % n_sets
+        st = sets[si]
         kn, vn = news[i % len(news)]
-        max_len = int(st["lens_h"].max())
+        c = taken[si]
+        max_len = max0 + ntok * c
         if args.unfused:
             api.kv_append(st["kc"], st["vc"], kn, vn, st["lens"], max_len)
         if ev_pair is not None:
@@ -314,8 +330,8 @@ def main():
                             path=args.path, workgroups=args.workgroups)
         if ev_pair is not None:
             ev_pair[1].record(stream)
-        st["lens_h"] += ntok
-        return kv_bytes_attended(wl.g, wl.d, wl.d, wl.elem_bytes, st["lens_h"])
+        taken[si] = c + 1
+        return step_bytes(c)
 
     for i in range(args.warmup):
         step(i)
