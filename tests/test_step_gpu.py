@@ -169,3 +169,25 @@ def test_step_maximum_batch(gpu_lib, oracle_mod):
         got, ref = pb.step(step)
         assert_parity(got, ref, "f32", f"step {step}")
         pb.check_state()
+
+
+def test_step_on_a_side_stream_equals_the_default_stream(gpu_lib, oracle_mod):
+    # the binding launches on torch's current stream: inside a side stream's
+    # context the step runs there (ordered after the inputs' copies by an
+    # explicit wait) and gives the same bits as on the default stream
+    a = StepProblem(oracle_mod, seed=307, b=3, h=32, g=2, d=128, cap=400, lens=[0, 129, 398], dtype="bf16")
+    b = StepProblem(oracle_mod, seed=307, b=3, h=32, g=2, d=128, cap=400, lens=[0, 129, 398], dtype="bf16")
+    got_a, ref = a.step(0)
+    q = b.batch.q(0)
+    kn, vn = b.batch.new_kv(0)
+    qd, knd, vnd = to_dev(q), to_dev(kn), to_dev(vn)
+    out = torch.empty(b.b, b.h, b.d, dtype=torch.bfloat16, device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        api.decode_step(out, qd, knd, vnd, b.kc, b.vc, b.lens, int(b.lens_h.max()), b.scale, b.ws)
+    side.synchronize()
+    assert torch.equal(out.view(torch.int16), got_a.view(torch.int16))
+    assert_parity(out, ref, "bf16", "side stream")
+    b.oracle.kv_append(b.batch.k_cache, b.batch.v_cache, kn, vn, b.lens_h)
+    b.check_state()
