@@ -20,17 +20,18 @@
 //
 // * The static split of the (sequence, KV head) segments over the persistent
 //   workgroups is balanced to one 32-position tile (16 KiB), not four.
-// * Inside a workgroup, the streaming waves (seven; six or four with two or
-//   four head blocks) take the range's tiles one at a time from an LDS counter, so a
-//   wave that is served faster takes more tiles and all finish together.
-//   Each tile's split-softmax state (max m, sum of weights l, unnormalised
-//   output o) is computed from scratch, so it does not depend on which wave
-//   computed it.
-// * A folding wave per block of 16 heads folds the tile states in tile order
-//   out of an LDS ring (m = max, o and l rescaled by 2^(m_k - m)), which
-//   fixes the arithmetic: results are bit for bit the same whichever wave
-//   took which tile. It also writes, publishes or merges each finished
-//   piece, so the streaming waves never stop for that.
+// * Inside a workgroup, the streaming waves (seven with one head block, six
+//   with two or four) take the range's tiles one at a time from an LDS
+//   counter, so a wave that is served faster takes more tiles and all
+//   finish together. Each tile's split-softmax state (max m, sum of
+//   weights l, unnormalised output o) is computed from scratch, so it does
+//   not depend on which wave computed it.
+// * A folding wave per block of 16 heads (per 32 heads with four blocks)
+//   folds the tile states in tile order out of an LDS ring (m = max, o and
+//   l rescaled by 2^(m_k - m)), which fixes the arithmetic: results are bit
+//   for bit the same whichever wave took which tile. It also writes,
+//   publishes or merges each finished piece, so the streaming waves never
+//   stop for that.
 // * A tile's K/V loads are issued before the query rows it needs.
 // * Fused step: a tile holding appended positions first stores their rows
 //   into the cache. The grown lengths can be written as soon as every
