@@ -699,9 +699,8 @@ __global__ __launch_bounds__(kBlockThreads, 1) void decode_stream_kernel(DecodeP
       // sequence s from k_new / v_new [b][n][g][d]) into their cache slots,
       // waits for the stores, then reads the tile. Lanes l and l + 32 take
       // two consecutive positions, lanes 0-15 of each half the K row and
-      // lanes 16-31 the V row; up to eight rows' loads (four with four head
-      // blocks, for registers) are issued before the first store, so that the
-      // rows cost one round trip, not one each.
+      // lanes 16-31 the V row; up to eight rows' loads are issued before the
+      // first store, so that the rows cost one round trip, not one each.
       const int first_new = pc.L - p.fused;
       if (FUSED && t0 + kTile > first_new) {
         const int n_new = p.fused;
@@ -823,7 +822,8 @@ __global__ __launch_bounds__(kBlockThreads, 1) void decode_stream_kernel(DecodeP
     return;
   }
 
-  // ---- folding waves (one per block of 16 heads; lane layout by the heads in use)
+  // ---- folding waves (one per block of 16 heads, or per 32 with four blocks;
+  // lane layout by the heads in use)
   if constexpr (NB == 1) {
     if (G <= 4) fold_range<2, FUSED, NB, CAUSAL>(p, range, Lreg, 0, s_o, s_m, s_l, s_ready, s_folded, s_tk, s_lens);
     else if (G <= 8) fold_range<4, FUSED, NB, CAUSAL>(p, range, Lreg, 0, s_o, s_m, s_l, s_ready, s_folded, s_tk, s_lens);
