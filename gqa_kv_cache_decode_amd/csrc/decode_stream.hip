@@ -38,8 +38,8 @@
 //   workgroup has read the old ones, which all do at their start. The
 //   folding wave of each workgroup counts it out right after that read on
 //   one of 16 counters, and the last of each group on one more, so no more
-//   than 16 atomics meet on one address and none waits at the end of the
-//   launch.
+//   than 16 atomics meet on one address; it waits for those results before
+//   its first tile state arrives, and none waits at the end of the launch.
 //
 // Split segments (a segment whose tiles fall in the ranges of several
 // workgroups, its "parts") are merged by the part that counts in last, with
@@ -346,50 +346,38 @@ __device__ __forceinline__ uint2 to_bf16x4(f32x4 v) {
 // Fused step: counting the workgroups out after their read of the lengths.
 // Workgroup wg counts on first-level counter wg mod 16; the last of each
 // group counts on the top counter; the last of those writes the lengths and
-// re-zeroes all counters. The folding wave drives it between tiles: the
-// atomics are issued early and their results looked at only later.
+// re-zeroes all counters.
 struct LenCount {
-  int state;  // 0 first-level count issued, 1 top count issued, 2 done
-  int val;
-  __device__ void start(const DecodeParams& p, int wg) {
-    // called after the workgroup barrier that follows the read of lens (its
-    // values are in LDS by then); keep the compiler from moving the count up
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  // called by one wave of the workgroup after the workgroup barrier that
+  // follows the read of lens (its values are in LDS by then). It waits for
+  // each count's result right away: the folding wave that runs it has
+  // nothing to fold until the first tile states arrive, well after both
+  // round trips, and no atomic's result is left pending into the fold loop
+  // (a result pending across the loop's back edge made the compiler wait
+  // for every outstanding memory access, stores included, at each piece).
+  __device__ static void run(const DecodeParams& p, const int* s_lens, int wg) {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);  // keep the count after the read of lens
+    const int lane = threadIdx.x & 63;
+    const int P = int(gridDim.x);
     int v = 0;
-    if ((threadIdx.x & 63) == 0)
+    if (lane == 0)
       v = __hip_atomic_fetch_add(p.ws_done + kCountStride * (1 + wg % kCountGroups), 1, __ATOMIC_RELAXED,
                                  __HIP_MEMORY_SCOPE_AGENT);
-    val = v;  // only lane 0's value is meaningful; read through readfirstlane
-    state = 0;
-  }
-  __device__ void step(const DecodeParams& p, const int* s_lens) {
-    if (state == 2) return;
-    const int wg = blockIdx.x;
-    const int P = int(gridDim.x);
-    const int v = __builtin_amdgcn_readfirstlane(val);
-    if (state == 0) {
-      const int grp = wg % kCountGroups;
-      const int members = (P - grp + kCountGroups - 1) / kCountGroups;
-      if (v != members - 1) {
-        state = 2;
-        return;
-      }
-      int t = 0;
-      if ((threadIdx.x & 63) == 0) t = __hip_atomic_fetch_add(p.ws_done, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      val = t;
-      state = 1;
-      return;
-    }
-    // state 1: the top count's result
+    v = __builtin_amdgcn_readfirstlane(v);
+    const int grp = wg % kCountGroups;
+    const int members = (P - grp + kCountGroups - 1) / kCountGroups;
+    if (v != members - 1) return;
+    // the last of its group counts the group out on the top counter
+    int t = 0;
+    if (lane == 0) t = __hip_atomic_fetch_add(p.ws_done, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    t = __builtin_amdgcn_readfirstlane(t);
     const int groups = P < kCountGroups ? P : kCountGroups;
-    if (v == groups - 1) {
-      const int lane = threadIdx.x & 63;
-      if (lane < p.b) p.lens[lane] = s_lens[lane];  // attended length = grown length
-      if (lane < groups) __hip_atomic_store(p.ws_done + kCountStride * (1 + lane), 0, __ATOMIC_RELAXED,
-                                            __HIP_MEMORY_SCOPE_AGENT);
-      if (lane == 0) __hip_atomic_store(p.ws_done, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    state = 2;
+    if (t != groups - 1) return;
+    // the last of all: every workgroup has read the old lengths
+    if (lane < p.b) p.lens[lane] = s_lens[lane];  // attended length = grown length
+    if (lane < groups)
+      __hip_atomic_store(p.ws_done + kCountStride * (1 + lane), 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (lane == 0) __hip_atomic_store(p.ws_done, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 };
 
@@ -500,9 +488,7 @@ __device__ void fold_range(const DecodeParams& p, const Range& range, int Lreg, 
   const int sub = lane % HP;
   const bool active = hh < G;
   const bool lead = hb == 0;  // counts, takes tickets
-  LenCount cnt;
-  cnt.state = 2;
-  if (FUSED && lead) cnt.start(p, wg);
+  if (FUSED && lead) LenCount::run(p, s_lens, wg);
   Range it = range;
   StreamPiece pc;
   int k = 0;    // next range tile to fold
@@ -574,7 +560,6 @@ __device__ void fold_range(const DecodeParams& p, const Range& range, int Lreg, 
       e += r;
       k += r;
       if (lane == 0) __hip_atomic_store(&s_folded[hb], k, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
-      if (FUSED && lead) cnt.step(p, s_lens);
     }
     // the piece is complete
     if (!shared) {
@@ -633,9 +618,6 @@ __device__ void fold_range(const DecodeParams& p, const Range& range, int Lreg, 
       if (lane == 0)
         __hip_atomic_store(slot_flag(p, wg, my_slot, hb), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-  }
-  if (FUSED && lead) {
-    while (cnt.state != 2) cnt.step(p, s_lens);
   }
 }
 
