@@ -25,6 +25,7 @@ PATH_VECTOR = 1
 PATH_MATRIX = 2
 MERGE_INLINE = 0x10  # OR into path: split segments merged inside the decode launch
 MERGE_KERNEL = 0x20  # OR into path: split segments merged by a second launch
+MERGE_SPREAD = 0x80  # OR into path: split segments merged by their parts at the end of the launch (stream kernel)
 PLAN_STREAM = 0x40   # reported by gqa_decode_plan: the matrix path's one-block streaming kernel
 
 ERROR_NAMES = {

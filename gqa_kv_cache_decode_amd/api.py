@@ -12,7 +12,7 @@ import ctypes
 import torch
 
 from . import _lib
-from ._lib import MERGE_INLINE, MERGE_KERNEL, PATH_AUTO, PATH_MATRIX, PATH_VECTOR  # noqa: F401  (re-exported)
+from ._lib import MERGE_INLINE, MERGE_KERNEL, MERGE_SPREAD, PATH_AUTO, PATH_MATRIX, PATH_VECTOR  # noqa: F401  (re-exported)
 
 _DTYPES = {torch.float32: _lib.F32, torch.bfloat16: _lib.BF16}
 
@@ -90,7 +90,7 @@ def make_workspace(b: int, h: int, g: int, d_k: int, d_v: int, max_len: int, dty
 def plan(b, h, g, d_k, d_v, cap, max_len, dtype: torch.dtype, path=PATH_AUTO, workgroups=0, stream_flag=False):
     """(path, workgroups, merge) the library would launch with on the current device; no GPU work.
 
-    path is PATH_VECTOR or PATH_MATRIX; merge is MERGE_INLINE or MERGE_KERNEL. With
+    path is PATH_VECTOR or PATH_MATRIX; merge is MERGE_INLINE, MERGE_KERNEL or MERGE_SPREAD. With
     stream_flag, a fourth value says whether the matrix path runs its one-block
     streaming kernel.
     """
@@ -99,8 +99,8 @@ def plan(b, h, g, d_k, d_v, cap, max_len, dtype: torch.dtype, path=PATH_AUTO, wo
     rc = lib.gqa_decode_plan(b, h, g, d_k, d_v, cap, int(max_len), _DTYPES[dtype], path, workgroups,
                              ctypes.byref(p), ctypes.byref(c))
     _lib.check(rc, "gqa_decode_plan")
-    merge = p.value & (MERGE_INLINE | MERGE_KERNEL)
-    chosen = p.value & ~(MERGE_INLINE | MERGE_KERNEL | _lib.PLAN_STREAM)
+    merge = p.value & (MERGE_INLINE | MERGE_KERNEL | MERGE_SPREAD)
+    chosen = p.value & ~(MERGE_INLINE | MERGE_KERNEL | MERGE_SPREAD | _lib.PLAN_STREAM)
     if stream_flag:
         return chosen, c.value, merge, bool(p.value & _lib.PLAN_STREAM)
     return chosen, c.value, merge
@@ -112,7 +112,7 @@ def decode_attention(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor, 
     """out[s,i] = softmax_t(scale * q[s,i] . K[s,j,t]) @ V[s,j,t], t < lens[s], j = i // (h/g).
 
     q [b,h,d_k], caches [b,g,cap,d], lens int32 [b] (attended lengths), out [b,h,d_v].
-    path: PATH_* optionally OR-ed with MERGE_INLINE / MERGE_KERNEL.
+    path: PATH_* optionally OR-ed with MERGE_INLINE / MERGE_KERNEL / MERGE_SPREAD.
     """
     _check_gpu(out, q, k_cache, v_cache, lens, workspace)
     if lens.dtype != torch.int32:

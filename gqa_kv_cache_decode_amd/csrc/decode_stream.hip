@@ -92,6 +92,16 @@ template <int NCH>
 constexpr int fold_batch() { return NCH == 16 ? 1 : (NCH == 8 ? 2 : 4); }
 constexpr int kCountGroups = 16;    // first-level counters of the fused step's length update
 constexpr int kCountStride = 32;    // ints between counters (128 bytes)
+// Spread merge: words of the stamp region, and the codes of its slot flags
+// (flag = 4 * generation + code).
+constexpr int kGenWord = 0;       // generation of the last launch
+constexpr int kStartedWord = 32;  // generation whose workgroups have all started
+constexpr unsigned kSpreadPublished = 0;  // state published; who merges its slice is not decided yet
+constexpr unsigned kSpreadMerging = 1;    // state published; its part merges its own slice of heads
+constexpr unsigned kSpreadOrphan = 2;     // state published; its slice is left to the workgroup that started last
+constexpr unsigned kSpreadNone = 3;       // no partial state in this slot
+constexpr int kStartSpins = 64;           // bound of a part's wait for every workgroup to have started
+constexpr int kSweepPerThread = 2 * kMaxWorkgroups * kFlagBlocks / kBlockThreads;  // flags a thread polls, at most
 
 __device__ __forceinline__ u32x4 ld16(const uint16_t* ptr) { return *reinterpret_cast<const u32x4*>(ptr); }
 __device__ __forceinline__ void st16(uint16_t* ptr, u32x4 v) { *reinterpret_cast<u32x4*>(ptr) = v; }
@@ -343,10 +353,12 @@ __device__ __forceinline__ uint2 to_bf16x4(f32x4 v) {
   return pk;
 }
 
-// Fused step: counting the workgroups out after their read of the lengths.
-// Workgroup wg counts on first-level counter wg mod 16; the last of each
-// group counts on the top counter; the last of those writes the lengths and
-// re-zeroes all counters.
+// Counting the workgroups out after their read of the lengths (fused step)
+// and of the launch generation (spread merge). Workgroup wg counts on
+// first-level counter wg mod 16; the last of each group counts on the top
+// counter; the last of those writes the lengths (fused step), publishes that
+// every workgroup of this generation has started and takes the orphaned
+// merges (spread merge), and re-zeroes all counters.
 struct LenCount {
   // called by one wave of the workgroup after the workgroup barrier that
   // follows the read of lens (its values are in LDS by then). It waits for
@@ -355,7 +367,9 @@ struct LenCount {
   // round trips, and no atomic's result is left pending into the fold loop
   // (a result pending across the loop's back edge made the compiler wait
   // for every outstanding memory access, stores included, at each piece).
-  __device__ static void run(const DecodeParams& p, const int* s_lens, int wg) {
+  template <bool SPREAD>
+  __device__ static void run(const DecodeParams& p, const int* s_lens, int wg, bool write_lens, unsigned stamp,
+                             int* s_sweep) {
     __atomic_signal_fence(__ATOMIC_SEQ_CST);  // keep the count after the read of lens
     const int lane = threadIdx.x & 63;
     const int P = int(gridDim.x);
@@ -373,8 +387,13 @@ struct LenCount {
     t = __builtin_amdgcn_readfirstlane(t);
     const int groups = P < kCountGroups ? P : kCountGroups;
     if (t != groups - 1) return;
-    // the last of all: every workgroup has read the old lengths
-    if (lane < p.b) p.lens[lane] = s_lens[lane];  // attended length = grown length
+    // the last of all: every workgroup has read the old lengths and the generation
+    if (write_lens && lane < p.b) p.lens[lane] = s_lens[lane];  // attended length = grown length
+    if (SPREAD && lane == 0) {
+      __hip_atomic_store(p.ws_stamp + kGenWord, int(stamp), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(p.ws_stamp + kStartedWord, int(stamp), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      *s_sweep = 1;
+    }
     if (lane < groups)
       __hip_atomic_store(p.ws_done + kCountStride * (1 + lane), 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (lane == 0) __hip_atomic_store(p.ws_done, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -385,6 +404,11 @@ struct LenCount {
 // (zero between calls).
 __device__ __forceinline__ int* slot_flag(const DecodeParams& p, int wg, int slot, int half) {
   return p.ws_done + kFlagsOffset / sizeof(int) + (wg * 2 + slot) * kFlagBlocks + half;
+}
+// Spread merge: stamped flag of folding wave `half`'s heads in partial slot
+// `slot` of workgroup `wg` (never reset).
+__device__ __forceinline__ int* spread_flag(const DecodeParams& p, int wg, int slot, int half) {
+  return p.ws_stamp + kStampFlagsOffset / sizeof(int) + (wg * 2 + slot) * kFlagBlocks + half;
 }
 
 // The merging folding wave `half` waits until every other part of segment
@@ -472,11 +496,11 @@ __device__ void merge_parts(const DecodeParams& p, int s, int j, int p0, int n_s
 // four-dim columns c = (l mod HP) + HP i, i < NCH, so each lane weighs a
 // single head per tile. The ring has ring_slots<NB>() slots of 16 NB heads;
 // s_folded[hb] counts the tiles folding wave hb has folded.
-template <int NCH, bool FUSED, int NB, bool CAUSAL>
+template <int NCH, bool FUSED, int NB, bool CAUSAL, bool SPREAD>
 __device__ void fold_range(const DecodeParams& p, const Range& range, int Lreg, int hb,
                            float (*s_o)[kBlockHeads * NB * kRow], float (*s_m)[kBlockHeads * NB],
                            float (*s_l)[kBlockHeads * NB], int* s_ready, int* s_folded, int (*s_tk)[16],
-                           const int* s_lens) {
+                           const int* s_lens, unsigned stamp, int* s_spread, int* s_sweep) {
   constexpr int HP = (kD / 4) / NCH;
   constexpr int R = fold_batch<NCH>();
   constexpr int kRing = ring_slots<NB>();
@@ -488,16 +512,17 @@ __device__ void fold_range(const DecodeParams& p, const Range& range, int Lreg, 
   const int sub = lane % HP;
   const bool active = hh < G;
   const bool lead = hb == 0;  // counts, takes tickets
-  if (FUSED && lead) LenCount::run(p, s_lens, wg);
+  if ((FUSED || SPREAD) && lead) LenCount::run<SPREAD>(p, s_lens, wg, FUSED, stamp, s_sweep);
   Range it = range;
   StreamPiece pc;
   int k = 0;    // next range tile to fold
   int ord = 0;  // pieces finished so far
+  int published = 0;  // spread merge: partial slots this wave has published (bits)
   for (; next_piece(p, it, Lreg, pc); ++ord) {
     const int n = pc.tile_end - pc.tile_begin;
     const int s = pc.s, j = pc.grp;
     const bool shared = pc.p0 != pc.p1;
-    const bool inline_merge = shared && !p.merge_kernel;
+    const bool inline_merge = shared && !p.merge_kernel && !SPREAD;
     const int n_slots = pc.p1 - pc.p0 + 1;
     const int own = wg - pc.p0;  // this workgroup's part of the segment
     int* ticket = p.ws_cnt + (size_t(s) * p.ngroups + j) * p.cnt_stride;
@@ -597,11 +622,19 @@ __device__ void fold_range(const DecodeParams& p, const Range& range, int Lreg, 
       if (lead && lane == 0) __hip_atomic_store(ticket, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       continue;
     }
-    // publish this part's state, then (inline merge) its ready flag
+    // publish this part's state, then (inline and spread merges) its flag
     const __amdgpu_buffer_rsrc_t rs = slots_rsrc(p);
     const int ml_off = G * kD * int(sizeof(float));
     const int my_slot = wg == pc.p0 ? 1 : 0;
     const int slot_off = slot_offset(p, wg, my_slot);
+    // spread merge: whether every workgroup of this launch has started, read
+    // while the state is stored. If so, every part of the segment reaches its
+    // end without waiting on anything, so this part may wait for them at the
+    // end of the launch and merge its own slice of heads; if not yet, that is
+    // decided at the end of the launch.
+    int started = 0;
+    if (SPREAD && lane == 0)
+      started = __hip_atomic_load(p.ws_stamp + kStartedWord, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (active) {
 #pragma unroll
       for (int i = 0; i < NCH; ++i)
@@ -611,7 +644,24 @@ __device__ void fold_range(const DecodeParams& p, const Range& range, int Lreg, 
         coherent_store1(rs, slot_off + ml_off + (G + hh) * 4, al);
       }
     }
-    if (p.merge_kernel) {
+    if (SPREAD) {
+      wait_stores();
+      const unsigned code =
+          unsigned(__builtin_amdgcn_readfirstlane(started)) == stamp ? kSpreadMerging : kSpreadPublished;
+      if (lane == 0) {
+        __hip_atomic_store(spread_flag(p, wg, my_slot, hb), int(4u * stamp + code), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+        int* job = s_spread + 8 * my_slot;  // the piece, for the end of the launch
+        job[0] = s;
+        job[1] = j;
+        job[2] = pc.p0;
+        job[3] = n_slots;
+        job[4] = own;
+        job[5 + hb] = int(code);
+        job[7] = 1;
+      }
+      published |= 1 << my_slot;
+    } else if (p.merge_kernel) {
       if (lead && pc.tile_begin == 0 && lane == 0) p.seg_info[size_t(s) * p.ngroups + j] = make_int2(pc.p0, pc.p1);
     } else {
       wait_stores();
@@ -619,9 +669,255 @@ __device__ void fold_range(const DecodeParams& p, const Range& range, int Lreg, 
         __hip_atomic_store(slot_flag(p, wg, my_slot, hb), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
+  // spread merge: the slots this wave left empty are stamped too, so that the
+  // workgroup that started last can tell when every part has published
+  if (SPREAD && lane == 0) {
+    for (int sl = 0; sl < 2; ++sl)
+      if (!(published & (1 << sl)))
+        __hip_atomic_store(spread_flag(p, wg, sl, hb), int(4u * stamp + kSpreadNone), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+  }
 }
 
-template <bool FUSED, bool PAGED, int NB, bool CAUSAL>
+// ---- spread merge: at the end of the launch, every thread of the workgroup
+
+__device__ __forceinline__ bool stamped(int flag, unsigned stamp) {
+  return (unsigned(flag) >> 2) == (stamp & 0x3fffffffu);
+}
+
+// Wave 0: wait until the n parts of a segment (partial slots of workgroups
+// p0 .. p0 + n - 1) have stamped the flags of their NF folding waves with this
+// generation. Only called once every workgroup of the generation has
+// started: each part then reaches its end without waiting on anything, so
+// the wait ends; it is bounded all the same.
+template <int NF>
+__device__ void wait_spread(const DecodeParams& p, int p0, int n, unsigned stamp) {
+  constexpr int U = 4;  // flags per lane in one round of loads
+  const int lane = threadIdx.x & 63;
+  const int total = n * NF;
+  for (int q0 = 0; q0 < total; q0 += 64 * U) {
+    int* f[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int q = q0 + 64 * u + lane;
+      const int k = q / NF;
+      f[u] = q < total ? spread_flag(p, p0 + k, k == 0 ? 1 : 0, q - k * NF) : nullptr;
+    }
+    for (int it = 0; it < kFlagSpins; ++it) {
+      int v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        v[u] = f[u] ? __hip_atomic_load(f[u], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0;
+      bool ready = true;
+#pragma unroll
+      for (int u = 0; u < U; ++u) ready = ready && (!f[u] || stamped(v[u], stamp));
+      if (__ballot(!ready) == 0) break;
+      __builtin_amdgcn_s_sleep(2);
+    }
+  }
+}
+
+// Merge of heads list[0 .. cnt) of segment (s, j), whose n parts' states sit
+// in the partial slots of workgroups p0 .. p0 + n - 1 (slot 1 of p0, slot 0
+// of the others), and their output rows, by the whole workgroup. A head's
+// arithmetic depends only on n, not on which workgroup merges it: its R =
+// min(16, n) rows of 32 threads (R a power of two; 16 / R heads per pass)
+// fold parts r, r + R, r + 2R, ... in order (row r, thread c: dims 4c ..
+// 4c + 3, four parts' loads in flight), and the R row states are then folded
+// in row order through LDS (buf: 16 x 32 f32x4, then 16 m and 16 l). Every
+// fold is the step of the in-order merge above.
+template <bool CAUSAL>
+__device__ void merge_heads(const DecodeParams& p, int s, int j, int p0, int n, const int* list, int cnt,
+                            float* buf) {
+  const int tid = threadIdx.x;
+  const int r16 = tid >> 5, c = tid & 31;
+  int R = 1;
+  while (2 * R <= n && 2 * R <= 16) R *= 2;
+  const int per_pass = 16 / R;
+  const int hs = r16 / R, rr = r16 - hs * R;
+  const int G = p.gblk;
+  const __amdgpu_buffer_rsrc_t rs = slots_rsrc(p);
+  const int ml_off = G * kD * int(sizeof(float));
+  for (int base = 0; base < cnt; base += per_pass) {
+    const int hi = base + hs;
+    const bool valid = hi < cnt;
+    const int hh = valid ? list[hi] : 0;
+    float run = kNegInf, den = 0.0f;
+    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (valid) {
+      for (int k0 = rr; k0 < n; k0 += 4 * R) {
+        f32x4 o[4];
+        float m[4], l[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int k = k0 + u * R;
+          if (k < n) {
+            const int sb = slot_offset(p, p0 + k, k == 0 ? 1 : 0);
+            o[u] = coherent_load4(rs, sb + (hh * kD + 4 * c) * int(sizeof(float)));
+            m[u] = coherent_load1(rs, sb + ml_off + hh * 4);
+            l[u] = coherent_load1(rs, sb + ml_off + (G + hh) * 4);
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          if (k0 + u * R < n) {
+            const MergeWeights2 mw = merge_weights2(run, m[u]);
+            acc = merge_o(acc, mw, o[u]);
+            den = merge_l(den, mw, l[u]);
+            run = mw.run;
+          }
+        }
+      }
+    }
+    *reinterpret_cast<f32x4*>(buf + 4 * tid) = acc;
+    if (c == 0) {
+      buf[2048 + r16] = run;
+      buf[2064 + r16] = den;
+    }
+    __syncthreads();
+    if (valid && rr == 0) {
+      float run2 = kNegInf, den2 = 0.0f;
+      f32x4 res = {0.0f, 0.0f, 0.0f, 0.0f};
+      for (int r = 0; r < R; ++r) {
+        const int row = hs * R + r;
+        const MergeWeights2 mw = merge_weights2(run2, buf[2048 + row]);
+        res = merge_o(res, mw, *reinterpret_cast<const f32x4*>(buf + 4 * (row * 32 + c)));
+        den2 = merge_l(den2, mw, buf[2064 + row]);
+        run2 = mw.run;
+      }
+      const float inv = den2 > 0.0f ? 1.0f / den2 : 0.0f;
+      uint16_t* out = static_cast<uint16_t*>(p.out) + vrow<CAUSAL>(p, s, j, G, hh) * kD;
+      *reinterpret_cast<uint2*>(out + 4 * c) = to_bf16x4(res * inv);
+    }
+    __syncthreads();
+  }
+}
+
+// The end of a spread-merge launch. Each shared piece of this workgroup
+// (s_spread: per partial slot the segment, its first part p0, its part count
+// n, this part's index, the code of each folding wave's flag) has been
+// published. A folding wave's heads whose flag is not decided yet wait a
+// bounded time for every workgroup to have started: if they all have, they
+// are this part's to merge (kSpreadMerging), else they are left to the
+// workgroup that started last (kSpreadOrphan); the flag then says which.
+// This part merges heads own, own + n, own + 2n, ... of the segment, those
+// that are its to merge, once every part has stamped its flags. The
+// workgroup that started last (s_sweep) then waits until every flag of the
+// generation is stamped and decided, and merges the orphaned slices.
+// buf: the free LDS ring.
+template <int NB, bool CAUSAL>
+__device__ void spread_end(const DecodeParams& p, int parts, int Lreg, unsigned stamp, int* s_spread,
+                           const int* s_sweep, float* buf) {
+  constexpr int NF = folders<NB>();
+  constexpr int kFolderHeads = kBlockHeads * NB / NF;  // heads per folding wave
+  int* list = reinterpret_cast<int*>(buf + 2080);      // heads to merge (up to 64)
+  int* orph = reinterpret_cast<int*>(buf + 2176);      // count, then orphaned flags (workgroup, slot, wave)
+  const int tid = threadIdx.x, w = tid >> 6;
+  const int G = p.gblk;
+  __syncthreads();  // every wave has published; the ring is free
+  // undecided slices: wait (bounded) for every workgroup to have started
+  bool undecided = false;
+  for (int slot = 0; slot < 2; ++slot)
+    for (int hb = 0; hb < NF; ++hb)
+      undecided = undecided || (s_spread[8 * slot + 7] != 0 && s_spread[8 * slot + 5 + hb] == int(kSpreadPublished));
+  if (undecided) {
+    __syncthreads();  // every thread has read the codes before they change
+    if (w == 0) {
+      bool all_started = false;
+      for (int it = 0; it < kStartSpins && !all_started; ++it) {
+        int v = 0;
+        if ((tid & 63) == 0)
+          v = __hip_atomic_load(p.ws_stamp + kStartedWord, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        all_started = unsigned(__builtin_amdgcn_readfirstlane(v)) == stamp;
+        if (!all_started) __builtin_amdgcn_s_sleep(8);
+      }
+      if (tid == 0) {
+        const unsigned code = all_started ? kSpreadMerging : kSpreadOrphan;
+        for (int slot = 0; slot < 2; ++slot)
+          for (int hb = 0; hb < NF; ++hb)
+            if (s_spread[8 * slot + 7] != 0 && s_spread[8 * slot + 5 + hb] == int(kSpreadPublished)) {
+              s_spread[8 * slot + 5 + hb] = int(code);
+              __hip_atomic_store(spread_flag(p, blockIdx.x, slot, hb), int(4u * stamp + code), __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
+            }
+      }
+    }
+    __syncthreads();
+  }
+  for (int slot = 0; slot < 2; ++slot) {
+    const int* job = s_spread + 8 * slot;
+    if (job[7] == 0) continue;
+    const int s = job[0], j = job[1], p0 = job[2], n = job[3], own = job[4];
+    int cnt = 0;
+    for (int hh = own; hh < G; hh += n)
+      if (job[5 + hh / kFolderHeads] == int(kSpreadMerging)) {
+        if (tid == 0) list[cnt] = hh;
+        ++cnt;
+      }
+    if (cnt == 0) continue;
+    if (w == 0) wait_spread<NF>(p, p0, n, stamp);
+    __syncthreads();
+    merge_heads<CAUSAL>(p, s, j, p0, n, list, cnt, buf);
+  }
+  if (*s_sweep == 0) return;
+  // every workgroup of the generation has started: wait for all their flags
+  // (one round of loads per thread), collect the orphaned slices
+  const int nflags = parts * 2 * NF;
+  if (tid == 0) orph[0] = 0;
+  __syncthreads();
+  int v[kSweepPerThread];
+  int* f[kSweepPerThread];
+#pragma unroll
+  for (int u = 0; u < kSweepPerThread; ++u) {
+    const int q = tid + u * kBlockThreads;
+    const int wgx = q / (2 * NF), rem = q - wgx * (2 * NF);
+    f[u] = q < nflags ? spread_flag(p, wgx, rem / NF, rem % NF) : nullptr;
+    v[u] = f[u] ? __hip_atomic_load(f[u], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0;
+  }
+#pragma unroll
+  for (int u = 0; u < kSweepPerThread; ++u) {
+    if (f[u]) {
+      for (int it = 0; it < kFlagSpins && !(stamped(v[u], stamp) && (unsigned(v[u]) & 3u) != kSpreadPublished);
+           ++it) {
+        __builtin_amdgcn_s_sleep(2);
+        v[u] = __hip_atomic_load(f[u], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      if ((unsigned(v[u]) & 3u) == kSpreadOrphan) {
+        const int pos = __hip_atomic_fetch_add(&orph[0], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        orph[1 + pos] = tid + u * kBlockThreads;
+      }
+    }
+  }
+  __syncthreads();
+  const int norph = orph[0];
+  for (int o = 0; o < norph; ++o) {
+    const int q = orph[1 + o];
+    const int wgx = q / (2 * NF), rem = q - wgx * (2 * NF);
+    const int sl = rem / NF, hb = rem - sl * NF;
+    // the orphan's piece: the shared piece of workgroup wgx's range in slot sl
+    Range rx = locate(p, Lreg, wgx);
+    StreamPiece pc;
+    bool found = false;
+    while (next_piece(p, rx, Lreg, pc))
+      if (pc.p0 != pc.p1 && (wgx == pc.p0 ? 1 : 0) == sl) {
+        found = true;
+        break;
+      }
+    if (!found) continue;
+    const int n = pc.p1 - pc.p0 + 1;
+    int cnt = 0;
+    for (int hh = wgx - pc.p0; hh < G; hh += n)
+      if (hh / kFolderHeads == hb) {
+        if (tid == 0) list[cnt] = hh;
+        ++cnt;
+      }
+    if (cnt == 0) continue;
+    __syncthreads();
+    merge_heads<CAUSAL>(p, pc.s, pc.grp, pc.p0, n, list, cnt, buf);
+  }
+}
+
+template <bool FUSED, bool PAGED, int NB, bool CAUSAL, bool SPREAD>
 __global__ __launch_bounds__(kBlockThreads, 1) void decode_stream_kernel(DecodeParams p) {
   constexpr int kRing = ring_slots<NB>();
   constexpr int kHeads = kBlockHeads * NB;
@@ -633,6 +929,9 @@ __global__ __launch_bounds__(kBlockThreads, 1) void decode_stream_kernel(DecodeP
   __shared__ int s_next;          // next range tile to hand out
   __shared__ int s_folded[folders<NB>()];  // range tiles folded so far, per folding wave
   __shared__ int s_tk[2][16];     // ticket results handed from block 0's folding wave to the others
+  __shared__ int s_gen;           // spread merge: the generation of the last launch
+  __shared__ int s_sweep;         // spread merge: this workgroup started last
+  __shared__ int s_spread[16];    // spread merge: this workgroup's shared pieces, by partial slot
   constexpr int kStreamers = kWaves - folders<NB>();  // waves 0 .. kStreamers - 1 stream, the others fold
 
   const int wg = blockIdx.x;
@@ -647,12 +946,18 @@ __global__ __launch_bounds__(kBlockThreads, 1) void decode_stream_kernel(DecodeP
   if (threadIdx.x < kRing) s_ready[threadIdx.x] = -1;
   if (threadIdx.x < folders<NB>()) s_folded[threadIdx.x] = 0;
   if (threadIdx.x < 16) s_tk[1][threadIdx.x] = 0;
-  if (threadIdx.x == 0) s_next = 0;
+  if (threadIdx.x < 16) s_spread[threadIdx.x] = 0;
+  if (threadIdx.x == 0) {
+    s_next = 0;
+    s_sweep = 0;
+    s_gen = SPREAD ? __hip_atomic_load(p.ws_stamp + kGenWord, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0;
+  }
   if (!FUSED) zero_empty_sequences<uint16_t, CAUSAL>(p, wg);
   __syncthreads();
 
   const int Lreg = s_lens[lane];
   const Range range = locate(p, Lreg, wg);
+  const unsigned stamp = unsigned(s_gen) + 1u;  // this launch's generation (spread merge)
 
   if (w < kStreamers) {
     // ---- streaming wave: take tiles, leave their states in the ring
@@ -801,33 +1106,44 @@ __global__ __launch_bounds__(kBlockThreads, 1) void decode_stream_kernel(DecodeP
       __builtin_amdgcn_wave_barrier();
       if (lane == 0) __hip_atomic_store(&s_ready[slot], k, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
     }
-    return;
-  }
-
-  // ---- folding waves (one per block of 16 heads, or per 32 with four blocks;
-  // lane layout by the heads in use)
-  if constexpr (NB == 1) {
-    if (G <= 4) fold_range<2, FUSED, NB, CAUSAL>(p, range, Lreg, 0, s_o, s_m, s_l, s_ready, s_folded, s_tk, s_lens);
-    else if (G <= 8) fold_range<4, FUSED, NB, CAUSAL>(p, range, Lreg, 0, s_o, s_m, s_l, s_ready, s_folded, s_tk, s_lens);
-    else fold_range<8, FUSED, NB, CAUSAL>(p, range, Lreg, 0, s_o, s_m, s_l, s_ready, s_folded, s_tk, s_lens);
+  } else if constexpr (NB == 1) {
+    // ---- folding waves (one per block of 16 heads, or per 32 with four
+    // blocks; lane layout by the heads in use)
+    if (G <= 4)
+      fold_range<2, FUSED, NB, CAUSAL, SPREAD>(p, range, Lreg, 0, s_o, s_m, s_l, s_ready, s_folded, s_tk, s_lens, stamp,
+                                       s_spread, &s_sweep);
+    else if (G <= 8)
+      fold_range<4, FUSED, NB, CAUSAL, SPREAD>(p, range, Lreg, 0, s_o, s_m, s_l, s_ready, s_folded, s_tk, s_lens, stamp,
+                                       s_spread, &s_sweep);
+    else
+      fold_range<8, FUSED, NB, CAUSAL, SPREAD>(p, range, Lreg, 0, s_o, s_m, s_l, s_ready, s_folded, s_tk, s_lens, stamp,
+                                       s_spread, &s_sweep);
   } else {
     // 16 heads per folding wave (NCH = 8) with two blocks, 32 (NCH = 16) with four
-    fold_range<NB == 4 ? 16 : 8, FUSED, NB, CAUSAL>(p, range, Lreg, w - kStreamers, s_o, s_m, s_l, s_ready,
-                                                    s_folded, s_tk, s_lens);
+    fold_range<NB == 4 ? 16 : 8, FUSED, NB, CAUSAL, SPREAD>(p, range, Lreg, w - kStreamers, s_o, s_m, s_l, s_ready,
+                                                    s_folded, s_tk, s_lens, stamp, s_spread, &s_sweep);
   }
+  if constexpr (SPREAD) spread_end<NB, CAUSAL>(p, range.parts, Lreg, stamp, s_spread, &s_sweep, &s_o[0][0]);
 }
 
+template <bool FUSED, bool PAGED, bool CAUSAL, bool SPREAD>
+void launch_merge(const DecodeParams& p, hipStream_t stream) {
+  if (p.gblk <= kBlockHeads)
+    hipLaunchKernelGGL((decode_stream_kernel<FUSED, PAGED, 1, CAUSAL, SPREAD>), dim3(p.workgroups),
+                       dim3(kBlockThreads), 0, stream, p);
+  else if (p.gblk <= 2 * kBlockHeads)
+    hipLaunchKernelGGL((decode_stream_kernel<FUSED, PAGED, 2, CAUSAL, SPREAD>), dim3(p.workgroups),
+                       dim3(kBlockThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL((decode_stream_kernel<FUSED, PAGED, 4, CAUSAL, SPREAD>), dim3(p.workgroups),
+                       dim3(kBlockThreads), 0, stream, p);
+}
+// The spread merge is its own set of instances, so that the others compile
+// as they would without it.
 template <bool FUSED, bool PAGED, bool CAUSAL>
 void launch(const DecodeParams& p, hipStream_t stream) {
-  if (p.gblk <= kBlockHeads)
-    hipLaunchKernelGGL((decode_stream_kernel<FUSED, PAGED, 1, CAUSAL>), dim3(p.workgroups), dim3(kBlockThreads), 0,
-                       stream, p);
-  else if (p.gblk <= 2 * kBlockHeads)
-    hipLaunchKernelGGL((decode_stream_kernel<FUSED, PAGED, 2, CAUSAL>), dim3(p.workgroups), dim3(kBlockThreads), 0,
-                       stream, p);
-  else
-    hipLaunchKernelGGL((decode_stream_kernel<FUSED, PAGED, 4, CAUSAL>), dim3(p.workgroups), dim3(kBlockThreads), 0,
-                       stream, p);
+  if (p.merge_spread) launch_merge<FUSED, PAGED, CAUSAL, true>(p, stream);
+  else launch_merge<FUSED, PAGED, CAUSAL, false>(p, stream);
 }
 
 }  // namespace
@@ -855,18 +1171,18 @@ int stream_workgroups_per_cu(bool fused, bool paged, int G) {
   int n = 0;
   hipError_t e;
   switch (k) {
-    case 0: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_stream_kernel<false, false, 1, false>, kBlockThreads, 0); break;
-    case 1: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_stream_kernel<true, false, 1, false>, kBlockThreads, 0); break;
-    case 2: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_stream_kernel<false, true, 1, false>, kBlockThreads, 0); break;
-    case 3: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_stream_kernel<true, true, 1, false>, kBlockThreads, 0); break;
-    case 4: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_stream_kernel<false, false, 2, false>, kBlockThreads, 0); break;
-    case 5: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_stream_kernel<true, false, 2, false>, kBlockThreads, 0); break;
-    case 6: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_stream_kernel<false, true, 2, false>, kBlockThreads, 0); break;
-    case 7: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_stream_kernel<true, true, 2, false>, kBlockThreads, 0); break;
-    case 8: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_stream_kernel<false, false, 4, false>, kBlockThreads, 0); break;
-    case 9: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_stream_kernel<true, false, 4, false>, kBlockThreads, 0); break;
-    case 10: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_stream_kernel<false, true, 4, false>, kBlockThreads, 0); break;
-    default: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_stream_kernel<true, true, 4, false>, kBlockThreads, 0); break;
+    case 0: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_stream_kernel<false, false, 1, false, false>, kBlockThreads, 0); break;
+    case 1: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_stream_kernel<true, false, 1, false, false>, kBlockThreads, 0); break;
+    case 2: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_stream_kernel<false, true, 1, false, false>, kBlockThreads, 0); break;
+    case 3: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_stream_kernel<true, true, 1, false, false>, kBlockThreads, 0); break;
+    case 4: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_stream_kernel<false, false, 2, false, false>, kBlockThreads, 0); break;
+    case 5: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_stream_kernel<true, false, 2, false, false>, kBlockThreads, 0); break;
+    case 6: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_stream_kernel<false, true, 2, false, false>, kBlockThreads, 0); break;
+    case 7: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_stream_kernel<true, true, 2, false, false>, kBlockThreads, 0); break;
+    case 8: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_stream_kernel<false, false, 4, false, false>, kBlockThreads, 0); break;
+    case 9: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_stream_kernel<true, false, 4, false, false>, kBlockThreads, 0); break;
+    case 10: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_stream_kernel<false, true, 4, false, false>, kBlockThreads, 0); break;
+    default: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_stream_kernel<true, true, 4, false, false>, kBlockThreads, 0); break;
   }
   if (e != hipSuccess || n <= 0) {
     (void)hipGetLastError();

@@ -70,6 +70,7 @@ struct Plan {
   int nhb;
   int workgroups;
   bool merge_kernel;  // shared segments merged by a second launch
+  bool merge_spread;  // (stream kernel) shared segments merged at the end of the launch, a slice of heads by each part
   int seg_lead;       // empty schedule units ahead of each segment (tiles for the stream kernel)
   bool stream;        // the one-block stream kernel (decode_stream.hip)
 };
@@ -101,10 +102,11 @@ int plan_decode(int b, int h, int g, int d_k, int d_v, int cap, int max_len, int
                 d_k, d_v);
   if (max_len > cap) return fail(GQA_ERR_CAPACITY, "max_len=%d exceeds cap=%d", max_len, cap);
   if (max_len > kMaxLen) return fail(GQA_ERR_UNSUPPORTED, "max_len=%d exceeds %d", max_len, kMaxLen);
-  const int merge_req = path & (GQA_MERGE_INLINE | GQA_MERGE_KERNEL);
-  const int path_req = path & ~(GQA_MERGE_INLINE | GQA_MERGE_KERNEL);
+  const int merge_flags = GQA_MERGE_INLINE | GQA_MERGE_KERNEL | GQA_MERGE_SPREAD;
+  const int merge_req = path & merge_flags;
+  const int path_req = path & ~merge_flags;
   if ((path_req != GQA_PATH_AUTO && path_req != GQA_PATH_VECTOR && path_req != GQA_PATH_MATRIX) ||
-      merge_req == (GQA_MERGE_INLINE | GQA_MERGE_KERNEL))
+      (merge_req & (merge_req - 1)) != 0)
     return fail(GQA_ERR_UNSUPPORTED, "path=%d is not a GQA_PATH_* value, optionally with one GQA_MERGE_* flag",
                 path);
   path = path_req;
@@ -165,7 +167,14 @@ int plan_decode(int b, int h, int g, int d_k, int d_v, int cap, int max_len, int
   // against 101, b = 64, h = 128, g = 2 at 2,048 positions 47 against 56;
   // four parts, b = 40, h = 64, g = 2, two tokens, 45.5 against 44; five
   // parts, b = 64, h = 64, g = 1, 45 against 36.5).
-  if (merge_req == GQA_MERGE_KERNEL) {
+  plan->merge_spread = false;
+  if (merge_req == GQA_MERGE_SPREAD) {
+    if (!plan->stream)
+      return fail(GQA_ERR_UNSUPPORTED,
+                  "GQA_MERGE_SPREAD needs the stream kernel (bf16, d = 128, 3-64 heads per KV head, b <= 64)");
+    plan->merge_kernel = false;
+    plan->merge_spread = true;
+  } else if (merge_req == GQA_MERGE_KERNEL) {
     plan->merge_kernel = true;
   } else if (merge_req == GQA_MERGE_INLINE) {
     plan->merge_kernel = false;
@@ -175,7 +184,7 @@ int plan_decode(int b, int h, int g, int d_k, int d_v, int cap, int max_len, int
     plan->merge_kernel = plan->stream && plan->gblk > 32 ? per_head * 32 > 48 * 1024
                                                         : per_head * plan->gblk > 64 * 1024;
   }
-  if (auto_grid && !plan->merge_kernel) {
+  if (auto_grid && !plan->merge_kernel && !plan->merge_spread) {
     // Inline merges: for large head groups keep at least G/2 tiles per
     // workgroup (at most 4 KiB of partial state per 16 KiB tile of K/V) so
     // that the single-workgroup merges stay small.
@@ -250,7 +259,8 @@ int gqa_decode_plan(int b, int h, int g, int d_k, int d_v, int cap, int max_len,
   const int rc = plan_decode(b, h, g, d_k, d_v, cap, max_len, dtype, path, workgroups, &plan);
   if (rc != GQA_OK) return rc;
   if (chosen_path)
-    *chosen_path = plan.path | (plan.merge_kernel ? GQA_MERGE_KERNEL : GQA_MERGE_INLINE) |
+    *chosen_path = plan.path |
+                   (plan.merge_spread ? GQA_MERGE_SPREAD : plan.merge_kernel ? GQA_MERGE_KERNEL : GQA_MERGE_INLINE) |
                    (plan.stream ? GQA_PLAN_STREAM : 0);
   if (chosen_workgroups) *chosen_workgroups = plan.workgroups;
   return ok();
@@ -294,10 +304,12 @@ int decode_prepare(const char* fn, void* out, const void* q, void* k_cache, void
   char* wsb = static_cast<char*>(workspace);
   p.seg_info = reinterpret_cast<int2*>(wsb);
   p.ws_slots = reinterpret_cast<float*>(wsb + ws.info_bytes);
-  p.ws_done = reinterpret_cast<int*>(wsb + usable - gqa::kDoneBytes);
-  p.ws_cnt = reinterpret_cast<int*>(wsb + usable - gqa::kDoneBytes - ws.cnt_bytes);
+  p.ws_stamp = reinterpret_cast<int*>(wsb + usable - gqa::kStampBytes);
+  p.ws_done = reinterpret_cast<int*>(wsb + usable - gqa::kStampBytes - gqa::kDoneBytes);
+  p.ws_cnt = reinterpret_cast<int*>(wsb + usable - gqa::kStampBytes - gqa::kDoneBytes - ws.cnt_bytes);
   p.cnt_stride = int(gqa::counter_stride(b, h));
   p.merge_kernel = plan.merge_kernel ? 1 : 0;
+  p.merge_spread = plan.merge_spread ? 1 : 0;
   p.b = b;
   p.h = h;
   p.g = g;

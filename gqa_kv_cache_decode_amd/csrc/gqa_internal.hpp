@@ -39,7 +39,8 @@
 //   [slots]  float [kMaxWorkgroups][2][slot_floats]           slot = o[gb][d], m[gb], l[gb]
 // and from its end (size rounded down to 256 bytes):
 //   [tickets] int32, cnt_stride apart                         zero between calls
-//   [done]   int32 counters and slot flags, last kDoneBytes   zero between calls
+//   [done]   int32 counters and slot flags, kDoneBytes         zero between calls
+//   [stamps] spread-merge generations and flags, last kStampBytes   zero before the first call
 // slot_floats = gb*d + round_up(2*gb, 4), so every slot and its o block are
 // 16-byte aligned. Each region starts on a 256-byte boundary.
 //
@@ -107,6 +108,8 @@ struct DecodeParams {
   int seg_lead;     // empty schedule units ahead of each segment (piece start-up cost)
   int cnt_stride;   // ints between consecutive tickets
   int merge_kernel; // 1: shared segments are merged by merge_partials_kernel after this launch
+  int merge_spread; // 1 (stream kernel): each part of a shared segment merges a slice of its heads at the end
+  int* ws_stamp;    // spread merge: generation words and stamped flags (never reset)
   int2* seg_info;   // merge_kernel: per segment (p0, p1) of its shared pieces, p1 = -1 if none
   float scale_log2; // scale * log2(e)
   PagedLayout pg;   // paged caches (pg.table != nullptr); cap = table_stride << bs_log2
@@ -122,6 +125,14 @@ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 constexpr size_t kFlagsOffset = 4096;
 constexpr int kFlagBlocks = 2;
 constexpr size_t kDoneBytes = kFlagsOffset + size_t(kMaxWorkgroups) * 2 * kFlagBlocks * sizeof(int);
+// After those, the stamps of the spread merge (stream kernel): the launch
+// generation and the generation whose workgroups have all started (first 256
+// bytes), then one flag per partial slot and folding wave holding
+// 4 * generation + code. They are never reset: a flag counts only when its
+// generation is the current one, so the region is zero before the first call
+// and then left as it is (or zeroed with the rest).
+constexpr size_t kStampFlagsOffset = 256;
+constexpr size_t kStampBytes = kStampFlagsOffset + size_t(kMaxWorkgroups) * 2 * kFlagBlocks * sizeof(int);
 
 // y_s = x w_s^T for up to three weight matrices w_s [n_out_s][n_in] (bf16,
 // packed by launch_pack_weight), x [rows][n_in], y_s [rows][n_out_s];
@@ -148,8 +159,9 @@ struct FoldParams {
 // Workspace layout, relative to the end of the caller's buffer so that a
 // buffer sized for one shape serves every smaller shape without the regions
 // of one call overlapping those of another: partial slots from the start,
-// then (at the end) the tickets and, in the last kDoneBytes bytes, the fused
-// step's counters. Tickets sit 128 bytes apart when b*h <= 8192, so that workgroups
+// then (at the end) the tickets, kDoneBytes bytes of the fused step's
+// counters and the slot flags, and the last kStampBytes bytes of spread-merge
+// stamps. Tickets sit 128 bytes apart when b*h <= 8192, so that workgroups
 // taking tickets of different segments at the same moment do not contend for
 // one cache line; the ticket region never shrinks as b*h grows.
 inline size_t counter_stride(int b, int h) { return size_t(b) * size_t(h) <= 8192 ? 32 : 1; }
@@ -174,7 +186,7 @@ inline WorkspaceLayout workspace_layout(int b, int h, int gblk_bound, int d_v, i
   w.info_bytes = align256(size_t(b) * size_t(h) * 2 * sizeof(int));
   w.slot_bytes = align256(size_t(slot_wgs) * 2 * size_t(slot_floats_for(gblk_bound, d_v)) * sizeof(float));
   w.cnt_bytes = align256(counter_ints(b, h) * sizeof(int));
-  w.total = w.info_bytes + w.slot_bytes + w.cnt_bytes + kDoneBytes;
+  w.total = w.info_bytes + w.slot_bytes + w.cnt_bytes + kDoneBytes + kStampBytes;
   return w;
 }
 

@@ -82,6 +82,10 @@ extern "C" {
 /* How segments split over several workgroups are merged; OR one into path. */
 #define GQA_MERGE_INLINE 0x10 /* by the segment's last workgroup, inside the decode launch */
 #define GQA_MERGE_KERNEL 0x20 /* by a second launch, one workgroup per (segment, head)  */
+/* By the segment's parts themselves at the end of the decode launch, each
+   merging a slice of the heads (the stream kernel only: bf16, d = 128, 3-64
+   heads per KV head, b <= 64; GQA_ERR_UNSUPPORTED elsewhere). */
+#define GQA_MERGE_SPREAD 0x80
 /* Reported by gqa_decode_plan only: the matrix path runs its one-block
    streaming kernel (one query token, up to 16 heads per KV head, b <= 64). */
 #define GQA_PLAN_STREAM 0x40
@@ -116,11 +120,14 @@ int gqa_kv_append(void* k_cache, void* v_cache, const void* k_new, const void* v
  *
  * The workspace (256-byte aligned) holds the split-softmax partial states of
  * the persistent workgroups from its start, and int32 counters and flags at
- * its end: the last 36864 + c bytes (of the buffer's size rounded down to
- * 256), where c = 4*n rounded up to a multiple of 256, with n = 32*b*h if
- * b*h <= 8192, else max(b*h, 262144). Those counter bytes must
- * be ZERO before the first call that uses a buffer (e.g. allocate it
- * zero-filled); every call leaves them zero again. Because the counters are
+ * its end: the last 36864 + 33024 + c bytes (of the buffer's size rounded
+ * down to 256), where c = 4*n rounded up to a multiple of 256, with n = 32*b*h
+ * if b*h <= 8192, else max(b*h, 262144). Those bytes must be ZERO before the
+ * first call that uses a buffer (e.g. allocate it zero-filled). Every call
+ * leaves the first 36864 + c of them zero again; the last 33024 hold launch
+ * stamps (a generation count and flags tagged with it) that calls merging
+ * split segments with GQA_MERGE_SPREAD update and never reset: leave them as
+ * they are between calls, or zero them together with the rest. Because the counters are
  * placed from the end, a buffer sized for one shape serves any sequence of
  * calls with b, h, h/g and d_v no larger. Two calls that share a workspace
  * must be ordered (same stream or synchronised); calls with distinct

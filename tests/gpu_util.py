@@ -65,13 +65,23 @@ def assert_parity(got_dev: torch.Tensor, ref: np.ndarray, dtype: str, what: str 
     return rep
 
 
+STAMP_BYTES = 33024  # the workspace's last bytes: spread-merge stamps, never reset
+
+
 def counter_bytes(ws, b, h):
-    """The workspace's counter region (its last 36864 + c bytes, as the header states)."""
+    """The workspace's counter region (36864 + c bytes before its last 33024, as the header states)."""
     bh = b * h
     n = 32 * bh if bh <= 8192 else max(bh, 262144)
     usable = (ws.numel() * ws.element_size()) & ~255
     cnt = ((4 * n + 255) // 256) * 256
-    return ws.view(torch.uint8)[usable - 36864 - cnt: usable]
+    return ws.view(torch.uint8)[usable - STAMP_BYTES - 36864 - cnt: usable - STAMP_BYTES]
+
+
+def stamp_words(ws):
+    """The spread merge's generation words (launch generation, generation whose workgroups all started)."""
+    usable = (ws.numel() * ws.element_size()) & ~255
+    words = ws.view(torch.uint8)[usable - STAMP_BYTES: usable - STAMP_BYTES + 256].view(torch.int32)
+    return int(words[0]), int(words[32])
 
 
 def assert_counters_zero(ws, b, h):

@@ -195,6 +195,25 @@ def test_plan_choices(lib):
                                ctypes.byref(c)) == _lib.ERR_UNSUPPORTED
 
 
+def test_plan_spread_merge(lib):
+    def plan(b, h, g, d, cap, max_len, dtype, path, wgs=0):
+        p, c = ctypes.c_int(), ctypes.c_int()
+        rc = lib.gqa_decode_plan(b, h, g, d, d, cap, max_len, dtype, path, wgs, ctypes.byref(p), ctypes.byref(c))
+        return rc, p.value
+    # kept where the stream kernel runs, whatever the grid
+    for args in [(8, 32, 1, 128, 4160, 4097), (16, 64, 8, 128, 8256, 8193), (2, 192, 3, 128, 300, 200)]:
+        for wgs in (0, 1, 2048):
+            rc, p = plan(*args, _lib.BF16, _lib.PATH_MATRIX | _lib.MERGE_SPREAD, wgs)
+            assert rc == _lib.OK and p == _lib.PATH_MATRIX | _lib.MERGE_SPREAD | _lib.PLAN_STREAM, (args, wgs)
+    # refused elsewhere: more than 64 sequences, fp32, other head dims, two heads per KV head
+    for args, dt in [((65, 32, 1, 128, 300, 200), _lib.BF16), ((2, 4, 2, 16, 128, 65), _lib.F32),
+                     ((8, 32, 1, 64, 300, 200), _lib.BF16), ((8, 2, 1, 128, 300, 200), _lib.BF16)]:
+        assert plan(*args, dt, _lib.MERGE_SPREAD)[0] == _lib.ERR_UNSUPPORTED, args
+    # with another merge flag
+    for other in (_lib.MERGE_INLINE, _lib.MERGE_KERNEL):
+        assert plan(8, 32, 1, 128, 4160, 4097, _lib.BF16, _lib.MERGE_SPREAD | other)[0] == _lib.ERR_UNSUPPORTED
+
+
 def test_step_rejects(lib):
     def call(**kw):
         a = dict(out=FAKE, q=FAKE, kn=FAKE, vn=FAKE, k=FAKE, v=FAKE, lens=FAKE, b=2, h=8, g=2, dk=128, dv=128,

@@ -8,7 +8,7 @@ for bit against the same loop run eagerly, with the program's own eager work
 (resetting the caches and lengths, reading results back) and
 synchronisations between the replays; every replay is also held to the
 oracle bar at its last step. Covered: the fused one-token step on both paths
-and with the split merge by a second launch, the multi-token step (append +
+and with the split merge by a second launch or by the parts themselves, the multi-token step (append +
 attention, two launches per step) on contiguous and paged caches, and the
 fused step over a block pool.
 """
@@ -23,12 +23,14 @@ from paged_util import make_paged
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("dtype,b,h,g,d,lens", [
-    ("bf16", 4, 28, 4, 128, [100, 300, 511, 64]),     # matrix path
-    ("f32", 2, 4, 2, 16, [37, 64]),                    # vector path (the tiny fp32 shape)
-    ("bf16", 2, 32, 1, 128, [700, 1300]),              # matrix path, merged by a second launch
+@pytest.mark.parametrize("dtype,b,h,g,d,lens,path", [
+    ("bf16", 4, 28, 4, 128, [100, 300, 511, 64], api.PATH_AUTO),     # matrix path
+    ("f32", 2, 4, 2, 16, [37, 64], api.PATH_AUTO),                    # vector path (the tiny fp32 shape)
+    ("bf16", 2, 32, 1, 128, [700, 1300], api.PATH_AUTO),              # matrix path, merged by a second launch
+    # merged by the parts at the end of the launch: the generation advances on every replay
+    ("bf16", 2, 32, 1, 128, [700, 1300], api.PATH_MATRIX | api.MERGE_SPREAD),
 ])
-def test_graph_replay_of_a_decode_loop(gpu_lib, oracle_mod, dtype, b, h, g, d, lens):
+def test_graph_replay_of_a_decode_loop(gpu_lib, oracle_mod, dtype, b, h, g, d, lens, path):
     steps = 6
     cap = max(lens) + steps + 4
     bt = inputs.Batch(seed=1600 + h + g, b=b, h=h, g=g, d=d, cap=cap, lens=lens, dtype=dtype, poison=True)
@@ -45,7 +47,7 @@ def test_graph_replay_of_a_decode_loop(gpu_lib, oracle_mod, dtype, b, h, g, d, l
     def loop():
         m = int(bt.lens.max())
         for s in range(steps):
-            api.decode_step(outs[s], qs[s], news[s][0], news[s][1], kc, vc, lens_d, m + s, scale, ws)
+            api.decode_step(outs[s], qs[s], news[s][0], news[s][1], kc, vc, lens_d, m + s, scale, ws, path=path)
 
     def reset():
         kc.copy_(kc0)
