@@ -45,6 +45,7 @@ constexpr int kSegmentLead64 = 5;      // four-wave kernel, 33-64 heads
 constexpr int kMaxSegmentLead = 5;
 constexpr int kLeadMinUnits = 8;       // four-wave kernels: lead units only from this many units per workgroup
 constexpr int kStreamLeadTiles = 6;    // one-block stream kernel: empty tiles ahead of each segment
+constexpr int kStreamSplitMinTiles = 5;  // stream kernel, second-launch merge: tiles per workgroup at least
 
 bool supported_head_dim(int d) { return d == 16 || d == 32 || d == 64 || d == 128 || d == 256; }
 
@@ -183,6 +184,17 @@ int plan_decode(int b, int h, int g, int d_k, int d_v, int cap, int max_len, int
     const long long per_head = slots_per_segment * d_v * 4;  // partial-state bytes per head
     plan->merge_kernel = plan->stream && plan->gblk > 32 ? per_head * 32 > 48 * 1024
                                                         : per_head * plan->gblk > 64 * 1024;
+  }
+  if (auto_grid && plan->stream && plan->merge_kernel) {
+    // Merged by the second launch, a split segment costs one partial state
+    // per part; where the parts would hold only a few tiles, fewer and longer
+    // ones are faster: at least kStreamSplitMinTiles tiles (schedule units,
+    // lead tiles included) per workgroup. MQA step, b = 8, h = 32, L = 4097
+    // (1,080 units): 17.35 us at 256 workgroups, 16.7 at 224, 16.8 at 192,
+    // 17.0 at 160; one long sequence per KV head (b = 4, L = 32769, 16 units
+    // per workgroup at 256) is fastest on the whole chip and unchanged.
+    const long long by_work = (units_bound + kStreamSplitMinTiles - 1) / kStreamSplitMinTiles;
+    if (workgroups > by_work) workgroups = int(by_work > 0 ? by_work : 1);
   }
   if (auto_grid && !plan->merge_kernel && !plan->merge_spread) {
     // Inline merges: for large head groups keep at least G/2 tiles per
