@@ -304,6 +304,8 @@ def main():
             bytes_after.append(kv_bytes_attended(wl.g, wl.d, wl.d, wl.elem_bytes, lens0 + ntok * (len(bytes_after) + 1)))
         return bytes_after[c]
 
+    launched = []  # attended bytes of every decode launch of the run, in order
+
     def step(i, ev_pair=None):
         si = i % n_sets
         st = sets[si]
@@ -331,6 +333,7 @@ def main():
         if ev_pair is not None:
             ev_pair[1].record(stream)
         taken[si] = c + 1
+        launched.append(step_bytes(c))
         return step_bytes(c)
 
     for i in range(args.warmup):
@@ -461,6 +464,9 @@ def main():
             "new_tokens_per_step": ntok, "tokens_per_s": round(wl.b * ntok * args.steps / (elapsed_ms / 1e3), 1),
             "launch": "one HIP graph of all timed steps" if args.graph else "eager, one call per step",
             "kv_bytes_per_step": int(bytes_per_launch),
+            # every decode launch of this run (warm-up, timed, percentile pass):
+            # the denominator of a counter run's traffic ratio
+            "kv_bytes_per_launch_all": int(round(float(np.mean(launched)))),
         },
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
