@@ -1139,11 +1139,17 @@ void launch_merge(const DecodeParams& p, hipStream_t stream) {
                        dim3(kBlockThreads), 0, stream, p);
 }
 // The spread merge is its own set of instances, so that the others compile
-// as they would without it.
+// as they would without it; it is requested through the contiguous
+// one-token calls only (the host refuses it elsewhere).
 template <bool FUSED, bool PAGED, bool CAUSAL>
 void launch(const DecodeParams& p, hipStream_t stream) {
-  if (p.merge_spread) launch_merge<FUSED, PAGED, CAUSAL, true>(p, stream);
-  else launch_merge<FUSED, PAGED, CAUSAL, false>(p, stream);
+  if constexpr (!PAGED && !CAUSAL) {
+    if (p.merge_spread) {
+      launch_merge<FUSED, PAGED, CAUSAL, true>(p, stream);
+      return;
+    }
+  }
+  launch_merge<FUSED, PAGED, CAUSAL, false>(p, stream);
 }
 
 }  // namespace

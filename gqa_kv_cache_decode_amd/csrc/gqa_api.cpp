@@ -170,9 +170,10 @@ int plan_decode(int b, int h, int g, int d_k, int d_v, int cap, int max_len, int
   // parts, b = 64, h = 64, g = 1, 45 against 36.5).
   plan->merge_spread = false;
   if (merge_req == GQA_MERGE_SPREAD) {
-    if (!plan->stream)
+    if (!plan->stream || paged || causal)
       return fail(GQA_ERR_UNSUPPORTED,
-                  "GQA_MERGE_SPREAD needs the stream kernel (bf16, d = 128, 3-64 heads per KV head, b <= 64)");
+                  "GQA_MERGE_SPREAD needs the stream kernel (bf16, d = 128, 3-64 heads per KV head, b <= 64) "
+                  "on a contiguous cache with one query token per sequence");
     plan->merge_kernel = false;
     plan->merge_spread = true;
   } else if (merge_req == GQA_MERGE_KERNEL) {

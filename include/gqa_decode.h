@@ -84,7 +84,8 @@ extern "C" {
 #define GQA_MERGE_KERNEL 0x20 /* by a second launch, one workgroup per (segment, head)  */
 /* By the segment's parts themselves at the end of the decode launch, each
    merging a slice of the heads (the stream kernel only: bf16, d = 128, 3-64
-   heads per KV head, b <= 64; GQA_ERR_UNSUPPORTED elsewhere). */
+   heads per KV head, b <= 64, through gqa_decode_attention_ex and
+   gqa_decode_step_ex; GQA_ERR_UNSUPPORTED elsewhere). */
 #define GQA_MERGE_SPREAD 0x80
 /* Reported by gqa_decode_plan only: the matrix path runs its one-block
    streaming kernel (one query token, up to 16 heads per KV head, b <= 64). */
