@@ -19,7 +19,11 @@ the attended lengths L_b. roofline.achieved uses the same bytes per decode
 launch over the decode kernel's average launch duration, from HIP events on
 the launch stream: for the fused step (one launch per step) the timed
 region's time over the step count; with --unfused, a pair of events around
-each decode launch.
+each decode launch. The roofline's peak is the nominal 8 TB/s; the line also
+states the rate against the read bandwidth this part sustains, measured in
+the same run by a plain streaming read of 2 GiB (gqa_read_bandwidth: one
+workgroup per compute unit, the decode kernels' non-temporal 16-byte loads;
+median of 10 launches): roofline.measured_read_gbs, frac_of_measured_read.
 
 With --layer the step is one gqa_decode_layer call instead: the query, key
 and value projections of the new token (one launch), the fused append +
@@ -425,6 +429,9 @@ def main():
     plan_stream = plan_stream and ntok == 1
     traffic = None if (args.paged or ntok > 1 or args.unfused) else traffic_from_profile(wl.name)
 
+    read_gbs = measured_read_bandwidth(dev)
+    log(f"measured streaming read: {read_gbs:.1f} GB/s")
+
     cpu = None
     if args.cpu_seconds > 0 and ntok == 1:
         log("timing the CPU oracle ...")
@@ -480,6 +487,9 @@ def main():
                       + ("" if args.unfused else " (fused step)" if ntok == 1 else
                          f" (causal, {ntok} tokens) + kv_append_kernel") + (", paged" if args.paged else ""),
             "kernel_avg_us": round(kern_avg_ms * 1e3, 3),
+            # the same rate against what a plain streaming read sustains on this part
+            "measured_read_gbs": round(read_gbs, 1),
+            "frac_of_measured_read": round(achieved / read_gbs, 4),
         },
         "cpu_baseline": cpu,
     }
@@ -488,6 +498,32 @@ def main():
     if flushed is not None:
         rec["flushed"] = flushed
     print(json.dumps(rec), flush=True)
+
+
+def measured_read_bandwidth(dev, nbytes: int = 2 << 30, reps: int = 10) -> float:
+    """Median GB/s of gqa_read_bandwidth over a buffer of nbytes (far beyond the last-level
+    cache), one 512-thread workgroup per compute unit: the read rate the decode kernels'
+    roofline is also stated against."""
+    import torch
+
+    from gqa_kv_cache_decode_amd import api
+
+    buf = torch.ones(nbytes // 4, dtype=torch.int32, device=dev)
+    sink = torch.zeros(torch.cuda.get_device_properties(dev).multi_processor_count, dtype=torch.int32, device=dev)
+    for _ in range(3):
+        api.read_bandwidth(buf, sink)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    stream = torch.cuda.current_stream()
+    for a, b in evs:
+        a.record(stream)
+        api.read_bandwidth(buf, sink)
+        b.record(stream)
+    torch.cuda.synchronize()
+    if int((sink.to(torch.int64) % (1 << 32)).sum().item()) % (1 << 32) != (nbytes // 4) % (1 << 32):
+        raise RuntimeError("streaming read: the checksum of the read buffer is wrong")
+    ms = float(np.median([a.elapsed_time(b) for a, b in evs]))
+    del buf
+    return nbytes / (ms / 1e3) / 1e9
 
 
 def bench_layer(args, wl, dev):

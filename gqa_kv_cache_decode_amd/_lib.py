@@ -65,6 +65,7 @@ SIGNATURES = {
     "gqa_decode_step_multi_paged": (_i32, [_vp] * 8 + [_i32] * 10 + [_f32, _i32, _vp, _sz, _vp]),
     "gqa_decode_step_static": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                                       _f32, _i32, _vp]),
+    "gqa_read_bandwidth": (_i32, [_vp, _sz, _vp, _i32, _vp]),
     "gqa_last_error": (ctypes.c_char_p, []),
 }
 

@@ -297,6 +297,21 @@ def fold_kv_heads(dst: torch.Tensor, src: torch.Tensor, lens: torch.Tensor | Non
     return dst
 
 
+def read_bandwidth(src: torch.Tensor, sink: torch.Tensor, stream=None) -> torch.Tensor:
+    """Read every byte of src once (C entry point gqa_read_bandwidth), one workgroup per sink word.
+
+    src: any contiguous device tensor whose byte size is a multiple of 16; sink: int32 [workgroups],
+    receiving each workgroup's sum of the 32-bit words it read (mod 2^32).
+    """
+    _check_gpu(src, sink)
+    if sink.dtype != torch.int32 or sink.dim() != 1:
+        raise ValueError("sink must be int32 [workgroups]")
+    rc = _lib.load().gqa_read_bandwidth(src.data_ptr(), src.numel() * src.element_size(), sink.data_ptr(),
+                                        sink.numel(), _stream_handle(stream))
+    _lib.check(rc, "gqa_read_bandwidth")
+    return sink
+
+
 def _paged_args(k_pool: torch.Tensor, v_pool: torch.Tensor, table: torch.Tensor, lens: torch.Tensor):
     _check_gpu(k_pool, v_pool, table, lens)
     if table.dtype != torch.int32 or lens.dtype != torch.int32 or table.dim() != 2:

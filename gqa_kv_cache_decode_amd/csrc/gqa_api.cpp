@@ -434,6 +434,22 @@ size_t gqa_packed_weight_bytes(int n_out, int n_in) {
   return gqa::packed_weight_bytes(n_out, n_in);
 }
 
+int gqa_read_bandwidth(const void* src, size_t bytes, uint32_t* sink, int workgroups, void* stream) {
+  if (!src || !sink) return fail(GQA_ERR_ARG, "gqa_read_bandwidth: null pointer argument");
+  if (workgroups < 1 || workgroups > gqa::kMaxWorkgroups)
+    return fail(GQA_ERR_ARG, "gqa_read_bandwidth: workgroups=%d must be in [1, %d]", workgroups, gqa::kMaxWorkgroups);
+  if (bytes % 16 != 0 || !aligned16(src))
+    return fail(GQA_ERR_ARG, "gqa_read_bandwidth: src must be 16-byte aligned and bytes=%zu a multiple of 16", bytes);
+  // one workgroup's range is addressed with 32-bit offsets
+  const size_t chunks_per_wg = (bytes / 16 + size_t(workgroups) - 1) / size_t(workgroups);
+  if (chunks_per_wg > size_t(INT32_MAX) / 16)
+    return fail(GQA_ERR_ARG, "gqa_read_bandwidth: %zu bytes over %d workgroups exceed 2 GiB per workgroup", bytes,
+                workgroups);
+  const hipError_t e = gqa::launch_read_bandwidth(src, bytes, sink, workgroups, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(GQA_ERR_HIP, "gqa_read_bandwidth launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
 int gqa_fold_kv_heads(void* dst, const void* src, const int32_t* lens, int b, int g_src, int g_dst, int cap_src,
                       int cap_dst, int d, int max_rows, int dtype, void* stream) {
   if (!dst || !src) return fail(GQA_ERR_ARG, "gqa_fold_kv_heads: null pointer argument");

@@ -210,6 +210,7 @@ hipError_t launch_linear(const LinearParams& p, hipStream_t stream);
 size_t packed_weight_bytes(int n_out, int n_in);
 hipError_t launch_pack_weight(void* dst, const void* src, int n_out, int n_in, hipStream_t stream);
 hipError_t launch_fold(const FoldParams& p, int b, int dtype, hipStream_t stream);
+hipError_t launch_read_bandwidth(const void* src, size_t bytes, uint32_t* sink, int workgroups, hipStream_t stream);
 
 // Workgroups of the decode kernel instance that fit on one compute unit at
 // once (runtime occupancy query, cached; 0 if the runtime cannot say).

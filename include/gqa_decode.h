@@ -14,8 +14,9 @@
  * paged caches (*_paged), n new tokens per sequence with a causal mask
  * (*_multi, and *_multi_paged over paged caches), the layer's projections
  * and the whole layer step (gqa_pack_weight, gqa_linear, gqa_decode_layer),
- * and the mean-fold of KV heads that turns an MHA cache into a GQA one
- * (gqa_fold_kv_heads).
+ * the mean-fold of KV heads that turns an MHA cache into a GQA one
+ * (gqa_fold_kv_heads), and a streaming read that measures the bandwidth the
+ * decode kernels are held to (gqa_read_bandwidth).
  * The step is the per-layer decode loop of the
  * "LLM inference 05" notes (albangk): push K, push V, then attend; and the
  * incremental attention of the "Fast Transformer Decoding: One Write-Head is
@@ -389,6 +390,22 @@ int gqa_decode_step_multi_paged(void* out, const void* q, const void* k_new, con
  */
 int gqa_fold_kv_heads(void* dst, const void* src, const int32_t* lens, int b, int g_src, int g_dst, int cap_src,
                       int cap_dst, int d, int max_rows, int dtype, void* stream);
+
+/*
+ * Read bandwidth of this part, for stating the decode kernels' roofline
+ * against what the memory system sustains as well as against the nominal
+ * peak (decode is memory-bound: "LLM inference 05", the decode phase).
+ * Reads the `bytes` bytes at src (device memory, 16-byte aligned, bytes a
+ * multiple of 16) once, with a persistent grid of `workgroups` 512-thread
+ * workgroups (1 .. 2048; one per compute unit is the decode kernels' grid)
+ * and the decode kernels' non-temporal 16-byte loads: workgroup w reads the
+ * contiguous chunks [w n / P, (w + 1) n / P) of the n = bytes / 16 chunks and
+ * writes the sum of their 32-bit words (mod 2^32) to sink[w] (device
+ * uint32 [workgroups]), so the sink's total is the sum of every word of the
+ * buffer. Errors: GQA_ERR_ARG (null pointers, alignment, workgroups out of
+ * range, more than 2 GiB per workgroup), GQA_ERR_HIP. Asynchronous on stream.
+ */
+int gqa_read_bandwidth(const void* src, size_t bytes, uint32_t* sink, int workgroups, void* stream);
 
 /*
  * Describe the launch gqa_decode_attention_ex would make on the current

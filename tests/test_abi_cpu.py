@@ -288,6 +288,19 @@ def test_fold_rejects(lib):
     assert lib.gqa_last_error().decode() != ""
 
 
+def test_read_bandwidth_rejects(lib):
+    def call(src=FAKE, nbytes=1 << 20, sink=FAKE, wgs=256):
+        return lib.gqa_read_bandwidth(src, nbytes, sink, wgs, None)
+    assert call(src=None) == _lib.ERR_ARG
+    assert call(sink=None) == _lib.ERR_ARG
+    for wgs in (0, -1, 2049):
+        assert call(wgs=wgs) == _lib.ERR_ARG, wgs
+    assert call(nbytes=(1 << 20) + 8) == _lib.ERR_ARG                # not a multiple of 16
+    assert call(src=ctypes.c_void_p(0x1008)) == _lib.ERR_ARG         # not 16-byte aligned
+    assert call(nbytes=(1 << 31) + 16, wgs=1) == _lib.ERR_ARG         # more than 2 GiB for one workgroup
+    assert b"gqa_read_bandwidth" in lib.gqa_last_error()
+
+
 def test_paged_rejects(lib):
     FAKE2 = ctypes.c_void_p(1 << 40)
 

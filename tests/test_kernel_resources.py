@@ -27,7 +27,7 @@ MAX_VGPRS = 256          # architected VGPRs a wave can address (occupancy aside
 
 SOURCES = ["decode_matrix.hip", "decode_stream.hip", "decode_vector.hip", "decode_vector_paged.hip",
            "decode_vector_multi.hip", "decode_vector_multi_paged.hip", "merge_partials.hip", "kv_append.hip",
-           "fold_heads.hip", "linear.hip"]
+           "fold_heads.hip", "linear.hip", "read_bandwidth.hip"]
 
 
 @pytest.fixture(scope="module")
@@ -105,7 +105,8 @@ def test_vector_kernel_instances_use_no_scratch(remarks, source, count):
         assert r["scratch"] == 0, f"{name}: {r['scratch']} bytes of scratch per lane"
 
 
-@pytest.mark.parametrize("source", ["merge_partials.hip", "kv_append.hip", "fold_heads.hip", "linear.hip"])
+@pytest.mark.parametrize("source", ["merge_partials.hip", "kv_append.hip", "fold_heads.hip", "linear.hip",
+                                    "read_bandwidth.hip"])
 def test_other_kernels_use_no_scratch(remarks, source):
     res = remarks[source]
     assert res, f"no kernels found in {source}"
