@@ -23,7 +23,9 @@ each decode launch. The roofline's peak is the nominal 8 TB/s; the line also
 states the rate against the read bandwidth this part sustains, measured in
 the same run by a plain streaming read of 2 GiB (gqa_read_bandwidth: one
 workgroup per compute unit, the decode kernels' non-temporal 16-byte loads;
-median of 10 launches): roofline.measured_read_gbs, frac_of_measured_read.
+20 launches back to back): roofline.measured_read_gbs, frac_of_measured_read;
+and the time of the same read of exactly one step's KV bytes in one launch
+(roofline.read_of_step_bytes_us), the floor of a step's time on this part.
 
 With --layer the step is one gqa_decode_layer call instead: the query, key
 and value projections of the new token (one launch), the fused append +
@@ -429,8 +431,8 @@ def main():
     plan_stream = plan_stream and ntok == 1
     traffic = None if (args.paged or ntok > 1 or args.unfused) else traffic_from_profile(wl.name)
 
-    read_gbs = measured_read_bandwidth(dev)
-    log(f"measured streaming read: {read_gbs:.1f} GB/s")
+    read_gbs, read_step_us = measured_read_bandwidth(dev, step_bytes=bytes_per_launch)
+    log(f"measured streaming read: {read_gbs:.1f} GB/s; of one step's KV bytes: {read_step_us:.2f} us")
 
     cpu = None
     if args.cpu_seconds > 0 and ntok == 1:
@@ -490,6 +492,8 @@ def main():
             # the same rate against what a plain streaming read sustains on this part
             "measured_read_gbs": round(read_gbs, 1),
             "frac_of_measured_read": round(achieved / read_gbs, 4),
+            # the same read of exactly one step's KV bytes, one launch: the floor of a step's time
+            "read_of_step_bytes_us": round(read_step_us, 2),
         },
         "cpu_baseline": cpu,
     }
@@ -500,30 +504,42 @@ def main():
     print(json.dumps(rec), flush=True)
 
 
-def measured_read_bandwidth(dev, nbytes: int = 2 << 30, reps: int = 10) -> float:
-    """Median GB/s of gqa_read_bandwidth over a buffer of nbytes (far beyond the last-level
-    cache), one 512-thread workgroup per compute unit: the read rate the decode kernels'
-    roofline is also stated against."""
+def measured_read_bandwidth(dev, step_bytes: float, nbytes: int = 2 << 30, reps: int = 20):
+    """gqa_read_bandwidth with one 512-thread workgroup per compute unit, timed back to back
+    like the decode steps: the GB/s of reading a buffer of nbytes (far beyond the last-level
+    cache), the rate the decode kernels' roofline is also stated against; and the time of
+    reading one step's KV bytes in one launch, from windows of that buffer taken in rotation
+    (as the cache sets are), so that no window is still in the last-level cache when it is
+    read again."""
     import torch
 
     from gqa_kv_cache_decode_amd import api
 
     buf = torch.ones(nbytes // 4, dtype=torch.int32, device=dev)
     sink = torch.zeros(torch.cuda.get_device_properties(dev).multi_processor_count, dtype=torch.int32, device=dev)
-    for _ in range(3):
-        api.read_bandwidth(buf, sink)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
     stream = torch.cuda.current_stream()
-    for a, b in evs:
+
+    def timed(views):
+        # back to back, as the decode steps are timed: the region's time over the launches
+        for v in views[:3]:
+            api.read_bandwidth(v, sink)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
         a.record(stream)
-        api.read_bandwidth(buf, sink)
+        for k in range(reps):
+            api.read_bandwidth(views[k % len(views)], sink)
         b.record(stream)
-    torch.cuda.synchronize()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    ms = timed([buf])
     if int((sink.to(torch.int64) % (1 << 32)).sum().item()) % (1 << 32) != (nbytes // 4) % (1 << 32):
         raise RuntimeError("streaming read: the checksum of the read buffer is wrong")
-    ms = float(np.median([a.elapsed_time(b) for a, b in evs]))
-    del buf
-    return nbytes / (ms / 1e3) / 1e9
+    words = max(4, int(step_bytes) // 16 * 4)
+    windows = [buf[k * words:(k + 1) * words] for k in range(max(1, min(8, buf.numel() // words)))]
+    step_ms = timed(windows)
+    del buf, windows
+    return nbytes / (ms / 1e3) / 1e9, step_ms * 1e3
 
 
 def bench_layer(args, wl, dev):
