@@ -88,8 +88,9 @@ extern "C" {
    heads per KV head, b <= 64, through gqa_decode_attention_ex and
    gqa_decode_step_ex; GQA_ERR_UNSUPPORTED elsewhere). */
 #define GQA_MERGE_SPREAD 0x80
-/* Reported by gqa_decode_plan only: the matrix path runs its one-block
-   streaming kernel (one query token, up to 16 heads per KV head, b <= 64). */
+/* Reported by gqa_decode_plan only: the matrix path runs its streaming
+   kernel (3-64 query heads, or virtual heads of several tokens, per KV
+   head, b <= 64). */
 #define GQA_PLAN_STREAM 0x40
 
 /*
@@ -166,11 +167,13 @@ int gqa_decode_attention(void* out, const void* q, const void* k_cache, const vo
 /*
  * gqa_decode_attention with explicit launch choices, for tests and tuning.
  * path: GQA_PATH_AUTO / GQA_PATH_VECTOR / GQA_PATH_MATRIX (MATRIX on an
- *   unsupported shape gives GQA_ERR_UNSUPPORTED), optionally OR-ed with
- *   GQA_MERGE_INLINE or GQA_MERGE_KERNEL to fix how split segments are
- *   merged (default: a second launch once a segment's partial states exceed
- *   64 KiB, e.g. few long sequences with many heads per KV head). The second
- *   launch goes to the same stream.
+ *   unsupported shape gives GQA_ERR_UNSUPPORTED), optionally OR-ed with one
+ *   of GQA_MERGE_INLINE, GQA_MERGE_KERNEL or GQA_MERGE_SPREAD to fix how
+ *   split segments are merged (default: a second launch once a segment's
+ *   partial states exceed 64 KiB, e.g. few long sequences with many heads
+ *   per KV head, else inside the launch). The second launch goes to the
+ *   same stream. GQA_MERGE_SPREAD keeps the call to one launch; it uses the
+ *   workspace's stamp region (see gqa_decode_workspace_size).
  * workgroups: size of the persistent grid that splits the work evenly;
  *   0 = automatic (compute units x resident workgroups per unit), otherwise
  *   1 .. 2048 (GQA_ERR_UNSUPPORTED outside that range).
