@@ -2,7 +2,9 @@
 every run): batch, head counts, head dim, element type, ragged lengths with
 empty sequences, kernel path, merge mode, grid size and call form (two calls
 or the fused step) all vary together, so that combinations the hand-picked
-cases miss are held to the same bar against the fp64 oracle.
+cases miss are held to the same bar against the fp64 oracle; a second set
+draws the stream kernel's shapes with their split segments merged by the
+parts at the end of the launch (GQA_MERGE_SPREAD).
 """
 import numpy as np
 import pytest
@@ -34,8 +36,35 @@ def _cases(n=40, seed=20261202):
     return out
 
 
+def _spread_cases(n=24, seed=20261203):
+    # shapes the stream kernel runs (bf16, d = 128, 3-64 heads per KV head, b <= 64), split
+    # segments merged by their parts at the end of the launch (GQA_MERGE_SPREAD)
+    rng = np.random.default_rng(seed)
+    out = []
+    for k in range(n):
+        g = int(rng.choice([1, 1, 2, 3, 4, 8]))
+        G = int(rng.choice([3, 4, 5, 7, 8, 12, 16, 17, 24, 32, 33, 48, 64]))
+        b = int(rng.integers(1, 65))
+        lens = rng.integers(0, 900, b)
+        lens[rng.random(b) < 0.15] = 0
+        path = int(rng.choice([api.PATH_AUTO, api.PATH_MATRIX])) | api.MERGE_SPREAD
+        wgs = int(rng.choice([0, 0, 1, 7, 64, 300, 2048]))
+        fused = bool(rng.random() < 0.5)
+        out.append((100 + k, "bf16", b, g * G, g, 128, [int(x) for x in lens], path, wgs, fused))
+    return out
+
+
 @pytest.mark.parametrize("case", _cases(), ids=lambda c: f"case{c[0]}")
 def test_random_shape(gpu_lib, oracle_mod, case):
+    _run_case(oracle_mod, case)
+
+
+@pytest.mark.parametrize("case", _spread_cases(), ids=lambda c: f"spread{c[0]}")
+def test_random_shape_spread_merge(gpu_lib, oracle_mod, case):
+    _run_case(oracle_mod, case)
+
+
+def _run_case(oracle_mod, case):
     k, dtype, b, h, g, d, lens, path, wgs, fused = case
     cap = max(lens) + 3
     bt = inputs.Batch(seed=3000 + k, b=b, h=h, g=g, d=d, cap=cap, lens=lens, dtype=dtype, poison=True)
