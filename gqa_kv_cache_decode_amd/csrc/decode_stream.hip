@@ -93,7 +93,7 @@ constexpr int fold_batch() { return NCH == 16 ? 1 : (NCH == 8 ? 2 : 4); }
 constexpr int kCountGroups = 16;    // first-level counters of the fused step's length update
 constexpr int kCountStride = 32;    // ints between counters (128 bytes)
 // Spread merge: words of the stamp region, and the codes of its slot flags
-// (flag = 4 * generation + code).
+// (a flag's high word; its low word is the generation that wrote it).
 constexpr int kGenWord = 0;       // generation of the last launch
 constexpr int kStartedWord = 32;  // generation whose workgroups have all started
 constexpr unsigned kSpreadPublished = 0;  // state published; who merges its slice is not decided yet
@@ -406,9 +406,14 @@ __device__ __forceinline__ int* slot_flag(const DecodeParams& p, int wg, int slo
   return p.ws_done + kFlagsOffset / sizeof(int) + (wg * 2 + slot) * kFlagBlocks + half;
 }
 // Spread merge: stamped flag of folding wave `half`'s heads in partial slot
-// `slot` of workgroup `wg` (never reset).
-__device__ __forceinline__ int* spread_flag(const DecodeParams& p, int wg, int slot, int half) {
-  return p.ws_stamp + kStampFlagsOffset / sizeof(int) + (wg * 2 + slot) * kFlagBlocks + half;
+// `slot` of workgroup `wg` (never reset), and its value for a generation and
+// a code.
+__device__ __forceinline__ unsigned long long* spread_flag(const DecodeParams& p, int wg, int slot, int half) {
+  return reinterpret_cast<unsigned long long*>(p.ws_stamp + kStampFlagsOffset / sizeof(int)) +
+         (wg * 2 + slot) * kFlagBlocks + half;
+}
+__device__ __forceinline__ unsigned long long flag_value(unsigned stamp, unsigned code) {
+  return (static_cast<unsigned long long>(code) << 32) | stamp;
 }
 
 // The merging folding wave `half` waits until every other part of segment
@@ -649,7 +654,7 @@ __device__ void fold_range(const DecodeParams& p, const Range& range, int Lreg, 
       const unsigned code =
           unsigned(__builtin_amdgcn_readfirstlane(started)) == stamp ? kSpreadMerging : kSpreadPublished;
       if (lane == 0) {
-        __hip_atomic_store(spread_flag(p, wg, my_slot, hb), int(4u * stamp + code), __ATOMIC_RELAXED,
+        __hip_atomic_store(spread_flag(p, wg, my_slot, hb), flag_value(stamp, code), __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
         int* job = s_spread + 8 * my_slot;  // the piece, for the end of the launch
         job[0] = s;
@@ -674,16 +679,17 @@ __device__ void fold_range(const DecodeParams& p, const Range& range, int Lreg, 
   if (SPREAD && lane == 0) {
     for (int sl = 0; sl < 2; ++sl)
       if (!(published & (1 << sl)))
-        __hip_atomic_store(spread_flag(p, wg, sl, hb), int(4u * stamp + kSpreadNone), __ATOMIC_RELAXED,
+        __hip_atomic_store(spread_flag(p, wg, sl, hb), flag_value(stamp, kSpreadNone), __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
 // ---- spread merge: at the end of the launch, every thread of the workgroup
 
-__device__ __forceinline__ bool stamped(int flag, unsigned stamp) {
-  return (unsigned(flag) >> 2) == (stamp & 0x3fffffffu);
+__device__ __forceinline__ bool stamped(unsigned long long flag, unsigned stamp) {
+  return unsigned(flag) == stamp;
 }
+__device__ __forceinline__ unsigned flag_code(unsigned long long flag) { return unsigned(flag >> 32); }
 
 // Wave 0: wait until the n parts of a segment (partial slots of workgroups
 // p0 .. p0 + n - 1) have stamped the flags of their NF folding waves with this
@@ -696,7 +702,7 @@ __device__ void wait_spread(const DecodeParams& p, int p0, int n, unsigned stamp
   const int lane = threadIdx.x & 63;
   const int total = n * NF;
   for (int q0 = 0; q0 < total; q0 += 64 * U) {
-    int* f[U];
+    unsigned long long* f[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int q = q0 + 64 * u + lane;
@@ -704,7 +710,7 @@ __device__ void wait_spread(const DecodeParams& p, int p0, int n, unsigned stamp
       f[u] = q < total ? spread_flag(p, p0 + k, k == 0 ? 1 : 0, q - k * NF) : nullptr;
     }
     for (int it = 0; it < kFlagSpins; ++it) {
-      int v[U];
+      unsigned long long v[U];
 #pragma unroll
       for (int u = 0; u < U; ++u)
         v[u] = f[u] ? __hip_atomic_load(f[u], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0;
@@ -837,7 +843,7 @@ __device__ void spread_end(const DecodeParams& p, int parts, int Lreg, unsigned 
           for (int hb = 0; hb < NF; ++hb)
             if (s_spread[8 * slot + 7] != 0 && s_spread[8 * slot + 5 + hb] == int(kSpreadPublished)) {
               s_spread[8 * slot + 5 + hb] = int(code);
-              __hip_atomic_store(spread_flag(p, blockIdx.x, slot, hb), int(4u * stamp + code), __ATOMIC_RELAXED,
+              __hip_atomic_store(spread_flag(p, blockIdx.x, slot, hb), flag_value(stamp, code), __ATOMIC_RELAXED,
                                  __HIP_MEMORY_SCOPE_AGENT);
             }
       }
@@ -865,8 +871,8 @@ __device__ void spread_end(const DecodeParams& p, int parts, int Lreg, unsigned 
   const int nflags = parts * 2 * NF;
   if (tid == 0) orph[0] = 0;
   __syncthreads();
-  int v[kSweepPerThread];
-  int* f[kSweepPerThread];
+  unsigned long long v[kSweepPerThread];
+  unsigned long long* f[kSweepPerThread];
 #pragma unroll
   for (int u = 0; u < kSweepPerThread; ++u) {
     const int q = tid + u * kBlockThreads;
@@ -877,12 +883,11 @@ __device__ void spread_end(const DecodeParams& p, int parts, int Lreg, unsigned 
 #pragma unroll
   for (int u = 0; u < kSweepPerThread; ++u) {
     if (f[u]) {
-      for (int it = 0; it < kFlagSpins && !(stamped(v[u], stamp) && (unsigned(v[u]) & 3u) != kSpreadPublished);
-           ++it) {
+      for (int it = 0; it < kFlagSpins && !(stamped(v[u], stamp) && flag_code(v[u]) != kSpreadPublished); ++it) {
         __builtin_amdgcn_s_sleep(2);
         v[u] = __hip_atomic_load(f[u], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
-      if ((unsigned(v[u]) & 3u) == kSpreadOrphan) {
+      if (flag_code(v[u]) == kSpreadOrphan) {
         const int pos = __hip_atomic_fetch_add(&orph[0], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
         orph[1 + pos] = tid + u * kBlockThreads;
       }
@@ -957,7 +962,8 @@ __global__ __launch_bounds__(kBlockThreads, 1) void decode_stream_kernel(DecodeP
 
   const int Lreg = s_lens[lane];
   const Range range = locate(p, Lreg, wg);
-  const unsigned stamp = unsigned(s_gen) + 1u;  // this launch's generation (spread merge)
+  // this launch's generation (spread merge); never zero, the value of zeroed flags
+  const unsigned stamp = unsigned(s_gen) + 1u == 0u ? 1u : unsigned(s_gen) + 1u;
 
   if (w < kStreamers) {
     // ---- streaming wave: take tiles, leave their states in the ring

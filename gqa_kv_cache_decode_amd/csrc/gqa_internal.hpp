@@ -127,12 +127,13 @@ constexpr int kFlagBlocks = 2;
 constexpr size_t kDoneBytes = kFlagsOffset + size_t(kMaxWorkgroups) * 2 * kFlagBlocks * sizeof(int);
 // After those, the stamps of the spread merge (stream kernel): the launch
 // generation and the generation whose workgroups have all started (first 256
-// bytes), then one flag per partial slot and folding wave holding
-// 4 * generation + code. They are never reset: a flag counts only when its
-// generation is the current one, so the region is zero before the first call
-// and then left as it is (or zeroed with the rest).
+// bytes), then one 64-bit flag per partial slot and folding wave holding the
+// generation (low word) and a code (high word). They are never reset: a flag
+// counts only when its generation is the current one (generations are
+// nonzero, so zeroed flags never do), so the region is zero before the first
+// call and then left as it is (or zeroed with the rest).
 constexpr size_t kStampFlagsOffset = 256;
-constexpr size_t kStampBytes = kStampFlagsOffset + size_t(kMaxWorkgroups) * 2 * kFlagBlocks * sizeof(int);
+constexpr size_t kStampBytes = kStampFlagsOffset + size_t(kMaxWorkgroups) * 2 * kFlagBlocks * sizeof(uint64_t);
 
 // y_s = x w_s^T for up to three weight matrices w_s [n_out_s][n_in] (bf16,
 // packed by launch_pack_weight), x [rows][n_in], y_s [rows][n_out_s];

@@ -123,11 +123,11 @@ int gqa_kv_append(void* k_cache, void* v_cache, const void* k_new, const void* v
  *
  * The workspace (256-byte aligned) holds the split-softmax partial states of
  * the persistent workgroups from its start, and int32 counters and flags at
- * its end: the last 36864 + 33024 + c bytes (of the buffer's size rounded
+ * its end: the last 36864 + 65792 + c bytes (of the buffer's size rounded
  * down to 256), where c = 4*n rounded up to a multiple of 256, with n = 32*b*h
  * if b*h <= 8192, else max(b*h, 262144). Those bytes must be ZERO before the
  * first call that uses a buffer (e.g. allocate it zero-filled). Every call
- * leaves the first 36864 + c of them zero again; the last 33024 hold launch
+ * leaves the first 36864 + c of them zero again; the last 65792 hold launch
  * stamps (a generation count and flags tagged with it) that calls merging
  * split segments with GQA_MERGE_SPREAD update and never reset: leave them as
  * they are between calls, or zero them together with the rest. Because the counters are

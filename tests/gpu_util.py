@@ -65,11 +65,11 @@ def assert_parity(got_dev: torch.Tensor, ref: np.ndarray, dtype: str, what: str 
     return rep
 
 
-STAMP_BYTES = 33024  # the workspace's last bytes: spread-merge stamps, never reset
+STAMP_BYTES = 65792  # the workspace's last bytes: spread-merge stamps, never reset
 
 
 def counter_bytes(ws, b, h):
-    """The workspace's counter region (36864 + c bytes before its last 33024, as the header states)."""
+    """The workspace's counter region (36864 + c bytes before its last 65792, as the header states)."""
     bh = b * h
     n = 32 * bh if bh <= 8192 else max(bh, 262144)
     usable = (ws.numel() * ws.element_size()) & ~255
