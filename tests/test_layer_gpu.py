@@ -11,7 +11,7 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_util import assert_parity, to_dev, to_host_bits
+from gpu_util import assert_counters_zero, assert_parity, to_dev, to_host_bits
 from gqa_kv_cache_decode_amd import api, inputs
 from gqa_kv_cache_decode_amd.workloads import WORKLOADS
 
@@ -128,3 +128,21 @@ def test_decode_layer_llama3_70b_shape(gpu_lib, oracle_mod):
     pb = LayerProblem(oracle_mod, seed=wl.seed, b=wl.b, h=wl.h, g=wl.g, d=wl.d, d_model=8192, cap=wl.cap,
                       lens=wl.lens)
     _check_layer(pb, 0)
+
+
+@pytest.mark.parametrize("b,h,g,d_model,steps", [
+    (64, 28, 4, 3584, 2),   # the Qwen2.5-7B shape: 64 batch rows, four 16-row batch blocks
+    (33, 16, 2, 1024, 3),   # 33 rows: the last batch block of three holds a single row
+    (24, 8, 8, 512, 2),     # 24 rows: two batch blocks; MHA
+])
+def test_decode_layer_wide_batch(gpu_lib, oracle_mod, b, h, g, d_model, steps):
+    # 17-64 batch rows: two to four 16-row batch blocks per projection MFMA, every
+    # intermediate and the cache against the oracle over several steps
+    print(f"decode layer: b={b} h={h} g={g} d_model={d_model}", flush=True)
+    rng = np.random.default_rng(b + h)
+    lens = rng.integers(0, 300, b).tolist()
+    pb = LayerProblem(oracle_mod, seed=470 + b, b=b, h=h, g=g, d=128, d_model=d_model, cap=max(lens) + steps + 2,
+                      lens=lens)
+    for step in range(steps):
+        _check_layer(pb, step)
+    assert_counters_zero(pb.ws, b, h)
